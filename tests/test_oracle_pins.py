@@ -1,0 +1,413 @@
+"""Pins of the float64 oracle to facts that do not come from the oracle itself.
+
+Each test checks one oracle function against a closed form, an invariant, a
+library routine, a brute-force enumeration or a value printed on the pages,
+chosen so that a dropped term, a wrong sign, a wrong GQA index or a transposed
+operand fails at least one of them.  CPU only.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.ndimage
+import scipy.special
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(1234)
+
+
+# ----------------------------------------------------------------- O1 decode
+def test_decode_single_key_closed_form():
+    d = 8
+    q = np.zeros((1, d)); q[0, 0] = 2.0
+    K = np.zeros((1, 1, d)); K[0, 0, 0] = 3.0
+    V = rng.normal(size=(1, 1, d))
+    r = O.decode_attention(q, K, V, 0.5)
+    assert r["probs"][0, 0] == 1.0
+    np.testing.assert_array_equal(r["out"][0], V[0, 0])
+    assert r["logits"][0, 0] == 3.0          # 0.5 * 2 * 3
+    assert r["lse"][0] == 3.0                # ln(e^3)
+
+
+@pytest.mark.parametrize("a", [-3.0, 0.0, 0.7, 5.0])
+def test_decode_two_keys_is_logistic(a):
+    d, scale = 4, 0.25
+    q = np.zeros((1, d)); q[0, 0] = a
+    K = np.zeros((1, 2, d)); K[0, 0, 0] = 1.0          # s0 = scale*a, s1 = 0
+    V = np.zeros((1, 2, d)); V[0, 0, 1] = 1.0; V[0, 1, 2] = 1.0
+    r = O.decode_attention(q, K, V, scale)
+    p0 = 1.0 / (1.0 + math.exp(-scale * a))
+    assert abs(r["probs"][0, 0] - p0) < 1e-15
+    assert abs(r["probs"][0, 1] - (1 - p0)) < 1e-15
+    assert abs(r["out"][0, 1] - p0) < 1e-15 and abs(r["out"][0, 2] - (1 - p0)) < 1e-15
+    assert abs(r["lse"][0] - math.log(math.exp(scale * a) + 1.0)) < 1e-14
+
+
+def test_decode_equal_keys_uniform():
+    Hq, Hkv, L, d = 4, 2, 37, 16
+    q = rng.normal(size=(Hq, d))
+    K = np.repeat(rng.normal(size=(Hkv, 1, d)), L, axis=1)
+    V = rng.normal(size=(Hkv, L, d))
+    r = O.decode_attention(q, K, V, 0.3)
+    np.testing.assert_allclose(r["probs"], 1.0 / L, rtol=1e-14)
+    for h in range(Hq):
+        np.testing.assert_allclose(r["out"][h], V[h // 2].mean(axis=0), rtol=1e-12, atol=1e-14)
+
+
+def test_decode_matches_scipy_softmax_and_logsumexp():
+    Hq, Hkv, L, d = 8, 2, 300, 64
+    q = rng.normal(size=(Hq, d)); K = rng.normal(size=(Hkv, L, d)); V = rng.normal(size=(Hkv, L, d))
+    scale = 1 / math.sqrt(d)
+    r = O.decode_attention(q, K, V, scale)
+    G = Hq // Hkv
+    for h in range(Hq):
+        s = np.array([scale * sum(q[h, t] * K[h // G, j, t] for t in range(d)) for j in range(L)])
+        np.testing.assert_allclose(r["logits"][h], s, rtol=1e-12, atol=1e-12)
+        p = scipy.special.softmax(s)
+        np.testing.assert_allclose(r["probs"][h], p, rtol=1e-12, atol=1e-15)
+        assert abs(r["lse"][h] - scipy.special.logsumexp(s)) < 1e-12
+        np.testing.assert_allclose(r["out"][h], np.einsum("j,jd->d", p, V[h // G]), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(r["probs"].sum(axis=1), 1.0, rtol=1e-13)
+
+
+def test_decode_gqa_head_mapping_repeat_interleave():
+    # KV head c has constant value c+1: query head h must read head h // G.
+    Hq, Hkv, L, d = 12, 3, 20, 8
+    q = rng.normal(size=(Hq, d)); K = rng.normal(size=(Hkv, L, d))
+    V = np.stack([np.full((L, d), c + 1.0) for c in range(Hkv)])
+    r = O.decode_attention(q, K, V, 0.5)
+    for h in range(Hq):
+        np.testing.assert_allclose(r["out"][h], h // 4 + 1.0, rtol=1e-13)
+
+
+def test_decode_stable_for_huge_logits_and_permutation_invariant():
+    d = 4
+    q = np.array([[100.0, 0, 0, 0]])
+    K = np.zeros((1, 3, d)); K[0, 0, 0] = 100.0; K[0, 1, 0] = -100.0
+    r = O.decode_attention(q, K, None, 1.0)
+    assert np.isfinite(r["probs"]).all() and abs(r["probs"][0, 0] - 1.0) < 1e-15
+    assert r["out"] is None
+    # permuting keys permutes probs and leaves out unchanged
+    Hq, L = 2, 50
+    q = rng.normal(size=(Hq, d)); K = rng.normal(size=(1, L, d)); V = rng.normal(size=(1, L, d))
+    perm = rng.permutation(L)
+    a = O.decode_attention(q, K, V, 0.9); b = O.decode_attention(q, K[:, perm], V[:, perm], 0.9)
+    np.testing.assert_allclose(b["probs"], a["probs"][:, perm], rtol=1e-13)
+    np.testing.assert_allclose(b["out"], a["out"], rtol=1e-12, atol=1e-14)
+
+
+def test_gather_paged_inverts_a_scatter():
+    Hkv, P, d, L = 3, 16, 8, 70
+    logical = rng.normal(size=(Hkv, L, d))
+    n_pages = 9
+    bt = rng.permutation(n_pages)[:5]
+    pages = rng.normal(size=(n_pages, Hkv, P, d))
+    for j in range(L):                       # test-side scatter, slot by slot
+        pages[bt[j // P], :, j % P, :] = logical[:, j, :]
+    np.testing.assert_array_equal(O.gather_paged(pages, bt, L), logical)
+
+
+def test_bf16_widening_exact():
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x7F80, 0x3E00, 0x0001], dtype=np.uint16)
+    want = [1.0, -2.0, 0.0, -0.0, math.inf, 0.125, 2.0 ** -133]
+    got = O.bf16_bits_to_f64(bits)
+    for g, w in zip(got, want):
+        assert g == w and math.copysign(1, g) == math.copysign(1, w)
+
+
+# -------------------------------------------------------------- O2 accumulate
+def test_accumulate_group_mapping_one_hot():
+    Hq, Hkv, L = 8, 2, 8
+    probs = np.eye(Hq, L)                   # head h puts all mass on key h
+    cum = O.accumulate(np.zeros((Hkv, L)), probs)
+    for c in range(Hkv):
+        for j in range(L):
+            assert cum[c, j] == (1.0 if j // 4 == c else 0.0)
+
+
+def test_accumulate_sums_to_steps_times_query_heads():
+    Hq, Hkv, L, d, steps = 6, 3, 40, 16, 7
+    cum = np.zeros((Hkv, L))
+    for _ in range(steps):
+        r = O.decode_attention(rng.normal(size=(Hq, d)), rng.normal(size=(Hkv, L, d)), None, 0.25)
+        cum = O.accumulate(cum, r["probs"])
+    assert abs(cum.sum() - steps * Hq) < 1e-11
+
+
+def test_accumulate_decay_geometric_series():
+    Hq, Hkv, L, n, delta = 4, 2, 5, 9, 0.8
+    p = rng.random((Hq, L))
+    cum = np.zeros((Hkv, L))
+    for _ in range(n):
+        cum = O.accumulate(cum, p, decay=delta)
+    group = p.reshape(Hkv, 2, L).sum(axis=1)
+    np.testing.assert_allclose(cum, group * (1 - delta ** n) / (1 - delta), rtol=1e-13)
+
+
+# ---------------------------------------------------------- O3 block aggregate
+def test_block_aggregate_hand_example():
+    mx, mean = O.block_aggregate(np.array([[1.0, 2, 3, 4, 5, 99]]), 5, 2)
+    np.testing.assert_array_equal(mx, [[2, 4, 5]])
+    np.testing.assert_array_equal(mean, [[1.5, 3.5, 5]])
+
+
+@pytest.mark.parametrize("L,bs", [(1, 16), (16, 16), (17, 16), (100, 7), (528, 16), (255, 64)])
+def test_block_aggregate_against_masked_reshape(L, bs):
+    H = 3
+    x = rng.random((H, L + 5))
+    mx, mean = O.block_aggregate(x, L, bs)
+    n_blk = -(-L // bs)
+    pad = np.full((H, n_blk * bs), np.nan)
+    pad[:, :L] = x[:, :L]
+    r = pad.reshape(H, n_blk, bs)
+    np.testing.assert_array_equal(mx, np.nanmax(r, axis=2))
+    np.testing.assert_allclose(mean, np.nanmean(r, axis=2), rtol=1e-14)
+    assert (mx >= mean - 1e-15).all()
+    counts = np.minimum(bs, L - np.arange(n_blk) * bs)
+    assert abs((mean * counts).sum() - x[:, :L].sum()) < 1e-10
+
+
+# ----------------------------------------------------------------- O4 select
+def _brute_keep(sc, n, s, w, budget):
+    """Independent definition: a middle item is a heavy hitter iff fewer than
+    k middle items beat it (higher score, or equal score and lower index)."""
+    if budget >= n:
+        return list(range(n))
+    forced = [j for j in range(n) if j < s or j >= n - w]
+    k = max(0, budget - len(forced))
+    mid = [j for j in range(n) if j not in forced]
+    keep = set(forced)
+    for j in mid:
+        beat = sum(1 for i in mid if sc[i] > sc[j] or (sc[i] == sc[j] and i < j))
+        if beat < k:
+            keep.add(j)
+    return sorted(keep)
+
+
+def test_select_hand_example_h2o():
+    sc = np.array([5.0, 1, 9, 2, 8, 3, 7, 4])
+    # sinks {0}, window {6,7}, heavy hitters = 2 best of positions 1..5 -> 2, 4
+    assert O.select_keep(sc, 8, 1, 2, 5).tolist() == [0, 2, 4, 6, 7]
+
+
+def test_select_budget_at_least_n_keeps_all():
+    sc = rng.random(50)
+    for b in (50, 51, 1000):
+        assert O.select_keep(sc, 50, 4, 8, b).tolist() == list(range(50))
+
+
+def test_select_streaming_and_recent_sets_exact():
+    n, budget = 300, 256
+    sc = rng.random(n)
+    got = O.select_keep(sc, n, 4, budget - 4, budget)
+    assert got.tolist() == list(range(4)) + list(range(n - 252, n))
+    assert O.streaming_keep(n, budget).tolist() == got.tolist()
+    got = O.select_keep(sc, n, 0, budget, budget)
+    assert got.tolist() == list(range(n - budget, n)) == O.recent_keep(n, budget).tolist()
+    assert O.streaming_keep(200, 256).tolist() == list(range(200))
+
+
+def test_select_against_brute_force_with_ties():
+    for trial in range(300):
+        n = int(rng.integers(1, 25))
+        sc = rng.integers(0, 4, size=n).astype(float)        # many ties
+        if trial % 3 == 0:
+            sc[sc == 0] = -0.0                                  # -0 equals +0
+        s, w = int(rng.integers(0, 5)), int(rng.integers(0, 5))
+        budget = int(rng.integers(0, n + 3))
+        got = O.select_keep(sc, n, s, w, budget).tolist()
+        assert got == _brute_keep(sc, n, s, w, budget), (sc, s, w, budget)
+        if budget < n:
+            forced = len(set(range(min(s, n))) | set(range(max(n - w, 0), n)))
+            assert len(got) == max(budget, forced)
+
+
+def test_select_neg_inf_is_lowest():
+    sc = np.array([-np.inf, 1.0, -np.inf, 0.5])
+    assert O.select_keep(sc, 4, 0, 0, 2).tolist() == [1, 3]
+    assert O.select_keep(sc, 4, 0, 0, 3).tolist() == [0, 1, 3]
+
+
+# ------------------------------------------------------- O5 global percentile
+def test_percentile_hand_example():
+    keys = O.percentile_keys(np.array([0.3, 0.1, 0.3, 0.2]), 4)
+    assert keys == [Fraction(4, 4), Fraction(1, 4), Fraction(3, 4), Fraction(2, 4)]
+
+
+def test_global_percentile_brute_force():
+    for _ in range(60):
+        R = int(rng.integers(1, 5))
+        lens = [int(rng.integers(1, 9)) for _ in range(R)]
+        rows = [rng.integers(0, 3, size=n).astype(float) for n in lens]
+        K = int(rng.integers(0, sum(lens) + 2))
+        got = O.global_percentile_select(rows, lens, K)
+        cand = []
+        for r, n in enumerate(lens):
+            for j in range(n):
+                below = sum(1 for i in range(n)
+                            if rows[r][i] < rows[r][j] or (rows[r][i] == rows[r][j] and i > j))
+                cand.append((Fraction(below + 1, n), r, j))
+        want = [[] for _ in lens]
+        for key, r, j in cand:
+            better = sum(1 for k2, r2, j2 in cand
+                         if k2 > key or (k2 == key and (r2, j2) < (r, j)))
+            if better < K:
+                want[r].append(j)
+        assert [g.tolist() for g in got] == [sorted(w) for w in want]
+
+
+def test_global_percentile_equal_lengths_is_per_row_topk():
+    R, n, frac = 8, 512, 0.25
+    rows = [rng.random(n) for _ in range(R)]
+    got = O.global_percentile_select(rows, [n] * R, int(frac * R * n))
+    for r in range(R):
+        assert got[r].tolist() == O.select_keep(rows[r], n, 0, 0, int(frac * n)).tolist()
+
+
+# ---------------------------------------------------------------- O6 SnapKV
+@pytest.mark.parametrize("k", [1, 3, 7, 9])
+def test_max_pool_matches_scipy(k):
+    x = rng.normal(size=57)
+    want = scipy.ndimage.maximum_filter1d(x, size=k, mode="constant", cval=-np.inf)
+    np.testing.assert_array_equal(O.max_pool_1d(x, k), want)
+
+
+def test_snapkv_window_one_equals_decode_probs():
+    Hq, Hkv, L, d = 4, 2, 64, 16
+    K = rng.normal(size=(Hkv, L, d)); q = rng.normal(size=(Hq, 1, d))
+    v = O.snapkv_vote(q, K, 0.25, 1, group_sum=False)
+    r = O.decode_attention(q[:, 0], K, None, 0.25)
+    np.testing.assert_allclose(v, r["probs"][:, :L - 1], rtol=1e-13)
+
+
+def test_snapkv_two_window_rows_are_causal():
+    Hq, Hkv, L, d = 2, 1, 40, 8
+    K = rng.normal(size=(Hkv, L, d)); q = rng.normal(size=(Hq, 2, d))
+    v = O.snapkv_vote(q, K, 0.5, 1, group_sum=False)
+    a = O.decode_attention(q[:, 0], K[:, :L - 1], None, 0.5)["probs"][:, :L - 2]
+    b = O.decode_attention(q[:, 1], K, None, 0.5)["probs"][:, :L - 2]
+    np.testing.assert_allclose(v, a + b, rtol=1e-13)
+
+
+def test_snapkv_votes_sum_to_window_when_window_keys_are_cold():
+    Hq, Hkv, L, W, d = 4, 2, 80, 8, 16
+    q0 = rng.normal(size=d)
+    q = np.broadcast_to(q0, (Hq, W, d)).copy()
+    K = rng.normal(size=(Hkv, L, d)) * 0.1
+    K[:, L - W:] = -40.0 * q0 / np.linalg.norm(q0)        # window keys get ~zero mass
+    per_head = O.snapkv_vote(q, K, 1.0, 1, group_sum=False)
+    np.testing.assert_allclose(per_head.sum(axis=1), W, rtol=1e-9)
+    grouped = O.snapkv_vote(q, K, 1.0, 1, group_sum=True)
+    np.testing.assert_allclose(grouped, per_head.reshape(Hkv, 2, -1).sum(axis=1), rtol=1e-13)
+    pooled = O.snapkv_vote(q, K, 1.0, 7, group_sum=True)
+    np.testing.assert_array_equal(
+        pooled, scipy.ndimage.maximum_filter1d(grouped, size=7, axis=1, mode="constant", cval=-np.inf))
+
+
+def test_snapkv_keep_is_topk_plus_window():
+    vote = rng.random(100)
+    keep = O.snapkv_keep(vote, 110, 10, 5)
+    top5 = np.argsort(-vote, kind="stable")[:5]
+    assert keep.tolist() == sorted(top5.tolist()) + list(range(100, 110))
+
+
+# --------------------------------------------------------------- O7 indexer
+def test_indexer_brute_force():
+    H, L, dI = 3, 11, 5
+    q = rng.normal(size=(H, dI)); K = rng.normal(size=(L, dI))
+    s = O.indexer_scores(q, K)
+    for h in range(H):
+        for j in range(L):
+            assert abs(s[h, j] - sum(q[h, t] * K[j, t] for t in range(dI))) < 1e-12
+
+
+# ---------------------------------------------------------------- O8 sparse
+def test_sparse_full_set_equals_dense():
+    Hq, Hkv, L, d = 8, 2, 90, 32
+    q = rng.normal(size=(Hq, d)); K = rng.normal(size=(Hkv, L, d)); V = rng.normal(size=(Hkv, L, d))
+    dense = O.decode_attention(q, K, V, 0.2)
+    sets = [rng.permutation(L) for _ in range(Hq)]
+    out, probs = O.sparse_attention(q, K, V, sets, 0.2)
+    np.testing.assert_allclose(out, dense["out"], rtol=1e-12, atol=1e-14)
+    for h in range(Hq):
+        np.testing.assert_allclose(probs[h], dense["probs"][h][sets[h]], rtol=1e-12)
+
+
+def test_sparse_single_key_and_padding():
+    Hq, Hkv, L, d = 2, 1, 30, 8
+    q = rng.normal(size=(Hq, d)); K = rng.normal(size=(Hkv, L, d)); V = rng.normal(size=(Hkv, L, d))
+    out, probs = O.sparse_attention(q, K, V, [[-1, 7, -1], [3]], 0.3)
+    np.testing.assert_array_equal(out[0], V[0, 7])
+    np.testing.assert_array_equal(out[1], V[0, 3])
+    assert probs[0].tolist() == [0.0, 1.0, 0.0]
+
+
+def test_relative_error_values():
+    assert O.relative_error(np.array([1.0, 1.0]), np.array([1.0, 0.0])) == 1.0
+    assert O.relative_error(np.array([3.0, 4.0]), np.array([3.0, 4.0])) == 0.0
+
+
+# ------------------------------------------------- sparse-comparison index sets
+def test_window_index_sets_hand():
+    assert O.window_index_set(10, 4).tolist() == [7, 8, 9, 10]
+    assert O.window_index_set(2, 4).tolist() == [0, 1, 2]
+    assert O.sink_window_index_set(20, 8, 4).tolist() == [0, 1, 2, 3, 17, 18, 19, 20]
+    assert O.sink_window_index_set(5, 8, 4).tolist() == [0, 1, 2, 3, 4, 5]
+
+
+def test_quest_picks_the_page_of_a_dominant_key_and_keeps_the_tail():
+    L, d, page = 70, 8, 16
+    q = rng.normal(size=d)
+    K = rng.normal(size=(L, d)) * 0.01
+    K[37] = 50 * q                          # page 2 holds the dominant key
+    sel = O.quest_page_selection(q, K, 69, 16, page)
+    assert sel.tolist() == list(range(32, 48)) + list(range(64, 70))
+    sel = O.quest_page_selection(q, K, 40, 16, page)     # causal cut at 40
+    assert sel.tolist() == list(range(32, 41))
+    # the bound dominates every key's score of the page
+    for pg in range(L // page):
+        blk = K[pg * page:(pg + 1) * page]
+        bound = np.maximum(q * blk.min(0), q * blk.max(0)).sum()
+        assert (blk @ q <= bound + 1e-12).all()
+
+
+# ------------------------------------------------------------ chunk attention
+def test_chunk_causal_attention_rows():
+    Hq, Hkv, S, n, d = 4, 2, 10, 5, 8
+    qc = rng.normal(size=(Hq, n, d))
+    Kc, Vc = rng.normal(size=(Hkv, S, d)), rng.normal(size=(Hkv, S, d))
+    Kn, Vn = rng.normal(size=(Hkv, n, d)), rng.normal(size=(Hkv, n, d))
+    out, probs = O.chunk_causal_attention(qc, Kc, Vc, Kn, Vn, 0.3)
+    assert [p.shape[1] for p in probs] == [S + i + 1 for i in range(n)]
+    full = O.decode_attention(qc[:, n - 1], np.concatenate([Kc, Kn], 1), np.concatenate([Vc, Vn], 1), 0.3)
+    np.testing.assert_allclose(out[n - 1], full["out"], rtol=1e-13)
+    first = O.decode_attention(qc[:, 0], np.concatenate([Kc, Kn[:, :1]], 1),
+                               np.concatenate([Vc, Vn[:, :1]], 1), 0.3)
+    np.testing.assert_allclose(out[0], first["out"], rtol=1e-13)
+
+
+# ------------------------------------------------------------ printed values
+def test_cost_model_reproduces_printed_values():
+    g = json.load(open(os.path.join(GOLDEN, "longctx_cost_model.json")))
+    for m in g["models"]:
+        cross = O.attention_linear_crossover(m["params"], m["layers"], m["heads"], m["head_dim"])
+        assert round(cross / 1000) == m["crossover_k"]
+        kv = O.kv_bytes_per_token(m["layers"], m["kv_heads"], m["head_dim"]) * 131072 / 1e9
+        assert round(kv, 1) == m["kv_128k_gb"]
+        # at the crossover, attention FLOPs per token equal 2*params
+        fl = O.attention_flops_per_token(cross, m["layers"], m["heads"], m["head_dim"])
+        assert abs(fl - 2 * m["params"]) < 1e-3 * m["params"]
+
+
+def test_decode_read_estimate_of_offloading_page():
+    g = json.load(open(os.path.join(GOLDEN, "offload_decode_read.json")))
+    m = g["model"]
+    gb = O.kv_bytes_per_token(m["layers"], m["kv_heads"], m["head_dim"], m["bytes_per_elt"]) * g["context"] / 1e9
+    assert abs(gb - g["kv_read_gb_approx"]) / g["kv_read_gb_approx"] < 0.1
+    ms = gb / g["hbm_tb_per_s"]
+    assert abs(ms - g["time_ms_approx"]) / g["time_ms_approx"] < 0.1
