@@ -1,0 +1,13 @@
+"""MI355X-native score-guided KV selection (library ``libkvsel.so``).
+
+The C ABI lives in ``include/kvsel.h``; this package is its Python binding
+(``_lib``) plus the in-tree build script (``build``).  Importing it loads the
+built library and fails loudly when it is missing.
+"""
+from ._lib import (  # noqa: F401
+    EMIT_LOGITS, EMIT_PROBS, EXPORTED, KVSEL_BF16, KVSEL_ERR_HIP, KVSEL_ERR_INVALID,
+    KVSEL_ERR_UNSUPPORTED, KVSEL_ERR_WORKSPACE, KVSEL_F32, KVSEL_OK, REDUCE_NONE, REDUCE_SUM,
+    SELECT_GLOBAL_PERCENTILE, SELECT_ROWS, KvselError, PagedKV, PagedKVDesc, accumulate,
+    block_aggregate, decode_attn_scores, decode_workspace_bytes, library, select_keep,
+    select_workspace_bytes, snapkv_vote, snapkv_workspace_bytes, sparse_attn,
+)

@@ -1,0 +1,243 @@
+"""ctypes binding of libkvsel.so.
+
+Argument marshalling only: every function checks that the tensors it is
+handed have the dtype, device and layout the C ABI documents, passes their
+device pointers and the current HIP stream, and turns a non-zero status into
+an exception.  Every step of the computation runs in the library's HIP
+kernels; there is no fallback.  The library must have been built
+(``python attention_score_guided_amd/build.py``): importing this module
+without it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvsel.so")
+
+KVSEL_OK, KVSEL_ERR_INVALID, KVSEL_ERR_UNSUPPORTED, KVSEL_ERR_WORKSPACE, KVSEL_ERR_HIP = 0, -1, -2, -3, -4
+KVSEL_F32, KVSEL_BF16 = 0, 1
+EMIT_PROBS, EMIT_LOGITS = 0, 1
+REDUCE_NONE, REDUCE_SUM = 0, 1
+SELECT_ROWS, SELECT_GLOBAL_PERCENTILE = 0, 1
+
+# Every symbol include/kvsel.h declares.
+EXPORTED = (
+    "kvsel_decode_attn_scores", "kvsel_decode_workspace_bytes", "kvsel_accumulate",
+    "kvsel_block_aggregate", "kvsel_select_keep", "kvsel_select_workspace_bytes",
+    "kvsel_snapkv_vote", "kvsel_snapkv_workspace_bytes", "kvsel_sparse_attn",
+    "kvsel_status_string", "kvsel_last_error",
+)
+
+
+class KvselError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+class PagedKVDesc(ctypes.Structure):
+    _fields_ = [
+        ("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("num_seqs", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python attention_score_guided_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    D = ctypes.POINTER(PagedKVDesc)
+    sig = {
+        "kvsel_decode_attn_scores": (ctypes.c_int, [D, P, I32, F, P, P, P, I64, I32, P, I64, F, P, SZ, P]),
+        "kvsel_decode_workspace_bytes": (SZ, [D, I32, I32]),
+        "kvsel_accumulate": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, F, P, I64, P]),
+        "kvsel_block_aggregate": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, I32, I32, P, P, I64, P]),
+        "kvsel_select_keep": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, P, I32, I32, I32, P, I64, P, P, SZ, P]),
+        "kvsel_select_workspace_bytes": (SZ, [I32, I32, I32]),
+        "kvsel_snapkv_vote": (ctypes.c_int, [D, P, I32, I32, I32, F, I32, P, I64, P, SZ, P]),
+        "kvsel_snapkv_workspace_bytes": (SZ, [D, I32, I32]),
+        "kvsel_sparse_attn": (ctypes.c_int, [D, P, I32, P, I64, P, I32, I32, F, P, P, P]),
+        "kvsel_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "kvsel_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+_LIB = _load()
+
+
+def library() -> ctypes.CDLL:
+    return _LIB
+
+
+def _status_name(status: int) -> str:
+    return _LIB.kvsel_status_string(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != KVSEL_OK:
+        raise KvselError(status, _LIB.kvsel_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name: str = "tensor") -> Optional[int]:
+    if t is None:
+        return None
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KVSEL_BF16
+    if t.dtype == torch.float32:
+        return KVSEL_F32
+    raise TypeError(f"KV dtype must be bfloat16 or float32, got {t.dtype}")
+
+
+class PagedKV:
+    """Descriptor of one layer's paged cache, holding references to its
+    tensors: pages ``[num_pages][H_kv][P][d]``, block table
+    ``[B][max_pages]`` int32, lengths ``[B]`` int32."""
+
+    def __init__(self, k_pages: torch.Tensor, v_pages: Optional[torch.Tensor], block_table: torch.Tensor,
+                 seq_lens: torch.Tensor, page_size: int, max_seq_len: int):
+        self.k_pages, self.v_pages, self.block_table, self.seq_lens = k_pages, v_pages, block_table, seq_lens
+        if v_pages is not None and v_pages.dtype != k_pages.dtype:
+            raise TypeError("k_pages and v_pages must share a dtype")
+        if k_pages.dim() != 4 or k_pages.shape[2] != page_size:
+            raise ValueError("k_pages must be [num_pages][H_kv][page_size][head_dim]")
+        self.desc = PagedKVDesc(
+            _ptr(k_pages, None, "k_pages"), _ptr(v_pages, None, "v_pages"),
+            _ptr(block_table, torch.int32, "block_table"), _ptr(seq_lens, torch.int32, "seq_lens"),
+            int(block_table.shape[0]), int(k_pages.shape[1]), int(k_pages.shape[3]), int(page_size),
+            int(block_table.shape[1]), int(max_seq_len), _dtype_code(k_pages))
+
+    @property
+    def dtype(self):
+        return self.k_pages.dtype
+
+    def ref(self):
+        return ctypes.byref(self.desc)
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    if workspace is None:
+        workspace = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+# --------------------------------------------------------------------------
+def decode_workspace_bytes(kv: PagedKV, num_q_heads: int, probs_given: bool) -> int:
+    return int(_LIB.kvsel_decode_workspace_bytes(kv.ref(), num_q_heads, int(bool(probs_given))))
+
+
+def decode_attn_scores(kv: PagedKV, q: torch.Tensor, num_q_heads: int, scale: float,
+                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                       probs: Optional[torch.Tensor] = None, emit: int = EMIT_PROBS,
+                       cum: Optional[torch.Tensor] = None, decay: float = 1.0,
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """kvsel_decode_attn_scores (see include/kvsel.h)."""
+    if q.dtype != kv.dtype:
+        raise TypeError("q must have the cache dtype")
+    ws, wsb = _workspace(decode_workspace_bytes(kv, num_q_heads, probs is not None or cum is None),
+                         q.device, workspace)
+    _check(_LIB.kvsel_decode_attn_scores(
+        kv.ref(), _ptr(q, None, "q"), num_q_heads, float(scale),
+        _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"),
+        _ptr(probs, torch.float32, "probs"), 0 if probs is None else probs.shape[-1], int(emit),
+        _ptr(cum, torch.float32, "cum"), 0 if cum is None else cum.shape[-1], float(decay),
+        _ptr(ws, None, "workspace"), wsb, _stream(stream)))
+
+
+def accumulate(probs: torch.Tensor, seq_lens: torch.Tensor, num_kv_heads: int, max_seq_len: int,
+               cum: torch.Tensor, decay: float = 1.0, stream=None) -> None:
+    """kvsel_accumulate: probs ``[B][H_q][stride]``, cum ``[B][H_kv][stride]``."""
+    B, Hq, _ = probs.shape
+    _check(_LIB.kvsel_accumulate(
+        _ptr(probs, torch.float32, "probs"), probs.shape[-1], _ptr(seq_lens, torch.int32, "seq_lens"),
+        B, Hq, num_kv_heads, max_seq_len, float(decay), _ptr(cum, torch.float32, "cum"),
+        cum.shape[-1], _stream(stream)))
+
+
+def block_aggregate(scores: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, block_size: int,
+                    head_reduce: int = REDUCE_NONE, accumulate: bool = False,
+                    out_max: Optional[torch.Tensor] = None, out_mean: Optional[torch.Tensor] = None,
+                    stream=None) -> None:
+    """kvsel_block_aggregate: scores ``[B][H][stride]``; outputs
+    ``[B][H][out_stride]`` (NONE) or ``[B][out_stride]`` (SUM)."""
+    B, H, _ = scores.shape
+    ref = out_max if out_max is not None else out_mean
+    _check(_LIB.kvsel_block_aggregate(
+        _ptr(scores, torch.float32, "scores"), scores.shape[-1], _ptr(seq_lens, torch.int32, "seq_lens"),
+        B, H, max_seq_len, block_size, int(head_reduce), int(bool(accumulate)),
+        _ptr(out_max, torch.float32, "out_max"), _ptr(out_mean, torch.float32, "out_mean"),
+        0 if ref is None else ref.shape[-1], _stream(stream)))
+
+
+def select_workspace_bytes(rows: int, max_len: int, mode: int) -> int:
+    return int(_LIB.kvsel_select_workspace_bytes(rows, max_len, mode))
+
+
+def select_keep(scores: torch.Tensor, lengths: torch.Tensor, max_len: int, sinks: int, window: int,
+                budgets: Optional[torch.Tensor], max_budget: int, out_idx: torch.Tensor,
+                out_count: torch.Tensor, mode: int = SELECT_ROWS, global_budget: int = 0,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """kvsel_select_keep: scores ``[rows][stride]`` -> out_idx ``[rows][out_stride]``."""
+    rows = scores.shape[0]
+    ws, wsb = _workspace(select_workspace_bytes(rows, max_len, mode), scores.device, workspace)
+    _check(_LIB.kvsel_select_keep(
+        _ptr(scores, torch.float32, "scores"), scores.shape[-1], _ptr(lengths, torch.int32, "lengths"),
+        rows, max_len, sinks, window, _ptr(budgets, torch.int32, "budgets"), max_budget, int(mode),
+        int(global_budget), _ptr(out_idx, torch.int32, "out_idx"), out_idx.shape[-1],
+        _ptr(out_count, torch.int32, "out_count"), _ptr(ws, None, "workspace"), wsb, _stream(stream)))
+
+
+def snapkv_workspace_bytes(kv: PagedKV, num_q_heads: int, window: int) -> int:
+    return int(_LIB.kvsel_snapkv_workspace_bytes(kv.ref(), num_q_heads, window))
+
+
+def snapkv_vote(kv: PagedKV, q_win: torch.Tensor, num_q_heads: int, window: int, pool_kernel: int,
+                scale: float, group_reduce: int, votes: torch.Tensor,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """kvsel_snapkv_vote: q_win ``[B][H_q][W][d]`` -> votes ``[B][H][stride]``."""
+    ws, wsb = _workspace(snapkv_workspace_bytes(kv, num_q_heads, window), q_win.device, workspace)
+    _check(_LIB.kvsel_snapkv_vote(
+        kv.ref(), _ptr(q_win, None, "q_win"), num_q_heads, window, pool_kernel, float(scale),
+        int(group_reduce), _ptr(votes, torch.float32, "votes"), votes.shape[-1],
+        _ptr(ws, None, "workspace"), wsb, _stream(stream)))
+
+
+def sparse_attn(kv: PagedKV, q: torch.Tensor, num_q_heads: int, indices: torch.Tensor,
+                counts: torch.Tensor, max_count: int, scale: float, out: torch.Tensor,
+                probs: Optional[torch.Tensor] = None, stream=None) -> None:
+    """kvsel_sparse_attn: indices ``[B][idx_heads][stride]``, counts ``[B][idx_heads]``."""
+    _check(_LIB.kvsel_sparse_attn(
+        kv.ref(), _ptr(q, None, "q"), num_q_heads, _ptr(indices, torch.int32, "indices"),
+        indices.shape[-1], _ptr(counts, torch.int32, "counts"), int(indices.shape[1]), max_count,
+        float(scale), _ptr(out, torch.float32, "out"), _ptr(probs, torch.float32, "probs"),
+        _stream(stream)))

@@ -1,0 +1,75 @@
+// Device helpers shared by the kvsel HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvsel {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+typedef short short2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---- bf16 <-> f32 --------------------------------------------------------
+// A 32-bit word holding two bf16 values (element 0 in the low half).
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Exact products of two bf16 pairs accumulated in fp32 (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// ---- transcendental ------------------------------------------------------
+// 2^x on the hardware exp unit; callers pre-multiply natural-log arguments by
+// log2(e).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// ---- cross-lane reductions (DPP within 16-lane rows) ----------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// DPP controls (gfx9 encoding)
+constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7-i within each half row
+constexpr int kRowMirror = 0x140;      // lane i <-> 15-i within each row
+
+// All-reduce (sum) over aligned groups of N lanes, N in {1,2,4,8,16,32,64};
+// every lane of the group ends with the group total.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp<kQuadXor1>(v);
+  if constexpr (N >= 4) v += dpp<kQuadXor2>(v);
+  if constexpr (N >= 8) v += dpp<kRowHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp<kRowMirror>(v);
+  if constexpr (N >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (N >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (N >= 2) v = fmaxf(v, dpp<kQuadXor1>(v));
+  if constexpr (N >= 4) v = fmaxf(v, dpp<kQuadXor2>(v));
+  if constexpr (N >= 8) v = fmaxf(v, dpp<kRowHalfMirror>(v));
+  if constexpr (N >= 16) v = fmaxf(v, dpp<kRowMirror>(v));
+  if constexpr (N >= 32) v = fmaxf(v, __shfl_xor(v, 16, 64));
+  if constexpr (N >= 64) v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
+__device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
+
+// 16-byte global load/store.
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+}  // namespace kvsel

@@ -1,0 +1,208 @@
+// C ABI of libkvsel.so: argument validation (before any HIP call), workspace
+// sizing, device check and dispatch to the HIP launchers.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/kvsel.h"
+#include "kvsel_internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return KVSEL_OK;
+}
+
+bool is_pow2(long long x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// 0 = unknown, 1 = gfx950, -1 = other.  Indexed by device ordinal.
+std::atomic<int> g_arch_ok[64];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(KVSEL_ERR_UNSUPPORTED, "no HIP device");
+  if (dev < 0 || dev >= 64) return fail(KVSEL_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+  int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+      return fail(KVSEL_ERR_UNSUPPORTED, "cannot query device %d", dev);
+    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_arch_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  if (st != 1) return fail(KVSEL_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return KVSEL_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(KVSEL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Validation of a paged-KV descriptor shared by every call that reads one.
+int check_kv(const kvsel_paged_kv* kv, int32_t num_q_heads, bool need_v) {
+  if (!kv) return fail(KVSEL_ERR_INVALID, "kv descriptor is NULL");
+  if (!kv->k_pages || !kv->block_table || !kv->seq_lens)
+    return fail(KVSEL_ERR_INVALID, "k_pages, block_table and seq_lens are required");
+  if (need_v && !kv->v_pages) return fail(KVSEL_ERR_INVALID, "v_pages is required for out");
+  if (kv->num_seqs <= 0 || kv->num_kv_heads <= 0 || num_q_heads <= 0 || kv->head_dim <= 0 ||
+      kv->page_size <= 0 || kv->max_pages_per_seq <= 0 || kv->max_seq_len <= 0)
+    return fail(KVSEL_ERR_INVALID, "dimensions must be positive");
+  if (num_q_heads % kv->num_kv_heads != 0)
+    return fail(KVSEL_ERR_INVALID, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads,
+                kv->num_kv_heads);
+  if ((long long)kv->max_pages_per_seq * kv->page_size < kv->max_seq_len)
+    return fail(KVSEL_ERR_INVALID, "max_pages_per_seq * page_size < max_seq_len");
+  if (kv->head_dim != 64 && kv->head_dim != 128)
+    return fail(KVSEL_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", kv->head_dim);
+  if (kv->dtype != KVSEL_F32 && kv->dtype != KVSEL_BF16)
+    return fail(KVSEL_ERR_UNSUPPORTED, "dtype %d", kv->dtype);
+  if (!is_pow2(kv->page_size) || kv->page_size < 16 || kv->page_size > 256)
+    return fail(KVSEL_ERR_UNSUPPORTED, "page_size %d (power of two in [16, 256])", kv->page_size);
+  return KVSEL_OK;
+}
+
+bool group_supported(int g) { return (g <= 8 && is_pow2(g)) || (g > 8 && g % 8 == 0); }
+
+}  // namespace
+
+extern "C" {
+
+const char* kvsel_status_string(int status) {
+  switch (status) {
+    case KVSEL_OK: return "KVSEL_OK";
+    case KVSEL_ERR_INVALID: return "KVSEL_ERR_INVALID";
+    case KVSEL_ERR_UNSUPPORTED: return "KVSEL_ERR_UNSUPPORTED";
+    case KVSEL_ERR_WORKSPACE: return "KVSEL_ERR_WORKSPACE";
+    case KVSEL_ERR_HIP: return "KVSEL_ERR_HIP";
+    default: return "KVSEL_UNKNOWN_STATUS";
+  }
+}
+
+const char* kvsel_last_error(void) { return g_last_error; }
+
+size_t kvsel_decode_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads,
+                                    int32_t probs_given) {
+  if (check_kv(kv, num_q_heads, false) != KVSEL_OK) return 0;
+  return kvsel::plan_decode(kv->num_seqs, kv->num_kv_heads, num_q_heads, kv->head_dim,
+                            kv->max_seq_len, probs_given == 0)
+      .total_bytes;
+}
+
+int kvsel_decode_attn_scores(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads,
+                             float scale, float* out, float* lse, float* probs,
+                             int64_t probs_stride, int32_t emit, float* cum, int64_t cum_stride,
+                             float decay, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_kv(kv, num_q_heads, out != nullptr);
+  if (st != KVSEL_OK) return st;
+  if (!q) return fail(KVSEL_ERR_INVALID, "q is NULL");
+  if (emit != KVSEL_EMIT_PROBS && emit != KVSEL_EMIT_LOGITS)
+    return fail(KVSEL_ERR_INVALID, "emit %d", emit);
+  if (probs && probs_stride < kv->max_seq_len)
+    return fail(KVSEL_ERR_INVALID, "probs_stride %lld < max_seq_len %d", (long long)probs_stride,
+                kv->max_seq_len);
+  if (cum && cum_stride < kv->max_seq_len)
+    return fail(KVSEL_ERR_INVALID, "cum_stride %lld < max_seq_len %d", (long long)cum_stride,
+                kv->max_seq_len);
+  if (emit == KVSEL_EMIT_LOGITS && cum)
+    return fail(KVSEL_ERR_UNSUPPORTED, "cum needs probabilities (emit = PROBS)");
+  if (!group_supported(num_q_heads / kv->num_kv_heads))
+    return fail(KVSEL_ERR_UNSUPPORTED, "group size %d (power of two <= 8 or multiple of 8)",
+                num_q_heads / kv->num_kv_heads);
+  // The logits scratch is needed only when probabilities are normalised
+  // for cum without a caller probs buffer.
+  const bool need_scratch = probs == nullptr && cum != nullptr;
+  const kvsel::DecodePlan plan = kvsel::plan_decode(kv->num_seqs, kv->num_kv_heads, num_q_heads,
+                                                    kv->head_dim, kv->max_seq_len, need_scratch);
+  if (!workspace || workspace_bytes < plan.total_bytes)
+    return fail(KVSEL_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes,
+                plan.total_bytes);
+  st = check_device();
+  if (st != KVSEL_OK) return st;
+  kvsel::DecodeArgs a{};
+  a.k_pages = kv->k_pages;
+  a.v_pages = kv->v_pages;
+  a.block_table = kv->block_table;
+  a.seq_lens = kv->seq_lens;
+  a.q = q;
+  a.num_seqs = kv->num_seqs;
+  a.num_kv_heads = kv->num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.head_dim = kv->head_dim;
+  a.page_size = kv->page_size;
+  a.max_pages = kv->max_pages_per_seq;
+  a.max_seq_len = kv->max_seq_len;
+  a.bf16 = kv->dtype == KVSEL_BF16;
+  a.scale = scale;
+  a.out = out;
+  a.lse = lse;
+  a.probs = probs;
+  a.probs_stride = probs_stride;
+  a.emit_logits = emit == KVSEL_EMIT_LOGITS;
+  a.cum = cum;
+  a.cum_stride = cum_stride;
+  a.decay = decay;
+  a.workspace = workspace;
+  return hip_status(kvsel::launch_decode(a, plan, static_cast<hipStream_t>(stream)),
+                    "decode_attn_scores launch");
+}
+
+int kvsel_accumulate(const float* probs, int64_t probs_stride, const int32_t* seq_lens,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t max_seq_len, float decay, float* cum, int64_t cum_stride,
+                     void* stream) {
+  if (!probs || !seq_lens || !cum) return fail(KVSEL_ERR_INVALID, "NULL pointer argument");
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len <= 0)
+    return fail(KVSEL_ERR_INVALID, "dimensions must be positive");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(KVSEL_ERR_INVALID, "num_q_heads is not a multiple of num_kv_heads");
+  if (probs_stride < max_seq_len || cum_stride < max_seq_len)
+    return fail(KVSEL_ERR_INVALID, "stride < max_seq_len");
+  int st = check_device();
+  if (st != KVSEL_OK) return st;
+  return hip_status(kvsel::launch_accumulate(probs, probs_stride, seq_lens, num_seqs, num_q_heads,
+                                             num_kv_heads, max_seq_len, decay, cum, cum_stride,
+                                             static_cast<hipStream_t>(stream)),
+                    "accumulate launch");
+}
+
+int kvsel_block_aggregate(const float* scores, int64_t score_stride, const int32_t* seq_lens,
+                          int32_t num_seqs, int32_t num_heads, int32_t max_seq_len,
+                          int32_t block_size, int32_t head_reduce, int32_t accumulate,
+                          float* out_max, float* out_mean, int64_t out_stride, void* stream) {
+  if (!scores || !seq_lens) return fail(KVSEL_ERR_INVALID, "NULL pointer argument");
+  if (!out_max && !out_mean) return fail(KVSEL_ERR_INVALID, "no output requested");
+  if (num_seqs <= 0 || num_heads <= 0 || max_seq_len <= 0 || block_size <= 0)
+    return fail(KVSEL_ERR_INVALID, "dimensions must be positive");
+  if (head_reduce != KVSEL_REDUCE_NONE && head_reduce != KVSEL_REDUCE_SUM)
+    return fail(KVSEL_ERR_INVALID, "head_reduce %d", head_reduce);
+  if (accumulate != 0 && accumulate != 1) return fail(KVSEL_ERR_INVALID, "accumulate %d", accumulate);
+  if (score_stride < max_seq_len) return fail(KVSEL_ERR_INVALID, "score_stride < max_seq_len");
+  const long long n_blk = ((long long)max_seq_len + block_size - 1) / block_size;
+  if (out_stride < n_blk)
+    return fail(KVSEL_ERR_INVALID, "out_stride %lld < %lld blocks", (long long)out_stride, n_blk);
+  int st = check_device();
+  if (st != KVSEL_OK) return st;
+  return hip_status(
+      kvsel::launch_block_aggregate(scores, score_stride, seq_lens, num_seqs, num_heads,
+                                    max_seq_len, block_size, head_reduce == KVSEL_REDUCE_SUM,
+                                    accumulate != 0, out_max, out_mean, out_stride,
+                                    static_cast<hipStream_t>(stream)),
+      "block_aggregate launch");
+}
+
+}  // extern "C"

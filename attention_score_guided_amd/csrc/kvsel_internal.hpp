@@ -1,0 +1,56 @@
+// Internal launch interface between the C ABI (kvsel_api.cpp) and the HIP
+// kernels.  All pointers are device pointers; all sizes were validated by the
+// caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvsel {
+
+// Split-K decode geometry shared by the launcher and the workspace query.
+struct DecodePlan {
+  int chunk;      // keys per split-K chunk (multiple of 64)
+  int n_chunks;   // ceil(max_seq_len / chunk)
+  int gt;         // query heads handled per workgroup (power of two <= 8)
+  int hgroups;    // G / gt
+  size_t part_o_bytes, part_ml_bytes, lse_bytes, scratch_bytes, total_bytes;
+};
+
+DecodePlan plan_decode(int num_seqs, int num_kv_heads, int num_q_heads, int head_dim,
+                       int max_seq_len, bool need_scratch);
+
+struct DecodeArgs {
+  const void* k_pages;
+  const void* v_pages;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const void* q;
+  int num_seqs, num_kv_heads, num_q_heads, head_dim, page_size, max_pages, max_seq_len;
+  bool bf16;
+  float scale;
+  float* out;
+  float* lse;
+  float* probs;
+  int64_t probs_stride;
+  bool emit_logits;
+  float* cum;
+  int64_t cum_stride;
+  float decay;
+  void* workspace;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
+
+hipError_t launch_accumulate(const float* probs, int64_t probs_stride, const int32_t* seq_lens,
+                             int num_seqs, int num_q_heads, int num_kv_heads, int max_seq_len,
+                             float decay, float* cum, int64_t cum_stride, hipStream_t stream);
+
+hipError_t launch_block_aggregate(const float* scores, int64_t score_stride,
+                                  const int32_t* seq_lens, int num_seqs, int num_heads,
+                                  int max_seq_len, int block_size, bool head_sum, bool accumulate,
+                                  float* out_max, float* out_mean, int64_t out_stride,
+                                  hipStream_t stream);
+
+}  // namespace kvsel

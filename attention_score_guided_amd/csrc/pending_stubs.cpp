@@ -1,0 +1,23 @@
+// Entry points declared in kvsel.h whose kernels are not in this build yet:
+// they validate nothing and return KVSEL_ERR_UNSUPPORTED.
+#include "../../include/kvsel.h"
+
+extern "C" {
+
+int kvsel_select_keep(const float*, int64_t, const int32_t*, int32_t, int32_t, int32_t, int32_t,
+                      const int32_t*, int32_t, int32_t, int32_t, int32_t*, int64_t, int32_t*, void*,
+                      size_t, void*) {
+  return KVSEL_ERR_UNSUPPORTED;
+}
+size_t kvsel_select_workspace_bytes(int32_t, int32_t, int32_t) { return 0; }
+int kvsel_snapkv_vote(const kvsel_paged_kv*, const void*, int32_t, int32_t, int32_t, float, int32_t,
+                      float*, int64_t, void*, size_t, void*) {
+  return KVSEL_ERR_UNSUPPORTED;
+}
+size_t kvsel_snapkv_workspace_bytes(const kvsel_paged_kv*, int32_t, int32_t) { return 0; }
+int kvsel_sparse_attn(const kvsel_paged_kv*, const void*, int32_t, const int32_t*, int64_t,
+                      const int32_t*, int32_t, int32_t, float, float*, float*, void*) {
+  return KVSEL_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,249 @@
+/*
+ * kvsel.h -- C ABI of the score-guided KV selection library (libkvsel.so).
+ *
+ * The library computes, on one AMD Instinct MI355X (gfx950), the hot path of
+ * attention-score-guided KV-cache management:
+ *   decode attention over a paged KV cache that also emits every key's softmax
+ *   probability -> H2O cumulative scores per KV head -> token-to-block
+ *   aggregation -> keep sets (sinks + heavy hitters + recent window), plus the
+ *   SnapKV observation-window vote and sparse attention over an index set.
+ *
+ * Sources, cited by title and section:
+ *   [OFFLOAD] "Sparse attention x KV-cache offloading: eight questions a
+ *             cross-layer design must answer"
+ *   [EVICT]   "KV-cache eviction strategies: from attention sinks to H2O and
+ *             SnapKV"
+ *   [LONGCTX] "Long context, KV eviction and sparse attention" (AI-infra
+ *             handbook, serving chapter)
+ *
+ * Conventions (every call):
+ *   - Tensor pointers are DEVICE pointers, allocated and owned by the caller.
+ *     The library allocates nothing, frees nothing and keeps no state besides
+ *     a per-device architecture check.  Scratch space is passed in as
+ *     `workspace` (device memory, size from the matching *_workspace_bytes).
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and returns a kvsel_status.  Nothing is synchronised inside.
+ *   - Host-visible arguments are validated before any HIP call; on error the
+ *     call returns KVSEL_ERR_INVALID / _UNSUPPORTED / _WORKSPACE, launches
+ *     nothing, and kvsel_last_error() (thread-local) says why.
+ *   - Device-resident values (seq_lens, block tables, indices, budgets) are
+ *     preconditions and are not read by the host: lengths must lie in
+ *     [1, max_seq_len], block-table entries must name pages of the pool,
+ *     indices must be < the row length.  Violating them is undefined.
+ *   - Results are bitwise reproducible for identical inputs (no float
+ *     atomics; every output element has exactly one writer).
+ *   - Strides are in elements.  Row-major layouts are spelled out per call.
+ *   - Query head h reads KV head h / G with G = num_q_heads / num_kv_heads
+ *     (grouped-query attention, repeat-interleaved KV heads as in [LONGCTX]
+ *     "sparse attention" experiment).
+ */
+#ifndef KVSEL_H
+#define KVSEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVSEL_OK = 0,
+  KVSEL_ERR_INVALID = -1,     /* an argument is out of its documented range  */
+  KVSEL_ERR_UNSUPPORTED = -2, /* valid, but not a shape/dtype this build runs */
+  KVSEL_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required  */
+  KVSEL_ERR_HIP = -4          /* a HIP runtime call or launch failed         */
+} kvsel_status;
+
+typedef enum { KVSEL_F32 = 0, KVSEL_BF16 = 1 } kvsel_dtype;
+typedef enum { KVSEL_EMIT_PROBS = 0, KVSEL_EMIT_LOGITS = 1 } kvsel_emit;
+typedef enum { KVSEL_REDUCE_NONE = 0, KVSEL_REDUCE_SUM = 1 } kvsel_reduce;
+typedef enum { KVSEL_SELECT_ROWS = 0, KVSEL_SELECT_GLOBAL_PERCENTILE = 1 } kvsel_select_mode;
+
+/* One layer's paged KV cache ([EVICT] prerequisites: PagedAttention block
+ * table).  Position j of sequence b lives in page block_table[b][j / page_size]
+ * at row j % page_size.  Each (page, kv head) tile of page_size x head_dim
+ * elements is contiguous. */
+typedef struct {
+  const void* k_pages;        /* [num_pages][num_kv_heads][page_size][head_dim] */
+  const void* v_pages;        /* same layout; NULL when no output is wanted     */
+  const int32_t* block_table; /* [num_seqs][max_pages_per_seq] page ids          */
+  const int32_t* seq_lens;    /* [num_seqs]; 1 <= L_b <= max_seq_len             */
+  int32_t num_seqs;
+  int32_t num_kv_heads;
+  int32_t head_dim;           /* 64 or 128                                       */
+  int32_t page_size;          /* power of two in [16, 256]                       */
+  int32_t max_pages_per_seq;  /* >= ceil(max_seq_len / page_size)                */
+  int32_t max_seq_len;        /* host-known bound on every L_b (grid sizing)     */
+  int32_t dtype;              /* kvsel_dtype of k_pages, v_pages and queries     */
+} kvsel_paged_kv;
+
+/* ------------------------------------------------------------------------
+ * Decode attention that emits per-key scores, with fused H2O accumulation.
+ *
+ * [OFFLOAD] §1.1 and §1.3: attention computes each key's importance every
+ * decode step and engines discard it; [EVICT] §4.2 (H2O): each step's
+ * attention weights are added to a per-position cumulative score.
+ *
+ * For sequence b, query head h (KV head c = h / G) and every key j < L_b:
+ *   s_j = scale * q[b][h] . k[c][j]
+ *   probs[b][h][j] = exp(s_j - lse[b][h])        (emit = KVSEL_EMIT_PROBS)
+ *   probs[b][h][j] = s_j                         (emit = KVSEL_EMIT_LOGITS)
+ *   out[b][h][:]   = sum_j softmax(s)_j v[c][j]
+ *   lse[b][h]      = ln sum_j exp(s_j)
+ *   cum[b][c][j]   = decay * cum[b][c][j] + sum_{h in group c} probs[b][h][j]
+ * The query is the current token; its key/value must already be appended,
+ * so the query sees L_b keys including its own.
+ *
+ *   q      [num_seqs][num_q_heads][head_dim], dtype kv->dtype.
+ *   out    [num_seqs][num_q_heads][head_dim] f32, or NULL.  Needs v_pages.
+ *   lse    [num_seqs][num_q_heads] f32, or NULL.
+ *   probs  [num_seqs][num_q_heads][probs_stride] f32, or NULL; entries at
+ *          j >= L_b are left untouched.  probs_stride >= max_seq_len.
+ *   cum    [num_seqs][num_kv_heads][cum_stride] f32, read and written, or
+ *          NULL.  Needs emit = PROBS.  cum_stride >= max_seq_len.
+ *   workspace: >= kvsel_decode_workspace_bytes(kv, num_q_heads,
+ *          probs != NULL || cum == NULL) bytes of device memory, 256-byte
+ *          aligned, contents ignored.
+ * Supported: head_dim 64/128; dtype F32/BF16; G a power of two <= 8 or a
+ * multiple of 8.  Errors: INVALID (NULL kv/q/k_pages/block_table/seq_lens,
+ * dims <= 0, num_q_heads % num_kv_heads != 0, stride < max_seq_len,
+ * out != NULL without v_pages, max_pages_per_seq too small), UNSUPPORTED
+ * (head_dim, dtype, page_size, G, cum with emit = LOGITS, no gfx950 device),
+ * WORKSPACE, HIP.
+ * ------------------------------------------------------------------------ */
+int kvsel_decode_attn_scores(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads,
+                             float scale, float* out, float* lse, float* probs,
+                             int64_t probs_stride, int32_t emit, float* cum, int64_t cum_stride,
+                             float decay, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for kvsel_decode_attn_scores (0 if the arguments are
+ * invalid).  probs_given = 0 adds the logits scratch needed when cum is
+ * fused without a caller probs buffer (an upper bound for every call). */
+size_t kvsel_decode_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads,
+                                    int32_t probs_given);
+
+/* ------------------------------------------------------------------------
+ * Standalone H2O accumulation ([EVICT] §4.2; decay < 1 is the exponential
+ * decay aggregation of [OFFLOAD] §2.1):
+ *   cum[b][c][j] = decay * cum[b][c][j] + sum_{h: h / G == c} probs[b][h][j],
+ * for j < seq_lens[b].  probs [num_seqs][num_q_heads][probs_stride] f32,
+ * cum [num_seqs][num_kv_heads][cum_stride] f32 (in place).  Errors: INVALID.
+ * ------------------------------------------------------------------------ */
+int kvsel_accumulate(const float* probs, int64_t probs_stride, const int32_t* seq_lens,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t max_seq_len, float decay, float* cum, int64_t cum_stride,
+                     void* stream);
+
+/* ------------------------------------------------------------------------
+ * Token-to-block aggregation ([OFFLOAD] §3.1: max keeps a block holding any
+ * key token, mean dilutes it).  Block n of row (b, h) covers positions
+ * [n*block_size, min((n+1)*block_size, L_b)); a partial last block aggregates
+ * its valid positions only (mean divides by their count).
+ *   scores   [num_seqs][num_heads][score_stride] f32.
+ *   head_reduce = NONE: out_* [num_seqs][num_heads][out_stride];
+ *   head_reduce = SUM:  out_* [num_seqs][out_stride], summed over heads (the
+ *                       one accumulator per block of [OFFLOAD] §5.1).
+ *   accumulate = 1 adds into out_* (e.g. a sum over layers); 0 overwrites.
+ * Blocks n >= ceil(L_b / block_size) are left untouched.  Either output may
+ * be NULL (not both).  out_stride >= ceil(max_seq_len / block_size).
+ * Errors: INVALID.
+ * ------------------------------------------------------------------------ */
+int kvsel_block_aggregate(const float* scores, int64_t score_stride, const int32_t* seq_lens,
+                          int32_t num_seqs, int32_t num_heads, int32_t max_seq_len,
+                          int32_t block_size, int32_t head_reduce, int32_t accumulate,
+                          float* out_max, float* out_mean, int64_t out_stride, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Keep-set selection.
+ *
+ * mode = ROWS ([EVICT] §4.2 H2O; §4.1 StreamingLLM is sinks = 4, window =
+ * budget - 4, and the sliding window is sinks = 0, window = budget): for row
+ * r of length n = lengths[r] and budget B_r (budgets[r], or max_budget when
+ * budgets is NULL):
+ *   if B_r >= n every position is kept; otherwise the forced positions
+ *   [0, min(sinks, n)) and [max(n - window, 0), n) are kept, plus the
+ *   max(0, B_r - |forced|) middle positions with the highest scores (equal
+ *   scores: lower position first; -0.0 equals +0.0; NaN is a precondition
+ *   violation; -inf ranks lowest).
+ * mode = GLOBAL_PERCENTILE ([OFFLOAD] §3.2): every position gets the
+ *   percentile (rank + 1) / n of its score within its own row (rank ascending,
+ *   equal scores: the lower position ranks higher); the global_budget
+ *   positions with the highest percentiles over all rows are kept (ties: lower
+ *   row, then lower position).  sinks and window must be 0.  Rows up to
+ *   1048576 positions.
+ * Output: out_idx[r][0 .. out_count[r]) holds the kept positions ascending;
+ *   the rest of the row is left untouched.
+ *   scores [rows][stride] f32, lengths [rows] i32 (1 <= n <= max_len),
+ *   out_idx [rows][out_stride] i32, out_count [rows] i32.
+ *   out_stride >= min(max_len, max(max_budget, sinks + window)) in ROWS mode
+ *   (budgets[r] <= max_budget is a precondition) and >= max_len in
+ *   GLOBAL_PERCENTILE mode.
+ *   workspace: >= kvsel_select_workspace_bytes(rows, max_len, mode).
+ * Errors: INVALID (NULL pointers, rows/max_len <= 0, stride < max_len,
+ * negative sinks/window/max_budget/global_budget, out_stride too small,
+ * GLOBAL with sinks or window), UNSUPPORTED, WORKSPACE, HIP.
+ * ------------------------------------------------------------------------ */
+int kvsel_select_keep(const float* scores, int64_t stride, const int32_t* lengths, int32_t rows,
+                      int32_t max_len, int32_t sinks, int32_t window, const int32_t* budgets,
+                      int32_t max_budget, int32_t mode, int32_t global_budget, int32_t* out_idx,
+                      int64_t out_stride, int32_t* out_count, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+size_t kvsel_select_workspace_bytes(int32_t rows, int32_t max_len, int32_t mode);
+
+/* ------------------------------------------------------------------------
+ * SnapKV observation-window vote ([EVICT] §4.3, steps 2-4).
+ * The `window` queries of each sequence sit at positions L_b - window + i,
+ * i < window, and each takes a causal softmax over keys 0 .. L_b - window + i.
+ * For prefix keys j < L_b - window:
+ *   vote_h[j] = sum_i softmax_i(j)              (sum pooling per query head)
+ *   group_reduce = SUM:  g = kv head, votes = sum of the group's vote_h
+ *   group_reduce = NONE: g = query head
+ *   votes[b][g][j] = max_{|t| <= pool_kernel/2, 0 <= j+t < L_b - window} vote[j+t]
+ *   q_win [num_seqs][num_q_heads][window][head_dim] (dtype kv->dtype),
+ *   votes [num_seqs][H_kv or H_q][votes_stride] f32; positions
+ *   j >= L_b - window are left untouched.  votes_stride >= max_seq_len.
+ * Precondition: window < L_b for every sequence.
+ * Errors: INVALID (window <= 0, window >= max_seq_len, even pool_kernel,
+ * ...), UNSUPPORTED (dtype other than BF16, head_dim other than 128 or 64),
+ * WORKSPACE, HIP.
+ * ------------------------------------------------------------------------ */
+int kvsel_snapkv_vote(const kvsel_paged_kv* kv, const void* q_win, int32_t num_q_heads,
+                      int32_t window, int32_t pool_kernel, float scale, int32_t group_reduce,
+                      float* votes, int64_t votes_stride, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+size_t kvsel_snapkv_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads, int32_t window);
+
+/* ------------------------------------------------------------------------
+ * Sparse attention over an index set ([LONGCTX] sparse-attention experiment:
+ * the softmax runs over the selected keys only; DeepSeek-style indexers pick
+ * 2048 keys per query).
+ * idx_heads = num_q_heads: one set per query head; idx_heads = num_kv_heads:
+ * one set shared by the query heads of a group.
+ *   indices [num_seqs][idx_heads][idx_stride] i32 logical positions < L_b,
+ *           distinct; entries < 0 are ignored; only the first
+ *           counts[b][g] entries of a row are read.
+ *   counts  [num_seqs][idx_heads] i32, 0 <= counts <= max_count <= idx_stride.
+ *   out     [num_seqs][num_q_heads][head_dim] f32 (all zero for an empty set).
+ *   probs   [num_seqs][num_q_heads][idx_stride] f32 or NULL: the probability of
+ *           each listed entry (0 for ignored entries).
+ * Errors: INVALID, UNSUPPORTED, HIP.
+ * ------------------------------------------------------------------------ */
+int kvsel_sparse_attn(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads,
+                      const int32_t* indices, int64_t idx_stride, const int32_t* counts,
+                      int32_t idx_heads, int32_t max_count, float scale, float* out,
+                      float* probs, void* stream);
+
+/* Name of a status code (static string). */
+const char* kvsel_status_string(int status);
+
+/* The message of the last failed call on this thread ("" if none). */
+const char* kvsel_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSEL_H */

@@ -1,0 +1,97 @@
+"""The C-ABI library loads, exports every declared symbol and rejects bad
+arguments before touching HIP.  CPU only: no call here launches a kernel."""
+import ctypes
+import re
+
+import pytest
+
+import attention_score_guided_amd as K
+from attention_score_guided_amd import _lib
+
+HEADER = "include/kvsel.h"
+
+
+def _declared_functions():
+    import os
+    src = open(os.path.join(os.path.dirname(__file__), "..", HEADER)).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvsel_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = K.library()
+    decl = _declared_functions()
+    assert len(decl) >= 11
+    for name in decl:
+        assert hasattr(lib, name), name
+    assert sorted(decl) == sorted(K.EXPORTED)
+
+
+def test_status_strings():
+    lib = K.library()
+    assert lib.kvsel_status_string(0) == b"KVSEL_OK"
+    assert lib.kvsel_status_string(-1) == b"KVSEL_ERR_INVALID"
+    assert lib.kvsel_status_string(-3) == b"KVSEL_ERR_WORKSPACE"
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _kv(**over):
+    d = dict(k_pages=FAKE, v_pages=FAKE, block_table=FAKE, seq_lens=FAKE, num_seqs=2, num_kv_heads=8,
+             head_dim=128, page_size=16, max_pages_per_seq=64, max_seq_len=1024, dtype=K.KVSEL_BF16)
+    d.update(over)
+    return K.PagedKVDesc(**d)
+
+
+def _decode(kv, hq=32, probs=FAKE, probs_stride=1024, emit=0, cum=None, cum_stride=1024, ws=FAKE,
+            wsb=1 << 30, out=FAKE, q=FAKE):
+    lib = K.library()
+    return lib.kvsel_decode_attn_scores(ctypes.byref(kv), q, hq, 0.1, out, None, probs, probs_stride,
+                                        emit, cum, cum_stride, 1.0, ws, wsb, None)
+
+
+@pytest.mark.parametrize("over,hq,kw,status", [
+    ({}, 32, dict(q=None), K.KVSEL_ERR_INVALID),
+    ({"k_pages": None}, 32, {}, K.KVSEL_ERR_INVALID),
+    ({"v_pages": None}, 32, {}, K.KVSEL_ERR_INVALID),          # out needs V
+    ({"num_seqs": 0}, 32, {}, K.KVSEL_ERR_INVALID),
+    ({}, 30, {}, K.KVSEL_ERR_INVALID),                           # 30 % 8 != 0
+    ({}, 32, dict(probs_stride=1000), K.KVSEL_ERR_INVALID),
+    ({}, 32, dict(cum=FAKE, cum_stride=10), K.KVSEL_ERR_INVALID),
+    ({"max_pages_per_seq": 10}, 32, {}, K.KVSEL_ERR_INVALID),
+    ({}, 32, dict(emit=7), K.KVSEL_ERR_INVALID),
+    ({"head_dim": 96}, 32, {}, K.KVSEL_ERR_UNSUPPORTED),
+    ({"dtype": 5}, 32, {}, K.KVSEL_ERR_UNSUPPORTED),
+    ({"page_size": 8, "max_pages_per_seq": 128}, 32, {}, K.KVSEL_ERR_UNSUPPORTED),
+    ({"page_size": 48}, 32, {}, K.KVSEL_ERR_UNSUPPORTED),
+    ({}, 32, dict(emit=1, cum=FAKE), K.KVSEL_ERR_UNSUPPORTED),   # cum needs probabilities
+    ({"num_kv_heads": 4}, 24, {}, K.KVSEL_ERR_UNSUPPORTED),      # G = 6
+    ({}, 32, dict(ws=None), K.KVSEL_ERR_WORKSPACE),
+    ({}, 32, dict(wsb=16), K.KVSEL_ERR_WORKSPACE),
+])
+def test_decode_validation(over, hq, kw, status):
+    assert _decode(_kv(**over), hq=hq, **kw) == status
+    assert K.library().kvsel_last_error() != b""
+
+
+def test_workspace_query():
+    lib = K.library()
+    kv = _kv()
+    a = lib.kvsel_decode_workspace_bytes(ctypes.byref(kv), 32, 1)
+    b = lib.kvsel_decode_workspace_bytes(ctypes.byref(kv), 32, 0)
+    assert a > 0 and b >= a + 2 * 32 * 1024 * 4
+    assert lib.kvsel_decode_workspace_bytes(ctypes.byref(_kv(head_dim=96)), 32, 1) == 0
+
+
+def test_accumulate_and_aggregate_validation():
+    lib = K.library()
+    assert lib.kvsel_accumulate(None, 8, FAKE, 1, 4, 1, 8, 1.0, FAKE, 8, None) == K.KVSEL_ERR_INVALID
+    assert lib.kvsel_accumulate(FAKE, 8, FAKE, 1, 6, 4, 8, 1.0, FAKE, 8, None) == K.KVSEL_ERR_INVALID
+    assert lib.kvsel_accumulate(FAKE, 4, FAKE, 1, 4, 1, 8, 1.0, FAKE, 8, None) == K.KVSEL_ERR_INVALID
+    agg = lib.kvsel_block_aggregate
+    assert agg(FAKE, 64, FAKE, 1, 1, 64, 16, 0, 0, None, None, 4, None) == K.KVSEL_ERR_INVALID
+    assert agg(FAKE, 64, FAKE, 1, 1, 64, 16, 0, 0, FAKE, None, 3, None) == K.KVSEL_ERR_INVALID
+    assert agg(FAKE, 64, FAKE, 1, 1, 64, 16, 2, 0, FAKE, None, 4, None) == K.KVSEL_ERR_INVALID
+    assert agg(FAKE, 63, FAKE, 1, 1, 64, 16, 0, 0, FAKE, None, 4, None) == K.KVSEL_ERR_INVALID
+    assert agg(FAKE, 64, FAKE, 1, 1, 64, 0, 0, 0, FAKE, None, 4, None) == K.KVSEL_ERR_INVALID
