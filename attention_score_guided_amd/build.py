@@ -36,30 +36,32 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, "-x", "hip", "-c", src, "-o", obj]
+def _compile(src: str, build_dir: str = BUILD_DIR, defines=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [_hipcc(), *COMMON, *[f"-D{d}" for d in defines], "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, out: str = OUT, build_dir: str = BUILD_DIR, defines=()) -> str:
+    """Compile every source and link ``out``.  ``defines`` are extra -D
+    tuning macros (the defaults in the sources are the shipped values)."""
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     jobs = min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = OUT + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, build_dir, defines), srcs))
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {OUT} from {len(srcs)} sources")
-    return OUT
+        print(f"built {out} from {len(srcs)} sources")
+    return out
 
 
 if __name__ == "__main__":

@@ -34,6 +34,37 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kUnroll = 4;
 
+// Tuning knobs (compile-time).
+#ifndef KVSEL_NT_KV
+#define KVSEL_NT_KV 1      // stream K/V with non-temporal loads
+#endif
+#ifndef KVSEL_MAX_CHUNK
+#define KVSEL_MAX_CHUNK 1024 // keys per split-K chunk (multiple of 64)
+#endif
+#ifndef KVSEL_MIN_WGS
+#define KVSEL_MIN_WGS 1024   // shrink the chunk until the grid has this many workgroups
+#endif
+#ifndef KVSEL_PV_VU
+#define KVSEL_PV_VU 8        // P.V value loads per lane per batch (double-buffered)
+#endif
+#ifndef KVSEL_QK_BATCH
+#define KVSEL_QK_BATCH 4     // >0: issue the K loads of this many tiles before their MFMAs
+#endif
+#ifndef KVSEL_WAVES_PER_EU
+#define KVSEL_WAVES_PER_EU 0 // >0: occupancy hint for the G=8 kernel
+#endif
+#ifndef KVSEL_NT_PROBS
+#define KVSEL_NT_PROBS 1   // write final probabilities with non-temporal stores
+#endif
+
+__device__ __forceinline__ uint4 ld_kv(const void* ptr) {
+#if KVSEL_NT_KV
+  return ld16_stream(ptr);
+#else
+  return ld16(ptr);
+#endif
+}
+
 struct PartialParams {
   const uint8_t* k_pages;
   const uint8_t* v_pages;
@@ -245,7 +276,251 @@ __global__ __launch_bounds__(kThreads) void decode_partial(PartialParams p) {
   }
 }
 
+// ---- bf16 partial pass with the QK^T tile on the matrix cores ---------------
+// One 16-key tile of one KV head against the (up to 16) query heads of its
+// group is the product K_tile (16 x d) . Q^T (d x 16): v_mfma_f32_16x16x32_bf16
+// with keys as rows and heads as columns.  bf16 x bf16 products are exact in
+// fp32, so the logits equal the VALU dot products up to summation order.
+// Every logit lands on exactly one lane (lane = head + 16 * (key / 4),
+// register = key % 4), so the softmax arithmetic is done once per (key, head).
+// P.V stays on the vector ALUs: lanes own 8 dims of a value row and read the
+// group's probabilities of that key from a key-major LDS tile.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kQkBatch = KVSEL_QK_BATCH > 0 ? KVSEL_QK_BATCH : 1;  // K tiles per load batch
+
+template <int D, int GT, bool HAS_V, bool WRITE_LOGITS>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(HAS_V ? (KVSEL_WAVES_PER_EU > 0 ? KVSEL_WAVES_PER_EU : 3) : 4)))
+void decode_partial_mfma(PartialParams p) {
+  constexpr int NU = D / 32;                 // MFMA k-steps (32 dims each)
+  constexpr int EPL = 8;                     // P.V: dims per lane
+  constexpr int LPK = D / EPL;               // P.V: lanes per value row
+  constexpr int KPW = kWave / LPK;           // P.V: keys per wave per load
+  constexpr int KPI = kWaves * KPW;          // P.V: keys per workgroup per load
+  constexpr int VU = KVSEL_PV_VU;            // P.V: loads per lane per batch
+  constexpr int QB = kQkBatch;
+
+  extern __shared__ float smem[];
+  const int C = p.chunk;
+  float* p_lds = smem;                               // [C][GT] logits, then exp(s - m)
+  float* red = smem + C * GT;                        // [kWaves][GT][D]
+  float* wstat = red + kWaves * GT * D;              // [2][kWaves][16]
+  float2* ml_lds = reinterpret_cast<float2*>(wstat + 2 * kWaves * 16);  // [GT]
+  int* page_lds = reinterpret_cast<int*>(ml_lds + GT);                  // [C/16 + 2]
+
+  const int chunk_id = blockIdx.x;
+  const int kvh = blockIdx.y / p.hgroups;
+  const int hg = blockIdx.y % p.hgroups;
+  const int b = blockIdx.z;
+  const int L = p.seq_lens[b];
+  const int start = chunk_id * C;
+  if (start >= L) return;
+  const int n_keys = min(C, L - start);
+  const int h0 = kvh * p.group + hg * GT;
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  const int col = lane & 15;   // A row (key slot) and B column (head slot)
+  const int grp = lane >> 4;   // k-group of the operands, row-quad of the result
+  const int P = 1 << p.page_log2;
+
+  const int first_page = start >> p.page_log2;
+  const int n_pages = ((start + n_keys - 1) >> p.page_log2) - first_page + 1;
+  for (int i = tid; i < n_pages; i += kThreads)
+    page_lds[i] = p.block_table[(size_t)b * p.max_pages + first_page + i];
+
+  // B operand (Q^T): column = head slot, k = dims u*32 + grp*8 .. +8.
+  bf16x8 qb[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (col < GT) w = ld16(p.q + (((size_t)b * p.num_q_heads + h0 + col) * D + u * 32 + grp * 8) * 2);
+    qb[u] = __builtin_bit_cast(bf16x8, w);
+  }
+  __syncthreads();
+
+  const size_t head_stride = (size_t)P * D * 2;
+  const size_t page_stride = head_stride * p.num_kv_heads;
+  auto row_base = [&](const uint8_t* base, int jl) -> const uint8_t* {
+    const int j = start + jl;
+    const int pg = page_lds[(j >> p.page_log2) - first_page];
+    return base + (size_t)pg * page_stride + kvh * head_stride + (size_t)(j & (P - 1)) * D * 2;
+  };
+
+  // ---- phase 1: logits, tile by tile, into LDS (and out to global) --------
+  // A wave owns a contiguous range of 16-key tiles.  K loads are issued a
+  // batch of QB tiles at a time, every address clamped to a valid key so
+  // the loads are unconditional; keys past the end are masked to -inf.
+  const int per_wave = C / kWaves;       // multiple of 16
+  const int nt = per_wave / 16;
+  const int wbase = wave * per_wave;
+  float* lg = nullptr;
+  bool lg_vec = false;
+  if constexpr (WRITE_LOGITS) {
+    lg = p.logits + ((size_t)b * p.num_q_heads + h0 + min(col, GT - 1)) * p.logits_stride + start;
+    lg_vec = (p.logits_stride & 3) == 0 && (reinterpret_cast<uintptr_t>(p.logits) & 15) == 0 &&
+             n_keys == C;
+  }
+  float mrun = kNegInf;
+  for (int t0 = 0; t0 < nt; t0 += QB) {
+    bf16x8 kb[QB][NU];
+#pragma unroll
+    for (int t = 0; t < QB; ++t) {
+      const int key = min(wbase + min(t0 + t, nt - 1) * 16 + col, n_keys - 1);
+      const uint8_t* rp = row_base(p.k_pages, key) + grp * 16;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) kb[t][u] = __builtin_bit_cast(bf16x8, ld_kv(rp + u * 64));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < QB; ++t) {
+      if (t0 + t < nt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[t][u], qb[u], acc, 0, 0, 0);
+        const int k0 = wbase + (t0 + t) * 16 + grp * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = (k0 + i < n_keys) ? acc[i] * p.scale : kNegInf;
+        mrun = fmaxf(mrun, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+        if (col < GT) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) p_lds[(k0 + i) * GT + col] = acc[i];
+          if constexpr (WRITE_LOGITS) {
+            if (lg_vec) {
+              *reinterpret_cast<float4*>(lg + k0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (k0 + i < n_keys) lg[k0 + i] = acc[i];
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // ---- phase 2: chunk max and sum of exp per head, p = exp(s - m) in LDS ---
+  mrun = fmaxf(mrun, __shfl_xor(mrun, 16, kWave));
+  mrun = fmaxf(mrun, __shfl_xor(mrun, 32, kWave));
+  if (grp == 0) wstat[wave * 16 + col] = mrun;
+  __syncthreads();
+  {
+    // A thread always meets the same head: element idx = tid + 256 i of the
+    // [C][GT] tile has head idx % GT = tid % GT.
+    const int hh = tid % GT;
+    const float m = fmaxf(fmaxf(wstat[hh], wstat[16 + hh]), fmaxf(wstat[32 + hh], wstat[48 + hh]));
+    const float ms = m * kLog2e;
+    float l = 0.f;
+    for (int idx = tid; idx < C * GT; idx += kThreads) {
+      const float e = exp2_hw(fmaf(p_lds[idx], kLog2e, -ms));
+      p_lds[idx] = e;
+      l += e;
+    }
+#pragma unroll
+    for (int off = GT; off < kWave; off *= 2) l += __shfl_xor(l, off, kWave);
+    if (lane < GT) wstat[64 + wave * 16 + lane] = l;
+    __syncthreads();
+    if (tid < GT)
+      ml_lds[tid] = make_float2(m, (wstat[64 + tid] + wstat[80 + tid]) + (wstat[96 + tid] + wstat[112 + tid]));
+  }
+
+  const size_t ml_base = ((size_t)b * p.num_q_heads + h0) * p.n_chunks + chunk_id;
+  if constexpr (!HAS_V) {
+    if (tid < GT) p.part_ml[ml_base + (size_t)tid * p.n_chunks] = ml_lds[tid];
+    return;
+  } else {
+    // ---- phase 3: P.V on the vector ALUs -----------------------------------
+    const int seg = lane % LPK;
+    const int slot = lane / LPK;
+    float acc[GT][EPL];
+#pragma unroll
+    for (int h = 0; h < GT; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+
+    // Clamped, unconditional loads; keys past the end get p = 0.
+    auto load_batch = [&](uint4 (&vr)[VU], int kb) {
+#pragma unroll
+      for (int u = 0; u < VU; ++u) {
+        const int jl = min(kb + u * KPI + wave * KPW + slot, n_keys - 1);
+        vr[u] = ld_kv(row_base(p.v_pages, jl) + seg * 16);
+      }
+    };
+    auto fma_batch = [&](const uint4 (&vr)[VU], int kb) {
+#pragma unroll
+      for (int u = 0; u < VU; ++u) {
+        const int jr = kb + u * KPI + wave * KPW + slot;
+        const bool valid = jr < n_keys;
+        const int jl = min(jr, n_keys - 1);
+        {
+          float v[EPL];
+          v[0] = bf16lo(vr[u].x); v[1] = bf16hi(vr[u].x);
+          v[2] = bf16lo(vr[u].y); v[3] = bf16hi(vr[u].y);
+          v[4] = bf16lo(vr[u].z); v[5] = bf16hi(vr[u].z);
+          v[6] = bf16lo(vr[u].w); v[7] = bf16hi(vr[u].w);
+          float pj[GT];
+          if constexpr (GT >= 4) {
+#pragma unroll
+            for (int h4 = 0; h4 < GT / 4; ++h4) {
+              const float4 t4 = *reinterpret_cast<const float4*>(p_lds + jl * GT + 4 * h4);
+              pj[4 * h4] = t4.x; pj[4 * h4 + 1] = t4.y; pj[4 * h4 + 2] = t4.z; pj[4 * h4 + 3] = t4.w;
+            }
+          } else {
+#pragma unroll
+            for (int h = 0; h < GT; ++h) pj[h] = p_lds[jl * GT + h];
+          }
+#pragma unroll
+          for (int h = 0; h < GT; ++h) pj[h] = valid ? pj[h] : 0.f;
+#pragma unroll
+          for (int h = 0; h < GT; ++h)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pj[h], v[e], acc[h][e]);
+        }
+      }
+    };
+    constexpr int STEP = KPI * VU;
+    uint4 va[VU], vb[VU];
+    load_batch(va, 0);
+    for (int kb = 0; kb < n_keys; kb += 2 * STEP) {
+      load_batch(vb, kb + STEP);
+      fma_batch(va, kb);
+      load_batch(va, kb + 2 * STEP);
+      fma_batch(vb, kb + STEP);
+    }
+
+#pragma unroll
+    for (int h = 0; h < GT; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float a = acc[h][e];
+#pragma unroll
+        for (int off = LPK; off < kWave; off *= 2) a += __shfl_xor(a, off, kWave);
+        acc[h][e] = a;
+      }
+    if (slot == 0) {
+#pragma unroll
+      for (int h = 0; h < GT; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) red[(wave * GT + h) * D + seg * EPL + e] = acc[h][e];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < GT * D; idx += kThreads) {
+      const float o = (red[idx] + red[GT * D + idx]) + (red[2 * GT * D + idx] + red[3 * GT * D + idx]);
+      const int h = idx / D, d = idx % D;
+      p.part_o[((ml_base + (size_t)h * p.n_chunks)) * D + d] = o;
+    }
+    if (tid < GT) p.part_ml[ml_base + (size_t)tid * p.n_chunks] = ml_lds[tid];
+  }
+}
+
 // ---- combine ----------------------------------------------------------------
+// One workgroup per (sequence, query head): global max M over the chunk
+// partials, weights w_c = exp(m_c - M), l = sum w_c l_c, out = sum w_c o_c / l,
+// lse = M + ln l.  The chunk rows of o are summed by 8 thread groups in
+// parallel (float4 per thread), then across the groups in LDS.
 struct CombineParams {
   const int32_t* seq_lens;
   const float* part_o;
@@ -256,28 +531,66 @@ struct CombineParams {
   int num_q_heads, chunk, n_chunks, D;
 };
 
+constexpr int kCombThreads = 256;
+
+__device__ __forceinline__ float block_reduce(float v, float* scratch, bool is_max) {
+  v = is_max ? wave_max(v) : wave_sum(v);
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  __syncthreads();
+  if (lane == 0) scratch[wave] = v;
+  __syncthreads();
+  float r = scratch[0];
+#pragma unroll
+  for (int w = 1; w < kCombThreads / kWave; ++w) r = is_max ? fmaxf(r, scratch[w]) : r + scratch[w];
+  return r;
+}
+
 template <bool HAS_V>
-__global__ __launch_bounds__(128) void decode_combine(CombineParams p) {
+__global__ __launch_bounds__(kCombThreads) void decode_combine(CombineParams p) {
+  extern __shared__ float csm[];
+  float* w_lds = csm;                          // [n_chunks]
+  float* red = csm + p.n_chunks;               // [kCombThreads][4]: one float4 per thread
+  float* scratch = red + 4 * kCombThreads;     // [kCombThreads / kWave]
   const int bh = blockIdx.x;
   const int b = bh / p.num_q_heads;
   const int L = p.seq_lens[b];
   const int nc = (L + p.chunk - 1) / p.chunk;
   const float2* ml = p.part_ml + (size_t)bh * p.n_chunks;
+  const int tid = threadIdx.x;
   float M = kNegInf;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, ml[c].x);
+  for (int c = tid; c < nc; c += kCombThreads) M = fmaxf(M, ml[c].x);
+  M = block_reduce(M, scratch, true);
   const float Ms = M * kLog2e;
   float l = 0.f;
-  for (int c = 0; c < nc; ++c) l += ml[c].y * exp2_hw(fmaf(ml[c].x, kLog2e, -Ms));
+  for (int c = tid; c < nc; c += kCombThreads) {
+    const float2 v = ml[c];
+    const float w = exp2_hw(fmaf(v.x, kLog2e, -Ms));
+    w_lds[c] = w;
+    l = fmaf(w, v.y, l);
+  }
+  l = block_reduce(l, scratch, false);   // also orders the w_lds writes
   if constexpr (HAS_V) {
-    const int d = threadIdx.x;
-    if (p.out && d < p.D) {
-      const float* po = p.part_o + (size_t)bh * p.n_chunks * p.D + d;
-      float o = 0.f;
-      for (int c = 0; c < nc; ++c) o = fmaf(exp2_hw(fmaf(ml[c].x, kLog2e, -Ms)), po[(size_t)c * p.D], o);
-      p.out[(size_t)bh * p.D + d] = o / l;
+    if (p.out) {
+      const int D4 = p.D / 4;
+      const int d4 = tid % D4, cg = tid / D4, ng = kCombThreads / D4;
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4* po = reinterpret_cast<const float4*>(p.part_o + (size_t)bh * p.n_chunks * p.D);
+      for (int c = cg; c < nc; c += ng) {
+        const float w = w_lds[c];
+        const float4 v = po[(size_t)c * D4 + d4];
+        o.x = fmaf(w, v.x, o.x); o.y = fmaf(w, v.y, o.y);
+        o.z = fmaf(w, v.z, o.z); o.w = fmaf(w, v.w, o.w);
+      }
+      reinterpret_cast<float4*>(red)[cg * D4 + d4] = o;
+      __syncthreads();
+      if (tid < p.D) {
+        float r = 0.f;
+        for (int g = 0; g < ng; ++g) r += red[g * p.D + tid];
+        p.out[(size_t)bh * p.D + tid] = r / l;
+      }
     }
   }
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     const float v = M + log2_hw(l) * kLn2;
     p.lse_ws[bh] = v;
     if (p.lse) p.lse[bh] = v;
@@ -300,6 +613,9 @@ struct FinalizeParams {
 
 constexpr int kFinThreads = 256;
 
+// VEC: 4 consecutive keys per thread with 16-byte accesses (every stride a
+// multiple of 4 and every base 16-byte aligned).
+template <bool VEC>
 __global__ __launch_bounds__(kFinThreads) void decode_finalize(FinalizeParams p) {
   const int b = blockIdx.z;
   const int c = blockIdx.y;
@@ -308,25 +624,66 @@ __global__ __launch_bounds__(kFinThreads) void decode_finalize(FinalizeParams p)
   if (start >= L) return;
   const int end = min(L, start + p.keys_per_block);
   const int h0 = c * p.group;
-  for (int j = start + threadIdx.x; j < end; j += kFinThreads) {
-    float acc = 0.f;
-    for (int g = 0; g < p.group; ++g) {
-      const size_t bh = (size_t)b * p.num_q_heads + h0 + g;
-      const float s = p.logits[bh * p.logits_stride + j];
-      const float e = exp2_hw((s - p.lse_ws[bh]) * kLog2e);
-      if (p.probs) p.probs[bh * p.probs_stride + j] = e;
-      acc += e;
+  const size_t bh0 = (size_t)b * p.num_q_heads + h0;
+  float* cp = p.cum ? p.cum + ((size_t)b * p.num_kv_heads + c) * p.cum_stride : nullptr;
+  if constexpr (VEC) {
+    for (int j = start + threadIdx.x * 4; j < end; j += kFinThreads * 4) {
+      if (j + 3 < end) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int g = 0; g < p.group; ++g) {
+          const float ls = p.lse_ws[bh0 + g] * kLog2e;
+          const float4 s = *reinterpret_cast<const float4*>(p.logits + (bh0 + g) * p.logits_stride + j);
+          float4 e;
+          e.x = exp2_hw(fmaf(s.x, kLog2e, -ls)); e.y = exp2_hw(fmaf(s.y, kLog2e, -ls));
+          e.z = exp2_hw(fmaf(s.z, kLog2e, -ls)); e.w = exp2_hw(fmaf(s.w, kLog2e, -ls));
+          if (p.probs) {
+#if KVSEL_NT_PROBS
+            st16_stream(p.probs + (bh0 + g) * p.probs_stride + j, e);
+#else
+            *reinterpret_cast<float4*>(p.probs + (bh0 + g) * p.probs_stride + j) = e;
+#endif
+          }
+          acc.x += e.x; acc.y += e.y; acc.z += e.z; acc.w += e.w;
+        }
+        if (cp) {
+          float4 cv = *reinterpret_cast<float4*>(cp + j);
+          cv.x = fmaf(p.decay, cv.x, acc.x); cv.y = fmaf(p.decay, cv.y, acc.y);
+          cv.z = fmaf(p.decay, cv.z, acc.z); cv.w = fmaf(p.decay, cv.w, acc.w);
+          *reinterpret_cast<float4*>(cp + j) = cv;
+        }
+      } else {
+        for (int jj = j; jj < end; ++jj) {
+          float acc = 0.f;
+          for (int g = 0; g < p.group; ++g) {
+            const float ls = p.lse_ws[bh0 + g] * kLog2e;
+            const float e = exp2_hw(fmaf(p.logits[(bh0 + g) * p.logits_stride + jj], kLog2e, -ls));
+            if (p.probs) p.probs[(bh0 + g) * p.probs_stride + jj] = e;
+            acc += e;
+          }
+          if (cp) cp[jj] = fmaf(p.decay, cp[jj], acc);
+        }
+      }
     }
-    if (p.cum) {
-      float* cp = p.cum + ((size_t)b * p.num_kv_heads + c) * p.cum_stride + j;
-      *cp = fmaf(p.decay, *cp, acc);
+  } else {
+    for (int j = start + threadIdx.x; j < end; j += kFinThreads) {
+      float acc = 0.f;
+      for (int g = 0; g < p.group; ++g) {
+        const float ls = p.lse_ws[bh0 + g] * kLog2e;
+        const float e = exp2_hw(fmaf(p.logits[(bh0 + g) * p.logits_stride + j], kLog2e, -ls));
+        if (p.probs) p.probs[(bh0 + g) * p.probs_stride + j] = e;
+        acc += e;
+      }
+      if (cp) cp[j] = fmaf(p.decay, cp[j], acc);
     }
   }
 }
 
 template <bool BF16, int D, int GT, bool HAS_V, bool WL>
 hipError_t launch_partial_t(const PartialParams& pp, dim3 grid, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((decode_partial<BF16, D, GT, HAS_V, WL>), grid, dim3(kThreads), lds, s, pp);
+  if constexpr (BF16)
+    hipLaunchKernelGGL((decode_partial_mfma<D, GT, HAS_V, WL>), grid, dim3(kThreads), lds, s, pp);
+  else
+    hipLaunchKernelGGL((decode_partial<false, D, GT, HAS_V, WL>), grid, dim3(kThreads), lds, s, pp);
   return hipGetLastError();
 }
 
@@ -363,13 +720,13 @@ DecodePlan plan_decode(int num_seqs, int num_kv_heads, int num_q_heads, int head
   const int G = num_q_heads / num_kv_heads;
   pl.gt = G >= 8 ? 8 : G;
   pl.hgroups = G / pl.gt;
-  // Largest chunk (<= 512 keys) that still gives the grid >= 2048 workgroups,
-  // never below 64 keys.
-  int chunk = 512;
+  // Largest chunk (<= KVSEL_MAX_CHUNK keys) that still gives the grid
+  // >= KVSEL_MIN_WGS workgroups, never below 64 keys.
+  int chunk = KVSEL_MAX_CHUNK;
   while (chunk > 64) {
     const long long wgs = (long long)num_seqs * num_kv_heads * pl.hgroups *
                           ((max_seq_len + chunk - 1) / chunk);
-    if (wgs >= 2048) break;
+    if (wgs >= KVSEL_MIN_WGS) break;
     chunk /= 2;
   }
   pl.chunk = chunk;
@@ -424,7 +781,8 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
 
   const dim3 grid(pl.n_chunks, a.num_kv_heads * pl.hgroups, a.num_seqs);
   const size_t lds = (size_t)pl.gt * pl.chunk * sizeof(float) +
-                     (size_t)kWaves * pl.gt * a.head_dim * sizeof(float) + pl.gt * sizeof(float2) +
+                     (size_t)kWaves * pl.gt * a.head_dim * sizeof(float) +
+                     (a.bf16 ? 2 * kWaves * 16 * sizeof(float) : 0) + pl.gt * sizeof(float2) +
                      ((size_t)pl.chunk / 16 + 2) * sizeof(int);
   const bool wl = logits != nullptr;
   hipError_t e;
@@ -452,10 +810,11 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
       cp.n_chunks = pl.n_chunks;
       cp.D = a.head_dim;
       const dim3 cgrid(a.num_seqs * a.num_q_heads);
+      const size_t clds = ((size_t)pl.n_chunks + 4 * kCombThreads + 8) * sizeof(float);
       if (use_v)
-        hipLaunchKernelGGL(decode_combine<true>, cgrid, dim3(a.head_dim), 0, stream, cp);
+        hipLaunchKernelGGL(decode_combine<true>, cgrid, dim3(kCombThreads), clds, stream, cp);
       else
-        hipLaunchKernelGGL(decode_combine<false>, cgrid, dim3(64), 0, stream, cp);
+        hipLaunchKernelGGL(decode_combine<false>, cgrid, dim3(kCombThreads), clds, stream, cp);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -478,7 +837,14 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     fp.keys_per_block = 1024;
     const dim3 fgrid((a.max_seq_len + fp.keys_per_block - 1) / fp.keys_per_block, a.num_kv_heads,
                      a.num_seqs);
-    hipLaunchKernelGGL(decode_finalize, fgrid, dim3(kFinThreads), 0, stream, fp);
+    auto al16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; };
+    const bool vec = logits_stride % 4 == 0 && al16(logits) &&
+                     (!a.probs || (a.probs_stride % 4 == 0 && al16(a.probs))) &&
+                     (!a.cum || (a.cum_stride % 4 == 0 && al16(a.cum)));
+    if (vec)
+      hipLaunchKernelGGL(decode_finalize<true>, fgrid, dim3(kFinThreads), 0, stream, fp);
+    else
+      hipLaunchKernelGGL(decode_finalize<false>, fgrid, dim3(kFinThreads), 0, stream, fp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

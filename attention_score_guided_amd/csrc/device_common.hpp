@@ -69,7 +69,18 @@ __device__ __forceinline__ float group_max(float v) {
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 __device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 
-// 16-byte global load/store.
+// 16-byte global loads.  ld16_stream marks the access non-temporal: data
+// read exactly once (the K/V stream) should not displace reused lines.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// Non-temporal 16-byte store (results not re-read by this library).
+__device__ __forceinline__ void st16_stream(void* p, float4 v) {
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(f32x4v{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4v*>(p));
+}
 
 }  // namespace kvsel
