@@ -2,6 +2,7 @@
 // sizing, device check and dispatch to the HIP launchers.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -203,6 +204,48 @@ int kvsel_block_aggregate(const float* scores, int64_t score_stride, const int32
                                     accumulate != 0, out_max, out_mean, out_stride,
                                     static_cast<hipStream_t>(stream)),
       "block_aggregate launch");
+}
+
+size_t kvsel_select_workspace_bytes(int32_t rows, int32_t max_len, int32_t mode) {
+  if (rows <= 0 || max_len <= 0 || (mode != KVSEL_SELECT_ROWS && mode != KVSEL_SELECT_GLOBAL_PERCENTILE))
+    return 0;
+  return kvsel::select_workspace_bytes(rows, max_len, mode);
+}
+
+int kvsel_select_keep(const float* scores, int64_t stride, const int32_t* lengths, int32_t rows,
+                      int32_t max_len, int32_t sinks, int32_t window, const int32_t* budgets,
+                      int32_t max_budget, int32_t mode, int32_t global_budget, int32_t* out_idx,
+                      int64_t out_stride, int32_t* out_count, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!scores || !lengths || !out_idx || !out_count)
+    return fail(KVSEL_ERR_INVALID, "NULL pointer argument");
+  if (rows <= 0 || max_len <= 0) return fail(KVSEL_ERR_INVALID, "rows and max_len must be positive");
+  if (stride < max_len) return fail(KVSEL_ERR_INVALID, "stride < max_len");
+  if (sinks < 0 || window < 0 || max_budget < 0 || global_budget < 0)
+    return fail(KVSEL_ERR_INVALID, "sinks, window and budgets must be >= 0");
+  if (mode == KVSEL_SELECT_ROWS) {
+    const long long need = std::min<long long>(max_len, std::max<long long>(max_budget, (long long)sinks + window));
+    if (out_stride < need)
+      return fail(KVSEL_ERR_INVALID, "out_stride %lld < %lld", (long long)out_stride, need);
+  } else if (mode == KVSEL_SELECT_GLOBAL_PERCENTILE) {
+    if (sinks != 0 || window != 0)
+      return fail(KVSEL_ERR_INVALID, "GLOBAL_PERCENTILE takes no sinks or window");
+    if (out_stride < max_len) return fail(KVSEL_ERR_INVALID, "out_stride < max_len");
+    if (max_len > 8192 || (long long)rows * max_len > (1LL << 20))
+      return fail(KVSEL_ERR_UNSUPPORTED, "GLOBAL_PERCENTILE needs max_len <= 8192 and rows * max_len <= 2^20");
+    const size_t need = kvsel::select_workspace_bytes(rows, max_len, mode);
+    if (!workspace || workspace_bytes < need)
+      return fail(KVSEL_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  } else {
+    return fail(KVSEL_ERR_INVALID, "mode %d", mode);
+  }
+  int st = check_device();
+  if (st != KVSEL_OK) return st;
+  return hip_status(kvsel::launch_select(scores, stride, lengths, rows, max_len, sinks, window,
+                                         budgets, max_budget, mode, global_budget, out_idx,
+                                         out_stride, out_count, workspace,
+                                         static_cast<hipStream_t>(stream)),
+                    "select_keep launch");
 }
 
 }  // extern "C"

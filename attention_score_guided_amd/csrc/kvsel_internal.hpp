@@ -53,4 +53,12 @@ hipError_t launch_block_aggregate(const float* scores, int64_t score_stride,
                                   float* out_max, float* out_mean, int64_t out_stride,
                                   hipStream_t stream);
 
+size_t select_workspace_bytes(int rows, int max_len, int mode);
+
+hipError_t launch_select(const float* scores, int64_t stride, const int32_t* lengths, int rows,
+                         int max_len, int sinks, int window, const int32_t* budgets,
+                         int max_budget, int mode, int global_budget, int32_t* out_idx,
+                         int64_t out_stride, int32_t* out_count, void* workspace,
+                         hipStream_t stream);
+
 }  // namespace kvsel

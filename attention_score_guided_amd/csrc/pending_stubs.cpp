@@ -4,12 +4,6 @@
 
 extern "C" {
 
-int kvsel_select_keep(const float*, int64_t, const int32_t*, int32_t, int32_t, int32_t, int32_t,
-                      const int32_t*, int32_t, int32_t, int32_t, int32_t*, int64_t, int32_t*, void*,
-                      size_t, void*) {
-  return KVSEL_ERR_UNSUPPORTED;
-}
-size_t kvsel_select_workspace_bytes(int32_t, int32_t, int32_t) { return 0; }
 int kvsel_snapkv_vote(const kvsel_paged_kv*, const void*, int32_t, int32_t, int32_t, float, int32_t,
                       float*, int64_t, void*, size_t, void*) {
   return KVSEL_ERR_UNSUPPORTED;

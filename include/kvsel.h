@@ -170,8 +170,8 @@ int kvsel_block_aggregate(const float* scores, int64_t score_stride, const int32
  *   percentile (rank + 1) / n of its score within its own row (rank ascending,
  *   equal scores: the lower position ranks higher); the global_budget
  *   positions with the highest percentiles over all rows are kept (ties: lower
- *   row, then lower position).  sinks and window must be 0.  Rows up to
- *   1048576 positions.
+ *   row, then lower position).  sinks and window must be 0.  Supported:
+ *   max_len <= 8192 and rows * max_len <= 2^20 (else UNSUPPORTED).
  * Output: out_idx[r][0 .. out_count[r]) holds the kept positions ascending;
  *   the rest of the row is left untouched.
  *   scores [rows][stride] f32, lengths [rows] i32 (1 <= n <= max_len),

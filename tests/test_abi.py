@@ -95,3 +95,29 @@ def test_accumulate_and_aggregate_validation():
     assert agg(FAKE, 64, FAKE, 1, 1, 64, 16, 2, 0, FAKE, None, 4, None) == K.KVSEL_ERR_INVALID
     assert agg(FAKE, 63, FAKE, 1, 1, 64, 16, 0, 0, FAKE, None, 4, None) == K.KVSEL_ERR_INVALID
     assert agg(FAKE, 64, FAKE, 1, 1, 64, 0, 0, 0, FAKE, None, 4, None) == K.KVSEL_ERR_INVALID
+
+
+def test_select_validation():
+    lib = K.library()
+    sel = lib.kvsel_select_keep
+    ok = dict(scores=FAKE, stride=100, lengths=FAKE, rows=4, max_len=100, sinks=4, window=8,
+              budgets=None, max_budget=20, mode=0, gb=0, out=FAKE, out_stride=20, cnt=FAKE,
+              ws=None, wsb=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return sel(a["scores"], a["stride"], a["lengths"], a["rows"], a["max_len"], a["sinks"],
+                   a["window"], a["budgets"], a["max_budget"], a["mode"], a["gb"], a["out"],
+                   a["out_stride"], a["cnt"], a["ws"], a["wsb"], None)
+    assert call(scores=None) == K.KVSEL_ERR_INVALID
+    assert call(rows=0) == K.KVSEL_ERR_INVALID
+    assert call(stride=99) == K.KVSEL_ERR_INVALID
+    assert call(sinks=-1) == K.KVSEL_ERR_INVALID
+    assert call(out_stride=19) == K.KVSEL_ERR_INVALID
+    assert call(mode=3) == K.KVSEL_ERR_INVALID
+    assert call(mode=1) == K.KVSEL_ERR_INVALID                      # sinks/window in GLOBAL
+    g = dict(mode=1, sinks=0, window=0, out_stride=100)
+    assert call(**g, ws=None) == K.KVSEL_ERR_WORKSPACE
+    assert call(**dict(g, max_len=9000, stride=9000, out_stride=9000)) == K.KVSEL_ERR_UNSUPPORTED
+    assert lib.kvsel_select_workspace_bytes(4, 100, 1) >= 4 * 100 * 8
+    assert lib.kvsel_select_workspace_bytes(4, 100, 0) == 0

@@ -1,0 +1,120 @@
+"""GPU parity of kvsel_select_keep against the oracle: keep sets are
+bit-exact (the GPU selects on the same fp32 scores the oracle reads)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from tests.parity_util import note
+
+pytestmark = pytest.mark.gpu
+
+
+def _K():
+    import attention_score_guided_amd as K
+    return K
+
+
+def _run_rows(scores, lengths, sinks, window, budgets, max_budget, per_row_budget=True):
+    K = _K()
+    rows, stride = scores.shape
+    max_len = int(max(lengths))
+    out_stride = max(1, min(max_len, max(max_budget, sinks + window)))
+    sc = torch.from_numpy(scores.astype(np.float32)).cuda()
+    lens = torch.tensor(lengths, dtype=torch.int32).cuda()
+    bud = torch.tensor(budgets, dtype=torch.int32).cuda() if per_row_budget else None
+    idx = torch.full((rows, out_stride), -5, dtype=torch.int32).cuda()
+    cnt = torch.full((rows,), -1, dtype=torch.int32).cuda()
+    K.select_keep(sc, lens, max_len, sinks, window, bud, max_budget, idx, cnt)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), cnt.cpu().numpy()
+
+
+def _check_rows(scores, lengths, sinks, window, budgets, idx, cnt):
+    for r, n in enumerate(lengths):
+        want = O.select_keep(scores[r].astype(np.float32).astype(np.float64), n, sinks, window, budgets[r])
+        got = idx[r, :cnt[r]]
+        assert cnt[r] == len(want), (r, cnt[r], len(want))
+        np.testing.assert_array_equal(got, want)
+        assert (idx[r, cnt[r]:] == -5).all(), "slots past the count must be untouched"
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_rows_random_with_ties(seed):
+    rng = np.random.default_rng(100 + seed)
+    rows = 40
+    lengths = [int(x) for x in rng.integers(1, 3000, size=rows)]
+    lengths[0], lengths[1], lengths[2] = 1, 2, 3000
+    stride = 3001
+    scores = rng.integers(0, 50 if seed % 2 else 5, size=(rows, stride)).astype(np.float32)
+    if seed == 3:
+        scores[scores == 0] = -0.0
+        scores[:, ::7] = -np.inf
+    sinks, window = [(4, 64), (0, 0), (4, 0), (0, 512), (16, 16), (3000, 0)][seed]
+    budgets = [int(rng.integers(0, n + 5)) for n in lengths]
+    max_budget = max(budgets)
+    note(f"select rows seed={seed} sinks={sinks} window={window}")
+    idx, cnt = _run_rows(scores, lengths, sinks, window, budgets, max_budget)
+    _check_rows(scores, lengths, sinks, window, budgets, idx, cnt)
+
+
+def test_rows_shared_budget_and_policies():
+    rng = np.random.default_rng(7)
+    n, budget = 300, 256
+    scores = rng.random((3, n)).astype(np.float32)
+    # H2O-style, StreamingLLM (sinks 4 + window 252) and recent-only
+    for sinks, window in [(4, 64), (4, budget - 4), (0, budget)]:
+        idx, cnt = _run_rows(scores, [n] * 3, sinks, window, [budget] * 3, budget, per_row_budget=False)
+        _check_rows(scores, [n] * 3, sinks, window, [budget] * 3, idx, cnt)
+    idx, cnt = _run_rows(scores, [n] * 3, 4, budget - 4, [budget] * 3, budget, per_row_budget=False)
+    assert idx[0, :cnt[0]].tolist() == list(range(4)) + list(range(n - 252, n))
+
+
+def test_rows_large_row_top4096():
+    """One 131040-key row per KV head, top-4096, nothing forced (the SnapKV
+    vote selection shape)."""
+    rng = np.random.default_rng(8)
+    rows, n = 4, 131040
+    scores = rng.random((rows, n)).astype(np.float32)
+    scores[1, 1000:2000] = 0.5          # a plateau of ties
+    idx, cnt = _run_rows(scores, [n] * rows, 0, 0, [4096] * rows, 4096)
+    _check_rows(scores, [n] * rows, 0, 0, [4096] * rows, idx, cnt)
+
+
+def test_rows_config3_shape():
+    """Per (sequence, KV head) keep budget floor(0.2 L_b) with sinks 4 and
+    window 512 over ragged rows of 8K-33K keys."""
+    rng = np.random.default_rng(9)
+    lens_b = [int(x) for x in rng.integers(8448, 33024, size=16)]
+    lengths = [L for L in lens_b for _ in range(8)]
+    stride = max(lengths)
+    scores = (rng.random((128, stride)) ** 8).astype(np.float32)
+    budgets = [int(0.2 * L) for L in lengths]
+    idx, cnt = _run_rows(scores, lengths, 4, 512, budgets, max(budgets))
+    _check_rows(scores, lengths, 4, 512, budgets, idx, cnt)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_global_percentile(seed):
+    K = _K()
+    rng = np.random.default_rng(200 + seed)
+    if seed == 0:
+        rows, lengths, gb = 8, [512] * 8, 1024          # the 70B block-selection shape
+    else:
+        rows = int(rng.integers(1, 12))
+        lengths = [int(x) for x in rng.integers(1, 700, size=rows)]
+        gb = int(rng.integers(0, sum(lengths) + 3))
+    max_len = max(lengths)
+    scores = rng.integers(0, 6 if seed > 1 else 10**6, size=(rows, max_len)).astype(np.float32)
+    sc = torch.from_numpy(scores).cuda()
+    lens = torch.tensor(lengths, dtype=torch.int32).cuda()
+    idx = torch.full((rows, max_len), -5, dtype=torch.int32).cuda()
+    cnt = torch.zeros((rows,), dtype=torch.int32).cuda()
+    K.select_keep(sc, lens, max_len, 0, 0, None, 0, idx, cnt, mode=K.SELECT_GLOBAL_PERCENTILE,
+                  global_budget=gb)
+    torch.cuda.synchronize()
+    want = O.global_percentile_select([scores[r].astype(np.float64) for r in range(rows)], lengths, gb)
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for r in range(rows):
+        np.testing.assert_array_equal(idx[r, :cnt[r]], want[r])
+    assert cnt.sum() == min(gb, sum(lengths))
