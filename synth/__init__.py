@@ -32,7 +32,7 @@ import torch
 __all__ = [
     "PagedKV", "generator", "shuffled_block_table", "normal", "write_positions",
     "orthonormal_directions", "plant_sinks_and_bumps",
-    "config1", "config2", "config3_layer", "config4_layer", "config5",
+    "tiny_case", "qwen_like_layer", "llama3_8b_layer", "llama70b_layer", "long_context_128k",
 ]
 
 
@@ -160,7 +160,7 @@ def _bump_centres(L_prefix: int, n: int, gen: torch.Generator):
 # --------------------------------------------------------------------------
 # workload builders
 # --------------------------------------------------------------------------
-def config1(seed: int = 1, prompt: int = 512, steps: int = 16, device="cpu"):
+def tiny_case(seed: int = 1, prompt: int = 512, steps: int = 16, device="cpu"):
     """Tiny case: 1 sequence, 4 query heads on 1 KV head, d=64, fp32, P=16,
     a 512-token prompt, +4 logit on keys 0-3, then ``steps`` decode steps each
     appending one N(0,1) key/value and drawing a fresh query."""
@@ -184,7 +184,7 @@ def config1(seed: int = 1, prompt: int = 512, steps: int = 16, device="cpu"):
             "block_size": 16, "sinks": 4, "window": 64, "budget": 128}
 
 
-def config2(seed: int = 2, n_tokens: int = 1600, device="cpu"):
+def qwen_like_layer(seed: int = 2, n_tokens: int = 1600, device="cpu"):
     """Qwen3-0.6B-like layer: 16 query / 8 KV heads, d=128, bf16; one
     sequence of ``n_tokens`` whose keys carry sink boosts U[3,5] on positions
     0-3.  Returns logical K, V, Q (queries for every position), bf16."""
@@ -202,7 +202,7 @@ def config2(seed: int = 2, n_tokens: int = 1600, device="cpu"):
             "page_size": 16}
 
 
-def config3_layer(seed: int = 3, num_seqs: int = 16, min_len: int = 8192, max_len: int = 32768,
+def llama3_8b_layer(seed: int = 3, num_seqs: int = 16, min_len: int = 8192, max_len: int = 32768,
                   steps: int = 256, device="cpu"):
     """Llama-3-8B-shape layer: 32 query / 8 KV heads, d=128, bf16, P=16,
     ragged L_b ~ U{min_len..max_len}, shuffled block table, N(0,1) data, and a
@@ -225,7 +225,7 @@ def config3_layer(seed: int = 3, num_seqs: int = 16, min_len: int = 8192, max_le
             "budget_frac": 0.2}
 
 
-def config4_layer(layer: int, seed: int = 4, num_seqs: int = 8, seq_len: int = 32768,
+def llama70b_layer(layer: int, seed: int = 4, num_seqs: int = 8, seq_len: int = 32768,
                   device="cpu", block_table: Optional[torch.Tensor] = None):
     """One layer of the LLaMA-70B-shape step: 64 query / 8 KV heads, d=128,
     bf16, P=64, B=8 at L=32768, N(0,1) data.  Each layer draws from its own
@@ -244,7 +244,7 @@ def config4_layer(layer: int, seed: int = 4, num_seqs: int = 8, seq_len: int = 3
             "scale": 1.0 / math.sqrt(d), "block_size": 64, "budget_frac": 0.25}
 
 
-def config5(seed: int = 5, num_seqs: int = 4, seq_len: int = 131072, window: int = 32,
+def long_context_128k(seed: int = 5, num_seqs: int = 4, seq_len: int = 131072, window: int = 32,
             sparse_steps: int = 64, device="cpu"):
     """128K long-context case: 32 query / 8 KV heads, d=128, bf16, P=16,
     planted sinks (U[3,5]) and 8 Gaussian hot regions per sequence; a

@@ -134,12 +134,12 @@ def test_decode_bitwise_deterministic():
         assert torch.equal(a, b)
 
 
-def test_config1_sixteen_steps_with_h2o_accumulation():
+def test_tiny_case_sixteen_steps_with_h2o_accumulation():
     """Tiny case: 1 sequence, G=4, d=64, fp32, 512-token prompt with planted
     sinks, 16 decode steps each appending a token; cum accumulated on the GPU
     with the fused path, compared step by step with the oracle."""
     K = _K()
-    cfg = synth.config1(device="cuda")
+    cfg = synth.tiny_case(device="cuda")
     kvt = cfg["kv"]
     steps, prompt, Hq = cfg["steps"], cfg["prompt"], cfg["num_q_heads"]
     cap = prompt + steps
@@ -166,12 +166,12 @@ def test_config1_sixteen_steps_with_h2o_accumulation():
     assert float(cum[0, 0, :4].min()) > float(cum[0, 0, 4:].max())
 
 
-def test_config3_reduced_steps_ragged():
+def test_llama3_8b_layer_reduced_steps_ragged():
     """Llama-3-8B-shape layer scaled down (B=4, L_b in [1000, 3000]): 8 decode
     steps appending one key per step, fused accumulation, q / T_b."""
     K = _K()
     steps = 8
-    cfg = synth.config3_layer(num_seqs=4, min_len=1000, max_len=3000, steps=steps, device="cuda")
+    cfg = synth.llama3_8b_layer(num_seqs=4, min_len=1000, max_len=3000, steps=steps, device="cuda")
     kvt = cfg["kv"]
     B, Hq, Hkv = 4, 32, 8
     base = kvt.seq_lens.clone()
@@ -198,13 +198,13 @@ def test_config3_reduced_steps_ragged():
         assert abs(float(cum[b].sum()) - steps * Hq) < 1e-2
 
 
-def test_config4_layer_full_size_sampled():
+def test_llama70b_layer_full_size_sampled():
     """LLaMA-70B-shape layer at full size (B=8, L=32768, G=8, P=64) in the
     launch configuration the benchmark times (probs emitted, cum fused):
     sampled (sequence, KV head) rows are checked in full against the oracle
     and the probability mass of every sequence against H_q."""
     K = _K()
-    cfg = synth.config4_layer(0, device="cuda")
+    cfg = synth.llama70b_layer(0, device="cuda")
     kvt = cfg["kv"]
     B, Hq, Hkv, L = 8, 64, 8, 32768
     kv = K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, kvt.seq_lens, 64, L)

@@ -81,7 +81,7 @@ def test_rows_large_row_top4096():
     _check_rows(scores, [n] * rows, 0, 0, [4096] * rows, idx, cnt)
 
 
-def test_rows_config3_shape():
+def test_rows_llama3_8b_keep_shape():
     """Per (sequence, KV head) keep budget floor(0.2 L_b) with sinks 4 and
     window 512 over ragged rows of 8K-33K keys."""
     rng = np.random.default_rng(9)

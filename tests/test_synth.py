@@ -16,8 +16,8 @@ def _digest(*ts):
     return h.hexdigest()
 
 
-def test_config1_deterministic_and_sink_bias():
-    a, b = synth.config1(), synth.config1()
+def test_tiny_case_deterministic_and_sink_bias():
+    a, b = synth.tiny_case(), synth.tiny_case()
     assert _digest(a["kv"].k_pages, a["kv"].v_pages, a["q_steps"], a["kv"].block_table) == \
         _digest(b["kv"].k_pages, b["kv"].v_pages, b["q_steps"], b["kv"].block_table)
     kv = a["kv"]
@@ -41,9 +41,9 @@ def test_shuffled_block_table_is_a_partial_permutation():
     assert len(set(flat)) == len(flat) and max(flat) < n and min(flat) >= 0
 
 
-def test_config3_small_deterministic():
-    a = synth.config3_layer(num_seqs=2, min_len=64, max_len=200, steps=4)
-    b = synth.config3_layer(num_seqs=2, min_len=64, max_len=200, steps=4)
+def test_llama3_8b_layer_small_deterministic():
+    a = synth.llama3_8b_layer(num_seqs=2, min_len=64, max_len=200, steps=4)
+    b = synth.llama3_8b_layer(num_seqs=2, min_len=64, max_len=200, steps=4)
     assert torch.equal(a["kv"].k_pages.view(torch.int16), b["kv"].k_pages.view(torch.int16))
     assert torch.equal(a["q_steps"].view(torch.int16), b["q_steps"].view(torch.int16))
     assert a["kv"].seq_lens.min() >= 64 and a["kv"].seq_lens.max() <= 200
