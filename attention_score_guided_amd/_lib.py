@@ -30,6 +30,7 @@ EXPORTED = (
     "kvsel_decode_attn_scores", "kvsel_decode_workspace_bytes", "kvsel_accumulate",
     "kvsel_block_aggregate", "kvsel_select_keep", "kvsel_select_workspace_bytes",
     "kvsel_snapkv_vote", "kvsel_snapkv_workspace_bytes", "kvsel_sparse_attn",
+    "kvsel_sparse_workspace_bytes",
     "kvsel_status_string", "kvsel_last_error",
 )
 
@@ -67,7 +68,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvsel_select_workspace_bytes": (SZ, [I32, I32, I32]),
         "kvsel_snapkv_vote": (ctypes.c_int, [D, P, I32, I32, I32, F, I32, P, I64, P, SZ, P]),
         "kvsel_snapkv_workspace_bytes": (SZ, [D, I32, I32]),
-        "kvsel_sparse_attn": (ctypes.c_int, [D, P, I32, P, I64, P, I32, I32, F, P, P, P]),
+        "kvsel_sparse_attn": (ctypes.c_int, [D, P, I32, P, I64, P, I32, I32, F, P, P, P, SZ, P]),
+        "kvsel_sparse_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "kvsel_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "kvsel_last_error": (ctypes.c_char_p, []),
     }
@@ -232,12 +234,21 @@ def snapkv_vote(kv: PagedKV, q_win: torch.Tensor, num_q_heads: int, window: int,
         _ptr(ws, None, "workspace"), wsb, _stream(stream)))
 
 
+def sparse_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_count: int) -> int:
+    return int(_LIB.kvsel_sparse_workspace_bytes(num_seqs, num_q_heads, head_dim, max_count))
+
+
 def sparse_attn(kv: PagedKV, q: torch.Tensor, num_q_heads: int, indices: torch.Tensor,
                 counts: torch.Tensor, max_count: int, scale: float, out: torch.Tensor,
-                probs: Optional[torch.Tensor] = None, stream=None) -> None:
+                probs: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                stream=None) -> None:
     """kvsel_sparse_attn: indices ``[B][idx_heads][stride]``, counts ``[B][idx_heads]``."""
+    if q.dtype != kv.dtype:
+        raise TypeError("q must have the cache dtype")
+    ws, wsb = _workspace(sparse_workspace_bytes(int(q.shape[0]), num_q_heads, int(q.shape[-1]), max_count),
+                         q.device, workspace)
     _check(_LIB.kvsel_sparse_attn(
         kv.ref(), _ptr(q, None, "q"), num_q_heads, _ptr(indices, torch.int32, "indices"),
         indices.shape[-1], _ptr(counts, torch.int32, "counts"), int(indices.shape[1]), max_count,
         float(scale), _ptr(out, torch.float32, "out"), _ptr(probs, torch.float32, "probs"),
-        _stream(stream)))
+        _ptr(ws, None, "workspace"), wsb, _stream(stream)))

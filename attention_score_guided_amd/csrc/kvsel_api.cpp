@@ -248,4 +248,55 @@ int kvsel_select_keep(const float* scores, int64_t stride, const int32_t* length
                     "select_keep launch");
 }
 
+size_t kvsel_sparse_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                    int32_t max_count) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_count < 0) return 0;
+  return kvsel::sparse_workspace_bytes(num_seqs, num_q_heads, head_dim, max_count);
+}
+
+int kvsel_sparse_attn(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads,
+                      const int32_t* indices, int64_t idx_stride, const int32_t* counts,
+                      int32_t idx_heads, int32_t max_count, float scale, float* out,
+                      float* probs, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_kv(kv, num_q_heads, true);
+  if (st != KVSEL_OK) return st;
+  if (!q || !indices || !counts || !out) return fail(KVSEL_ERR_INVALID, "NULL pointer argument");
+  if (idx_heads != num_q_heads && idx_heads != kv->num_kv_heads)
+    return fail(KVSEL_ERR_INVALID, "idx_heads %d must be num_q_heads or num_kv_heads", idx_heads);
+  if (max_count < 0 || idx_stride < max_count)
+    return fail(KVSEL_ERR_INVALID, "need 0 <= max_count <= idx_stride");
+  const int G = num_q_heads / kv->num_kv_heads;
+  if (idx_heads != num_q_heads && !(G <= 8 && is_pow2(G)))
+    return fail(KVSEL_ERR_UNSUPPORTED, "shared index sets need a group size that is a power of two <= 8");
+  const size_t need = kvsel::sparse_workspace_bytes(kv->num_seqs, num_q_heads, kv->head_dim, max_count);
+  if (!workspace || workspace_bytes < need)
+    return fail(KVSEL_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  st = check_device();
+  if (st != KVSEL_OK) return st;
+  if (max_count == 0) max_count = 1;  // one (empty) slice still writes out = 0
+  kvsel::SparseArgs a{};
+  a.k_pages = kv->k_pages;
+  a.v_pages = kv->v_pages;
+  a.block_table = kv->block_table;
+  a.seq_lens = kv->seq_lens;
+  a.q = q;
+  a.indices = indices;
+  a.idx_stride = idx_stride;
+  a.counts = counts;
+  a.num_seqs = kv->num_seqs;
+  a.num_kv_heads = kv->num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.head_dim = kv->head_dim;
+  a.page_size = kv->page_size;
+  a.max_pages = kv->max_pages_per_seq;
+  a.idx_heads = idx_heads;
+  a.max_count = max_count;
+  a.bf16 = kv->dtype == KVSEL_BF16;
+  a.scale = scale;
+  a.out = out;
+  a.probs = probs;
+  a.workspace = workspace;
+  return hip_status(kvsel::launch_sparse(a, static_cast<hipStream_t>(stream)), "sparse_attn launch");
+}
+
 }  // extern "C"

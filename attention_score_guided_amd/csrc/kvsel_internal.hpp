@@ -61,4 +61,24 @@ hipError_t launch_select(const float* scores, int64_t stride, const int32_t* len
                          int64_t out_stride, int32_t* out_count, void* workspace,
                          hipStream_t stream);
 
+struct SparseArgs {
+  const void* k_pages;
+  const void* v_pages;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const void* q;
+  const int32_t* indices;
+  int64_t idx_stride;
+  const int32_t* counts;
+  int num_seqs, num_kv_heads, num_q_heads, head_dim, page_size, max_pages, idx_heads, max_count;
+  bool bf16;
+  float scale;
+  float* out;
+  float* probs;
+  void* workspace;
+};
+
+size_t sparse_workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int max_count);
+hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream);
+
 }  // namespace kvsel

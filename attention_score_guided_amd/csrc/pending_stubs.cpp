@@ -9,9 +9,5 @@ int kvsel_snapkv_vote(const kvsel_paged_kv*, const void*, int32_t, int32_t, int3
   return KVSEL_ERR_UNSUPPORTED;
 }
 size_t kvsel_snapkv_workspace_bytes(const kvsel_paged_kv*, int32_t, int32_t) { return 0; }
-int kvsel_sparse_attn(const kvsel_paged_kv*, const void*, int32_t, const int32_t*, int64_t,
-                      const int32_t*, int32_t, int32_t, float, float*, float*, void*) {
-  return KVSEL_ERR_UNSUPPORTED;
-}
 
 }  // extern "C"

@@ -221,20 +221,26 @@ size_t kvsel_snapkv_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_head
  * the softmax runs over the selected keys only; DeepSeek-style indexers pick
  * 2048 keys per query).
  * idx_heads = num_q_heads: one set per query head; idx_heads = num_kv_heads:
- * one set shared by the query heads of a group.
+ * one set shared by the query heads of a group (G a power of two <= 8).
  *   indices [num_seqs][idx_heads][idx_stride] i32 logical positions < L_b,
- *           distinct; entries < 0 are ignored; only the first
- *           counts[b][g] entries of a row are read.
+ *           distinct; entries < 0 are ignored; only the first counts[b][g]
+ *           entries of a row are read.
  *   counts  [num_seqs][idx_heads] i32, 0 <= counts <= max_count <= idx_stride.
  *   out     [num_seqs][num_q_heads][head_dim] f32 (all zero for an empty set).
- *   probs   [num_seqs][num_q_heads][idx_stride] f32 or NULL: the probability of
- *           each listed entry (0 for ignored entries).
- * Errors: INVALID, UNSUPPORTED, HIP.
+ *   probs   [num_seqs][num_q_heads][idx_stride] f32 or NULL: entry i < count
+ *           receives the probability of the listed position (0 for an ignored
+ *           entry); entries past the count are left untouched.
+ *   workspace: >= kvsel_sparse_workspace_bytes(num_seqs, num_q_heads,
+ *           head_dim, max_count) bytes of device memory.
+ * Errors: INVALID, UNSUPPORTED, WORKSPACE, HIP.
  * ------------------------------------------------------------------------ */
 int kvsel_sparse_attn(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads,
                       const int32_t* indices, int64_t idx_stride, const int32_t* counts,
                       int32_t idx_heads, int32_t max_count, float scale, float* out,
-                      float* probs, void* stream);
+                      float* probs, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t kvsel_sparse_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                    int32_t max_count);
 
 /* Name of a status code (static string). */
 const char* kvsel_status_string(int status);

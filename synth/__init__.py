@@ -104,7 +104,7 @@ def write_positions(pages: torch.Tensor, block_table_row: torch.Tensor, start: i
 
 def orthonormal_directions(n: int, d: int, gen: torch.Generator, device="cpu") -> torch.Tensor:
     """``n`` seeded orthonormal directions in R^d (rows), float32."""
-    a = torch.randn(d, n, generator=gen, dtype=torch.float64, device="cpu")
+    a = torch.randn(d, n, generator=gen, dtype=torch.float64, device=gen.device).cpu()
     qm, _ = torch.linalg.qr(a)
     return qm.T.contiguous().to(torch.float32).to(device)
 
@@ -151,7 +151,7 @@ def _bump_centres(L_prefix: int, n: int, gen: torch.Generator):
     assert hi - lo > n * 512, "sequence too short for disjoint bumps"
     centres = []
     while len(centres) < n:
-        c = int(torch.randint(lo, hi, (1,), generator=gen))
+        c = int(torch.randint(lo, hi, (1,), generator=gen, device=gen.device))
         if all(abs(c - x) >= 512 for x in centres):
             centres.append(c)
     return sorted(centres)

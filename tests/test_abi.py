@@ -121,3 +121,19 @@ def test_select_validation():
     assert call(**dict(g, max_len=9000, stride=9000, out_stride=9000)) == K.KVSEL_ERR_UNSUPPORTED
     assert lib.kvsel_select_workspace_bytes(4, 100, 1) >= 4 * 100 * 8
     assert lib.kvsel_select_workspace_bytes(4, 100, 0) == 0
+
+
+def test_sparse_validation():
+    lib = K.library()
+    kv = _kv()
+    def call(hq=32, idx=FAKE, cnt=FAKE, idx_heads=32, max_count=10, stride=16, out=FAKE, ws=FAKE, wsb=1 << 30, kvd=kv):
+        return lib.kvsel_sparse_attn(ctypes.byref(kvd), FAKE, hq, idx, stride, cnt, idx_heads, max_count, 0.1,
+                                     out, None, ws, wsb, None)
+    assert call(idx=None) == K.KVSEL_ERR_INVALID
+    assert call(out=None) == K.KVSEL_ERR_INVALID
+    assert call(idx_heads=5) == K.KVSEL_ERR_INVALID
+    assert call(max_count=20) == K.KVSEL_ERR_INVALID
+    assert call(kvd=_kv(v_pages=None)) == K.KVSEL_ERR_INVALID
+    assert call(hq=96, idx_heads=8) == K.KVSEL_ERR_UNSUPPORTED     # shared sets with G = 12
+    assert call(ws=None) == K.KVSEL_ERR_WORKSPACE
+    assert lib.kvsel_sparse_workspace_bytes(4, 32, 128, 2048) >= 4 * 32 * 8 * 128 * 4
