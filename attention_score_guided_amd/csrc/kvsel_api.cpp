@@ -299,4 +299,52 @@ int kvsel_sparse_attn(const kvsel_paged_kv* kv, const void* q, int32_t num_q_hea
   return hip_status(kvsel::launch_sparse(a, static_cast<hipStream_t>(stream)), "sparse_attn launch");
 }
 
+size_t kvsel_snapkv_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads, int32_t window) {
+  if (check_kv(kv, num_q_heads, false) != KVSEL_OK || window <= 0) return 0;
+  return kvsel::snapkv_workspace_bytes(kv->num_seqs, num_q_heads, window, kv->max_seq_len);
+}
+
+int kvsel_snapkv_vote(const kvsel_paged_kv* kv, const void* q_win, int32_t num_q_heads,
+                      int32_t window, int32_t pool_kernel, float scale, int32_t group_reduce,
+                      float* votes, int64_t votes_stride, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int st = check_kv(kv, num_q_heads, false);
+  if (st != KVSEL_OK) return st;
+  if (!q_win || !votes) return fail(KVSEL_ERR_INVALID, "NULL pointer argument");
+  if (window <= 0 || window >= kv->max_seq_len)
+    return fail(KVSEL_ERR_INVALID, "window %d must lie in [1, max_seq_len)", window);
+  if (pool_kernel <= 0 || pool_kernel % 2 == 0)
+    return fail(KVSEL_ERR_INVALID, "pool_kernel %d must be odd and positive", pool_kernel);
+  if (group_reduce != KVSEL_REDUCE_NONE && group_reduce != KVSEL_REDUCE_SUM)
+    return fail(KVSEL_ERR_INVALID, "group_reduce %d", group_reduce);
+  if (votes_stride < kv->max_seq_len) return fail(KVSEL_ERR_INVALID, "votes_stride < max_seq_len");
+  if (kv->dtype != KVSEL_BF16) return fail(KVSEL_ERR_UNSUPPORTED, "the vote runs on bf16 caches");
+  if (window > 64) return fail(KVSEL_ERR_UNSUPPORTED, "window %d > 64", window);
+  const size_t need = kvsel::snapkv_workspace_bytes(kv->num_seqs, num_q_heads, window, kv->max_seq_len);
+  if (!workspace || workspace_bytes < need)
+    return fail(KVSEL_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  st = check_device();
+  if (st != KVSEL_OK) return st;
+  kvsel::SnapkvArgs a{};
+  a.k_pages = kv->k_pages;
+  a.block_table = kv->block_table;
+  a.seq_lens = kv->seq_lens;
+  a.q_win = q_win;
+  a.num_seqs = kv->num_seqs;
+  a.num_kv_heads = kv->num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.head_dim = kv->head_dim;
+  a.page_size = kv->page_size;
+  a.max_pages = kv->max_pages_per_seq;
+  a.max_seq_len = kv->max_seq_len;
+  a.window = window;
+  a.pool_kernel = pool_kernel;
+  a.group_sum = group_reduce == KVSEL_REDUCE_SUM;
+  a.scale = scale;
+  a.votes = votes;
+  a.votes_stride = votes_stride;
+  a.workspace = workspace;
+  return hip_status(kvsel::launch_snapkv(a, static_cast<hipStream_t>(stream)), "snapkv_vote launch");
+}
+
 }  // extern "C"

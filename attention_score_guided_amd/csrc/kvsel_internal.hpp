@@ -81,4 +81,21 @@ struct SparseArgs {
 size_t sparse_workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int max_count);
 hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream);
 
+struct SnapkvArgs {
+  const void* k_pages;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const void* q_win;
+  int num_seqs, num_kv_heads, num_q_heads, head_dim, page_size, max_pages, max_seq_len;
+  int window, pool_kernel;
+  bool group_sum;
+  float scale;
+  float* votes;
+  int64_t votes_stride;
+  void* workspace;
+};
+
+size_t snapkv_workspace_bytes(int num_seqs, int num_q_heads, int window, int max_seq_len);
+hipError_t launch_snapkv(const SnapkvArgs& a, hipStream_t stream);
+
 }  // namespace kvsel

@@ -205,9 +205,10 @@ size_t kvsel_select_workspace_bytes(int32_t rows, int32_t max_len, int32_t mode)
  *   votes [num_seqs][H_kv or H_q][votes_stride] f32; positions
  *   j >= L_b - window are left untouched.  votes_stride >= max_seq_len.
  * Precondition: window < L_b for every sequence.
- * Errors: INVALID (window <= 0, window >= max_seq_len, even pool_kernel,
- * ...), UNSUPPORTED (dtype other than BF16, head_dim other than 128 or 64),
- * WORKSPACE, HIP.
+ *   workspace: >= kvsel_snapkv_workspace_bytes(kv, num_q_heads, window).
+ * Errors: INVALID (NULL pointers, window <= 0, window >= max_seq_len, even or
+ * non-positive pool_kernel, votes_stride < max_seq_len), UNSUPPORTED (dtype
+ * other than BF16, head_dim other than 64/128, window > 64), WORKSPACE, HIP.
  * ------------------------------------------------------------------------ */
 int kvsel_snapkv_vote(const kvsel_paged_kv* kv, const void* q_win, int32_t num_q_heads,
                       int32_t window, int32_t pool_kernel, float scale, int32_t group_reduce,

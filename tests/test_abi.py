@@ -137,3 +137,20 @@ def test_sparse_validation():
     assert call(hq=96, idx_heads=8) == K.KVSEL_ERR_UNSUPPORTED     # shared sets with G = 12
     assert call(ws=None) == K.KVSEL_ERR_WORKSPACE
     assert lib.kvsel_sparse_workspace_bytes(4, 32, 128, 2048) >= 4 * 32 * 8 * 128 * 4
+
+
+def test_snapkv_validation():
+    lib = K.library()
+    def call(kvd=None, window=32, pool=7, red=1, votes=FAKE, stride=1024, ws=FAKE, wsb=1 << 30):
+        kvd = kvd or _kv()
+        return lib.kvsel_snapkv_vote(ctypes.byref(kvd), FAKE, 32, window, pool, 0.1, red, votes, stride, ws, wsb, None)
+    assert call(votes=None) == K.KVSEL_ERR_INVALID
+    assert call(window=0) == K.KVSEL_ERR_INVALID
+    assert call(window=1024) == K.KVSEL_ERR_INVALID
+    assert call(pool=6) == K.KVSEL_ERR_INVALID
+    assert call(red=3) == K.KVSEL_ERR_INVALID
+    assert call(stride=100) == K.KVSEL_ERR_INVALID
+    assert call(kvd=_kv(dtype=K.KVSEL_F32)) == K.KVSEL_ERR_UNSUPPORTED
+    assert call(window=65) == K.KVSEL_ERR_UNSUPPORTED
+    assert call(ws=None) == K.KVSEL_ERR_WORKSPACE
+    assert lib.kvsel_snapkv_workspace_bytes(ctypes.byref(_kv()), 32, 32) > 2 * 32 * 1024 * 4
