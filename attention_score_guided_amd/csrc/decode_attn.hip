@@ -516,6 +516,93 @@ void decode_partial_mfma(PartialParams p) {
   }
 }
 
+// ---- bf16 logits-only pass (indexer scores) ---------------------------------
+// Emit raw scale * q.k for every key and up to 32 query heads of a KV head
+// per workgroup: NCT 16-column B tiles of Q^T share each K tile, so the K
+// stream is read once for the whole group.  No softmax, no V, no LDS tile.
+template <int D, int NCT>
+__global__ __launch_bounds__(kThreads) void decode_logits_mfma(PartialParams p) {
+  constexpr int NU = D / 32;
+  constexpr int QB = kQkBatch;
+  constexpr int GTL = 16 * NCT;
+  __shared__ int page_lds[KVSEL_MAX_CHUNK / 16 + 2];
+  const int C = p.chunk;
+  const int chunk_id = blockIdx.x;
+  const int kvh = blockIdx.y / p.hgroups;
+  const int hg = blockIdx.y % p.hgroups;
+  const int b = blockIdx.z;
+  const int L = p.seq_lens[b];
+  const int start = chunk_id * C;
+  if (start >= L) return;
+  const int n_keys = min(C, L - start);
+  const int n_heads = min(GTL, p.group - hg * GTL);    // real heads in this pass
+  const int h0 = kvh * p.group + hg * GTL;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int col = lane & 15, grp = lane >> 4;
+  const int P = 1 << p.page_log2;
+  const int first_page = start >> p.page_log2;
+  const int n_pages = ((start + n_keys - 1) >> p.page_log2) - first_page + 1;
+  for (int i = tid; i < n_pages; i += kThreads)
+    page_lds[i] = p.block_table[(size_t)b * p.max_pages + first_page + i];
+  bf16x8 qb[NCT][NU];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int hh = ct * 16 + col;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (hh < n_heads) w = ld16(p.q + (((size_t)b * p.num_q_heads + h0 + hh) * D + u * 32 + grp * 8) * 2);
+      qb[ct][u] = __builtin_bit_cast(bf16x8, w);
+    }
+  __syncthreads();
+  const size_t head_stride = (size_t)P * D * 2;
+  const size_t page_stride = head_stride * p.num_kv_heads;
+  const int per_wave = C / kWaves;
+  const int nt = per_wave / 16;
+  const int wbase = wave * per_wave;
+  const bool vec = (p.logits_stride & 3) == 0 && (reinterpret_cast<uintptr_t>(p.logits) & 15) == 0 &&
+                   n_keys == C;
+  for (int t0 = 0; t0 < nt; t0 += QB) {
+    bf16x8 kb[QB][NU];
+#pragma unroll
+    for (int t = 0; t < QB; ++t) {
+      const int key = min(wbase + min(t0 + t, nt - 1) * 16 + col, n_keys - 1);
+      const int j = start + key;
+      const int pg = page_lds[(j >> p.page_log2) - first_page];
+      const uint8_t* rp = p.k_pages + (size_t)pg * page_stride + kvh * head_stride +
+                          (size_t)(j & (P - 1)) * D * 2 + grp * 16;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) kb[t][u] = __builtin_bit_cast(bf16x8, ld_kv(rp + u * 64));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < QB; ++t) {
+      if (t0 + t < nt) {
+        const int k0 = wbase + (t0 + t) * 16 + grp * 4;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int u = 0; u < NU; ++u)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[t][u], qb[ct][u], acc, 0, 0, 0);
+          const int hh = ct * 16 + col;
+          if (hh < n_heads) {
+            float* lg = p.logits + ((size_t)b * p.num_q_heads + h0 + hh) * p.logits_stride + start;
+            if (vec) {
+              *reinterpret_cast<float4*>(lg + k0) =
+                  make_float4(acc[0] * p.scale, acc[1] * p.scale, acc[2] * p.scale, acc[3] * p.scale);
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (k0 + i < n_keys) lg[k0 + i] = acc[i] * p.scale;
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
 // ---- combine ----------------------------------------------------------------
 // One workgroup per (sequence, query head): global max M over the chunk
 // partials, weights w_c = exp(m_c - M), l = sum w_c l_c, out = sum w_c o_c / l,
@@ -779,6 +866,22 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   pp.n_chunks = pl.n_chunks;
   pp.scale = a.scale;
 
+  // Pure logits (indexer scores): the dedicated kernel serving up to 32 heads
+  // per K read.
+  if (a.bf16 && a.emit_logits && !a.out && !a.lse && !a.cum && a.probs) {
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const int nct = G > 16 ? 2 : 1;
+    pp.hgroups = (G + 16 * nct - 1) / (16 * nct);
+    const dim3 lgrid(pl.n_chunks, a.num_kv_heads * pp.hgroups, a.num_seqs);
+    if (a.head_dim == 128) {
+      if (nct == 2) hipLaunchKernelGGL((decode_logits_mfma<128, 2>), lgrid, dim3(kThreads), 0, stream, pp);
+      else hipLaunchKernelGGL((decode_logits_mfma<128, 1>), lgrid, dim3(kThreads), 0, stream, pp);
+    } else {
+      if (nct == 2) hipLaunchKernelGGL((decode_logits_mfma<64, 2>), lgrid, dim3(kThreads), 0, stream, pp);
+      else hipLaunchKernelGGL((decode_logits_mfma<64, 1>), lgrid, dim3(kThreads), 0, stream, pp);
+    }
+    return hipGetLastError();
+  }
   const dim3 grid(pl.n_chunks, a.num_kv_heads * pl.hgroups, a.num_seqs);
   const size_t lds = (size_t)pl.gt * pl.chunk * sizeof(float) +
                      (size_t)kWaves * pl.gt * a.head_dim * sizeof(float) +

@@ -26,8 +26,10 @@ namespace kvsel {
 
 namespace {
 
-constexpr int kSelThreads = 512;
-constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kSelThreads = 512;     // global-percentile kernels
+constexpr int kRowThreads = 1024;    // per-row select
+constexpr int kRowUnroll = 8;        // independent loads in flight per thread
+constexpr int kSubHist = 4;          // LDS sub-histograms (waves w, w+4, ... share one)
 
 // Order-preserving map from float to uint32 (larger float -> larger key);
 // -0.0 is folded onto +0.0 first.
@@ -36,9 +38,11 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive scan of one int per thread over the block; `total` receives the
-// block sum.  `ws` needs kSelWaves ints.  Every thread must call it.
+// Exclusive scan of one int per thread over the block of NT threads; `total`
+// receives the block sum.  `ws` needs NT / 64 ints.  Every thread must call it.
+template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* ws, int& total) {
+  constexpr int kSelWaves = NT / kWave;
   const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
   int x = v;
 #pragma unroll
@@ -60,11 +64,12 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* ws, int& total) 
   return before + x - v;
 }
 
-// Given a histogram of `nb` bins (nb a multiple of kSelThreads), find digit d
-// with count(bins > d) < rank <= count(bins >= d), rank >= 1.  Returns d and
-// sets `above` to count(bins > d).
+// Given a histogram of `nb` bins (nb a multiple of NT), find digit d with
+// count(bins > d) < rank <= count(bins >= d), rank >= 1.  Returns d and sets
+// `above` to count(bins > d).
+template <int NT>
 __device__ int find_digit(const int* hist, int nb, int rank, int* ws, int* res, int& above) {
-  const int per = nb / kSelThreads;
+  const int per = nb / NT;
   const int tid = threadIdx.x;
   // thread t owns bins [nb - (t+1)*per, nb - t*per): scanning threads in
   // order walks the bins from the top.
@@ -72,7 +77,7 @@ __device__ int find_digit(const int* hist, int nb, int rank, int* ws, int* res, 
   int local = 0;
   for (int i = 1; i <= per; ++i) local += hist[hi_bin - i];
   int total;
-  const int before = block_exclusive_scan(local, ws, total);  // bins above my range
+  const int before = block_exclusive_scan<NT>(local, ws, total);  // bins above my range
   int run = before;
   for (int i = 1; i <= per; ++i) {
     const int bin = hi_bin - i;
@@ -101,9 +106,10 @@ struct RowsParams {
   int32_t* out_count;
 };
 
-__global__ __launch_bounds__(kSelThreads) void select_rows_kernel(RowsParams p) {
-  __shared__ int hist[2048];
-  __shared__ int ws[kSelWaves];
+__global__ __launch_bounds__(kRowThreads) void select_rows_kernel(RowsParams p) {
+  constexpr int NT = kRowThreads;
+  __shared__ int hist[kSubHist][2048];
+  __shared__ int ws[NT / kWave];
   __shared__ int res[2];
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
@@ -118,7 +124,7 @@ __global__ __launch_bounds__(kSelThreads) void select_rows_kernel(RowsParams p) 
   const int k = keep_all ? 0 : max(0, B - fsize);
   if (k == 0) {
     // Everything, or exactly the forced positions [0, lo) and [hi, n).
-    for (int j = tid; j < n; j += kSelThreads) {
+    for (int j = tid; j < n; j += NT) {
       if (keep_all) out[j] = j;
       else if (j < lo) out[j] = j;
       else if (j >= hi) out[lo + (j - hi)] = j;
@@ -128,6 +134,9 @@ __global__ __launch_bounds__(kSelThreads) void select_rows_kernel(RowsParams p) 
   }
 
   // ---- radix select of the k-th largest key among positions [lo, hi) ------
+  // Each pass streams the middle with kRowUnroll independent loads in flight
+  // per thread and counts digits in one of kSubHist LDS histograms.
+  int* my_hist = hist[(tid / kWave) % kSubHist];
   uint32_t prefix = 0, pmask = 0;
   int rank = k;
   const int shifts[3] = {21, 10, 0};
@@ -137,15 +146,31 @@ __global__ __launch_bounds__(kSelThreads) void select_rows_kernel(RowsParams p) 
     const int sh = shifts[pass];
     const uint32_t dmask = (1u << widths[pass]) - 1u;
     const int nb = 1 << widths[pass];
-    for (int i = tid; i < 2048; i += kSelThreads) hist[i] = 0;
+    for (int i = tid; i < kSubHist * 2048; i += NT) (&hist[0][0])[i] = 0;
     __syncthreads();
-    for (int j = lo + tid; j < hi; j += kSelThreads) {
-      const uint32_t kk = order_key(row[j]);
-      if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> sh) & dmask], 1);
+    for (int j0 = lo + tid; j0 < hi; j0 += NT * kRowUnroll) {
+      float v[kRowUnroll];
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        const int j = j0 + u * NT;
+        v[u] = j < hi ? row[j] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        const uint32_t kk = order_key(v[u]);
+        if (j0 + u * NT < hi && (kk & pmask) == prefix) atomicAdd(&my_hist[(kk >> sh) & dmask], 1);
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < nb; i += NT) {
+      int c = 0;
+#pragma unroll
+      for (int h = 0; h < kSubHist; ++h) c += hist[h][i];
+      hist[0][i] = c;
     }
     __syncthreads();
     int above;
-    const int d = find_digit(hist, nb, rank, ws, res, above);
+    const int d = find_digit<NT>(hist[0], nb, rank, ws, res, above);
     rank -= above;
     prefix |= (uint32_t)d << sh;
     pmask |= dmask << sh;
@@ -155,21 +180,24 @@ __global__ __launch_bounds__(kSelThreads) void select_rows_kernel(RowsParams p) 
 
   // ---- ordered output pass -------------------------------------------------
   int tie_base = 0, out_base = 0;
-  for (int t0 = 0; t0 < n; t0 += kSelThreads * 4) {
+  for (int t0 = 0; t0 < n; t0 += NT * 4) {
     const int j0 = t0 + tid * 4;
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = (j0 + i < n) ? row[j0 + i] : 0.f;
     int eq[4], keep[4];
     int n_eq = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int j = j0 + i;
       const bool mid = j >= lo && j < hi;
-      const uint32_t kk = (j < n && mid) ? order_key(row[j]) : 0u;
+      const uint32_t kk = (j < n && mid) ? order_key(sv[i]) : 0u;
       eq[i] = (j < n && mid && kk == tau) ? 1 : 0;
       keep[i] = (j < n) ? ((!mid) || kk > tau ? 1 : 0) : 0;
       n_eq += eq[i];
     }
     int eq_total;
-    const int eq_before = tie_base + block_exclusive_scan(n_eq, ws, eq_total);
+    const int eq_before = tie_base + block_exclusive_scan<NT>(n_eq, ws, eq_total);
     int run = eq_before, n_keep = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -180,7 +208,7 @@ __global__ __launch_bounds__(kSelThreads) void select_rows_kernel(RowsParams p) 
       n_keep += keep[i];
     }
     int keep_total;
-    int pos = out_base + block_exclusive_scan(n_keep, ws, keep_total);
+    int pos = out_base + block_exclusive_scan<NT>(n_keep, ws, keep_total);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (keep[i]) out[pos++] = j0 + i;
@@ -251,14 +279,14 @@ __global__ __launch_bounds__(kSelThreads) void global_threshold_kernel(const uin
                                                                        int total, int K,
                                                                        uint64_t* thr) {
   __shared__ int hist[512];
-  __shared__ int ws[kSelWaves];
+  __shared__ int ws[kSelThreads / kWave];
   __shared__ int res[2];
   __shared__ int n_valid_s;
   const int tid = threadIdx.x;
   int cnt = 0;
   for (int i = tid; i < total; i += kSelThreads) cnt += comp[i] != 0ull;
   int n_valid;
-  block_exclusive_scan(cnt, ws, n_valid);
+  block_exclusive_scan<kSelThreads>(cnt, ws, n_valid);
   if (K >= n_valid || K <= 0) {
     if (tid == 0) thr[0] = K <= 0 ? ~0ull : 1ull;  // keep nothing / keep every item
     return;
@@ -276,7 +304,7 @@ __global__ __launch_bounds__(kSelThreads) void global_threshold_kernel(const uin
     }
     __syncthreads();
     int above;
-    const int d = find_digit(hist, 512, rank, ws, res, above);
+    const int d = find_digit<kSelThreads>(hist, 512, rank, ws, res, above);
     rank -= above;
     prefix |= (uint64_t)d << sh;
     pmask |= 0xffull << sh;
@@ -290,7 +318,7 @@ __global__ __launch_bounds__(kSelThreads) void global_output_kernel(const uint64
                                                                     int32_t* out_idx,
                                                                     int64_t out_stride,
                                                                     int32_t* out_count) {
-  __shared__ int ws[kSelWaves];
+  __shared__ int ws[kSelThreads / kWave];
   const int r = blockIdx.x;
   const uint64_t t = thr[0];
   const uint64_t* row = comp + (size_t)r * max_len;
@@ -306,7 +334,7 @@ __global__ __launch_bounds__(kSelThreads) void global_output_kernel(const uint64
       n_keep += keep[i];
     }
     int tot;
-    int pos = base + block_exclusive_scan(n_keep, ws, tot);
+    int pos = base + block_exclusive_scan<kSelThreads>(n_keep, ws, tot);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (keep[i]) out[pos++] = j0 + i;
@@ -330,7 +358,7 @@ hipError_t launch_select(const float* scores, int64_t stride, const int32_t* len
   if (mode == 0) {
     RowsParams rp{scores, stride, lengths, budgets, max_budget, sinks, window, out_idx, out_stride,
                   out_count};
-    hipLaunchKernelGGL(select_rows_kernel, dim3(rows), dim3(kSelThreads), 0, stream, rp);
+    hipLaunchKernelGGL(select_rows_kernel, dim3(rows), dim3(kRowThreads), 0, stream, rp);
     return hipGetLastError();
   }
   uint8_t* ws = static_cast<uint8_t*>(workspace);

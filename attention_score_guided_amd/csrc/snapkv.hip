@@ -8,15 +8,16 @@
 // The window logits are a real dense contraction: for one query head, the
 // W x d window queries against every key.  Each 16-key x 16-row tile is one
 // chain of v_mfma_f32_16x16x32_bf16 (keys as A rows, window rows as B
-// columns).  Two passes over K:
-//   pass 1  per (head, 256-key chunk): online (max, sum of exp) of every
-//           window row over the chunk's visible keys -> chunk partials;
+// columns).  One workgroup serves all G query heads of a KV head for a chunk
+// of 256 keys, so the chunk is fetched from HBM once per pass and reused by
+// the waves through the caches.  Two passes over K:
+//   pass 1  online (max, sum of exp) of every window row over the chunk's
+//           visible keys -> chunk partials, laid out [chunk][row];
 //   combine per window row: lse over the chunks;
-//   pass 2  per (head, chunk of prefix keys): recompute the tile,
-//           p = exp(s - lse), column sums over the head's rows (16-lane DPP
-//           reductions) -> per-head votes;
-//   pool    per output: sum the group's heads in head order, max over the
-//           pooling window.
+//   pass 2  recompute the tiles of the chunk plus a 16-key halo on each side,
+//           p = exp(s - lse), column sums over each head's rows (16-lane DPP
+//           reductions) into LDS, the group sum in head order, the max-pool,
+//           and the final votes of the chunk's prefix keys.
 // Every output element has one writer; there are no atomics.
 #include "device_common.hpp"
 #include "kvsel_internal.hpp"
@@ -30,20 +31,22 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kChunk = 256;             // keys per workgroup: 4 waves x 4 tiles of 16
-constexpr int kTilesPerWave = kChunk / (16 * kWaves);
+constexpr int kChunk = 256;             // keys per workgroup
+constexpr int kTiles = kChunk / 16;     // 16-key tiles per chunk
+constexpr int kHalo = 16;               // extra keys on each side for pooling (radius <= 16)
 
 struct VoteParams {
   const uint8_t* k_pages;
   const int32_t* block_table;
   const int32_t* seq_lens;
   const uint8_t* q_win;   // [B][Hq][W][D] bf16
-  int num_kv_heads, num_q_heads, window, page_log2, max_pages, n_chunks;
+  int num_kv_heads, num_q_heads, window, page_log2, max_pages, n_chunks, radius;
+  bool group_sum;
   float scale;
-  float2* part_ml;        // [B][Hq][W][n_chunks]
+  float2* part_ml;        // [B][Hq][n_chunks][W]
   const float* lse;       // [B][Hq][W]
-  float* head_votes;      // [B][Hq][hv_stride]
-  int64_t hv_stride;
+  float* votes;           // [B][H_out][votes_stride]
+  int64_t votes_stride;
 };
 
 __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2) {
@@ -53,191 +56,278 @@ __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2)
   m = mn;
 }
 
-template <int D, int RT, int PASS>
-__global__ __launch_bounds__(kThreads) void snapkv_pass(VoteParams p) {
-  constexpr int NU = D / 32;
-  __shared__ int page_lds[kChunk / 16 + 2];
-  __shared__ float2 wml[kWaves][RT * 16];
-
-  const int G = p.num_q_heads / p.num_kv_heads;
-  const int g = blockIdx.x;
-  const int chunk = blockIdx.y;
-  const int b = blockIdx.z / p.num_kv_heads;
-  const int kvh = blockIdx.z % p.num_kv_heads;
-  const int h = kvh * G + g;
-  const int L = p.seq_lens[b];
-  const int W = p.window;
-  const int prefix = L - W;
-  const int start = chunk * kChunk;
-  const int limit = PASS == 1 ? L : prefix;   // pass 2 only votes for prefix keys
-  if (start >= limit) return;
-  const int n_keys = min(kChunk, limit - start);
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int col = lane & 15, grp = lane >> 4;
-  const int P = 1 << p.page_log2;
-  const int first_page = start >> p.page_log2;
-  const int n_pages = ((start + n_keys - 1) >> p.page_log2) - first_page + 1;
-  for (int i = tid; i < n_pages; i += kThreads)
-    page_lds[i] = p.block_table[(size_t)b * p.max_pages + first_page + i];
-
-  // B operand: Q_win^T, column = window row rt*16 + col (zero past W).
-  bf16x8 qb[RT][NU];
+// Work split inside a workgroup: the G x T (head, tile) items of the chunk
+// are cut into 4 contiguous runs, one per wave, so a wave changes head (and
+// reloads its window queries) at most ceil(G / 4) times.
+template <int D, int RT>
+__device__ __forceinline__ void load_q(const VoteParams& p, int b, int h, int col, int grp,
+                                       bf16x8 (&qb)[RT][D / 32]) {
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int row = rt * 16 + col;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
+    for (int u = 0; u < D / 32; ++u) {
       uint4 w = make_uint4(0, 0, 0, 0);
-      if (row < W) w = ld16(p.q_win + ((((size_t)b * p.num_q_heads + h) * W + row) * D + u * 32 + grp * 8) * 2);
+      if (row < p.window)
+        w = ld16(p.q_win + ((((size_t)b * p.num_q_heads + h) * p.window + row) * D + u * 32 + grp * 8) * 2);
       qb[rt][u] = __builtin_bit_cast(bf16x8, w);
     }
   }
-  float lse_row[RT];
-  if constexpr (PASS == 2) {
+}
+
+// Logits of one 16-key tile (keys key0 .. key0+15, some possibly outside
+// [0, L)) against the head's window rows: s[rt][i] for key key0 + grp*4 + i
+// and row rt*16 + col, -inf where not visible.
+template <int D, int RT>
+__device__ __forceinline__ void tile_logits(const VoteParams& p, const int* page_lds, int first_page,
+                                            int b, int kvh, int L, int key0, int col, int grp,
+                                            const bf16x8 (&qb)[RT][D / 32], float (&s)[RT][4]) {
+  constexpr int NU = D / 32;
+  const int P = 1 << p.page_log2;
+  const size_t head_stride = (size_t)P * D * 2;
+  const size_t page_stride = head_stride * p.num_kv_heads;
+  const int key = min(max(key0 + col, 0), L - 1);     // clamped: every load in bounds
+  const int pg = page_lds[(key >> p.page_log2) - first_page];
+  const uint8_t* rp = p.k_pages + (size_t)pg * page_stride + kvh * head_stride +
+                      (size_t)(key & (P - 1)) * D * 2 + grp * 16;
+  bf16x8 ka[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) ka[u] = __builtin_bit_cast(bf16x8, ld16_stream(rp + u * 64));
+  const int prefix = L - p.window;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < NU; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u], qb[rt][u], acc, 0, 0, 0);
+    const int row = rt * 16 + col;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = key0 + grp * 4 + i;
+      const bool vis = j >= 0 && j < L && row < p.window && j <= prefix + row;
+      s[rt][i] = vis ? acc[i] * p.scale : kNegInf;
+    }
+  }
+}
+
+// Pass 1: per (chunk, sequence, KV head), the online (max, sum of exp) of
+// every window row of every head of the group over the chunk's keys.
+template <int D, int RT>
+__global__ __launch_bounds__(kThreads) void snapkv_pass1(VoteParams p) {
+  constexpr int NU = D / 32;
+  __shared__ int page_lds[kChunk / 16 + 2];
+  extern __shared__ float2 wml[];            // [G][kWaves][RT*16]
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int chunk = blockIdx.x;
+  const int b = blockIdx.y / p.num_kv_heads, kvh = blockIdx.y % p.num_kv_heads;
+  const int L = p.seq_lens[b];
+  const int start = chunk * kChunk;
+  if (start >= L) return;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int col = lane & 15, grp = lane >> 4;
+  const int first_page = start >> p.page_log2;
+  const int last_key = min(L, start + kChunk) - 1;
+  const int n_pages = (last_key >> p.page_log2) - first_page + 1;
+  for (int i = tid; i < n_pages; i += kThreads)
+    page_lds[i] = p.block_table[(size_t)b * p.max_pages + first_page + i];
+  for (int i = tid; i < G * kWaves * RT * 16; i += kThreads) wml[i] = make_float2(kNegInf, 0.f);
+  __syncthreads();
+
+  const int items = G * kTiles;
+  const int per = (items + kWaves - 1) / kWaves;
+  const int i0 = wave * per, i1 = min(items, i0 + per);
+  int cur_h = -1;
+  bf16x8 qb[RT][NU];
+  float m_run[RT], l_run[RT];
+  for (int it = i0; it < i1; ++it) {
+    const int g = it / kTiles, t = it % kTiles;
+    if (g != cur_h) {
+      if (cur_h >= 0) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          for (int off = 16; off < kWave; off *= 2)
+            merge_ml(m_run[rt], l_run[rt], __shfl_xor(m_run[rt], off, kWave), __shfl_xor(l_run[rt], off, kWave));
+          if (grp == 0) wml[(cur_h * kWaves + wave) * RT * 16 + rt * 16 + col] = make_float2(m_run[rt], l_run[rt]);
+        }
+      }
+      cur_h = g;
+      load_q<D, RT>(p, b, kvh * G + g, col, grp, qb);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) { m_run[rt] = kNegInf; l_run[rt] = 0.f; }
+    }
+    float s[RT][4];
+    tile_logits<D, RT>(p, page_lds, first_page, b, kvh, L, start + t * 16, col, grp, qb, s);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const int row = rt * 16 + col;
-      lse_row[rt] = row < W ? p.lse[((size_t)b * p.num_q_heads + h) * W + row] * kLog2e : 0.f;
+      const float tmax = fmaxf(fmaxf(s[rt][0], s[rt][1]), fmaxf(s[rt][2], s[rt][3]));
+      const float mn = fmaxf(m_run[rt], tmax);
+      if (mn != kNegInf) {
+        const float ms = mn * kLog2e;
+        float add = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) add += exp2_hw(fmaf(s[rt][i], kLog2e, -ms));
+        l_run[rt] = l_run[rt] * exp2_hw(fmaf(m_run[rt], kLog2e, -ms)) + add;
+        m_run[rt] = mn;
+      }
+    }
+  }
+  if (cur_h >= 0) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      for (int off = 16; off < kWave; off *= 2)
+        merge_ml(m_run[rt], l_run[rt], __shfl_xor(m_run[rt], off, kWave), __shfl_xor(l_run[rt], off, kWave));
+      if (grp == 0) wml[(cur_h * kWaves + wave) * RT * 16 + rt * 16 + col] = make_float2(m_run[rt], l_run[rt]);
     }
   }
   __syncthreads();
-
-  const size_t head_stride = (size_t)P * D * 2;
-  const size_t page_stride = head_stride * p.num_kv_heads;
-  float m_run[RT], l_run[RT];
+  // merge the waves of each (head, row) in wave order; coalesced [chunk][row] writes
+  for (int i = tid; i < G * p.window; i += kThreads) {
+    const int g = i / p.window, row = i % p.window;
+    float m = kNegInf, l = 0.f;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) { m_run[rt] = kNegInf; l_run[rt] = 0.f; }
-
-  bf16x8 ka[kTilesPerWave][NU];
-#pragma unroll
-  for (int t = 0; t < kTilesPerWave; ++t) {
-    const int kl = min(wave * kTilesPerWave * 16 + t * 16 + col, n_keys - 1);
-    const int j = start + kl;
-    const int pg = page_lds[(j >> p.page_log2) - first_page];
-    const uint8_t* rp = p.k_pages + (size_t)pg * page_stride + kvh * head_stride +
-                        (size_t)(j & (P - 1)) * D * 2 + grp * 16;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) ka[t][u] = __builtin_bit_cast(bf16x8, ld16_stream(rp + u * 64));
-  }
-#pragma unroll
-  for (int t = 0; t < kTilesPerWave; ++t) {
-    const int k0 = wave * kTilesPerWave * 16 + t * 16 + grp * 4;   // chunk-local key of acc[0]
-    float colsum[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < NU; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t][u], qb[rt][u], acc, 0, 0, 0);
-      const int row = rt * 16 + col;
-      float s[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = start + k0 + i;
-        // visible: a real key, a real window row, causal (j <= L - W + row)
-        const bool vis = (k0 + i < n_keys) && row < W && j <= prefix + row;
-        s[i] = vis ? acc[i] * p.scale : kNegInf;
-      }
-      if constexpr (PASS == 1) {
-        const float tmax = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-        const float mn = fmaxf(m_run[rt], tmax);
-        if (mn != kNegInf) {
-          const float ms = mn * kLog2e;
-          float add = 0.f;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) add += exp2_hw(fmaf(s[i], kLog2e, -ms));
-          l_run[rt] = l_run[rt] * exp2_hw(fmaf(m_run[rt], kLog2e, -ms)) + add;
-          m_run[rt] = mn;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) colsum[i] += exp2_hw(fmaf(s[i], kLog2e, -lse_row[rt]));
-      }
+    for (int w = 0; w < kWaves; ++w) {
+      const float2 v = wml[(g * kWaves + w) * RT * 16 + row];
+      merge_ml(m, l, v.x, v.y);
     }
-    if constexpr (PASS == 2) {
-      // sum over the 16 window rows held by the lanes of this DPP row
-#pragma unroll
-      for (int i = 0; i < 4; ++i) colsum[i] = group_sum<16>(colsum[i]);
-      if (col == 0) {
-        float* hv = p.head_votes + ((size_t)b * p.num_q_heads + h) * p.hv_stride + start;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (k0 + i < n_keys) hv[k0 + i] = colsum[i];
-      }
-    }
-  }
-
-  if constexpr (PASS == 1) {
-    // merge the key groups (lanes 16 apart hold other keys of the same rows)
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      for (int off = 16; off < kWave; off *= 2) {
-        const float m2 = __shfl_xor(m_run[rt], off, kWave);
-        const float l2 = __shfl_xor(l_run[rt], off, kWave);
-        merge_ml(m_run[rt], l_run[rt], m2, l2);
-      }
-      if (grp == 0) wml[wave][rt * 16 + col] = make_float2(m_run[rt], l_run[rt]);
-    }
-    __syncthreads();
-    if (tid < W) {
-      float m = kNegInf, l = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) merge_ml(m, l, wml[w][tid].x, wml[w][tid].y);
-      p.part_ml[(((size_t)b * p.num_q_heads + h) * W + tid) * p.n_chunks + chunk] = make_float2(m, l);
-    }
+    const int h = kvh * G + g;
+    p.part_ml[(((size_t)b * p.num_q_heads + h) * p.n_chunks + chunk) * p.window + row] = make_float2(m, l);
   }
 }
 
-// lse of every window row from its chunk partials (chunks past the row's
-// last visible key were not launched or hold (-inf, 0)).
+// lse of every window row: one workgroup per (sequence, query head); 8
+// threads per row merge interleaved chunks, then each other.
 __global__ __launch_bounds__(256) void snapkv_lse(const float2* part_ml, const int32_t* seq_lens,
-                                                  int num_q_heads, int window, int n_chunks,
-                                                  int total_rows, float* lse) {
-  const int r = blockIdx.x * 256 + threadIdx.x;
-  if (r >= total_rows) return;
-  const int b = r / (num_q_heads * window);
-  const int L = seq_lens[b];
-  const int nc = (L + kChunk - 1) / kChunk;
-  float m = kNegInf, l = 0.f;
-  const float2* ml = part_ml + (size_t)r * n_chunks;
-  for (int c = 0; c < nc; ++c) merge_ml(m, l, ml[c].x, ml[c].y);
-  lse[r] = m + log2_hw(l) * kLn2;
-}
-
-// votes[b][g][j] = max over |t| <= r of v(j + t), v = head vote summed over the
-// group (SUM) or the head's own vote (NONE); j < L - W; padding ignored.
-__global__ __launch_bounds__(256) void snapkv_pool(const float* head_votes, int64_t hv_stride,
-                                                   const int32_t* seq_lens, int num_q_heads,
-                                                   int num_out_heads, int group, int window,
-                                                   int radius, float* votes, int64_t votes_stride) {
-  const int b = blockIdx.z, og = blockIdx.y;
-  const int n = seq_lens[b] - window;
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= n) return;
-  const int h0 = og * group;
-  const float* hv = head_votes + ((size_t)b * num_q_heads + h0) * hv_stride;
-  float best = kNegInf;
-  for (int t = max(0, j - radius); t <= min(n - 1, j + radius); ++t) {
-    float v = 0.f;
-    for (int gg = 0; gg < group; ++gg) v += hv[(size_t)gg * hv_stride + t];
-    best = fmaxf(best, v);
+                                                  int num_q_heads, int window, int n_chunks, float* lse) {
+  const int bh = blockIdx.x;
+  const int b = bh / num_q_heads;
+  const int nc = (seq_lens[b] + kChunk - 1) / kChunk;
+  const int row = threadIdx.x / 8, part = threadIdx.x % 8;
+  for (int r0 = 0; r0 < window; r0 += 32) {
+    const int r = r0 + row;
+    float m = kNegInf, l = 0.f;
+    if (r < window) {
+      const float2* ml = part_ml + (size_t)bh * n_chunks * window + r;
+      for (int c = part; c < nc; c += 8) merge_ml(m, l, ml[(size_t)c * window].x, ml[(size_t)c * window].y);
+    }
+    for (int off = 1; off < 8; off *= 2) merge_ml(m, l, __shfl_xor(m, off, 8), __shfl_xor(l, off, 8));
+    if (r < window && part == 0) lse[(size_t)bh * window + r] = m + log2_hw(l) * kLn2;
   }
-  votes[((size_t)b * num_out_heads + og) * votes_stride + j] = best;
 }
 
-template <int D, int RT, int PASS>
-void launch_pass(const VoteParams& vp, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((snapkv_pass<D, RT, PASS>), grid, dim3(kThreads), 0, s, vp);
+// Pass 2: per (chunk, sequence, KV head): p = exp(s - lse) for every window
+// row, column sums per head over the chunk's keys plus a halo on each side,
+// the group sum in head order, then the max-pool; writes the final votes of
+// the chunk's prefix keys.
+template <int D, int RT>
+__global__ __launch_bounds__(kThreads) void snapkv_pass2(VoteParams p) {
+  constexpr int NU = D / 32;
+  constexpr int NK = kChunk + 2 * kHalo;               // keys with votes computed
+  constexpr int NT = NK / 16;                          // tiles incl. the two halo tiles
+  __shared__ int page_lds[NK / 16 + 2];
+  extern __shared__ float hv[];                        // [G][NK] per-head votes
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int chunk = blockIdx.x;
+  const int b = blockIdx.y / p.num_kv_heads, kvh = blockIdx.y % p.num_kv_heads;
+  const int L = p.seq_lens[b];
+  const int prefix = L - p.window;
+  const int start = chunk * kChunk;
+  if (start >= prefix) return;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int col = lane & 15, grp = lane >> 4;
+  const int kbase = start - kHalo;                     // key of hv[.][0]
+  const int lo_key = max(kbase, 0), hi_key = min(kbase + NK, L) - 1;
+  const int first_page = lo_key >> p.page_log2;
+  const int n_pages = (hi_key >> p.page_log2) - first_page + 1;
+  for (int i = tid; i < n_pages; i += kThreads)
+    page_lds[i] = p.block_table[(size_t)b * p.max_pages + first_page + i];
+  __syncthreads();
+
+  const int items = G * NT;
+  const int per = (items + kWaves - 1) / kWaves;
+  const int i0 = wave * per, i1 = min(items, i0 + per);
+  int cur_h = -1;
+  bf16x8 qb[RT][NU];
+  float lrow[RT];
+  for (int it = i0; it < i1; ++it) {
+    const int g = it / NT, t = it % NT;
+    if (g != cur_h) {
+      cur_h = g;
+      const int h = kvh * G + g;
+      load_q<D, RT>(p, b, h, col, grp, qb);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int row = rt * 16 + col;
+        lrow[rt] = row < p.window ? p.lse[((size_t)b * p.num_q_heads + h) * p.window + row] * kLog2e : 0.f;
+      }
+    }
+    float s[RT][4];
+    tile_logits<D, RT>(p, page_lds, first_page, b, kvh, L, kbase + t * 16, col, grp, qb, s);
+    float cs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cs[i] += exp2_hw(fmaf(s[rt][i], kLog2e, -lrow[rt]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cs[i] = group_sum<16>(cs[i]);
+    if (col == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hv[g * NK + t * 16 + grp * 4 + i] = cs[i];
+    }
+  }
+  __syncthreads();
+  // group sum (head order) or per head, then the max-pool over [0, prefix)
+  const int n_out = p.group_sum ? 1 : G;
+  for (int i = tid; i < n_out * kChunk; i += kThreads) {
+    const int og = i / kChunk, jl = i % kChunk;
+    const int j = start + jl;
+    if (j >= prefix) continue;
+    float best = kNegInf;
+    for (int t = max(0, j - p.radius); t <= min(prefix - 1, j + p.radius); ++t) {
+      const int x = t - kbase;
+      float v;
+      if (p.group_sum) {
+        v = 0.f;
+        for (int g = 0; g < G; ++g) v += hv[g * NK + x];
+      } else {
+        v = hv[og * NK + x];
+      }
+      best = fmaxf(best, v);
+    }
+    const int out_h = p.group_sum ? kvh : kvh * G + og;
+    const int out_heads = p.group_sum ? p.num_kv_heads : p.num_q_heads;
+    p.votes[((size_t)b * out_heads + out_h) * p.votes_stride + j] = best;
+  }
 }
 
-template <int D, int PASS>
-hipError_t launch_pass_rt(const VoteParams& vp, int rt, dim3 grid, hipStream_t s) {
+template <int D>
+hipError_t launch_passes(const VoteParams& vp, int rt, dim3 grid, float* lse, float2* part_ml,
+                         const int32_t* seq_lens, int B, hipStream_t s) {
+  const int G = vp.num_q_heads / vp.num_kv_heads;
+  const size_t lds1 = (size_t)G * kWaves * rt * 16 * sizeof(float2);
+  const size_t lds2 = (size_t)G * (kChunk + 2 * kHalo) * sizeof(float);
+#define KVSEL_P1(R) hipLaunchKernelGGL((snapkv_pass1<D, R>), grid, dim3(kThreads), lds1, s, vp)
+#define KVSEL_P2(R) hipLaunchKernelGGL((snapkv_pass2<D, R>), grid, dim3(kThreads), lds2, s, vp)
   switch (rt) {
-    case 1: launch_pass<D, 1, PASS>(vp, grid, s); break;
-    case 2: launch_pass<D, 2, PASS>(vp, grid, s); break;
-    case 3: launch_pass<D, 3, PASS>(vp, grid, s); break;
-    case 4: launch_pass<D, 4, PASS>(vp, grid, s); break;
+    case 1: KVSEL_P1(1); break;
+    case 2: KVSEL_P1(2); break;
+    case 3: KVSEL_P1(3); break;
+    case 4: KVSEL_P1(4); break;
     default: return hipErrorInvalidValue;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(snapkv_lse, dim3(B * vp.num_q_heads), dim3(256), 0, s, part_ml, seq_lens,
+                     vp.num_q_heads, vp.window, vp.n_chunks, lse);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (rt) {
+    case 1: KVSEL_P2(1); break;
+    case 2: KVSEL_P2(2); break;
+    case 3: KVSEL_P2(3); break;
+    case 4: KVSEL_P2(4); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef KVSEL_P1
+#undef KVSEL_P2
   return hipGetLastError();
 }
 
@@ -248,8 +338,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 size_t snapkv_workspace_bytes(int num_seqs, int num_q_heads, int window, int max_seq_len) {
   const int n_chunks = (max_seq_len + kChunk - 1) / kChunk;
   const size_t rows = (size_t)num_seqs * num_q_heads * window;
-  return align256(rows * n_chunks * sizeof(float2)) + align256(rows * sizeof(float)) +
-         align256((size_t)num_seqs * num_q_heads * max_seq_len * sizeof(float));
+  return align256(rows * n_chunks * sizeof(float2)) + align256(rows * sizeof(float));
 }
 
 hipError_t launch_snapkv(const SnapkvArgs& a, hipStream_t stream) {
@@ -258,7 +347,6 @@ hipError_t launch_snapkv(const SnapkvArgs& a, hipStream_t stream) {
   uint8_t* ws = static_cast<uint8_t*>(a.workspace);
   float2* part_ml = reinterpret_cast<float2*>(ws);
   float* lse = reinterpret_cast<float*>(ws + align256(rows * n_chunks * sizeof(float2)));
-  float* head_votes = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(lse) + align256(rows * sizeof(float)));
   VoteParams vp{};
   vp.k_pages = static_cast<const uint8_t*>(a.k_pages);
   vp.block_table = a.block_table;
@@ -270,30 +358,17 @@ hipError_t launch_snapkv(const SnapkvArgs& a, hipStream_t stream) {
   vp.page_log2 = __builtin_ctz((unsigned)a.page_size);
   vp.max_pages = a.max_pages;
   vp.n_chunks = n_chunks;
+  vp.radius = a.pool_kernel / 2;
+  vp.group_sum = a.group_sum;
   vp.scale = a.scale;
   vp.part_ml = part_ml;
   vp.lse = lse;
-  vp.head_votes = head_votes;
-  vp.hv_stride = a.max_seq_len;
-  const int G = a.num_q_heads / a.num_kv_heads;
+  vp.votes = a.votes;
+  vp.votes_stride = a.votes_stride;
   const int rt = (a.window + 15) / 16;
-  const dim3 grid(G, n_chunks, a.num_seqs * a.num_kv_heads);
-  hipError_t e = a.head_dim == 128 ? launch_pass_rt<128, 1>(vp, rt, grid, stream)
-                                   : launch_pass_rt<64, 1>(vp, rt, grid, stream);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(snapkv_lse, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, part_ml,
-                     a.seq_lens, a.num_q_heads, a.window, n_chunks, (int)rows, lse);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  e = a.head_dim == 128 ? launch_pass_rt<128, 2>(vp, rt, grid, stream)
-                        : launch_pass_rt<64, 2>(vp, rt, grid, stream);
-  if (e != hipSuccess) return e;
-  const int out_heads = a.group_sum ? a.num_kv_heads : a.num_q_heads;
-  const dim3 pgrid((a.max_seq_len + 255) / 256, out_heads, a.num_seqs);
-  hipLaunchKernelGGL(snapkv_pool, pgrid, dim3(256), 0, stream, head_votes, (int64_t)a.max_seq_len,
-                     a.seq_lens, a.num_q_heads, out_heads, a.group_sum ? G : 1, a.window,
-                     a.pool_kernel / 2, a.votes, a.votes_stride);
-  return hipGetLastError();
+  const dim3 grid(n_chunks, a.num_seqs * a.num_kv_heads);
+  return a.head_dim == 128 ? launch_passes<128>(vp, rt, grid, lse, part_ml, a.seq_lens, a.num_seqs, stream)
+                           : launch_passes<64>(vp, rt, grid, lse, part_ml, a.seq_lens, a.num_seqs, stream);
 }
 
 }  // namespace kvsel

@@ -200,6 +200,168 @@ def counters_mode(torch, K, synth) -> int:
     return 0
 
 
+def timed(torch, fn, reps: int, warmup: int = 1) -> float:
+    """Average milliseconds of ``fn`` over ``reps`` runs (HIP events on the
+    current stream, after ``warmup`` untimed runs)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def long_context_workload(torch, K, synth, args) -> dict:
+    """128K case: B=4, 32/8 heads, d=128, bf16, page 16, L=131072, planted
+    sinks and hot regions.  (i) SnapKV vote (window 32, pool 7, group sum)
+    and the top-4096 per KV head; (ii) sparse decode steps: the one-head
+    d=64 indexer in logits mode, top-2048 per query head, sparse attention;
+    (iii) dense decode over the same cache (out only) for comparison."""
+    Bq, HQq, HKVq, Lq, W = 4, 32, 8, 131072, 32
+    steps = args.steps
+    cfg = synth.long_context_128k(seq_len=Lq, sparse_steps=steps, device="cuda")
+    kvt, kit = cfg["kv"], cfg["kv_index"]
+    cap = Lq + steps
+    kv_k = K.PagedKV(kvt.k_pages, None, kvt.block_table, kvt.seq_lens, 16, Lq)
+    votes = torch.zeros((Bq, HKVq, Lq), device="cuda")
+    ws_v = torch.empty(K.snapkv_workspace_bytes(kv_k, HQq, W), dtype=torch.uint8, device="cuda")
+    vrows = votes.view(Bq * HKVq, Lq)
+    vlens = torch.full((Bq * HKVq,), Lq - W, dtype=torch.int32, device="cuda")
+    vkeep = torch.empty((Bq * HKVq, 4096), dtype=torch.int32, device="cuda")
+    vcnt = torch.empty((Bq * HKVq,), dtype=torch.int32, device="cuda")
+
+    def vote():
+        K.snapkv_vote(kv_k, cfg["q_win"], HQq, W, 7, cfg["scale"], K.REDUCE_SUM, votes, workspace=ws_v)
+
+    def vote_select():
+        vote()
+        K.select_keep(vrows, vlens, Lq - W, 0, 0, None, 4096, vkeep, vcnt)
+
+    t_vote = timed(torch, vote, 5)
+    t_vote_sel = timed(torch, vote_select, 5)
+    k_bytes = Bq * HKVq * Lq * 128 * 2
+    vote_flops = 2 * (2.0 * Bq * HQq * W * Lq * 128)       # two passes of Q_win K^T
+
+    # sparse decode steps: lengths grow by one per step (the K/V were drawn ahead)
+    lens = kvt.seq_lens.clone()
+    kv_i = K.PagedKV(kit.k_pages, None, kit.block_table, lens, 16, cap)
+    kv_f = K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, lens, 16, cap)
+    scores = torch.empty((Bq, HQq, cap), device="cuda")
+    srows = scores.view(Bq * HQq, cap)
+    slens = torch.empty((Bq * HQq,), dtype=torch.int32, device="cuda")
+    keep = torch.empty((Bq * HQq, 2048), dtype=torch.int32, device="cuda")
+    kcnt = torch.empty((Bq * HQq,), dtype=torch.int32, device="cuda")
+    out = torch.empty((Bq, HQq, 128), device="cuda")
+    ws_d = torch.empty(K.decode_workspace_bytes(kv_i, HQq, True), dtype=torch.uint8, device="cuda")
+    ws_s = torch.empty(K.sparse_workspace_bytes(Bq, HQq, 128, 2048), dtype=torch.uint8, device="cuda")
+
+    def sparse_step(s):
+        lens.fill_(Lq + s + 1)
+        slens.fill_(Lq + s + 1)
+        K.decode_attn_scores(kv_i, cfg["qi_dec"][s], HQq, 1.0, None, None, scores, K.EMIT_LOGITS,
+                             workspace=ws_d)
+        K.select_keep(srows, slens, cap, 0, 0, None, 2048, keep, kcnt)
+        K.sparse_attn(kv_f, cfg["q_dec"][s], HQq, keep.view(Bq, HQq, 2048), kcnt.view(Bq, HQq), 2048,
+                      cfg["scale"], out, workspace=ws_s)
+
+    sparse_step(0)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for s in range(steps):
+        sparse_step(s)
+    b.record()
+    torch.cuda.synchronize()
+    t_sparse = a.elapsed_time(b) / steps
+    sparse_bytes = (Bq * Lq * 64 * 2) + 2 * Bq * HQq * Lq * 4 + Bq * HQq * 2048 * 128 * 2 * 2
+
+    # dense decode over the same cache (out only; the current token included)
+    lens.fill_(Lq)
+    ws_dd = torch.empty(K.decode_workspace_bytes(kv_f, HQq, True), dtype=torch.uint8, device="cuda")
+    q0 = cfg["q_dec"][0]
+    t_dense = timed(torch, lambda: K.decode_attn_scores(kv_f, q0, HQq, cfg["scale"], out, None, None,
+                                                        K.EMIT_PROBS, None, 1.0, workspace=ws_dd), 10)
+    dense_bytes = Bq * HKVq * Lq * 128 * 2 * 2
+    return {
+        "metric": "KV GB/s (% HBM peak) for score-emitting decode attn + keep-set select",
+        "value": round(dense_bytes / (t_dense * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": steps, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "long_context_128k", "batch": Bq, "seq_len": Lq, "q_heads": HQq,
+                   "kv_heads": HKVq, "head_dim": 128, "page_size": 16, "window": W, "pool_kernel": 7,
+                   "vote_top_k": 4096, "index_top_k": 2048},
+        "dense_decode_us": round(t_dense * 1e3, 1),
+        "vote": {"us": round(t_vote * 1e3, 1), "us_with_top4096": round(t_vote_sel * 1e3, 1),
+                 "k_gb_per_s": round(k_bytes / (t_vote * 1e-3) / 1e9, 1),
+                 "mfma_tflops": round(vote_flops / (t_vote * 1e-3) / 1e12, 1),
+                 "mfma_util_vs_2500_tflops": round(vote_flops / (t_vote * 1e-3) / 2.5e15, 4)},
+        "sparse_step": {"us": round(t_sparse * 1e3, 1),
+                        "gb_per_s": round(sparse_bytes / (t_sparse * 1e-3) / 1e9, 1),
+                        "bytes": sparse_bytes},
+    }
+
+
+def llama3_workload(torch, K, synth, args) -> dict:
+    """Llama-3-8B-shape layer, B=16, ragged L_b ~ U[8K, 32K]: ``steps``
+    decode steps, each appending a token, with the H2O accumulation fused
+    (probabilities not emitted); then block aggregation (16: max and mean)
+    and the keep set of 20% per (sequence, KV head) with sinks 4 and window
+    512."""
+    steps = args.steps
+    cfg = synth.llama3_8b_layer(steps=steps, device="cuda")
+    kvt = cfg["kv"]
+    Bq, HQq, HKVq = 16, 32, 8
+    base = kvt.seq_lens.clone()
+    cap = int(base.max()) + steps
+    lens = base.clone()
+    kv = K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, lens, 16, cap)
+    cum = torch.zeros((Bq, HKVq, cap), device="cuda")
+    out = torch.empty((Bq, HQq, 128), device="cuda")
+    ws = torch.empty(K.decode_workspace_bytes(kv, HQq, False), dtype=torch.uint8, device="cuda")
+    n_blk = -(-cap // 16)
+    bmax = torch.zeros((Bq, HKVq, n_blk), device="cuda")
+    bmean = torch.zeros((Bq, HKVq, n_blk), device="cuda")
+    rows = cum.view(Bq * HKVq, cap)
+    final = (base + steps).to(torch.int32)
+    rlens = final.repeat_interleave(HKVq).to(torch.int32)
+    budgets = (rlens.double() * 0.2).floor().to(torch.int32)
+    mb = int(budgets.max())
+    keep = torch.empty((Bq * HKVq, mb), dtype=torch.int32, device="cuda")
+    kcnt = torch.empty((Bq * HKVq,), dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    a, b, c = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    a.record()
+    for s in range(steps):
+        lens.copy_(base + s + 1)
+        K.decode_attn_scores(kv, cfg["q_steps"][s], HQq, cfg["scale"], out, None, None, K.EMIT_PROBS,
+                             cum, 1.0, workspace=ws)
+    b.record()
+    K.block_aggregate(cum, final, cap, 16, K.REDUCE_NONE, False, bmax, bmean)
+    K.select_keep(rows, rlens, cap, 4, 512, budgets, mb, keep, kcnt)
+    c.record()
+    torch.cuda.synchronize()
+    t_dec = a.elapsed_time(b) / steps
+    t_sel = b.elapsed_time(c)
+    # keys read per step, averaged over the steps (each step appends one token)
+    mean_keys = sum(int(L) for L in base.tolist()) + Bq * (steps + 1) / 2.0
+    kv_bytes = mean_keys * HKVq * 128 * 2 * 2
+    mass = float(cum.double().sum()) / Bq
+    return {
+        "metric": "KV GB/s (% HBM peak) for score-emitting decode attn + keep-set select",
+        "value": round(kv_bytes / (t_dec * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": steps, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "llama3_8b_steps", "batch": Bq, "seq_len": "U[8192,32768]",
+                   "q_heads": HQq, "kv_heads": HKVq, "head_dim": 128, "page_size": 16,
+                   "block_size": 16, "keep": "0.2 L (sinks 4, window 512)"},
+        "decode_us_per_step": round(t_dec * 1e3, 1),
+        "aggregate_and_select_us": round(t_sel * 1e3, 1),
+        "prob_mass_per_seq": round(mass, 3),
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,6 +372,9 @@ def main() -> int:
                     help="replay each part of the step as a captured HIP graph (measured slower than "
                          "eager launches on this path)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--workload", default="llama70b_step",
+                    choices=["llama70b_step", "long_context_128k", "llama3_8b_steps"],
+                    help="the default is the 70B decode step; the others report their own line")
     ap.add_argument("--counters", action="store_true",
                     help="counter-collection mode: one layer, 3 decode calls, then a plain 1 GiB "
                          "device copy used to calibrate FETCH_SIZE / WRITE_SIZE; prints no JSON")
@@ -228,6 +393,12 @@ def main() -> int:
 
     if args.counters:
         return counters_mode(torch, K, synth)
+    if args.workload == "long_context_128k":
+        print(json.dumps(long_context_workload(torch, K, synth, args)), flush=True)
+        return 0
+    if args.workload == "llama3_8b_steps":
+        print(json.dumps(llama3_workload(torch, K, synth, args)), flush=True)
+        return 0
 
     log("setup: generating 80 layers of synthetic paged KV on the GPU")
     t0 = time.time()
