@@ -320,7 +320,7 @@ int kvsel_snapkv_vote(const kvsel_paged_kv* kv, const void* q_win, int32_t num_q
   if (votes_stride < kv->max_seq_len) return fail(KVSEL_ERR_INVALID, "votes_stride < max_seq_len");
   if (kv->dtype != KVSEL_BF16) return fail(KVSEL_ERR_UNSUPPORTED, "the vote runs on bf16 caches");
   if (window > 64) return fail(KVSEL_ERR_UNSUPPORTED, "window %d > 64", window);
-  if (pool_kernel > 33) return fail(KVSEL_ERR_UNSUPPORTED, "pool_kernel %d > 33", pool_kernel);
+  if (pool_kernel > 17) return fail(KVSEL_ERR_UNSUPPORTED, "pool_kernel %d > 17", pool_kernel);
   const size_t need = kvsel::snapkv_workspace_bytes(kv->num_seqs, num_q_heads, window, kv->max_seq_len);
   if (!workspace || workspace_bytes < need)
     return fail(KVSEL_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);

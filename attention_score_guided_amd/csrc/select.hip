@@ -137,6 +137,7 @@ __global__ __launch_bounds__(kRowThreads) void select_rows_kernel(RowsParams p) 
   // Each pass streams the middle with kRowUnroll independent loads in flight
   // per thread and counts digits in one of kSubHist LDS histograms.
   int* my_hist = hist[(tid / kWave) % kSubHist];
+  const bool vec = (p.stride & 3) == 0 && (reinterpret_cast<uintptr_t>(p.scores) & 15) == 0;
   uint32_t prefix = 0, pmask = 0;
   int rank = k;
   const int shifts[3] = {21, 10, 0};
@@ -148,17 +149,41 @@ __global__ __launch_bounds__(kRowThreads) void select_rows_kernel(RowsParams p) 
     const int nb = 1 << widths[pass];
     for (int i = tid; i < kSubHist * 2048; i += NT) (&hist[0][0])[i] = 0;
     __syncthreads();
-    for (int j0 = lo + tid; j0 < hi; j0 += NT * kRowUnroll) {
-      float v[kRowUnroll];
+    if (vec) {
+      // 16-byte loads of aligned quads covering [lo, hi); lanes mask the edges
+      const int q_lo = lo >> 2, q_hi = (hi + 3) >> 2;
+      for (int q0 = q_lo + tid; q0 < q_hi; q0 += NT * kRowUnroll) {
+        float4 v[kRowUnroll];
 #pragma unroll
-      for (int u = 0; u < kRowUnroll; ++u) {
-        const int j = j0 + u * NT;
-        v[u] = j < hi ? row[j] : 0.f;
+        for (int u = 0; u < kRowUnroll; ++u) {
+          const int q = q0 + u * NT;
+          v[u] = q < q_hi ? reinterpret_cast<const float4*>(row)[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < kRowUnroll; ++u) {
+          const int j = (q0 + u * NT) * 4;
+          const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t kk = order_key(e[c]);
+            if (j + c >= lo && j + c < hi && (kk & pmask) == prefix)
+              atomicAdd(&my_hist[(kk >> sh) & dmask], 1);
+          }
+        }
       }
+    } else {
+      for (int j0 = lo + tid; j0 < hi; j0 += NT * kRowUnroll) {
+        float v[kRowUnroll];
 #pragma unroll
-      for (int u = 0; u < kRowUnroll; ++u) {
-        const uint32_t kk = order_key(v[u]);
-        if (j0 + u * NT < hi && (kk & pmask) == prefix) atomicAdd(&my_hist[(kk >> sh) & dmask], 1);
+        for (int u = 0; u < kRowUnroll; ++u) {
+          const int j = j0 + u * NT;
+          v[u] = j < hi ? row[j] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kRowUnroll; ++u) {
+          const uint32_t kk = order_key(v[u]);
+          if (j0 + u * NT < hi && (kk & pmask) == prefix) atomicAdd(&my_hist[(kk >> sh) & dmask], 1);
+        }
       }
     }
     __syncthreads();
@@ -183,8 +208,13 @@ __global__ __launch_bounds__(kRowThreads) void select_rows_kernel(RowsParams p) 
   for (int t0 = 0; t0 < n; t0 += NT * 4) {
     const int j0 = t0 + tid * 4;
     float sv[4];
+    if (vec && j0 + 3 < n) {
+      const float4 v4 = reinterpret_cast<const float4*>(row)[j0 >> 2];
+      sv[0] = v4.x; sv[1] = v4.y; sv[2] = v4.z; sv[3] = v4.w;
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sv[i] = (j0 + i < n) ? row[j0 + i] : 0.f;
+      for (int i = 0; i < 4; ++i) sv[i] = (j0 + i < n) ? row[j0 + i] : 0.f;
+    }
     int eq[4], keep[4];
     int n_eq = 0;
 #pragma unroll

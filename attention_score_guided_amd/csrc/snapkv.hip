@@ -14,7 +14,7 @@
 //   pass 1  online (max, sum of exp) of every window row over the chunk's
 //           visible keys -> chunk partials, laid out [chunk][row];
 //   combine per window row: lse over the chunks;
-//   pass 2  recompute the tiles of the chunk plus a 16-key halo on each side,
+//   pass 2  recompute the tiles of the chunk plus an 8-key halo on each side,
 //           p = exp(s - lse), column sums over each head's rows (16-lane DPP
 //           reductions) into LDS, the group sum in head order, the max-pool,
 //           and the final votes of the chunk's prefix keys.
@@ -33,7 +33,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kChunk = 256;             // keys per workgroup
 constexpr int kTiles = kChunk / 16;     // 16-key tiles per chunk
-constexpr int kHalo = 16;               // extra keys on each side for pooling (radius <= 16)
+constexpr int kHalo = 8;                // extra keys on each side for pooling (radius <= 8)
 
 struct VoteParams {
   const uint8_t* k_pages;
@@ -75,24 +75,61 @@ __device__ __forceinline__ void load_q(const VoteParams& p, int b, int h, int co
   }
 }
 
-// Logits of one 16-key tile (keys key0 .. key0+15, some possibly outside
-// [0, L)) against the head's window rows: s[rt][i] for key key0 + grp*4 + i
-// and row rt*16 + col, -inf where not visible.
-template <int D, int RT>
-__device__ __forceinline__ void tile_logits(const VoteParams& p, const int* page_lds, int first_page,
-                                            int b, int kvh, int L, int key0, int col, int grp,
-                                            const bf16x8 (&qb)[RT][D / 32], float (&s)[RT][4]) {
-  constexpr int NU = D / 32;
+// The K rows of a workgroup's keys are staged in LDS once (all loads in
+// flight together) and read back as MFMA fragments by every wave.  Rows are
+// padded by 16 bytes so the 16 rows a fragment read touches fall in distinct
+// banks.
+template <int D>
+struct Stage {
+  static constexpr int kRowBytes = D * 2 + 16;
+  static constexpr int kPieces = D / 8;      // 16-byte pieces per key row
+};
+
+// Stage keys kbase .. kbase + nk - 1 (clamped into [0, L)) into `kst`.
+template <int D>
+__device__ __forceinline__ void stage_keys(const VoteParams& p, const int* page_lds, int first_page,
+                                           int b, int kvh, int L, int kbase, int nk, uint8_t* kst) {
+  constexpr int PC = Stage<D>::kPieces;
   const int P = 1 << p.page_log2;
   const size_t head_stride = (size_t)P * D * 2;
   const size_t page_stride = head_stride * p.num_kv_heads;
-  const int key = min(max(key0 + col, 0), L - 1);     // clamped: every load in bounds
-  const int pg = page_lds[(key >> p.page_log2) - first_page];
-  const uint8_t* rp = p.k_pages + (size_t)pg * page_stride + kvh * head_stride +
-                      (size_t)(key & (P - 1)) * D * 2 + grp * 16;
-  bf16x8 ka[NU];
+  constexpr int kMaxPer = ((kChunk + 2 * kHalo) * PC + kThreads - 1) / kThreads;
+  uint4 buf[kMaxPer];
 #pragma unroll
-  for (int u = 0; u < NU; ++u) ka[u] = __builtin_bit_cast(bf16x8, ld16_stream(rp + u * 64));
+  for (int r = 0; r < kMaxPer; ++r) {
+    const int pi = threadIdx.x + r * kThreads;
+    const int kl = pi / PC, seg = pi % PC;
+    buf[r] = make_uint4(0, 0, 0, 0);
+    if (kl < nk) {
+      const int key = min(max(kbase + kl, 0), L - 1);
+      const int pg = page_lds[(key >> p.page_log2) - first_page];
+      buf[r] = ld16_stream(p.k_pages + (size_t)pg * page_stride + kvh * head_stride +
+                           (size_t)(key & (P - 1)) * D * 2 + seg * 16);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kMaxPer; ++r) {
+    const int pi = threadIdx.x + r * kThreads;
+    const int kl = pi / PC, seg = pi % PC;
+    if (kl < nk) *reinterpret_cast<uint4*>(kst + kl * Stage<D>::kRowBytes + seg * 16) = buf[r];
+  }
+}
+
+// MFMA A fragments of staged tile t (keys t*16 .. t*16+15 of the stage).
+template <int D>
+__device__ __forceinline__ void tile_frag(const uint8_t* kst, int t, int col, int grp, bf16x8 (&ka)[D / 32]) {
+  const uint8_t* rp = kst + (t * 16 + col) * Stage<D>::kRowBytes + grp * 16;
+#pragma unroll
+  for (int u = 0; u < D / 32; ++u) ka[u] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(rp + u * 64));
+}
+
+// Logits of a loaded tile against the head's window rows: s[rt][i] for key
+// key0 + grp*4 + i and row rt*16 + col, -inf where not visible.
+template <int D, int RT>
+__device__ __forceinline__ void tile_logits(const VoteParams& p, int L, int key0, int col, int grp,
+                                            const bf16x8 (&ka)[D / 32], const bf16x8 (&qb)[RT][D / 32],
+                                            float (&s)[RT][4]) {
+  constexpr int NU = D / 32;
   const int prefix = L - p.window;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -115,7 +152,9 @@ template <int D, int RT>
 __global__ __launch_bounds__(kThreads) void snapkv_pass1(VoteParams p) {
   constexpr int NU = D / 32;
   __shared__ int page_lds[kChunk / 16 + 2];
-  extern __shared__ float2 wml[];            // [G][kWaves][RT*16]
+  extern __shared__ __align__(16) uint8_t sm1[];
+  uint8_t* kst = sm1;                                                    // [kChunk][row bytes]
+  float2* wml = reinterpret_cast<float2*>(sm1 + kChunk * Stage<D>::kRowBytes);  // [G][kWaves][RT*16]
   const int G = p.num_q_heads / p.num_kv_heads;
   const int chunk = blockIdx.x;
   const int b = blockIdx.y / p.num_kv_heads, kvh = blockIdx.y % p.num_kv_heads;
@@ -124,12 +163,14 @@ __global__ __launch_bounds__(kThreads) void snapkv_pass1(VoteParams p) {
   if (start >= L) return;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int col = lane & 15, grp = lane >> 4;
+  const int nk = min(kChunk, L - start);
   const int first_page = start >> p.page_log2;
-  const int last_key = min(L, start + kChunk) - 1;
-  const int n_pages = (last_key >> p.page_log2) - first_page + 1;
+  const int n_pages = ((start + nk - 1) >> p.page_log2) - first_page + 1;
   for (int i = tid; i < n_pages; i += kThreads)
     page_lds[i] = p.block_table[(size_t)b * p.max_pages + first_page + i];
   for (int i = tid; i < G * kWaves * RT * 16; i += kThreads) wml[i] = make_float2(kNegInf, 0.f);
+  __syncthreads();
+  stage_keys<D>(p, page_lds, first_page, b, kvh, L, start, kChunk, kst);
   __syncthreads();
 
   const int items = G * kTiles;
@@ -154,8 +195,10 @@ __global__ __launch_bounds__(kThreads) void snapkv_pass1(VoteParams p) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) { m_run[rt] = kNegInf; l_run[rt] = 0.f; }
     }
+    bf16x8 ka[NU];
+    tile_frag<D>(kst, t, col, grp, ka);
     float s[RT][4];
-    tile_logits<D, RT>(p, page_lds, first_page, b, kvh, L, start + t * 16, col, grp, qb, s);
+    tile_logits<D, RT>(p, L, start + t * 16, col, grp, ka, qb, s);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const float tmax = fmaxf(fmaxf(s[rt][0], s[rt][1]), fmaxf(s[rt][2], s[rt][3]));
@@ -223,7 +266,9 @@ __global__ __launch_bounds__(kThreads) void snapkv_pass2(VoteParams p) {
   constexpr int NK = kChunk + 2 * kHalo;               // keys with votes computed
   constexpr int NT = NK / 16;                          // tiles incl. the two halo tiles
   __shared__ int page_lds[NK / 16 + 2];
-  extern __shared__ float hv[];                        // [G][NK] per-head votes
+  extern __shared__ __align__(16) uint8_t sm2[];
+  uint8_t* kst = sm2;                                                    // [NK][row bytes]
+  float* hv = reinterpret_cast<float*>(sm2 + NK * Stage<D>::kRowBytes);  // [G][NK] per-head votes
   const int G = p.num_q_heads / p.num_kv_heads;
   const int chunk = blockIdx.x;
   const int b = blockIdx.y / p.num_kv_heads, kvh = blockIdx.y % p.num_kv_heads;
@@ -239,6 +284,8 @@ __global__ __launch_bounds__(kThreads) void snapkv_pass2(VoteParams p) {
   const int n_pages = (hi_key >> p.page_log2) - first_page + 1;
   for (int i = tid; i < n_pages; i += kThreads)
     page_lds[i] = p.block_table[(size_t)b * p.max_pages + first_page + i];
+  __syncthreads();
+  stage_keys<D>(p, page_lds, first_page, b, kvh, L, kbase, NK, kst);
   __syncthreads();
 
   const int items = G * NT;
@@ -259,8 +306,10 @@ __global__ __launch_bounds__(kThreads) void snapkv_pass2(VoteParams p) {
         lrow[rt] = row < p.window ? p.lse[((size_t)b * p.num_q_heads + h) * p.window + row] * kLog2e : 0.f;
       }
     }
+    bf16x8 ka[NU];
+    tile_frag<D>(kst, t, col, grp, ka);
     float s[RT][4];
-    tile_logits<D, RT>(p, page_lds, first_page, b, kvh, L, kbase + t * 16, col, grp, qb, s);
+    tile_logits<D, RT>(p, L, kbase + t * 16, col, grp, ka, qb, s);
     float cs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -302,10 +351,17 @@ template <int D>
 hipError_t launch_passes(const VoteParams& vp, int rt, dim3 grid, float* lse, float2* part_ml,
                          const int32_t* seq_lens, int B, hipStream_t s) {
   const int G = vp.num_q_heads / vp.num_kv_heads;
-  const size_t lds1 = (size_t)G * kWaves * rt * 16 * sizeof(float2);
-  const size_t lds2 = (size_t)G * (kChunk + 2 * kHalo) * sizeof(float);
-#define KVSEL_P1(R) hipLaunchKernelGGL((snapkv_pass1<D, R>), grid, dim3(kThreads), lds1, s, vp)
-#define KVSEL_P2(R) hipLaunchKernelGGL((snapkv_pass2<D, R>), grid, dim3(kThreads), lds2, s, vp)
+  const size_t lds1 = (size_t)kChunk * Stage<D>::kRowBytes + (size_t)G * kWaves * rt * 16 * sizeof(float2);
+  const size_t lds2 = (size_t)(kChunk + 2 * kHalo) * Stage<D>::kRowBytes +
+                      (size_t)G * (kChunk + 2 * kHalo) * sizeof(float);
+#define KVSEL_P1(R)                                                                              \
+  hipFuncSetAttribute(reinterpret_cast<const void*>(&snapkv_pass1<D, R>),                       \
+                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);                    \
+  hipLaunchKernelGGL((snapkv_pass1<D, R>), grid, dim3(kThreads), lds1, s, vp)
+#define KVSEL_P2(R)                                                                              \
+  hipFuncSetAttribute(reinterpret_cast<const void*>(&snapkv_pass2<D, R>),                       \
+                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds2);                    \
+  hipLaunchKernelGGL((snapkv_pass2<D, R>), grid, dim3(kThreads), lds2, s, vp)
   switch (rt) {
     case 1: KVSEL_P1(1); break;
     case 2: KVSEL_P1(2); break;

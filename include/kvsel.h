@@ -208,7 +208,7 @@ size_t kvsel_select_workspace_bytes(int32_t rows, int32_t max_len, int32_t mode)
  *   workspace: >= kvsel_snapkv_workspace_bytes(kv, num_q_heads, window).
  * Errors: INVALID (NULL pointers, window <= 0, window >= max_seq_len, even or
  * non-positive pool_kernel, votes_stride < max_seq_len), UNSUPPORTED (dtype
- * other than BF16, head_dim other than 64/128, window > 64, pool_kernel > 33),
+ * other than BF16, head_dim other than 64/128, window > 64, pool_kernel > 17),
  * WORKSPACE, HIP.
  * ------------------------------------------------------------------------ */
 int kvsel_snapkv_vote(const kvsel_paged_kv* kv, const void* q_win, int32_t num_q_heads,
