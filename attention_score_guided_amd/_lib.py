@@ -30,7 +30,7 @@ EXPORTED = (
     "kvsel_decode_attn_scores", "kvsel_decode_workspace_bytes", "kvsel_accumulate",
     "kvsel_block_aggregate", "kvsel_select_keep", "kvsel_select_workspace_bytes",
     "kvsel_snapkv_vote", "kvsel_snapkv_workspace_bytes", "kvsel_sparse_attn",
-    "kvsel_sparse_workspace_bytes",
+    "kvsel_sparse_workspace_bytes", "kvsel_set_sync_spin_limit",
     "kvsel_status_string", "kvsel_last_error",
 )
 
@@ -71,6 +71,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvsel_sparse_attn": (ctypes.c_int, [D, P, I32, P, I64, P, I32, I32, F, P, P, P, SZ, P]),
         "kvsel_sparse_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "kvsel_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "kvsel_set_sync_spin_limit": (I32, [I32]),
         "kvsel_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -154,6 +155,14 @@ def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
 
 
 # --------------------------------------------------------------------------
+def set_sync_spin_limit(iterations: int) -> int:
+    """kvsel_set_sync_spin_limit: returns the previous limit."""
+    r = int(_LIB.kvsel_set_sync_spin_limit(int(iterations)))
+    if r < 0:
+        _check(r)
+    return r
+
+
 def decode_workspace_bytes(kv: PagedKV, num_q_heads: int, probs_given: bool) -> int:
     return int(_LIB.kvsel_decode_workspace_bytes(kv.ref(), num_q_heads, int(bool(probs_given))))
 

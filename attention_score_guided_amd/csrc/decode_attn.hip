@@ -53,6 +53,9 @@ constexpr int kUnroll = 4;
 #ifndef KVSEL_WAVES_PER_EU
 #define KVSEL_WAVES_PER_EU 0 // >0: occupancy hint for the G=8 kernel
 #endif
+#ifndef KVSEL_COOP_NORM
+#define KVSEL_COOP_NORM 1  // normalise probabilities inside the split-K pass (bf16, G <= 8)
+#endif
 #ifndef KVSEL_NT_PROBS
 #define KVSEL_NT_PROBS 1   // write final probabilities with non-temporal stores
 #endif
@@ -77,6 +80,18 @@ struct PartialParams {
   float2* part_ml;  // [B][Hq][n_chunks]  (chunk max, chunk sum of exp)
   int num_kv_heads, num_q_heads, group, hgroups, page_log2, max_pages, chunk, n_chunks;
   float scale;
+  // In-kernel normalisation (rows of one (sequence, KV head)):
+  unsigned long long* lse_post;  // [B][Hq][n_chunks] (call epoch << 32) | bits of the chunk lse
+  uint32_t* chunk_flag;          // [B][H_kv][n_chunks] = epoch when a chunk fell back
+  uint32_t epoch;
+  int spin_limit;
+  float* probs;                  // final probabilities [B][Hq][probs_stride] or null
+  int64_t probs_stride;
+  float* raw;                    // fallback target for chunk-relative exp values
+  int64_t raw_stride;
+  float* cum;                    // [B][H_kv][cum_stride] or null
+  int64_t cum_stride;
+  float decay;
 };
 
 // Elements of one 16-byte lane segment.
@@ -290,7 +305,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQkBatch = KVSEL_QK_BATCH > 0 ? KVSEL_QK_BATCH : 1;  // K tiles per load batch
 
-template <int D, int GT, bool HAS_V, bool WRITE_LOGITS>
+template <int D, int GT, bool HAS_V, bool WRITE_LOGITS, bool COOP>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(HAS_V ? (KVSEL_WAVES_PER_EU > 0 ? KVSEL_WAVES_PER_EU : 3) : 4)))
 void decode_partial_mfma(PartialParams p) {
@@ -425,12 +440,26 @@ void decode_partial_mfma(PartialParams p) {
     __syncthreads();
     if (tid < GT)
       ml_lds[tid] = make_float2(m, (wstat[64 + tid] + wstat[80 + tid]) + (wstat[96 + tid] + wstat[112 + tid]));
+    __syncthreads();
   }
 
   const size_t ml_base = ((size_t)b * p.num_q_heads + h0) * p.n_chunks + chunk_id;
+  const size_t row = (size_t)b * p.num_kv_heads + kvh;   // COOP runs with hgroups == 1
+  if constexpr (COOP) {
+    // Post this chunk's log-sum-exp per head as one 64-bit word tagged with
+    // the call's epoch.  The word validates itself, so neither side needs a
+    // fence: a relaxed agent-scope store, read back with relaxed loads.
+    if (tid < GT) {
+      const float2 ml = ml_lds[tid];
+      const float lse_c = ml.x + log2_hw(ml.y) * kLn2;
+      const unsigned long long w = ((unsigned long long)p.epoch << 32) | __float_as_uint(lse_c);
+      __hip_atomic_store(p.lse_post + ml_base + (size_t)tid * p.n_chunks, w, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   if constexpr (!HAS_V) {
     if (tid < GT) p.part_ml[ml_base + (size_t)tid * p.n_chunks] = ml_lds[tid];
-    return;
+    if constexpr (!COOP) return;
   } else {
     // ---- phase 3: P.V on the vector ALUs -----------------------------------
     const int seg = lane % LPK;
@@ -513,6 +542,105 @@ void decode_partial_mfma(PartialParams p) {
       p.part_o[((ml_base + (size_t)h * p.n_chunks)) * D + d] = o;
     }
     if (tid < GT) p.part_ml[ml_base + (size_t)tid * p.n_chunks] = ml_lds[tid];
+  }
+  if constexpr (COOP) {
+    // ---- phase 4: exact probabilities and cum, written once ---------------
+    // Gather the posted lse of every chunk of the row (bounded wait); the
+    // posts happen before P.V, so the first poll normally finds them all.
+    float* lse_lds = red;                                     // [GT][nc], red is free again
+    float* fac = wstat;                                       // [GT] exp(m_chunk - lse)
+    const int nc = (L + C - 1) / C;
+    const int nw = GT * nc;
+    const unsigned long long* post = p.lse_post + ((size_t)b * p.num_q_heads + h0) * p.n_chunks;
+    __syncthreads();
+    bool ok = false;
+    for (int it = 0;; ++it) {
+      int miss = 0;
+      for (int i = tid; i < nw; i += kThreads) {
+        const int h = i / nc, c = i - h * nc;
+        const unsigned long long w =
+            __hip_atomic_load(post + (size_t)h * p.n_chunks + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)(w >> 32) != p.epoch) miss = 1;
+        else lse_lds[i] = __uint_as_float((uint32_t)w);
+      }
+      if (!__syncthreads_or(miss)) {
+        ok = true;
+        break;
+      }
+      if (it >= p.spin_limit) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (ok) {
+      for (int h = wave; h < GT; h += kWaves) {
+        float M = kNegInf;
+        for (int c = lane; c < nc; c += kWave) M = fmaxf(M, lse_lds[h * nc + c]);
+        M = wave_max(M);
+        const float Ms = M * kLog2e;
+        float l = 0.f;
+        for (int c = lane; c < nc; c += kWave) l += exp2_hw(fmaf(lse_lds[h * nc + c], kLog2e, -Ms));
+        l = wave_sum(l);
+        const float lse = M + log2_hw(l) * kLn2;
+        if (lane == 0) fac[h] = exp2_hw((ml_lds[h].x - lse) * kLog2e);
+      }
+      __syncthreads();
+      float f[GT];
+#pragma unroll
+      for (int h = 0; h < GT; ++h) f[h] = fac[h];
+      for (int j = tid; j < n_keys; j += kThreads) {
+        float acc = 0.f;
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+          const float pv = p_lds[j * GT + h] * f[h];
+          if (p.probs) p.probs[((size_t)b * p.num_q_heads + h0 + h) * p.probs_stride + start + j] = pv;
+          acc += pv;
+        }
+        if (p.cum) {
+          float* cp = p.cum + row * p.cum_stride + start + j;
+          *cp = fmaf(p.decay, *cp, acc);
+        }
+      }
+    } else {
+      // The row did not complete in time: hand the chunk-relative values to
+      // the fix-up pass, which scales them once the row's lse is known.
+      for (int j = tid; j < n_keys; j += kThreads) {
+#pragma unroll
+        for (int h = 0; h < GT; ++h)
+          p.raw[((size_t)b * p.num_q_heads + h0 + h) * p.raw_stride + start + j] = p_lds[j * GT + h];
+      }
+      if (tid == 0) p.chunk_flag[row * p.n_chunks + chunk_id] = p.epoch;
+    }
+  }
+}
+
+// Zeroes the synchronisation words of the in-kernel normalisation.
+__global__ __launch_bounds__(256) void decode_sync_clear(uint4* w, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    w[i] = make_uint4(0, 0, 0, 0);
+}
+
+// Fix-up of chunks whose workgroup fell back: raw holds exp(s - m_chunk);
+// scale by exp(m_chunk - lse), write the probabilities and fold cum.
+__global__ __launch_bounds__(256) void decode_fixup(PartialParams p, const float* lse_ws) {
+  const int chunk_id = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const size_t row = (size_t)b * p.num_kv_heads + kvh;
+  if (p.chunk_flag[row * p.n_chunks + chunk_id] != p.epoch) return;
+  const int L = p.seq_lens[b];
+  const int start = chunk_id * p.chunk;
+  const int n_keys = min(p.chunk, L - start);
+  const int G = p.group;
+  for (int j = threadIdx.x; j < n_keys; j += 256) {
+    float acc = 0.f;
+    for (int g = 0; g < G; ++g) {
+      const size_t bh = (size_t)b * p.num_q_heads + (size_t)kvh * G + g;
+      const float f = exp2_hw((p.part_ml[bh * p.n_chunks + chunk_id].x - lse_ws[bh]) * kLog2e);
+      const float pv = p.raw[bh * p.raw_stride + start + j] * f;
+      if (p.probs) p.probs[bh * p.probs_stride + start + j] = pv;
+      acc += pv;
+    }
+    if (p.cum) {
+      float* cp = p.cum + row * p.cum_stride + start + j;
+      *cp = fmaf(p.decay, *cp, acc);
+    }
   }
 }
 
@@ -768,7 +896,7 @@ __global__ __launch_bounds__(kFinThreads) void decode_finalize(FinalizeParams p)
 template <bool BF16, int D, int GT, bool HAS_V, bool WL>
 hipError_t launch_partial_t(const PartialParams& pp, dim3 grid, size_t lds, hipStream_t s) {
   if constexpr (BF16)
-    hipLaunchKernelGGL((decode_partial_mfma<D, GT, HAS_V, WL>), grid, dim3(kThreads), lds, s, pp);
+    hipLaunchKernelGGL((decode_partial_mfma<D, GT, HAS_V, WL, false>), grid, dim3(kThreads), lds, s, pp);
   else
     hipLaunchKernelGGL((decode_partial<false, D, GT, HAS_V, WL>), grid, dim3(kThreads), lds, s, pp);
   return hipGetLastError();
@@ -797,6 +925,25 @@ hipError_t launch_partial_d(const PartialParams& pp, int gt, bool has_v, bool wl
   }
 }
 
+template <int D>
+hipError_t launch_coop_d(const PartialParams& pp, int gt, bool has_v, dim3 grid, size_t lds, hipStream_t s) {
+#define KVSEL_COOP(G)                                                                                        \
+  if (has_v)                                                                                                 \
+    hipLaunchKernelGGL((decode_partial_mfma<D, G, true, false, true>), grid, dim3(kThreads), lds, s, pp);   \
+  else                                                                                                       \
+    hipLaunchKernelGGL((decode_partial_mfma<D, G, false, false, true>), grid, dim3(kThreads), lds, s, pp);  \
+  break;
+  switch (gt) {
+    case 1: KVSEL_COOP(1)
+    case 2: KVSEL_COOP(2)
+    case 4: KVSEL_COOP(4)
+    case 8: KVSEL_COOP(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef KVSEL_COOP
+  return hipGetLastError();
+}
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
@@ -823,7 +970,10 @@ DecodePlan plan_decode(int num_seqs, int num_kv_heads, int num_q_heads, int head
   pl.part_ml_bytes = align256(bh * pl.n_chunks * sizeof(float2));
   pl.lse_bytes = align256(bh * sizeof(float));
   pl.scratch_bytes = need_scratch ? align256(bh * (size_t)max_seq_len * sizeof(float)) : 0;
-  pl.total_bytes = pl.part_o_bytes + pl.part_ml_bytes + pl.lse_bytes + pl.scratch_bytes;
+  const size_t rows = (size_t)num_seqs * num_kv_heads;
+  pl.sync_bytes = align256(bh * pl.n_chunks * sizeof(unsigned long long)) +
+                  align256(rows * pl.n_chunks * sizeof(uint32_t));
+  pl.total_bytes = pl.part_o_bytes + pl.part_ml_bytes + pl.lse_bytes + pl.scratch_bytes + pl.sync_bytes;
   return pl;
 }
 
@@ -833,17 +983,26 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   float2* part_ml = reinterpret_cast<float2*>(ws + pl.part_o_bytes);
   float* lse_ws = reinterpret_cast<float*>(ws + pl.part_o_bytes + pl.part_ml_bytes);
   float* scratch = reinterpret_cast<float*>(ws + pl.part_o_bytes + pl.part_ml_bytes + pl.lse_bytes);
+  uint8_t* sync_base = ws + pl.part_o_bytes + pl.part_ml_bytes + pl.lse_bytes + pl.scratch_bytes;
+  const size_t rows = (size_t)a.num_seqs * a.num_kv_heads;
 
   const bool use_v = a.v_pages != nullptr && a.out != nullptr;
   const bool need_norm = !a.emit_logits && (a.probs != nullptr || a.cum != nullptr);
+  // In-kernel normalisation: bf16, one workgroup serves a whole group.
+  // The lse of a row's chunks are gathered in the kWaves x GT x D staging
+  // area of the P.V reduction, hence the bound on the chunk count.
+  const bool coop = KVSEL_COOP_NORM && a.bf16 && need_norm && pl.hgroups == 1 &&
+                    pl.n_chunks <= kWaves * a.head_dim && (a.probs != nullptr || pl.scratch_bytes > 0);
   float* logits = nullptr;
   int64_t logits_stride = 0;
-  if (a.probs) {
-    logits = a.probs;
-    logits_stride = a.probs_stride;
-  } else if (need_norm) {
-    logits = scratch;
-    logits_stride = a.max_seq_len;
+  if (!coop) {
+    if (a.probs) {
+      logits = a.probs;
+      logits_stride = a.probs_stride;
+    } else if (need_norm) {
+      logits = scratch;
+      logits_stride = a.max_seq_len;
+    }
   }
 
   PartialParams pp{};
@@ -865,6 +1024,18 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   pp.chunk = pl.chunk;
   pp.n_chunks = pl.n_chunks;
   pp.scale = a.scale;
+  const size_t post_bytes = align256((size_t)a.num_seqs * a.num_q_heads * pl.n_chunks * sizeof(unsigned long long));
+  pp.lse_post = reinterpret_cast<unsigned long long*>(sync_base);
+  pp.chunk_flag = reinterpret_cast<uint32_t*>(sync_base + post_bytes);
+  pp.epoch = a.epoch;
+  pp.spin_limit = a.spin_limit;
+  pp.probs = a.probs;
+  pp.probs_stride = a.probs_stride;
+  pp.raw = a.probs ? a.probs : scratch;
+  pp.raw_stride = a.probs ? a.probs_stride : a.max_seq_len;
+  pp.cum = a.cum;
+  pp.cum_stride = a.cum_stride;
+  pp.decay = a.decay;
 
   // Pure logits (indexer scores): the dedicated kernel serving up to 32 heads
   // per K read.
@@ -889,7 +1060,17 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
                      ((size_t)pl.chunk / 16 + 2) * sizeof(int);
   const bool wl = logits != nullptr;
   hipError_t e;
-  if (a.bf16) {
+  if (coop) {
+    // Whatever the workspace held, no word may carry this call's tag.
+    const size_t n16 = (post_bytes + align256(rows * pl.n_chunks * sizeof(uint32_t))) / 16;
+    const int cblocks = (int)std::min<size_t>((n16 + 255) / 256, 1024);
+    hipLaunchKernelGGL(decode_sync_clear, dim3(cblocks), dim3(256), 0, stream, reinterpret_cast<uint4*>(sync_base),
+                       n16);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = a.head_dim == 128 ? launch_coop_d<128>(pp, pl.gt, use_v, grid, lds, stream)
+                          : launch_coop_d<64>(pp, pl.gt, use_v, grid, lds, stream);
+  } else if (a.bf16) {
     e = a.head_dim == 128 ? launch_partial_d<true, 128>(pp, pl.gt, use_v, wl, grid, lds, stream)
                           : launch_partial_d<true, 64>(pp, pl.gt, use_v, wl, grid, lds, stream);
   } else {
@@ -923,6 +1104,12 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     }
   }
 
+  if (coop) {
+    // chunks whose workgroup fell back are finished here (usually none)
+    hipLaunchKernelGGL(decode_fixup, dim3(pl.n_chunks, a.num_kv_heads, a.num_seqs), dim3(256), 0, stream, pp,
+                       lse_ws);
+    return hipGetLastError();
+  }
   if (need_norm) {
     FinalizeParams fp{};
     fp.seq_lens = a.seq_lens;

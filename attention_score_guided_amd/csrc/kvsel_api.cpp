@@ -79,6 +79,20 @@ int check_kv(const kvsel_paged_kv* kv, int32_t num_q_heads, bool need_v) {
 
 bool group_supported(int g) { return (g <= 8 && is_pow2(g)) || (g > 8 && g % 8 == 0); }
 
+// Per-call tag of the decode pass's row arrival words.  A call counter times
+// an odd constant is a bijection on 32 bits, so words left in a workspace by
+// any of the previous 2^32 calls never match, and the scattered values make
+// a chance match with whatever a fresh workspace holds unlikely (2^-32).
+std::atomic<uint32_t> g_calls{0};
+uint32_t next_epoch() {
+  for (;;) {
+    const uint32_t e = (g_calls.fetch_add(1, std::memory_order_relaxed) + 1u) * 0x9E3779B1u;
+    if (e != 0) return e;
+  }
+}
+
+std::atomic<int> g_spin_limit{1 << 14};
+
 }  // namespace
 
 extern "C" {
@@ -95,6 +109,11 @@ const char* kvsel_status_string(int status) {
 }
 
 const char* kvsel_last_error(void) { return g_last_error; }
+
+int32_t kvsel_set_sync_spin_limit(int32_t iterations) {
+  if (iterations < 0) return fail(KVSEL_ERR_INVALID, "spin limit %d < 0", iterations);
+  return g_spin_limit.exchange(iterations, std::memory_order_relaxed);
+}
 
 size_t kvsel_decode_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads,
                                     int32_t probs_given) {
@@ -158,6 +177,8 @@ int kvsel_decode_attn_scores(const kvsel_paged_kv* kv, const void* q, int32_t nu
   a.cum_stride = cum_stride;
   a.decay = decay;
   a.workspace = workspace;
+  a.epoch = next_epoch();
+  a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   return hip_status(kvsel::launch_decode(a, plan, static_cast<hipStream_t>(stream)),
                     "decode_attn_scores launch");
 }

@@ -15,7 +15,7 @@ struct DecodePlan {
   int n_chunks;   // ceil(max_seq_len / chunk)
   int gt;         // query heads handled per workgroup (power of two <= 8)
   int hgroups;    // G / gt
-  size_t part_o_bytes, part_ml_bytes, lse_bytes, scratch_bytes, total_bytes;
+  size_t part_o_bytes, part_ml_bytes, lse_bytes, scratch_bytes, sync_bytes, total_bytes;
 };
 
 DecodePlan plan_decode(int num_seqs, int num_kv_heads, int num_q_heads, int head_dim,
@@ -39,6 +39,8 @@ struct DecodeArgs {
   int64_t cum_stride;
   float decay;
   void* workspace;
+  uint32_t epoch;      // unique per call (never 0): tags the row arrival words
+  int spin_limit;      // bounded wait of the in-kernel normalisation
 };
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);

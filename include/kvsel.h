@@ -18,9 +18,11 @@
  *
  * Conventions (every call):
  *   - Tensor pointers are DEVICE pointers, allocated and owned by the caller.
- *     The library allocates nothing, frees nothing and keeps no state besides
- *     a per-device architecture check.  Scratch space is passed in as
- *     `workspace` (device memory, size from the matching *_workspace_bytes).
+ *     The library allocates nothing and frees nothing.  Its only state is a
+ *     per-device architecture check, a per-call counter that tags the decode
+ *     pass's synchronisation words, and the spin limit below.  Scratch space
+ *     is passed in as `workspace` (device memory, size from the matching
+ *     *_workspace_bytes); two calls must not share a workspace concurrently.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream) and returns a kvsel_status.  Nothing is synchronised inside.
  *   - Host-visible arguments are validated before any HIP call; on error the
@@ -243,6 +245,15 @@ int kvsel_sparse_attn(const kvsel_paged_kv* kv, const void* q, int32_t num_q_hea
 
 size_t kvsel_sparse_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                     int32_t max_count);
+
+/* The bf16 decode pass normalises probabilities in-kernel: each workgroup
+ * posts its chunk's log-sum-exp per head and waits, at most `iterations`
+ * polls, for the other chunks of its (sequence, KV head) row; a workgroup that stops
+ * waiting leaves its chunk to a fix-up pass, so results are exact either
+ * way.  0 makes every chunk take the fix-up path (used by tests).  Returns
+ * the previous limit, or KVSEL_ERR_INVALID for a negative value.
+ * Process-wide. */
+int32_t kvsel_set_sync_spin_limit(int32_t iterations);
 
 /* Name of a status code (static string). */
 const char* kvsel_status_string(int status);

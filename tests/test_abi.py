@@ -155,3 +155,15 @@ def test_snapkv_validation():
     assert call(ws=None) == K.KVSEL_ERR_WORKSPACE
     # chunk partials (max, sum) of every window row plus the per-row lse
     assert lib.kvsel_snapkv_workspace_bytes(ctypes.byref(_kv()), 32, 32) >= 2 * 32 * 32 * 4 * 8
+
+
+def test_sync_spin_limit_setter():
+    prev = K.set_sync_spin_limit(7)
+    try:
+        assert prev >= 0
+        assert K.set_sync_spin_limit(0) == 7
+        with pytest.raises(K.KvselError):
+            K.set_sync_spin_limit(-1)
+        assert K.set_sync_spin_limit(0) == 0
+    finally:
+        K.set_sync_spin_limit(prev)

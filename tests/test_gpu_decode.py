@@ -224,3 +224,56 @@ def test_llama70b_layer_full_size_sampled():
         assert max_rel(f64(lse[b, hs]), r["lse"]) < SCORE_TOL
         assert max_rel(f64(probs[b, hs]), r["probs"]) < SCORE_TOL
         assert max_rel(f64(cum[b, c]), r["probs"].sum(axis=0)) < SCORE_TOL
+
+
+@pytest.mark.parametrize("spin", [0, 1 << 14], ids=["fallback", "in-kernel"])
+def test_decode_normalisation_paths_and_workspace_reuse(spin):
+    """The bf16 pass normalises in-kernel once all chunks of a (sequence, KV
+    head) row have posted their (max, sum); a workgroup that stops waiting
+    hands its chunk to the fix-up pass.  Spin limit 0 forces a mix of both
+    (only the last chunk of a row to arrive sees the row complete).  One
+    workspace, first filled with junk, serves three calls in a row so stale
+    arrival words of earlier calls are exercised."""
+    K = _K()
+    c = _random_case(31, torch.bfloat16, 128, 8, 2, 16, [5000, 1, 2049, 4096])
+    B, Hq, Hkv = 4, 16, 2
+    kv = K.PagedKV(c["kp"], c["vp"], c["bt"], c["lens"], 16, c["max_len"])
+    nbytes = K.decode_workspace_bytes(kv, Hq, True)
+    ws = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda")
+    prev = K.set_sync_spin_limit(spin)
+    try:
+        cum = torch.zeros((B, Hkv, c["stride"]), device="cuda")
+        for it in range(3):
+            out = torch.empty((B, Hq, 128), device="cuda")
+            probs = torch.full((B, Hq, c["stride"]), -3.0, device="cuda")
+            K.decode_attn_scores(kv, c["q"], Hq, c["scale"], out, None, probs, K.EMIT_PROBS, cum, 1.0,
+                                 workspace=ws)
+            torch.cuda.synchronize()
+            for b, L in enumerate([5000, 1, 2049, 4096]):
+                r = _oracle(c, b)
+                assert rel_l2(f64(out[b]), r["out"]) < OUT_TOL
+                assert max_rel(f64(probs[b, :, :L]), r["probs"]) < SCORE_TOL
+                assert (probs[b, :, L:] == -3.0).all()
+                want = (it + 1) * r["probs"].reshape(Hkv, Hq // Hkv, L).sum(axis=1)
+                assert max_rel(f64(cum[b, :, :L]), want) < SCORE_TOL
+    finally:
+        K.set_sync_spin_limit(prev)
+
+
+def test_decode_cum_only_fallback_uses_scratch():
+    """cum without probs on the forced fix-up path: chunk values go through
+    the workspace scratch rows."""
+    K = _K()
+    c = _random_case(32, torch.bfloat16, 64, 4, 3, 32, [3100, 700])
+    kv = K.PagedKV(c["kp"], None, c["bt"], c["lens"], 32, c["max_len"])
+    prev = K.set_sync_spin_limit(0)
+    try:
+        cum = torch.zeros((2, 3, c["stride"]), device="cuda")
+        K.decode_attn_scores(kv, c["q"], 12, c["scale"], None, None, None, K.EMIT_PROBS, cum, 1.0)
+        torch.cuda.synchronize()
+    finally:
+        K.set_sync_spin_limit(prev)
+    for b, L in enumerate([3100, 700]):
+        r = _oracle(c, b, with_v=False)
+        want = r["probs"].reshape(3, 4, L).sum(axis=1)
+        assert max_rel(f64(cum[b, :, :L]), want) < SCORE_TOL
