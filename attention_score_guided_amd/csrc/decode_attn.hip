@@ -41,11 +41,14 @@ constexpr int kUnroll = 4;
 #ifndef KVSEL_MAX_CHUNK
 #define KVSEL_MAX_CHUNK 1024 // keys per split-K chunk (multiple of 64)
 #endif
+#ifndef KVSEL_FIXED_CHUNK
+#define KVSEL_FIXED_CHUNK 0  // >0: always use this chunk (multiple of 64, <= KVSEL_MAX_CHUNK)
+#endif
 #ifndef KVSEL_MIN_WGS
 #define KVSEL_MIN_WGS 1024   // shrink the chunk until the grid has this many workgroups
 #endif
 #ifndef KVSEL_PV_VU
-#define KVSEL_PV_VU 8        // P.V value loads per lane per batch (double-buffered)
+#define KVSEL_PV_VU 4        // P.V value loads per lane per batch (double-buffered)
 #endif
 #ifndef KVSEL_QK_BATCH
 #define KVSEL_QK_BATCH 4     // >0: issue the K loads of this many tiles before their MFMAs
@@ -81,8 +84,8 @@ struct PartialParams {
   int num_kv_heads, num_q_heads, group, hgroups, page_log2, max_pages, chunk, n_chunks;
   float scale;
   // In-kernel normalisation (rows of one (sequence, KV head)):
-  unsigned long long* lse_post;  // [B][Hq][n_chunks] (call epoch << 32) | bits of the chunk lse
-  uint32_t* chunk_flag;          // [B][H_kv][n_chunks] = epoch when a chunk fell back
+  unsigned long long* lse_post;  // [B][Hq][n_chunks][2] chunk lse tagged with epoch / ~epoch
+  uint32_t* chunk_flag;          // [B][H_kv][n_chunks] 1 when the chunk fell back, else 0
   uint32_t epoch;
   int spin_limit;
   float* probs;                  // final probabilities [B][Hq][probs_stride] or null
@@ -417,6 +420,22 @@ void decode_partial_mfma(PartialParams p) {
     }
   }
 
+  // P.V lane mapping: a lane owns 8 dims (one 16-byte segment) of a value
+  // row.  The first V batch is issued here so that it is in flight while the
+  // softmax of phase 2 runs.
+  const int seg = lane % LPK;
+  const int slot = lane / LPK;
+  // Clamped, unconditional loads; keys past the end get p = 0.
+  auto load_batch = [&](uint4 (&vr)[VU], int kb) {
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+      const int jl = min(kb + u * KPI + wave * KPW + slot, n_keys - 1);
+      vr[u] = ld_kv(row_base(p.v_pages, jl) + seg * 16);
+    }
+  };
+  [[maybe_unused]] uint4 va[VU];
+  if constexpr (HAS_V) load_batch(va, 0);
+
   // ---- phase 2: chunk max and sum of exp per head, p = exp(s - m) in LDS ---
   mrun = fmaxf(mrun, __shfl_xor(mrun, 16, kWave));
   mrun = fmaxf(mrun, __shfl_xor(mrun, 32, kWave));
@@ -446,15 +465,47 @@ void decode_partial_mfma(PartialParams p) {
   const size_t ml_base = ((size_t)b * p.num_q_heads + h0) * p.n_chunks + chunk_id;
   const size_t row = (size_t)b * p.num_kv_heads + kvh;   // COOP runs with hgroups == 1
   if constexpr (COOP) {
-    // Post this chunk's log-sum-exp per head as one 64-bit word tagged with
-    // the call's epoch.  The word validates itself, so neither side needs a
-    // fence: a relaxed agent-scope store, read back with relaxed loads.
-    if (tid < GT) {
-      const float2 ml = ml_lds[tid];
+    // Post this chunk's log-sum-exp per head as two 64-bit words, the value
+    // tagged once with the call's epoch and once with its complement.  Each
+    // word validates itself, so neither side needs a fence (relaxed
+    // agent-scope stores, read back with relaxed loads), and whatever the
+    // workspace held before passes the check with probability 2^-64.
+    if (tid < 2 * GT) {
+      const int h = tid >> 1;
+      const float2 ml = ml_lds[h];
       const float lse_c = ml.x + log2_hw(ml.y) * kLn2;
-      const unsigned long long w = ((unsigned long long)p.epoch << 32) | __float_as_uint(lse_c);
-      __hip_atomic_store(p.lse_post + ml_base + (size_t)tid * p.n_chunks, w, __ATOMIC_RELAXED,
+      const uint32_t tag = (tid & 1) ? ~p.epoch : p.epoch;
+      const unsigned long long w = ((unsigned long long)tag << 32) | __float_as_uint(lse_c);
+      __hip_atomic_store(p.lse_post + 2 * (ml_base + (size_t)h * p.n_chunks) + (tid & 1), w, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  // Row-wide state of the in-kernel normalisation.  The chunk's slice of cum
+  // is read here, ahead of P.V, so no latency is left for the end (probs and
+  // cum may alias, so the compiler could not hoist it itself).
+  constexpr int JPT = (KVSEL_MAX_CHUNK + kThreads - 1) / kThreads;
+  const int nc = (L + C - 1) / C;
+  const int nw = GT * nc;
+  const unsigned long long* post = p.lse_post + 2 * ((size_t)b * p.num_q_heads + h0) * p.n_chunks;
+  // Reads post i = (head, chunk) of the row; a miss is reported as NaN bits
+  // with a zero high word, which never equals a valid tag pair.
+  auto post_word = [&](int i) -> unsigned long long {
+    const int h = i / nc, c = i - h * nc;
+    const unsigned long long* w = post + 2 * ((size_t)h * p.n_chunks + c);
+    const unsigned long long w0 = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long w1 = __hip_atomic_load(w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool valid = (uint32_t)(w0 >> 32) == p.epoch && (uint32_t)(w1 >> 32) == ~p.epoch &&
+                       (uint32_t)w0 == (uint32_t)w1;
+    return valid ? w0 : 0ull;
+  };
+  float* cum_row = (COOP && p.cum) ? p.cum + row * p.cum_stride + start : nullptr;
+  [[maybe_unused]] float cpre[JPT];
+  [[maybe_unused]] unsigned long long w_first = 0;
+  if constexpr (COOP) {
+#pragma unroll
+    for (int i = 0; i < JPT; ++i) {
+      const int j = tid + i * kThreads;
+      cpre[i] = (cum_row && j < n_keys) ? cum_row[j] : 0.f;
     }
   }
   if constexpr (!HAS_V) {
@@ -462,22 +513,12 @@ void decode_partial_mfma(PartialParams p) {
     if constexpr (!COOP) return;
   } else {
     // ---- phase 3: P.V on the vector ALUs -----------------------------------
-    const int seg = lane % LPK;
-    const int slot = lane / LPK;
     float acc[GT][EPL];
 #pragma unroll
     for (int h = 0; h < GT; ++h)
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
 
-    // Clamped, unconditional loads; keys past the end get p = 0.
-    auto load_batch = [&](uint4 (&vr)[VU], int kb) {
-#pragma unroll
-      for (int u = 0; u < VU; ++u) {
-        const int jl = min(kb + u * KPI + wave * KPW + slot, n_keys - 1);
-        vr[u] = ld_kv(row_base(p.v_pages, jl) + seg * 16);
-      }
-    };
     auto fma_batch = [&](const uint4 (&vr)[VU], int kb) {
 #pragma unroll
       for (int u = 0; u < VU; ++u) {
@@ -511,14 +552,16 @@ void decode_partial_mfma(PartialParams p) {
       }
     };
     constexpr int STEP = KPI * VU;
-    uint4 va[VU], vb[VU];
-    load_batch(va, 0);
+    uint4 vb[VU];
     for (int kb = 0; kb < n_keys; kb += 2 * STEP) {
       load_batch(vb, kb + STEP);
       fma_batch(va, kb);
       load_batch(va, kb + 2 * STEP);
       fma_batch(vb, kb + STEP);
     }
+    // First poll of the row's posts, overlapping the reduction below.
+    if constexpr (COOP)
+      if (tid < nw) w_first = post_word(tid);
 
 #pragma unroll
     for (int h = 0; h < GT; ++h)
@@ -549,26 +592,24 @@ void decode_partial_mfma(PartialParams p) {
     // posts happen before P.V, so the first poll normally finds them all.
     float* lse_lds = red;                                     // [GT][nc], red is free again
     float* fac = wstat;                                       // [GT] exp(m_chunk - lse)
-    const int nc = (L + C - 1) / C;
-    const int nw = GT * nc;
-    const unsigned long long* post = p.lse_post + ((size_t)b * p.num_q_heads + h0) * p.n_chunks;
     __syncthreads();
-    bool ok = false;
-    for (int it = 0;; ++it) {
+    if constexpr (!HAS_V)
+      if (tid < nw) w_first = post_word(tid);
+    int miss0 = nw > kThreads;
+    if (tid < nw) {
+      if ((uint32_t)(w_first >> 32) != p.epoch) miss0 = 1;
+      else lse_lds[tid] = __uint_as_float((uint32_t)w_first);
+    }
+    bool ok = !__syncthreads_or(miss0);
+    for (int it = 0; !ok && it < p.spin_limit; ++it) {
+      __builtin_amdgcn_s_sleep(2);
       int miss = 0;
       for (int i = tid; i < nw; i += kThreads) {
-        const int h = i / nc, c = i - h * nc;
-        const unsigned long long w =
-            __hip_atomic_load(post + (size_t)h * p.n_chunks + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long w = post_word(i);
         if ((uint32_t)(w >> 32) != p.epoch) miss = 1;
         else lse_lds[i] = __uint_as_float((uint32_t)w);
       }
-      if (!__syncthreads_or(miss)) {
-        ok = true;
-        break;
-      }
-      if (it >= p.spin_limit) break;
-      __builtin_amdgcn_s_sleep(2);
+      ok = !__syncthreads_or(miss);
     }
     if (ok) {
       for (int h = wave; h < GT; h += kWaves) {
@@ -586,17 +627,19 @@ void decode_partial_mfma(PartialParams p) {
       float f[GT];
 #pragma unroll
       for (int h = 0; h < GT; ++h) f[h] = fac[h];
-      for (int j = tid; j < n_keys; j += kThreads) {
-        float acc = 0.f;
+      float* prow = p.probs ? p.probs + ((size_t)b * p.num_q_heads + h0) * p.probs_stride + start : nullptr;
 #pragma unroll
-        for (int h = 0; h < GT; ++h) {
-          const float pv = p_lds[j * GT + h] * f[h];
-          if (p.probs) p.probs[((size_t)b * p.num_q_heads + h0 + h) * p.probs_stride + start + j] = pv;
-          acc += pv;
-        }
-        if (p.cum) {
-          float* cp = p.cum + row * p.cum_stride + start + j;
-          *cp = fmaf(p.decay, *cp, acc);
+      for (int i = 0; i < JPT; ++i) {
+        const int j = tid + i * kThreads;
+        if (j < n_keys) {
+          float acc = 0.f;
+#pragma unroll
+          for (int h = 0; h < GT; ++h) {
+            const float pv = p_lds[j * GT + h] * f[h];
+            if (prow) __builtin_nontemporal_store(pv, prow + (size_t)h * p.probs_stride + j);
+            acc += pv;
+          }
+          if (cum_row) cum_row[j] = fmaf(p.decay, cpre[i], acc);
         }
       }
     } else {
@@ -607,40 +650,8 @@ void decode_partial_mfma(PartialParams p) {
         for (int h = 0; h < GT; ++h)
           p.raw[((size_t)b * p.num_q_heads + h0 + h) * p.raw_stride + start + j] = p_lds[j * GT + h];
       }
-      if (tid == 0) p.chunk_flag[row * p.n_chunks + chunk_id] = p.epoch;
     }
-  }
-}
-
-// Zeroes the synchronisation words of the in-kernel normalisation.
-__global__ __launch_bounds__(256) void decode_sync_clear(uint4* w, size_t n16) {
-  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
-    w[i] = make_uint4(0, 0, 0, 0);
-}
-
-// Fix-up of chunks whose workgroup fell back: raw holds exp(s - m_chunk);
-// scale by exp(m_chunk - lse), write the probabilities and fold cum.
-__global__ __launch_bounds__(256) void decode_fixup(PartialParams p, const float* lse_ws) {
-  const int chunk_id = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const size_t row = (size_t)b * p.num_kv_heads + kvh;
-  if (p.chunk_flag[row * p.n_chunks + chunk_id] != p.epoch) return;
-  const int L = p.seq_lens[b];
-  const int start = chunk_id * p.chunk;
-  const int n_keys = min(p.chunk, L - start);
-  const int G = p.group;
-  for (int j = threadIdx.x; j < n_keys; j += 256) {
-    float acc = 0.f;
-    for (int g = 0; g < G; ++g) {
-      const size_t bh = (size_t)b * p.num_q_heads + (size_t)kvh * G + g;
-      const float f = exp2_hw((p.part_ml[bh * p.n_chunks + chunk_id].x - lse_ws[bh]) * kLog2e);
-      const float pv = p.raw[bh * p.raw_stride + start + j] * f;
-      if (p.probs) p.probs[bh * p.probs_stride + start + j] = pv;
-      acc += pv;
-    }
-    if (p.cum) {
-      float* cp = p.cum + row * p.cum_stride + start + j;
-      *cp = fmaf(p.decay, *cp, acc);
-    }
+    if (tid == 0) p.chunk_flag[row * p.n_chunks + chunk_id] = ok ? 0u : 1u;
   }
 }
 
@@ -744,6 +755,16 @@ struct CombineParams {
   float* lse;       // [B][Hq] or null
   float* lse_ws;    // [B][Hq]
   int num_q_heads, chunk, n_chunks, D;
+  // Fix-up of chunks the in-kernel normalisation left behind (null: none).
+  const uint32_t* chunk_flag;  // [B][H_kv][n_chunks]
+  int group, num_kv_heads;
+  float* probs;                // [B][Hq][probs_stride] or null
+  int64_t probs_stride;
+  const float* raw;            // chunk-relative exp values of flagged chunks
+  int64_t raw_stride;
+  float* cum;                  // [B][H_kv][cum_stride] or null
+  int64_t cum_stride;
+  float decay;
 };
 
 constexpr int kCombThreads = 256;
@@ -809,6 +830,47 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(CombineParams p) 
     const float v = M + log2_hw(l) * kLn2;
     p.lse_ws[bh] = v;
     if (p.lse) p.lse[bh] = v;
+  }
+  if (p.chunk_flag == nullptr || (bh % p.num_q_heads) % p.group != 0) return;
+  // The first head of each group finishes its row's flagged chunks: raw
+  // holds exp(s - m_chunk) for every head of the group; scale by
+  // exp(m_chunk - lse), write the probabilities and fold cum.
+  const int G = p.group;
+  const size_t row = (size_t)b * p.num_kv_heads + (bh % p.num_q_heads) / G;
+  const uint32_t* flags = p.chunk_flag + row * p.n_chunks;
+  int any = 0;
+  for (int c = tid; c < nc; c += kCombThreads) any |= (int)flags[c];
+  if (!__syncthreads_or(any)) return;
+  __shared__ float lse_g[8];
+  for (int g = 0; g < G; ++g) {
+    const float2* mlg = p.part_ml + (size_t)(bh + g) * p.n_chunks;
+    float Mg = kNegInf;
+    for (int c = tid; c < nc; c += kCombThreads) Mg = fmaxf(Mg, mlg[c].x);
+    Mg = block_reduce(Mg, scratch, true);
+    float lg = 0.f;
+    for (int c = tid; c < nc; c += kCombThreads) lg = fmaf(mlg[c].y, exp2_hw((mlg[c].x - Mg) * kLog2e), lg);
+    lg = block_reduce(lg, scratch, false);
+    if (tid == 0) lse_g[g] = Mg + log2_hw(lg) * kLn2;
+  }
+  __syncthreads();
+  for (int c = 0; c < nc; ++c) {
+    if (flags[c] == 0) continue;
+    const int start = c * p.chunk;
+    const int n_keys = min(p.chunk, L - start);
+    for (int j = tid; j < n_keys; j += kCombThreads) {
+      float acc = 0.f;
+      for (int g = 0; g < G; ++g) {
+        const size_t bhg = (size_t)bh + g;
+        const float f = exp2_hw((p.part_ml[bhg * p.n_chunks + c].x - lse_g[g]) * kLog2e);
+        const float pv = p.raw[bhg * p.raw_stride + start + j] * f;
+        if (p.probs) p.probs[bhg * p.probs_stride + start + j] = pv;
+        acc += pv;
+      }
+      if (p.cum) {
+        float* cp = p.cum + row * p.cum_stride + start + j;
+        *cp = fmaf(p.decay, *cp, acc);
+      }
+    }
   }
 }
 
@@ -956,8 +1018,8 @@ DecodePlan plan_decode(int num_seqs, int num_kv_heads, int num_q_heads, int head
   pl.hgroups = G / pl.gt;
   // Largest chunk (<= KVSEL_MAX_CHUNK keys) that still gives the grid
   // >= KVSEL_MIN_WGS workgroups, never below 64 keys.
-  int chunk = KVSEL_MAX_CHUNK;
-  while (chunk > 64) {
+  int chunk = KVSEL_FIXED_CHUNK > 0 ? KVSEL_FIXED_CHUNK : KVSEL_MAX_CHUNK;
+  while (KVSEL_FIXED_CHUNK == 0 && chunk > 64) {
     const long long wgs = (long long)num_seqs * num_kv_heads * pl.hgroups *
                           ((max_seq_len + chunk - 1) / chunk);
     if (wgs >= KVSEL_MIN_WGS) break;
@@ -971,7 +1033,7 @@ DecodePlan plan_decode(int num_seqs, int num_kv_heads, int num_q_heads, int head
   pl.lse_bytes = align256(bh * sizeof(float));
   pl.scratch_bytes = need_scratch ? align256(bh * (size_t)max_seq_len * sizeof(float)) : 0;
   const size_t rows = (size_t)num_seqs * num_kv_heads;
-  pl.sync_bytes = align256(bh * pl.n_chunks * sizeof(unsigned long long)) +
+  pl.sync_bytes = align256(bh * pl.n_chunks * 2 * sizeof(unsigned long long)) +
                   align256(rows * pl.n_chunks * sizeof(uint32_t));
   pl.total_bytes = pl.part_o_bytes + pl.part_ml_bytes + pl.lse_bytes + pl.scratch_bytes + pl.sync_bytes;
   return pl;
@@ -1024,7 +1086,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   pp.chunk = pl.chunk;
   pp.n_chunks = pl.n_chunks;
   pp.scale = a.scale;
-  const size_t post_bytes = align256((size_t)a.num_seqs * a.num_q_heads * pl.n_chunks * sizeof(unsigned long long));
+  const size_t post_bytes = align256((size_t)a.num_seqs * a.num_q_heads * pl.n_chunks * 2 * sizeof(unsigned long long));
   pp.lse_post = reinterpret_cast<unsigned long long*>(sync_base);
   pp.chunk_flag = reinterpret_cast<uint32_t*>(sync_base + post_bytes);
   pp.epoch = a.epoch;
@@ -1061,13 +1123,6 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   const bool wl = logits != nullptr;
   hipError_t e;
   if (coop) {
-    // Whatever the workspace held, no word may carry this call's tag.
-    const size_t n16 = (post_bytes + align256(rows * pl.n_chunks * sizeof(uint32_t))) / 16;
-    const int cblocks = (int)std::min<size_t>((n16 + 255) / 256, 1024);
-    hipLaunchKernelGGL(decode_sync_clear, dim3(cblocks), dim3(256), 0, stream, reinterpret_cast<uint4*>(sync_base),
-                       n16);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
     e = a.head_dim == 128 ? launch_coop_d<128>(pp, pl.gt, use_v, grid, lds, stream)
                           : launch_coop_d<64>(pp, pl.gt, use_v, grid, lds, stream);
   } else if (a.bf16) {
@@ -1093,6 +1148,18 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
       cp.chunk = pl.chunk;
       cp.n_chunks = pl.n_chunks;
       cp.D = a.head_dim;
+      if (coop) {
+        cp.chunk_flag = pp.chunk_flag;
+        cp.group = pp.group;
+        cp.num_kv_heads = a.num_kv_heads;
+        cp.probs = a.probs;
+        cp.probs_stride = a.probs_stride;
+        cp.raw = pp.raw;
+        cp.raw_stride = pp.raw_stride;
+        cp.cum = a.cum;
+        cp.cum_stride = a.cum_stride;
+        cp.decay = a.decay;
+      }
       const dim3 cgrid(a.num_seqs * a.num_q_heads);
       const size_t clds = ((size_t)pl.n_chunks + 4 * kCombThreads + 8) * sizeof(float);
       if (use_v)
@@ -1104,12 +1171,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     }
   }
 
-  if (coop) {
-    // chunks whose workgroup fell back are finished here (usually none)
-    hipLaunchKernelGGL(decode_fixup, dim3(pl.n_chunks, a.num_kv_heads, a.num_seqs), dim3(256), 0, stream, pp,
-                       lse_ws);
-    return hipGetLastError();
-  }
+  if (coop) return hipSuccess;   // the combine finished any chunk left behind
   if (need_norm) {
     FinalizeParams fp{};
     fp.seq_lens = a.seq_lens;

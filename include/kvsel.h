@@ -247,12 +247,13 @@ size_t kvsel_sparse_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
                                     int32_t max_count);
 
 /* The bf16 decode pass normalises probabilities in-kernel: each workgroup
- * posts its chunk's log-sum-exp per head and waits, at most `iterations`
- * polls, for the other chunks of its (sequence, KV head) row; a workgroup that stops
- * waiting leaves its chunk to a fix-up pass, so results are exact either
- * way.  0 makes every chunk take the fix-up path (used by tests).  Returns
- * the previous limit, or KVSEL_ERR_INVALID for a negative value.
- * Process-wide. */
+ * posts its chunk's log-sum-exp per head, then reads the posts of the other
+ * chunks of its (sequence, KV head) row, polling again up to `iterations`
+ * times while some are missing.  A workgroup that stops waiting leaves its
+ * chunk to a fix-up pass, so results are exact either way.  With 0 only
+ * the chunks that find their whole row posted at the first look finish
+ * in-kernel (tests use this to exercise the fix-up).  Returns the previous
+ * limit, or KVSEL_ERR_INVALID for a negative value.  Process-wide. */
 int32_t kvsel_set_sync_spin_limit(int32_t iterations);
 
 /* Name of a status code (static string). */
