@@ -480,10 +480,12 @@ void decode_partial_mfma(PartialParams p) {
                          __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  // Row-wide state of the in-kernel normalisation.  The chunk's slice of cum
-  // is read here, ahead of P.V, so no latency is left for the end (probs and
-  // cum may alias, so the compiler could not hoist it itself).
-  constexpr int JPT = (KVSEL_MAX_CHUNK + kThreads - 1) / kThreads;
+  // Row-wide state of the in-kernel normalisation.  A thread owns 4
+  // consecutive keys of the chunk (16-byte accesses when the rows allow).
+  // The chunk's slice of cum is read here, ahead of P.V, so no latency is
+  // left for the end (probs and cum may alias, so the compiler could not
+  // hoist it itself).
+  constexpr int JPT = (KVSEL_MAX_CHUNK + 4 * kThreads - 1) / (4 * kThreads);
   const int nc = (L + C - 1) / C;
   const int nw = GT * nc;
   const unsigned long long* post = p.lse_post + 2 * ((size_t)b * p.num_q_heads + h0) * p.n_chunks;
@@ -499,13 +501,27 @@ void decode_partial_mfma(PartialParams p) {
     return valid ? w0 : 0ull;
   };
   float* cum_row = (COOP && p.cum) ? p.cum + row * p.cum_stride + start : nullptr;
-  [[maybe_unused]] float cpre[JPT];
+  float* prow = (COOP && p.probs) ? p.probs + ((size_t)b * p.num_q_heads + h0) * p.probs_stride + start : nullptr;
+  const bool cum_vec = ((reinterpret_cast<uintptr_t>(cum_row) | ((uintptr_t)p.cum_stride * 4)) & 15) == 0;
+  const bool probs_vec = ((reinterpret_cast<uintptr_t>(prow) | ((uintptr_t)p.probs_stride * 4)) & 15) == 0;
+  [[maybe_unused]] float4 cpre[JPT];
   [[maybe_unused]] unsigned long long w_first = 0;
   if constexpr (COOP) {
 #pragma unroll
     for (int i = 0; i < JPT; ++i) {
-      const int j = tid + i * kThreads;
-      cpre[i] = (cum_row && j < n_keys) ? cum_row[j] : 0.f;
+      const int j0 = 4 * (tid + i * kThreads);
+      float4 c = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (cum_row && j0 < n_keys) {
+        if (cum_vec && j0 + 3 < n_keys) {
+          c = *reinterpret_cast<const float4*>(cum_row + j0);
+        } else {
+          c.x = cum_row[j0];
+          if (j0 + 1 < n_keys) c.y = cum_row[j0 + 1];
+          if (j0 + 2 < n_keys) c.z = cum_row[j0 + 2];
+          if (j0 + 3 < n_keys) c.w = cum_row[j0 + 3];
+        }
+      }
+      cpre[i] = c;
     }
   }
   if constexpr (!HAS_V) {
@@ -627,19 +643,64 @@ void decode_partial_mfma(PartialParams p) {
       float f[GT];
 #pragma unroll
       for (int h = 0; h < GT; ++h) f[h] = fac[h];
-      float* prow = p.probs ? p.probs + ((size_t)b * p.num_q_heads + h0) * p.probs_stride + start : nullptr;
 #pragma unroll
       for (int i = 0; i < JPT; ++i) {
-        const int j = tid + i * kThreads;
-        if (j < n_keys) {
-          float acc = 0.f;
+        const int j0 = 4 * (tid + i * kThreads);
+        if (j0 < n_keys) {
+          // p_lds[(j0 .. j0+3) * GT + h]: 4 GT contiguous floats
+          float pv[4][GT];
 #pragma unroll
-          for (int h = 0; h < GT; ++h) {
-            const float pv = p_lds[j * GT + h] * f[h];
-            if (prow) __builtin_nontemporal_store(pv, prow + (size_t)h * p.probs_stride + j);
-            acc += pv;
+          for (int k = 0; k < 4; ++k) {
+            if constexpr (GT >= 4) {
+#pragma unroll
+              for (int h4 = 0; h4 < GT / 4; ++h4) {
+                const float4 t4 = *reinterpret_cast<const float4*>(p_lds + (j0 + k) * GT + 4 * h4);
+                pv[k][4 * h4] = t4.x * f[4 * h4];
+                pv[k][4 * h4 + 1] = t4.y * f[4 * h4 + 1];
+                pv[k][4 * h4 + 2] = t4.z * f[4 * h4 + 2];
+                pv[k][4 * h4 + 3] = t4.w * f[4 * h4 + 3];
+              }
+            } else {
+#pragma unroll
+              for (int h = 0; h < GT; ++h) pv[k][h] = p_lds[(j0 + k) * GT + h] * f[h];
+            }
           }
-          if (cum_row) cum_row[j] = fmaf(p.decay, cpre[i], acc);
+          const bool full = j0 + 3 < n_keys;
+          if (prow) {
+#pragma unroll
+            for (int h = 0; h < GT; ++h) {
+              float* dst = prow + (size_t)h * p.probs_stride + j0;
+              if (probs_vec && full) {
+                typedef float f32x4v __attribute__((ext_vector_type(4)));
+                __builtin_nontemporal_store(f32x4v{pv[0][h], pv[1][h], pv[2][h], pv[3][h]},
+                                            reinterpret_cast<f32x4v*>(dst));
+              } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                  if (j0 + k < n_keys) dst[k] = pv[k][h];
+              }
+            }
+          }
+          if (cum_row) {
+            float a[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              a[k] = 0.f;
+#pragma unroll
+              for (int h = 0; h < GT; ++h) a[k] += pv[k][h];
+            }
+            const float4 c = cpre[i];
+            const float4 r = make_float4(fmaf(p.decay, c.x, a[0]), fmaf(p.decay, c.y, a[1]),
+                                         fmaf(p.decay, c.z, a[2]), fmaf(p.decay, c.w, a[3]));
+            if (cum_vec && full) {
+              *reinterpret_cast<float4*>(cum_row + j0) = r;
+            } else {
+              cum_row[j0] = r.x;
+              if (j0 + 1 < n_keys) cum_row[j0 + 1] = r.y;
+              if (j0 + 2 < n_keys) cum_row[j0 + 2] = r.z;
+              if (j0 + 3 < n_keys) cum_row[j0 + 3] = r.w;
+            }
+          }
         }
       }
     } else {
