@@ -48,7 +48,7 @@ constexpr int kUnroll = 4;
 #define KVSEL_MIN_WGS 1024   // shrink the chunk until the grid has this many workgroups
 #endif
 #ifndef KVSEL_PV_VU
-#define KVSEL_PV_VU 4        // P.V value loads per lane per batch (double-buffered)
+#define KVSEL_PV_VU 0        // >0: P.V value loads per lane per batch (double-buffered) for every group width
 #endif
 #ifndef KVSEL_QK_BATCH
 #define KVSEL_QK_BATCH 4     // >0: issue the K loads of this many tiles before their MFMAs
@@ -83,6 +83,7 @@ struct PartialParams {
   float2* part_ml;  // [B][Hq][n_chunks]  (chunk max, chunk sum of exp)
   int num_kv_heads, num_q_heads, group, hgroups, page_log2, max_pages, chunk, n_chunks;
   float scale;
+  int num_rows;                  // B * H_kv
   // In-kernel normalisation (rows of one (sequence, KV head)):
   unsigned long long* lse_post;  // [B][Hq][n_chunks][2] chunk lse tagged with epoch / ~epoch
   uint32_t* chunk_flag;          // [B][H_kv][n_chunks] 1 when the chunk fell back, else 0
@@ -317,7 +318,9 @@ void decode_partial_mfma(PartialParams p) {
   constexpr int LPK = D / EPL;               // P.V: lanes per value row
   constexpr int KPW = kWave / LPK;           // P.V: keys per wave per load
   constexpr int KPI = kWaves * KPW;          // P.V: keys per workgroup per load
-  constexpr int VU = KVSEL_PV_VU;            // P.V: loads per lane per batch
+  // P.V: value loads per lane per batch, as many as the register budget of
+  // the group width allows without spilling.
+  constexpr int VU = KVSEL_PV_VU > 0 ? KVSEL_PV_VU : GT >= 8 ? 4 : !COOP ? 8 : GT == 4 ? 6 : GT == 2 ? 7 : 8;
   constexpr int QB = kQkBatch;
 
   extern __shared__ float smem[];
@@ -328,10 +331,54 @@ void decode_partial_mfma(PartialParams p) {
   float2* ml_lds = reinterpret_cast<float2*>(wstat + 2 * kWaves * 16);  // [GT]
   int* page_lds = reinterpret_cast<int*>(ml_lds + GT);                  // [C/16 + 2]
 
-  const int chunk_id = blockIdx.x;
-  const int kvh = blockIdx.y / p.hgroups;
-  const int hg = blockIdx.y % p.hgroups;
-  const int b = blockIdx.z;
+  int chunk_id, kvh, hg, b;
+  if constexpr (COOP) {
+    // 1-D grid over the chunks that exist: sequence-major, then KV head,
+    // then chunk, with the chunks past each sequence's end left out.  Every
+    // workgroup recomputes the map from seq_lens (a scan by wave 0).  Rows
+    // of the same length are thus dispatched as one burst spread over all
+    // XCDs, so a row's chunks run together and the wait for the row's posts
+    // stays short; surplus workgroups at the end of the grid exit.
+    int* map = reinterpret_cast<int*>(wstat);
+    const int w = blockIdx.x;
+    const int lane0 = threadIdx.x % kWave;
+    const int nseq = p.num_rows / p.num_kv_heads;
+    if (threadIdx.x < kWave) {
+      if (lane0 == 0) map[0] = -1;
+      int base = 0;
+      for (int b0 = 0; b0 < nseq; b0 += kWave) {
+        const int bb = b0 + lane0;
+        const int cnt = bb < nseq ? p.num_kv_heads * ((p.seq_lens[bb] + C - 1) / C) : 0;
+        int incl = cnt;
+#pragma unroll
+        for (int off = 1; off < kWave; off *= 2) {
+          const int t = __shfl_up(incl, off, kWave);
+          if (lane0 >= off) incl += t;
+        }
+        const int lo = base + incl - cnt;
+        if (cnt > 0 && w >= lo && w < lo + cnt) {
+          const int ncb = cnt / p.num_kv_heads;
+          map[0] = bb;
+          map[1] = (w - lo) / ncb;
+          map[2] = (w - lo) % ncb;
+        }
+        base += __shfl(incl, kWave - 1, kWave);
+        if (w < base) break;
+      }
+    }
+    __syncthreads();
+    if (map[0] < 0) return;
+    b = map[0];
+    kvh = map[1];
+    chunk_id = map[2];
+    hg = 0;
+    __syncthreads();   // map lives in wstat, which phase 2 reuses
+  } else {
+    chunk_id = blockIdx.x;
+    kvh = blockIdx.y / p.hgroups;
+    hg = blockIdx.y % p.hgroups;
+    b = blockIdx.z;
+  }
   const int L = p.seq_lens[b];
   const int start = chunk_id * C;
   if (start >= L) return;
@@ -489,23 +536,31 @@ void decode_partial_mfma(PartialParams p) {
   const int nc = (L + C - 1) / C;
   const int nw = GT * nc;
   const unsigned long long* post = p.lse_post + 2 * ((size_t)b * p.num_q_heads + h0) * p.n_chunks;
-  // Reads post i = (head, chunk) of the row; a miss is reported as NaN bits
-  // with a zero high word, which never equals a valid tag pair.
-  auto post_word = [&](int i) -> unsigned long long {
+  // Post i = (head, chunk) of the row: the two tagged words are loaded, and
+  // validated separately so the loads can be issued well ahead of the check.
+  // An invalid pair reads as 0, whose high word never equals the tag.
+  auto post_load = [&](int i, unsigned long long& w0, unsigned long long& w1) {
     const int h = i / nc, c = i - h * nc;
     const unsigned long long* w = post + 2 * ((size_t)h * p.n_chunks + c);
-    const unsigned long long w0 = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned long long w1 = __hip_atomic_load(w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    w0 = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    w1 = __hip_atomic_load(w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto post_check = [&](unsigned long long w0, unsigned long long w1) -> unsigned long long {
     const bool valid = (uint32_t)(w0 >> 32) == p.epoch && (uint32_t)(w1 >> 32) == ~p.epoch &&
                        (uint32_t)w0 == (uint32_t)w1;
     return valid ? w0 : 0ull;
+  };
+  auto post_word = [&](int i) -> unsigned long long {
+    unsigned long long w0, w1;
+    post_load(i, w0, w1);
+    return post_check(w0, w1);
   };
   float* cum_row = (COOP && p.cum) ? p.cum + row * p.cum_stride + start : nullptr;
   float* prow = (COOP && p.probs) ? p.probs + ((size_t)b * p.num_q_heads + h0) * p.probs_stride + start : nullptr;
   const bool cum_vec = ((reinterpret_cast<uintptr_t>(cum_row) | ((uintptr_t)p.cum_stride * 4)) & 15) == 0;
   const bool probs_vec = ((reinterpret_cast<uintptr_t>(prow) | ((uintptr_t)p.probs_stride * 4)) & 15) == 0;
   [[maybe_unused]] float4 cpre[JPT];
-  [[maybe_unused]] unsigned long long w_first = 0;
+  [[maybe_unused]] unsigned long long w_first = 0, w_first1 = 0;
   if constexpr (COOP) {
 #pragma unroll
     for (int i = 0; i < JPT; ++i) {
@@ -569,15 +624,17 @@ void decode_partial_mfma(PartialParams p) {
     };
     constexpr int STEP = KPI * VU;
     uint4 vb[VU];
+    // The first poll of the row's posts is issued half way through P.V (the
+    // other chunks posted long before), and checked after it.
+    const int kb_poll = (n_keys / (4 * STEP)) * (2 * STEP);
     for (int kb = 0; kb < n_keys; kb += 2 * STEP) {
+      if constexpr (COOP)
+        if (kb == kb_poll && tid < nw) post_load(tid, w_first, w_first1);
       load_batch(vb, kb + STEP);
       fma_batch(va, kb);
       load_batch(va, kb + 2 * STEP);
       fma_batch(vb, kb + STEP);
     }
-    // First poll of the row's posts, overlapping the reduction below.
-    if constexpr (COOP)
-      if (tid < nw) w_first = post_word(tid);
 
 #pragma unroll
     for (int h = 0; h < GT; ++h)
@@ -609,8 +666,11 @@ void decode_partial_mfma(PartialParams p) {
     float* lse_lds = red;                                     // [GT][nc], red is free again
     float* fac = wstat;                                       // [GT] exp(m_chunk - lse)
     __syncthreads();
-    if constexpr (!HAS_V)
+    if constexpr (!HAS_V) {
       if (tid < nw) w_first = post_word(tid);
+    } else {
+      if (tid < nw) w_first = post_check(w_first, w_first1);
+    }
     int miss0 = nw > kThreads;
     if (tid < nw) {
       if ((uint32_t)(w_first >> 32) != p.epoch) miss0 = 1;
@@ -723,7 +783,7 @@ void decode_partial_mfma(PartialParams p) {
 template <int D, int NCT>
 __global__ __launch_bounds__(kThreads) void decode_logits_mfma(PartialParams p) {
   constexpr int NU = D / 32;
-  constexpr int QB = kQkBatch;
+  constexpr int QB = 4;                      // K tiles per load batch
   constexpr int GTL = 16 * NCT;
   __shared__ int page_lds[KVSEL_MAX_CHUNK / 16 + 2];
   const int C = p.chunk;
@@ -1147,6 +1207,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   pp.chunk = pl.chunk;
   pp.n_chunks = pl.n_chunks;
   pp.scale = a.scale;
+  pp.num_rows = (int)rows;
   const size_t post_bytes = align256((size_t)a.num_seqs * a.num_q_heads * pl.n_chunks * 2 * sizeof(unsigned long long));
   pp.lse_post = reinterpret_cast<unsigned long long*>(sync_base);
   pp.chunk_flag = reinterpret_cast<uint32_t*>(sync_base + post_bytes);
@@ -1184,8 +1245,9 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   const bool wl = logits != nullptr;
   hipError_t e;
   if (coop) {
-    e = a.head_dim == 128 ? launch_coop_d<128>(pp, pl.gt, use_v, grid, lds, stream)
-                          : launch_coop_d<64>(pp, pl.gt, use_v, grid, lds, stream);
+    const dim3 cgrid((unsigned)(rows * (size_t)pl.n_chunks));
+    e = a.head_dim == 128 ? launch_coop_d<128>(pp, pl.gt, use_v, cgrid, lds, stream)
+                          : launch_coop_d<64>(pp, pl.gt, use_v, cgrid, lds, stream);
   } else if (a.bf16) {
     e = a.head_dim == 128 ? launch_partial_d<true, 128>(pp, pl.gt, use_v, wl, grid, lds, stream)
                           : launch_partial_d<true, 64>(pp, pl.gt, use_v, wl, grid, lds, stream);
