@@ -322,7 +322,7 @@ int kvsel_sparse_attn(const kvsel_paged_kv* kv, const void* q, int32_t num_q_hea
 
 size_t kvsel_snapkv_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads, int32_t window) {
   if (check_kv(kv, num_q_heads, false) != KVSEL_OK || window <= 0) return 0;
-  return kvsel::snapkv_workspace_bytes(kv->num_seqs, num_q_heads, window, kv->max_seq_len);
+  return kvsel::snapkv_workspace_bytes(kv->num_seqs, kv->num_kv_heads, num_q_heads, window, kv->max_seq_len);
 }
 
 int kvsel_snapkv_vote(const kvsel_paged_kv* kv, const void* q_win, int32_t num_q_heads,
@@ -342,7 +342,7 @@ int kvsel_snapkv_vote(const kvsel_paged_kv* kv, const void* q_win, int32_t num_q
   if (kv->dtype != KVSEL_BF16) return fail(KVSEL_ERR_UNSUPPORTED, "the vote runs on bf16 caches");
   if (window > 64) return fail(KVSEL_ERR_UNSUPPORTED, "window %d > 64", window);
   if (pool_kernel > 17) return fail(KVSEL_ERR_UNSUPPORTED, "pool_kernel %d > 17", pool_kernel);
-  const size_t need = kvsel::snapkv_workspace_bytes(kv->num_seqs, num_q_heads, window, kv->max_seq_len);
+  const size_t need = kvsel::snapkv_workspace_bytes(kv->num_seqs, kv->num_kv_heads, num_q_heads, window, kv->max_seq_len);
   if (!workspace || workspace_bytes < need)
     return fail(KVSEL_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
   st = check_device();

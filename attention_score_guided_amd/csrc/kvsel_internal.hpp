@@ -97,7 +97,7 @@ struct SnapkvArgs {
   void* workspace;
 };
 
-size_t snapkv_workspace_bytes(int num_seqs, int num_q_heads, int window, int max_seq_len);
+size_t snapkv_workspace_bytes(int num_seqs, int num_kv_heads, int num_q_heads, int window, int max_seq_len);
 hipError_t launch_snapkv(const SnapkvArgs& a, hipStream_t stream);
 
 }  // namespace kvsel
