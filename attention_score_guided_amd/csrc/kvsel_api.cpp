@@ -248,6 +248,9 @@ int kvsel_select_keep(const float* scores, int64_t stride, const int32_t* length
     const long long need = std::min<long long>(max_len, std::max<long long>(max_budget, (long long)sinks + window));
     if (out_stride < need)
       return fail(KVSEL_ERR_INVALID, "out_stride %lld < %lld", (long long)out_stride, need);
+    const size_t wneed = kvsel::select_workspace_bytes(rows, max_len, mode);
+    if (wneed && (!workspace || workspace_bytes < wneed))
+      return fail(KVSEL_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, wneed);
   } else if (mode == KVSEL_SELECT_GLOBAL_PERCENTILE) {
     if (sinks != 0 || window != 0)
       return fail(KVSEL_ERR_INVALID, "GLOBAL_PERCENTILE takes no sinks or window");

@@ -19,6 +19,8 @@
 // rational for n <= 2^20; packed above the inverted global position it gives
 // distinct 64-bit composites whose top-K (radix select in one workgroup)
 // equals the top-K by (percentile desc, row asc, position asc).
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "kvsel_internal.hpp"
 
@@ -248,6 +250,323 @@ __global__ __launch_bounds__(kRowThreads) void select_rows_kernel(RowsParams p) 
   if (tid == 0) p.out_count[r] = out_base;
 }
 
+// ---- ROWS mode, split over workgroups (long rows, few rows) ---------------
+// One workgroup per row leaves most of the chip idle when a handful of rows
+// are each 100K+ long.  The same selection is then cut into segments of
+// kSegLen positions: each radix pass is a histogram kernel (one workgroup per
+// (segment, row), LDS histograms folded into the row's global histogram
+// with integer atomics, so the counts are exact and order-free) followed by
+// a digit kernel (one workgroup per row); the ordered output is a count
+// kernel (kept and tied positions per segment) followed by an output kernel
+// that places each segment's positions after those of the segments before
+// it.  Results are identical to the one-workgroup kernel.
+constexpr int kSegQuantum = 4096;      // segment lengths are multiples of this
+constexpr int kSegTarget = 1024;       // aim for about this many workgroups per kernel
+constexpr int kSegThreads = 256;
+constexpr int kOutSeg = 4096;          // count / output segment: 4 float4 per thread
+constexpr int kSplitMinLen = 16384;    // split rows at least this long ...
+constexpr int kSplitMaxRows = 512;     // ... when there are fewer rows than this
+
+struct RowPlan {
+  int n, lo, hi, k, fsize;
+  bool keep_all;
+};
+
+__device__ __forceinline__ RowPlan row_plan(const RowsParams& p, int r) {
+  RowPlan q;
+  q.n = p.lengths[r];
+  const int B = p.budgets ? p.budgets[r] : p.max_budget;
+  q.lo = min(p.sinks, q.n);
+  q.hi = max(q.n - p.window, 0);
+  q.keep_all = B >= q.n || q.hi <= q.lo;
+  q.fsize = q.keep_all ? q.n : q.lo + (q.n - q.hi);
+  q.k = q.keep_all ? 0 : max(0, B - q.fsize);
+  return q;
+}
+
+struct SplitParams {
+  RowsParams rp;
+  uint32_t* ghist;   // [rows][2048], zero between passes
+  int4* state;       // [rows]: prefix, pmask, rank, -
+  int2* counts;      // [rows][n_oseg]: definite keeps, ties
+  int n_seg, seg_len;  // histogram passes: segments of the middle
+  int n_oseg;          // count / output: segments of kOutSeg positions of the row
+  bool vec;          // rows 16-byte aligned: float4 loads
+};
+
+// Loads positions j0 .. j0+3 of a row (entries outside [j_lo, j_hi) are
+// returned but must be ignored by the caller).
+__device__ __forceinline__ float4 load4(const float* row, bool vec, int j0, int j_lo, int j_hi) {
+  if (vec) return *reinterpret_cast<const float4*>(row + j0);
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = (j0 + i >= j_lo && j0 + i < j_hi) ? row[j0 + i] : 0.f;
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+template <int PASS>
+__global__ __launch_bounds__(kSegThreads) void select_split_hist(SplitParams sp) {
+  constexpr int kShift[3] = {21, 10, 0};
+  constexpr int kWidth[3] = {11, 11, 10};
+  constexpr int sh = kShift[PASS];
+  constexpr uint32_t dmask = (1u << kWidth[PASS]) - 1u;
+  __shared__ int hist[2][2048];
+  const RowsParams& p = sp.rp;
+  const int r = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
+  const RowPlan q = row_plan(p, r);
+  if (q.k == 0) return;
+  const int j_lo = q.lo + s * sp.seg_len, j_hi = min(j_lo + sp.seg_len, q.hi);
+  if (j_lo >= j_hi) return;
+  uint32_t prefix = 0, pmask = 0;
+  if (PASS > 0) {
+    const int4 st = sp.state[r];
+    prefix = (uint32_t)st.x;
+    pmask = (uint32_t)st.y;
+  }
+  for (int i = tid; i < 2 * 2048; i += kSegThreads) (&hist[0][0])[i] = 0;
+  __syncthreads();
+  int* my = hist[(tid / kWave) & 1];
+  const float* row = p.scores + (size_t)r * p.stride;
+  // aligned quads covering [j_lo, j_hi), four per thread in flight
+  const int q_lo = j_lo >> 2, q_hi = (j_hi + 3) >> 2;
+  constexpr int QU = 8;
+  for (int q0 = q_lo + tid; q0 < q_hi; q0 += kSegThreads * QU) {
+    float4 v[QU];
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+      const int qq = min(q0 + u * kSegThreads, q_hi - 1);
+      v[u] = load4(row, sp.vec, qq * 4, j_lo, j_hi);
+    }
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+      const int j = (q0 + u * kSegThreads) * 4;
+      const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t kk = order_key(e[c]);
+        if (q0 + u * kSegThreads < q_hi && j + c >= j_lo && j + c < j_hi && (kk & pmask) == prefix)
+          atomicAdd(&my[(kk >> sh) & dmask], 1);
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = sp.ghist + (size_t)r * 2048;
+  for (int i = tid; i <= (int)dmask; i += kSegThreads) {
+    const int c = hist[0][i] + hist[1][i];
+    if (c) atomicAdd(&gh[i], (uint32_t)c);
+  }
+}
+
+template <int PASS>
+__global__ __launch_bounds__(kSegThreads) void select_split_digit(SplitParams sp) {
+  constexpr int kShift[3] = {21, 10, 0};
+  constexpr int kWidth[3] = {11, 11, 10};
+  constexpr int sh = kShift[PASS];
+  constexpr int nb = 1 << kWidth[PASS];
+  __shared__ int hist[2048];
+  __shared__ int ws[kSegThreads / kWave];
+  __shared__ int res[2];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const RowPlan q = row_plan(sp.rp, r);
+  if (q.k == 0) return;
+  uint32_t* gh = sp.ghist + (size_t)r * 2048;
+  for (int i = tid; i < nb; i += kSegThreads) {
+    hist[i] = (int)gh[i];
+    gh[i] = 0u;                       // ready for the next pass (or the next call)
+  }
+  __syncthreads();
+  uint32_t prefix = 0, pmask = 0;
+  int rank = q.k;
+  if (PASS > 0) {
+    const int4 st = sp.state[r];
+    prefix = (uint32_t)st.x;
+    pmask = (uint32_t)st.y;
+    rank = st.z;
+  }
+  int above;
+  const int d = find_digit<kSegThreads>(hist, nb, rank, ws, res, above);
+  if (tid == 0)
+    sp.state[r] = make_int4((int)(prefix | ((uint32_t)d << sh)), (int)(pmask | ((uint32_t)(nb - 1) << sh)),
+                            rank - above, 0);
+}
+
+// Keep rule of position j (after the three passes): forced positions, middle
+// keys above tau, and middle keys equal to tau (ties, ranked by position).
+__device__ __forceinline__ void keep_class(const RowPlan& q, uint32_t tau, int j, float v, int& def, int& eq) {
+  def = 0;
+  eq = 0;
+  if (j >= q.n) return;
+  if (q.k == 0) {
+    def = (q.keep_all || j < q.lo || j >= q.hi) ? 1 : 0;
+    return;
+  }
+  const bool mid = j >= q.lo && j < q.hi;
+  if (!mid) { def = 1; return; }
+  const uint32_t kk = order_key(v);
+  def = kk > tau ? 1 : 0;
+  eq = kk == tau ? 1 : 0;
+}
+
+// The kOutSeg positions of segment s of row r, one float4 per thread and
+// iteration (4 iterations), all loaded up front.
+__device__ __forceinline__ void load_out_seg(const SplitParams& sp, const RowPlan& q, const float* row,
+                                             int j_lo, int j_hi, float4 (&v)[kOutSeg / (4 * kSegThreads)]) {
+#pragma unroll
+  for (int it = 0; it < kOutSeg / (4 * kSegThreads); ++it) {
+    const int j0 = j_lo + (it * kSegThreads + threadIdx.x) * 4;
+    v[it] = (q.k && j0 < j_hi) ? load4(row, sp.vec, j0, j_lo, j_hi) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+__global__ __launch_bounds__(kSegThreads) void select_split_count(SplitParams sp) {
+  constexpr int IT = kOutSeg / (4 * kSegThreads);
+  __shared__ int ws[kSegThreads / kWave];
+  const RowsParams& p = sp.rp;
+  const int r = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
+  const RowPlan q = row_plan(p, r);
+  const int j_lo = s * kOutSeg, j_hi = min(j_lo + kOutSeg, q.n);
+  if (j_lo >= j_hi) return;
+  const uint32_t tau = q.k ? (uint32_t)sp.state[r].x : 0u;
+  const float* row = p.scores + (size_t)r * p.stride;
+  float4 v[IT];
+  load_out_seg(sp, q, row, j_lo, j_hi, v);
+  int nd = 0, ne = 0;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int j0 = j_lo + (it * kSegThreads + tid) * 4;
+    const float e4[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      int d, e;
+      keep_class(q, tau, j0 + c < j_hi ? j0 + c : q.n, e4[c], d, e);
+      nd += d;
+      ne += e;
+    }
+  }
+  int td, te;
+  block_exclusive_scan<kSegThreads>(nd, ws, td);
+  block_exclusive_scan<kSegThreads>(ne, ws, te);
+  if (tid == 0) sp.counts[(size_t)r * sp.n_oseg + s] = make_int2(td, te);
+}
+
+__global__ __launch_bounds__(kSegThreads) void select_split_out(SplitParams sp) {
+  constexpr int IT = kOutSeg / (4 * kSegThreads);
+  __shared__ int ws[kSegThreads / kWave];
+  const RowsParams& p = sp.rp;
+  const int r = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
+  const RowPlan q = row_plan(p, r);
+  const int j_lo = s * kOutSeg, j_hi = min(j_lo + kOutSeg, q.n);
+  if (j_lo >= j_hi) return;
+  const float* row = p.scores + (size_t)r * p.stride;
+  float4 v[IT];
+  load_out_seg(sp, q, row, j_lo, j_hi, v);
+  const int4 st = q.k ? sp.state[r] : make_int4(0, 0, 0, 0);
+  const uint32_t tau = (uint32_t)st.x;
+  const int ties_needed = st.z;
+  // definite keeps and ties of the segments before this one (and the total)
+  const int n_seg_r = (q.n + kOutSeg - 1) / kOutSeg;
+  int d_before = 0, e_before = 0, d_all = 0, e_all = 0;
+  for (int i = tid; i < n_seg_r; i += kSegThreads) {
+    const int2 c = sp.counts[(size_t)r * sp.n_oseg + i];
+    d_all += c.x;
+    e_all += c.y;
+    if (i < s) { d_before += c.x; e_before += c.y; }
+  }
+  block_exclusive_scan<kSegThreads>(d_before, ws, d_before);
+  block_exclusive_scan<kSegThreads>(e_before, ws, e_before);
+  if (s == 0) {
+    block_exclusive_scan<kSegThreads>(d_all, ws, d_all);
+    block_exclusive_scan<kSegThreads>(e_all, ws, e_all);
+    if (tid == 0) p.out_count[r] = d_all + min(e_all, ties_needed);
+  }
+  int32_t* out = p.out_idx + (size_t)r * p.out_stride;
+  int tie_base = e_before;
+  int out_base = d_before + min(e_before, ties_needed);
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int j0 = j_lo + (it * kSegThreads + tid) * 4;
+    int eq[4], keep[4];
+    int n_eq = 0;
+    const float e4[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + i;
+      keep_class(q, tau, j < j_hi ? j : q.n, e4[i], keep[i], eq[i]);
+      n_eq += eq[i];
+    }
+    int eq_total;
+    const int eq_before = tie_base + block_exclusive_scan<kSegThreads>(n_eq, ws, eq_total);
+    int run = eq_before, n_keep = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (eq[i]) {
+        keep[i] = run < ties_needed ? 1 : 0;
+        ++run;
+      }
+      n_keep += keep[i];
+    }
+    int keep_total;
+    int pos = out_base + block_exclusive_scan<kSegThreads>(n_keep, ws, keep_total);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (keep[i]) out[pos++] = j0 + i;
+    tie_base += eq_total;
+    out_base += keep_total;
+  }
+}
+
+inline bool use_split(int rows, int max_len) { return rows < kSplitMaxRows && max_len >= kSplitMinLen; }
+
+// Segment length: a multiple of kSegQuantum giving about kSegTarget
+// workgroups over all rows.
+inline int split_seg_len(int rows, int max_len) {
+  const int per_row = std::max(1, (kSegTarget + rows - 1) / rows);
+  const int len = (max_len + per_row - 1) / per_row;
+  return std::max(kSegQuantum, (len + kSegQuantum - 1) / kSegQuantum * kSegQuantum);
+}
+
+inline size_t split_layout(int rows, int max_len, size_t* o_state, size_t* o_counts) {
+  const int n_seg = (max_len + kOutSeg - 1) / kOutSeg;
+  const size_t a = ((size_t)rows * 2048 * sizeof(uint32_t) + 255) & ~size_t(255);
+  const size_t b = ((size_t)rows * sizeof(int4) + 255) & ~size_t(255);
+  const size_t c = ((size_t)rows * n_seg * sizeof(int2) + 255) & ~size_t(255);
+  if (o_state) *o_state = a;
+  if (o_counts) *o_counts = a + b;
+  return a + b + c;
+}
+
+// The global histograms must start at zero: they are cleared here once per
+// call (every digit kernel leaves its row's histogram cleared again).
+__global__ void select_split_zero(uint32_t* gh, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    gh[i] = 0u;
+}
+
+hipError_t launch_split(const RowsParams& rp, int rows, int max_len, void* workspace, hipStream_t stream) {
+  size_t o_state, o_counts;
+  split_layout(rows, max_len, &o_state, &o_counts);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const int seg_len = split_seg_len(rows, max_len);
+  SplitParams sp{rp, reinterpret_cast<uint32_t*>(ws), reinterpret_cast<int4*>(ws + o_state),
+                 reinterpret_cast<int2*>(ws + o_counts), (max_len + seg_len - 1) / seg_len, seg_len,
+                 (max_len + kOutSeg - 1) / kOutSeg,
+                 (rp.stride & 3) == 0 && (reinterpret_cast<uintptr_t>(rp.scores) & 15) == 0};
+  const dim3 seg_grid(sp.n_seg, rows);
+  const size_t nh = (size_t)rows * 2048;
+  hipLaunchKernelGGL(select_split_zero, dim3((unsigned)std::min<size_t>((nh + 255) / 256, 1024)), dim3(256), 0,
+                     stream, sp.ghist, nh);
+  hipLaunchKernelGGL(select_split_hist<0>, seg_grid, dim3(kSegThreads), 0, stream, sp);
+  hipLaunchKernelGGL(select_split_digit<0>, dim3(rows), dim3(kSegThreads), 0, stream, sp);
+  hipLaunchKernelGGL(select_split_hist<1>, seg_grid, dim3(kSegThreads), 0, stream, sp);
+  hipLaunchKernelGGL(select_split_digit<1>, dim3(rows), dim3(kSegThreads), 0, stream, sp);
+  hipLaunchKernelGGL(select_split_hist<2>, seg_grid, dim3(kSegThreads), 0, stream, sp);
+  hipLaunchKernelGGL(select_split_digit<2>, dim3(rows), dim3(kSegThreads), 0, stream, sp);
+  const dim3 out_grid(sp.n_oseg, rows);
+  hipLaunchKernelGGL(select_split_count, out_grid, dim3(kSegThreads), 0, stream, sp);
+  hipLaunchKernelGGL(select_split_out, out_grid, dim3(kSegThreads), 0, stream, sp);
+  return hipGetLastError();
+}
+
 // ---- GLOBAL_PERCENTILE ------------------------------------------------------
 constexpr int kPctMaxLen = 8192;
 
@@ -376,7 +695,7 @@ __global__ __launch_bounds__(kSelThreads) void global_output_kernel(const uint64
 }  // namespace
 
 size_t select_workspace_bytes(int rows, int max_len, int mode) {
-  if (mode != 1) return 0;
+  if (mode != 1) return use_split(rows, max_len) ? split_layout(rows, max_len, nullptr, nullptr) : 0;
   return ((size_t)rows * max_len * sizeof(uint64_t) + 255 & ~size_t(255)) + 256;
 }
 
@@ -388,6 +707,7 @@ hipError_t launch_select(const float* scores, int64_t stride, const int32_t* len
   if (mode == 0) {
     RowsParams rp{scores, stride, lengths, budgets, max_budget, sinks, window, out_idx, out_stride,
                   out_count};
+    if (use_split(rows, max_len)) return launch_split(rp, rows, max_len, workspace, stream);
     hipLaunchKernelGGL(select_rows_kernel, dim3(rows), dim3(kRowThreads), 0, stream, rp);
     return hipGetLastError();
   }

@@ -118,3 +118,43 @@ def test_global_percentile(seed):
     for r in range(rows):
         np.testing.assert_array_equal(idx[r, :cnt[r]], want[r])
     assert cnt.sum() == min(gb, sum(lengths))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_rows_long_rows_split_over_workgroups(seed):
+    """Rows of up to 70K positions (few rows, long rows) run the selection
+    split over many workgroups per row; keep sets must equal the oracle's,
+    including heavy ties across segment boundaries, forced sinks and
+    windows, per-row budgets, and a workspace that starts out as junk."""
+    K = _K()
+    rng = np.random.default_rng(900 + seed)
+    rows = 24
+    lengths = [int(x) for x in rng.integers(1, 70000, size=rows)]
+    lengths[:5] = [1, 16384, 4096 * 7, 69999, 4097]
+    stride = 70001
+    if seed % 2:
+        scores = rng.integers(0, 7, size=(rows, stride)).astype(np.float32)     # heavy ties
+    else:
+        scores = rng.standard_normal((rows, stride)).astype(np.float32)
+        scores[:, 5000:9000] = 1.5                                                # a tied plateau
+    sinks, window = [(4, 512), (0, 0), (16, 0), (0, 2048)][seed]
+    if seed == 1:
+        budgets = [2048] * rows
+    else:
+        budgets = [int(rng.integers(0, n + 5)) for n in lengths]
+    max_budget = max(budgets)
+    note(f"select long rows seed={seed} sinks={sinks} window={window}")
+    max_len = int(max(lengths))
+    out_stride = max(1, min(max_len, max(max_budget, sinks + window)))
+    sc = torch.from_numpy(scores).cuda()
+    lens = torch.tensor(lengths, dtype=torch.int32).cuda()
+    bud = None if seed == 1 else torch.tensor(budgets, dtype=torch.int32).cuda()
+    nbytes = K.select_workspace_bytes(rows, max_len, K.SELECT_ROWS)
+    assert nbytes > 0
+    ws = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda")
+    for rep in range(2):          # the second call reuses the workspace as the first left it
+        idx = torch.full((rows, out_stride), -5, dtype=torch.int32).cuda()
+        cnt = torch.full((rows,), -1, dtype=torch.int32).cuda()
+        K.select_keep(sc, lens, max_len, sinks, window, bud, max_budget, idx, cnt, workspace=ws)
+        torch.cuda.synchronize()
+        _check_rows(scores, lengths, sinks, window, budgets, idx.cpu().numpy(), cnt.cpu().numpy())
