@@ -264,7 +264,8 @@ constexpr int kSegQuantum = 4096;      // segment lengths are multiples of this
 constexpr int kSegTarget = 1024;       // aim for about this many workgroups per kernel
 constexpr int kSegThreads = 256;
 constexpr int kOutSeg = 4096;          // count / output segment: 4 float4 per thread
-constexpr int kSplitMinLen = 16384;    // split rows at least this long ...
+constexpr int kSplitMinLen = 65536;    // split rows at least this long (below, the one-workgroup
+                                       // kernel beats the nine launches of the split) ...
 constexpr int kSplitMaxRows = 512;     // ... when there are fewer rows than this
 
 struct RowPlan {

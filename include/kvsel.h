@@ -184,7 +184,7 @@ int kvsel_block_aggregate(const float* scores, int64_t score_stride, const int32
  *   workspace: >= kvsel_select_workspace_bytes(rows, max_len, mode) bytes
  *   (device memory, any contents; may be 0 bytes).  ROWS mode needs one only
  *   when it splits long rows over several workgroups (fewer than 512 rows of
- *   max_len >= 16384); the result is the same either way.
+ *   max_len >= 65536); the result is the same either way.
  * Errors: INVALID (NULL pointers, rows/max_len <= 0, stride < max_len,
  * negative sinks/window/max_budget/global_budget, out_stride too small,
  * GLOBAL with sinks or window), UNSUPPORTED, WORKSPACE, HIP.

@@ -131,6 +131,7 @@ def test_rows_long_rows_split_over_workgroups(seed):
     rows = 24
     lengths = [int(x) for x in rng.integers(1, 70000, size=rows)]
     lengths[:5] = [1, 16384, 4096 * 7, 69999, 4097]
+    lengths[5] = 65536
     stride = 70001
     if seed % 2:
         scores = rng.integers(0, 7, size=(rows, stride)).astype(np.float32)     # heavy ties
