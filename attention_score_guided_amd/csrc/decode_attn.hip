@@ -1254,7 +1254,15 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     const int G = a.num_q_heads / a.num_kv_heads;
     const int nct = G > 16 ? 2 : 1;
     pp.hgroups = (G + 16 * nct - 1) / (16 * nct);
-    const dim3 lgrid(pl.n_chunks, a.num_kv_heads * pp.hgroups, a.num_seqs);
+    // its own chunk: the largest (<= the plan's) that gives this grid
+    // KVSEL_MIN_WGS workgroups, never below 128 keys
+    int lchunk = pl.chunk;
+    while (lchunk > 128 && (long long)a.num_seqs * a.num_kv_heads * pp.hgroups *
+                                   ((a.max_seq_len + lchunk - 1) / lchunk) < KVSEL_MIN_WGS)
+      lchunk /= 2;
+    pp.chunk = lchunk;
+    pp.n_chunks = (a.max_seq_len + lchunk - 1) / lchunk;
+    const dim3 lgrid(pp.n_chunks, a.num_kv_heads * pp.hgroups, a.num_seqs);
     if (a.head_dim == 128) {
       if (nct == 2) hipLaunchKernelGGL((decode_logits_mfma<128, 2>), lgrid, dim3(kThreads), 0, stream, pp);
       else hipLaunchKernelGGL((decode_logits_mfma<128, 1>), lgrid, dim3(kThreads), 0, stream, pp);
