@@ -8,6 +8,7 @@ from ._lib import (  # noqa: F401
     EMIT_LOGITS, EMIT_PROBS, EXPORTED, KVSEL_BF16, KVSEL_ERR_HIP, KVSEL_ERR_INVALID,
     KVSEL_ERR_UNSUPPORTED, KVSEL_ERR_WORKSPACE, KVSEL_F32, KVSEL_OK, REDUCE_NONE, REDUCE_SUM,
     SELECT_GLOBAL_PERCENTILE, SELECT_ROWS, KvselError, PagedKV, PagedKVDesc, accumulate,
-    block_aggregate, decode_attn_scores, decode_workspace_bytes, library, select_keep,
-    select_workspace_bytes, set_sync_spin_limit, snapkv_vote, snapkv_workspace_bytes, sparse_attn, sparse_workspace_bytes,
+    block_aggregate, decode_attn_scores, decode_attn_scores_agg, decode_workspace_bytes, library,
+    select_keep, select_workspace_bytes, set_sync_spin_limit, snapkv_vote, snapkv_workspace_bytes,
+    sparse_attn, sparse_workspace_bytes,
 )

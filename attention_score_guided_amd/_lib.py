@@ -27,7 +27,8 @@ SELECT_ROWS, SELECT_GLOBAL_PERCENTILE = 0, 1
 
 # Every symbol include/kvsel.h declares.
 EXPORTED = (
-    "kvsel_decode_attn_scores", "kvsel_decode_workspace_bytes", "kvsel_accumulate",
+    "kvsel_decode_attn_scores", "kvsel_decode_attn_scores_agg", "kvsel_decode_workspace_bytes",
+    "kvsel_accumulate",
     "kvsel_block_aggregate", "kvsel_select_keep", "kvsel_select_workspace_bytes",
     "kvsel_snapkv_vote", "kvsel_snapkv_workspace_bytes", "kvsel_sparse_attn",
     "kvsel_sparse_workspace_bytes", "kvsel_set_sync_spin_limit",
@@ -61,6 +62,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     D = ctypes.POINTER(PagedKVDesc)
     sig = {
         "kvsel_decode_attn_scores": (ctypes.c_int, [D, P, I32, F, P, P, P, I64, I32, P, I64, F, P, SZ, P]),
+        "kvsel_decode_attn_scores_agg": (ctypes.c_int, [D, P, I32, F, P, P, P, I64, P, I64, F, I32, P, P, I64, I64,
+                                                         P, SZ, P]),
         "kvsel_decode_workspace_bytes": (SZ, [D, I32, I32]),
         "kvsel_accumulate": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, F, P, I64, P]),
         "kvsel_block_aggregate": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, I32, I32, P, P, I64, P]),
@@ -183,6 +186,26 @@ def decode_attn_scores(kv: PagedKV, q: torch.Tensor, num_q_heads: int, scale: fl
         _ptr(probs, torch.float32, "probs"), 0 if probs is None else probs.shape[-1], int(emit),
         _ptr(cum, torch.float32, "cum"), 0 if cum is None else cum.shape[-1], float(decay),
         _ptr(ws, None, "workspace"), wsb, _stream(stream)))
+
+
+def decode_attn_scores_agg(kv: PagedKV, q: torch.Tensor, num_q_heads: int, scale: float,
+                           out: Optional[torch.Tensor], lse: Optional[torch.Tensor],
+                           probs: Optional[torch.Tensor], cum: torch.Tensor, decay: float,
+                           block_size: int, blk_max: Optional[torch.Tensor], blk_mean: Optional[torch.Tensor],
+                           blk_head_stride: int, blk_seq_stride: int,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """kvsel_decode_attn_scores_agg: blk_* are flat float32 tensors indexed
+    ``b * blk_seq_stride + kvh * blk_head_stride + block`` (or None)."""
+    if q.dtype != kv.dtype:
+        raise TypeError("q must have the cache dtype")
+    ws, wsb = _workspace(decode_workspace_bytes(kv, num_q_heads, probs is not None), q.device, workspace)
+    _check(_LIB.kvsel_decode_attn_scores_agg(
+        kv.ref(), _ptr(q, None, "q"), num_q_heads, float(scale),
+        _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"),
+        _ptr(probs, torch.float32, "probs"), 0 if probs is None else probs.shape[-1],
+        _ptr(cum, torch.float32, "cum"), cum.shape[-1], float(decay), int(block_size),
+        _ptr(blk_max, torch.float32, "blk_max"), _ptr(blk_mean, torch.float32, "blk_mean"),
+        int(blk_head_stride), int(blk_seq_stride), _ptr(ws, None, "workspace"), wsb, _stream(stream)))
 
 
 def accumulate(probs: torch.Tensor, seq_lens: torch.Tensor, num_kv_heads: int, max_seq_len: int,

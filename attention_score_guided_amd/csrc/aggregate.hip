@@ -46,7 +46,7 @@ template <int TPB>
 __global__ __launch_bounds__(kThreads) void block_agg_vec(
     const float* __restrict__ scores, int64_t score_stride, const int32_t* __restrict__ seq_lens,
     int num_heads, int block_size, bool head_sum, bool accumulate, float* __restrict__ out_max,
-    float* __restrict__ out_mean, int64_t out_stride) {
+    float* __restrict__ out_mean, int64_t out_stride, int64_t out_seq_stride) {
   const int b = head_sum ? blockIdx.y : blockIdx.y / num_heads;
   const int hsel = head_sum ? 0 : blockIdx.y % num_heads;
   const int L = seq_lens[b];
@@ -79,8 +79,7 @@ __global__ __launch_bounds__(kThreads) void block_agg_vec(
     mean_tot += sm / (float)count;
   }
   if (threadIdx.x % TPB != 0 || blk >= n_blk) return;
-  const size_t o = head_sum ? (size_t)b * out_stride + blk
-                            : ((size_t)b * num_heads + hsel) * out_stride + blk;
+  const size_t o = (size_t)b * out_seq_stride + (head_sum ? 0 : (size_t)hsel * out_stride) + blk;
   if (out_max) out_max[o] = accumulate ? out_max[o] + mx_tot : mx_tot;
   if (out_mean) out_mean[o] = accumulate ? out_mean[o] + mean_tot : mean_tot;
 }
@@ -89,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void block_agg_vec(
 __global__ __launch_bounds__(kThreads) void block_agg_generic(
     const float* __restrict__ scores, int64_t score_stride, const int32_t* __restrict__ seq_lens,
     int num_seqs, int num_heads, int n_blk_max, int block_size, bool head_sum, bool accumulate,
-    float* __restrict__ out_max, float* __restrict__ out_mean, int64_t out_stride) {
+    float* __restrict__ out_max, float* __restrict__ out_mean, int64_t out_stride, int64_t out_seq_stride) {
   const int rows = head_sum ? num_seqs : num_seqs * num_heads;
   const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
   if (gid >= (long long)rows * n_blk_max) return;
@@ -112,9 +111,42 @@ __global__ __launch_bounds__(kThreads) void block_agg_generic(
     mx_tot += mx;
     mean_tot += sm / (float)(hi - lo);
   }
-  const size_t o = (size_t)r * out_stride + blk;
+  const size_t o = (size_t)b * out_seq_stride + (head_sum ? 0 : (size_t)(r % num_heads) * out_stride) + blk;
   if (out_max) out_max[o] = accumulate ? out_max[o] + mx_tot : mx_tot;
   if (out_mean) out_mean[o] = accumulate ? out_mean[o] + mean_tot : mean_tot;
+}
+
+// Block size 1 summed over heads: a column sum of [B][H][stride] rows, e.g.
+// per-layer block scores stacked as extra heads.  A workgroup owns 64
+// columns of one sequence; its 16 waves split the heads, then LDS adds the
+// 16 partial sums in a fixed order.
+constexpr int kColWaves = 16;
+__global__ __launch_bounds__(64 * kColWaves) void head_sum_columns(
+    const float* __restrict__ scores, int64_t score_stride, const int32_t* __restrict__ seq_lens,
+    int num_heads, int max_len, bool accumulate, float* __restrict__ out_max,
+    float* __restrict__ out_mean, int64_t out_seq_stride) {
+  __shared__ float part[kColWaves][64];
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = blockIdx.x * 64 + lane;
+  const bool live = col < min(seq_lens[b], max_len);
+  float acc = 0.f;
+  if (live) {
+    const float* p = scores + (size_t)b * num_heads * score_stride + col;
+#pragma unroll 8
+    for (int h = w; h < num_heads; h += kColWaves)
+      acc += __builtin_nontemporal_load(p + (size_t)h * score_stride);
+  }
+  part[w][lane] = acc;
+  __syncthreads();
+  if (w == 0 && live) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kColWaves; ++i) s += part[i][lane];
+    const size_t o = (size_t)b * out_seq_stride + col;
+    if (out_max) out_max[o] = accumulate ? out_max[o] + s : s;
+    if (out_mean) out_mean[o] = accumulate ? out_mean[o] + s : s;
+  }
 }
 
 }  // namespace
@@ -133,7 +165,8 @@ hipError_t launch_block_aggregate(const float* scores, int64_t score_stride,
                                   const int32_t* seq_lens, int num_seqs, int num_heads,
                                   int max_seq_len, int block_size, bool head_sum, bool accumulate,
                                   float* out_max, float* out_mean, int64_t out_stride,
-                                  hipStream_t stream) {
+                                  int64_t out_seq_stride, hipStream_t stream) {
+  if (out_seq_stride <= 0) out_seq_stride = head_sum ? out_stride : (int64_t)num_heads * out_stride;
   const bool pow2 = (block_size & (block_size - 1)) == 0;
   const bool vec_ok = pow2 && block_size >= 4 && block_size <= 256 && score_stride % 4 == 0 &&
                       (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
@@ -144,7 +177,7 @@ hipError_t launch_block_aggregate(const float* scores, int64_t score_stride,
   case T:                                                                                  \
     hipLaunchKernelGGL(block_agg_vec<T>, grid, dim3(kThreads), 0, stream, scores,          \
                        score_stride, seq_lens, num_heads, block_size, head_sum, accumulate, \
-                       out_max, out_mean, out_stride);                                     \
+                       out_max, out_mean, out_stride, out_seq_stride);                     \
     break;
     switch (tpb) {
       KVSEL_AGG(1)
@@ -159,12 +192,19 @@ hipError_t launch_block_aggregate(const float* scores, int64_t score_stride,
 #undef KVSEL_AGG
     return hipGetLastError();
   }
+  if (block_size == 1 && head_sum) {
+    const dim3 grid((max_seq_len + 63) / 64, num_seqs);
+    hipLaunchKernelGGL(head_sum_columns, grid, dim3(64 * kColWaves), 0, stream, scores,
+                       score_stride, seq_lens, num_heads, max_seq_len, accumulate, out_max,
+                       out_mean, out_seq_stride);
+    return hipGetLastError();
+  }
   const int n_blk_max = (max_seq_len + block_size - 1) / block_size;
   const long long total = (long long)(head_sum ? num_seqs : num_seqs * num_heads) * n_blk_max;
   const dim3 grid((unsigned)((total + kThreads - 1) / kThreads));
   hipLaunchKernelGGL(block_agg_generic, grid, dim3(kThreads), 0, stream, scores, score_stride,
                      seq_lens, num_seqs, num_heads, n_blk_max, block_size, head_sum, accumulate,
-                     out_max, out_mean, out_stride);
+                     out_max, out_mean, out_stride, out_seq_stride);
   return hipGetLastError();
 }
 

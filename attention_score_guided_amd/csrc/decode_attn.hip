@@ -104,6 +104,12 @@ struct PartialParams {
   float* cum;                    // [B][H_kv][cum_stride] or null
   int64_t cum_stride;
   float decay;
+  // Block aggregates of the updated cum (blk_bs > 0): max and mean over the
+  // valid positions of each block of blk_bs, per (sequence, KV head).
+  int blk_bs;
+  float* blk_max;                // [b * blk_seq_stride + kvh * blk_head_stride + block] or null
+  float* blk_mean;
+  int64_t blk_head_stride, blk_seq_stride;
 };
 
 // Elements of one 16-byte lane segment.
@@ -733,6 +739,7 @@ void decode_partial_mfma(PartialParams p) {
 #pragma unroll
       for (int i = 0; i < JPT; ++i) {
         const int j0 = 4 * (tid + i * kThreads);
+        float bmax = kNegInf, bsum = 0.f;        // this thread's part of its block
         if (j0 < n_keys) {
           // p_lds[(j0 .. j0+3) * GT + h]: 4 GT contiguous floats
           float pv[4][GT];
@@ -787,6 +794,27 @@ void decode_partial_mfma(PartialParams p) {
               if (j0 + 2 < n_keys) cum_row[j0 + 2] = r.z;
               if (j0 + 3 < n_keys) cum_row[j0 + 3] = r.w;
             }
+            const float rv[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              if (j0 + k < n_keys) { bmax = fmaxf(bmax, rv[k]); bsum += rv[k]; }
+          }
+        }
+        if (p.blk_bs > 0) {
+          // A block of blk_bs keys is held by blk_bs / 4 consecutive lanes
+          // (blocks are aligned to the chunk): reduce across that lane group.
+          const int tpb = p.blk_bs >> 2;
+          for (int off = 1; off < tpb; off <<= 1) {
+            bmax = fmaxf(bmax, __shfl_xor(bmax, off, kWave));
+            bsum += __shfl_xor(bsum, off, kWave);
+          }
+          const int key_b = start + (j0 / p.blk_bs) * p.blk_bs;
+          // only blocks that start inside this chunk's keys (threads past the
+          // chunk would otherwise name blocks of the next chunk)
+          if ((tid & (tpb - 1)) == 0 && key_b < start + n_keys) {
+            const size_t o = (size_t)b * p.blk_seq_stride + (size_t)kvh * p.blk_head_stride + key_b / p.blk_bs;
+            if (p.blk_max) p.blk_max[o] = bmax;
+            if (p.blk_mean) p.blk_mean[o] = bsum / (float)min(p.blk_bs, L - key_b);
           }
         }
       }
@@ -913,6 +941,10 @@ struct CombineParams {
   float* cum;                  // [B][H_kv][cum_stride] or null
   int64_t cum_stride;
   float decay;
+  int blk_bs;                  // > 0: block aggregates of the chunks finished here
+  float* blk_max;
+  float* blk_mean;
+  int64_t blk_head_stride, blk_seq_stride;
 };
 
 constexpr int kCombThreads = 256;
@@ -1017,6 +1049,19 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(CombineParams p) 
       if (p.cum) {
         float* cp = p.cum + row * p.cum_stride + start + j;
         *cp = fmaf(p.decay, *cp, acc);
+      }
+    }
+    if (p.blk_bs > 0) {
+      __syncthreads();                     // this chunk's cum writes are visible to the block
+      const float* cr = p.cum + row * p.cum_stride;
+      const int kvh = (int)(row % p.num_kv_heads);
+      for (int bl = tid; bl * p.blk_bs < n_keys; bl += kCombThreads) {
+        const int k0 = start + bl * p.blk_bs, k1 = min(k0 + p.blk_bs, L);
+        float mx = kNegInf, sm = 0.f;
+        for (int k = k0; k < k1; ++k) { mx = fmaxf(mx, cr[k]); sm += cr[k]; }
+        const size_t o = (size_t)b * p.blk_seq_stride + (size_t)kvh * p.blk_head_stride + k0 / p.blk_bs;
+        if (p.blk_max) p.blk_max[o] = mx;
+        if (p.blk_mean) p.blk_mean[o] = sm / (float)(k1 - k0);
       }
     }
   }
@@ -1247,6 +1292,19 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   pp.cum = a.cum;
   pp.cum_stride = a.cum_stride;
   pp.decay = a.decay;
+  // Block aggregates inside the normalising pass when the blocks tile its
+  // chunks (power-of-two sizes 4..256 dividing the chunk); otherwise by the
+  // aggregation kernel after the pass.
+  const bool blk = a.blk_bs > 0 && (a.blk_max || a.blk_mean);
+  const bool blk_fused = blk && coop && (a.blk_bs & (a.blk_bs - 1)) == 0 && a.blk_bs >= 4 &&
+                         a.blk_bs <= 256 && pl.chunk % a.blk_bs == 0;
+  if (blk_fused) {
+    pp.blk_bs = a.blk_bs;
+    pp.blk_max = a.blk_max;
+    pp.blk_mean = a.blk_mean;
+    pp.blk_head_stride = a.blk_head_stride;
+    pp.blk_seq_stride = a.blk_seq_stride;
+  }
 
   // Pure logits (indexer scores): the dedicated kernel serving up to 32 heads
   // per K read.
@@ -1307,6 +1365,11 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
       cp.n_chunks = pl.n_chunks;
       cp.D = a.head_dim;
       if (coop) {
+        cp.blk_bs = pp.blk_bs;
+        cp.blk_max = pp.blk_max;
+        cp.blk_mean = pp.blk_mean;
+        cp.blk_head_stride = pp.blk_head_stride;
+        cp.blk_seq_stride = pp.blk_seq_stride;
         cp.chunk_flag = pp.chunk_flag;
         cp.group = pp.group;
         cp.num_kv_heads = a.num_kv_heads;
@@ -1329,7 +1392,13 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     }
   }
 
-  if (coop) return hipSuccess;   // the combine finished any chunk left behind
+  auto blocks_after = [&]() -> hipError_t {
+    if (!blk || blk_fused) return hipSuccess;
+    return launch_block_aggregate(a.cum, a.cum_stride, a.seq_lens, a.num_seqs, a.num_kv_heads, a.max_seq_len,
+                                  a.blk_bs, false, false, a.blk_max, a.blk_mean, a.blk_head_stride,
+                                  a.blk_seq_stride, stream);
+  };
+  if (coop) return blocks_after();   // the combine finished any chunk left behind
   if (need_norm) {
     FinalizeParams fp{};
     fp.seq_lens = a.seq_lens;
@@ -1358,7 +1427,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  return blocks_after();
 }
 
 }  // namespace kvsel

@@ -123,10 +123,12 @@ size_t kvsel_decode_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_head
       .total_bytes;
 }
 
-int kvsel_decode_attn_scores(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads,
-                             float scale, float* out, float* lse, float* probs,
-                             int64_t probs_stride, int32_t emit, float* cum, int64_t cum_stride,
-                             float decay, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+int decode_impl(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads, float scale, float* out,
+                float* lse, float* probs, int64_t probs_stride, int32_t emit, float* cum, int64_t cum_stride,
+                float decay, int32_t block_size, float* blk_max, float* blk_mean, int64_t blk_head_stride,
+                int64_t blk_seq_stride, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_kv(kv, num_q_heads, out != nullptr);
   if (st != KVSEL_OK) return st;
   if (!q) return fail(KVSEL_ERR_INVALID, "q is NULL");
@@ -179,8 +181,46 @@ int kvsel_decode_attn_scores(const kvsel_paged_kv* kv, const void* q, int32_t nu
   a.workspace = workspace;
   a.epoch = next_epoch();
   a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  a.blk_bs = block_size;
+  a.blk_max = blk_max;
+  a.blk_mean = blk_mean;
+  a.blk_head_stride = blk_head_stride;
+  a.blk_seq_stride = blk_seq_stride;
   return hip_status(kvsel::launch_decode(a, plan, static_cast<hipStream_t>(stream)),
                     "decode_attn_scores launch");
+}
+
+}  // namespace
+
+int kvsel_decode_attn_scores(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads,
+                             float scale, float* out, float* lse, float* probs,
+                             int64_t probs_stride, int32_t emit, float* cum, int64_t cum_stride,
+                             float decay, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(kv, q, num_q_heads, scale, out, lse, probs, probs_stride, emit, cum, cum_stride, decay,
+                     0, nullptr, nullptr, 0, 0, workspace, workspace_bytes, stream);
+}
+
+int kvsel_decode_attn_scores_agg(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads,
+                                 float scale, float* out, float* lse, float* probs,
+                                 int64_t probs_stride, float* cum, int64_t cum_stride, float decay,
+                                 int32_t block_size, float* blk_max, float* blk_mean,
+                                 int64_t blk_head_stride, int64_t blk_seq_stride, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (!kv) return fail(KVSEL_ERR_INVALID, "kv is NULL");
+  if (!cum) return fail(KVSEL_ERR_INVALID, "block aggregates need cum");
+  if (!blk_max && !blk_mean) return fail(KVSEL_ERR_INVALID, "blk_max and blk_mean are both NULL");
+  if (block_size <= 0) return fail(KVSEL_ERR_INVALID, "block_size %d <= 0", block_size);
+  if (kv->num_kv_heads <= 0 || kv->max_seq_len <= 0)
+    return fail(KVSEL_ERR_INVALID, "dimensions must be positive");
+  const long long n_blk = ((long long)kv->max_seq_len + block_size - 1) / block_size;
+  if (blk_head_stride < n_blk)
+    return fail(KVSEL_ERR_INVALID, "blk_head_stride %lld < %lld blocks", (long long)blk_head_stride, n_blk);
+  if (blk_seq_stride < (long long)kv->num_kv_heads * blk_head_stride)
+    return fail(KVSEL_ERR_INVALID, "blk_seq_stride %lld < num_kv_heads * blk_head_stride",
+                (long long)blk_seq_stride);
+  return decode_impl(kv, q, num_q_heads, scale, out, lse, probs, probs_stride, KVSEL_EMIT_PROBS, cum,
+                     cum_stride, decay, block_size, blk_max, blk_mean, blk_head_stride, blk_seq_stride,
+                     workspace, workspace_bytes, stream);
 }
 
 int kvsel_accumulate(const float* probs, int64_t probs_stride, const int32_t* seq_lens,
@@ -222,7 +262,7 @@ int kvsel_block_aggregate(const float* scores, int64_t score_stride, const int32
   return hip_status(
       kvsel::launch_block_aggregate(scores, score_stride, seq_lens, num_seqs, num_heads,
                                     max_seq_len, block_size, head_reduce == KVSEL_REDUCE_SUM,
-                                    accumulate != 0, out_max, out_mean, out_stride,
+                                    accumulate != 0, out_max, out_mean, out_stride, 0,
                                     static_cast<hipStream_t>(stream)),
       "block_aggregate launch");
 }

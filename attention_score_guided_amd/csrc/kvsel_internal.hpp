@@ -41,6 +41,11 @@ struct DecodeArgs {
   void* workspace;
   uint32_t epoch;      // unique per call (never 0): tags the row arrival words
   int spin_limit;      // bounded wait of the in-kernel normalisation
+  // Optional block aggregates of the updated cum (blk_bs > 0, cum required).
+  int blk_bs;
+  float* blk_max;
+  float* blk_mean;
+  int64_t blk_head_stride, blk_seq_stride;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
@@ -53,7 +58,7 @@ hipError_t launch_block_aggregate(const float* scores, int64_t score_stride,
                                   const int32_t* seq_lens, int num_seqs, int num_heads,
                                   int max_seq_len, int block_size, bool head_sum, bool accumulate,
                                   float* out_max, float* out_mean, int64_t out_stride,
-                                  hipStream_t stream);
+                                  int64_t out_seq_stride, hipStream_t stream);  // <= 0: packed rows
 
 size_t select_workspace_bytes(int rows, int max_len, int mode);
 

@@ -92,6 +92,10 @@ def setup(torch, K, synth):
         lse=torch.empty((B, HQ), device="cuda"),
         probs=torch.empty((B, HQ, L), device="cuda"),
         cum=torch.zeros((LAYERS, B, HKV, L), device="cuda"),
+        # per-layer, per-KV-head block max / mean of the updated cum, the
+        # layers stacked as extra heads: [B][LAYERS * HKV][n_blk]
+        blk_max=torch.zeros((B, LAYERS * HKV, n_blk), device="cuda"),
+        blk_mean=torch.zeros((B, LAYERS * HKV, n_blk), device="cuda"),
         agg_max=torch.zeros((B, n_blk), device="cuda"),
         agg_mean=torch.zeros((B, n_blk), device="cuda"),
         blk_lens=torch.full((B,), n_blk, dtype=torch.int32, device="cuda"),
@@ -108,19 +112,24 @@ def setup(torch, K, synth):
 
 def step_decode(K, layers, bufs, scale):
     """Part 1 of a step: score-emitting decode attention of every layer
-    (probabilities emitted, cumulative scores updated)."""
+    (probabilities emitted, cumulative scores updated), with the block max /
+    mean of each layer's updated cum produced by the same pass."""
+    n_blk = L // BLOCK
+    bmax, bmean = bufs["blk_max"].view(-1), bufs["blk_mean"].view(-1)
     for li, (kv, q) in enumerate(layers):
-        K.decode_attn_scores(kv, q, HQ, scale, bufs["out"], bufs["lse"], bufs["probs"], K.EMIT_PROBS,
-                             bufs["cum"][li], 1.0, workspace=bufs["ws_dec"])
+        off = li * HKV * n_blk
+        K.decode_attn_scores_agg(kv, q, HQ, scale, bufs["out"], bufs["lse"], bufs["probs"], bufs["cum"][li],
+                                 1.0, BLOCK, bmax[off:], bmean[off:], n_blk, LAYERS * HKV * n_blk,
+                                 workspace=bufs["ws_dec"])
 
 
 def step_select(K, layers, bufs):
-    """Part 2 of a step: block aggregation summed over heads and layers, then
-    the per-request percentile and the global top-K of blocks."""
+    """Part 2 of a step: the block scores summed over heads and layers (one
+    pass over the stacked per-layer blocks: block size 1, head sum), then the
+    per-request percentile and the global top-K of blocks."""
     n_blk = L // BLOCK
-    for li in range(len(layers)):
-        K.block_aggregate(bufs["cum"][li], bufs["lens"], L, BLOCK, K.REDUCE_SUM, li > 0,
-                          bufs["agg_max"], bufs["agg_mean"])
+    K.block_aggregate(bufs["blk_max"], bufs["blk_lens"], n_blk, 1, K.REDUCE_SUM, False, bufs["agg_max"], None)
+    K.block_aggregate(bufs["blk_mean"], bufs["blk_lens"], n_blk, 1, K.REDUCE_SUM, False, bufs["agg_mean"], None)
     K.select_keep(bufs["agg_max"], bufs["blk_lens"], n_blk, 0, 0, None, 0, bufs["keep_idx"],
                   bufs["keep_cnt"], mode=K.SELECT_GLOBAL_PERCENTILE,
                   global_budget=int(BUDGET_FRAC * B * n_blk), workspace=bufs["ws_sel"])
@@ -419,7 +428,7 @@ def main() -> int:
         run_decode = lambda: step_decode(K, layers, bufs, scale)  # noqa: E731
         run_select = lambda: step_select(K, layers, bufs)  # noqa: E731
     else:
-        # Each part of the step is one graph: 160 (decode) and 81 (select)
+        # Each part of the step is one graph: 160 (decode) and 5 (select)
         # kernel launches replayed without host round trips.
         g_dec = capture(torch, lambda: step_decode(K, layers, bufs, scale))
         g_sel = capture(torch, lambda: step_select(K, layers, bufs))

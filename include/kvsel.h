@@ -138,6 +138,33 @@ int kvsel_accumulate(const float* probs, int64_t probs_stride, const int32_t* se
                      void* stream);
 
 /* ------------------------------------------------------------------------
+ * Decode attention with the token-to-block aggregation of the updated
+ * cumulative scores in the same pass ([OFFLOAD] §3.1 and §5.1 on top of the
+ * call above): identical to kvsel_decode_attn_scores with emit = PROBS and
+ * cum != NULL, and in addition, for every (sequence b, KV head h) and block
+ * n < ceil(L_b / block_size) of positions [n*block_size, min((n+1)*block_size,
+ * L_b)), the max (blk_max) and mean (blk_mean) of the updated cum there,
+ * written at blk_*[b * blk_seq_stride + h * blk_head_stride + n].  Other
+ * entries are left untouched.  Either output may be NULL (not both).
+ * blk_head_stride >= ceil(max_seq_len / block_size) and blk_seq_stride >=
+ * num_kv_heads * blk_head_stride; a larger blk_seq_stride lets the blocks of
+ * several layers be stacked as extra heads of one array, so one
+ * kvsel_block_aggregate call (block_size 1, head_reduce SUM) sums them over
+ * heads and layers.  For bf16 caches with G <= 8 and power-of-two block sizes
+ * 4..256 the blocks come out of the attention pass itself; otherwise the
+ * aggregation runs after it (same results).  Workspace as for
+ * kvsel_decode_attn_scores with these probs and cum.
+ * Errors: as kvsel_decode_attn_scores, plus INVALID for cum == NULL, both
+ * block outputs NULL, block_size <= 0 or strides too small.
+ * ------------------------------------------------------------------------ */
+int kvsel_decode_attn_scores_agg(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads,
+                                 float scale, float* out, float* lse, float* probs,
+                                 int64_t probs_stride, float* cum, int64_t cum_stride, float decay,
+                                 int32_t block_size, float* blk_max, float* blk_mean,
+                                 int64_t blk_head_stride, int64_t blk_seq_stride, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Token-to-block aggregation ([OFFLOAD] §3.1: max keeps a block holding any
  * key token, mean dilutes it).  Block n of row (b, h) covers positions
  * [n*block_size, min((n+1)*block_size, L_b)); a partial last block aggregates

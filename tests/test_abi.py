@@ -167,3 +167,22 @@ def test_sync_spin_limit_setter():
         assert K.set_sync_spin_limit(0) == 0
     finally:
         K.set_sync_spin_limit(prev)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cum=None), K.KVSEL_ERR_INVALID),                       # blocks aggregate cum
+    (dict(blk_max=None, blk_mean=None), K.KVSEL_ERR_INVALID),
+    (dict(block_size=0), K.KVSEL_ERR_INVALID),
+    (dict(head_stride=15), K.KVSEL_ERR_INVALID),                 # 1024 / 64 = 16 blocks
+    (dict(seq_stride=16 * 8 - 1), K.KVSEL_ERR_INVALID),
+    (dict(wsb=0), K.KVSEL_ERR_WORKSPACE),
+])
+def test_decode_agg_validation(kw, status):
+    lib = K.library()
+    a = dict(cum=FAKE, blk_max=FAKE, blk_mean=FAKE, block_size=64, head_stride=16, seq_stride=16 * 8,
+             wsb=1 << 30)
+    a.update(kw)
+    st = lib.kvsel_decode_attn_scores_agg(ctypes.byref(_kv()), FAKE, 32, 0.1, FAKE, None, FAKE, 1024,
+                                          a["cum"], 1024, 1.0, a["block_size"], a["blk_max"], a["blk_mean"],
+                                          a["head_stride"], a["seq_stride"], FAKE, a["wsb"], None)
+    assert st == status

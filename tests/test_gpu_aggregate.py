@@ -36,7 +36,8 @@ def test_accumulate_standalone(G, Hkv, lengths, decay):
 
 
 @pytest.mark.parametrize("bs,lengths,H", [(16, [1, 15, 16, 17, 528], 2), (64, [32768, 1000], 8),
-                                          (7, [100, 49], 3), (256, [1025, 256], 1), (4, [9], 2)])
+                                          (7, [100, 49], 3), (256, [1025, 256], 1), (4, [9], 2),
+                                          (1, [512, 300, 1], 640), (1, [70], 3)])
 @pytest.mark.parametrize("head_sum", [False, True])
 def test_block_aggregate(bs, lengths, H, head_sum):
     note(f"block_aggregate bs={bs} L={lengths} H={H} head_sum={head_sum}")

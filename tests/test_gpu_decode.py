@@ -277,3 +277,64 @@ def test_decode_cum_only_fallback_uses_scratch():
         r = _oracle(c, b, with_v=False)
         want = r["probs"].reshape(3, 4, L).sum(axis=1)
         assert max_rel(f64(cum[b, :, :L]), want) < SCORE_TOL
+
+
+AGG_CASES = [
+    # seed, dtype, d, G, Hkv, P, lengths, block, spin (None: default)
+    (41, torch.bfloat16, 128, 8, 2, 64, [4096, 1500, 64], 64, None),    # fused in the pass
+    (42, torch.bfloat16, 128, 4, 3, 16, [2049, 777], 16, None),
+    (43, torch.bfloat16, 64, 2, 2, 32, [3000, 100], 256, None),
+    (44, torch.bfloat16, 128, 8, 2, 64, [4096, 1500], 64, 0),            # chunks finished by the fix-up
+    (45, torch.float32, 128, 4, 2, 16, [1000, 333], 16, None),          # aggregation after the pass
+    (46, torch.bfloat16, 128, 4, 2, 16, [2000, 1111], 48, None),         # block size not a power of two
+]
+
+
+@pytest.mark.parametrize("case", AGG_CASES, ids=lambda c: f"s{c[0]}-{str(c[1])[6:]}-G{c[3]}-bs{c[7]}-spin{c[8]}")
+def test_decode_with_block_aggregates(case):
+    """kvsel_decode_attn_scores_agg: probabilities and cum as the plain call,
+    plus the block max / mean of the updated cum per (sequence, KV head),
+    written into a strided array (two 'layers' stacked as extra heads)."""
+    seed, dtype, d, G, Hkv, P, lengths, bs, spin = case
+    note(f"decode+agg case {case}")
+    K = _K()
+    c = _random_case(seed, dtype, d, G, Hkv, P, lengths, extra_stride=3)
+    B, Hq = len(lengths), c["Hq"]
+    kv = K.PagedKV(c["kp"], c["vp"], c["bt"], c["lens"], P, c["max_len"])
+    n_blk = -(-c["max_len"] // bs)
+    head_stride = n_blk + 2
+    layers = 2
+    seq_stride = layers * Hkv * head_stride + 5
+    blk_max = torch.full((B * seq_stride,), -9.0, device="cuda")
+    blk_mean = torch.full((B * seq_stride,), -9.0, device="cuda")
+    out = torch.empty((B, Hq, d), device="cuda")
+    probs = torch.full((B, Hq, c["stride"]), -7.0, device="cuda")
+    cum0 = torch.rand((B, Hkv, c["stride"]), device="cuda")
+    cum = cum0.clone()
+    prev = K.set_sync_spin_limit(spin) if spin is not None else None
+    try:
+        layer = 1                                                # write the second stacked layer
+        off = layer * Hkv * head_stride
+        K.decode_attn_scores_agg(kv, c["q"], Hq, c["scale"], out, None, probs, cum, 0.5, bs,
+                                 blk_max[off:], blk_mean[off:], head_stride, seq_stride)
+        torch.cuda.synchronize()
+    finally:
+        if prev is not None:
+            K.set_sync_spin_limit(prev)
+    bm = blk_max.view(-1)
+    bn = blk_mean.view(-1)
+    for b in range(B):
+        L = lengths[b]
+        r = _oracle(c, b)
+        assert max_rel(f64(probs[b, :, :L]), r["probs"]) < SCORE_TOL
+        cum_ref = O.accumulate(f64(cum0[b, :, :L]), r["probs"], decay=0.5)
+        assert max_rel(f64(cum[b, :, :L]), cum_ref) < SCORE_TOL
+        want_max, want_mean = O.block_aggregate(cum_ref, L, bs)
+        nb = -(-L // bs)
+        for h in range(Hkv):
+            base = b * seq_stride + off + h * head_stride
+            assert max_rel(f64(bm[base:base + nb]), want_max[h]) < SCORE_TOL
+            assert max_rel(f64(bn[base:base + nb]), want_mean[h]) < SCORE_TOL
+            assert (bm[base + nb:base + head_stride] == -9.0).all()
+        # the other stacked layer and the padding are untouched
+        assert (bm[b * seq_stride:b * seq_stride + off] == -9.0).all()
