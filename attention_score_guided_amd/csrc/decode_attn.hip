@@ -39,9 +39,9 @@ constexpr int kUnroll = 4;
 #define KVSEL_NT_KV 1      // stream K/V with non-temporal loads
 #endif
 #ifndef KVSEL_NT_K_QK
-#define KVSEL_NT_K_QK 0    // 1: the MFMA K-fragment loads non-temporal too.  Each instruction reads
-                           // half of 16 rows' 128-byte lines and the next one the other halves,
-                           // so cached loads let the second half hit (measured 1-7% faster)
+#define KVSEL_NT_K_QK 1    // 1: the MFMA K-fragment loads non-temporal too (with whole-line loads
+                           // no line is read twice; with half-line loads cached reads let the
+                           // second half hit)
 #endif
 #ifndef KVSEL_MAX_CHUNK
 #define KVSEL_MAX_CHUNK 1024 // keys per split-K chunk (multiple of 64)
@@ -69,6 +69,12 @@ constexpr int kUnroll = 4;
 #endif
 #ifndef KVSEL_NT_PROBS
 #define KVSEL_NT_PROBS 1   // write final probabilities with non-temporal stores
+#endif
+#ifndef KVSEL_NT_CUM
+#define KVSEL_NT_CUM 0     // 1: write the updated cum with non-temporal stores
+#endif
+#ifndef KVSEL_K_LINES
+#define KVSEL_K_LINES 1    // 1: K fragments loaded as whole 128-byte lines, then traded between lanes
 #endif
 
 __device__ __forceinline__ uint4 ld_kv(const void* ptr) {
@@ -321,6 +327,32 @@ __global__ __launch_bounds__(kThreads) void decode_partial(PartialParams p) {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Whole-line K fragment loads for v_mfma_f32_16x16x32_bf16.  Its A operand
+// gives lane (r = lane & 15, g = lane >> 4) 8 dims of key row r, so the
+// fragment of one 32-dim k-step holds 64 bytes of each of 16 rows: every
+// load instruction touches 16 half lines.  Two consecutive k-steps 2v and
+// 2v + 1 together span bytes [128 v, 128 v + 128) of each row, one line.
+// They are loaded as two instructions that each read 8 whole lines: lane
+// (r, g) takes 16 bytes at line segment g + 4 (r >> 3) of key r & 7 (first
+// load) and of key 8 + (r & 7) (second).  Lane r < 8 then holds its own
+// step-2v fragment and lane r + 8's step-2v + 1 fragment; lane r >= 8 the
+// reverse.  One DPP row rotation by 8 per dword swaps the misplaced halves.
+__device__ __forceinline__ void k_line_exchange(bf16x8& s0, bf16x8& s1, bool lo) {
+  uint4 a = __builtin_bit_cast(uint4, s0), c = __builtin_bit_cast(uint4, s1);
+  auto ex = [lo](uint32_t& u0, uint32_t& u1) {
+    const uint32_t give = lo ? u1 : u0;
+    const uint32_t take = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)give, 0x128 /* row_ror:8 */, 0xF, 0xF, false);
+    u0 = lo ? u0 : take;
+    u1 = lo ? take : u1;
+  };
+  ex(a.x, c.x);
+  ex(a.y, c.y);
+  ex(a.z, c.z);
+  ex(a.w, c.w);
+  s0 = __builtin_bit_cast(bf16x8, a);
+  s1 = __builtin_bit_cast(bf16x8, c);
+}
+
 constexpr int kQkBatch = KVSEL_QK_BATCH > 0 ? KVSEL_QK_BATCH : 1;  // K tiles per load batch
 
 template <int D, int GT, bool HAS_V, bool WRITE_LOGITS, bool COOP>
@@ -446,16 +478,32 @@ void decode_partial_mfma(PartialParams p) {
   auto load_k = [&](bf16x8 (&kb)[QB][NU], int t0) {
 #pragma unroll
     for (int t = 0; t < QB; ++t) {
-      const int key = min(wbase + min(t0 + t, nt - 1) * 16 + col, n_keys - 1);
-      const uint8_t* rp = row_base(p.k_pages, key) + grp * 16;
+      if constexpr (KVSEL_K_LINES) {
+        const int key = wbase + min(t0 + t, nt - 1) * 16 + (col & 7);
+        const int sg = (grp + 4 * (col >> 3)) * 16;
+        const uint8_t* ra = row_base(p.k_pages, min(key, n_keys - 1)) + sg;
+        const uint8_t* rb = row_base(p.k_pages, min(key + 8, n_keys - 1)) + sg;
 #pragma unroll
-      for (int u = 0; u < NU; ++u) kb[t][u] = __builtin_bit_cast(bf16x8, KVSEL_NT_K_QK ? ld_kv(rp + u * 64) : ld16(rp + u * 64));
+        for (int v = 0; v < NU / 2; ++v) {
+          kb[t][2 * v] = __builtin_bit_cast(bf16x8, KVSEL_NT_K_QK ? ld_kv(ra + v * 128) : ld16(ra + v * 128));
+          kb[t][2 * v + 1] = __builtin_bit_cast(bf16x8, KVSEL_NT_K_QK ? ld_kv(rb + v * 128) : ld16(rb + v * 128));
+        }
+      } else {
+        const int key = min(wbase + min(t0 + t, nt - 1) * 16 + col, n_keys - 1);
+        const uint8_t* rp = row_base(p.k_pages, key) + grp * 16;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) kb[t][u] = __builtin_bit_cast(bf16x8, KVSEL_NT_K_QK ? ld_kv(rp + u * 64) : ld16(rp + u * 64));
+      }
     }
   };
-  auto tile_k = [&](const bf16x8 (&kb)[QB][NU], int t0) {
+  auto tile_k = [&](bf16x8 (&kb)[QB][NU], int t0) {
 #pragma unroll
     for (int t = 0; t < QB; ++t) {
       if (t0 + t < nt) {
+        if constexpr (KVSEL_K_LINES) {
+#pragma unroll
+          for (int v = 0; v < NU / 2; ++v) k_line_exchange(kb[t][2 * v], kb[t][2 * v + 1], col < 8);
+        }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < NU; ++u)
@@ -787,7 +835,12 @@ void decode_partial_mfma(PartialParams p) {
             const float4 r = make_float4(fmaf(p.decay, c.x, a[0]), fmaf(p.decay, c.y, a[1]),
                                          fmaf(p.decay, c.z, a[2]), fmaf(p.decay, c.w, a[3]));
             if (cum_vec && full) {
-              *reinterpret_cast<float4*>(cum_row + j0) = r;
+              if constexpr (KVSEL_NT_CUM) {
+                typedef float f32x4v __attribute__((ext_vector_type(4)));
+                __builtin_nontemporal_store(f32x4v{r.x, r.y, r.z, r.w}, reinterpret_cast<f32x4v*>(cum_row + j0));
+              } else {
+                *reinterpret_cast<float4*>(cum_row + j0) = r;
+              }
             } else {
               cum_row[j0] = r.x;
               if (j0 + 1 < n_keys) cum_row[j0 + 1] = r.y;
@@ -879,20 +932,37 @@ __global__ __launch_bounds__(kThreads) void decode_logits_mfma(PartialParams p) 
                    n_keys == C;
   for (int t0 = 0; t0 < nt; t0 += QB) {
     bf16x8 kb[QB][NU];
-#pragma unroll
-    for (int t = 0; t < QB; ++t) {
-      const int key = min(wbase + min(t0 + t, nt - 1) * 16 + col, n_keys - 1);
+    auto krow = [&](int key) -> const uint8_t* {
       const int j = start + key;
       const int pg = page_lds[(j >> p.page_log2) - first_page];
-      const uint8_t* rp = p.k_pages + (size_t)pg * page_stride + kvh * head_stride +
-                          (size_t)(j & (P - 1)) * D * 2 + grp * 16;
+      return p.k_pages + (size_t)pg * page_stride + kvh * head_stride + (size_t)(j & (P - 1)) * D * 2;
+    };
 #pragma unroll
-      for (int u = 0; u < NU; ++u) kb[t][u] = __builtin_bit_cast(bf16x8, KVSEL_NT_K_QK ? ld_kv(rp + u * 64) : ld16(rp + u * 64));
+    for (int t = 0; t < QB; ++t) {
+      if constexpr (KVSEL_K_LINES) {
+        const int key = wbase + min(t0 + t, nt - 1) * 16 + (col & 7);
+        const int sg = (grp + 4 * (col >> 3)) * 16;
+        const uint8_t* ra = krow(min(key, n_keys - 1)) + sg;
+        const uint8_t* rb = krow(min(key + 8, n_keys - 1)) + sg;
+#pragma unroll
+        for (int v = 0; v < NU / 2; ++v) {
+          kb[t][2 * v] = __builtin_bit_cast(bf16x8, KVSEL_NT_K_QK ? ld_kv(ra + v * 128) : ld16(ra + v * 128));
+          kb[t][2 * v + 1] = __builtin_bit_cast(bf16x8, KVSEL_NT_K_QK ? ld_kv(rb + v * 128) : ld16(rb + v * 128));
+        }
+      } else {
+        const uint8_t* rp = krow(min(wbase + min(t0 + t, nt - 1) * 16 + col, n_keys - 1)) + grp * 16;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) kb[t][u] = __builtin_bit_cast(bf16x8, KVSEL_NT_K_QK ? ld_kv(rp + u * 64) : ld16(rp + u * 64));
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < QB; ++t) {
       if (t0 + t < nt) {
+        if constexpr (KVSEL_K_LINES) {
+#pragma unroll
+          for (int v = 0; v < NU / 2; ++v) k_line_exchange(kb[t][2 * v], kb[t][2 * v + 1], col < 8);
+        }
         const int k0 = wbase + (t0 + t) * 16 + grp * 4;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
@@ -948,6 +1018,7 @@ struct CombineParams {
 };
 
 constexpr int kCombThreads = 256;
+constexpr int kCombPre = 4;    // partial-output rows per thread loaded up front
 
 __device__ __forceinline__ float block_reduce(float v, float* scratch, bool is_max) {
   v = is_max ? wave_max(v) : wave_sum(v);
@@ -973,37 +1044,58 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(CombineParams p) 
   const int nc = (L + p.chunk - 1) / p.chunk;
   const float2* ml = p.part_ml + (size_t)bh * p.n_chunks;
   const int tid = threadIdx.x;
-  float M = kNegInf;
-  for (int c = tid; c < nc; c += kCombThreads) M = fmaxf(M, ml[c].x);
+  // Every global load of the common case is issued before the first
+  // reduction: the chunk (max, sum) pairs, the first kCombPre partial
+  // outputs of this thread's chunk group, and the fix-up flags.
+  const bool do_out = HAS_V && p.out != nullptr;
+  const int D4 = p.D / 4;
+  const int d4 = tid % D4, cg = tid / D4, ng = kCombThreads / D4;
+  const float4* po = reinterpret_cast<const float4*>(p.part_o + (size_t)bh * p.n_chunks * p.D);
+  float2 mv = make_float2(kNegInf, 0.f);
+  if (tid < nc) mv = ml[tid];
+  float4 pre[kCombPre];
+#pragma unroll
+  for (int i = 0; i < kCombPre; ++i) {
+    const int c = cg + i * ng;
+    pre[i] = (do_out && c < nc) ? po[(size_t)c * D4 + d4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const bool fix_head = p.chunk_flag != nullptr && (bh % p.num_q_heads) % p.group == 0;
+  const size_t row = (size_t)b * p.num_kv_heads + (bh % p.num_q_heads) / p.group;
+  const uint32_t* flags = fix_head ? p.chunk_flag + row * p.n_chunks : nullptr;
+  int any = 0;
+  if (fix_head)
+    for (int c = tid; c < nc; c += kCombThreads) any |= (int)flags[c];
+
+  float M = mv.x;
+  for (int c = tid + kCombThreads; c < nc; c += kCombThreads) M = fmaxf(M, ml[c].x);
   M = block_reduce(M, scratch, true);
   const float Ms = M * kLog2e;
   float l = 0.f;
   for (int c = tid; c < nc; c += kCombThreads) {
-    const float2 v = ml[c];
+    const float2 v = c == tid ? mv : ml[c];
     const float w = exp2_hw(fmaf(v.x, kLog2e, -Ms));
     w_lds[c] = w;
     l = fmaf(w, v.y, l);
   }
   l = block_reduce(l, scratch, false);   // also orders the w_lds writes
-  if constexpr (HAS_V) {
-    if (p.out) {
-      const int D4 = p.D / 4;
-      const int d4 = tid % D4, cg = tid / D4, ng = kCombThreads / D4;
-      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4* po = reinterpret_cast<const float4*>(p.part_o + (size_t)bh * p.n_chunks * p.D);
-      for (int c = cg; c < nc; c += ng) {
-        const float w = w_lds[c];
-        const float4 v = po[(size_t)c * D4 + d4];
-        o.x = fmaf(w, v.x, o.x); o.y = fmaf(w, v.y, o.y);
-        o.z = fmaf(w, v.z, o.z); o.w = fmaf(w, v.w, o.w);
-      }
-      reinterpret_cast<float4*>(red)[cg * D4 + d4] = o;
-      __syncthreads();
-      if (tid < p.D) {
-        float r = 0.f;
-        for (int g = 0; g < ng; ++g) r += red[g * p.D + tid];
-        p.out[(size_t)bh * p.D + tid] = r / l;
-      }
+  if (do_out) {
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto add = [&](float w, const float4& v) {
+      o.x = fmaf(w, v.x, o.x); o.y = fmaf(w, v.y, o.y);
+      o.z = fmaf(w, v.z, o.z); o.w = fmaf(w, v.w, o.w);
+    };
+#pragma unroll
+    for (int i = 0; i < kCombPre; ++i) {
+      const int c = cg + i * ng;
+      if (c < nc) add(w_lds[c], pre[i]);
+    }
+    for (int c = cg + kCombPre * ng; c < nc; c += ng) add(w_lds[c], po[(size_t)c * D4 + d4]);
+    reinterpret_cast<float4*>(red)[cg * D4 + d4] = o;
+    __syncthreads();
+    if (tid < p.D) {
+      float r = 0.f;
+      for (int g = 0; g < ng; ++g) r += red[g * p.D + tid];
+      p.out[(size_t)bh * p.D + tid] = r / l;
     }
   }
   if (tid == 0) {
@@ -1011,15 +1103,11 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(CombineParams p) 
     p.lse_ws[bh] = v;
     if (p.lse) p.lse[bh] = v;
   }
-  if (p.chunk_flag == nullptr || (bh % p.num_q_heads) % p.group != 0) return;
+  if (!fix_head) return;
   // The first head of each group finishes its row's flagged chunks: raw
   // holds exp(s - m_chunk) for every head of the group; scale by
   // exp(m_chunk - lse), write the probabilities and fold cum.
   const int G = p.group;
-  const size_t row = (size_t)b * p.num_kv_heads + (bh % p.num_q_heads) / G;
-  const uint32_t* flags = p.chunk_flag + row * p.n_chunks;
-  int any = 0;
-  for (int c = tid; c < nc; c += kCombThreads) any |= (int)flags[c];
   if (!__syncthreads_or(any)) return;
   __shared__ float lse_g[8];
   for (int g = 0; g < G; ++g) {
