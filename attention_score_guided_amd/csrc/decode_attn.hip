@@ -116,6 +116,7 @@ struct PartialParams {
   float* blk_max;                // [b * blk_seq_stride + kvh * blk_head_stride + block] or null
   float* blk_mean;
   int64_t blk_head_stride, blk_seq_stride;
+  float* lse_out;                // [B][Hq] or null: written by the first chunk of a completed row
 };
 
 // Elements of one 16-byte lane segment.
@@ -660,6 +661,8 @@ void decode_partial_mfma(PartialParams p) {
       cpre[i] = c;
     }
   }
+  constexpr int kNO = (GT * D + kThreads - 1) / kThreads;   // partial outputs per thread
+  [[maybe_unused]] float ov[kNO];
   if constexpr (!HAS_V) {
     if (tid < GT) p.part_ml[ml_base + (size_t)tid * p.n_chunks] = ml_lds[tid];
     if constexpr (!COOP) return;
@@ -733,10 +736,13 @@ void decode_partial_mfma(PartialParams p) {
         for (int e = 0; e < EPL; ++e) red[(wave * GT + h) * D + seg * EPL + e] = acc[h][e];
     }
     __syncthreads();
-    for (int idx = tid; idx < GT * D; idx += kThreads) {
-      const float o = (red[idx] + red[GT * D + idx]) + (red[2 * GT * D + idx] + red[3 * GT * D + idx]);
-      const int h = idx / D, d = idx % D;
-      p.part_o[((ml_base + (size_t)h * p.n_chunks)) * D + d] = o;
+#pragma unroll
+    for (int i = 0; i < kNO; ++i) {
+      const int idx = tid + i * kThreads;
+      ov[i] = idx < GT * D ? (red[idx] + red[GT * D + idx]) + (red[2 * GT * D + idx] + red[3 * GT * D + idx]) : 0.f;
+      // Without in-kernel normalisation the partial output goes out as is;
+      // with it, once the row's lse is known (phase 4).
+      if (!COOP && idx < GT * D) p.part_o[((ml_base + (size_t)(idx / D) * p.n_chunks)) * D + idx % D] = ov[i];
     }
     if (tid < GT) p.part_ml[ml_base + (size_t)tid * p.n_chunks] = ml_lds[tid];
   }
@@ -778,9 +784,22 @@ void decode_partial_mfma(PartialParams p) {
         for (int c = lane; c < nc; c += kWave) l += exp2_hw(fmaf(lse_lds[h * nc + c], kLog2e, -Ms));
         l = wave_sum(l);
         const float lse = M + log2_hw(l) * kLn2;
-        if (lane == 0) fac[h] = exp2_hw((ml_lds[h].x - lse) * kLog2e);
+        if (lane == 0) {
+          fac[h] = exp2_hw((ml_lds[h].x - lse) * kLog2e);
+          if (chunk_id == 0 && p.lse_out) p.lse_out[(size_t)b * p.num_q_heads + h0 + h] = lse;
+        }
       }
       __syncthreads();
+      if constexpr (HAS_V) {
+        // The partial output already weighted by exp(m_chunk - lse): the
+        // combine only sums the chunks of a completed row.
+#pragma unroll
+        for (int i = 0; i < kNO; ++i) {
+          const int idx = tid + i * kThreads;
+          if (idx < GT * D)
+            p.part_o[((ml_base + (size_t)(idx / D) * p.n_chunks)) * D + idx % D] = ov[i] * fac[idx / D];
+        }
+      }
       float f[GT];
 #pragma unroll
       for (int h = 0; h < GT; ++h) f[h] = fac[h];
@@ -874,6 +893,13 @@ void decode_partial_mfma(PartialParams p) {
     } else {
       // The row did not complete in time: hand the chunk-relative values to
       // the fix-up pass, which scales them once the row's lse is known.
+      if constexpr (HAS_V) {
+#pragma unroll
+        for (int i = 0; i < kNO; ++i) {
+          const int idx = tid + i * kThreads;
+          if (idx < GT * D) p.part_o[((ml_base + (size_t)(idx / D) * p.n_chunks)) * D + idx % D] = ov[i];
+        }
+      }
       for (int j = tid; j < n_keys; j += kThreads) {
 #pragma unroll
         for (int h = 0; h < GT; ++h)
@@ -1015,6 +1041,10 @@ struct CombineParams {
   float* blk_max;
   float* blk_mean;
   int64_t blk_head_stride, blk_seq_stride;
+  // 1: chunks that completed in the pass hold exp(m_chunk - lse) o_chunk
+  // (flag 0), the others the plain partial output (flag 1); the row's first
+  // chunk wrote lse when it completed.
+  int prescaled;
 };
 
 constexpr int kCombThreads = 256;
@@ -1059,12 +1089,39 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(CombineParams p) 
     const int c = cg + i * ng;
     pre[i] = (do_out && c < nc) ? po[(size_t)c * D4 + d4] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  const bool fix_head = p.chunk_flag != nullptr && (bh % p.num_q_heads) % p.group == 0;
+  const bool pres = HAS_V && p.prescaled != 0;
   const size_t row = (size_t)b * p.num_kv_heads + (bh % p.num_q_heads) / p.group;
-  const uint32_t* flags = fix_head ? p.chunk_flag + row * p.n_chunks : nullptr;
+  const uint32_t* flags = p.chunk_flag != nullptr ? p.chunk_flag + row * p.n_chunks : nullptr;
+  const bool fix_head = flags != nullptr && (bh % p.num_q_heads) % p.group == 0;
   int any = 0;
-  if (fix_head)
+  if (fix_head || (pres && flags))
     for (int c = tid; c < nc; c += kCombThreads) any |= (int)flags[c];
+
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto add = [&](float w, const float4& v) {
+    o.x = fmaf(w, v.x, o.x); o.y = fmaf(w, v.y, o.y);
+    o.z = fmaf(w, v.z, o.z); o.w = fmaf(w, v.w, o.w);
+  };
+  // Cross-group sum of o and the store of out (divided by den).
+  auto finish_out = [&](float den) {
+    reinterpret_cast<float4*>(red)[cg * D4 + d4] = o;
+    __syncthreads();
+    if (tid < p.D) {
+      float r = 0.f;
+      for (int g = 0; g < ng; ++g) r += red[g * p.D + tid];
+      p.out[(size_t)bh * p.D + tid] = r / den;
+    }
+  };
+  if (pres && !__syncthreads_or(any)) {
+    // Every chunk of the row completed in the pass: out is the plain sum of
+    // the weighted partial outputs, and lse is already written.
+#pragma unroll
+    for (int i = 0; i < kCombPre; ++i)
+      if (cg + i * ng < nc) add(1.f, pre[i]);
+    for (int c = cg + kCombPre * ng; c < nc; c += ng) add(1.f, po[(size_t)c * D4 + d4]);
+    finish_out(1.f);
+    return;
+  }
 
   float M = mv.x;
   for (int c = tid + kCombThreads; c < nc; c += kCombThreads) M = fmaxf(M, ml[c].x);
@@ -1078,25 +1135,21 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(CombineParams p) 
     l = fmaf(w, v.y, l);
   }
   l = block_reduce(l, scratch, false);   // also orders the w_lds writes
+  if (pres) {
+    // Mixed row: weighted chunks count once, plain ones get exp(m_c - lse).
+    const float lse2 = M * kLog2e + log2_hw(l);
+    for (int c = tid; c < nc; c += kCombThreads)
+      w_lds[c] = flags[c] ? exp2_hw(fmaf(ml[c].x, kLog2e, -lse2)) : 1.f;
+    __syncthreads();
+  }
   if (do_out) {
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    auto add = [&](float w, const float4& v) {
-      o.x = fmaf(w, v.x, o.x); o.y = fmaf(w, v.y, o.y);
-      o.z = fmaf(w, v.z, o.z); o.w = fmaf(w, v.w, o.w);
-    };
 #pragma unroll
     for (int i = 0; i < kCombPre; ++i) {
       const int c = cg + i * ng;
       if (c < nc) add(w_lds[c], pre[i]);
     }
     for (int c = cg + kCombPre * ng; c < nc; c += ng) add(w_lds[c], po[(size_t)c * D4 + d4]);
-    reinterpret_cast<float4*>(red)[cg * D4 + d4] = o;
-    __syncthreads();
-    if (tid < p.D) {
-      float r = 0.f;
-      for (int g = 0; g < ng; ++g) r += red[g * p.D + tid];
-      p.out[(size_t)bh * p.D + tid] = r / l;
-    }
+    finish_out(pres ? 1.f : l);
   }
   if (tid == 0) {
     const float v = M + log2_hw(l) * kLn2;
@@ -1386,6 +1439,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   const bool blk = a.blk_bs > 0 && (a.blk_max || a.blk_mean);
   const bool blk_fused = blk && coop && (a.blk_bs & (a.blk_bs - 1)) == 0 && a.blk_bs >= 4 &&
                          a.blk_bs <= 256 && pl.chunk % a.blk_bs == 0;
+  if (coop && use_v) pp.lse_out = a.lse;
   if (blk_fused) {
     pp.blk_bs = a.blk_bs;
     pp.blk_max = a.blk_max;
@@ -1468,6 +1522,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
         cp.cum = a.cum;
         cp.cum_stride = a.cum_stride;
         cp.decay = a.decay;
+        cp.prescaled = use_v ? 1 : 0;
       }
       const dim3 cgrid(a.num_seqs * a.num_q_heads);
       const size_t clds = ((size_t)pl.n_chunks + 4 * kCombThreads + 8) * sizeof(float);
