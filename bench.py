@@ -325,15 +325,17 @@ def llama3_workload(torch, K, synth, args) -> dict:
     Bq, HQq, HKVq = 16, 32, 8
     base = kvt.seq_lens.clone()
     cap = int(base.max()) + steps
+    # score rows span the cache capacity in whole pages (16-byte aligned rows)
+    stride = -(-cap // 16) * 16
     lens = base.clone()
     kv = K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, lens, 16, cap)
-    cum = torch.zeros((Bq, HKVq, cap), device="cuda")
+    cum = torch.zeros((Bq, HKVq, stride), device="cuda")
     out = torch.empty((Bq, HQq, 128), device="cuda")
     ws = torch.empty(K.decode_workspace_bytes(kv, HQq, False), dtype=torch.uint8, device="cuda")
     n_blk = -(-cap // 16)
     bmax = torch.zeros((Bq, HKVq, n_blk), device="cuda")
     bmean = torch.zeros((Bq, HKVq, n_blk), device="cuda")
-    rows = cum.view(Bq * HKVq, cap)
+    rows = cum.view(Bq * HKVq, stride)
     final = (base + steps).to(torch.int32)
     rlens = final.repeat_interleave(HKVq).to(torch.int32)
     budgets = (rlens.double() * 0.2).floor().to(torch.int32)
@@ -346,7 +348,7 @@ def llama3_workload(torch, K, synth, args) -> dict:
         K.decode_attn_scores(kv, cfg["q_steps"][0], HQq, cfg["scale"], out, None, None, K.EMIT_PROBS,
                              cum_w, 1.0, workspace=ws)
     K.block_aggregate(cum_w, final, cap, 16, K.REDUCE_NONE, False, bmax, bmean)
-    K.select_keep(cum_w.view(Bq * HKVq, cap), rlens, cap, 4, 512, budgets, mb, keep, kcnt)
+    K.select_keep(cum_w.view(Bq * HKVq, stride), rlens, cap, 4, 512, budgets, mb, keep, kcnt)
     del cum_w
     torch.cuda.synchronize()
     a, b, c = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
