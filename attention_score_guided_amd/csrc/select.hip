@@ -108,12 +108,20 @@ struct RowsParams {
   int32_t* out_count;
 };
 
-__global__ __launch_bounds__(kRowThreads) void select_rows_kernel(RowsParams p) {
+// LDS of the one-workgroup row selection.
+struct RowLds {
+  int hist[kSubHist][2048];
+  int ws[kRowThreads / kWave];
+  int res[2];
+};
+
+// Selection of row r by one workgroup of kRowThreads threads (every thread
+// calls it).
+__device__ void select_row(const RowsParams& p, int r, RowLds& sh) {
   constexpr int NT = kRowThreads;
-  __shared__ int hist[kSubHist][2048];
-  __shared__ int ws[NT / kWave];
-  __shared__ int res[2];
-  const int r = blockIdx.x;
+  auto& hist = sh.hist;
+  int* ws = sh.ws;
+  int* res = sh.res;
   const int tid = threadIdx.x;
   const int n = p.lengths[r];
   const int B = p.budgets ? p.budgets[r] : p.max_budget;
@@ -250,6 +258,11 @@ __global__ __launch_bounds__(kRowThreads) void select_rows_kernel(RowsParams p) 
   if (tid == 0) p.out_count[r] = out_base;
 }
 
+__global__ __launch_bounds__(kRowThreads) void select_rows_kernel(RowsParams p) {
+  __shared__ RowLds sh;
+  select_row(p, blockIdx.x, sh);
+}
+
 // ---- ROWS mode, split over workgroups (long rows, few rows) ---------------
 // One workgroup per row leaves most of the chip idle when a handful of rows
 // are each 100K+ long.  The same selection is then cut into segments of
@@ -263,10 +276,19 @@ __global__ __launch_bounds__(kRowThreads) void select_rows_kernel(RowsParams p) 
 constexpr int kSegQuantum = 4096;      // segment lengths are multiples of this
 constexpr int kSegTarget = 1024;       // aim for about this many workgroups per kernel
 constexpr int kSegThreads = 256;
-constexpr int kOutSeg = 4096;          // count / output segment: 4 float4 per thread
-constexpr int kSplitMinLen = 65536;    // split rows at least this long (below, the one-workgroup
-                                       // kernel beats the nine launches of the split) ...
-constexpr int kSplitMaxRows = 512;     // ... when there are fewer rows than this
+constexpr int kOutSeg = 4096;          // compaction segment: 4 float4 per thread
+constexpr int kCapSeg = 1024;          // entries stored per compaction segment
+constexpr int kFinCand = 8192;         // boundary-digit candidates the final kernel holds in LDS
+constexpr int kFinSegs = kRowThreads;  // compaction segments per row the final kernel handles
+#ifndef KVSEL_SPLIT_MIN_LEN
+#define KVSEL_SPLIT_MIN_LEN 65536
+#endif
+#ifndef KVSEL_SPLIT_MAX_ROWS
+#define KVSEL_SPLIT_MAX_ROWS 512
+#endif
+constexpr int kSplitMinLen = KVSEL_SPLIT_MIN_LEN;    // split rows at least this long (below, the
+                                                     // one-workgroup kernel beats the split's launches)
+constexpr int kSplitMaxRows = KVSEL_SPLIT_MAX_ROWS;  // ... when there are fewer rows than this
 
 struct RowPlan {
   int n, lo, hi, k, fsize;
@@ -287,9 +309,10 @@ __device__ __forceinline__ RowPlan row_plan(const RowsParams& p, int r) {
 
 struct SplitParams {
   RowsParams rp;
-  uint32_t* ghist;   // [rows][2048], zero between passes
-  int4* state;       // [rows]: prefix, pmask, rank, -
-  int2* counts;      // [rows][n_oseg]: definite keeps, ties
+  uint32_t* ghist;   // [rows][2048], zero between calls
+  int4* state;       // [rows]: prefix, pmask, rank after the first digit, -
+  int2* counts;      // [rows][n_oseg]: stored entries, candidates
+  uint32_t* slots;   // [rows][n_oseg][kCapSeg]: positions past the first digit, bit 31 = candidate
   int n_seg, seg_len;  // histogram passes: segments of the middle
   int n_oseg;          // count / output: segments of kOutSeg positions of the row
   bool vec;          // rows 16-byte aligned: float4 loads
@@ -391,23 +414,6 @@ __global__ __launch_bounds__(kSegThreads) void select_split_digit(SplitParams sp
                             rank - above, 0);
 }
 
-// Keep rule of position j (after the three passes): forced positions, middle
-// keys above tau, and middle keys equal to tau (ties, ranked by position).
-__device__ __forceinline__ void keep_class(const RowPlan& q, uint32_t tau, int j, float v, int& def, int& eq) {
-  def = 0;
-  eq = 0;
-  if (j >= q.n) return;
-  if (q.k == 0) {
-    def = (q.keep_all || j < q.lo || j >= q.hi) ? 1 : 0;
-    return;
-  }
-  const bool mid = j >= q.lo && j < q.hi;
-  if (!mid) { def = 1; return; }
-  const uint32_t kk = order_key(v);
-  def = kk > tau ? 1 : 0;
-  eq = kk == tau ? 1 : 0;
-}
-
 // The kOutSeg positions of segment s of row r, one float4 per thread and
 // iteration (4 iterations), all loaded up front.
 __device__ __forceinline__ void load_out_seg(const SplitParams& sp, const RowPlan& q, const float* row,
@@ -419,101 +425,166 @@ __device__ __forceinline__ void load_out_seg(const SplitParams& sp, const RowPla
   }
 }
 
-__global__ __launch_bounds__(kSegThreads) void select_split_count(SplitParams sp) {
+// Middle positions of output segment s (kOutSeg positions) that pass the
+// first digit: above the row's boundary digit (kept whatever the rest of
+// the selection decides) or equal to it (candidates).  They are stored in
+// position order, at most kCapSeg per segment, bit 31 marking a candidate;
+// the segment's (stored-or-not count, candidate count) goes to `counts`.
+__global__ __launch_bounds__(kSegThreads) void select_split_compact(SplitParams sp) {
   constexpr int IT = kOutSeg / (4 * kSegThreads);
   __shared__ int ws[kSegThreads / kWave];
   const RowsParams& p = sp.rp;
   const int r = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
   const RowPlan q = row_plan(p, r);
-  const int j_lo = s * kOutSeg, j_hi = min(j_lo + kOutSeg, q.n);
-  if (j_lo >= j_hi) return;
-  const uint32_t tau = q.k ? (uint32_t)sp.state[r].x : 0u;
+  if (q.k == 0) return;
+  const int sb = s * kOutSeg, sb_hi = min(sb + kOutSeg, q.n);
+  int2* cnt = sp.counts + (size_t)r * sp.n_oseg + s;
+  if (max(sb, q.lo) >= min(sb_hi, q.hi)) {
+    if (tid == 0) *cnt = make_int2(0, 0);
+    return;
+  }
+  const uint32_t d0 = (uint32_t)sp.state[r].x >> 21;
   const float* row = p.scores + (size_t)r * p.stride;
   float4 v[IT];
-  load_out_seg(sp, q, row, j_lo, j_hi, v);
-  int nd = 0, ne = 0;
+  load_out_seg(sp, q, row, sb, sb_hi, v);
+  uint32_t* slot = sp.slots + ((size_t)r * sp.n_oseg + s) * kCapSeg;
+  int base = 0, n_cand = 0;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const int j0 = j_lo + (it * kSegThreads + tid) * 4;
+    const int j0 = sb + (it * kSegThreads + tid) * 4;
     const float e4[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+    int f[4], packed = 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      int d, e;
-      keep_class(q, tau, j0 + c < j_hi ? j0 + c : q.n, e4[c], d, e);
-      nd += d;
-      ne += e;
+      const int j = j0 + c;
+      const bool mid = j >= q.lo && j < q.hi && j < sb_hi;
+      const uint32_t dig = order_key(e4[c]) >> 21;
+      f[c] = !mid ? 0 : dig > d0 ? 1 : dig == d0 ? 2 : 0;
+      packed += (f[c] != 0) + ((f[c] == 2) << 16);   // stored | candidates << 16 (both <= 4096)
     }
+    int tot;
+    int pos = base + (block_exclusive_scan<kSegThreads>(packed, ws, tot) & 0xFFFF);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (f[c]) {
+        if (pos < kCapSeg) slot[pos] = (uint32_t)(j0 + c) | (f[c] == 2 ? 0x80000000u : 0u);
+        ++pos;
+      }
+    }
+    base += tot & 0xFFFF;
+    n_cand += tot >> 16;
   }
-  int td, te;
-  block_exclusive_scan<kSegThreads>(nd, ws, td);
-  block_exclusive_scan<kSegThreads>(ne, ws, te);
-  if (tid == 0) sp.counts[(size_t)r * sp.n_oseg + s] = make_int2(td, te);
+  if (tid == 0) *cnt = make_int2(base, n_cand);
 }
 
-__global__ __launch_bounds__(kSegThreads) void select_split_out(SplitParams sp) {
-  constexpr int IT = kOutSeg / (4 * kSegThreads);
-  __shared__ int ws[kSegThreads / kWave];
+// Segment of flat entry f: the s with pre[s] <= f < pre[s + 1].
+__device__ __forceinline__ int seg_of(const int* pre, int n_seg, int f) {
+  int lo = 0, hi = n_seg - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= f) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// One workgroup per row: the remaining two digits among the row's
+// candidates (held in LDS), then the ordered output of the stored entries
+// between the forced ranges.  A row whose segments overflowed their slots,
+// or with more candidates than LDS holds, is selected from its scores by
+// the one-workgroup algorithm instead; the result is the same.
+__global__ __launch_bounds__(kRowThreads) void select_split_final(SplitParams sp) {
+  constexpr int NT = kRowThreads;
+  __shared__ RowLds sh;
+  __shared__ uint32_t ckey[kFinCand];
+  __shared__ int seg_pre[kFinSegs + 1];
+  __shared__ int n_seen;
   const RowsParams& p = sp.rp;
-  const int r = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
+  const int r = blockIdx.x, tid = threadIdx.x;
   const RowPlan q = row_plan(p, r);
-  const int j_lo = s * kOutSeg, j_hi = min(j_lo + kOutSeg, q.n);
-  if (j_lo >= j_hi) return;
+  const int n_seg = (q.n + kOutSeg - 1) / kOutSeg;
+  if (q.k == 0 || n_seg > kFinSegs) {
+    select_row(p, r, sh);
+    return;
+  }
+  int* ws = sh.ws;
+  const int2 c = tid < n_seg ? sp.counts[(size_t)r * sp.n_oseg + tid] : make_int2(0, 0);
+  int tot_int, tot_cand;
+  const int pre = block_exclusive_scan<NT>(c.x, ws, tot_int);
+  block_exclusive_scan<NT>(c.y, ws, tot_cand);
+  if (tid < n_seg) seg_pre[tid] = pre;
+  if (tid == 0) {
+    seg_pre[n_seg] = tot_int;
+    n_seen = 0;
+  }
+  if (__syncthreads_or(c.x > kCapSeg) || tot_cand > kFinCand) {
+    select_row(p, r, sh);
+    return;
+  }
   const float* row = p.scores + (size_t)r * p.stride;
-  float4 v[IT];
-  load_out_seg(sp, q, row, j_lo, j_hi, v);
-  const int4 st = q.k ? sp.state[r] : make_int4(0, 0, 0, 0);
-  const uint32_t tau = (uint32_t)st.x;
-  const int ties_needed = st.z;
-  // definite keeps and ties of the segments before this one (and the total)
-  const int n_seg_r = (q.n + kOutSeg - 1) / kOutSeg;
-  int d_before = 0, e_before = 0, d_all = 0, e_all = 0;
-  for (int i = tid; i < n_seg_r; i += kSegThreads) {
-    const int2 c = sp.counts[(size_t)r * sp.n_oseg + i];
-    d_all += c.x;
-    e_all += c.y;
-    if (i < s) { d_before += c.x; e_before += c.y; }
+  const uint32_t* slots = sp.slots + (size_t)r * sp.n_oseg * kCapSeg;
+  auto entry = [&](int f) -> uint32_t {
+    const int s = seg_of(seg_pre, n_seg, f);
+    return slots[(size_t)s * kCapSeg + (f - seg_pre[s])];
+  };
+  // candidate keys into LDS (any order: only histograms read them)
+  for (int f = tid; f < tot_int; f += NT) {
+    const uint32_t e = entry(f);
+    if (e >> 31) ckey[atomicAdd(&n_seen, 1)] = order_key(row[e & 0x7FFFFFFFu]);
   }
-  block_exclusive_scan<kSegThreads>(d_before, ws, d_before);
-  block_exclusive_scan<kSegThreads>(e_before, ws, e_before);
-  if (s == 0) {
-    block_exclusive_scan<kSegThreads>(d_all, ws, d_all);
-    block_exclusive_scan<kSegThreads>(e_all, ws, e_all);
-    if (tid == 0) p.out_count[r] = d_all + min(e_all, ties_needed);
+  __syncthreads();
+  const int4 st = sp.state[r];
+  uint32_t prefix = (uint32_t)st.x, pmask = (uint32_t)st.y;
+  int rank = st.z;
+  int* hist = sh.hist[0];
+  constexpr int kShift[2] = {10, 0};
+  constexpr int kWidth[2] = {11, 10};
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shf = kShift[pass];
+    const uint32_t dmask = (1u << kWidth[pass]) - 1u;
+    for (int i = tid; i < 2048; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < tot_cand; i += NT) {
+      const uint32_t kk = ckey[i];
+      if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shf) & dmask], 1);
+    }
+    __syncthreads();
+    int above;
+    const int d = find_digit<NT>(hist, 1 << kWidth[pass], rank, ws, sh.res, above);
+    rank -= above;
+    prefix |= (uint32_t)d << shf;
+    pmask |= dmask << shf;
   }
+  const uint32_t tau = prefix;
+  const int ties_needed = rank;
   int32_t* out = p.out_idx + (size_t)r * p.out_stride;
-  int tie_base = e_before;
-  int out_base = d_before + min(e_before, ties_needed);
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int j0 = j_lo + (it * kSegThreads + tid) * 4;
-    int eq[4], keep[4];
-    int n_eq = 0;
-    const float e4[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = j0 + i;
-      keep_class(q, tau, j < j_hi ? j : q.n, e4[i], keep[i], eq[i]);
-      n_eq += eq[i];
-    }
-    int eq_total;
-    const int eq_before = tie_base + block_exclusive_scan<kSegThreads>(n_eq, ws, eq_total);
-    int run = eq_before, n_keep = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (eq[i]) {
-        keep[i] = run < ties_needed ? 1 : 0;
-        ++run;
+  for (int j = tid; j < q.lo; j += NT) out[j] = j;
+  int out_base = q.lo, tie_base = 0;
+  for (int f0 = 0; f0 < tot_int; f0 += NT) {
+    const int f = f0 + tid;
+    int keep = 0, eq = 0, j = 0;
+    if (f < tot_int) {
+      const uint32_t e = entry(f);
+      j = (int)(e & 0x7FFFFFFFu);
+      if (e >> 31) {
+        const uint32_t kk = order_key(row[j]);
+        keep = kk > tau ? 1 : 0;
+        eq = kk == tau ? 1 : 0;
+      } else {
+        keep = 1;
       }
-      n_keep += keep[i];
     }
-    int keep_total;
-    int pos = out_base + block_exclusive_scan<kSegThreads>(n_keep, ws, keep_total);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (keep[i]) out[pos++] = j0 + i;
+    int eq_total, keep_total;
+    const int eq_before = tie_base + block_exclusive_scan<NT>(eq, ws, eq_total);
+    if (eq) keep = eq_before < ties_needed ? 1 : 0;
+    const int pos = out_base + block_exclusive_scan<NT>(keep, ws, keep_total);
+    if (keep) out[pos] = j;
     tie_base += eq_total;
     out_base += keep_total;
   }
+  for (int j = q.hi + tid; j < q.n; j += NT) out[out_base + (j - q.hi)] = j;
+  if (tid == 0) p.out_count[r] = out_base + (q.n - q.hi);
 }
 
 inline bool use_split(int rows, int max_len) { return rows < kSplitMaxRows && max_len >= kSplitMinLen; }
@@ -526,45 +597,41 @@ inline int split_seg_len(int rows, int max_len) {
   return std::max(kSegQuantum, (len + kSegQuantum - 1) / kSegQuantum * kSegQuantum);
 }
 
-inline size_t split_layout(int rows, int max_len, size_t* o_state, size_t* o_counts) {
+inline size_t split_layout(int rows, int max_len, size_t* o_state, size_t* o_counts, size_t* o_slots) {
   const int n_seg = (max_len + kOutSeg - 1) / kOutSeg;
   const size_t a = ((size_t)rows * 2048 * sizeof(uint32_t) + 255) & ~size_t(255);
   const size_t b = ((size_t)rows * sizeof(int4) + 255) & ~size_t(255);
   const size_t c = ((size_t)rows * n_seg * sizeof(int2) + 255) & ~size_t(255);
+  const size_t d = ((size_t)rows * n_seg * kCapSeg * sizeof(uint32_t) + 255) & ~size_t(255);
   if (o_state) *o_state = a;
   if (o_counts) *o_counts = a + b;
-  return a + b + c;
+  if (o_slots) *o_slots = a + b + c;
+  return a + b + c + d;
 }
 
 // The global histograms must start at zero: they are cleared here once per
-// call (every digit kernel leaves its row's histogram cleared again).
+// call (the digit kernel leaves its row's histogram cleared again).
 __global__ void select_split_zero(uint32_t* gh, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
     gh[i] = 0u;
 }
 
 hipError_t launch_split(const RowsParams& rp, int rows, int max_len, void* workspace, hipStream_t stream) {
-  size_t o_state, o_counts;
-  split_layout(rows, max_len, &o_state, &o_counts);
+  size_t o_state, o_counts, o_slots;
+  split_layout(rows, max_len, &o_state, &o_counts, &o_slots);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const int seg_len = split_seg_len(rows, max_len);
   SplitParams sp{rp, reinterpret_cast<uint32_t*>(ws), reinterpret_cast<int4*>(ws + o_state),
-                 reinterpret_cast<int2*>(ws + o_counts), (max_len + seg_len - 1) / seg_len, seg_len,
-                 (max_len + kOutSeg - 1) / kOutSeg,
+                 reinterpret_cast<int2*>(ws + o_counts), reinterpret_cast<uint32_t*>(ws + o_slots),
+                 (max_len + seg_len - 1) / seg_len, seg_len, (max_len + kOutSeg - 1) / kOutSeg,
                  (rp.stride & 3) == 0 && (reinterpret_cast<uintptr_t>(rp.scores) & 15) == 0};
-  const dim3 seg_grid(sp.n_seg, rows);
   const size_t nh = (size_t)rows * 2048;
   hipLaunchKernelGGL(select_split_zero, dim3((unsigned)std::min<size_t>((nh + 255) / 256, 1024)), dim3(256), 0,
                      stream, sp.ghist, nh);
-  hipLaunchKernelGGL(select_split_hist<0>, seg_grid, dim3(kSegThreads), 0, stream, sp);
+  hipLaunchKernelGGL(select_split_hist<0>, dim3(sp.n_seg, rows), dim3(kSegThreads), 0, stream, sp);
   hipLaunchKernelGGL(select_split_digit<0>, dim3(rows), dim3(kSegThreads), 0, stream, sp);
-  hipLaunchKernelGGL(select_split_hist<1>, seg_grid, dim3(kSegThreads), 0, stream, sp);
-  hipLaunchKernelGGL(select_split_digit<1>, dim3(rows), dim3(kSegThreads), 0, stream, sp);
-  hipLaunchKernelGGL(select_split_hist<2>, seg_grid, dim3(kSegThreads), 0, stream, sp);
-  hipLaunchKernelGGL(select_split_digit<2>, dim3(rows), dim3(kSegThreads), 0, stream, sp);
-  const dim3 out_grid(sp.n_oseg, rows);
-  hipLaunchKernelGGL(select_split_count, out_grid, dim3(kSegThreads), 0, stream, sp);
-  hipLaunchKernelGGL(select_split_out, out_grid, dim3(kSegThreads), 0, stream, sp);
+  hipLaunchKernelGGL(select_split_compact, dim3(sp.n_oseg, rows), dim3(kSegThreads), 0, stream, sp);
+  hipLaunchKernelGGL(select_split_final, dim3(rows), dim3(kRowThreads), 0, stream, sp);
   return hipGetLastError();
 }
 
@@ -696,7 +763,7 @@ __global__ __launch_bounds__(kSelThreads) void global_output_kernel(const uint64
 }  // namespace
 
 size_t select_workspace_bytes(int rows, int max_len, int mode) {
-  if (mode != 1) return use_split(rows, max_len) ? split_layout(rows, max_len, nullptr, nullptr) : 0;
+  if (mode != 1) return use_split(rows, max_len) ? split_layout(rows, max_len, nullptr, nullptr, nullptr) : 0;
   return ((size_t)rows * max_len * sizeof(uint64_t) + 255 & ~size_t(255)) + 256;
 }
 

@@ -46,6 +46,15 @@ constexpr int kOut = kStage - 2 * kHalo;  // pass 2: keys voted per chunk
 #ifndef KVSEL_VOTE_WGS
 #define KVSEL_VOTE_WGS 2048
 #endif
+#ifndef KVSEL_VOTE_TN1
+#define KVSEL_VOTE_TN1 4     // pass 1: fully visible tiles computed together
+#endif
+#ifndef KVSEL_VOTE_WPE1
+#define KVSEL_VOTE_WPE1 0    // >0: occupancy hint (waves per SIMD) for pass 1
+#endif
+#ifndef KVSEL_VOTE_WPE2
+#define KVSEL_VOTE_WPE2 0    // >0: occupancy hint (waves per SIMD) for pass 2
+#endif
 constexpr int kMaxWgs = KVSEL_VOTE_WGS;  // grid target: chunks are grouped into runs beyond it
 constexpr float kRescale = 64.f;        // pass 1: move the reference past this (base-2 units)
 
@@ -170,7 +179,9 @@ __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2)
 // them (vector loads retire in order).  NHW == 0: the rows are reloaded per
 // chunk and head (wide groups).
 template <int D, int RT, int NHW>
-__global__ __launch_bounds__(kThreads) void snapkv_pass1(VoteParams p) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(KVSEL_VOTE_WPE1 > 0 ? KVSEL_VOTE_WPE1 : 1)))
+void snapkv_pass1(VoteParams p) {
   constexpr int NU = D / 32;
   constexpr bool PRE = NHW > 0;
   constexpr int NS = PRE ? NHW : 1;      // register slots of window rows
@@ -295,8 +306,9 @@ __global__ __launch_bounds__(kThreads) void snapkv_pass1(VoteParams p) {
   };
   auto tiles = [&](int start, int t_lo, int t_hi, const bf16x8 (&q)[RT][NU], float (&m_)[RT], float (&l_)[RT]) {
     int t = t_lo;
-    for (; t + 3 < t_hi && start + t * 16 + 63 < prefix; t += 4)
-      tile_multi(std::integral_constant<int, 4>{}, start, t, q, m_, l_);
+    constexpr int TN = KVSEL_VOTE_TN1;
+    for (; t + TN - 1 < t_hi && start + t * 16 + 16 * TN - 1 < prefix; t += TN)
+      tile_multi(std::integral_constant<int, TN>{}, start, t, q, m_, l_);
     for (; t < t_hi; ++t) tile(start, t, q, m_, l_);
   };
 
@@ -377,7 +389,9 @@ __global__ __launch_bounds__(256) void snapkv_lse(const float2* part_ml, const i
 // lane%16) holds rows rt*16 + (lane/16)*4 + i, i < 4.  NHW as in pass 1
 // (the rows' lse are held in registers with them).
 template <int D, int RT, int NHW>
-__global__ __launch_bounds__(kThreads) void snapkv_pass2(VoteParams p) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(KVSEL_VOTE_WPE2 > 0 ? KVSEL_VOTE_WPE2 : 1)))
+void snapkv_pass2(VoteParams p) {
   constexpr int NU = D / 32;
   constexpr bool PRE = NHW > 0;
   constexpr int NS = PRE ? NHW : 1;

@@ -159,3 +159,50 @@ def test_rows_long_rows_split_over_workgroups(seed):
         K.select_keep(sc, lens, max_len, sinks, window, bud, max_budget, idx, cnt, workspace=ws)
         torch.cuda.synchronize()
         _check_rows(scores, lengths, sinks, window, budgets, idx.cpu().numpy(), cnt.cpu().numpy())
+
+
+@pytest.mark.parametrize("case", ["gaussian", "quantised", "clustered", "many_candidates", "dense_segment"])
+def test_rows_long_rows_compaction(case):
+    """Long rows with a small keep fraction (the indexer and vote shape):
+    after the first digit, the positions that pass it are compacted per
+    segment and the selection finishes on them.  Cases cover ties at the
+    threshold (quantised scores), kept positions clustered in a few
+    segments, more boundary-digit candidates than the final stage holds,
+    and a segment with more passing positions than its slots (both fall
+    back to the per-row selection); every result must equal the oracle's."""
+    K = _K()
+    rng = np.random.default_rng({"gaussian": 11, "quantised": 12, "clustered": 13,
+                                 "many_candidates": 14, "dense_segment": 15}[case])
+    rows, n = 6, 131072
+    lengths = [n, n - 1, 65536, 100003, 70001, n]
+    scores = rng.standard_normal((rows, n)).astype(np.float32)
+    budgets = [2048, 2048, 1500, 4096, 777, 2048]
+    sinks, window = (4, 512) if case in ("gaussian", "clustered") else (0, 0)
+    if case == "quantised":
+        scores = np.round(scores * 64.0).astype(np.float32) / 64.0        # heavy ties at tau
+    if case == "clustered":
+        for r in range(rows):                                            # top keys in a few segments
+            for c in rng.integers(2000, lengths[r] - 2000, size=3):
+                scores[r, c - 300:c + 300] += 4.0
+    if case == "many_candidates":
+        # ~12% of positions share the threshold's first digit, spread evenly:
+        # under the slot cap per segment, but more than the final stage holds
+        sel = rng.random((rows, n)) < 0.12
+        scores[sel] = (1.0 + 0.18 * rng.random(int(sel.sum()))).astype(np.float32)
+        scores[~sel] = np.minimum(scores[~sel], 0.9)
+    if case == "dense_segment":
+        scores[:, 8192:8192 + 4096] = 3.0 + rng.random((rows, 4096)).astype(np.float32)  # one full segment passes
+    note(f"select compaction case={case}")
+    max_budget = max(budgets)
+    out_stride = max(max_budget, sinks + window)
+    sc = torch.from_numpy(scores).cuda()
+    lens = torch.tensor(lengths, dtype=torch.int32).cuda()
+    bud = torch.tensor(budgets, dtype=torch.int32).cuda()
+    nbytes = K.select_workspace_bytes(rows, n, K.SELECT_ROWS)
+    ws = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        idx = torch.full((rows, out_stride), -5, dtype=torch.int32).cuda()
+        cnt = torch.full((rows,), -1, dtype=torch.int32).cuda()
+        K.select_keep(sc, lens, n, sinks, window, bud, max_budget, idx, cnt, workspace=ws)
+        torch.cuda.synchronize()
+        _check_rows(scores, lengths, sinks, window, budgets, idx.cpu().numpy(), cnt.cpu().numpy())
