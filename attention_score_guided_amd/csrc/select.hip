@@ -278,7 +278,7 @@ constexpr int kSegTarget = 1024;       // aim for about this many workgroups per
 constexpr int kSegThreads = 256;
 constexpr int kOutSeg = 4096;          // compaction segment: 4 float4 per thread
 constexpr int kCapSeg = 1024;          // entries stored per compaction segment
-constexpr int kFinCand = 8192;         // boundary-digit candidates the final kernel holds in LDS
+constexpr int kFinEnt = 12288;         // stored entries the final kernel holds in LDS
 constexpr int kFinSegs = kRowThreads;  // compaction segments per row the final kernel handles
 #ifndef KVSEL_SPLIT_MIN_LEN
 #define KVSEL_SPLIT_MIN_LEN 65536
@@ -312,7 +312,7 @@ struct SplitParams {
   uint32_t* ghist;   // [rows][2048], zero between calls
   int4* state;       // [rows]: prefix, pmask, rank after the first digit, -
   int2* counts;      // [rows][n_oseg]: stored entries, candidates
-  uint32_t* slots;   // [rows][n_oseg][kCapSeg]: positions past the first digit, bit 31 = candidate
+  uint2* slots;      // [rows][n_oseg][kCapSeg]: (position | candidate << 31, key) past the first digit
   int n_seg, seg_len;  // histogram passes: segments of the middle
   int n_oseg;          // count / output: segments of kOutSeg positions of the row
   bool vec;          // rows 16-byte aligned: float4 loads
@@ -430,6 +430,7 @@ __device__ __forceinline__ void load_out_seg(const SplitParams& sp, const RowPla
 // the selection decides) or equal to it (candidates).  They are stored in
 // position order, at most kCapSeg per segment, bit 31 marking a candidate;
 // the segment's (stored-or-not count, candidate count) goes to `counts`.
+// Each entry carries its order key.
 __global__ __launch_bounds__(kSegThreads) void select_split_compact(SplitParams sp) {
   constexpr int IT = kOutSeg / (4 * kSegThreads);
   __shared__ int ws[kSegThreads / kWave];
@@ -447,18 +448,20 @@ __global__ __launch_bounds__(kSegThreads) void select_split_compact(SplitParams 
   const float* row = p.scores + (size_t)r * p.stride;
   float4 v[IT];
   load_out_seg(sp, q, row, sb, sb_hi, v);
-  uint32_t* slot = sp.slots + ((size_t)r * sp.n_oseg + s) * kCapSeg;
+  uint2* slot = sp.slots + ((size_t)r * sp.n_oseg + s) * kCapSeg;
   int base = 0, n_cand = 0;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int j0 = sb + (it * kSegThreads + tid) * 4;
     const float e4[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
     int f[4], packed = 0;
+    uint32_t kk[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int j = j0 + c;
       const bool mid = j >= q.lo && j < q.hi && j < sb_hi;
-      const uint32_t dig = order_key(e4[c]) >> 21;
+      kk[c] = order_key(e4[c]);
+      const uint32_t dig = kk[c] >> 21;
       f[c] = !mid ? 0 : dig > d0 ? 1 : dig == d0 ? 2 : 0;
       packed += (f[c] != 0) + ((f[c] == 2) << 16);   // stored | candidates << 16 (both <= 4096)
     }
@@ -467,7 +470,7 @@ __global__ __launch_bounds__(kSegThreads) void select_split_compact(SplitParams 
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       if (f[c]) {
-        if (pos < kCapSeg) slot[pos] = (uint32_t)(j0 + c) | (f[c] == 2 ? 0x80000000u : 0u);
+        if (pos < kCapSeg) slot[pos] = make_uint2((uint32_t)(j0 + c) | (f[c] == 2 ? 0x80000000u : 0u), kk[c]);
         ++pos;
       }
     }
@@ -488,17 +491,18 @@ __device__ __forceinline__ int seg_of(const int* pre, int n_seg, int f) {
   return lo;
 }
 
-// One workgroup per row: the remaining two digits among the row's
-// candidates (held in LDS), then the ordered output of the stored entries
-// between the forced ranges.  A row whose segments overflowed their slots,
-// or with more candidates than LDS holds, is selected from its scores by
-// the one-workgroup algorithm instead; the result is the same.
+// One workgroup per row: the row's stored entries are loaded into LDS in one
+// batch; the remaining two digits are resolved among the candidates there,
+// then the entries are written out in position order between the forced
+// ranges.  A row whose segments overflowed their slots, or with more
+// entries than LDS holds, is selected from its scores by the one-workgroup
+// algorithm instead; the result is the same.
 __global__ __launch_bounds__(kRowThreads) void select_split_final(SplitParams sp) {
   constexpr int NT = kRowThreads;
+  constexpr int EPT = 4;                  // entries per thread and output step
   __shared__ RowLds sh;
-  __shared__ uint32_t ckey[kFinCand];
+  __shared__ uint2 ent[kFinEnt];
   __shared__ int seg_pre[kFinSegs + 1];
-  __shared__ int n_seen;
   const RowsParams& p = sp.rp;
   const int r = blockIdx.x, tid = threadIdx.x;
   const RowPlan q = row_plan(p, r);
@@ -509,29 +513,29 @@ __global__ __launch_bounds__(kRowThreads) void select_split_final(SplitParams sp
   }
   int* ws = sh.ws;
   const int2 c = tid < n_seg ? sp.counts[(size_t)r * sp.n_oseg + tid] : make_int2(0, 0);
-  int tot_int, tot_cand;
-  const int pre = block_exclusive_scan<NT>(c.x, ws, tot_int);
-  block_exclusive_scan<NT>(c.y, ws, tot_cand);
+  int tot;
+  const int pre = block_exclusive_scan<NT>(c.x, ws, tot);
   if (tid < n_seg) seg_pre[tid] = pre;
-  if (tid == 0) {
-    seg_pre[n_seg] = tot_int;
-    n_seen = 0;
-  }
-  if (__syncthreads_or(c.x > kCapSeg) || tot_cand > kFinCand) {
+  if (tid == 0) seg_pre[n_seg] = tot;
+  if (__syncthreads_or(c.x > kCapSeg) || tot > kFinEnt) {
     select_row(p, r, sh);
     return;
   }
-  const float* row = p.scores + (size_t)r * p.stride;
-  const uint32_t* slots = sp.slots + (size_t)r * sp.n_oseg * kCapSeg;
-  auto entry = [&](int f) -> uint32_t {
-    const int s = seg_of(seg_pre, n_seg, f);
-    return slots[(size_t)s * kCapSeg + (f - seg_pre[s])];
-  };
-  // candidate keys into LDS (any order: only histograms read them)
-  for (int f = tid; f < tot_int; f += NT) {
-    const uint32_t e = entry(f);
-    if (e >> 31) ckey[atomicAdd(&n_seen, 1)] = order_key(row[e & 0x7FFFFFFFu]);
+  // every entry's load is issued before any is stored
+  const uint2* slots = sp.slots + (size_t)r * sp.n_oseg * kCapSeg;
+  constexpr int kLoads = (kFinEnt + NT - 1) / NT;
+  uint2 e[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int f = tid + i * NT;
+    if (f < tot) {
+      const int sg = seg_of(seg_pre, n_seg, f);
+      e[i] = slots[(size_t)sg * kCapSeg + (f - seg_pre[sg])];
+    }
   }
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i)
+    if (tid + i * NT < tot) ent[tid + i * NT] = e[i];
   __syncthreads();
   const int4 st = sp.state[r];
   uint32_t prefix = (uint32_t)st.x, pmask = (uint32_t)st.y;
@@ -545,9 +549,9 @@ __global__ __launch_bounds__(kRowThreads) void select_split_final(SplitParams sp
     const uint32_t dmask = (1u << kWidth[pass]) - 1u;
     for (int i = tid; i < 2048; i += NT) hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < tot_cand; i += NT) {
-      const uint32_t kk = ckey[i];
-      if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shf) & dmask], 1);
+    for (int i = tid; i < tot; i += NT) {
+      const uint2 v = ent[i];
+      if ((v.x >> 31) && (v.y & pmask) == prefix) atomicAdd(&hist[(v.y >> shf) & dmask], 1);
     }
     __syncthreads();
     int above;
@@ -561,25 +565,36 @@ __global__ __launch_bounds__(kRowThreads) void select_split_final(SplitParams sp
   int32_t* out = p.out_idx + (size_t)r * p.out_stride;
   for (int j = tid; j < q.lo; j += NT) out[j] = j;
   int out_base = q.lo, tie_base = 0;
-  for (int f0 = 0; f0 < tot_int; f0 += NT) {
-    const int f = f0 + tid;
-    int keep = 0, eq = 0, j = 0;
-    if (f < tot_int) {
-      const uint32_t e = entry(f);
-      j = (int)(e & 0x7FFFFFFFu);
-      if (e >> 31) {
-        const uint32_t kk = order_key(row[j]);
-        keep = kk > tau ? 1 : 0;
-        eq = kk == tau ? 1 : 0;
-      } else {
-        keep = 1;
+  for (int f0 = 0; f0 < tot; f0 += NT * EPT) {
+    int keep[EPT], eq[EPT], jv[EPT], n_eq = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int f = f0 + tid * EPT + i;
+      keep[i] = eq[i] = jv[i] = 0;
+      if (f < tot) {
+        const uint2 v = ent[f];
+        jv[i] = (int)(v.x & 0x7FFFFFFFu);
+        if (v.x >> 31) {
+          keep[i] = v.y > tau ? 1 : 0;
+          eq[i] = v.y == tau ? 1 : 0;
+        } else {
+          keep[i] = 1;
+        }
       }
+      n_eq += eq[i];
     }
     int eq_total, keep_total;
-    const int eq_before = tie_base + block_exclusive_scan<NT>(eq, ws, eq_total);
-    if (eq) keep = eq_before < ties_needed ? 1 : 0;
-    const int pos = out_base + block_exclusive_scan<NT>(keep, ws, keep_total);
-    if (keep) out[pos] = j;
+    int run = tie_base + block_exclusive_scan<NT>(n_eq, ws, eq_total);
+    int n_keep = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      if (eq[i]) keep[i] = run++ < ties_needed ? 1 : 0;
+      n_keep += keep[i];
+    }
+    int pos = out_base + block_exclusive_scan<NT>(n_keep, ws, keep_total);
+#pragma unroll
+    for (int i = 0; i < EPT; ++i)
+      if (keep[i]) out[pos++] = jv[i];
     tie_base += eq_total;
     out_base += keep_total;
   }
@@ -602,7 +617,7 @@ inline size_t split_layout(int rows, int max_len, size_t* o_state, size_t* o_cou
   const size_t a = ((size_t)rows * 2048 * sizeof(uint32_t) + 255) & ~size_t(255);
   const size_t b = ((size_t)rows * sizeof(int4) + 255) & ~size_t(255);
   const size_t c = ((size_t)rows * n_seg * sizeof(int2) + 255) & ~size_t(255);
-  const size_t d = ((size_t)rows * n_seg * kCapSeg * sizeof(uint32_t) + 255) & ~size_t(255);
+  const size_t d = ((size_t)rows * n_seg * kCapSeg * sizeof(uint2) + 255) & ~size_t(255);
   if (o_state) *o_state = a;
   if (o_counts) *o_counts = a + b;
   if (o_slots) *o_slots = a + b + c;
@@ -622,7 +637,7 @@ hipError_t launch_split(const RowsParams& rp, int rows, int max_len, void* works
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const int seg_len = split_seg_len(rows, max_len);
   SplitParams sp{rp, reinterpret_cast<uint32_t*>(ws), reinterpret_cast<int4*>(ws + o_state),
-                 reinterpret_cast<int2*>(ws + o_counts), reinterpret_cast<uint32_t*>(ws + o_slots),
+                 reinterpret_cast<int2*>(ws + o_counts), reinterpret_cast<uint2*>(ws + o_slots),
                  (max_len + seg_len - 1) / seg_len, seg_len, (max_len + kOutSeg - 1) / kOutSeg,
                  (rp.stride & 3) == 0 && (reinterpret_cast<uintptr_t>(rp.scores) & 15) == 0};
   const size_t nh = (size_t)rows * 2048;
