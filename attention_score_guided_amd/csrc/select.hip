@@ -263,32 +263,44 @@ __global__ __launch_bounds__(kRowThreads) void select_rows_kernel(RowsParams p) 
   select_row(p, blockIdx.x, sh);
 }
 
-// ---- ROWS mode, split over workgroups (long rows, few rows) ---------------
-// One workgroup per row leaves most of the chip idle when a handful of rows
-// are each 100K+ long.  The same selection is then cut into segments of
-// kSegLen positions: each radix pass is a histogram kernel (one workgroup per
-// (segment, row), LDS histograms folded into the row's global histogram
-// with integer atomics, so the counts are exact and order-free) followed by
-// a digit kernel (one workgroup per row); the ordered output is a count
-// kernel (kept and tied positions per segment) followed by an output kernel
-// that places each segment's positions after those of the segments before
-// it.  Results are identical to the one-workgroup kernel.
+// ---- ROWS mode, split over workgroups (long rows, small budgets) ---------
+// One workgroup per row leaves most of the chip idle when a few hundred rows
+// are each tens of thousands of positions long.  Rows are then cut into
+// segments:
+//   1. histogram kernel: the first digit (top 11 bits of the key) of every
+//      middle position, one workgroup per (segment, row), LDS histograms
+//      folded into the row's global histogram with integer atomics;
+//   2. digit kernel (one workgroup per row): the boundary digit d0 and the
+//      rank still needed among the keys whose first digit is d0;
+//   3. compaction kernel: per 4096-position segment, the middle positions
+//      whose first digit is above d0 (kept) or equal to it (candidates) are
+//      stored in position order with their keys, in bounded slots;
+//   4. final kernel (one workgroup per row): the last two digits among the
+//      candidates in LDS give tau and the ties still needed; the stored
+//      positions are written out in order between the forced ranges.
+// With budgets of at most 1/8 of a row the stored positions are a small
+// fraction of it; a row with more stored positions than the final kernel
+// holds in LDS (a boundary digit shared by many positions) is selected by
+// the one-workgroup algorithm inside the final kernel.  Results are
+// identical either way.
 constexpr int kSegQuantum = 4096;      // segment lengths are multiples of this
 constexpr int kSegTarget = 1024;       // aim for about this many workgroups per kernel
 constexpr int kSegThreads = 256;
 constexpr int kOutSeg = 4096;          // compaction segment: 4 float4 per thread
-constexpr int kCapSeg = 1024;          // entries stored per compaction segment
+constexpr int kCapSeg = kOutSeg;       // entries stored per compaction segment: all of it, so
+                                       // keeps clustered in a few segments never overflow
 constexpr int kFinEnt = 12288;         // stored entries the final kernel holds in LDS
 constexpr int kFinSegs = kRowThreads;  // compaction segments per row the final kernel handles
 #ifndef KVSEL_SPLIT_MIN_LEN
-#define KVSEL_SPLIT_MIN_LEN 65536
+#define KVSEL_SPLIT_MIN_LEN 16384
 #endif
 #ifndef KVSEL_SPLIT_MAX_ROWS
-#define KVSEL_SPLIT_MAX_ROWS 512
+#define KVSEL_SPLIT_MAX_ROWS 2048
 #endif
-constexpr int kSplitMinLen = KVSEL_SPLIT_MIN_LEN;    // split rows at least this long (below, the
-                                                     // one-workgroup kernel beats the split's launches)
-constexpr int kSplitMaxRows = KVSEL_SPLIT_MAX_ROWS;  // ... when there are fewer rows than this
+constexpr int kSplitMinLen = KVSEL_SPLIT_MIN_LEN;    // split rows at least this long ...
+constexpr int kSplitMaxRows = KVSEL_SPLIT_MAX_ROWS;  // ... when there are at most this many rows ...
+constexpr int kSplitMaxFrac = 8;                     // ... and budgets keep at most 1/8 of a row
+                                                     // (more would overflow the final kernel's LDS)
 
 struct RowPlan {
   int n, lo, hi, k, fsize;
@@ -602,7 +614,11 @@ __global__ __launch_bounds__(kRowThreads) void select_split_final(SplitParams sp
   if (tid == 0) p.out_count[r] = out_base + (q.n - q.hi);
 }
 
-inline bool use_split(int rows, int max_len) { return rows < kSplitMaxRows && max_len >= kSplitMinLen; }
+// Shapes that may split (the workspace is sized for them) and those that do.
+inline bool may_split(int rows, int max_len) { return rows <= kSplitMaxRows && max_len >= kSplitMinLen; }
+inline bool use_split(int rows, int max_len, int max_budget) {
+  return may_split(rows, max_len) && (long long)max_budget * kSplitMaxFrac <= max_len;
+}
 
 // Segment length: a multiple of kSegQuantum giving about kSegTarget
 // workgroups over all rows.
@@ -778,7 +794,7 @@ __global__ __launch_bounds__(kSelThreads) void global_output_kernel(const uint64
 }  // namespace
 
 size_t select_workspace_bytes(int rows, int max_len, int mode) {
-  if (mode != 1) return use_split(rows, max_len) ? split_layout(rows, max_len, nullptr, nullptr, nullptr) : 0;
+  if (mode != 1) return may_split(rows, max_len) ? split_layout(rows, max_len, nullptr, nullptr, nullptr) : 0;
   return ((size_t)rows * max_len * sizeof(uint64_t) + 255 & ~size_t(255)) + 256;
 }
 
@@ -790,7 +806,7 @@ hipError_t launch_select(const float* scores, int64_t stride, const int32_t* len
   if (mode == 0) {
     RowsParams rp{scores, stride, lengths, budgets, max_budget, sinks, window, out_idx, out_stride,
                   out_count};
-    if (use_split(rows, max_len)) return launch_split(rp, rows, max_len, workspace, stream);
+    if (use_split(rows, max_len, max_budget)) return launch_split(rp, rows, max_len, workspace, stream);
     hipLaunchKernelGGL(select_rows_kernel, dim3(rows), dim3(kRowThreads), 0, stream, rp);
     return hipGetLastError();
   }

@@ -242,13 +242,15 @@ def long_context_workload(torch, K, synth, args) -> dict:
     vlens = torch.full((Bq * HKVq,), Lq - W, dtype=torch.int32, device="cuda")
     vkeep = torch.empty((Bq * HKVq, 4096), dtype=torch.int32, device="cuda")
     vcnt = torch.empty((Bq * HKVq,), dtype=torch.int32, device="cuda")
+    ws_vs = torch.empty(max(256, K.select_workspace_bytes(Bq * HKVq, Lq - W, K.SELECT_ROWS)), dtype=torch.uint8,
+                        device="cuda")
 
     def vote():
         K.snapkv_vote(kv_k, cfg["q_win"], HQq, W, 7, cfg["scale"], K.REDUCE_SUM, votes, workspace=ws_v)
 
     def vote_select():
         vote()
-        K.select_keep(vrows, vlens, Lq - W, 0, 0, None, 4096, vkeep, vcnt)
+        K.select_keep(vrows, vlens, Lq - W, 0, 0, None, 4096, vkeep, vcnt, workspace=ws_vs)
 
     t_vote = timed(torch, vote, 5)
     t_vote_sel = timed(torch, vote_select, 5)
@@ -267,13 +269,15 @@ def long_context_workload(torch, K, synth, args) -> dict:
     out = torch.empty((Bq, HQq, 128), device="cuda")
     ws_d = torch.empty(K.decode_workspace_bytes(kv_i, HQq, True), dtype=torch.uint8, device="cuda")
     ws_s = torch.empty(K.sparse_workspace_bytes(Bq, HQq, 128, 2048), dtype=torch.uint8, device="cuda")
+    ws_k = torch.empty(max(256, K.select_workspace_bytes(Bq * HQq, cap, K.SELECT_ROWS)), dtype=torch.uint8,
+                       device="cuda")
 
     def sparse_step(s):
         lens.fill_(Lq + s + 1)
         slens.fill_(Lq + s + 1)
         K.decode_attn_scores(kv_i, cfg["qi_dec"][s], HQq, 1.0, None, None, scores, K.EMIT_LOGITS,
                              workspace=ws_d)
-        K.select_keep(srows, slens, cap, 0, 0, None, 2048, keep, kcnt)
+        K.select_keep(srows, slens, cap, 0, 0, None, 2048, keep, kcnt, workspace=ws_k)
         K.sparse_attn(kv_f, cfg["q_dec"][s], HQq, keep.view(Bq, HQq, 2048), kcnt.view(Bq, HQq), 2048,
                       cfg["scale"], out, workspace=ws_s)
 
@@ -348,7 +352,9 @@ def llama3_workload(torch, K, synth, args) -> dict:
         K.decode_attn_scores(kv, cfg["q_steps"][0], HQq, cfg["scale"], out, None, None, K.EMIT_PROBS,
                              cum_w, 1.0, workspace=ws)
     K.block_aggregate(cum_w, final, cap, 16, K.REDUCE_NONE, False, bmax, bmean)
-    K.select_keep(cum_w.view(Bq * HKVq, stride), rlens, cap, 4, 512, budgets, mb, keep, kcnt)
+    ws_sel = torch.empty(max(256, K.select_workspace_bytes(Bq * HKVq, cap, K.SELECT_ROWS)), dtype=torch.uint8,
+                         device="cuda")
+    K.select_keep(cum_w.view(Bq * HKVq, stride), rlens, cap, 4, 512, budgets, mb, keep, kcnt, workspace=ws_sel)
     del cum_w
     torch.cuda.synchronize()
     a, b, c = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -359,7 +365,7 @@ def llama3_workload(torch, K, synth, args) -> dict:
                              cum, 1.0, workspace=ws)
     b.record()
     K.block_aggregate(cum, final, cap, 16, K.REDUCE_NONE, False, bmax, bmean)
-    K.select_keep(rows, rlens, cap, 4, 512, budgets, mb, keep, kcnt)
+    K.select_keep(rows, rlens, cap, 4, 512, budgets, mb, keep, kcnt, workspace=ws_sel)
     c.record()
     torch.cuda.synchronize()
     t_dec = a.elapsed_time(b) / steps

@@ -210,8 +210,9 @@ int kvsel_block_aggregate(const float* scores, int64_t score_stride, const int32
  *   GLOBAL_PERCENTILE mode.
  *   workspace: >= kvsel_select_workspace_bytes(rows, max_len, mode) bytes
  *   (device memory, any contents; may be 0 bytes).  ROWS mode needs one only
- *   when it splits long rows over several workgroups (fewer than 512 rows of
- *   max_len >= 65536); the result is the same either way.
+ *   for shapes whose long rows it may split over several workgroups (at most
+ *   2048 rows of max_len >= 16384; it splits when also max_budget <=
+ *   max_len / 8); the result is the same either way.
  * Errors: INVALID (NULL pointers, rows/max_len <= 0, stride < max_len,
  * negative sinks/window/max_budget/global_budget, out_stride too small,
  * GLOBAL with sinks or window), UNSUPPORTED, WORKSPACE, HIP.
