@@ -197,9 +197,7 @@ def counters_mode(torch, K, synth) -> int:
     layers, bufs = setup(torch, K, synth)
     scale = 1.0 / math.sqrt(D)
     for _ in range(3):
-        kv, q = layers[0]
-        K.decode_attn_scores(kv, q, HQ, scale, bufs["out"], bufs["lse"], bufs["probs"], K.EMIT_PROBS,
-                             bufs["cum"][0], 1.0, workspace=bufs["ws_dec"])
+        step_decode(K, layers, bufs, scale)
     torch.cuda.synchronize()
     src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -500,9 +498,10 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if tr is None else int(tr),
-                     "kernel": "kvsel_decode_attn_scores of one layer (decode_partial_mfma, which "
-                               "also normalises the probabilities and folds cum, + decode_combine); "
-                               "HIP events around the 80 decode calls of each step, divided by 80",
+                     "kernel": "kvsel_decode_attn_scores_agg of one layer (decode_partial_mfma, which "
+                               "also normalises the probabilities, folds cum and writes its block "
+                               "max/mean, + decode_combine); HIP events around the 80 decode calls "
+                               "of each step, divided by 80",
                      "algorithmic_bytes": alg, "avg_call_us": round(dec_avg_ms * 1e3, 2)},
         "extra": {"decode_share_of_step": round(dec_avg_ms * LAYERS / ms_step, 4),
                   "aggregate_select_us_per_step": round(sel_avg_ms * 1e3, 2),
