@@ -282,25 +282,35 @@ void snapkv_pass1(VoteParams p) {
       for (int u = 0; u < NU; ++u)
 #pragma unroll
         for (int k = 0; k < TN; ++k) a[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k][u], q[rt][u], a[k], 0, 0, 0);
-      float smax = kNegInf;
+      // exp2 against the current reference (one FMA and one exp per
+      // logit); a logit far enough above it to push the tile's sum past
+      // 2^64 (or the first tile, reference -inf) redoes the tile against
+      // the tile's max (rare)
+      auto tile_sum = [&](float m) {
+        float e[TN];
 #pragma unroll
-      for (int k = 0; k < TN; ++k)
+        for (int k = 0; k < TN; ++k) {
+          e[k] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { a[k][i] *= p.c2; smax = fmaxf(smax, a[k][i]); }
-      if (smax > m_[rt] + kRescale) {
-        l_[rt] *= exp2_hw(m_[rt] - smax);
-        m_[rt] = smax;
+          for (int i = 0; i < 4; ++i) e[k] += exp2_hw(fmaf(a[k][i], p.c2, -m));
+        }
+        float tot = 0.f;
+#pragma unroll
+        for (int k = 0; k < TN; ++k) tot += e[k];
+        return tot;
+      };
+      float tot = tile_sum(m_[rt]);
+      if (!(tot <= 0x1p64f)) {
+        float smax = kNegInf;
+#pragma unroll
+        for (int k = 0; k < TN; ++k)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) smax = fmaxf(smax, a[k][i]);
+        const float mn = fmaxf(m_[rt], smax * p.c2);
+        l_[rt] = m_[rt] == kNegInf ? 0.f : l_[rt] * exp2_hw(m_[rt] - mn);
+        m_[rt] = mn;
+        tot = tile_sum(mn);
       }
-      float e[TN];
-#pragma unroll
-      for (int k = 0; k < TN; ++k) {
-        e[k] = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) e[k] += exp2_hw(a[k][i] - m_[rt]);
-      }
-      float tot = 0.f;
-#pragma unroll
-      for (int k = 0; k < TN; ++k) tot += e[k];
       l_[rt] += tot;
     }
   };
