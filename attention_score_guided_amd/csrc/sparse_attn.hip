@@ -22,6 +22,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kSlice = 256;   // listed positions per workgroup
+constexpr int kUnroll = 8;    // gathered rows in flight per lane
 
 struct SparseParams {
   const uint8_t* k_pages;
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void sparse_partial(SparseParams p) {
   __shared__ float s_lds[GT][kSlice];
   __shared__ float red[kWaves][GT][D];
   __shared__ float2 ml_lds[GT];
-  __shared__ int pos_lds[kSlice];
+  __shared__ long long off_lds[kSlice];     // byte offset of the listed row in a head's pages, or -1
 
   const int chunk = blockIdx.x;
   const int set = blockIdx.y;                 // 0 .. idx_heads-1
@@ -69,9 +70,18 @@ __global__ __launch_bounds__(kThreads) void sparse_partial(SparseParams p) {
   const int P = 1 << p.page_log2;
   const int* list = p.indices + ((size_t)b * p.idx_heads + set) * p.idx_stride + start;
   const int L = p.seq_lens[b];
+  const size_t head_stride = (size_t)P * D * EB;
+  const size_t page_stride = head_stride * p.num_kv_heads;
+  // Row offsets of the listed positions, resolved through the block table
+  // once, so the gathers below need no dependent load.
   for (int i = tid; i < kSlice; i += kThreads) {
     const int j = i < n ? list[i] : -1;
-    pos_lds[i] = (j >= 0 && j < L) ? j : -1;
+    long long off = -1;
+    if (j >= 0 && j < L) {
+      const int pg = p.block_table[(size_t)b * p.max_pages + (j >> p.page_log2)];
+      off = (long long)((size_t)pg * page_stride + kvh * head_stride + (size_t)(j & (P - 1)) * D * EB);
+    }
+    off_lds[i] = off;
   }
   uint32_t qw[GT][4];
 #pragma unroll
@@ -81,39 +91,47 @@ __global__ __launch_bounds__(kThreads) void sparse_partial(SparseParams p) {
   }
   __syncthreads();
 
-  const size_t head_stride = (size_t)P * D * EB;
-  const size_t page_stride = head_stride * p.num_kv_heads;
-  auto row_ptr = [&](const uint8_t* base, int j) -> const uint8_t* {
-    const int pg = p.block_table[(size_t)b * p.max_pages + (j >> p.page_log2)];
-    return base + (size_t)pg * page_stride + kvh * head_stride + (size_t)(j & (P - 1)) * D * EB + seg * 16;
+  // Lane segment of listed row i (null when the entry is ignored).
+  auto row_seg = [&](const uint8_t* base, int i) -> const uint8_t* {
+    const long long off = i < n ? off_lds[i] : -1;
+    return off >= 0 ? base + off + seg * 16 : nullptr;
   };
 
   // ---- logits of the listed positions -------------------------------------
-  for (int i0 = 0; i0 < n; i0 += KPI) {
-    const int i = i0 + wave * KPW + slot;
-    const int j = i < n ? pos_lds[i] : -1;
-    const uint4 kr = j >= 0 ? ld16(row_ptr(p.k_pages, j)) : make_uint4(0, 0, 0, 0);
-    float part[GT];
+  // kUnroll rows per lane are loaded before any is used.
+  for (int i0 = 0; i0 < n; i0 += KPI * kUnroll) {
+    uint4 kr[kUnroll];
 #pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      if constexpr (BF16) {
-        float a = dot2_bf16(qw[h][0], kr.x, 0.f);
-        a = dot2_bf16(qw[h][1], kr.y, a);
-        a = dot2_bf16(qw[h][2], kr.z, a);
-        part[h] = dot2_bf16(qw[h][3], kr.w, a);
-      } else {
-        float a = __uint_as_float(qw[h][0]) * __uint_as_float(kr.x);
-        a = fmaf(__uint_as_float(qw[h][1]), __uint_as_float(kr.y), a);
-        a = fmaf(__uint_as_float(qw[h][2]), __uint_as_float(kr.z), a);
-        part[h] = fmaf(__uint_as_float(qw[h][3]), __uint_as_float(kr.w), a);
-      }
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint8_t* rp = row_seg(p.k_pages, i0 + u * KPI + wave * KPW + slot);
+      kr[u] = rp ? ld16(rp) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int h = 0; h < GT; ++h) part[h] = group_sum<LPK>(part[h]);
-    if (i < n) {
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = i0 + u * KPI + wave * KPW + slot;
+      float part[GT];
 #pragma unroll
-      for (int h = 0; h < GT; ++h)
-        if (seg == h) s_lds[h][i] = j >= 0 ? part[h] * p.scale : kNegInf;
+      for (int h = 0; h < GT; ++h) {
+        if constexpr (BF16) {
+          float a = dot2_bf16(qw[h][0], kr[u].x, 0.f);
+          a = dot2_bf16(qw[h][1], kr[u].y, a);
+          a = dot2_bf16(qw[h][2], kr[u].z, a);
+          part[h] = dot2_bf16(qw[h][3], kr[u].w, a);
+        } else {
+          float a = __uint_as_float(qw[h][0]) * __uint_as_float(kr[u].x);
+          a = fmaf(__uint_as_float(qw[h][1]), __uint_as_float(kr[u].y), a);
+          a = fmaf(__uint_as_float(qw[h][2]), __uint_as_float(kr[u].z), a);
+          part[h] = fmaf(__uint_as_float(qw[h][3]), __uint_as_float(kr[u].w), a);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < GT; ++h) part[h] = group_sum<LPK>(part[h]);
+      if (i < n) {
+        const bool valid = off_lds[i] >= 0;
+#pragma unroll
+        for (int h = 0; h < GT; ++h)
+          if (seg == h) s_lds[h][i] = valid ? part[h] * p.scale : kNegInf;
+      }
     }
   }
   __syncthreads();
@@ -144,11 +162,18 @@ __global__ __launch_bounds__(kThreads) void sparse_partial(SparseParams p) {
   for (int h = 0; h < GT; ++h)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-  for (int i0 = 0; i0 < n; i0 += KPI) {
-    const int i = i0 + wave * KPW + slot;
-    const int j = i < n ? pos_lds[i] : -1;
-    if (j >= 0) {
-      const uint4 vr = ld16(row_ptr(p.v_pages, j));
+  for (int i0 = 0; i0 < n; i0 += KPI * kUnroll) {
+    uint4 vb[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint8_t* rp = row_seg(p.v_pages, i0 + u * KPI + wave * KPW + slot);
+      vb[u] = rp ? ld16(rp) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = i0 + u * KPI + wave * KPW + slot;
+      if (i >= n || off_lds[i] < 0) continue;
+      const uint4 vr = vb[u];
       float v[EPL];
       if constexpr (BF16) {
         v[0] = bf16lo(vr.x); v[1] = bf16hi(vr.x); v[2] = bf16lo(vr.y); v[3] = bf16hi(vr.y);
