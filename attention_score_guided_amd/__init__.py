@@ -10,5 +10,5 @@ from ._lib import (  # noqa: F401
     SELECT_GLOBAL_PERCENTILE, SELECT_ROWS, KvselError, PagedKV, PagedKVDesc, accumulate,
     block_aggregate, decode_attn_scores, decode_attn_scores_agg, decode_workspace_bytes, library,
     select_keep, select_workspace_bytes, set_sync_spin_limit, snapkv_vote, snapkv_workspace_bytes,
-    sparse_attn, sparse_workspace_bytes,
+    sparse_attn, sparse_workspace_bytes, quest_summarize, quest_select, quest_workspace_bytes,
 )

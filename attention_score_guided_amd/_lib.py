@@ -31,7 +31,8 @@ EXPORTED = (
     "kvsel_accumulate",
     "kvsel_block_aggregate", "kvsel_select_keep", "kvsel_select_workspace_bytes",
     "kvsel_snapkv_vote", "kvsel_snapkv_workspace_bytes", "kvsel_sparse_attn",
-    "kvsel_sparse_workspace_bytes", "kvsel_set_sync_spin_limit",
+    "kvsel_sparse_workspace_bytes", "kvsel_quest_summarize", "kvsel_quest_select",
+    "kvsel_quest_workspace_bytes", "kvsel_set_sync_spin_limit",
     "kvsel_status_string", "kvsel_last_error",
 )
 
@@ -73,6 +74,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvsel_snapkv_workspace_bytes": (SZ, [D, I32, I32]),
         "kvsel_sparse_attn": (ctypes.c_int, [D, P, I32, P, I64, P, I32, I32, F, P, P, P, SZ, P]),
         "kvsel_sparse_workspace_bytes": (SZ, [I32, I32, I32, I32]),
+        "kvsel_quest_summarize": (ctypes.c_int, [D, I32, P, P]),
+        "kvsel_quest_select": (ctypes.c_int, [D, P, P, I32, I32, P, I64, P, I64, P, P, SZ, P]),
+        "kvsel_quest_workspace_bytes": (SZ, [D, I32, I32]),
         "kvsel_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "kvsel_set_sync_spin_limit": (I32, [I32]),
         "kvsel_last_error": (ctypes.c_char_p, []),
@@ -283,4 +287,31 @@ def sparse_attn(kv: PagedKV, q: torch.Tensor, num_q_heads: int, indices: torch.T
         kv.ref(), _ptr(q, None, "q"), num_q_heads, _ptr(indices, torch.int32, "indices"),
         indices.shape[-1], _ptr(counts, torch.int32, "counts"), int(indices.shape[1]), max_count,
         float(scale), _ptr(out, torch.float32, "out"), _ptr(probs, torch.float32, "probs"),
+        _ptr(ws, None, "workspace"), wsb, _stream(stream)))
+
+
+def quest_summarize(kv: PagedKV, summary: torch.Tensor, first_page: int = 0, stream=None) -> None:
+    """kvsel_quest_summarize: summary ``[num_pages][H_kv][2][head_dim]`` in the
+    cache dtype (per physical page: channel min, then max)."""
+    if summary.dtype != kv.dtype:
+        raise TypeError("summary must have the cache dtype")
+    _check(_LIB.kvsel_quest_summarize(kv.ref(), int(first_page), _ptr(summary, None, "summary"), _stream(stream)))
+
+
+def quest_workspace_bytes(kv: PagedKV, num_q_heads: int, budget_pages: int) -> int:
+    return int(_LIB.kvsel_quest_workspace_bytes(kv.ref(), num_q_heads, int(budget_pages)))
+
+
+def quest_select(kv: PagedKV, summary: torch.Tensor, q: torch.Tensor, num_q_heads: int, budget_pages: int,
+                 out_idx: torch.Tensor, out_count: torch.Tensor, bounds: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """kvsel_quest_select: out_idx ``[B][H_q][out_stride]``, out_count ``[B][H_q]``,
+    bounds ``[B][H_q][bounds_stride]`` or None."""
+    if q.dtype != kv.dtype or summary.dtype != kv.dtype:
+        raise TypeError("q and summary must have the cache dtype")
+    ws, wsb = _workspace(quest_workspace_bytes(kv, num_q_heads, budget_pages), q.device, workspace)
+    _check(_LIB.kvsel_quest_select(
+        kv.ref(), _ptr(summary, None, "summary"), _ptr(q, None, "q"), num_q_heads, int(budget_pages),
+        _ptr(bounds, torch.float32, "bounds"), 0 if bounds is None else bounds.shape[-1],
+        _ptr(out_idx, torch.int32, "out_idx"), out_idx.shape[-1], _ptr(out_count, torch.int32, "out_count"),
         _ptr(ws, None, "workspace"), wsb, _stream(stream)))

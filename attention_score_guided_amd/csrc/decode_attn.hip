@@ -758,10 +758,15 @@ void decode_partial_mfma(PartialParams p) {
     } else {
       if (tid < nw) w_first = post_check(w_first, w_first1);
     }
-    int miss0 = nw > kThreads;
+    int miss0 = 0;
     if (tid < nw) {
       if ((uint32_t)(w_first >> 32) != p.epoch) miss0 = 1;
       else lse_lds[tid] = __uint_as_float((uint32_t)w_first);
+    }
+    for (int i = tid + kThreads; i < nw; i += kThreads) {   // rows of more than kThreads posts
+      const unsigned long long w = post_word(i);
+      if ((uint32_t)(w >> 32) != p.epoch) miss0 = 1;
+      else lse_lds[i] = __uint_as_float((uint32_t)w);
     }
     bool ok = !__syncthreads_or(miss0);
     for (int it = 0; !ok && it < p.spin_limit; ++it) {

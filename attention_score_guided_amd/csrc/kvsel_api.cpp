@@ -412,4 +412,56 @@ int kvsel_snapkv_vote(const kvsel_paged_kv* kv, const void* q_win, int32_t num_q
   return hip_status(kvsel::launch_snapkv(a, static_cast<hipStream_t>(stream)), "snapkv_vote launch");
 }
 
+int kvsel_quest_summarize(const kvsel_paged_kv* kv, int32_t first_page, void* summary, void* stream) {
+  int st = check_kv(kv, kv ? kv->num_kv_heads : 1, false);
+  if (st != KVSEL_OK) return st;
+  if (!summary) return fail(KVSEL_ERR_INVALID, "summary is NULL");
+  if (first_page < 0) return fail(KVSEL_ERR_INVALID, "first_page %d < 0", first_page);
+  st = check_device();
+  if (st != KVSEL_OK) return st;
+  kvsel::QuestArgs a{kv->k_pages, kv->block_table, kv->seq_lens, kv->num_seqs, kv->num_kv_heads,
+                     kv->num_kv_heads, kv->head_dim, kv->page_size, kv->max_pages_per_seq,
+                     kv->max_seq_len, kv->dtype == KVSEL_BF16};
+  return hip_status(kvsel::launch_quest_summary(a, summary, first_page, static_cast<hipStream_t>(stream)),
+                    "quest_summarize launch");
+}
+
+size_t kvsel_quest_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads, int32_t budget_pages) {
+  if (check_kv(kv, num_q_heads, false) != KVSEL_OK || budget_pages < 0) return 0;
+  return kvsel::quest_workspace_bytes(kv->num_seqs, num_q_heads, kv->page_size, kv->max_seq_len, budget_pages);
+}
+
+int kvsel_quest_select(const kvsel_paged_kv* kv, const void* summary, const void* q, int32_t num_q_heads,
+                       int32_t budget_pages, float* bounds, int64_t bounds_stride, int32_t* out_idx,
+                       int64_t out_stride, int32_t* out_count, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  int st = check_kv(kv, num_q_heads, false);
+  if (st != KVSEL_OK) return st;
+  if (!summary || !q || !out_idx || !out_count) return fail(KVSEL_ERR_INVALID, "NULL pointer argument");
+  if (budget_pages < 0) return fail(KVSEL_ERR_INVALID, "budget_pages %d < 0", budget_pages);
+  const long long max_whole = kv->max_seq_len / kv->page_size;
+  if (bounds && bounds_stride < max_whole)
+    return fail(KVSEL_ERR_INVALID, "bounds_stride %lld < %lld whole pages", (long long)bounds_stride, max_whole);
+  const long long need = std::min<long long>((long long)budget_pages * kv->page_size + kv->page_size - 1,
+                                             kv->max_seq_len);
+  if (out_stride < need)
+    return fail(KVSEL_ERR_INVALID, "out_stride %lld < %lld", (long long)out_stride, need);
+  if (!group_supported(num_q_heads / kv->num_kv_heads))
+    return fail(KVSEL_ERR_UNSUPPORTED, "group size %d (power of two <= 8 or multiple of 8)",
+                num_q_heads / kv->num_kv_heads);
+  const size_t wneed = kvsel::quest_workspace_bytes(kv->num_seqs, num_q_heads, kv->page_size, kv->max_seq_len,
+                                                    budget_pages);
+  if (!workspace || workspace_bytes < wneed)
+    return fail(KVSEL_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, wneed);
+  st = check_device();
+  if (st != KVSEL_OK) return st;
+  kvsel::QuestArgs a{kv->k_pages, kv->block_table, kv->seq_lens, kv->num_seqs, kv->num_kv_heads,
+                     num_q_heads, kv->head_dim, kv->page_size, kv->max_pages_per_seq,
+                     kv->max_seq_len, kv->dtype == KVSEL_BF16};
+  return hip_status(kvsel::launch_quest_select(a, summary, q, budget_pages, bounds, bounds_stride, out_idx,
+                                               out_stride, out_count, workspace,
+                                               static_cast<hipStream_t>(stream)),
+                    "quest_select launch");
+}
+
 }  // extern "C"

@@ -105,4 +105,19 @@ struct SnapkvArgs {
 size_t snapkv_workspace_bytes(int num_seqs, int num_kv_heads, int num_q_heads, int window, int max_seq_len);
 hipError_t launch_snapkv(const SnapkvArgs& a, hipStream_t stream);
 
+// Quest page-bound selection: the paged cache, the queries' shape.
+struct QuestArgs {
+  const void* k_pages;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int num_seqs, num_kv_heads, num_q_heads, head_dim, page_size, max_pages, max_seq_len;
+  bool bf16;
+};
+
+hipError_t launch_quest_summary(const QuestArgs& a, void* summary, int first_page, hipStream_t stream);
+size_t quest_workspace_bytes(int num_seqs, int num_q_heads, int page_size, int max_seq_len, int budget_pages);
+hipError_t launch_quest_select(const QuestArgs& a, const void* summary, const void* q, int budget_pages,
+                               float* bounds, int64_t bounds_stride, int32_t* out_idx, int64_t out_stride,
+                               int32_t* out_count, void* workspace, hipStream_t stream);
+
 }  // namespace kvsel

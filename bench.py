@@ -255,28 +255,28 @@ def long_context_workload(torch, K, synth, args) -> dict:
     k_bytes = Bq * HKVq * Lq * 128 * 2
     vote_flops = 2 * (2.0 * Bq * HQq * W * Lq * 128)       # two passes of Q_win K^T
 
-    # sparse decode steps: lengths grow by one per step (the K/V were drawn ahead)
-    lens = kvt.seq_lens.clone()
-    kv_i = K.PagedKV(kit.k_pages, None, kit.block_table, lens, 16, cap)
-    kv_f = K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, lens, 16, cap)
+    # sparse decode steps: lengths grow by one per step (the K/V were drawn
+    # ahead); each step's length arrays are made before the timed region, so
+    # a step launches only the path's own kernels
+    step_lens = [torch.full((Bq,), Lq + s + 1, dtype=torch.int32, device="cuda") for s in range(steps)]
+    step_rlens = [torch.full((Bq * HQq,), Lq + s + 1, dtype=torch.int32, device="cuda") for s in range(steps)]
+    kv_i_s = [K.PagedKV(kit.k_pages, None, kit.block_table, ls, 16, cap) for ls in step_lens]
+    kv_f_s = [K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, ls, 16, cap) for ls in step_lens]
     scores = torch.empty((Bq, HQq, cap), device="cuda")
     srows = scores.view(Bq * HQq, cap)
-    slens = torch.empty((Bq * HQq,), dtype=torch.int32, device="cuda")
     keep = torch.empty((Bq * HQq, 2048), dtype=torch.int32, device="cuda")
     kcnt = torch.empty((Bq * HQq,), dtype=torch.int32, device="cuda")
     out = torch.empty((Bq, HQq, 128), device="cuda")
-    ws_d = torch.empty(K.decode_workspace_bytes(kv_i, HQq, True), dtype=torch.uint8, device="cuda")
+    ws_d = torch.empty(K.decode_workspace_bytes(kv_i_s[0], HQq, True), dtype=torch.uint8, device="cuda")
     ws_s = torch.empty(K.sparse_workspace_bytes(Bq, HQq, 128, 2048), dtype=torch.uint8, device="cuda")
     ws_k = torch.empty(max(256, K.select_workspace_bytes(Bq * HQq, cap, K.SELECT_ROWS)), dtype=torch.uint8,
                        device="cuda")
 
     def sparse_step(s):
-        lens.fill_(Lq + s + 1)
-        slens.fill_(Lq + s + 1)
-        K.decode_attn_scores(kv_i, cfg["qi_dec"][s], HQq, 1.0, None, None, scores, K.EMIT_LOGITS,
+        K.decode_attn_scores(kv_i_s[s], cfg["qi_dec"][s], HQq, 1.0, None, None, scores, K.EMIT_LOGITS,
                              workspace=ws_d)
-        K.select_keep(srows, slens, cap, 0, 0, None, 2048, keep, kcnt, workspace=ws_k)
-        K.sparse_attn(kv_f, cfg["q_dec"][s], HQq, keep.view(Bq, HQq, 2048), kcnt.view(Bq, HQq), 2048,
+        K.select_keep(srows, step_rlens[s], cap, 0, 0, None, 2048, keep, kcnt, workspace=ws_k)
+        K.sparse_attn(kv_f_s[s], cfg["q_dec"][s], HQq, keep.view(Bq, HQq, 2048), kcnt.view(Bq, HQq), 2048,
                       cfg["scale"], out, workspace=ws_s)
 
     sparse_step(0)
@@ -291,7 +291,7 @@ def long_context_workload(torch, K, synth, args) -> dict:
     sparse_bytes = (Bq * Lq * 64 * 2) + 2 * Bq * HQq * Lq * 4 + Bq * HQq * 2048 * 128 * 2 * 2
 
     # dense decode over the same cache (out only; the current token included)
-    lens.fill_(Lq)
+    kv_f = K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, kvt.seq_lens, 16, cap)
     ws_dd = torch.empty(K.decode_workspace_bytes(kv_f, HQq, True), dtype=torch.uint8, device="cuda")
     q0 = cfg["q_dec"][0]
     t_dense = timed(torch, lambda: K.decode_attn_scores(kv_f, q0, HQq, cfg["scale"], out, None, None,
@@ -329,8 +329,10 @@ def llama3_workload(torch, K, synth, args) -> dict:
     cap = int(base.max()) + steps
     # score rows span the cache capacity in whole pages (16-byte aligned rows)
     stride = -(-cap // 16) * 16
-    lens = base.clone()
-    kv = K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, lens, 16, cap)
+    # each step appends a token: its lengths are made before the timed region
+    kv_s = [K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, (base + s + 1).to(torch.int32), 16, cap)
+            for s in range(steps)]
+    kv = kv_s[0]
     cum = torch.zeros((Bq, HKVq, stride), device="cuda")
     out = torch.empty((Bq, HQq, 128), device="cuda")
     ws = torch.empty(K.decode_workspace_bytes(kv, HQq, False), dtype=torch.uint8, device="cuda")
@@ -358,8 +360,7 @@ def llama3_workload(torch, K, synth, args) -> dict:
     a, b, c = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     a.record()
     for s in range(steps):
-        lens.copy_(base + s + 1)
-        K.decode_attn_scores(kv, cfg["q_steps"][s], HQq, cfg["scale"], out, None, None, K.EMIT_PROBS,
+        K.decode_attn_scores(kv_s[s], cfg["q_steps"][s], HQq, cfg["scale"], out, None, None, K.EMIT_PROBS,
                              cum, 1.0, workspace=ws)
     b.record()
     K.block_aggregate(cum, final, cap, 16, K.REDUCE_NONE, False, bmax, bmean)

@@ -277,6 +277,54 @@ int kvsel_sparse_attn(const kvsel_paged_kv* kv, const void* q, int32_t num_q_hea
 size_t kvsel_sparse_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                     int32_t max_count);
 
+/* ------------------------------------------------------------------------
+ * Quest page summaries ([LONGCTX] sparse-attention experiment, the Quest
+ * strategy: the per-channel minimum and maximum of a page's keys).
+ * For every whole page p of every sequence with p >= first_page (pages with
+ * (p + 1) * page_size <= L_b; the trailing partial page is never summarised)
+ * and every KV head c:
+ *   summary[pg][c][0][i] = min over the page's keys k of k[i]
+ *   summary[pg][c][1][i] = max over the page's keys k of k[i]
+ * where pg = block_table[b][p] is the page's PHYSICAL id, so a summary lives
+ * beside its page and stays valid while the page is unchanged: call with
+ * first_page = 0 after a prefill and with first_page = the page that just
+ * filled after a decode step.  Layout [num_pages][num_kv_heads][2][head_dim]
+ * in the cache dtype (min and max of stored values are stored values, so
+ * the summary is exact).  Entries of other pages are left untouched.
+ * Errors: INVALID (NULL pointers, first_page < 0, bad descriptor),
+ * UNSUPPORTED (as the descriptor checks), HIP.
+ * ------------------------------------------------------------------------ */
+int kvsel_quest_summarize(const kvsel_paged_kv* kv, int32_t first_page, void* summary, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Quest selection for one decode query per query head ([LONGCTX]
+ * sparse-attention experiment, the Quest strategy).  For sequence b, query
+ * head h (KV head c = h / G) and every whole page p < n_b = floor(L_b / P):
+ *   bound[b][h][p] = sum_i max(q[b][h][i] * kmin[i], q[b][h][i] * kmax[i])
+ * (kmin/kmax: the summary of page block_table[b][p], KV head c; no softmax
+ * scale: the order is scale-free).  The min(budget_pages, n_b) pages with the
+ * largest bounds are chosen, ties to the lower page, and expanded to their
+ * token positions; every token of the partial page [n_b * P, L_b) follows.
+ *   summary  as written by kvsel_quest_summarize for every whole page.
+ *   q        [num_seqs][num_q_heads][head_dim] (dtype kv->dtype).
+ *   bounds   [num_seqs][num_q_heads][bounds_stride] f32 or NULL: receives the
+ *            bounds of the whole pages (bounds_stride >= floor(max_seq_len / P)).
+ *   out_idx  [num_seqs][num_q_heads][out_stride] i32: ascending positions;
+ *            out_stride >= min(budget_pages * P + P - 1, max_seq_len).
+ *   out_count[num_seqs][num_q_heads] i32: positions written per row.
+ * The index set feeds kvsel_sparse_attn with idx_heads = num_q_heads.
+ *   workspace: >= kvsel_quest_workspace_bytes(kv, num_q_heads, budget_pages).
+ * Errors: INVALID (NULL pointers, budget_pages < 0, strides too small),
+ * UNSUPPORTED (group size not a power of two <= 8 nor a multiple of 8, and
+ * the descriptor checks), WORKSPACE, HIP.
+ * ------------------------------------------------------------------------ */
+int kvsel_quest_select(const kvsel_paged_kv* kv, const void* summary, const void* q,
+                       int32_t num_q_heads, int32_t budget_pages, float* bounds,
+                       int64_t bounds_stride, int32_t* out_idx, int64_t out_stride,
+                       int32_t* out_count, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t kvsel_quest_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads, int32_t budget_pages);
+
 /* The bf16 decode pass normalises probabilities in-kernel: each workgroup
  * posts its chunk's log-sum-exp per head, then reads the posts of the other
  * chunks of its (sequence, KV head) row, polling again up to `iterations`

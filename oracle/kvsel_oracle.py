@@ -51,6 +51,8 @@ __all__ = [
     "attention_flops_per_token",
     "attention_linear_crossover",
     "kv_bytes_per_token",
+    "quest_page_summary",
+    "quest_page_bounds",
     "quest_page_selection",
     "window_index_set",
     "sink_window_index_set",
@@ -398,6 +400,25 @@ def sink_window_index_set(qpos: int, budget: int, sinks: int = 4) -> np.ndarray:
     return np.array(sorted(recent | set(range(min(sinks, qpos + 1)))), dtype=np.int64)
 
 
+def quest_page_summary(K: np.ndarray, page: int = 16):
+    """Per-channel min and max of the keys of every whole page of K (``[L][d]``)
+    ([LONGCTX] sparse-attention experiment, Quest): returns (kmin, kmax), each
+    ``[L // page][d]``.  The trailing partial page has no summary."""
+    n_full = K.shape[0] // page
+    kmin = np.empty((n_full, K.shape[1]))
+    kmax = np.empty((n_full, K.shape[1]))
+    for pg in range(n_full):
+        blk = K[pg * page:(pg + 1) * page]
+        kmin[pg], kmax[pg] = blk.min(axis=0), blk.max(axis=0)
+    return kmin, kmax
+
+
+def quest_page_bounds(q: np.ndarray, kmin: np.ndarray, kmax: np.ndarray) -> np.ndarray:
+    """Upper bound of q.k over each page's keys from its channel min / max:
+    bound = sum_d max(q_d*kmin_d, q_d*kmax_d) ([LONGCTX], Quest)."""
+    return np.array([np.maximum(q * kmin[pg], q * kmax[pg]).sum() for pg in range(kmin.shape[0])])
+
+
 def quest_page_selection(q: np.ndarray, K: np.ndarray, qpos: int, budget: int, page: int = 16) -> np.ndarray:
     """Quest page-bound selection for one query of one head.
 
@@ -409,11 +430,7 @@ def quest_page_selection(q: np.ndarray, K: np.ndarray, qpos: int, budget: int, p
     """
     L = K.shape[0]
     n_full = L // page
-    bounds = np.empty(n_full)
-    for pg in range(n_full):
-        blk = K[pg * page:(pg + 1) * page]
-        kmin, kmax = blk.min(axis=0), blk.max(axis=0)
-        bounds[pg] = np.maximum(q * kmin, q * kmax).sum()
+    bounds = quest_page_bounds(q, *quest_page_summary(K, page))
     n_pick = min(budget // page, n_full)
     order = sorted(range(n_full), key=lambda pg: (-bounds[pg], pg))
     keys = set()

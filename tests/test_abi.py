@@ -186,3 +186,28 @@ def test_decode_agg_validation(kw, status):
                                           a["cum"], 1024, 1.0, a["block_size"], a["blk_max"], a["blk_mean"],
                                           a["head_stride"], a["seq_stride"], FAKE, a["wsb"], None)
     assert st == status
+
+
+def test_quest_validation():
+    lib = K.library()
+    kv = _kv()          # page 16, max_seq_len 1024: 64 whole pages
+    assert lib.kvsel_quest_summarize(None, 0, FAKE, None) == K.KVSEL_ERR_INVALID
+    assert lib.kvsel_quest_summarize(ctypes.byref(kv), 0, None, None) == K.KVSEL_ERR_INVALID
+    assert lib.kvsel_quest_summarize(ctypes.byref(kv), -1, FAKE, None) == K.KVSEL_ERR_INVALID
+    assert lib.kvsel_quest_summarize(ctypes.byref(_kv(head_dim=96)), 0, FAKE, None) == K.KVSEL_ERR_UNSUPPORTED
+
+    def call(kvd=kv, hq=32, summary=FAKE, budget=8, bounds=None, bstride=0, out=FAKE, ostride=8 * 16 + 15,
+             ws=FAKE, wsb=1 << 30):
+        return lib.kvsel_quest_select(ctypes.byref(kvd), summary, FAKE, hq, budget, bounds, bstride, out,
+                                      ostride, FAKE, ws, wsb, None)
+    assert call(summary=None) == K.KVSEL_ERR_INVALID
+    assert call(out=None) == K.KVSEL_ERR_INVALID
+    assert call(budget=-1) == K.KVSEL_ERR_INVALID
+    assert call(ostride=8 * 16 + 14) == K.KVSEL_ERR_INVALID     # 8 pages + a partial page
+    assert call(budget=100, ostride=1023) == K.KVSEL_ERR_INVALID  # capped at max_seq_len
+    assert call(bounds=FAKE, bstride=63) == K.KVSEL_ERR_INVALID
+    assert call(hq=24, kvd=_kv(num_kv_heads=4)) == K.KVSEL_ERR_UNSUPPORTED   # G = 6
+    assert call(ws=None) == K.KVSEL_ERR_WORKSPACE
+    need = lib.kvsel_quest_workspace_bytes(ctypes.byref(kv), 32, 8)
+    assert need >= 2 * 32 * 64 * 4              # the bounds rows of every (sequence, head)
+    assert call(wsb=need - 1) == K.KVSEL_ERR_WORKSPACE

@@ -376,6 +376,41 @@ def test_quest_picks_the_page_of_a_dominant_key_and_keeps_the_tail():
         assert (blk @ q <= bound + 1e-12).all()
 
 
+def test_quest_summary_is_the_page_min_and_max():
+    # hand example: two whole pages of 2 keys, one partial page
+    K = np.array([[1.0, -2.0], [3.0, 0.5], [-1.0, 4.0], [-1.0, 4.0], [9.0, 9.0]])
+    kmin, kmax = O.quest_page_summary(K, 2)
+    assert kmin.tolist() == [[1.0, -2.0], [-1.0, 4.0]]
+    assert kmax.tolist() == [[3.0, 0.5], [-1.0, 4.0]]
+
+
+def test_quest_bound_is_the_box_maximum_by_brute_force():
+    # sum_d max(q_d*lo_d, q_d*hi_d) is the maximum of q.x over the box
+    # [lo, hi]; a linear function peaks at a corner, so enumerate all 2^d.
+    d = 6
+    for trial in range(20):
+        q = rng.normal(size=d)
+        K = rng.normal(size=(32, d))
+        kmin, kmax = O.quest_page_summary(K, 16)
+        bounds = O.quest_page_bounds(q, kmin, kmax)
+        for pg in range(2):
+            corners = [np.where([(m >> i) & 1 for i in range(d)], kmax[pg], kmin[pg]) for m in range(1 << d)]
+            assert bounds[pg] == pytest.approx(max(c @ q for c in corners), rel=1e-12, abs=1e-12)
+            assert (K[pg * 16:(pg + 1) * 16] @ q <= bounds[pg] + 1e-12).all()
+
+
+def test_quest_bound_sign_cases_and_tightness():
+    K = rng.normal(size=(48, 5))
+    kmin, kmax = O.quest_page_summary(K, 16)
+    qp = np.abs(rng.normal(size=5))
+    np.testing.assert_allclose(O.quest_page_bounds(qp, kmin, kmax), kmax @ qp, rtol=1e-13)
+    np.testing.assert_allclose(O.quest_page_bounds(-qp, kmin, kmax), kmin @ -qp, rtol=1e-13)
+    # a page of identical keys: the bound is the exact score
+    Ke = np.repeat(rng.normal(size=(1, 5)), 16, axis=0)
+    q = rng.normal(size=5)
+    assert O.quest_page_bounds(q, *O.quest_page_summary(Ke, 16))[0] == pytest.approx(Ke[0] @ q, rel=1e-13)
+
+
 # ------------------------------------------------------------ chunk attention
 def test_chunk_causal_attention_rows():
     Hq, Hkv, S, n, d = 4, 2, 10, 5, 8
