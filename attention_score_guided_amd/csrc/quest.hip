@@ -77,10 +77,10 @@ __global__ __launch_bounds__(kQThreads) void quest_summary_kernel(SummaryParams 
   constexpr int LPR = D / EPL;       // lanes per key row
   constexpr int RPW = kWave / LPR;   // key rows per wave load
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int lp = blockIdx.x * kQWaves + wave;
+  const int lp = p.first_page + blockIdx.x * kQWaves + wave;   // the grid starts at first_page
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int P = 1 << p.page_log2;
-  if (lp < p.first_page || (long long)(lp + 1) * P > p.seq_lens[b]) return;   // whole pages only
+  if ((long long)(lp + 1) * P > p.seq_lens[b]) return;   // whole pages only
   const int pg = p.block_table[(size_t)b * p.max_pages + lp];
   const uint8_t* base = p.k_pages + ((size_t)pg * p.num_kv_heads + kvh) * (size_t)P * D * EB;
   const int seg = lane % LPR, r0 = lane / LPR;
@@ -242,7 +242,7 @@ hipError_t launch_quest_summary(const QuestArgs& a, void* summary, int first_pag
   sp.first_page = first_page;
   const int max_whole = a.max_seq_len / a.page_size;
   if (max_whole <= first_page) return hipSuccess;   // no whole page from first_page on
-  const dim3 grid((max_whole + kQWaves - 1) / kQWaves, a.num_kv_heads, a.num_seqs);
+  const dim3 grid((max_whole - first_page + kQWaves - 1) / kQWaves, a.num_kv_heads, a.num_seqs);
   if (a.bf16) {
     if (a.head_dim == 128) hipLaunchKernelGGL((quest_summary_kernel<true, 128>), grid, dim3(kQThreads), 0, stream, sp);
     else hipLaunchKernelGGL((quest_summary_kernel<true, 64>), grid, dim3(kQThreads), 0, stream, sp);

@@ -290,6 +290,39 @@ def long_context_workload(torch, K, synth, args) -> dict:
     t_sparse = a.elapsed_time(b) / steps
     sparse_bytes = (Bq * Lq * 64 * 2) + 2 * Bq * HQq * Lq * 4 + Bq * HQq * 2048 * 128 * 2 * 2
 
+    # Quest over the same cache: page summaries at prefill, then sparse decode
+    # steps whose index sets are the top-128 pages (2048 keys) by page bound;
+    # each step refreshes the summary of the last whole page (the page that
+    # fills as tokens are appended)
+    QP = 128
+    summary = torch.empty((kvt.k_pages.shape[0], HKVq, 2, 128), dtype=torch.bfloat16, device="cuda")
+    kv_q0 = K.PagedKV(kvt.k_pages, None, kvt.block_table, kvt.seq_lens, 16, cap)
+    t_qsum = timed(torch, lambda: K.quest_summarize(kv_q0, summary), 5)
+    qidx = torch.empty((Bq, HQq, QP * 16 + 15), dtype=torch.int32, device="cuda")
+    qcnt = torch.empty((Bq, HQq), dtype=torch.int32, device="cuda")
+    ws_q = torch.empty(K.quest_workspace_bytes(kv_f_s[0], HQq, QP), dtype=torch.uint8, device="cuda")
+    ws_qs = torch.empty(K.sparse_workspace_bytes(Bq, HQq, 128, QP * 16 + 15), dtype=torch.uint8, device="cuda")
+
+    def quest_step(s):
+        K.quest_summarize(kv_f_s[s], summary, first_page=(Lq + s + 1) // 16 - 1)
+        K.quest_select(kv_f_s[s], summary, cfg["q_dec"][s], HQq, QP, qidx, qcnt, workspace=ws_q)
+        K.sparse_attn(kv_f_s[s], cfg["q_dec"][s], HQq, qidx, qcnt, qidx.shape[-1], cfg["scale"], out,
+                      workspace=ws_qs)
+
+    quest_step(0)
+    torch.cuda.synchronize()
+    a.record()
+    for s in range(steps):
+        quest_step(s)
+    b.record()
+    torch.cuda.synchronize()
+    t_quest = a.elapsed_time(b) / steps
+    t_qsel = timed(torch, lambda: K.quest_select(kv_f_s[0], summary, cfg["q_dec"][0], HQq, QP, qidx, qcnt,
+                                                 workspace=ws_q), 10)
+    n_pg = Lq // 16
+    qsel_bytes = Bq * HKVq * n_pg * 2 * 128 * 2 + Bq * HQq * n_pg * 4     # summaries in, bounds out
+    quest_bytes = qsel_bytes + Bq * HQq * QP * 16 * 128 * 2 * 2           # + gathered K/V
+
     # dense decode over the same cache (out only; the current token included)
     kv_f = K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, kvt.seq_lens, 16, cap)
     ws_dd = torch.empty(K.decode_workspace_bytes(kv_f, HQq, True), dtype=torch.uint8, device="cuda")
@@ -312,6 +345,13 @@ def long_context_workload(torch, K, synth, args) -> dict:
         "sparse_step": {"us": round(t_sparse * 1e3, 1),
                         "gb_per_s": round(sparse_bytes / (t_sparse * 1e-3) / 1e9, 1),
                         "bytes": sparse_bytes},
+        "quest": {"summarize_prefill_us": round(t_qsum * 1e3, 1),
+                  "summarize_k_gb_per_s": round(k_bytes / (t_qsum * 1e-3) / 1e9, 1),
+                  "select_us": round(t_qsel * 1e3, 1),
+                  "select_gb_per_s": round(qsel_bytes / (t_qsel * 1e-3) / 1e9, 1),
+                  "step_us": round(t_quest * 1e3, 1),
+                  "step_gb_per_s": round(quest_bytes / (t_quest * 1e-3) / 1e9, 1),
+                  "pages_per_head": QP},
     }
 
 
