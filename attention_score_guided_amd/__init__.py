@@ -11,4 +11,5 @@ from ._lib import (  # noqa: F401
     block_aggregate, decode_attn_scores, decode_attn_scores_agg, decode_workspace_bytes, library,
     select_keep, select_workspace_bytes, set_sync_spin_limit, snapkv_vote, snapkv_workspace_bytes,
     sparse_attn, sparse_workspace_bytes, quest_summarize, quest_select, quest_workspace_bytes,
+    h2o_step, h2o_workspace_bytes,
 )

@@ -32,7 +32,7 @@ EXPORTED = (
     "kvsel_block_aggregate", "kvsel_select_keep", "kvsel_select_workspace_bytes",
     "kvsel_snapkv_vote", "kvsel_snapkv_workspace_bytes", "kvsel_sparse_attn",
     "kvsel_sparse_workspace_bytes", "kvsel_quest_summarize", "kvsel_quest_select",
-    "kvsel_quest_workspace_bytes", "kvsel_set_sync_spin_limit",
+    "kvsel_quest_workspace_bytes", "kvsel_h2o_step", "kvsel_h2o_workspace_bytes", "kvsel_set_sync_spin_limit",
     "kvsel_status_string", "kvsel_last_error",
 )
 
@@ -77,6 +77,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvsel_quest_summarize": (ctypes.c_int, [D, I32, P, P]),
         "kvsel_quest_select": (ctypes.c_int, [D, P, P, I32, I32, P, I64, P, I64, P, P, SZ, P]),
         "kvsel_quest_workspace_bytes": (SZ, [D, I32, I32]),
+        "kvsel_h2o_step": (ctypes.c_int, [D, P, I32, F, P, P, P, I64, I32, I32, I32, F, P, P, P, SZ, P]),
+        "kvsel_h2o_workspace_bytes": (SZ, [D, I32, I64, I32, I32, I32]),
         "kvsel_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "kvsel_set_sync_spin_limit": (I32, [I32]),
         "kvsel_last_error": (ctypes.c_char_p, []),
@@ -315,3 +317,28 @@ def quest_select(kv: PagedKV, summary: torch.Tensor, q: torch.Tensor, num_q_head
         _ptr(bounds, torch.float32, "bounds"), 0 if bounds is None else bounds.shape[-1],
         _ptr(out_idx, torch.int32, "out_idx"), out_idx.shape[-1], _ptr(out_count, torch.int32, "out_count"),
         _ptr(ws, None, "workspace"), wsb, _stream(stream)))
+
+
+def h2o_workspace_bytes(kv: PagedKV, num_q_heads: int, slot_stride: int, sinks: int, window: int,
+                        budget: int) -> int:
+    return int(_LIB.kvsel_h2o_workspace_bytes(kv.ref(), num_q_heads, int(slot_stride), int(sinks), int(window),
+                                              int(budget)))
+
+
+def h2o_step(kv: PagedKV, q: torch.Tensor, num_q_heads: int, scale: float, slots: torch.Tensor,
+             slot_cum: torch.Tensor, slot_count: torch.Tensor, sinks: int, window: int, budget: int,
+             out: torch.Tensor, probs: Optional[torch.Tensor] = None, decay: float = 1.0,
+             workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """kvsel_h2o_step: slots / slot_cum ``[B][H_kv][slot_stride]``, slot_count ``[B][H_kv]``
+    (updated in place), out ``[B][H_q][d]``, probs ``[B][H_q][slot_stride]`` or None."""
+    if q.dtype != kv.dtype:
+        raise TypeError("q must have the cache dtype")
+    stride = slots.shape[-1]
+    if slot_cum.shape[-1] != stride or (probs is not None and probs.shape[-1] != stride):
+        raise ValueError("slots, slot_cum and probs must share the slot stride")
+    ws, wsb = _workspace(h2o_workspace_bytes(kv, num_q_heads, stride, sinks, window, budget), q.device, workspace)
+    _check(_LIB.kvsel_h2o_step(
+        kv.ref(), _ptr(q, None, "q"), num_q_heads, float(scale), _ptr(slots, torch.int32, "slots"),
+        _ptr(slot_cum, torch.float32, "slot_cum"), _ptr(slot_count, torch.int32, "slot_count"), stride,
+        int(sinks), int(window), int(budget), float(decay), _ptr(out, torch.float32, "out"),
+        _ptr(probs, torch.float32, "probs"), _ptr(ws, None, "workspace"), wsb, _stream(stream)))

@@ -464,4 +464,61 @@ int kvsel_quest_select(const kvsel_paged_kv* kv, const void* summary, const void
                     "quest_select launch");
 }
 
+size_t kvsel_h2o_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads, int64_t slot_stride,
+                                 int32_t sinks, int32_t window, int32_t budget) {
+  if (check_kv(kv, num_q_heads, false) != KVSEL_OK || slot_stride <= 0 || slot_stride > (1 << 30) || sinks < 0 ||
+      window < 0 || budget < 0)
+    return 0;
+  return kvsel::h2o_workspace_bytes(kv->num_seqs, kv->num_kv_heads, num_q_heads, kv->head_dim, slot_stride, sinks,
+                                    window, budget);
+}
+
+int kvsel_h2o_step(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads, float scale, int32_t* slots,
+                   float* slot_cum, int32_t* slot_count, int64_t slot_stride, int32_t sinks, int32_t window,
+                   int32_t budget, float decay, float* out, float* probs, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int st = check_kv(kv, num_q_heads, true);
+  if (st != KVSEL_OK) return st;
+  if (!q || !slots || !slot_cum || !slot_count || !out) return fail(KVSEL_ERR_INVALID, "NULL pointer argument");
+  if (sinks < 0 || window < 0 || budget < 0) return fail(KVSEL_ERR_INVALID, "sinks, window and budget must be >= 0");
+  if (slot_stride > (1 << 30)) return fail(KVSEL_ERR_INVALID, "slot_stride %lld too large", (long long)slot_stride);
+  if (slot_stride < (long long)budget + 1 || slot_stride < (long long)sinks + window + 1)
+    return fail(KVSEL_ERR_INVALID, "slot_stride %lld < max(budget, sinks + window) + 1", (long long)slot_stride);
+  const int G = num_q_heads / kv->num_kv_heads;
+  if (!(G <= 8 && is_pow2(G)))
+    return fail(KVSEL_ERR_UNSUPPORTED, "group size %d (slot lists are shared by a group: power of two <= 8)", G);
+  const size_t need = kvsel::h2o_workspace_bytes(kv->num_seqs, kv->num_kv_heads, num_q_heads, kv->head_dim,
+                                                 slot_stride, sinks, window, budget);
+  if (!workspace || workspace_bytes < need)
+    return fail(KVSEL_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  st = check_device();
+  if (st != KVSEL_OK) return st;
+  kvsel::H2oArgs a{};
+  a.sp.k_pages = kv->k_pages;
+  a.sp.v_pages = kv->v_pages;
+  a.sp.block_table = kv->block_table;
+  a.sp.seq_lens = kv->seq_lens;
+  a.sp.q = q;
+  a.sp.num_seqs = kv->num_seqs;
+  a.sp.num_kv_heads = kv->num_kv_heads;
+  a.sp.num_q_heads = num_q_heads;
+  a.sp.head_dim = kv->head_dim;
+  a.sp.page_size = kv->page_size;
+  a.sp.max_pages = kv->max_pages_per_seq;
+  a.sp.bf16 = kv->dtype == KVSEL_BF16;
+  a.sp.scale = scale;
+  a.sp.out = out;
+  a.sp.probs = probs;
+  a.sp.workspace = workspace;
+  a.slots = slots;
+  a.slot_cum = slot_cum;
+  a.slot_count = slot_count;
+  a.slot_stride = slot_stride;
+  a.sinks = sinks;
+  a.window = window;
+  a.budget = budget;
+  a.decay = decay;
+  return hip_status(kvsel::launch_h2o_step(a, static_cast<hipStream_t>(stream)), "h2o_step launch");
+}
+
 }  // extern "C"

@@ -83,6 +83,10 @@ struct SparseArgs {
   float* out;
   float* probs;
   void* workspace;
+  // Listed logits left raw in `probs` (no normalisation pass), with each
+  // (sequence, query head)'s log-sum-exp also written to lse_out (or null).
+  bool raw_logits;
+  float* lse_out;
 };
 
 size_t sparse_workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int max_count);
@@ -119,5 +123,20 @@ size_t quest_workspace_bytes(int num_seqs, int num_q_heads, int page_size, int m
 hipError_t launch_quest_select(const QuestArgs& a, const void* summary, const void* q, int budget_pages,
                                float* bounds, int64_t bounds_stride, int32_t* out_idx, int64_t out_stride,
                                int32_t* out_count, void* workspace, hipStream_t stream);
+
+// H2O decode step with per-step eviction over per-KV-head slot lists.
+struct H2oArgs {
+  SparseArgs sp;             // the paged cache, q, out; indices/counts = the slot lists
+  int32_t* slots;            // [B][H_kv][slot_stride] ascending positions
+  float* slot_cum;           // [B][H_kv][slot_stride]
+  int32_t* slot_count;       // [B][H_kv]
+  int64_t slot_stride;
+  int sinks, window, budget;
+  float decay;
+};
+
+size_t h2o_workspace_bytes(int num_seqs, int num_kv_heads, int num_q_heads, int head_dim, int64_t slot_stride,
+                           int sinks, int window, int budget);
+hipError_t launch_h2o_step(const H2oArgs& a, hipStream_t stream);
 
 }  // namespace kvsel

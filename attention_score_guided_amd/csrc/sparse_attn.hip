@@ -332,14 +332,14 @@ hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream) {
     e = a.head_dim == 128 ? launch_sparse_d<false, 128>(sp, gt, grid, stream)
                           : launch_sparse_d<false, 64>(sp, gt, grid, stream);
   if (e != hipSuccess) return e;
-  SparseCombineParams cp{a.counts, part_o, part_ml, a.out, lse_ws, a.num_q_heads, a.num_kv_heads,
-                         a.idx_heads, n_chunks, a.head_dim};
+  SparseCombineParams cp{a.counts, part_o, part_ml, a.out, a.lse_out ? a.lse_out : lse_ws, a.num_q_heads,
+                         a.num_kv_heads, a.idx_heads, n_chunks, a.head_dim};
   hipLaunchKernelGGL(sparse_combine, dim3((unsigned)bh), dim3(128), 0, stream, cp);
   e = hipGetLastError();
-  if (e != hipSuccess || !a.probs) return e;
+  if (e != hipSuccess || !a.probs || a.raw_logits) return e;
   hipLaunchKernelGGL(sparse_normalize, dim3((a.max_count + 255) / 256, (unsigned)bh), dim3(256), 0,
                      stream, a.counts, a.indices, a.idx_stride, a.num_q_heads, a.num_kv_heads,
-                     a.idx_heads, lse_ws, a.probs);
+                     a.idx_heads, cp.lse_ws, a.probs);
   return hipGetLastError();
 }
 

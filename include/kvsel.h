@@ -325,6 +325,44 @@ int kvsel_quest_select(const kvsel_paged_kv* kv, const void* summary, const void
 
 size_t kvsel_quest_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads, int32_t budget_pages);
 
+/* ------------------------------------------------------------------------
+ * H2O decode step with per-step eviction ([EVICT] §4.2 H2O, with the
+ * eviction inside the decode loop: the cache never holds more than the
+ * budget plus the new token).  Per (sequence b, KV head c) the caller keeps
+ * a list of slots: ascending kept positions slots[b][c][0 .. n) with their
+ * cumulative scores slot_cum[b][c][..], n = slot_count[b][c].  The new
+ * token's K/V must already sit at position L_b - 1 (seq_lens raised).  The
+ * call
+ *   1. appends position L_b - 1 with score 0 (n += 1);
+ *   2. out[b][h] = softmax attention of query head h over the listed
+ *      positions of KV head h / G only; probs[b][h][i] = the probability of
+ *      slot i (when probs != NULL);
+ *   3. slot_cum[b][c][i] = decay * slot_cum + sum over the group of probs;
+ *   4. when n > budget: keeps slots [0, min(sinks, n)), [max(n - window, 0),
+ *      n) and the top max(0, budget - forced) of the others by score (ties
+ *      to the lower slot, i.e. the lower position), in slot order, and drops
+ *      the rest permanently; slot_count becomes the kept count.
+ *   slots     [num_seqs][num_kv_heads][slot_stride] i32, slot_cum f32 alike,
+ *   slot_count[num_seqs][num_kv_heads] i32; slot_stride >= budget + 1 and
+ *             >= sinks + window + 1 (room for the appended token).
+ *   out       [num_seqs][num_q_heads][head_dim] f32.
+ *   probs     [num_seqs][num_q_heads][slot_stride] f32 or NULL; entries past
+ *             the pre-eviction count are left untouched.
+ *   workspace >= kvsel_h2o_workspace_bytes(...).
+ * Preconditions: listed positions distinct, ascending and < L_b - 1, and
+ * slot_count < slot_stride before the call.
+ * Errors: INVALID (NULL pointers, negative sinks / window / budget, slot_stride
+ * too small), UNSUPPORTED (group size not a power of two <= 8, and the
+ * descriptor checks), WORKSPACE, HIP.
+ * ------------------------------------------------------------------------ */
+int kvsel_h2o_step(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads, float scale,
+                   int32_t* slots, float* slot_cum, int32_t* slot_count, int64_t slot_stride,
+                   int32_t sinks, int32_t window, int32_t budget, float decay, float* out,
+                   float* probs, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t kvsel_h2o_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads, int64_t slot_stride,
+                                 int32_t sinks, int32_t window, int32_t budget);
+
 /* The bf16 decode pass normalises probabilities in-kernel: each workgroup
  * posts its chunk's log-sum-exp per head, then reads the posts of the other
  * chunks of its (sequence, KV head) row, polling again up to `iterations`

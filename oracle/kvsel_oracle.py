@@ -46,6 +46,7 @@ __all__ = [
     "snapkv_keep",
     "indexer_scores",
     "sparse_attention",
+    "h2o_evict_step",
     "relative_error",
     "chunk_causal_attention",
     "attention_flops_per_token",
@@ -358,6 +359,36 @@ def sparse_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, index_sets, sc
             p_full[valid] = p
         probs.append(p_full)
     return out, probs
+
+
+def h2o_evict_step(q: np.ndarray, K: np.ndarray, V: np.ndarray, kept, cum, scale: float, sinks: int,
+                   window: int, budget: int, decay: float = 1.0):
+    """One decode step of H2O with the eviction inside the decode loop
+    ([EVICT] §4.2: attention over the cached keys, scores accumulated per key,
+    then sinks + heavy hitters + recent window kept and the rest evicted; here
+    the cache is the per-KV-head list of kept positions).
+
+    q ``[H_q][d]``; K, V ``[H_kv][L][d]`` logical, position L-1 being the new
+    token; ``kept[c]`` the ascending kept positions of KV head c (all < L-1),
+    ``cum[c]`` their scores.  The new position joins every list with score 0,
+    every query head attends over its KV head's list only, the group's
+    probabilities are folded into the list's scores, and the list is cut back
+    with ``select_keep`` applied to the list in slot order.
+    Returns (out ``[H_q][d]``, probs per query head aligned with its KV head's
+    list after the append, new kept lists, new scores).
+    """
+    Hq, Hkv, L = q.shape[0], K.shape[0], K.shape[1]
+    G = Hq // Hkv
+    lists = [np.append(np.asarray(kept[c], dtype=np.int64), L - 1) for c in range(Hkv)]
+    scores = [np.append(np.asarray(cum[c], dtype=np.float64), 0.0) for c in range(Hkv)]
+    out, probs = sparse_attention(q, K, V, [lists[h // G] for h in range(Hq)], scale)
+    new_kept, new_cum = [], []
+    for c in range(Hkv):
+        folded = accumulate(scores[c][None, :], np.stack(probs[c * G:(c + 1) * G]), decay)[0]
+        keep = select_keep(folded, len(folded), sinks, window, budget)
+        new_kept.append(lists[c][keep])
+        new_cum.append(folded[keep])
+    return out, probs, new_kept, new_cum
 
 
 def chunk_causal_attention(q_chunk: np.ndarray, K_cache: np.ndarray, V_cache: np.ndarray,

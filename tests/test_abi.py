@@ -15,7 +15,7 @@ def _declared_functions():
     import os
     src = open(os.path.join(os.path.dirname(__file__), "..", HEADER)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(kvsel_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(kvsel_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -210,4 +210,26 @@ def test_quest_validation():
     assert call(ws=None) == K.KVSEL_ERR_WORKSPACE
     need = lib.kvsel_quest_workspace_bytes(ctypes.byref(kv), 32, 8)
     assert need >= 2 * 32 * 64 * 4              # the bounds rows of every (sequence, head)
+    assert call(wsb=need - 1) == K.KVSEL_ERR_WORKSPACE
+
+
+def test_h2o_validation():
+    lib = K.library()
+
+    def call(kvd=None, hq=32, slots=FAKE, out=FAKE, stride=80, sinks=4, window=16, budget=64, ws=FAKE,
+             wsb=1 << 30):
+        kvd = kvd or _kv()
+        return lib.kvsel_h2o_step(ctypes.byref(kvd), FAKE, hq, 0.1, slots, FAKE, FAKE, stride, sinks, window,
+                                  budget, 1.0, out, None, ws, wsb, None)
+    assert call(slots=None) == K.KVSEL_ERR_INVALID
+    assert call(out=None) == K.KVSEL_ERR_INVALID
+    assert call(kvd=_kv(v_pages=None)) == K.KVSEL_ERR_INVALID
+    assert call(budget=-1) == K.KVSEL_ERR_INVALID
+    assert call(stride=64) == K.KVSEL_ERR_INVALID                  # no room for the appended token
+    assert call(sinks=40, window=40, stride=80) == K.KVSEL_ERR_INVALID
+    assert call(hq=96, kvd=_kv(num_kv_heads=8)) == K.KVSEL_ERR_UNSUPPORTED   # G = 12
+    assert call(hq=128) == K.KVSEL_ERR_UNSUPPORTED                 # G = 16: lists are shared by a group
+    assert call(ws=None) == K.KVSEL_ERR_WORKSPACE
+    need = lib.kvsel_h2o_workspace_bytes(ctypes.byref(_kv()), 32, 80, 4, 16, 64)
+    assert need >= 2 * 32 * 80 * 4                                 # the logits of every listed slot
     assert call(wsb=need - 1) == K.KVSEL_ERR_WORKSPACE

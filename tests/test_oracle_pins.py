@@ -411,6 +411,79 @@ def test_quest_bound_sign_cases_and_tightness():
     assert O.quest_page_bounds(q, *O.quest_page_summary(Ke, 16))[0] == pytest.approx(Ke[0] @ q, rel=1e-13)
 
 
+def test_h2o_evict_step_hand_example():
+    # one head, d = 1, q = 1, scale 1: logits are the key values themselves.
+    # Prompt keys 3, 0, 2 all kept; the new key 1 joins; budget 2, window 1:
+    # forced = the new slot, one heavy hitter among positions 0..2 -> position 0.
+    K = np.array([[[3.0], [0.0], [2.0], [1.0]]])
+    V = np.array([[[10.0], [20.0], [30.0], [40.0]]])
+    out, probs, kept, cum = O.h2o_evict_step(np.array([[1.0]]), K, V, [[0, 1, 2]], [np.zeros(3)], 1.0,
+                                             0, 1, 2)
+    e = np.exp([3.0, 0.0, 2.0, 1.0])
+    p = e / e.sum()
+    np.testing.assert_allclose(probs[0], p, rtol=1e-15)
+    assert out[0, 0] == pytest.approx(p @ [10, 20, 30, 40], rel=1e-14)
+    assert kept[0].tolist() == [0, 3]
+    np.testing.assert_allclose(cum[0], [p[0], p[3]], rtol=1e-15)
+
+
+def _h2o_run(T, L0, Hq, Hkv, d, sinks, window, budget, seed=5):
+    r = np.random.default_rng(seed)
+    K = r.normal(size=(Hkv, L0 + T, d))
+    V = r.normal(size=(Hkv, L0 + T, d))
+    qs = r.normal(size=(T, Hq, d))
+    kept = [np.arange(L0) for _ in range(Hkv)]
+    cum = [np.zeros(L0) for _ in range(Hkv)]
+    hist = []
+    for t in range(T):
+        L = L0 + t + 1
+        out, probs, kept, cum = O.h2o_evict_step(qs[t], K[:, :L], V[:, :L], kept, cum, 0.3, sinks, window,
+                                                 budget)
+        hist.append((out, probs, [k.copy() for k in kept], [c.copy() for c in cum]))
+    return K, V, qs, hist
+
+
+def test_h2o_evict_without_eviction_is_full_decode_and_accumulate():
+    # budget above every length: no eviction, so each step is full decode
+    # attention and the scores are the plain accumulated probabilities
+    T, L0, Hq, Hkv, d = 6, 9, 4, 2, 5
+    K, V, qs, hist = _h2o_run(T, L0, Hq, Hkv, d, 2, 3, 1000)
+    cum = np.zeros((Hkv, L0 + T))
+    for t, (out, probs, kept, c) in enumerate(hist):
+        L = L0 + t + 1
+        r = O.decode_attention(qs[t], K[:, :L], V[:, :L], 0.3)
+        np.testing.assert_allclose(out, r["out"], rtol=1e-12, atol=1e-14)
+        cum[:, :L] = O.accumulate(cum[:, :L], r["probs"])
+        for ci in range(Hkv):
+            assert kept[ci].tolist() == list(range(L))
+            np.testing.assert_allclose(c[ci], cum[ci, :L], rtol=1e-12)
+
+
+def test_h2o_evict_with_sinks_and_window_filling_the_budget_is_streaming():
+    # sinks + window = budget leaves no heavy hitter: StreamingLLM's list
+    T, L0, budget = 12, 20, 10
+    _, _, _, hist = _h2o_run(T, L0, 2, 1, 4, 4, budget - 4, budget)
+    for t, (_, probs, kept, cum) in enumerate(hist):
+        L = L0 + t + 1
+        assert kept[0].tolist() == O.streaming_keep(L, budget, 4).tolist()
+        assert all(abs(p.sum() - 1) < 1e-12 for p in probs)
+
+
+def test_h2o_evict_invariants_with_heavy_hitters():
+    T, L0, Hq, Hkv, budget = 10, 30, 4, 2, 12
+    _, _, _, hist = _h2o_run(T, L0, Hq, Hkv, 6, 2, 3, budget)
+    mass = 0.0
+    for t, (_, probs, kept, cum) in enumerate(hist):
+        L = L0 + t + 1
+        for ci in range(Hkv):
+            assert len(kept[ci]) == budget
+            assert kept[ci][:2].tolist() == [0, 1] and kept[ci][-3:].tolist() == [L - 3, L - 2, L - 1]
+            assert (np.diff(kept[ci]) > 0).all()
+        # scores only ever gain mass while kept, and lose a slot's when evicted
+        assert sum(c.sum() for c in cum) <= (t + 1) * Hq + 1e-9
+        assert all(abs(p.sum() - 1) < 1e-12 for p in probs)
+
+
 # ------------------------------------------------------------ chunk attention
 def test_chunk_causal_attention_rows():
     Hq, Hkv, S, n, d = 4, 2, 10, 5, 8
