@@ -77,7 +77,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvsel_quest_summarize": (ctypes.c_int, [D, I32, P, P]),
         "kvsel_quest_select": (ctypes.c_int, [D, P, P, I32, I32, P, I64, P, I64, P, P, SZ, P]),
         "kvsel_quest_workspace_bytes": (SZ, [D, I32, I32]),
-        "kvsel_h2o_step": (ctypes.c_int, [D, P, I32, F, P, P, P, I64, I32, I32, I32, F, P, P, P, SZ, P]),
+        "kvsel_h2o_step": (ctypes.c_int, [D, P, I32, F, P, P, P, I64, I32, I32, I32, P, F, P, P, P, SZ, P]),
         "kvsel_h2o_workspace_bytes": (SZ, [D, I32, I64, I32, I32, I32]),
         "kvsel_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "kvsel_set_sync_spin_limit": (I32, [I32]),
@@ -328,9 +328,11 @@ def h2o_workspace_bytes(kv: PagedKV, num_q_heads: int, slot_stride: int, sinks: 
 def h2o_step(kv: PagedKV, q: torch.Tensor, num_q_heads: int, scale: float, slots: torch.Tensor,
              slot_cum: torch.Tensor, slot_count: torch.Tensor, sinks: int, window: int, budget: int,
              out: torch.Tensor, probs: Optional[torch.Tensor] = None, decay: float = 1.0,
-             workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+             budgets: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+             stream=None) -> None:
     """kvsel_h2o_step: slots / slot_cum ``[B][H_kv][slot_stride]``, slot_count ``[B][H_kv]``
-    (updated in place), out ``[B][H_q][d]``, probs ``[B][H_q][slot_stride]`` or None."""
+    (updated in place), out ``[B][H_q][d]``, probs ``[B][H_q][slot_stride]`` or None,
+    budgets ``[B][H_kv]`` int32 (each <= budget) or None."""
     if q.dtype != kv.dtype:
         raise TypeError("q must have the cache dtype")
     stride = slots.shape[-1]
@@ -340,5 +342,6 @@ def h2o_step(kv: PagedKV, q: torch.Tensor, num_q_heads: int, scale: float, slots
     _check(_LIB.kvsel_h2o_step(
         kv.ref(), _ptr(q, None, "q"), num_q_heads, float(scale), _ptr(slots, torch.int32, "slots"),
         _ptr(slot_cum, torch.float32, "slot_cum"), _ptr(slot_count, torch.int32, "slot_count"), stride,
-        int(sinks), int(window), int(budget), float(decay), _ptr(out, torch.float32, "out"),
+        int(sinks), int(window), int(budget), _ptr(budgets, torch.int32, "budgets"), float(decay),
+        _ptr(out, torch.float32, "out"),
         _ptr(probs, torch.float32, "probs"), _ptr(ws, None, "workspace"), wsb, _stream(stream)))

@@ -329,6 +329,7 @@ int kvsel_sparse_attn(const kvsel_paged_kv* kv, const void* q, int32_t num_q_hea
     return fail(KVSEL_ERR_INVALID, "idx_heads %d must be num_q_heads or num_kv_heads", idx_heads);
   if (max_count < 0 || idx_stride < max_count)
     return fail(KVSEL_ERR_INVALID, "need 0 <= max_count <= idx_stride");
+  if (max_count > (1 << 24)) return fail(KVSEL_ERR_UNSUPPORTED, "max_count %d > 2^24", max_count);
   const int G = num_q_heads / kv->num_kv_heads;
   if (idx_heads != num_q_heads && !(G <= 8 && is_pow2(G)))
     return fail(KVSEL_ERR_UNSUPPORTED, "shared index sets need a group size that is a power of two <= 8");
@@ -466,7 +467,7 @@ int kvsel_quest_select(const kvsel_paged_kv* kv, const void* summary, const void
 
 size_t kvsel_h2o_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads, int64_t slot_stride,
                                  int32_t sinks, int32_t window, int32_t budget) {
-  if (check_kv(kv, num_q_heads, false) != KVSEL_OK || slot_stride <= 0 || slot_stride > (1 << 30) || sinks < 0 ||
+  if (check_kv(kv, num_q_heads, false) != KVSEL_OK || slot_stride <= 0 || slot_stride > (1 << 24) || sinks < 0 ||
       window < 0 || budget < 0)
     return 0;
   return kvsel::h2o_workspace_bytes(kv->num_seqs, kv->num_kv_heads, num_q_heads, kv->head_dim, slot_stride, sinks,
@@ -475,13 +476,13 @@ size_t kvsel_h2o_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads, 
 
 int kvsel_h2o_step(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads, float scale, int32_t* slots,
                    float* slot_cum, int32_t* slot_count, int64_t slot_stride, int32_t sinks, int32_t window,
-                   int32_t budget, float decay, float* out, float* probs, void* workspace,
+                   int32_t budget, const int32_t* budgets, float decay, float* out, float* probs, void* workspace,
                    size_t workspace_bytes, void* stream) {
   int st = check_kv(kv, num_q_heads, true);
   if (st != KVSEL_OK) return st;
   if (!q || !slots || !slot_cum || !slot_count || !out) return fail(KVSEL_ERR_INVALID, "NULL pointer argument");
   if (sinks < 0 || window < 0 || budget < 0) return fail(KVSEL_ERR_INVALID, "sinks, window and budget must be >= 0");
-  if (slot_stride > (1 << 30)) return fail(KVSEL_ERR_INVALID, "slot_stride %lld too large", (long long)slot_stride);
+  if (slot_stride > (1 << 24)) return fail(KVSEL_ERR_UNSUPPORTED, "slot_stride %lld > 2^24", (long long)slot_stride);
   if (slot_stride < (long long)budget + 1 || slot_stride < (long long)sinks + window + 1)
     return fail(KVSEL_ERR_INVALID, "slot_stride %lld < max(budget, sinks + window) + 1", (long long)slot_stride);
   const int G = num_q_heads / kv->num_kv_heads;
@@ -517,6 +518,7 @@ int kvsel_h2o_step(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads,
   a.sinks = sinks;
   a.window = window;
   a.budget = budget;
+  a.budgets = budgets;
   a.decay = decay;
   return hip_status(kvsel::launch_h2o_step(a, static_cast<hipStream_t>(stream)), "h2o_step launch");
 }

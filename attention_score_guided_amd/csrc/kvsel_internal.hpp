@@ -132,6 +132,7 @@ struct H2oArgs {
   int32_t* slot_count;       // [B][H_kv]
   int64_t slot_stride;
   int sinks, window, budget;
+  const int32_t* budgets;    // [B][H_kv] per-list budgets (<= budget), or null
   float decay;
 };
 

@@ -227,6 +227,8 @@ struct SparseCombineParams {
 };
 
 __global__ __launch_bounds__(128) void sparse_combine(SparseCombineParams p) {
+  extern __shared__ float w_lds[];            // [n_chunks] exp(m_c - M)
+  __shared__ float red[2][2];
   const int bh = blockIdx.x;
   const int b = bh / p.num_q_heads, h = bh % p.num_q_heads;
   const int G = p.num_q_heads / p.num_kv_heads;
@@ -234,21 +236,42 @@ __global__ __launch_bounds__(128) void sparse_combine(SparseCombineParams p) {
   const int count = p.counts[(size_t)b * p.idx_heads + set];
   const int nc = (count + kSlice - 1) / kSlice;
   const float2* ml = p.part_ml + (size_t)bh * p.n_chunks;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  // chunk maxima and sums are read once, in parallel, and reduced over the
+  // two waves; empty chunks (m = -inf) weigh nothing
   float M = kNegInf;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, ml[c].x);
-  float l = 0.f;
+  for (int c = tid; c < nc; c += 128) M = fmaxf(M, ml[c].x);
+  M = wave_max(M);
+  if (lane == 0) red[0][wave] = M;
+  __syncthreads();
+  M = fmaxf(red[0][0], red[0][1]);
   const float Ms = M == kNegInf ? 0.f : M * kLog2e;
-  for (int c = 0; c < nc; ++c)
-    if (ml[c].x != kNegInf) l += ml[c].y * exp2_hw(fmaf(ml[c].x, kLog2e, -Ms));
-  const int d = threadIdx.x;
-  if (d < p.D) {
-    float o = 0.f;
-    for (int c = 0; c < nc; ++c)
-      if (ml[c].x != kNegInf)
-        o = fmaf(exp2_hw(fmaf(ml[c].x, kLog2e, -Ms)), p.part_o[((size_t)bh * p.n_chunks + c) * p.D + d], o);
-    p.out[(size_t)bh * p.D + d] = l > 0.f ? o / l : 0.f;
+  float l = 0.f;
+  for (int c = tid; c < nc; c += 128) {
+    const float2 v = ml[c];
+    const float w = v.x == kNegInf ? 0.f : exp2_hw(fmaf(v.x, kLog2e, -Ms));
+    w_lds[c] = w;
+    l = fmaf(w, v.y, l);
   }
-  if (threadIdx.x == 0) p.lse_ws[bh] = l > 0.f ? M + log2_hw(l) * kLn2 : kNegInf;
+  l = wave_sum(l);
+  if (lane == 0) red[1][wave] = l;
+  __syncthreads();
+  l = red[1][0] + red[1][1];
+  const int d = tid;
+  if (d < p.D) {
+    // independent loads of the chunk rows, eight in flight
+    const float* po = p.part_o + (size_t)bh * p.n_chunks * p.D + d;
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int c = 0;
+    for (; c + 8 <= nc; c += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) o[u] = fmaf(w_lds[c + u], po[(size_t)(c + u) * p.D], o[u]);
+    }
+    for (; c < nc; ++c) o[0] = fmaf(w_lds[c], po[(size_t)c * p.D], o[0]);
+    const float os = ((o[0] + o[1]) + (o[2] + o[3])) + ((o[4] + o[5]) + (o[6] + o[7]));
+    p.out[(size_t)bh * p.D + d] = l > 0.f ? os / l : 0.f;
+  }
+  if (tid == 0) p.lse_ws[bh] = l > 0.f ? M + log2_hw(l) * kLn2 : kNegInf;
 }
 
 // Listed probabilities: raw logit -> exp(s - lse); ignored entries -> 0.
@@ -334,7 +357,7 @@ hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   SparseCombineParams cp{a.counts, part_o, part_ml, a.out, a.lse_out ? a.lse_out : lse_ws, a.num_q_heads,
                          a.num_kv_heads, a.idx_heads, n_chunks, a.head_dim};
-  hipLaunchKernelGGL(sparse_combine, dim3((unsigned)bh), dim3(128), 0, stream, cp);
+  hipLaunchKernelGGL(sparse_combine, dim3((unsigned)bh), dim3(128), n_chunks * sizeof(float), stream, cp);
   e = hipGetLastError();
   if (e != hipSuccess || !a.probs || a.raw_logits) return e;
   hipLaunchKernelGGL(sparse_normalize, dim3((a.max_count + 255) / 256, (unsigned)bh), dim3(256), 0,

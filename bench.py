@@ -426,6 +426,75 @@ def llama3_workload(torch, K, synth, args) -> dict:
     }
 
 
+def llama3_h2o_workload(torch, K, synth, args) -> dict:
+    """Llama-3-8B-shape layer, B=16, ragged L_b ~ U[8K, 32K], H2O with the
+    eviction inside the decode loop: the lists of kept positions are seeded
+    by one full score-emitting decode pass and the 20% keep set (sinks 4,
+    window 512), then ``steps`` decode steps each append the new token,
+    attend over the kept keys only, fold the probabilities into the list
+    scores and cut every list back to its budget."""
+    steps = args.steps
+    cfg = synth.llama3_8b_layer(steps=steps + 1, device="cuda")
+    kvt = cfg["kv"]
+    Bq, HQq, HKVq = 16, 32, 8
+    base = kvt.seq_lens.clone()
+    cap = int(base.max()) + steps + 1
+    kv0 = K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, base, 16, cap)
+    full = torch.zeros((Bq, HKVq, cap), device="cuda")
+    out = torch.empty((Bq, HQq, 128), device="cuda")
+    K.decode_attn_scores(kv0, cfg["q_steps"][0], HQq, cfg["scale"], out, None, None, K.EMIT_PROBS, full, 1.0)
+    budgets = (base.double() * 0.2).floor().to(torch.int32).repeat_interleave(HKVq).contiguous()
+    budget = int(budgets.max())
+    rows = full.view(Bq * HKVq, cap)
+    keep = torch.zeros((Bq * HKVq, budget), dtype=torch.int32, device="cuda")
+    kc = torch.empty((Bq * HKVq,), dtype=torch.int32, device="cuda")
+    K.select_keep(rows, base.repeat_interleave(HKVq).to(torch.int32), cap, 4, 512, budgets, budget, keep, kc)
+    stride = -(-(budget + 1) // 16) * 16
+    slots = torch.zeros((Bq, HKVq, stride), dtype=torch.int32, device="cuda")
+    cum = torch.zeros((Bq, HKVq, stride), device="cuda")
+    slots.view(-1, stride)[:, :budget] = keep
+    valid = torch.arange(budget, device="cuda")[None, :] < kc[:, None]
+    cum.view(-1, stride)[:, :budget] = torch.where(valid, torch.gather(rows, 1, keep.long()), 0.0)
+    cnt = kc.view(Bq, HKVq).clone()
+    kv_s = [K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, (base + s + 1).to(torch.int32), 16, cap)
+            for s in range(steps)]
+    ws = torch.empty(K.h2o_workspace_bytes(kv0, HQq, stride, 4, 512, budget), dtype=torch.uint8, device="cuda")
+    bview = budgets.view(Bq, HKVq)
+    # untimed warm-up on copies of the lists
+    s2, c2, n2 = slots.clone(), cum.clone(), cnt.clone()
+    for s in range(2):
+        K.h2o_step(kv_s[s], cfg["q_steps"][s + 1], HQq, cfg["scale"], s2, c2, n2, 4, 512, budget, out,
+                   budgets=bview, workspace=ws)
+    del s2, c2, n2
+    torch.cuda.synchronize()
+    kept_before = int(cnt.sum())
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for s in range(steps):
+        K.h2o_step(kv_s[s], cfg["q_steps"][s + 1], HQq, cfg["scale"], slots, cum, cnt, 4, 512, budget, out,
+                   budgets=bview, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / steps
+    kept_after = int(cnt.sum())
+    # keys read per step: the kept lists plus the appended token
+    keys = (kept_before + kept_after) / 2.0 + Bq * HKVq
+    kv_bytes = keys * 128 * 2 * 2
+    full_keys = float(base.sum()) * HKVq
+    return {
+        "metric": "KV GB/s (% HBM peak) for score-emitting decode attn + keep-set select",
+        "value": round(kv_bytes / (t * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "llama3_8b_h2o_evict", "batch": Bq, "seq_len": "U[8192,32768]", "q_heads": HQq,
+                   "kv_heads": HKVq, "head_dim": 128, "page_size": 16,
+                   "keep": "0.2 L per sequence (sinks 4, window 512), evicted every step"},
+        "step_us": round(t * 1e3, 1),
+        "kept_keys_per_step": round(keys),
+        "kept_fraction": round(keys / full_keys, 4),
+        "launches_per_step": 6,
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -437,7 +506,7 @@ def main() -> int:
                          "eager launches on this path)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--workload", default="llama70b_step",
-                    choices=["llama70b_step", "long_context_128k", "llama3_8b_steps"],
+                    choices=["llama70b_step", "long_context_128k", "llama3_8b_steps", "llama3_8b_h2o_evict"],
                     help="the default is the 70B decode step; the others report their own line")
     ap.add_argument("--counters", action="store_true",
                     help="counter-collection mode: one layer, 3 decode calls, then a plain 1 GiB "
@@ -462,6 +531,9 @@ def main() -> int:
         return 0
     if args.workload == "llama3_8b_steps":
         print(json.dumps(llama3_workload(torch, K, synth, args)), flush=True)
+        return 0
+    if args.workload == "llama3_8b_h2o_evict":
+        print(json.dumps(llama3_h2o_workload(torch, K, synth, args)), flush=True)
         return 0
 
     log("setup: generating 80 layers of synthetic paged KV on the GPU")

@@ -267,7 +267,7 @@ size_t kvsel_snapkv_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_head
  *           entry); entries past the count are left untouched.
  *   workspace: >= kvsel_sparse_workspace_bytes(num_seqs, num_q_heads,
  *           head_dim, max_count) bytes of device memory.
- * Errors: INVALID, UNSUPPORTED, WORKSPACE, HIP.
+ * Errors: INVALID, UNSUPPORTED (also max_count > 2^24), WORKSPACE, HIP.
  * ------------------------------------------------------------------------ */
 int kvsel_sparse_attn(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads,
                       const int32_t* indices, int64_t idx_stride, const int32_t* counts,
@@ -338,10 +338,13 @@ size_t kvsel_quest_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads
  *      positions of KV head h / G only; probs[b][h][i] = the probability of
  *      slot i (when probs != NULL);
  *   3. slot_cum[b][c][i] = decay * slot_cum + sum over the group of probs;
- *   4. when n > budget: keeps slots [0, min(sinks, n)), [max(n - window, 0),
- *      n) and the top max(0, budget - forced) of the others by score (ties
- *      to the lower slot, i.e. the lower position), in slot order, and drops
- *      the rest permanently; slot_count becomes the kept count.
+ *   4. when n > B (B = budgets[b * num_kv_heads + c] when `budgets` is not
+ *      NULL, else `budget`): keeps slots [0, min(sinks, n)), [max(n - window,
+ *      0), n) and the top max(0, B - forced) of the others by score (ties to
+ *      the lower slot, i.e. the lower position), in slot order, and drops the
+ *      rest permanently; slot_count becomes the kept count.
+ *   budgets   [num_seqs][num_kv_heads] i32 device array or NULL; every entry
+ *             must lie in [0, budget] (`budget` is their host-known bound).
  *   slots     [num_seqs][num_kv_heads][slot_stride] i32, slot_cum f32 alike,
  *   slot_count[num_seqs][num_kv_heads] i32; slot_stride >= budget + 1 and
  *             >= sinks + window + 1 (room for the appended token).
@@ -352,13 +355,13 @@ size_t kvsel_quest_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads
  * Preconditions: listed positions distinct, ascending and < L_b - 1, and
  * slot_count < slot_stride before the call.
  * Errors: INVALID (NULL pointers, negative sinks / window / budget, slot_stride
- * too small), UNSUPPORTED (group size not a power of two <= 8, and the
- * descriptor checks), WORKSPACE, HIP.
+ * too small), UNSUPPORTED (group size not a power of two <= 8, slot_stride >
+ * 2^24, and the descriptor checks), WORKSPACE, HIP.
  * ------------------------------------------------------------------------ */
 int kvsel_h2o_step(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads, float scale,
                    int32_t* slots, float* slot_cum, int32_t* slot_count, int64_t slot_stride,
-                   int32_t sinks, int32_t window, int32_t budget, float decay, float* out,
-                   float* probs, void* workspace, size_t workspace_bytes, void* stream);
+                   int32_t sinks, int32_t window, int32_t budget, const int32_t* budgets, float decay,
+                   float* out, float* probs, void* workspace, size_t workspace_bytes, void* stream);
 
 size_t kvsel_h2o_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads, int64_t slot_stride,
                                  int32_t sinks, int32_t window, int32_t budget);

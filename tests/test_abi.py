@@ -220,7 +220,7 @@ def test_h2o_validation():
              wsb=1 << 30):
         kvd = kvd or _kv()
         return lib.kvsel_h2o_step(ctypes.byref(kvd), FAKE, hq, 0.1, slots, FAKE, FAKE, stride, sinks, window,
-                                  budget, 1.0, out, None, ws, wsb, None)
+                                  budget, None, 1.0, out, None, ws, wsb, None)
     assert call(slots=None) == K.KVSEL_ERR_INVALID
     assert call(out=None) == K.KVSEL_ERR_INVALID
     assert call(kvd=_kv(v_pages=None)) == K.KVSEL_ERR_INVALID

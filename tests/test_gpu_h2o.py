@@ -128,7 +128,8 @@ def test_h2o_step_llama3_shape_with_vote_seeded_lists():
     """Llama-3-8B-shape layer scaled down (B=4, 32 / 8 heads, L_b in [1000,
     3000]): lists seeded by one full score-emitting decode pass and the
     keep-set selection at 20% (sinks 4, window 64), then 6 steps of per-step
-    eviction; each step checked against the oracle on the GPU's state."""
+    eviction with the same per-sequence budgets; each step checked against
+    the oracle on the GPU's state."""
     K = _K()
     steps = 6
     cfg = synth.llama3_8b_layer(num_seqs=4, min_len=1000, max_len=3000, steps=steps + 1, device="cuda")
@@ -165,10 +166,59 @@ def test_h2o_step_llama3_shape_with_vote_seeded_lists():
         kv = K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, lens, 16, cap)
         prev = (f64(slots).astype(np.int64), f64(cum), cnt.cpu().numpy().copy())
         q = cfg["q_steps"][t + 1].contiguous()
-        K.h2o_step(kv, q, Hq, cfg["scale"], slots, cum, cnt, 4, 64, budget, out)
+        K.h2o_step(kv, q, Hq, cfg["scale"], slots, cum, cnt, 4, 64, budget, out, budgets=budgets.view(B, Hkv))
         torch.cuda.synchronize()
         s_h, c_h, n_h, o_h = slots.cpu().numpy(), f64(cum), cnt.cpu().numpy(), f64(out)
         for b in range(B):
             Kl, Vl = logical[b]
             _check_step(f64(q[b]), Kl, Vl, int(lens[b]), prev, b, o_h[b], None, s_h, c_h, n_h, 4,
-                        cfg["scale"], 4, 64, budget)
+                        cfg["scale"], 4, 64, int(budgets[b * Hkv]))
+
+
+def test_h2o_step_general_and_fused_eviction_paths():
+    """A list seeded longer than its budget sheds many slots at the first
+    step (the general selection) and one per step afterwards (the fused
+    argmin); a list over 8192 slots always takes the general path.  Budgets
+    differ per list (one below the forced sinks + window)."""
+    K = _K()
+    g = synth.generator(88)
+    prompts, P, d, G, Hkv, T = [12000, 700], 16, 64, 2, 2, 3
+    B, Hq = 2, Hkv * G
+    cap = max(prompts) + T
+    bt, n_pages = synth.shuffled_block_table(B, cap, P, g)
+    kp = synth.normal((n_pages, Hkv, P, d), g, torch.bfloat16).cuda()
+    vp = synth.normal((n_pages, Hkv, P, d), g, torch.bfloat16).cuda()
+    qs = synth.normal((T, B, Hq, d), g, torch.bfloat16).cuda()
+    bt = bt.cuda()
+    stride = 12000 + T + 1
+    slots = torch.zeros((B, Hkv, stride), dtype=torch.int32)
+    cum = torch.zeros((B, Hkv, stride))
+    cnt = torch.zeros((B, Hkv), dtype=torch.int32)
+    rng = np.random.default_rng(88)
+    for b, L0 in enumerate(prompts):
+        for c in range(Hkv):
+            slots[b, c, :L0] = torch.arange(L0, dtype=torch.int32)
+            cum[b, c, :L0] = torch.from_numpy(rng.uniform(0, 3, L0).astype(np.float32))
+            cnt[b, c] = L0
+    slots, cum, cnt = slots.cuda(), cum.cuda(), cnt.cuda()
+    # list (0, 0) keeps more than 8192 slots; (1, 1) has a budget below sinks + window
+    budgets = torch.tensor([[10000, 3000], [500, 10]], dtype=torch.int32, device="cuda")
+    scale = 1 / math.sqrt(d)
+    logical = [logical_kv(kp, vp, bt, b, L0 + T) for b, L0 in enumerate(prompts)]
+    for t in range(T):
+        lens = torch.tensor([L0 + t + 1 for L0 in prompts], dtype=torch.int32, device="cuda")
+        kv = K.PagedKV(kp, vp, bt, lens, P, cap)
+        prev = (f64(slots).astype(np.int64), f64(cum), cnt.cpu().numpy().copy())
+        out = torch.empty((B, Hq, d), device="cuda")
+        K.h2o_step(kv, qs[t].contiguous(), Hq, scale, slots, cum, cnt, 4, 16, 10000, out, budgets=budgets)
+        torch.cuda.synchronize()
+        s_h, c_h, n_h, o_h = slots.cpu().numpy(), f64(cum), cnt.cpu().numpy(), f64(out)
+        for b, L0 in enumerate(prompts):
+            Kl, Vl = logical[b]
+            for c in range(Hkv):
+                # one KV head at a time: its own budget
+                sub = (prev[0][:, c:c + 1], prev[1][:, c:c + 1], prev[2][:, c:c + 1])
+                _check_step(f64(qs[t, b, c * G:(c + 1) * G]), Kl[c:c + 1], Vl[c:c + 1], L0 + t + 1, sub, b,
+                            o_h[b, c * G:(c + 1) * G], None, s_h[:, c:c + 1], c_h[:, c:c + 1], n_h[:, c:c + 1], G,
+                            scale, 4, 16, int(budgets[b, c]))
+        assert int(cnt[1, 1]) == 20 and int(cnt[0, 0]) == 10000
