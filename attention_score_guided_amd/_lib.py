@@ -24,6 +24,8 @@ KVSEL_F32, KVSEL_BF16 = 0, 1
 EMIT_PROBS, EMIT_LOGITS = 0, 1
 REDUCE_NONE, REDUCE_SUM = 0, 1
 SELECT_ROWS, SELECT_GLOBAL_PERCENTILE = 0, 1
+ACC_SUM, ACC_MAX, ACC_WINDOW_MEAN = 0, 1, 2
+BLOCK_TOP_P_MEAN, BLOCK_FRAC_ABOVE, BLOCK_ALL_COLD = 0, 1, 2
 
 # Every symbol include/kvsel.h declares.
 EXPORTED = (
@@ -32,7 +34,8 @@ EXPORTED = (
     "kvsel_block_aggregate", "kvsel_select_keep", "kvsel_select_workspace_bytes",
     "kvsel_snapkv_vote", "kvsel_snapkv_workspace_bytes", "kvsel_sparse_attn",
     "kvsel_sparse_workspace_bytes", "kvsel_quest_summarize", "kvsel_quest_select",
-    "kvsel_quest_workspace_bytes", "kvsel_h2o_step", "kvsel_h2o_workspace_bytes", "kvsel_set_sync_spin_limit",
+    "kvsel_quest_workspace_bytes", "kvsel_accumulate_ex", "kvsel_block_aggregate_ex", "kvsel_select_threshold",
+    "kvsel_h2o_step", "kvsel_h2o_workspace_bytes", "kvsel_set_sync_spin_limit",
     "kvsel_status_string", "kvsel_last_error",
 )
 
@@ -79,6 +82,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvsel_quest_workspace_bytes": (SZ, [D, I32, I32]),
         "kvsel_h2o_step": (ctypes.c_int, [D, P, I32, F, P, P, P, I64, I32, I32, I32, P, F, P, P, P, SZ, P]),
         "kvsel_h2o_workspace_bytes": (SZ, [D, I32, I64, I32, I32, I32]),
+        "kvsel_accumulate_ex": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, I32, F, I32, I32, P, P, I64, P]),
+        "kvsel_block_aggregate_ex": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, I32, F, P, I64, P]),
+        "kvsel_select_threshold": (ctypes.c_int, [P, I64, P, I32, I32, F, P, I64, P, P]),
         "kvsel_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "kvsel_set_sync_spin_limit": (I32, [I32]),
         "kvsel_last_error": (ctypes.c_char_p, []),
@@ -345,3 +351,34 @@ def h2o_step(kv: PagedKV, q: torch.Tensor, num_q_heads: int, scale: float, slots
         int(sinks), int(window), int(budget), _ptr(budgets, torch.int32, "budgets"), float(decay),
         _ptr(out, torch.float32, "out"),
         _ptr(probs, torch.float32, "probs"), _ptr(ws, None, "workspace"), wsb, _stream(stream)))
+
+
+def accumulate_ex(probs: torch.Tensor, seq_lens: torch.Tensor, num_kv_heads: int, max_seq_len: int,
+                  cum: torch.Tensor, mode: int, decay: float = 1.0, window: int = 0, step: int = 0,
+                  ring: Optional[torch.Tensor] = None, stream=None) -> None:
+    """kvsel_accumulate_ex: probs ``[B][H_q][stride]``, cum ``[B][H_kv][stride]``,
+    ring ``[window][B][H_kv][stride]`` (WINDOW_MEAN)."""
+    B, Hq, _ = probs.shape
+    _check(_LIB.kvsel_accumulate_ex(
+        _ptr(probs, torch.float32, "probs"), probs.shape[-1], _ptr(seq_lens, torch.int32, "seq_lens"), B, Hq,
+        num_kv_heads, max_seq_len, int(mode), float(decay), int(window), int(step),
+        _ptr(ring, torch.float32, "ring"), _ptr(cum, torch.float32, "cum"), cum.shape[-1], _stream(stream)))
+
+
+def block_aggregate_ex(scores: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, block_size: int,
+                       mode: int, param: float, out: torch.Tensor, stream=None) -> None:
+    """kvsel_block_aggregate_ex: scores ``[B][H][stride]`` -> out ``[B][H][out_stride]``."""
+    B, H, _ = scores.shape
+    _check(_LIB.kvsel_block_aggregate_ex(
+        _ptr(scores, torch.float32, "scores"), scores.shape[-1], _ptr(seq_lens, torch.int32, "seq_lens"), B, H,
+        max_seq_len, block_size, int(mode), float(param), _ptr(out, torch.float32, "out"), out.shape[-1],
+        _stream(stream)))
+
+
+def select_threshold(scores: torch.Tensor, lengths: torch.Tensor, max_len: int, threshold: float,
+                     out_idx: torch.Tensor, out_count: torch.Tensor, stream=None) -> None:
+    """kvsel_select_threshold: scores ``[rows][stride]`` -> out_idx ``[rows][out_stride]``."""
+    _check(_LIB.kvsel_select_threshold(
+        _ptr(scores, torch.float32, "scores"), scores.shape[-1], _ptr(lengths, torch.int32, "lengths"),
+        scores.shape[0], max_len, float(threshold), _ptr(out_idx, torch.int32, "out_idx"), out_idx.shape[-1],
+        _ptr(out_count, torch.int32, "out_count"), _stream(stream)))

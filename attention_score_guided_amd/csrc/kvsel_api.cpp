@@ -413,6 +413,57 @@ int kvsel_snapkv_vote(const kvsel_paged_kv* kv, const void* q_win, int32_t num_q
   return hip_status(kvsel::launch_snapkv(a, static_cast<hipStream_t>(stream)), "snapkv_vote launch");
 }
 
+int kvsel_accumulate_ex(const float* probs, int64_t probs_stride, const int32_t* seq_lens, int32_t num_seqs,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len, int32_t mode, float decay,
+                        int32_t window, int32_t step, float* ring, float* cum, int64_t cum_stride, void* stream) {
+  if (!probs || !seq_lens || !cum) return fail(KVSEL_ERR_INVALID, "NULL pointer argument");
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len <= 0)
+    return fail(KVSEL_ERR_INVALID, "dimensions must be positive");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(KVSEL_ERR_INVALID, "num_q_heads is not a multiple of num_kv_heads");
+  if (probs_stride < max_seq_len || cum_stride < max_seq_len) return fail(KVSEL_ERR_INVALID, "stride < max_seq_len");
+  if (mode < KVSEL_ACC_SUM || mode > KVSEL_ACC_WINDOW_MEAN) return fail(KVSEL_ERR_INVALID, "mode %d", mode);
+  if (mode == KVSEL_ACC_WINDOW_MEAN && (!ring || window <= 0 || step < 0))
+    return fail(KVSEL_ERR_INVALID, "WINDOW_MEAN needs a ring, window > 0 and step >= 0");
+  int st = check_device();
+  if (st != KVSEL_OK) return st;
+  return hip_status(kvsel::launch_accumulate_ex(probs, probs_stride, seq_lens, num_seqs, num_q_heads, num_kv_heads,
+                                                max_seq_len, mode, decay, window, step, ring, cum, cum_stride,
+                                                static_cast<hipStream_t>(stream)),
+                    "accumulate_ex launch");
+}
+
+int kvsel_block_aggregate_ex(const float* scores, int64_t score_stride, const int32_t* seq_lens, int32_t num_seqs,
+                             int32_t num_heads, int32_t max_seq_len, int32_t block_size, int32_t mode, float param,
+                             float* out, int64_t out_stride, void* stream) {
+  if (!scores || !seq_lens || !out) return fail(KVSEL_ERR_INVALID, "NULL pointer argument");
+  if (num_seqs <= 0 || num_heads <= 0 || max_seq_len <= 0 || block_size <= 0)
+    return fail(KVSEL_ERR_INVALID, "dimensions must be positive");
+  if (mode < KVSEL_BLOCK_TOP_P_MEAN || mode > KVSEL_BLOCK_ALL_COLD) return fail(KVSEL_ERR_INVALID, "mode %d", mode);
+  if (score_stride < max_seq_len) return fail(KVSEL_ERR_INVALID, "score_stride < max_seq_len");
+  const long long n_blk = ((long long)max_seq_len + block_size - 1) / block_size;
+  if (out_stride < n_blk) return fail(KVSEL_ERR_INVALID, "out_stride %lld < %lld blocks", (long long)out_stride, n_blk);
+  if (block_size > 256) return fail(KVSEL_ERR_UNSUPPORTED, "block_size %d > 256", block_size);
+  int st = check_device();
+  if (st != KVSEL_OK) return st;
+  return hip_status(kvsel::launch_block_variant(scores, score_stride, seq_lens, num_seqs, num_heads, max_seq_len,
+                                                block_size, mode, param, out, out_stride,
+                                                static_cast<hipStream_t>(stream)),
+                    "block_aggregate_ex launch");
+}
+
+int kvsel_select_threshold(const float* scores, int64_t stride, const int32_t* lengths, int32_t rows, int32_t max_len,
+                           float threshold, int32_t* out_idx, int64_t out_stride, int32_t* out_count, void* stream) {
+  if (!scores || !lengths || !out_idx || !out_count) return fail(KVSEL_ERR_INVALID, "NULL pointer argument");
+  if (rows <= 0 || max_len <= 0) return fail(KVSEL_ERR_INVALID, "rows and max_len must be positive");
+  if (stride < max_len || out_stride < max_len) return fail(KVSEL_ERR_INVALID, "stride or out_stride < max_len");
+  int st = check_device();
+  if (st != KVSEL_OK) return st;
+  return hip_status(kvsel::launch_select_threshold(scores, stride, lengths, rows, threshold, out_idx, out_stride,
+                                                   out_count, static_cast<hipStream_t>(stream)),
+                    "select_threshold launch");
+}
+
 int kvsel_quest_summarize(const kvsel_paged_kv* kv, int32_t first_page, void* summary, void* stream) {
   int st = check_kv(kv, kv ? kv->num_kv_heads : 1, false);
   if (st != KVSEL_OK) return st;

@@ -60,6 +60,17 @@ hipError_t launch_block_aggregate(const float* scores, int64_t score_stride,
                                   float* out_max, float* out_mean, int64_t out_stride,
                                   int64_t out_seq_stride, hipStream_t stream);  // <= 0: packed rows
 
+hipError_t launch_accumulate_ex(const float* probs, int64_t probs_stride, const int32_t* seq_lens, int num_seqs,
+                                int num_q_heads, int num_kv_heads, int max_seq_len, int mode, float decay,
+                                int window, int step, float* ring, float* cum, int64_t cum_stride,
+                                hipStream_t stream);
+hipError_t launch_block_variant(const float* scores, int64_t score_stride, const int32_t* seq_lens, int num_seqs,
+                                int num_heads, int max_seq_len, int block_size, int mode, float param, float* out,
+                                int64_t out_stride, hipStream_t stream);
+hipError_t launch_select_threshold(const float* scores, int64_t stride, const int32_t* lengths, int rows,
+                                   float threshold, int32_t* out_idx, int64_t out_stride, int32_t* out_count,
+                                   hipStream_t stream);
+
 size_t select_workspace_bytes(int rows, int max_len, int mode);
 
 hipError_t launch_select(const float* scores, int64_t stride, const int32_t* lengths, int rows,

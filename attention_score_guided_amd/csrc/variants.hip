@@ -1,0 +1,190 @@
+// Score-aggregation variants the pages leave open as design choices.
+//
+// Across decode steps ([OFFLOAD] "Sparse attention x KV-cache offloading",
+// §2.1: sliding-window average, exponential decay, max pooling):
+//   accumulate_max_kernel     cum = max(decay * cum, g)
+//   accumulate_window_kernel  ring[step % W] = g, cum = (1/W) sum of the ring
+// where g is the group sum of one step's probabilities per KV head.
+// Token -> block ([OFFLOAD] §3.1 top-p%; [EVICT] §5.1 ranking blocks by their
+// share of important tokens, and evicting only all-cold blocks):
+//   block_variant_kernel      top-p% mean | fraction >= threshold | all-cold flag
+// Across requests ([OFFLOAD] §3.2, absolute-threshold normalisation):
+//   select_threshold_kernel   positions with score >= threshold, ascending
+// All are HBM-bound streaming passes with one writer per output element.
+#include "device_common.hpp"
+#include "kvsel_internal.hpp"
+
+namespace kvsel {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float group_prob_sum(const float* pr, int64_t stride, int G, int j) {
+  float acc = 0.f;
+  for (int g = 0; g < G; ++g) acc += pr[(size_t)g * stride + j];
+  return acc;
+}
+
+__global__ __launch_bounds__(kThreads) void accumulate_max_kernel(
+    const float* __restrict__ probs, int64_t probs_stride, const int32_t* __restrict__ seq_lens, int num_q_heads,
+    int num_kv_heads, float decay, float* __restrict__ cum, int64_t cum_stride) {
+  const int b = blockIdx.z, c = blockIdx.y;
+  const int L = seq_lens[b];
+  const int j = blockIdx.x * kThreads + threadIdx.x;
+  if (j >= L) return;
+  const int G = num_q_heads / num_kv_heads;
+  const float g = group_prob_sum(probs + ((size_t)b * num_q_heads + (size_t)c * G) * probs_stride, probs_stride, G, j);
+  float* cp = cum + ((size_t)b * num_kv_heads + c) * cum_stride + j;
+  *cp = fmaxf(decay * *cp, g);
+}
+
+// ring [W][B][H_kv][cum_stride]: slot `slot` receives this step's g, and cum
+// the mean of the W slots (summed in slot order: the result does not depend
+// on which slot is the newest).
+__global__ __launch_bounds__(kThreads) void accumulate_window_kernel(
+    const float* __restrict__ probs, int64_t probs_stride, const int32_t* __restrict__ seq_lens, int num_q_heads,
+    int num_kv_heads, int num_seqs, int window, int slot, float* __restrict__ ring, float* __restrict__ cum,
+    int64_t cum_stride) {
+  const int b = blockIdx.z, c = blockIdx.y;
+  const int L = seq_lens[b];
+  const int j = blockIdx.x * kThreads + threadIdx.x;
+  if (j >= L) return;
+  const int G = num_q_heads / num_kv_heads;
+  const float g = group_prob_sum(probs + ((size_t)b * num_q_heads + (size_t)c * G) * probs_stride, probs_stride, G, j);
+  const size_t row = (size_t)b * num_kv_heads + c;
+  const size_t plane = (size_t)num_seqs * num_kv_heads * cum_stride;
+  float s = 0.f;
+  for (int w = 0; w < window; ++w) {
+    float* r = ring + w * plane + row * cum_stride + j;
+    float v = *r;
+    if (w == slot) {
+      v = g;
+      *r = g;
+    }
+    s += v;
+  }
+  cum[row * cum_stride + j] = s / (float)window;
+}
+
+// One wave per block of <= 256 positions: its valid scores in LDS; the
+// top-p% mean ranks each element by counting the elements that beat it
+// (greater, or equal at a lower position), so the m largest are exact and the
+// order of equal scores cannot change the sum's terms.
+constexpr int kVarWaves = kThreads / kWave;
+constexpr int kVarMaxBlock = 256;
+
+__global__ __launch_bounds__(kThreads) void block_variant_kernel(
+    const float* __restrict__ scores, int64_t score_stride, const int32_t* __restrict__ seq_lens, int num_heads,
+    int block_size, int mode, float param, float* __restrict__ out, int64_t out_stride) {
+  __shared__ float v_lds[kVarWaves][kVarMaxBlock];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int L = seq_lens[b];
+  const int blk = blockIdx.x * kVarWaves + wave;
+  const int start = blk * block_size;
+  if (start >= L) return;
+  const int n = min(block_size, L - start);
+  const float* row = scores + ((size_t)b * num_heads + h) * score_stride + start;
+  float* vs = v_lds[wave];
+  for (int i = lane; i < n; i += kWave) vs[i] = row[i];
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // the wave's LDS writes before its reads
+  __builtin_amdgcn_wave_barrier();
+  float res;
+  if (mode == 0) {                       // mean of the m = ceil(p * n) largest
+    const int m = max(1, min(n, (int)ceilf(param * (float)n)));
+    float part = 0.f;
+    for (int i = lane; i < n; i += kWave) {
+      const float x = vs[i];
+      int beat = 0;
+      for (int t = 0; t < n; ++t) {
+        const float y = vs[t];
+        beat += (y > x || (y == x && t < i)) ? 1 : 0;
+      }
+      if (beat < m) part += x;
+    }
+    res = wave_sum(part) / (float)m;
+  } else {
+    int cnt = 0;                          // elements >= threshold
+    for (int i = lane; i < n; i += kWave) cnt += vs[i] >= param ? 1 : 0;
+    for (int off = kWave / 2; off > 0; off /= 2) cnt += __shfl_xor(cnt, off, kWave);
+    res = mode == 1 ? (float)cnt / (float)n : (cnt == 0 ? 1.f : 0.f);
+  }
+  if (lane == 0) out[((size_t)b * num_heads + h) * out_stride + blk] = res;
+}
+
+// One workgroup per row: the positions with score >= threshold, ascending,
+// by a block-wide scan over chunks of kThreads positions.
+__global__ __launch_bounds__(kThreads) void select_threshold_kernel(
+    const float* __restrict__ scores, int64_t stride, const int32_t* __restrict__ lengths, float threshold,
+    int32_t* __restrict__ out_idx, int64_t out_stride, int32_t* __restrict__ out_count) {
+  __shared__ int wsum[kThreads / kWave];
+  const int r = blockIdx.x;
+  const int n = lengths[r];
+  const float* row = scores + (size_t)r * stride;
+  int32_t* out = out_idx + (size_t)r * out_stride;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  int base = 0;
+  for (int j0 = 0; j0 < n; j0 += kThreads) {
+    const int j = j0 + tid;
+    const int keep = (j < n && row[j] >= threshold) ? 1 : 0;
+    // inclusive scan within the wave, then across the waves
+    int incl = keep;
+#pragma unroll
+    for (int off = 1; off < kWave; off *= 2) {
+      const int t = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += t;
+    }
+    if (lane == kWave - 1) wsum[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / kWave; ++w) {
+      before += w < wave ? wsum[w] : 0;
+      total += wsum[w];
+    }
+    if (keep) out[base + before + incl - 1] = j;
+    base += total;
+    __syncthreads();
+  }
+  if (tid == 0) out_count[r] = base;
+}
+
+}  // namespace
+
+hipError_t launch_accumulate_ex(const float* probs, int64_t probs_stride, const int32_t* seq_lens, int num_seqs,
+                                int num_q_heads, int num_kv_heads, int max_seq_len, int mode, float decay,
+                                int window, int step, float* ring, float* cum, int64_t cum_stride,
+                                hipStream_t stream) {
+  const dim3 grid((max_seq_len + kThreads - 1) / kThreads, num_kv_heads, num_seqs);
+  if (mode == 0)
+    return launch_accumulate(probs, probs_stride, seq_lens, num_seqs, num_q_heads, num_kv_heads, max_seq_len, decay,
+                             cum, cum_stride, stream);
+  if (mode == 1)
+    hipLaunchKernelGGL(accumulate_max_kernel, grid, dim3(kThreads), 0, stream, probs, probs_stride, seq_lens,
+                       num_q_heads, num_kv_heads, decay, cum, cum_stride);
+  else
+    hipLaunchKernelGGL(accumulate_window_kernel, grid, dim3(kThreads), 0, stream, probs, probs_stride, seq_lens,
+                       num_q_heads, num_kv_heads, num_seqs, window, step % window, ring, cum, cum_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_variant(const float* scores, int64_t score_stride, const int32_t* seq_lens, int num_seqs,
+                                int num_heads, int max_seq_len, int block_size, int mode, float param, float* out,
+                                int64_t out_stride, hipStream_t stream) {
+  const int n_blk = (max_seq_len + block_size - 1) / block_size;
+  const dim3 grid((n_blk + kVarWaves - 1) / kVarWaves, num_heads, num_seqs);
+  hipLaunchKernelGGL(block_variant_kernel, grid, dim3(kThreads), 0, stream, scores, score_stride, seq_lens, num_heads,
+                     block_size, mode, param, out, out_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_threshold(const float* scores, int64_t stride, const int32_t* lengths, int rows,
+                                   float threshold, int32_t* out_idx, int64_t out_stride, int32_t* out_count,
+                                   hipStream_t stream) {
+  hipLaunchKernelGGL(select_threshold_kernel, dim3(rows), dim3(kThreads), 0, stream, scores, stride, lengths,
+                     threshold, out_idx, out_stride, out_count);
+  return hipGetLastError();
+}
+
+}  // namespace kvsel

@@ -278,6 +278,58 @@ size_t kvsel_sparse_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
                                     int32_t max_count);
 
 /* ------------------------------------------------------------------------
+ * Score-aggregation variants that the pages leave open as design choices.
+ *
+ * kvsel_accumulate_ex: one step's probabilities folded across decode steps
+ * ([OFFLOAD] §2.1: exponential decay, max pooling, sliding-window average).
+ * With g[b][c][j] = sum over the query heads of KV head c of probs[b][h][j],
+ * for j < L_b:
+ *   KVSEL_ACC_SUM (0):         cum = decay * cum + g    (H2O; = kvsel_accumulate)
+ *   KVSEL_ACC_MAX (1):         cum = max(decay * cum, g)
+ *   KVSEL_ACC_WINDOW_MEAN (2): ring[step % window][b][c][j] = g, then
+ *                              cum = (sum of the `window` ring slots) / window
+ *                              (slots never written count as 0: the ring must
+ *                              start zeroed).
+ *   ring  [window][num_seqs][num_kv_heads][cum_stride] f32 (WINDOW_MEAN only).
+ * Errors: INVALID (NULL pointers, bad dims, strides, mode, window <= 0 or
+ * step < 0 for WINDOW_MEAN), HIP.
+ * ------------------------------------------------------------------------ */
+typedef enum { KVSEL_ACC_SUM = 0, KVSEL_ACC_MAX = 1, KVSEL_ACC_WINDOW_MEAN = 2 } kvsel_acc_mode;
+
+int kvsel_accumulate_ex(const float* probs, int64_t probs_stride, const int32_t* seq_lens, int32_t num_seqs,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len, int32_t mode,
+                        float decay, int32_t window, int32_t step, float* ring, float* cum, int64_t cum_stride,
+                        void* stream);
+
+/* kvsel_block_aggregate_ex: one score per block of `block_size` positions
+ * (the last block partial: only valid positions count), per (b, h):
+ *   KVSEL_BLOCK_TOP_P_MEAN (0): mean of the m = max(1, ceil(param * n)) largest
+ *     scores of the block's n valid positions ([OFFLOAD] §3.1 "top-p%", read
+ *     as the mean of the block's top p fraction: between max and mean);
+ *   KVSEL_BLOCK_FRAC_ABOVE (1): fraction of the n positions with score >= param
+ *     ([EVICT] §5.1: rank blocks by their share of important tokens);
+ *   KVSEL_BLOCK_ALL_COLD (2): 1 when every position scores < param, else 0
+ *     ([EVICT] §5.1: evict only blocks that are cold throughout).
+ *   out [num_seqs][num_heads][out_stride] f32, out_stride >= ceil(max_seq_len /
+ *   block_size); block_size in [1, 256].
+ * Errors: INVALID, UNSUPPORTED (block_size > 256), HIP.
+ * ------------------------------------------------------------------------ */
+typedef enum { KVSEL_BLOCK_TOP_P_MEAN = 0, KVSEL_BLOCK_FRAC_ABOVE = 1, KVSEL_BLOCK_ALL_COLD = 2 } kvsel_block_mode;
+
+int kvsel_block_aggregate_ex(const float* scores, int64_t score_stride, const int32_t* seq_lens, int32_t num_seqs,
+                             int32_t num_heads, int32_t max_seq_len, int32_t block_size, int32_t mode, float param,
+                             float* out, int64_t out_stride, void* stream);
+
+/* kvsel_select_threshold: absolute-threshold selection across requests
+ * ([OFFLOAD] §3.2): per row r, the positions j < lengths[r] with
+ * scores[r][j] >= threshold, ascending, and their count.  out_stride >= max_len.
+ * Errors: INVALID, HIP.
+ * ------------------------------------------------------------------------ */
+int kvsel_select_threshold(const float* scores, int64_t stride, const int32_t* lengths, int32_t rows,
+                           int32_t max_len, float threshold, int32_t* out_idx, int64_t out_stride,
+                           int32_t* out_count, void* stream);
+
+/* ------------------------------------------------------------------------
  * Quest page summaries ([LONGCTX] sparse-attention experiment, the Quest
  * strategy: the per-channel minimum and maximum of a page's keys).
  * For every whole page p of every sequence with p >= first_page (pages with

@@ -26,6 +26,7 @@ no function here claims to reproduce them.
 """
 from __future__ import annotations
 
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -36,6 +37,12 @@ __all__ = [
     "decode_attention",
     "accumulate",
     "block_aggregate",
+    "accumulate_max",
+    "accumulate_window",
+    "block_top_p_mean",
+    "block_fraction_above",
+    "block_all_cold",
+    "select_threshold",
     "select_keep",
     "streaming_keep",
     "recent_keep",
@@ -150,6 +157,27 @@ def accumulate(cum: np.ndarray, probs: np.ndarray, decay: float = 1.0) -> np.nda
     return new
 
 
+def accumulate_max(cum: np.ndarray, probs: np.ndarray, decay: float = 1.0) -> np.ndarray:
+    """Max pooling across decode steps ([OFFLOAD] §2.1): each position keeps
+    the peak of its group-summed probability, cum = max(decay*cum, g)."""
+    g = accumulate(np.zeros_like(cum, dtype=np.float64), probs)
+    return np.maximum(decay * cum.astype(np.float64), g)
+
+
+def accumulate_window(history, probs: np.ndarray, Hkv: int, window: int) -> np.ndarray:
+    """Sliding-window average across decode steps ([OFFLOAD] §2.1): the mean of
+    the group-summed probabilities of the last ``window`` steps, steps before
+    the first counting as 0.  ``history`` is the list of earlier steps' group
+    sums (``[H_kv][L]`` each, newest last); this step's is appended to it."""
+    L = probs.shape[1]
+    history.append(accumulate(np.zeros((Hkv, L)), probs))
+    last = history[-window:]
+    total = np.zeros((Hkv, L))
+    for g in last:
+        total[:, :g.shape[1]] += g
+    return total / window
+
+
 # --------------------------------------------------------------------------
 # O3: token -> block aggregation
 # --------------------------------------------------------------------------
@@ -177,6 +205,37 @@ def block_aggregate(scores: np.ndarray, length: int, block_size: int):
 # --------------------------------------------------------------------------
 # O4: keep-set selection (sinks + heavy hitters + recent window)
 # --------------------------------------------------------------------------
+def block_top_p_mean(scores: np.ndarray, length: int, block_size: int, p: float) -> np.ndarray:
+    """Per block, the mean of its m = max(1, ceil(p*n)) largest valid scores
+    ([OFFLOAD] §3.1 "top-p%", between the block max (p -> 0) and mean (p = 1))."""
+    out = []
+    for s in range(0, length, block_size):
+        vals = sorted(np.asarray(scores[s:min(s + block_size, length)], dtype=np.float64), reverse=True)
+        m = max(1, min(len(vals), math.ceil(p * len(vals))))
+        out.append(sum(vals[:m]) / m)
+    return np.array(out)
+
+
+def block_fraction_above(scores: np.ndarray, length: int, block_size: int, threshold: float) -> np.ndarray:
+    """Per block, the share of its valid positions scoring >= threshold (blocks
+    ranked by their share of important tokens, [EVICT] §5.1)."""
+    return np.array([np.mean(np.asarray(scores[s:min(s + block_size, length)]) >= threshold)
+                     for s in range(0, length, block_size)])
+
+
+def block_all_cold(scores: np.ndarray, length: int, block_size: int, threshold: float) -> np.ndarray:
+    """1 for a block whose every valid position scores < threshold, else 0
+    (only all-cold blocks may be evicted, [EVICT] §5.1)."""
+    return np.array([float(all(x < threshold for x in scores[s:min(s + block_size, length)]))
+                     for s in range(0, length, block_size)])
+
+
+def select_threshold(scores: np.ndarray, n: int, threshold: float) -> np.ndarray:
+    """Absolute-threshold selection ([OFFLOAD] §3.2): the positions scoring
+    >= threshold, ascending."""
+    return np.array([j for j in range(n) if scores[j] >= threshold], dtype=np.int64)
+
+
 def select_keep(scores: np.ndarray, n: int, sinks: int, window: int, budget: int) -> np.ndarray:
     """H2O keep set of one row: sinks, heavy hitters and the recent window.
 

@@ -233,3 +233,23 @@ def test_h2o_validation():
     need = lib.kvsel_h2o_workspace_bytes(ctypes.byref(_kv()), 32, 80, 4, 16, 64)
     assert need >= 2 * 32 * 80 * 4                                 # the logits of every listed slot
     assert call(wsb=need - 1) == K.KVSEL_ERR_WORKSPACE
+
+
+def test_variant_validation():
+    lib = K.library()
+    acc = lib.kvsel_accumulate_ex
+    assert acc(None, 8, FAKE, 1, 4, 1, 8, 1, 1.0, 0, 0, None, FAKE, 8, None) == K.KVSEL_ERR_INVALID
+    assert acc(FAKE, 8, FAKE, 1, 4, 1, 8, 3, 1.0, 0, 0, None, FAKE, 8, None) == K.KVSEL_ERR_INVALID   # mode
+    assert acc(FAKE, 8, FAKE, 1, 4, 1, 8, 2, 1.0, 4, 0, None, FAKE, 8, None) == K.KVSEL_ERR_INVALID   # no ring
+    assert acc(FAKE, 8, FAKE, 1, 4, 1, 8, 2, 1.0, 0, 0, FAKE, FAKE, 8, None) == K.KVSEL_ERR_INVALID   # window 0
+    assert acc(FAKE, 8, FAKE, 1, 4, 1, 8, 2, 1.0, 4, -1, FAKE, FAKE, 8, None) == K.KVSEL_ERR_INVALID  # step < 0
+    assert acc(FAKE, 7, FAKE, 1, 4, 1, 8, 1, 1.0, 0, 0, None, FAKE, 8, None) == K.KVSEL_ERR_INVALID   # stride
+    blk = lib.kvsel_block_aggregate_ex
+    assert blk(FAKE, 64, FAKE, 1, 1, 64, 16, 0, 0.5, None, 4, None) == K.KVSEL_ERR_INVALID
+    assert blk(FAKE, 64, FAKE, 1, 1, 64, 16, 3, 0.5, FAKE, 4, None) == K.KVSEL_ERR_INVALID
+    assert blk(FAKE, 64, FAKE, 1, 1, 64, 16, 0, 0.5, FAKE, 3, None) == K.KVSEL_ERR_INVALID
+    assert blk(FAKE, 1024, FAKE, 1, 1, 1024, 512, 0, 0.5, FAKE, 4, None) == K.KVSEL_ERR_UNSUPPORTED
+    thr = lib.kvsel_select_threshold
+    assert thr(FAKE, 100, FAKE, 4, 100, 0.5, None, 100, FAKE, None) == K.KVSEL_ERR_INVALID
+    assert thr(FAKE, 100, FAKE, 4, 100, 0.5, FAKE, 99, FAKE, None) == K.KVSEL_ERR_INVALID
+    assert thr(FAKE, 100, FAKE, 0, 100, 0.5, FAKE, 100, FAKE, None) == K.KVSEL_ERR_INVALID

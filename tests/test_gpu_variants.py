@@ -1,0 +1,104 @@
+"""GPU parity of the score-aggregation variants (kvsel_accumulate_ex,
+kvsel_block_aggregate_ex, kvsel_select_threshold) against the float64
+oracle: scores within 1e-4 relative (1e-6 for exact order statistics),
+fractions, flags and index sets exact except decisions on values within
+1e-6 of the threshold."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests.parity_util import f64, max_rel, note
+
+pytestmark = pytest.mark.gpu
+
+
+def _K():
+    import attention_score_guided_amd as K
+    return K
+
+
+def _probs(g, B, Hq, stride, lengths):
+    p = torch.rand((B, Hq, stride), generator=g)
+    for b, L in enumerate(lengths):
+        p[b, :, :L] /= p[b, :, :L].sum(dim=1, keepdim=True)
+        p[b, :, L:] = 0.5          # past the row: must be ignored
+    return p
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_accumulate_max_and_window_over_steps(G):
+    K = _K()
+    g = synth.generator(91 + G)
+    Hkv, lengths, steps, W = 2, [700, 33, 1], 7, 3
+    B, Hq, stride = len(lengths), Hkv * G, 704
+    lens = torch.tensor(lengths, dtype=torch.int32).cuda()
+    cum_max = torch.zeros((B, Hkv, stride), device="cuda")
+    cum_win = torch.full((B, Hkv, stride), -2.0, device="cuda")
+    ring = torch.zeros((W, B, Hkv, stride), device="cuda")
+    o_max = [np.zeros((Hkv, L)) for L in lengths]
+    hist = [[] for _ in lengths]
+    for t in range(steps):
+        p = _probs(g, B, Hq, stride, lengths)
+        pc = p.cuda()
+        K.accumulate_ex(pc, lens, Hkv, max(lengths), cum_max, K.ACC_MAX, decay=0.9)
+        K.accumulate_ex(pc, lens, Hkv, max(lengths), cum_win, K.ACC_WINDOW_MEAN, window=W, step=t, ring=ring)
+        torch.cuda.synchronize()
+        for b, L in enumerate(lengths):
+            pb = p[b, :, :L].double().numpy()
+            o_max[b] = O.accumulate_max(o_max[b], pb, 0.9)
+            o_win = O.accumulate_window(hist[b], pb, Hkv, W)
+            assert max_rel(f64(cum_max[b, :, :L]), o_max[b]) < 1e-5
+            assert max_rel(f64(cum_win[b, :, :L]), o_win) < 1e-5
+            assert (cum_win[b, :, L:] == -2.0).all()
+
+
+@pytest.mark.parametrize("bs,param", [(16, 0.25), (64, 0.1), (256, 0.5), (5, 1.0)])
+def test_block_variants(bs, param):
+    K = _K()
+    note(f"block variants bs={bs} p={param}")
+    g = synth.generator(95 + bs)
+    lengths, H = [1000, 77, 3], 3
+    B, stride = len(lengths), 1003
+    sc = torch.rand((B, H, stride), generator=g)
+    sc[0, 0, :64] = 0.5                                   # ties inside blocks
+    lens = torch.tensor(lengths, dtype=torch.int32).cuda()
+    n_blk = -(-max(lengths) // bs)
+    scd = sc.cuda()
+    outs = {}
+    for mode, prm in [(K.BLOCK_TOP_P_MEAN, param), (K.BLOCK_FRAC_ABOVE, 0.6), (K.BLOCK_ALL_COLD, 0.97)]:
+        out = torch.full((B, H, n_blk + 2), -1.0, device="cuda")
+        K.block_aggregate_ex(scd, lens, max(lengths), bs, mode, prm, out)
+        outs[mode] = out
+    torch.cuda.synchronize()
+    for b, L in enumerate(lengths):
+        nb = -(-L // bs)
+        for h in range(H):
+            row = sc[b, h].double().numpy()
+            assert max_rel(f64(outs[K.BLOCK_TOP_P_MEAN][b, h, :nb]), O.block_top_p_mean(row, L, bs, param)) < 1e-6
+            assert np.array_equal(f64(outs[K.BLOCK_FRAC_ABOVE][b, h, :nb]),
+                                  O.block_fraction_above(row.astype(np.float32), L, bs, np.float32(0.6)).astype(np.float32))
+            assert np.array_equal(f64(outs[K.BLOCK_ALL_COLD][b, h, :nb]),
+                                  O.block_all_cold(row.astype(np.float32), L, bs, np.float32(0.97)))
+            for m in outs:
+                assert (outs[m][b, h, nb:] == -1.0).all()
+
+
+def test_select_threshold_rows():
+    K = _K()
+    g = synth.generator(99)
+    lengths = [5000, 1, 256, 257, 0 + 3]
+    rows, stride = len(lengths), 5004
+    sc = torch.rand((rows, stride), generator=g)
+    sc[2] = 0.7                                           # every position exactly at the threshold
+    lens = torch.tensor(lengths, dtype=torch.int32).cuda()
+    idx = torch.full((rows, stride), -5, dtype=torch.int32, device="cuda")
+    cnt = torch.empty((rows,), dtype=torch.int32, device="cuda")
+    K.select_threshold(sc.cuda(), lens, max(lengths), 0.7, idx, cnt)
+    torch.cuda.synchronize()
+    for r, L in enumerate(lengths):
+        want = O.select_threshold(sc[r].numpy(), L, np.float32(0.7))
+        n = int(cnt[r])
+        assert idx[r, :n].cpu().numpy().tolist() == want.tolist()
+        assert (idx[r, n:] == -5).all()

@@ -484,6 +484,36 @@ def test_h2o_evict_invariants_with_heavy_hitters():
         assert all(abs(p.sum() - 1) < 1e-12 for p in probs)
 
 
+def test_accumulate_max_and_window_closed_forms():
+    probs = rng.uniform(size=(6, 4, 9))              # 6 steps, 4 query heads, 9 keys
+    probs /= probs.sum(axis=2, keepdims=True)
+    cum_max = np.zeros((2, 9))
+    hist = []
+    for t in range(6):
+        cum_max = O.accumulate_max(cum_max, probs[t])
+        win = O.accumulate_window(hist, probs[t], 2, 3)
+        g = probs[:t + 1].reshape(t + 1, 2, 2, 9).sum(axis=2)     # group sums so far
+        np.testing.assert_allclose(cum_max, g.max(axis=0), rtol=1e-15)
+        np.testing.assert_allclose(win, g[-3:].sum(axis=0) / 3, rtol=1e-14)
+    # decay 0 keeps only the current step; window 1 is the current step too
+    np.testing.assert_allclose(O.accumulate_max(np.full((2, 9), 5.0), probs[0], 0.0),
+                               probs[0].reshape(2, 2, 9).sum(axis=1), rtol=1e-15)
+
+
+def test_block_variants_limits_and_hand_values():
+    sc = np.array([0.1, 0.9, 0.3, 0.3, 0.2, 0.0, 0.7])
+    # top-p mean: p -> 0 is the block max, p = 1 the block mean
+    mx, mean = O.block_aggregate(sc[None, :], 7, 3)
+    np.testing.assert_allclose(O.block_top_p_mean(sc, 7, 3, 1e-9), mx[0], rtol=1e-15)
+    np.testing.assert_allclose(O.block_top_p_mean(sc, 7, 3, 1.0), mean[0], rtol=1e-15)
+    assert O.block_top_p_mean(sc, 7, 3, 0.5).tolist() == pytest.approx([0.6, 0.25, 0.7])   # top 2 of 3
+    assert O.block_fraction_above(sc, 7, 3, 0.3).tolist() == pytest.approx([2 / 3, 1 / 3, 1.0])
+    assert O.block_all_cold(sc, 7, 3, 0.3).tolist() == [0.0, 0.0, 0.0]
+    assert O.block_all_cold(sc, 7, 3, 0.35).tolist() == [0.0, 1.0, 0.0]
+    assert O.select_threshold(sc, 7, 0.3).tolist() == [1, 2, 3, 6]
+    assert O.select_threshold(sc, 5, 2.0).tolist() == []
+
+
 # ------------------------------------------------------------ chunk attention
 def test_chunk_causal_attention_rows():
     Hq, Hkv, S, n, d = 4, 2, 10, 5, 8
