@@ -8,6 +8,7 @@
 // Token -> block ([OFFLOAD] §3.1 top-p%; [EVICT] §5.1 ranking blocks by their
 // share of important tokens, and evicting only all-cold blocks):
 //   block_variant_kernel      top-p% mean | fraction >= threshold | all-cold flag
+//   (block_variant_lanes: the same for power-of-two blocks of 4..64, one lane per position)
 // Across requests ([OFFLOAD] §3.2, absolute-threshold normalisation):
 //   select_threshold_kernel   positions with score >= threshold, ascending
 // All are HBM-bound streaming passes with one writer per output element.
@@ -113,6 +114,44 @@ __global__ __launch_bounds__(kThreads) void block_variant_kernel(
   if (lane == 0) out[((size_t)b * num_heads + h) * out_stride + blk] = res;
 }
 
+// Power-of-two blocks of BS <= 64 positions: BS consecutive lanes hold one
+// block, one position each (consecutive lanes read consecutive positions);
+// the rank of a score counts the lanes of its block that beat it, by
+// shuffles; the sums are group reductions.
+template <int BS>
+__global__ __launch_bounds__(kThreads) void block_variant_lanes(
+    const float* __restrict__ scores, int64_t score_stride, const int32_t* __restrict__ seq_lens, int num_heads,
+    int mode, float param, float* __restrict__ out, int64_t out_stride) {
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int L = seq_lens[b];
+  const int lane = threadIdx.x % kWave;
+  const int blk = blockIdx.x * (kThreads / BS) + threadIdx.x / BS;
+  const int i = threadIdx.x % BS;
+  const int start = blk * BS;
+  if (blockIdx.x * (kThreads / BS) * BS >= L) return;   // the whole workgroup lies past the row
+  const int n = start < L ? min(BS, L - start) : 0;
+  const float* row = scores + ((size_t)b * num_heads + h) * score_stride;
+  const float x = i < n ? row[start + i] : 0.f;
+  float part;
+  if (mode == 0) {
+    const int m = max(1, min(n, (int)ceilf(param * (float)n)));
+    int beat = 0;
+    const int g0 = lane & ~(BS - 1);
+#pragma unroll
+    for (int t = 0; t < BS; ++t) {
+      const float y = __shfl(x, g0 + t, kWave);
+      beat += (t < n && (y > x || (y == x && t < i))) ? 1 : 0;
+    }
+    part = (i < n && beat < m) ? x : 0.f;
+    part = group_sum<BS>(part) / (float)max(m, 1);
+  } else {
+    part = (i < n && x >= param) ? 1.f : 0.f;
+    part = group_sum<BS>(part);                 // exact: small integers
+    part = mode == 1 ? part / (float)max(n, 1) : (part == 0.f ? 1.f : 0.f);
+  }
+  if (i == 0 && n > 0) out[((size_t)b * num_heads + h) * out_stride + blk] = part;
+}
+
 // One workgroup per row: the positions with score >= threshold, ascending,
 // by a block-wide scan over chunks of kThreads positions.
 __global__ __launch_bounds__(kThreads) void select_threshold_kernel(
@@ -173,6 +212,21 @@ hipError_t launch_block_variant(const float* scores, int64_t score_stride, const
                                 int num_heads, int max_seq_len, int block_size, int mode, float param, float* out,
                                 int64_t out_stride, hipStream_t stream) {
   const int n_blk = (max_seq_len + block_size - 1) / block_size;
+#define KVSEL_LANES(BS)                                                                                        \
+  case BS:                                                                                                     \
+    hipLaunchKernelGGL(block_variant_lanes<BS>, dim3((n_blk + kThreads / BS - 1) / (kThreads / BS), num_heads,  \
+                       num_seqs), dim3(kThreads), 0, stream, scores, score_stride, seq_lens, num_heads, mode,   \
+                       param, out, out_stride);                                                                \
+    return hipGetLastError();
+  switch (block_size) {
+    KVSEL_LANES(4)
+    KVSEL_LANES(8)
+    KVSEL_LANES(16)
+    KVSEL_LANES(32)
+    KVSEL_LANES(64)
+    default: break;
+  }
+#undef KVSEL_LANES
   const dim3 grid((n_blk + kVarWaves - 1) / kVarWaves, num_heads, num_seqs);
   hipLaunchKernelGGL(block_variant_kernel, grid, dim3(kThreads), 0, stream, scores, score_stride, seq_lens, num_heads,
                      block_size, mode, param, out, out_stride);

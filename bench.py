@@ -409,6 +409,41 @@ def llama3_workload(torch, K, synth, args) -> dict:
     torch.cuda.synchronize()
     t_dec = a.elapsed_time(b) / steps
     t_sel = b.elapsed_time(c)
+    # the aggregation variants on the same rows: one step's probabilities
+    # (emitted by one more decode call) folded by max pooling and by a
+    # 16-step window mean; block top-p% mean, fraction above and all-cold flag
+    # of the block-16 scores; absolute-threshold selection of those blocks
+    final_kv = K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, final, 16, cap)
+    probs = torch.empty((Bq, HQq, stride), device="cuda")
+    K.decode_attn_scores(final_kv, cfg["q_steps"][steps - 1], HQq, cfg["scale"], out, None, probs, K.EMIT_PROBS,
+                         None, 1.0, workspace=torch.empty(K.decode_workspace_bytes(final_kv, HQq, True),
+                                                          dtype=torch.uint8, device="cuda"))
+    cum_v = cum.clone()
+    ring = torch.zeros((16, Bq, HKVq, stride), device="cuda")
+    t_max = timed(torch, lambda: K.accumulate_ex(probs, final, HKVq, cap, cum_v, K.ACC_MAX, decay=0.99), 10)
+    t_win = timed(torch, lambda: K.accumulate_ex(probs, final, HKVq, cap, cum_v, K.ACC_WINDOW_MEAN, window=16,
+                                                 step=3, ring=ring), 10)
+    blk_out = torch.empty((Bq, HKVq, n_blk), device="cuda")
+    t_topp = timed(torch, lambda: K.block_aggregate_ex(cum, final, cap, 16, K.BLOCK_TOP_P_MEAN, 0.25, blk_out), 10)
+    t_frac = timed(torch, lambda: K.block_aggregate_ex(cum, final, cap, 16, K.BLOCK_FRAC_ABOVE, 0.01, blk_out), 10)
+    blens = ((final + 15) // 16).repeat_interleave(HKVq).to(torch.int32)
+    bidx = torch.empty((Bq * HKVq, n_blk), dtype=torch.int32, device="cuda")
+    bcnt = torch.empty((Bq * HKVq,), dtype=torch.int32, device="cuda")
+    t_thr = timed(torch, lambda: K.select_threshold(blk_out.view(Bq * HKVq, n_blk), blens, n_blk, 0.5, bidx, bcnt),
+                  10)
+    tok = float(final.sum()) * HKVq
+    variants = {
+        "acc_max_us": round(t_max * 1e3, 1),
+        "acc_max_gb_per_s": round(tok * (4 * HQq // HKVq + 8) / (t_max * 1e-3) / 1e9, 1),
+        "acc_window16_us": round(t_win * 1e3, 1),
+        "acc_window16_gb_per_s": round(tok * (4 * HQq // HKVq + 4 + 16 * 4 + 4) / (t_win * 1e-3) / 1e9, 1),
+        "block16_top25pct_mean_us": round(t_topp * 1e3, 1),
+        "block16_frac_above_us": round(t_frac * 1e3, 1),
+        "block16_frac_above_gb_per_s": round(tok * 4 / (t_frac * 1e-3) / 1e9, 1),
+        "select_threshold_blocks_us": round(t_thr * 1e3, 1),
+    }
+    del probs, ring, cum_v
+
     # keys read per step, averaged over the steps (each step appends one token)
     mean_keys = sum(int(L) for L in base.tolist()) + Bq * (steps + 1) / 2.0
     kv_bytes = mean_keys * HKVq * 128 * 2 * 2
@@ -423,6 +458,7 @@ def llama3_workload(torch, K, synth, args) -> dict:
         "decode_us_per_step": round(t_dec * 1e3, 1),
         "aggregate_and_select_us": round(t_sel * 1e3, 1),
         "prob_mass_per_seq": round(mass, 3),
+        "aggregation_variants": variants,
     }
 
 

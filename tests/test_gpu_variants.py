@@ -1,6 +1,6 @@
 """GPU parity of the score-aggregation variants (kvsel_accumulate_ex,
 kvsel_block_aggregate_ex, kvsel_select_threshold) against the float64
-oracle: scores within 1e-4 relative (1e-6 for exact order statistics),
+oracle: scores within 1e-5 relative (block top-p% means: tree sums),
 fractions, flags and index sets exact except decisions on values within
 1e-6 of the threshold."""
 import numpy as np
@@ -54,7 +54,7 @@ def test_accumulate_max_and_window_over_steps(G):
             assert (cum_win[b, :, L:] == -2.0).all()
 
 
-@pytest.mark.parametrize("bs,param", [(16, 0.25), (64, 0.1), (256, 0.5), (5, 1.0)])
+@pytest.mark.parametrize("bs,param", [(16, 0.25), (4, 0.5), (32, 0.1), (64, 0.1), (256, 0.5), (5, 1.0)])
 def test_block_variants(bs, param):
     K = _K()
     note(f"block variants bs={bs} p={param}")
@@ -76,7 +76,7 @@ def test_block_variants(bs, param):
         nb = -(-L // bs)
         for h in range(H):
             row = sc[b, h].double().numpy()
-            assert max_rel(f64(outs[K.BLOCK_TOP_P_MEAN][b, h, :nb]), O.block_top_p_mean(row, L, bs, param)) < 1e-6
+            assert max_rel(f64(outs[K.BLOCK_TOP_P_MEAN][b, h, :nb]), O.block_top_p_mean(row, L, bs, param)) < 1e-5
             assert np.array_equal(f64(outs[K.BLOCK_FRAC_ABOVE][b, h, :nb]),
                                   O.block_fraction_above(row.astype(np.float32), L, bs, np.float32(0.6)).astype(np.float32))
             assert np.array_equal(f64(outs[K.BLOCK_ALL_COLD][b, h, :nb]),
