@@ -35,7 +35,7 @@ EXPORTED = (
     "kvsel_snapkv_vote", "kvsel_snapkv_workspace_bytes", "kvsel_sparse_attn",
     "kvsel_sparse_workspace_bytes", "kvsel_quest_summarize", "kvsel_quest_select",
     "kvsel_quest_workspace_bytes", "kvsel_accumulate_ex", "kvsel_block_aggregate_ex", "kvsel_select_threshold",
-    "kvsel_h2o_step", "kvsel_h2o_workspace_bytes", "kvsel_set_sync_spin_limit",
+    "kvsel_union_keep", "kvsel_h2o_step", "kvsel_h2o_workspace_bytes", "kvsel_set_sync_spin_limit",
     "kvsel_status_string", "kvsel_last_error",
 )
 
@@ -85,6 +85,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvsel_accumulate_ex": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, I32, F, I32, I32, P, P, I64, P]),
         "kvsel_block_aggregate_ex": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, I32, F, P, I64, P]),
         "kvsel_select_threshold": (ctypes.c_int, [P, I64, P, I32, I32, F, P, I64, P, P]),
+        "kvsel_union_keep": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, P, I64, P, P]),
         "kvsel_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "kvsel_set_sync_spin_limit": (I32, [I32]),
         "kvsel_last_error": (ctypes.c_char_p, []),
@@ -382,3 +383,13 @@ def select_threshold(scores: torch.Tensor, lengths: torch.Tensor, max_len: int, 
         _ptr(scores, torch.float32, "scores"), scores.shape[-1], _ptr(lengths, torch.int32, "lengths"),
         scores.shape[0], max_len, float(threshold), _ptr(out_idx, torch.int32, "out_idx"), out_idx.shape[-1],
         _ptr(out_count, torch.int32, "out_count"), _stream(stream)))
+
+
+def union_keep(idx: torch.Tensor, counts: torch.Tensor, num_kv_heads: int, max_len: int, out: torch.Tensor,
+               out_count: torch.Tensor, stream=None) -> None:
+    """kvsel_union_keep: idx ``[B][H_q][stride]``, counts ``[B][H_q]`` -> out ``[B][H_kv][out_stride]``."""
+    B, Hq, _ = idx.shape
+    _check(_LIB.kvsel_union_keep(
+        _ptr(idx, torch.int32, "idx"), idx.shape[-1], _ptr(counts, torch.int32, "counts"), B, Hq, num_kv_heads,
+        max_len, _ptr(out, torch.int32, "out"), out.shape[-1], _ptr(out_count, torch.int32, "out_count"),
+        _stream(stream)))

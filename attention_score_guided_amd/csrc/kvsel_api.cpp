@@ -464,6 +464,24 @@ int kvsel_select_threshold(const float* scores, int64_t stride, const int32_t* l
                     "select_threshold launch");
 }
 
+int kvsel_union_keep(const int32_t* idx, int64_t idx_stride, const int32_t* counts, int32_t num_seqs,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t max_len, int32_t* out, int64_t out_stride,
+                     int32_t* out_count, void* stream) {
+  if (!idx || !counts || !out || !out_count) return fail(KVSEL_ERR_INVALID, "NULL pointer argument");
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_len <= 0 || idx_stride <= 0)
+    return fail(KVSEL_ERR_INVALID, "dimensions must be positive");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(KVSEL_ERR_INVALID, "num_q_heads is not a multiple of num_kv_heads");
+  const long long need = std::min<long long>(max_len, (long long)(num_q_heads / num_kv_heads) * idx_stride);
+  if (out_stride < need) return fail(KVSEL_ERR_INVALID, "out_stride %lld < %lld", (long long)out_stride, need);
+  if (max_len > (1 << 20)) return fail(KVSEL_ERR_UNSUPPORTED, "max_len %d > 2^20", max_len);
+  int st = check_device();
+  if (st != KVSEL_OK) return st;
+  return hip_status(kvsel::launch_union_keep(idx, idx_stride, counts, num_seqs, num_q_heads, num_kv_heads, max_len,
+                                             out, out_stride, out_count, static_cast<hipStream_t>(stream)),
+                    "union_keep launch");
+}
+
 int kvsel_quest_summarize(const kvsel_paged_kv* kv, int32_t first_page, void* summary, void* stream) {
   int st = check_kv(kv, kv ? kv->num_kv_heads : 1, false);
   if (st != KVSEL_OK) return st;

@@ -71,6 +71,10 @@ hipError_t launch_select_threshold(const float* scores, int64_t stride, const in
                                    float threshold, int32_t* out_idx, int64_t out_stride, int32_t* out_count,
                                    hipStream_t stream);
 
+hipError_t launch_union_keep(const int32_t* idx, int64_t idx_stride, const int32_t* counts, int num_seqs,
+                             int num_q_heads, int num_kv_heads, int max_len, int32_t* out, int64_t out_stride,
+                             int32_t* out_count, hipStream_t stream);
+
 size_t select_workspace_bytes(int rows, int max_len, int mode);
 
 hipError_t launch_select(const float* scores, int64_t stride, const int32_t* lengths, int rows,

@@ -330,6 +330,22 @@ int kvsel_select_threshold(const float* scores, int64_t stride, const int32_t* l
                            int32_t* out_count, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Union of a GQA group's index sets ([EVICT] §4.3, SnapKV under GQA: each
+ * query head picks its own positions, the KV head keeps the union).
+ *   idx     [num_seqs][num_q_heads][idx_stride] i32 positions (entries < 0 or
+ *           >= max_len are ignored; only the first counts[b][h] are read)
+ *   counts  [num_seqs][num_q_heads] i32
+ *   out     [num_seqs][num_kv_heads][out_stride] i32: the union, ascending,
+ *           without repeats; out_count [num_seqs][num_kv_heads].
+ *   out_stride >= min(max_len, G * idx_stride); max_len <= 2^20.
+ * Errors: INVALID (NULL pointers, bad dims or strides), UNSUPPORTED
+ * (max_len > 2^20), HIP.
+ * ------------------------------------------------------------------------ */
+int kvsel_union_keep(const int32_t* idx, int64_t idx_stride, const int32_t* counts, int32_t num_seqs,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t max_len, int32_t* out,
+                     int64_t out_stride, int32_t* out_count, void* stream);
+
+/* ------------------------------------------------------------------------
  * Quest page summaries ([LONGCTX] sparse-attention experiment, the Quest
  * strategy: the per-channel minimum and maximum of a page's keys).
  * For every whole page p of every sequence with p >= first_page (pages with

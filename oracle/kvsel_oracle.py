@@ -51,6 +51,7 @@ __all__ = [
     "max_pool_1d",
     "snapkv_vote",
     "snapkv_keep",
+    "union_keep",
     "indexer_scores",
     "sparse_attention",
     "h2o_evict_step",
@@ -379,6 +380,15 @@ def snapkv_keep(pooled_vote: np.ndarray, L: int, W: int, k: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 # O7: lightweight indexer score
 # --------------------------------------------------------------------------
+def union_keep(index_sets) -> np.ndarray:
+    """Positions kept for a KV head under GQA: the union of its query heads'
+    picks ([EVICT] §4.3, SnapKV's GQA note), ascending, negatives ignored."""
+    kept = set()
+    for s in index_sets:
+        kept |= {int(j) for j in s if j >= 0}
+    return np.array(sorted(kept), dtype=np.int64)
+
+
 def indexer_scores(q_idx: np.ndarray, K_idx: np.ndarray) -> np.ndarray:
     """Dot-product indexer: score_hj = q_h . k_j over a single indexer key
     head ([LONGCTX] sparse attention: a cheap scorer ranks every past token and

@@ -253,3 +253,12 @@ def test_variant_validation():
     assert thr(FAKE, 100, FAKE, 4, 100, 0.5, None, 100, FAKE, None) == K.KVSEL_ERR_INVALID
     assert thr(FAKE, 100, FAKE, 4, 100, 0.5, FAKE, 99, FAKE, None) == K.KVSEL_ERR_INVALID
     assert thr(FAKE, 100, FAKE, 0, 100, 0.5, FAKE, 100, FAKE, None) == K.KVSEL_ERR_INVALID
+
+
+def test_union_validation():
+    lib = K.library()
+    u = lib.kvsel_union_keep
+    assert u(None, 8, FAKE, 1, 4, 2, 100, FAKE, 16, FAKE, None) == K.KVSEL_ERR_INVALID
+    assert u(FAKE, 8, FAKE, 1, 6, 4, 100, FAKE, 16, FAKE, None) == K.KVSEL_ERR_INVALID    # 6 % 4
+    assert u(FAKE, 8, FAKE, 1, 4, 2, 100, FAKE, 15, FAKE, None) == K.KVSEL_ERR_INVALID    # 2 x 8 = 16 slots
+    assert u(FAKE, 8, FAKE, 1, 4, 2, (1 << 20) + 1, FAKE, 16, FAKE, None) == K.KVSEL_ERR_UNSUPPORTED

@@ -514,6 +514,13 @@ def test_block_variants_limits_and_hand_values():
     assert O.select_threshold(sc, 5, 2.0).tolist() == []
 
 
+def test_union_keep_hand_example_and_library_union():
+    assert O.union_keep([[3, 1, -1], [1, 7], []]).tolist() == [1, 3, 7]
+    sets = [rng.integers(-3, 50, size=int(n)) for n in rng.integers(0, 30, size=5)]
+    want = np.unique(np.concatenate([s[s >= 0] for s in sets] + [np.array([], dtype=np.int64)]))
+    assert O.union_keep(sets).tolist() == want.tolist()
+
+
 # ------------------------------------------------------------ chunk attention
 def test_chunk_causal_attention_rows():
     Hq, Hkv, S, n, d = 4, 2, 10, 5, 8
