@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvsel.so")
 
 KVSEL_OK, KVSEL_ERR_INVALID, KVSEL_ERR_UNSUPPORTED, KVSEL_ERR_WORKSPACE, KVSEL_ERR_HIP = 0, -1, -2, -3, -4
-KVSEL_F32, KVSEL_BF16 = 0, 1
+KVSEL_F32, KVSEL_BF16, KVSEL_FP8_E4M3 = 0, 1, 2
 EMIT_PROBS, EMIT_LOGITS = 0, 1
 REDUCE_NONE, REDUCE_SUM = 0, 1
 SELECT_ROWS, SELECT_GLOBAL_PERCENTILE = 0, 1
@@ -35,7 +35,7 @@ EXPORTED = (
     "kvsel_snapkv_vote", "kvsel_snapkv_workspace_bytes", "kvsel_sparse_attn",
     "kvsel_sparse_workspace_bytes", "kvsel_quest_summarize", "kvsel_quest_select",
     "kvsel_quest_workspace_bytes", "kvsel_accumulate_ex", "kvsel_block_aggregate_ex", "kvsel_select_threshold",
-    "kvsel_union_keep", "kvsel_h2o_step", "kvsel_h2o_workspace_bytes", "kvsel_set_sync_spin_limit",
+    "kvsel_union_keep", "kvsel_indexer_scores_fp8", "kvsel_h2o_step", "kvsel_h2o_workspace_bytes", "kvsel_set_sync_spin_limit",
     "kvsel_status_string", "kvsel_last_error",
 )
 
@@ -86,6 +86,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvsel_block_aggregate_ex": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, I32, F, P, I64, P]),
         "kvsel_select_threshold": (ctypes.c_int, [P, I64, P, I32, I32, F, P, I64, P, P]),
         "kvsel_union_keep": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, P, I64, P, P]),
+        "kvsel_indexer_scores_fp8": (ctypes.c_int, [D, P, I32, F, P, I64, P]),
         "kvsel_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "kvsel_set_sync_spin_limit": (I32, [I32]),
         "kvsel_last_error": (ctypes.c_char_p, []),
@@ -135,6 +136,8 @@ def _dtype_code(t: torch.Tensor) -> int:
         return KVSEL_BF16
     if t.dtype == torch.float32:
         return KVSEL_F32
+    if t.dtype == torch.float8_e4m3fn:
+        return KVSEL_FP8_E4M3
     raise TypeError(f"KV dtype must be bfloat16 or float32, got {t.dtype}")
 
 
@@ -393,3 +396,12 @@ def union_keep(idx: torch.Tensor, counts: torch.Tensor, num_kv_heads: int, max_l
         _ptr(idx, torch.int32, "idx"), idx.shape[-1], _ptr(counts, torch.int32, "counts"), B, Hq, num_kv_heads,
         max_len, _ptr(out, torch.int32, "out"), out.shape[-1], _ptr(out_count, torch.int32, "out_count"),
         _stream(stream)))
+
+
+def indexer_scores_fp8(kv: PagedKV, q: torch.Tensor, num_q_heads: int, scale: float, scores: torch.Tensor,
+                       stream=None) -> None:
+    """kvsel_indexer_scores_fp8: kv pages and q in torch.float8_e4m3fn; scores ``[B][H_q][stride]``."""
+    if q.dtype != torch.float8_e4m3fn or kv.dtype != torch.float8_e4m3fn:
+        raise TypeError("the FP8 indexer takes float8_e4m3fn pages and queries")
+    _check(_LIB.kvsel_indexer_scores_fp8(kv.ref(), _ptr(q, None, "q"), num_q_heads, float(scale),
+                                         _ptr(scores, torch.float32, "scores"), scores.shape[-1], _stream(stream)))

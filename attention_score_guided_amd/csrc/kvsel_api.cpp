@@ -482,6 +482,27 @@ int kvsel_union_keep(const int32_t* idx, int64_t idx_stride, const int32_t* coun
                     "union_keep launch");
 }
 
+int kvsel_indexer_scores_fp8(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads, float scale,
+                             float* scores, int64_t stride, void* stream) {
+  if (!kv) return fail(KVSEL_ERR_INVALID, "kv descriptor is NULL");
+  if (kv->dtype != KVSEL_FP8_E4M3) return fail(KVSEL_ERR_INVALID, "dtype %d: the FP8 indexer needs FP8_E4M3", kv->dtype);
+  kvsel_paged_kv shape = *kv;
+  shape.dtype = KVSEL_BF16;   // the shape checks of the other calls
+  int st = check_kv(&shape, num_q_heads, false);
+  if (st != KVSEL_OK) return st;
+  if (!q || !scores) return fail(KVSEL_ERR_INVALID, "NULL pointer argument");
+  if (stride < kv->max_seq_len) return fail(KVSEL_ERR_INVALID, "stride < max_seq_len");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv->k_pages)) & 15)
+    return fail(KVSEL_ERR_INVALID, "q and k_pages must be 16-byte aligned");
+  st = check_device();
+  if (st != KVSEL_OK) return st;
+  return hip_status(kvsel::launch_indexer_fp8(kv->k_pages, kv->block_table, kv->seq_lens, q, kv->num_seqs,
+                                              kv->num_kv_heads, num_q_heads, kv->head_dim, kv->page_size,
+                                              kv->max_pages_per_seq, kv->max_seq_len, scale, scores, stride,
+                                              static_cast<hipStream_t>(stream)),
+                    "indexer_scores_fp8 launch");
+}
+
 int kvsel_quest_summarize(const kvsel_paged_kv* kv, int32_t first_page, void* summary, void* stream) {
   int st = check_kv(kv, kv ? kv->num_kv_heads : 1, false);
   if (st != KVSEL_OK) return st;

@@ -75,6 +75,11 @@ hipError_t launch_union_keep(const int32_t* idx, int64_t idx_stride, const int32
                              int num_q_heads, int num_kv_heads, int max_len, int32_t* out, int64_t out_stride,
                              int32_t* out_count, hipStream_t stream);
 
+hipError_t launch_indexer_fp8(const void* k_pages, const int32_t* block_table, const int32_t* seq_lens,
+                              const void* q, int num_seqs, int num_kv_heads, int num_q_heads, int head_dim,
+                              int page_size, int max_pages, int max_seq_len, float scale, float* scores,
+                              int64_t stride, hipStream_t stream);
+
 size_t select_workspace_bytes(int rows, int max_len, int mode);
 
 hipError_t launch_select(const float* scores, int64_t stride, const int32_t* lengths, int rows,

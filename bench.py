@@ -290,6 +290,15 @@ def long_context_workload(torch, K, synth, args) -> dict:
     t_sparse = a.elapsed_time(b) / steps
     sparse_bytes = (Bq * Lq * 64 * 2) + 2 * Bq * HQq * Lq * 4 + Bq * HQq * 2048 * 128 * 2 * 2
 
+    # the same indexer with its keys and queries stored as FP8 E4M3
+    kv_i8 = K.PagedKV(kit.k_pages.to(torch.float8_e4m3fn), None, kit.block_table, kv_i_s[0].seq_lens, 16, cap)
+    qi8 = cfg["qi_dec"][0].to(torch.float8_e4m3fn)
+    t_ix8 = timed(torch, lambda: K.indexer_scores_fp8(kv_i8, qi8, HQq, 1.0, scores), 10)
+    t_ix16 = timed(torch, lambda: K.decode_attn_scores(kv_i_s[0], cfg["qi_dec"][0], HQq, 1.0, None, None, scores,
+                                                       K.EMIT_LOGITS, workspace=ws_d), 10)
+    ix_scores_bytes = Bq * HQq * (Lq + 1) * 4
+    del kv_i8
+
     # Quest over the same cache: page summaries at prefill, then sparse decode
     # steps whose index sets are the top-128 pages (2048 keys) by page bound;
     # each step refreshes the summary of the last whole page (the page that
@@ -345,6 +354,10 @@ def long_context_workload(torch, K, synth, args) -> dict:
         "sparse_step": {"us": round(t_sparse * 1e3, 1),
                         "gb_per_s": round(sparse_bytes / (t_sparse * 1e-3) / 1e9, 1),
                         "bytes": sparse_bytes},
+        "indexer": {"bf16_us": round(t_ix16 * 1e3, 1),
+                    "bf16_gb_per_s": round((Bq * (Lq + 1) * 64 * 2 + ix_scores_bytes) / (t_ix16 * 1e-3) / 1e9, 1),
+                    "fp8_us": round(t_ix8 * 1e3, 1),
+                    "fp8_gb_per_s": round((Bq * (Lq + 1) * 64 + ix_scores_bytes) / (t_ix8 * 1e-3) / 1e9, 1)},
         "quest": {"summarize_prefill_us": round(t_qsum * 1e3, 1),
                   "summarize_k_gb_per_s": round(k_bytes / (t_qsum * 1e-3) / 1e9, 1),
                   "select_us": round(t_qsel * 1e3, 1),

@@ -57,7 +57,7 @@ typedef enum {
   KVSEL_ERR_HIP = -4          /* a HIP runtime call or launch failed         */
 } kvsel_status;
 
-typedef enum { KVSEL_F32 = 0, KVSEL_BF16 = 1 } kvsel_dtype;
+typedef enum { KVSEL_F32 = 0, KVSEL_BF16 = 1, KVSEL_FP8_E4M3 = 2 /* kvsel_indexer_scores_fp8 only */ } kvsel_dtype;
 typedef enum { KVSEL_EMIT_PROBS = 0, KVSEL_EMIT_LOGITS = 1 } kvsel_emit;
 typedef enum { KVSEL_REDUCE_NONE = 0, KVSEL_REDUCE_SUM = 1 } kvsel_reduce;
 typedef enum { KVSEL_SELECT_ROWS = 0, KVSEL_SELECT_GLOBAL_PERCENTILE = 1 } kvsel_select_mode;
@@ -344,6 +344,22 @@ int kvsel_select_threshold(const float* scores, int64_t stride, const int32_t* l
 int kvsel_union_keep(const int32_t* idx, int64_t idx_stride, const int32_t* counts, int32_t num_seqs,
                      int32_t num_q_heads, int32_t num_kv_heads, int32_t max_len, int32_t* out,
                      int64_t out_stride, int32_t* out_count, void* stream);
+
+/* ------------------------------------------------------------------------
+ * FP8 indexer scores ([LONGCTX] sparse-attention section: a lightweight
+ * indexer with few heads scores every token in FP8; the top 2048 per query
+ * feed the sparse attention).  kv->dtype must be KVSEL_FP8_E4M3 (OCP E4M3:
+ * 1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, the
+ * all-ones code NaN, max 448); kv->v_pages is not read.
+ *   q       [num_seqs][num_q_heads][head_dim] E4M3, 16-byte aligned
+ *   scores  [num_seqs][num_q_heads][stride] f32: scale * q . k_j for j < L_b
+ *           (query head h reads indexer head h / G), products accumulated in
+ *           fp32; entries j >= L_b are left untouched.  stride >= max_seq_len.
+ * Errors: INVALID (NULL pointers, stride, dtype not FP8_E4M3, unaligned q or
+ * pages), UNSUPPORTED (as the descriptor checks), HIP.
+ * ------------------------------------------------------------------------ */
+int kvsel_indexer_scores_fp8(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads, float scale,
+                             float* scores, int64_t stride, void* stream);
 
 /* ------------------------------------------------------------------------
  * Quest page summaries ([LONGCTX] sparse-attention experiment, the Quest

@@ -33,6 +33,7 @@ import numpy as np
 
 __all__ = [
     "bf16_bits_to_f64",
+    "fp8_e4m3_bits_to_f64",
     "gather_paged",
     "decode_attention",
     "accumulate",
@@ -78,6 +79,20 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
     return b.view(np.float32).astype(np.float64)
+
+
+def fp8_e4m3_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Widen FP8 E4M3 codes (uint8, OCP layout: sign, 4 exponent bits with
+    bias 7, 3 mantissa bits; exponent 0 is subnormal, the all-ones
+    exponent-and-mantissa code is NaN, there are no infinities) to float64."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 0x7).astype(np.float64)
+    normal = sign * np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64))
+    sub = sign * np.ldexp(m / 8.0, -6)
+    out = np.where(e == 0, sub, normal)
+    return np.where((e == 0xF) & ((b & 0x7) == 0x7), np.nan, out)
 
 
 def gather_paged(pages: np.ndarray, block_table_row: np.ndarray, length: int) -> np.ndarray:

@@ -262,3 +262,17 @@ def test_union_validation():
     assert u(FAKE, 8, FAKE, 1, 6, 4, 100, FAKE, 16, FAKE, None) == K.KVSEL_ERR_INVALID    # 6 % 4
     assert u(FAKE, 8, FAKE, 1, 4, 2, 100, FAKE, 15, FAKE, None) == K.KVSEL_ERR_INVALID    # 2 x 8 = 16 slots
     assert u(FAKE, 8, FAKE, 1, 4, 2, (1 << 20) + 1, FAKE, 16, FAKE, None) == K.KVSEL_ERR_UNSUPPORTED
+
+
+def test_indexer_fp8_validation():
+    lib = K.library()
+    f = lib.kvsel_indexer_scores_fp8
+    kv8 = _kv(dtype=K.KVSEL_FP8_E4M3, v_pages=None)
+    assert f(ctypes.byref(_kv()), FAKE, 32, 1.0, FAKE, 1024, None) == K.KVSEL_ERR_INVALID      # bf16 pages
+    assert f(ctypes.byref(kv8), None, 32, 1.0, FAKE, 1024, None) == K.KVSEL_ERR_INVALID
+    assert f(ctypes.byref(kv8), FAKE, 32, 1.0, FAKE, 1000, None) == K.KVSEL_ERR_INVALID         # stride
+    assert f(ctypes.byref(kv8), FAKE + 4, 32, 1.0, FAKE, 1024, None) == K.KVSEL_ERR_INVALID     # unaligned q
+    assert f(ctypes.byref(_kv(dtype=K.KVSEL_FP8_E4M3, head_dim=96)), FAKE, 32, 1.0, FAKE, 1024,
+             None) == K.KVSEL_ERR_UNSUPPORTED
+    # the other calls refuse FP8 pages
+    assert _decode(_kv(dtype=K.KVSEL_FP8_E4M3)) == K.KVSEL_ERR_UNSUPPORTED

@@ -521,6 +521,21 @@ def test_union_keep_hand_example_and_library_union():
     assert O.union_keep(sets).tolist() == want.tolist()
 
 
+def test_fp8_e4m3_decoding():
+    # codes fixed by the format: 1.0, the largest finite 448, the smallest
+    # subnormal 2^-9, the smallest normal 2^-6, signed zero, NaN
+    v = O.fp8_e4m3_bits_to_f64(np.array([0x38, 0x7E, 0x01, 0x08, 0x00, 0x80, 0xB8, 0x7F, 0xFF]))
+    assert v[:7].tolist() == [1.0, 448.0, 2.0 ** -9, 2.0 ** -6, 0.0, 0.0, -1.0]
+    assert np.signbit(v[5]) and np.isnan(v[7]) and np.isnan(v[8])
+    # every code against torch's float8_e4m3fn widening (a library routine)
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.fp8_e4m3_bits_to_f64(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+
+
 # ------------------------------------------------------------ chunk attention
 def test_chunk_causal_attention_rows():
     Hq, Hkv, S, n, d = 4, 2, 10, 5, 8
