@@ -1,0 +1,132 @@
+"""Parity at the full workload sizes, in the launch configurations the
+benchmark times, on outputs the float64 oracle can compute one by one:
+  * Llama-3-8B-shape layer (B=16, L_b ~ U[8K, 32K], 32 / 8 heads): decode
+    steps with the H2O accumulation fused, block max / mean, the 20% keep
+    sets; sampled rows in full, the probability mass of every row;
+  * 128K long-context case (B=4, L=131072, 32 / 8 heads): the SnapKV vote
+    and its top-4096, the indexer scores and their top-2048, sparse attention
+    over them, and dense decode; sampled rows in full, every keep set against
+    the oracle's selection on the GPU's own scores for sampled rows."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests.parity_util import f64, logical_kv_rows, max_rel, note, rel_l2
+
+pytestmark = pytest.mark.gpu
+OUT_TOL, SCORE_TOL = 2e-3, 1e-4
+
+
+def _K():
+    import attention_score_guided_amd as K
+    return K
+
+
+def test_llama3_8b_layer_full_size_sampled():
+    K = _K()
+    steps = 2
+    cfg = synth.llama3_8b_layer(steps=steps, device="cuda")
+    kvt = cfg["kv"]
+    B, Hq, Hkv = 16, 32, 8
+    base = kvt.seq_lens.clone()
+    cap = int(base.max()) + steps
+    stride = -(-cap // 16) * 16
+    cum = torch.zeros((B, Hkv, stride), device="cuda")
+    outs = []
+    for s in range(steps):
+        kv = K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, (base + s + 1).to(torch.int32), 16, cap)
+        out = torch.empty((B, Hq, 128), device="cuda")
+        K.decode_attn_scores(kv, cfg["q_steps"][s], Hq, cfg["scale"], out, None, None, K.EMIT_PROBS, cum, 1.0)
+        outs.append(out)
+    final = (base + steps).to(torch.int32)
+    n_blk = -(-cap // 16)
+    bmax = torch.zeros((B, Hkv, n_blk), device="cuda")
+    bmean = torch.zeros((B, Hkv, n_blk), device="cuda")
+    K.block_aggregate(cum, final, cap, 16, K.REDUCE_NONE, False, bmax, bmean)
+    rl = final.repeat_interleave(Hkv).to(torch.int32)
+    budgets = (rl.double() * 0.2).floor().to(torch.int32)
+    mb = int(budgets.max())
+    keep = torch.empty((B * Hkv, mb), dtype=torch.int32, device="cuda")
+    kc = torch.empty((B * Hkv,), dtype=torch.int32, device="cuda")
+    K.select_keep(cum.view(B * Hkv, stride), rl, cap, 4, 512, budgets, mb, keep, kc)
+    torch.cuda.synchronize()
+    sums = cum.double().sum(dim=2).cpu().numpy()
+    np.testing.assert_allclose(sums, steps * (Hq // Hkv), rtol=1e-4)
+    for b, c in [(0, 0), (7, 3), (15, 7)]:
+        note(f"llama3 full-size row b={b} kvh={c}")
+        L = int(final[b])
+        Kl, Vl = logical_kv_rows(kvt.k_pages, kvt.v_pages, kvt.block_table, b, c, L)
+        hs = slice(c * 4, c * 4 + 4)
+        cum_ref = np.zeros((1, L))
+        for s in range(steps):
+            Ls = int(base[b]) + s + 1
+            r = O.decode_attention(f64(cfg["q_steps"][s, b, hs]), Kl[:, :Ls], Vl[:, :Ls], cfg["scale"])
+            assert rel_l2(f64(outs[s][b, hs]), r["out"]) < OUT_TOL
+            cum_ref[:, :Ls] = O.accumulate(cum_ref[:, :Ls], r["probs"])
+        got = f64(cum[b, c, :L])
+        assert max_rel(got, cum_ref[0]) < SCORE_TOL
+        mx, mean = O.block_aggregate(got[None, :], L, 16)
+        nb = mx.shape[1]
+        assert max_rel(f64(bmax[b, c, :nb]), mx[0]) < 1e-6 and max_rel(f64(bmean[b, c, :nb]), mean[0]) < 1e-5
+        want = O.select_keep(got, L, 4, 512, int(budgets[b * Hkv + c]))
+        assert keep[b * Hkv + c, :int(kc[b * Hkv + c])].cpu().numpy().tolist() == want.tolist()
+
+
+def test_long_context_128k_full_size_sampled():
+    K = _K()
+    L, W = 131072, 32
+    cfg = synth.long_context_128k(seq_len=L, sparse_steps=1, device="cuda")
+    kvt, kit = cfg["kv"], cfg["kv_index"]
+    B, Hq, Hkv = 4, 32, 8
+    # (i) vote + top-4096 per KV head
+    kv_k = K.PagedKV(kvt.k_pages, None, kvt.block_table, kvt.seq_lens, 16, L)
+    votes = torch.zeros((B, Hkv, L), device="cuda")
+    K.snapkv_vote(kv_k, cfg["q_win"], Hq, W, 7, cfg["scale"], K.REDUCE_SUM, votes)
+    vrows = votes.view(B * Hkv, L)
+    vk = torch.empty((B * Hkv, 4096), dtype=torch.int32, device="cuda")
+    vc = torch.empty((B * Hkv,), dtype=torch.int32, device="cuda")
+    K.select_keep(vrows, torch.full((B * Hkv,), L - W, dtype=torch.int32, device="cuda"), L - W, 0, 0, None, 4096,
+                  vk, vc)
+    # (ii) one sparse decode step: indexer, top-2048, sparse attention
+    lens = kvt.seq_lens.clone() + 1
+    kvi = K.PagedKV(kit.k_pages, None, kit.block_table, lens, 16, L + 1)
+    scores = torch.empty((B, Hq, L + 1), device="cuda")
+    K.decode_attn_scores(kvi, cfg["qi_dec"][0], Hq, 1.0, None, None, scores, K.EMIT_LOGITS)
+    srows = scores.view(B * Hq, L + 1)
+    sk = torch.empty((B * Hq, 2048), dtype=torch.int32, device="cuda")
+    sc = torch.empty((B * Hq,), dtype=torch.int32, device="cuda")
+    K.select_keep(srows, lens.repeat_interleave(Hq).to(torch.int32), L + 1, 0, 0, None, 2048, sk, sc)
+    kvf = K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, lens, 16, L + 1)
+    sout = torch.empty((B, Hq, 128), device="cuda")
+    K.sparse_attn(kvf, cfg["q_dec"][0], Hq, sk.view(B, Hq, 2048), sc.view(B, Hq), 2048, cfg["scale"], sout)
+    # (iii) dense decode over the same cache
+    kvd = K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, kvt.seq_lens, 16, L)
+    dout = torch.empty((B, Hq, 128), device="cuda")
+    K.decode_attn_scores(kvd, cfg["q_dec"][0], Hq, cfg["scale"], dout, None, None, K.EMIT_PROBS)
+    torch.cuda.synchronize()
+
+    for b, c in [(1, 5)]:
+        note(f"128K vote row b={b} kvh={c}")
+        Kl, _ = logical_kv_rows(kvt.k_pages, None, kvt.block_table, b, c, L)
+        want = O.snapkv_vote(f64(cfg["q_win"][b, c * 4:c * 4 + 4]), Kl, cfg["scale"], 7, group_sum=True)
+        assert max_rel(f64(votes[b, c, :L - W]), want[0]) < SCORE_TOL
+    vg = f64(votes)
+    for r in [0, 13, 31]:
+        want = O.select_keep(vg[r // Hkv, r % Hkv], L - W, 0, 0, 4096)
+        assert vk[r, :int(vc[r])].cpu().numpy().tolist() == want.tolist()
+    sg = f64(scores)
+    for b, h in [(0, 0), (2, 17), (3, 31)]:
+        note(f"128K indexer / sparse / dense row b={b} h={h}")
+        KI, _ = logical_kv_rows(kit.k_pages, None, kit.block_table, b, 0, L + 1)
+        want_s = O.indexer_scores(f64(cfg["qi_dec"][0, b, h])[None, :], KI[0])[0]
+        assert np.max(np.abs(sg[b, h, :L + 1] - want_s)) <= 1e-5 * np.abs(want_s).max()
+        sel = O.select_keep(sg[b, h], L + 1, 0, 0, 2048)
+        r = b * Hq + h
+        assert sk[r, :int(sc[r])].cpu().numpy().tolist() == sel.tolist()
+        Kl, Vl = logical_kv_rows(kvt.k_pages, kvt.v_pages, kvt.block_table, b, h // 4, L + 1)
+        so, _ = O.sparse_attention(f64(cfg["q_dec"][0, b, h])[None, :], Kl, Vl, [sel], cfg["scale"])
+        assert rel_l2(f64(sout[b, h]), so[0]) < OUT_TOL
+        dr = O.decode_attention(f64(cfg["q_dec"][0, b, h])[None, :], Kl[:, :L], Vl[:, :L], cfg["scale"])
+        assert rel_l2(f64(dout[b, h]), dr["out"][0]) < OUT_TOL
