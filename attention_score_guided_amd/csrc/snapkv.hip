@@ -505,17 +505,32 @@ void snapkv_pass2(VoteParams p) {
       for (int k = 0; k < TN; ++k) hv[g * kStage + (t + k) * 16 + col] = cs[k];
     }
   };
+  // Fully visible tiles per step: four when the window rows of one head are
+  // held (measured ~1.5% faster at W = 32 with the same two waves per SIMD
+  // the staged keys allow, bitwise the same), else two.
   auto tiles = [&](int kbase, int g, int t_lo, int t_hi, const bf16x8 (&q)[RT][NU], const float (&lr)[RT][4]) {
     int t = t_lo;
-    // two tiles per step: four would need more registers than two waves per
-    // SIMD leave
-    for (; t + 1 < t_hi; t += 2) {
-      const int key0 = kbase + t * 16;
-      if (key0 >= 0 && key0 + 31 < prefix) {
-        tile_multi(std::integral_constant<int, 2>{}, g, t, q, lr);
-      } else {
-        tile(kbase, g, t, q, lr);
-        tile(kbase, g, t + 1, q, lr);
+    if constexpr (NS == 1 && RT <= 2) {
+      for (; t + 3 < t_hi; t += 4) {
+        const int key0 = kbase + t * 16;
+        if (key0 >= 0 && key0 + 63 < prefix) {
+          tile_multi(std::integral_constant<int, 4>{}, g, t, q, lr);
+        } else {
+          tile(kbase, g, t, q, lr);
+          tile(kbase, g, t + 1, q, lr);
+          tile(kbase, g, t + 2, q, lr);
+          tile(kbase, g, t + 3, q, lr);
+        }
+      }
+    } else {
+      for (; t + 1 < t_hi; t += 2) {
+        const int key0 = kbase + t * 16;
+        if (key0 >= 0 && key0 + 31 < prefix) {
+          tile_multi(std::integral_constant<int, 2>{}, g, t, q, lr);
+        } else {
+          tile(kbase, g, t, q, lr);
+          tile(kbase, g, t + 1, q, lr);
+        }
       }
     }
     for (; t < t_hi; ++t) tile(kbase, g, t, q, lr);
