@@ -41,8 +41,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kStage = 256;             // keys staged per chunk (16 tiles)
 constexpr int kTiles = kStage / 16;
-constexpr int kHalo = 8;                // pass 2: extra keys on each side (pool radius <= 8)
-constexpr int kOut = kStage - 2 * kHalo;  // pass 2: keys voted per chunk
+constexpr int kMaxHalo = 8;             // pass 2: extra keys on each side = the pool radius (<= 8)
 #ifndef KVSEL_VOTE_WGS
 #define KVSEL_VOTE_WGS 2048
 #endif
@@ -66,6 +65,7 @@ struct VoteParams {
   int num_kv_heads, num_q_heads, window, page_log2, max_pages, radius;
   int cpw1, n_run1;       // pass 1: chunks per workgroup, runs per sequence
   int cpw2;               // pass 2: chunks per workgroup
+  int halo, outc;         // pass 2: extra keys on each side (the pool radius), keys voted per chunk
   bool group_sum;
   float c2;               // scale * log2(e)
   float2* part_ml;        // [B][Hq][n_run1][W]  (reference, sum) in base-2 units
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(256) void snapkv_lse(const float2* part_ml, const i
 }
 
 // Pass 2: per (run of chunks, sequence, KV head).  For each chunk: the
-// staged keys are the chunk's kOut voted keys plus kHalo on each side;
+// staged keys are the chunk's voted keys plus the pool radius on each side;
 // p = exp2(s - lse2) for every window row, column sums per head, the group
 // sum in head order (or per head), the max-pool over the prefix, and the
 // chunk's votes.  MFMA with the window rows as A: lane (key = key0 +
@@ -415,6 +415,7 @@ void snapkv_pass2(VoteParams p) {
   const int L = p.seq_lens[b];
   const int prefix = L - p.window;
   const int c_first = run * p.cpw2;
+  const int kOut = p.outc, kHalo = p.halo;
   const int c_end = min(c_first + p.cpw2, (prefix + kOut - 1) / kOut);
   if (c_first >= c_end) return;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -591,7 +592,7 @@ hipError_t launch_rt(const VoteParams& vp, dim3 grid1, dim3 grid2, float* lse2, 
   const int G = vp.num_q_heads / vp.num_kv_heads;
   const int P = 1 << vp.page_log2;
   const size_t pages1 = (size_t)vp.cpw1 * kStage / P + 2;
-  const size_t pages2 = ((size_t)vp.cpw2 * kOut + 2 * kHalo) / P + 2;
+  const size_t pages2 = ((size_t)vp.cpw2 * vp.outc + 2 * vp.halo) / P + 2;
   const size_t lds1 = (size_t)kStage * Stage<D>::kRowBytes + (size_t)G * kWaves * RT * 16 * sizeof(float2) +
                       pages1 * sizeof(int);
   const size_t lds2 = (size_t)kStage * Stage<D>::kRowBytes + (size_t)G * kStage * sizeof(float) +
@@ -648,10 +649,11 @@ struct VotePlan {
   int cpw1, n_run1, cpw2, n_run2;
 };
 
-inline VotePlan plan_vote(int num_seqs, int num_kv_heads, int max_seq_len) {
+inline VotePlan plan_vote(int num_seqs, int num_kv_heads, int max_seq_len, int radius) {
   VotePlan v{};
   const int n1 = (max_seq_len + kStage - 1) / kStage;
-  const int n2 = (max_seq_len + kOut - 1) / kOut;
+  const int out2 = kStage - 2 * radius;
+  const int n2 = (max_seq_len + out2 - 1) / out2;
   const long long rows = (long long)num_seqs * num_kv_heads;
   v.cpw1 = chunks_per_wg(rows, n1);
   v.n_run1 = (n1 + v.cpw1 - 1) / v.cpw1;
@@ -663,13 +665,13 @@ inline VotePlan plan_vote(int num_seqs, int num_kv_heads, int max_seq_len) {
 }  // namespace
 
 size_t snapkv_workspace_bytes(int num_seqs, int num_kv_heads, int num_q_heads, int window, int max_seq_len) {
-  const VotePlan v = plan_vote(num_seqs, num_kv_heads, max_seq_len);
+  const VotePlan v = plan_vote(num_seqs, num_kv_heads, max_seq_len, kMaxHalo);   // pass 1's layout only
   const size_t rows = (size_t)num_seqs * num_q_heads * window;
   return align256(rows * v.n_run1 * sizeof(float2)) + align256(rows * sizeof(float));
 }
 
 hipError_t launch_snapkv(const SnapkvArgs& a, hipStream_t stream) {
-  const VotePlan v = plan_vote(a.num_seqs, a.num_kv_heads, a.max_seq_len);
+  const VotePlan v = plan_vote(a.num_seqs, a.num_kv_heads, a.max_seq_len, a.pool_kernel / 2);
   const size_t rows = (size_t)a.num_seqs * a.num_q_heads * a.window;
   uint8_t* ws = static_cast<uint8_t*>(a.workspace);
   float2* part_ml = reinterpret_cast<float2*>(ws);
@@ -688,6 +690,8 @@ hipError_t launch_snapkv(const SnapkvArgs& a, hipStream_t stream) {
   vp.cpw1 = v.cpw1;
   vp.n_run1 = v.n_run1;
   vp.cpw2 = v.cpw2;
+  vp.halo = a.pool_kernel / 2;
+  vp.outc = kStage - 2 * vp.halo;
   vp.group_sum = a.group_sum;
   vp.c2 = a.scale * kLog2e;
   vp.part_ml = part_ml;

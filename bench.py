@@ -250,8 +250,8 @@ def long_context_workload(torch, K, synth, args) -> dict:
         vote()
         K.select_keep(vrows, vlens, Lq - W, 0, 0, None, 4096, vkeep, vcnt, workspace=ws_vs)
 
-    t_vote = timed(torch, vote, 5)
-    t_vote_sel = timed(torch, vote_select, 5)
+    t_vote = timed(torch, vote, 10, warmup=3)
+    t_vote_sel = timed(torch, vote_select, 10, warmup=1)
     k_bytes = Bq * HKVq * Lq * 128 * 2
     vote_flops = 2 * (2.0 * Bq * HQq * W * Lq * 128)       # two passes of Q_win K^T
 
