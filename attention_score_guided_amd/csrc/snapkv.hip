@@ -43,16 +43,16 @@ constexpr int kStage = 256;             // keys staged per chunk (16 tiles)
 constexpr int kTiles = kStage / 16;
 constexpr int kMaxHalo = 8;             // pass 2: extra keys on each side = the pool radius (<= 8)
 #ifndef KVSEL_VOTE_WGS
-#define KVSEL_VOTE_WGS 2048
+#define KVSEL_VOTE_WGS 1024   // grid target (128K case: 992 workgroups, ~2 rounds of 2 per CU)
 #endif
 #ifndef KVSEL_VOTE_TN1
 #define KVSEL_VOTE_TN1 4     // pass 1: fully visible tiles computed together
 #endif
 #ifndef KVSEL_VOTE_WPE1
-#define KVSEL_VOTE_WPE1 0    // >0: occupancy hint (waves per SIMD) for pass 1
+#define KVSEL_VOTE_WPE1 2    // >0: occupancy hint (waves per SIMD) for pass 1
 #endif
 #ifndef KVSEL_VOTE_WPE2
-#define KVSEL_VOTE_WPE2 0    // >0: occupancy hint (waves per SIMD) for pass 2
+#define KVSEL_VOTE_WPE2 2    // >0: occupancy hint (waves per SIMD) for pass 2
 #endif
 constexpr int kMaxWgs = KVSEL_VOTE_WGS;  // grid target: chunks are grouped into runs beyond it
 constexpr float kRescale = 64.f;        // pass 1: move the reference past this (base-2 units)
