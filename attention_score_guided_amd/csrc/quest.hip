@@ -37,6 +37,12 @@ namespace {
 
 constexpr int kQThreads = 256;
 constexpr int kQWaves = kQThreads / kWave;
+#ifndef KVSEL_QUEST_U
+#define KVSEL_QUEST_U 4          // bounds: wave steps whose summary loads are issued together
+#endif
+#ifndef KVSEL_QUEST_MIN_WGS
+#define KVSEL_QUEST_MIN_WGS 1024 // bounds: fewer pages per workgroup until the grid has this many
+#endif
 
 // 16 bytes of the cache dtype widened to fp32 (EPL = 8 bf16 or 4 f32).
 template <bool BF16>
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(kQThreads) void quest_bounds_kernel(BoundParams p) 
   constexpr int EPL = 16 / EB;
   constexpr int LPR = D / EPL;       // lanes per page (8..32)
   constexpr int RPW = kWave / LPR;   // pages per wave step
-  constexpr int U = 4;               // wave steps whose loads are issued together
+  constexpr int U = KVSEL_QUEST_U;   // wave steps whose loads are issued together
   const int hgroups = p.group / GT;
   const int kvh = blockIdx.y / hgroups, hg = blockIdx.y % hgroups, b = blockIdx.z;
   const int h0 = kvh * p.group + hg * GT;
@@ -304,7 +310,7 @@ hipError_t launch_quest_select(const QuestArgs& a, const void* summary, const vo
     const int gt = bp.group >= 8 ? 8 : bp.group;
     const long long cols = (long long)a.num_seqs * a.num_kv_heads * (bp.group / gt);
     int ppw = 256;
-    while (ppw > 16 && cols * ((max_whole + ppw - 1) / ppw) < 1024) ppw /= 2;
+    while (ppw > 16 && cols * ((max_whole + ppw - 1) / ppw) < KVSEL_QUEST_MIN_WGS) ppw /= 2;
     bp.pages_per_wg = ppw;
     const dim3 grid((max_whole + ppw - 1) / ppw, a.num_kv_heads * (bp.group / gt), a.num_seqs);
     hipError_t e;
