@@ -30,8 +30,14 @@ namespace {
 
 constexpr int kSelThreads = 512;     // global-percentile kernels
 constexpr int kRowThreads = 1024;    // per-row select
-constexpr int kRowUnroll = 8;        // independent loads in flight per thread
-constexpr int kSubHist = 4;          // LDS sub-histograms (waves w, w+4, ... share one)
+#ifndef KVSEL_ROW_UNROLL
+#define KVSEL_ROW_UNROLL 2   // same-box A/B: 128 x 8192 top-128 22.0 -> 17.0 us; 128 x ~20K at 20% 32.2 -> 31.5 us (8 was the old value)
+#endif
+#ifndef KVSEL_SUB_HIST
+#define KVSEL_SUB_HIST 4
+#endif
+constexpr int kRowUnroll = KVSEL_ROW_UNROLL;  // independent loads in flight per thread
+constexpr int kSubHist = KVSEL_SUB_HIST;      // LDS sub-histograms (waves w, w+kSubHist, ... share one)
 
 // Order-preserving map from float to uint32 (larger float -> larger key);
 // -0.0 is folded onto +0.0 first.
