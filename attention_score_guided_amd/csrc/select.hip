@@ -290,7 +290,10 @@ __global__ __launch_bounds__(kRowThreads) void select_rows_kernel(RowsParams p) 
 // the one-workgroup algorithm inside the final kernel.  Results are
 // identical either way.
 constexpr int kSegQuantum = 4096;      // segment lengths are multiples of this
-constexpr int kSegTarget = 1024;       // aim for about this many workgroups per kernel
+#ifndef KVSEL_SEG_TARGET
+#define KVSEL_SEG_TARGET 1024
+#endif
+constexpr int kSegTarget = KVSEL_SEG_TARGET;  // aim for about this many workgroups per kernel
 constexpr int kSegThreads = 256;
 constexpr int kOutSeg = 4096;          // compaction segment: 4 float4 per thread
 constexpr int kCapSeg = kOutSeg;       // entries stored per compaction segment: all of it, so
