@@ -52,7 +52,7 @@ extern "C" {
 typedef enum {
   KVSEL_OK = 0,
   KVSEL_ERR_INVALID = -1,     /* an argument is out of its documented range  */
-  KVSEL_ERR_UNSUPPORTED = -2, /* valid, but not a shape/dtype this build runs */
+  KVSEL_ERR_UNSUPPORTED = -2, /* valid, but a shape/dtype the library does not run */
   KVSEL_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required  */
   KVSEL_ERR_HIP = -4          /* a HIP runtime call or launch failed         */
 } kvsel_status;
