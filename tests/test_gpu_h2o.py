@@ -124,7 +124,7 @@ def test_h2o_step_against_oracle(case):
                         s_h, c_h, n_h, G, scale, sinks, window, budget)
 
 
-def test_h2o_step_llama3_shape_with_vote_seeded_lists():
+def test_h2o_step_llama3_shape_with_decode_seeded_lists():
     """Llama-3-8B-shape layer scaled down (B=4, 32 / 8 heads, L_b in [1000,
     3000]): lists seeded by one full score-emitting decode pass and the
     keep-set selection at 20% (sinks 4, window 64), then 6 steps of per-step
@@ -222,3 +222,52 @@ def test_h2o_step_general_and_fused_eviction_paths():
                             o_h[b, c * G:(c + 1) * G], None, s_h[:, c:c + 1], c_h[:, c:c + 1], n_h[:, c:c + 1], G,
                             scale, 4, 16, int(budgets[b, c]))
         assert int(cnt[1, 1]) == 20 and int(cnt[0, 0]) == 10000
+
+
+def test_h2o_lists_seeded_by_the_snapkv_vote():
+    """Prefill-vote seeding: the SnapKV vote of the prompt's last 32 queries
+    (group sum, pool 7) picks the top-480 prefix positions per KV head; with
+    the window they form each list, seeded with their votes (window keys 0).
+    Then 4 decode steps of per-step eviction with budget 512 (sinks 4,
+    window 64), each checked against the oracle on the GPU's state."""
+    K = _K()
+    L, W, k, steps = 8192, 32, 480, 4
+    cfg = synth.long_context_128k(num_seqs=2, seq_len=L, sparse_steps=steps, device="cuda")
+    kvt = cfg["kv"]
+    B, Hq, Hkv = 2, 32, 8
+    kv0 = K.PagedKV(kvt.k_pages, None, kvt.block_table, kvt.seq_lens, 16, L)
+    votes = torch.zeros((B, Hkv, L), device="cuda")
+    K.snapkv_vote(kv0, cfg["q_win"], Hq, W, 7, cfg["scale"], K.REDUCE_SUM, votes)
+    rows = votes.view(B * Hkv, L)
+    keep = torch.empty((B * Hkv, k), dtype=torch.int32, device="cuda")
+    kc = torch.empty((B * Hkv,), dtype=torch.int32, device="cuda")
+    K.select_keep(rows, torch.full((B * Hkv,), L - W, dtype=torch.int32, device="cuda"), L - W, 0, 0, None, k,
+                  keep, kc)
+    torch.cuda.synchronize()
+    stride = k + W + 8
+    slots = torch.zeros((B, Hkv, stride), dtype=torch.int32)
+    cum = torch.zeros((B, Hkv, stride))
+    vh = votes.cpu()
+    for b in range(B):
+        for c in range(Hkv):
+            lst = torch.cat([keep[b * Hkv + c, :k].cpu(), torch.arange(L - W, L, dtype=torch.int32)])
+            slots[b, c, :k + W] = lst
+            cum[b, c, :k] = vh[b, c, lst[:k].long()]
+    cnt = torch.full((B, Hkv), k + W, dtype=torch.int32)
+    slots, cum, cnt = slots.cuda(), cum.cuda(), cnt.cuda()
+    logical = [logical_kv(kvt.k_pages, kvt.v_pages, kvt.block_table, b, L + steps) for b in range(B)]
+    budget = k + W
+    for t in range(steps):
+        lens = torch.full((B,), L + t + 1, dtype=torch.int32, device="cuda")
+        kv = K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, lens, 16, L + steps)
+        prev = (f64(slots).astype(np.int64), f64(cum), cnt.cpu().numpy().copy())
+        out = torch.empty((B, Hq, 128), device="cuda")
+        q = cfg["q_dec"][t].contiguous()
+        K.h2o_step(kv, q, Hq, cfg["scale"], slots, cum, cnt, 4, 64, budget, out)
+        torch.cuda.synchronize()
+        s_h, c_h, n_h, o_h = slots.cpu().numpy(), f64(cum), cnt.cpu().numpy(), f64(out)
+        for b in range(B):
+            Kl, Vl = logical[b]
+            _check_step(f64(q[b]), Kl, Vl, L + t + 1, prev, b, o_h[b], None, s_h, c_h, n_h, Hq // Hkv,
+                        cfg["scale"], 4, 64, budget)
+        assert (cnt == budget).all()

@@ -8,7 +8,8 @@ oracle:
     sets), and the next chunk attends to the kept keys plus its own causal
     prefix (sparse attention over those positions);
   * exact top-256 per query on the last 64 queries: the decode pass in
-    logits mode, the row selection, sparse attention.
+    logits mode, the row selection, sparse attention;
+  * Quest (16 pages of 16 per query head) on the last 64 queries.
 Outputs within 2e-3 relative L2, keep sets bit-exact."""
 import math
 
@@ -19,6 +20,7 @@ import torch
 import oracle as O
 import synth
 from tests.parity_util import f64, note, rel_l2
+from tests.test_gpu_quest import _check_row
 
 pytestmark = pytest.mark.gpu
 OUT_TOL = 2e-3
@@ -125,3 +127,41 @@ def test_qwen_like_exact_top256_on_last_queries():
             sets.append(s)
         want, _ = O.sparse_attention(Qd[:, p], Kd, Vd, sets, scale)
         assert rel_l2(f64(out[i]), want) < OUT_TOL
+
+
+def test_qwen_like_quest_on_last_queries():
+    """The Quest strategy of the same experiment: page summaries (16 tokens)
+    once over the prompt, then for each of the last 64 queries the 16 pages
+    with the largest bounds over its causal prefix (plus the partial tail
+    page), and sparse attention over them; sets and outputs against the
+    oracle."""
+    K = _K()
+    cfg = synth.qwen_like_layer()
+    Kd, Vd, Qd = f64(cfg["K"]), f64(cfg["V"]), f64(cfg["Q"])
+    Hkv, N, d = Kd.shape
+    Hq, C, scale, P = cfg["num_q_heads"], 64, cfg["scale"], 16
+    G = Hq // Hkv
+    kp, vp, bt = _paged(cfg)
+    full = K.PagedKV(kp, vp, bt.cuda(), torch.tensor([N], dtype=torch.int32, device="cuda"), P, N)
+    summary = torch.empty((kp.shape[0], Hkv, 2, d), dtype=torch.bfloat16, device="cuda")
+    K.quest_summarize(full, summary)
+    pos = np.arange(N - C, N)
+    kv = K.PagedKV(kp, vp, bt.repeat(C, 1).cuda(), torch.tensor(pos + 1, dtype=torch.int32, device="cuda"), P, N)
+    q = cfg["Q"][:, N - C:].permute(1, 0, 2).contiguous().cuda()
+    idx = torch.empty((C, Hq, 16 * P + P - 1), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((C, Hq), dtype=torch.int32, device="cuda")
+    bounds = torch.empty((C, Hq, N // P), device="cuda")
+    K.quest_select(kv, summary, q, Hq, 16, idx, cnt, bounds=bounds)
+    out = torch.empty((C, Hq, d), device="cuda")
+    K.sparse_attn(kv, q, Hq, idx, cnt, idx.shape[-1], scale, out)
+    torch.cuda.synchronize()
+    for i in range(0, C, 7):
+        p = int(pos[i])
+        sets = []
+        for h in range(Hq):
+            got = idx[i, h, :int(cnt[i, h])].cpu().numpy()
+            # the oracle's pages, except swaps between bounds within rounding of the cut
+            _check_row(Qd[h, p], Kd[h // G, :p + 1], P, 16, f64(bounds[i, h]), got)
+            sets.append(got)
+        o_out, _ = O.sparse_attention(Qd[:, p], Kd, Vd, sets, scale)
+        assert rel_l2(f64(out[i]), o_out) < OUT_TOL
