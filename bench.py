@@ -475,6 +475,141 @@ def llama3_workload(torch, K, synth, args) -> dict:
     }
 
 
+def qwen_like_workload(torch, K, synth, args) -> dict:
+    """Qwen3-0.6B-like layer (16 / 8 heads, d=128, bf16, page 16): 1600
+    tokens in 64-token chunks, causal within each chunk (one pseudo-sequence
+    per chunk query), under keep-all, recent-256 and sinks-4 + recent (cut back
+    to 256 keys after every chunk); then the last 64 queries under the four
+    strategies of the long-context experiment (recent window, sinks + window,
+    Quest 16 pages, exact top-256), each against full attention."""
+    import numpy as np
+    cfg = synth.qwen_like_layer()
+    Hkv, N, d = cfg["K"].shape
+    Hq, C, budget, scale, P = cfg["num_q_heads"], cfg["chunk"], cfg["budget"], cfg["scale"], 16
+    g = synth.generator(21)
+    bt, n_pages = synth.shuffled_block_table(1, N, P, g)
+    kp = torch.zeros((n_pages, Hkv, P, d), dtype=torch.bfloat16)
+    vp = torch.zeros((n_pages, Hkv, P, d), dtype=torch.bfloat16)
+    synth.write_positions(kp, bt[0], 0, cfg["K"])
+    synth.write_positions(vp, bt[0], 0, cfg["V"])
+    kp, vp = kp.cuda(), vp.cuda()
+    bt64 = bt.repeat(C, 1).cuda()
+    Q = cfg["Q"].cuda()
+    chunks = list(range(0, N, C))
+    qs = [Q[:, c0:c0 + C].permute(1, 0, 2).contiguous() for c0 in chunks]
+    out = torch.empty((C, Hq, d), device="cuda")
+    ws_d = torch.empty(K.decode_workspace_bytes(K.PagedKV(kp, vp, bt64, torch.ones(C, dtype=torch.int32,
+                                                                                   device="cuda"), P, N), Hq, True),
+                       dtype=torch.uint8, device="cuda")
+    # keep-all: each chunk's queries against every earlier key
+    kv_all = [K.PagedKV(kp, vp, bt64, torch.arange(c0 + 1, c0 + C + 1, dtype=torch.int32, device="cuda"), P,
+                        c0 + C) for c0 in chunks]
+
+    def run_all():
+        for i in range(len(chunks)):
+            K.decode_attn_scores(kv_all[i], qs[i], Hq, scale, out, None, None, K.EMIT_PROBS, workspace=ws_d)
+    t_all = timed(torch, run_all, 5) / len(chunks)
+    # K+V of the cache each chunk reads (every pseudo-sequence reads the same
+    # prefix again, from the caches: the HBM bytes are the cache once)
+    kv_bytes = sum(c0 + C for c0 in chunks) * Hkv * d * 2 * 2 / len(chunks)
+
+    # recent-256 / sinks-4 + recent: the index lists of every chunk follow
+    # from the policy (the kept keys are the policy's forced sets), so they
+    # are made before the timed region; each chunk runs the sparse attention
+    # and the cut of its cache back to 256 keys
+    stride = budget + C
+    ws_s = torch.empty(K.sparse_workspace_bytes(C, Hq, d, stride), dtype=torch.uint8, device="cuda")
+    keep = torch.empty((1, budget), dtype=torch.int32, device="cuda")
+    kc = torch.empty((1,), dtype=torch.int32, device="cuda")
+    zeros = torch.zeros((1, N), device="cuda")
+    policy_us = {}
+    for name, sinks in [("recent_256", 0), ("sinks_4_recent", 4)]:
+        idxs, cnts, lens_c, cut_lens = [], [], [], []
+        for c0 in chunks:
+            kept = np.arange(c0) if c0 <= budget else np.concatenate(
+                [np.arange(min(sinks, c0)), np.arange(c0 - (budget - sinks), c0)])
+            idx = np.full((C, Hkv, stride), -1, dtype=np.int32)
+            cnt = np.zeros((C, Hkv), dtype=np.int32)
+            for i in range(C):
+                lst = np.concatenate([kept, np.arange(c0, c0 + i + 1)])
+                idx[i, :, :len(lst)] = lst
+                cnt[i] = len(lst)
+            idxs.append(torch.from_numpy(idx).cuda())
+            cnts.append(torch.from_numpy(cnt).cuda())
+            lens_c.append(K.PagedKV(kp, vp, bt64, torch.full((C,), c0 + C, dtype=torch.int32, device="cuda"), P,
+                                    c0 + C))
+            cut_lens.append(torch.tensor([c0 + C], dtype=torch.int32, device="cuda"))
+
+        def run_policy():
+            for i, c0 in enumerate(chunks):
+                K.sparse_attn(lens_c[i], qs[i], Hq, idxs[i], cnts[i], stride, scale, out, workspace=ws_s)
+                K.select_keep(zeros, cut_lens[i], c0 + C, sinks, budget - sinks, None, budget, keep, kc)
+        policy_us[name] = round(timed(torch, run_policy, 5) / len(chunks) * 1e3, 1)
+
+    # the last 64 queries: full attention and the four strategies
+    pos = np.arange(N - C, N)
+    kvl = K.PagedKV(kp, vp, bt64, torch.tensor(pos + 1, dtype=torch.int32, device="cuda"), P, N)
+    ql = qs[-1]
+    full = torch.empty((C, Hq, d), device="cuda")
+    K.decode_attn_scores(kvl, ql, Hq, scale, full, None, None, K.EMIT_PROBS, workspace=ws_d)
+
+    def rel(o):
+        return round(float((o - full).norm() / full.norm()), 4)
+    errs = {}
+    for name, sinks in [("recent_256", 0), ("sinks_4_recent", 4)]:
+        idx = np.full((C, Hkv, budget), -1, dtype=np.int32)
+        cnt = np.zeros((C, Hkv), dtype=np.int32)
+        for i, p in enumerate(pos):
+            lst = np.array(sorted(set(range(min(sinks, p + 1))) | set(range(max(0, p + 1 - (budget - sinks)), p + 1))))
+            idx[i, :, :len(lst)] = lst
+            cnt[i] = len(lst)
+        o = torch.empty_like(full)
+        K.sparse_attn(kvl, ql, Hq, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), budget, scale, o,
+                      workspace=ws_s)
+        errs[name] = rel(o)
+    # Quest: summaries once, 16 pages of 16 per query head
+    summary = torch.empty((n_pages, Hkv, 2, d), dtype=torch.bfloat16, device="cuda")
+    K.quest_summarize(K.PagedKV(kp, vp, bt.cuda(), torch.tensor([N], dtype=torch.int32, device="cuda"), P, N), summary)
+    qidx = torch.empty((C, Hq, 16 * P + P - 1), dtype=torch.int32, device="cuda")
+    qcnt = torch.empty((C, Hq), dtype=torch.int32, device="cuda")
+    ws_q = torch.empty(K.quest_workspace_bytes(kvl, Hq, 16), dtype=torch.uint8, device="cuda")
+    ws_qs = torch.empty(K.sparse_workspace_bytes(C, Hq, d, qidx.shape[-1]), dtype=torch.uint8, device="cuda")
+    oq = torch.empty_like(full)
+
+    def quest():
+        K.quest_select(kvl, summary, ql, Hq, 16, qidx, qcnt, workspace=ws_q)
+        K.sparse_attn(kvl, ql, Hq, qidx, qcnt, qidx.shape[-1], scale, oq, workspace=ws_qs)
+    t_quest = timed(torch, quest, 10)
+    errs["quest_16_pages"] = rel(oq)
+    # exact top-256 per query head
+    logits = torch.empty((C, Hq, N), device="cuda")
+    tk = torch.empty((C * Hq, budget), dtype=torch.int32, device="cuda")
+    tc = torch.empty((C * Hq,), dtype=torch.int32, device="cuda")
+    rl = kvl.seq_lens.repeat_interleave(Hq).to(torch.int32)
+    ot = torch.empty_like(full)
+    ws_t = torch.empty(K.sparse_workspace_bytes(C, Hq, d, budget), dtype=torch.uint8, device="cuda")
+
+    def exact():
+        K.decode_attn_scores(kvl, ql, Hq, scale, None, None, logits, K.EMIT_LOGITS, workspace=ws_d)
+        K.select_keep(logits.view(C * Hq, N), rl, N, 0, 0, None, budget, tk, tc)
+        K.sparse_attn(kvl, ql, Hq, tk.view(C, Hq, budget), tc.view(C, Hq), budget, scale, ot, workspace=ws_t)
+    t_exact = timed(torch, exact, 10)
+    errs["exact_top256"] = rel(ot)
+    return {
+        "metric": "KV GB/s (% HBM peak) for score-emitting decode attn + keep-set select",
+        "value": round(kv_bytes / (t_all * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "qwen_like_chunks", "tokens": N, "chunk": C, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": d, "page_size": P, "budget": budget},
+        "note": "megabyte-sized and launch-bound: the per-chunk times are the figures; the errors are of "
+                "synthetic N(0,1) data, whose attention is far from sparse",
+        "keep_all_us_per_chunk": round(t_all * 1e3, 1),
+        "policy_us_per_chunk": policy_us,
+        "last_64_queries": {"rel_error_vs_full": errs, "quest_us": round(t_quest * 1e3, 1),
+                            "exact_top256_us": round(t_exact * 1e3, 1)},
+    }
+
+
 def llama3_h2o_workload(torch, K, synth, args) -> dict:
     """Llama-3-8B-shape layer, B=16, ragged L_b ~ U[8K, 32K], H2O with the
     eviction inside the decode loop: the lists of kept positions are seeded
@@ -555,7 +690,8 @@ def main() -> int:
                          "eager launches on this path)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--workload", default="llama70b_step",
-                    choices=["llama70b_step", "long_context_128k", "llama3_8b_steps", "llama3_8b_h2o_evict"],
+                    choices=["llama70b_step", "long_context_128k", "llama3_8b_steps", "llama3_8b_h2o_evict",
+                             "qwen_like_chunks"],
                     help="the default is the 70B decode step; the others report their own line")
     ap.add_argument("--counters", action="store_true",
                     help="counter-collection mode: one layer, 3 decode calls, then a plain 1 GiB "
@@ -580,6 +716,9 @@ def main() -> int:
         return 0
     if args.workload == "llama3_8b_steps":
         print(json.dumps(llama3_workload(torch, K, synth, args)), flush=True)
+        return 0
+    if args.workload == "qwen_like_chunks":
+        print(json.dumps(qwen_like_workload(torch, K, synth, args)), flush=True)
         return 0
     if args.workload == "llama3_8b_h2o_evict":
         print(json.dumps(llama3_h2o_workload(torch, K, synth, args)), flush=True)
