@@ -475,6 +475,49 @@ def llama3_workload(torch, K, synth, args) -> dict:
     }
 
 
+def tiny_workload(torch, K, synth, args) -> dict:
+    """Tiny case: 1 sequence, 4 query heads on 1 KV head, d=64, fp32, page 16,
+    512-token prompt, 16 decode steps with the H2O accumulation fused, then
+    block 16 max / mean and the keep set (sinks 4, window 64, budget 128)."""
+    cfg = synth.tiny_case(device="cuda")
+    kvt = cfg["kv"]
+    prompt, steps = cfg["prompt"], cfg["steps"]
+    cap = prompt + steps
+    kv_s = [K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table,
+                      torch.tensor([prompt + s + 1], dtype=torch.int32, device="cuda"), 16, cap) for s in range(steps)]
+    cum = torch.zeros((1, 1, cap), device="cuda")
+    out = torch.empty((1, 4, 64), device="cuda")
+    probs = torch.empty((1, 4, cap), device="cuda")
+    ws = torch.empty(K.decode_workspace_bytes(kv_s[-1], 4, True), dtype=torch.uint8, device="cuda")
+    n_blk = cap // 16
+    bmax = torch.empty((1, 1, n_blk), device="cuda")
+    bmean = torch.empty((1, 1, n_blk), device="cuda")
+    keep = torch.empty((1, 128), dtype=torch.int32, device="cuda")
+    kc = torch.empty((1,), dtype=torch.int32, device="cuda")
+    final = torch.tensor([cap], dtype=torch.int32, device="cuda")
+    bud = torch.tensor([128], dtype=torch.int32, device="cuda")
+
+    def run():
+        cum.zero_()
+        for s in range(steps):
+            K.decode_attn_scores(kv_s[s], cfg["q_steps"][s], 4, cfg["scale"], out, None, probs, K.EMIT_PROBS, cum,
+                                 1.0, workspace=ws)
+        K.block_aggregate(cum, final, cap, 16, K.REDUCE_NONE, False, bmax, bmean)
+        K.select_keep(cum.view(1, cap), final, cap, 4, 64, bud, 128, keep, kc)
+    t = timed(torch, run, 20, warmup=3)
+    kv_bytes = sum(prompt + s + 1 for s in range(steps)) * 64 * 4 * 2
+    return {
+        "metric": "KV GB/s (% HBM peak) for score-emitting decode attn + keep-set select",
+        "value": round(kv_bytes / (t * 1e-3) / 1e9, 3), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "higher_is_better": True, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "tiny_case", "prompt": prompt, "q_heads": 4, "kv_heads": 1, "head_dim": 64,
+                   "page_size": 16, "block_size": 16, "keep": "sinks 4, window 64, budget 128"},
+        "note": "kilobyte-sized and launch-bound: the time per step is the figure",
+        "us_per_decode_step": round(t * 1e3 / steps, 1),
+        "us_all_steps_plus_select": round(t * 1e3, 1),
+    }
+
+
 def qwen_like_workload(torch, K, synth, args) -> dict:
     """Qwen3-0.6B-like layer (16 / 8 heads, d=128, bf16, page 16): 1600
     tokens in 64-token chunks, causal within each chunk (one pseudo-sequence
@@ -691,7 +734,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--workload", default="llama70b_step",
                     choices=["llama70b_step", "long_context_128k", "llama3_8b_steps", "llama3_8b_h2o_evict",
-                             "qwen_like_chunks"],
+                             "qwen_like_chunks", "tiny_case"],
                     help="the default is the 70B decode step; the others report their own line")
     ap.add_argument("--counters", action="store_true",
                     help="counter-collection mode: one layer, 3 decode calls, then a plain 1 GiB "
@@ -716,6 +759,9 @@ def main() -> int:
         return 0
     if args.workload == "llama3_8b_steps":
         print(json.dumps(llama3_workload(torch, K, synth, args)), flush=True)
+        return 0
+    if args.workload == "tiny_case":
+        print(json.dumps(tiny_workload(torch, K, synth, args)), flush=True)
         return 0
     if args.workload == "qwen_like_chunks":
         print(json.dumps(qwen_like_workload(torch, K, synth, args)), flush=True)
