@@ -34,7 +34,7 @@ EXPORTED = (
     "kvsel_block_aggregate", "kvsel_select_keep", "kvsel_select_workspace_bytes",
     "kvsel_snapkv_vote", "kvsel_snapkv_workspace_bytes", "kvsel_sparse_attn",
     "kvsel_sparse_workspace_bytes", "kvsel_quest_summarize", "kvsel_quest_select",
-    "kvsel_quest_workspace_bytes", "kvsel_accumulate_ex", "kvsel_block_aggregate_ex", "kvsel_select_threshold",
+    "kvsel_quest_workspace_bytes", "kvsel_accumulate_ex", "kvsel_block_aggregate_ex", "kvsel_select_threshold", "kvsel_block_update",
     "kvsel_union_keep", "kvsel_indexer_scores_fp8", "kvsel_h2o_step", "kvsel_h2o_workspace_bytes", "kvsel_set_sync_spin_limit",
     "kvsel_status_string", "kvsel_last_error",
 )
@@ -87,6 +87,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvsel_select_threshold": (ctypes.c_int, [P, I64, P, I32, I32, F, P, I64, P, P]),
         "kvsel_union_keep": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, P, I64, P, P]),
         "kvsel_indexer_scores_fp8": (ctypes.c_int, [D, P, I32, F, P, I64, P]),
+        "kvsel_block_update": (ctypes.c_int, [P, I64, P, I32, I32, P, I64, I32, I32, F, P, I64, P]),
         "kvsel_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "kvsel_set_sync_spin_limit": (I32, [I32]),
         "kvsel_last_error": (ctypes.c_char_p, []),
@@ -405,3 +406,27 @@ def indexer_scores_fp8(kv: PagedKV, q: torch.Tensor, num_q_heads: int, scale: fl
         raise TypeError("the FP8 indexer takes float8_e4m3fn pages and queries")
     _check(_LIB.kvsel_indexer_scores_fp8(kv.ref(), _ptr(q, None, "q"), num_q_heads, float(scale),
                                          _ptr(scores, torch.float32, "scores"), scores.shape[-1], _stream(stream)))
+
+
+def block_meta(rows: int, num_blocks: int, device="cuda") -> torch.Tensor:
+    """Zeroed per-block metadata for kvsel_block_update: int32 ``[rows][num_blocks][2]``
+    holding kvsel_block_meta records (score bits, stamp); see block_meta_views."""
+    return torch.zeros((rows, num_blocks, 2), dtype=torch.int32, device=device)
+
+
+def block_meta_views(meta: torch.Tensor):
+    """(score f32, stamp int32) views ``[rows][num_blocks]`` of a block_meta tensor."""
+    return meta.view(torch.float32)[..., 0], meta[..., 1]
+
+
+def block_update(idx: torch.Tensor, counts: torch.Tensor, block_size: int, step: int, meta: torch.Tensor,
+                 values: Optional[torch.Tensor] = None, decay: float = 1.0, stream=None) -> None:
+    """kvsel_block_update: idx ``[rows][stride]``, counts ``[rows]``, values aligned with idx
+    or None, meta int32 ``[rows][meta_stride][2]`` (block_meta) updated in place."""
+    rows, stride = idx.reshape(-1, idx.shape[-1]).shape
+    if meta.dim() != 3 or meta.shape[-1] != 2 or meta.shape[0] != rows or not meta.is_contiguous():
+        raise ValueError("meta must be a contiguous int32 [rows][meta_stride][2] tensor")
+    _check(_LIB.kvsel_block_update(
+        _ptr(idx, torch.int32, "idx"), stride, _ptr(counts, torch.int32, "counts"), rows, stride,
+        _ptr(values, torch.float32, "values"), 0 if values is None else values.shape[-1], int(block_size),
+        int(step), float(decay), _ptr(meta, torch.int32, "meta"), meta.shape[1], _stream(stream)))

@@ -452,6 +452,23 @@ int kvsel_block_aggregate_ex(const float* scores, int64_t score_stride, const in
                     "block_aggregate_ex launch");
 }
 
+int kvsel_block_update(const int32_t* idx, int64_t idx_stride, const int32_t* counts, int32_t rows,
+                       int32_t max_count, const float* values, int64_t values_stride, int32_t block_size,
+                       int32_t step, float decay, kvsel_block_meta* meta, int64_t meta_stride, void* stream) {
+  if (!idx || !counts || !meta) return fail(KVSEL_ERR_INVALID, "NULL pointer argument");
+  if (rows <= 0 || block_size <= 0 || max_count < 0 || meta_stride <= 0)
+    return fail(KVSEL_ERR_INVALID, "rows, block_size and meta_stride must be positive");
+  if (idx_stride < max_count || (values && values_stride < max_count))
+    return fail(KVSEL_ERR_INVALID, "idx_stride / values_stride < max_count");
+  if (rows > 65535) return fail(KVSEL_ERR_UNSUPPORTED, "rows > 65535");
+  int st = check_device();
+  if (st != KVSEL_OK) return st;
+  return hip_status(kvsel::launch_block_update(idx, idx_stride, counts, rows, max_count, values, values_stride,
+                                               block_size, step, decay, meta, meta_stride,
+                                               static_cast<hipStream_t>(stream)),
+                    "block_update launch");
+}
+
 int kvsel_select_threshold(const float* scores, int64_t stride, const int32_t* lengths, int32_t rows, int32_t max_len,
                            float threshold, int32_t* out_idx, int64_t out_stride, int32_t* out_count, void* stream) {
   if (!scores || !lengths || !out_idx || !out_count) return fail(KVSEL_ERR_INVALID, "NULL pointer argument");

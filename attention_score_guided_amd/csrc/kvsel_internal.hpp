@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "kvsel.h"
+
 namespace kvsel {
 
 // Split-K decode geometry shared by the launcher and the workspace query.
@@ -79,6 +81,10 @@ hipError_t launch_indexer_fp8(const void* k_pages, const int32_t* block_table, c
                               const void* q, int num_seqs, int num_kv_heads, int num_q_heads, int head_dim,
                               int page_size, int max_pages, int max_seq_len, float scale, float* scores,
                               int64_t stride, hipStream_t stream);
+
+hipError_t launch_block_update(const int32_t* idx, int64_t idx_stride, const int32_t* counts, int rows,
+                               int max_count, const float* values, int64_t values_stride, int block_size,
+                               int step, float decay, kvsel_block_meta* meta, int64_t meta_stride, hipStream_t stream);
 
 size_t select_workspace_bytes(int rows, int max_len, int mode);
 

@@ -11,6 +11,8 @@
 //   (block_variant_lanes: the same for power-of-two blocks of 4..64, one lane per position)
 // Across requests ([OFFLOAD] §3.2, absolute-threshold normalisation):
 //   select_threshold_kernel   positions with score >= threshold, ascending
+// Per-block metadata ([OFFLOAD] §5.1, score accumulator + last-update stamp):
+//   block_update_kernel       lazy-decayed score and stamp of the blocks a step selected
 // All are HBM-bound streaming passes with one writer per output element.
 #include "device_common.hpp"
 #include "kvsel_internal.hpp"
@@ -189,7 +191,87 @@ __global__ __launch_bounds__(kThreads) void select_threshold_kernel(
   if (tid == 0) out_count[r] = base;
 }
 
+// Per-block metadata update from one step's selection ([OFFLOAD] §5.1: a
+// float score accumulator and an int32 last-update stamp per block; each
+// step walks the selected blocks).  One thread per list entry (grid: entry
+// chunks x rows); the listed positions are ascending, so the positions of a
+// block are consecutive among the row's valid entries: the first of them (its
+// head) sums them all and is the block's only writer.  score = score *
+// decay^(step - stamp) + sum (the stamp makes the decay lazy: untouched
+// blocks are not written), stamp = step.  A workgroup stages its entries and
+// the next kBUTail ones in LDS, so heads sum from LDS; a block reaching past
+// them (long blocks, padding runs) continues from global memory.
+constexpr int kBUTail = 64;
+
+// kPow2: block_of (position -> block index) is (a shift for power-of-two block sizes,
+// which the usual 16 / 32 / 64 are, else a division).
+template <bool kPow2>
+__global__ __launch_bounds__(kThreads) void block_update_kernel(
+    const int32_t* __restrict__ idx, int64_t idx_stride, const int32_t* __restrict__ counts, int max_count,
+    const float* __restrict__ values, int64_t values_stride, int block_size, int bs_shift, int step, float decay,
+    kvsel_block_meta* __restrict__ meta, int64_t meta_stride) {
+  __shared__ int32_t sidx[kThreads + kBUTail];
+  __shared__ float sval[kThreads + kBUTail];
+  auto block_of = [&](int pos) { return kPow2 ? pos >> bs_shift : pos / block_size; };
+  const int r = blockIdx.y;
+  const int32_t* li = idx + (size_t)r * idx_stride;
+  const float* lv = values ? values + (size_t)r * values_stride : nullptr;
+  const int i0 = blockIdx.x * kThreads;
+  const int i = i0 + threadIdx.x;
+  // The count and the own entry load together, and the block's record loads
+  // with the staging loads: two dependent memory levels before the store.
+  const int n = counts[r];
+  const int j = i < max_count ? li[i] : -1;                 // idx_stride >= max_count
+  const bool live = i < n && j >= 0;
+  const int blk = live ? block_of(j) : 0;
+  kvsel_block_meta* m = meta + (size_t)r * meta_stride + blk;
+  kvsel_block_meta old{0.f, 0};
+  if (live) old = *m;                                       // one 8-byte load
+  const int lim = min(n, i0 + kThreads + kBUTail);          // LDS holds entries [i0, lim)
+  for (int t = threadIdx.x; t < kThreads + kBUTail; t += kThreads) {
+    if (i0 + t < lim) {
+      sidx[t] = li[i0 + t];
+      sval[t] = lv ? lv[i0 + t] : 1.f;
+    }
+  }
+  __syncthreads();
+  if (!live) return;
+  int k = i - 1;                                            // previous valid entry
+  int jk = -1;
+  for (; k >= 0; --k) {
+    jk = k >= i0 ? sidx[k - i0] : li[k];
+    if (jk >= 0) break;
+  }
+  if (k >= 0 && block_of(jk) == blk) return;             // not the block's first entry
+  float sum = 0.f;
+  for (int t = i; t < n; ++t) {
+    const bool in_lds = t < lim;
+    const int jt = in_lds ? sidx[t - i0] : li[t];
+    if (jt < 0) continue;
+    if (block_of(jt) != blk) break;
+    sum += in_lds ? sval[t - i0] : (lv ? lv[t] : 1.f);
+  }
+  const float keep = decay == 1.f ? 1.f : powf(decay, (float)(step - old.stamp));
+  *m = kvsel_block_meta{fmaf(keep, old.score, sum), step};  // one 8-byte store
+}
+
 }  // namespace
+
+hipError_t launch_block_update(const int32_t* idx, int64_t idx_stride, const int32_t* counts, int rows,
+                               int max_count, const float* values, int64_t values_stride, int block_size,
+                               int step, float decay, kvsel_block_meta* meta, int64_t meta_stride, hipStream_t stream) {
+  if (max_count == 0) return hipSuccess;
+  const dim3 grid((max_count + kThreads - 1) / kThreads, rows);
+  if ((block_size & (block_size - 1)) == 0) {
+    const int shift = __builtin_ctz((unsigned)block_size);
+    hipLaunchKernelGGL(block_update_kernel<true>, grid, dim3(kThreads), 0, stream, idx, idx_stride, counts,
+                       max_count, values, values_stride, block_size, shift, step, decay, meta, meta_stride);
+  } else {
+    hipLaunchKernelGGL(block_update_kernel<false>, grid, dim3(kThreads), 0, stream, idx, idx_stride, counts,
+                       max_count, values, values_stride, block_size, 0, step, decay, meta, meta_stride);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_accumulate_ex(const float* probs, int64_t probs_stride, const int32_t* seq_lens, int num_seqs,
                                 int num_q_heads, int num_kv_heads, int max_seq_len, int mode, float decay,

@@ -290,6 +290,22 @@ def long_context_workload(torch, K, synth, args) -> dict:
     t_sparse = a.elapsed_time(b) / steps
     sparse_bytes = (Bq * Lq * 64 * 2) + 2 * Bq * HQq * Lq * 4 + Bq * HQq * 2048 * 128 * 2 * 2
 
+    # per-block metadata of the offloading layer: the step's probabilities
+    # (emitted by the sparse pass) walked into a float score and an int32
+    # stamp per block of 16 for every (sequence, query head) row
+    sprobs = torch.empty((Bq, HQq, 2048), device="cuda")
+    K.sparse_attn(kv_f_s[0], cfg["q_dec"][0], HQq, keep.view(Bq, HQq, 2048), kcnt.view(Bq, HQq), 2048,
+                  cfg["scale"], out, sprobs, workspace=ws_s)
+    n_blk = -(-cap // 16)
+    bmeta = K.block_meta(Bq * HQq, n_blk)
+    sp2 = sprobs.view(Bq * HQq, 2048)
+    # a launch of a few microseconds: 10 launches replayed from one HIP graph,
+    # so the time is the GPU's and not the Python call rate
+    g_bup = capture(torch, lambda: [K.block_update(keep, kcnt, 16, 1, bmeta, sp2, 0.9) for _ in range(10)])
+    t_bup = timed(torch, g_bup.replay, 5) / 10
+    t_bup_eager = timed(torch, lambda: K.block_update(keep, kcnt, 16, 1, bmeta, sp2, 0.9), 10)
+    del sprobs, sp2, bmeta, g_bup
+
     # the same indexer with its keys and queries stored as FP8 E4M3
     kv_i8 = K.PagedKV(kit.k_pages.to(torch.float8_e4m3fn), None, kit.block_table, kv_i_s[0].seq_lens, 16, cap)
     qi8 = cfg["qi_dec"][0].to(torch.float8_e4m3fn)
@@ -354,6 +370,8 @@ def long_context_workload(torch, K, synth, args) -> dict:
         "sparse_step": {"us": round(t_sparse * 1e3, 1),
                         "gb_per_s": round(sparse_bytes / (t_sparse * 1e-3) / 1e9, 1),
                         "bytes": sparse_bytes},
+        "block_update": {"us_graph": round(t_bup * 1e3, 2), "us_eager_calls": round(t_bup_eager * 1e3, 1),
+                         "rows": Bq * HQq, "entries_per_row": 2048, "block_size": 16},
         "indexer": {"bf16_us": round(t_ix16 * 1e3, 1),
                     "bf16_gb_per_s": round((Bq * (Lq + 1) * 64 * 2 + ix_scores_bytes) / (t_ix16 * 1e-3) / 1e9, 1),
                     "fp8_us": round(t_ix8 * 1e3, 1),

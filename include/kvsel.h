@@ -320,6 +320,34 @@ int kvsel_block_aggregate_ex(const float* scores, int64_t score_stride, const in
                              int32_t num_heads, int32_t max_seq_len, int32_t block_size, int32_t mode, float param,
                              float* out, int64_t out_stride, void* stream);
 
+/* kvsel_block_update: per-block metadata from one decode step's selection
+ * ([OFFLOAD] §5.1: a float score accumulator and an int32 last-update stamp,
+ * 8 bytes per block, updated by walking the blocks each step selected).  The
+ * two live side by side in one kvsel_block_meta record, so an update touches
+ * one cache line per block.  For row r and every block b holding at least one
+ * listed position j (j / block_size = b) of idx[r][0 .. counts[r]):
+ *   meta[r][b].score = meta[r][b].score * decay^(step - meta[r][b].stamp)
+ *                      + sum of values[r][i] over the listed positions i of
+ *                        block b (values NULL: 1 each)
+ *   meta[r][b].stamp = step
+ * Blocks without a listed position are not touched: the stamp makes the decay
+ * lazy.  Lists are ascending among their non-negative entries; negative
+ * entries are ignored.  meta [rows][meta_stride] records, meta_stride >= max
+ * block index + 1 (a precondition); values [rows][values_stride] aligned with
+ * idx (e.g. the probabilities that kvsel_sparse_attn emits for the same
+ * lists); counts[r] <= max_count (a precondition).
+ * Errors: INVALID (NULL pointers, rows <= 0, block_size <= 0, a stride
+ * smaller than max_count), UNSUPPORTED (rows > 65535), HIP.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  float score;
+  int32_t stamp;
+} kvsel_block_meta;
+
+int kvsel_block_update(const int32_t* idx, int64_t idx_stride, const int32_t* counts, int32_t rows,
+                       int32_t max_count, const float* values, int64_t values_stride, int32_t block_size,
+                       int32_t step, float decay, kvsel_block_meta* meta, int64_t meta_stride, void* stream);
+
 /* kvsel_select_threshold: absolute-threshold selection across requests
  * ([OFFLOAD] §3.2): per row r, the positions j < lengths[r] with
  * scores[r][j] >= threshold, ascending, and their count.  out_stride >= max_len.

@@ -43,6 +43,7 @@ __all__ = [
     "block_top_p_mean",
     "block_fraction_above",
     "block_all_cold",
+    "block_update",
     "select_threshold",
     "select_keep",
     "streaming_keep",
@@ -244,6 +245,30 @@ def block_all_cold(scores: np.ndarray, length: int, block_size: int, threshold: 
     (only all-cold blocks may be evicted, [EVICT] §5.1)."""
     return np.array([float(all(x < threshold for x in scores[s:min(s + block_size, length)]))
                      for s in range(0, length, block_size)])
+
+
+def block_update(score: np.ndarray, stamp: np.ndarray, index_list, values, block_size: int, step: int,
+                 decay: float = 1.0):
+    """Per-block metadata of one decode step ([OFFLOAD] §5.1): every block keeps
+    a score accumulator and the step of its last update, and each step walks
+    the blocks its selection touched.  A touched block first ages its score by
+    decay per step since its stamp (the stamp makes the exponential decay of
+    [OFFLOAD] §2.1 lazy), then adds the weights of its selected positions
+    (``values`` aligned with ``index_list``; None weighs each position 1), and
+    takes the current step as its stamp.  Negative list entries are padding.
+    Returns new (score, stamp) arrays; untouched blocks keep both."""
+    score = np.array(score, dtype=np.float64)
+    stamp = np.array(stamp, dtype=np.int64)
+    add = {}
+    for i, j in enumerate(index_list):
+        if j < 0:
+            continue
+        b = int(j) // block_size
+        add[b] = add.get(b, 0.0) + (1.0 if values is None else float(values[i]))
+    for b, s in add.items():
+        score[b] = score[b] * decay ** (step - stamp[b]) + s
+        stamp[b] = step
+    return score, stamp
 
 
 def select_threshold(scores: np.ndarray, n: int, threshold: float) -> np.ndarray:

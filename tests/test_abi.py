@@ -255,6 +255,18 @@ def test_variant_validation():
     assert thr(FAKE, 100, FAKE, 0, 100, 0.5, FAKE, 100, FAKE, None) == K.KVSEL_ERR_INVALID
 
 
+def test_block_update_validation():
+    lib = K.library()
+    f = lib.kvsel_block_update
+    assert f(None, 8, FAKE, 1, 8, None, 0, 16, 1, 1.0, FAKE, 4, None) == K.KVSEL_ERR_INVALID
+    assert f(FAKE, 8, FAKE, 1, 8, None, 0, 0, 1, 1.0, FAKE, 4, None) == K.KVSEL_ERR_INVALID     # block
+    assert f(FAKE, 8, FAKE, 0, 8, None, 0, 16, 1, 1.0, FAKE, 4, None) == K.KVSEL_ERR_INVALID     # rows
+    assert f(FAKE, 7, FAKE, 1, 8, None, 0, 16, 1, 1.0, FAKE, 4, None) == K.KVSEL_ERR_INVALID     # stride
+    assert f(FAKE, 8, FAKE, 1, 8, FAKE, 7, 16, 1, 1.0, FAKE, 4, None) == K.KVSEL_ERR_INVALID     # values
+    assert f(FAKE, 8, FAKE, 1, 8, None, 0, 16, 1, 1.0, None, 4, None) == K.KVSEL_ERR_INVALID
+    assert f(FAKE, 8, FAKE, 65536, 8, None, 0, 16, 1, 1.0, FAKE, 4, None) == K.KVSEL_ERR_UNSUPPORTED
+
+
 def test_union_validation():
     lib = K.library()
     u = lib.kvsel_union_keep

@@ -102,3 +102,47 @@ def test_select_threshold_rows():
         n = int(cnt[r])
         assert idx[r, :n].cpu().numpy().tolist() == want.tolist()
         assert (idx[r, n:] == -5).all()
+
+
+@pytest.mark.parametrize("bs,decay,weighted", [(16, 0.9, True), (64, 1.0, False), (1, 0.5, True)])
+def test_block_update_over_steps(bs, decay, weighted):
+    """kvsel_block_update over 6 steps of fresh ascending lists (ragged counts,
+    an empty row, a row of padding only, -1 entries inside lists): stamps
+    exact, scores within 1e-5 relative of the oracle, records past the last
+    block untouched."""
+    K = _K()
+    note(f"block_update bs={bs} decay={decay} weighted={weighted}")
+    rng = np.random.default_rng(300 + bs)
+    L = 3000
+    nb = -(-L // bs)
+    counts_base = [0, 1, 2048, 5, 777, 40]
+    rows, stride = len(counts_base), 2048 + 16
+    sc_o = [np.zeros(nb) for _ in range(rows)]
+    st_o = [np.zeros(nb, dtype=np.int64) for _ in range(rows)]
+    meta = K.block_meta(rows, nb + 3)
+    score, stamp = K.block_meta_views(meta)
+    for step in range(1, 7):
+        idx = np.full((rows, stride), -1, dtype=np.int32)
+        vals = np.full((rows, stride), 7.0, dtype=np.float32)
+        cnt = np.zeros(rows, dtype=np.int32)
+        for r, c in enumerate(counts_base):
+            sel = np.sort(rng.choice(L, size=c, replace=False)).astype(np.int32)
+            if r == 5:
+                lst = np.full(c, -1, dtype=np.int32)              # padding only
+            else:
+                lst = np.insert(sel, rng.integers(0, c + 1, size=min(c, 9)), -1) if c else sel
+            idx[r, :len(lst)] = lst
+            vals[r, :len(lst)] = rng.random(len(lst))
+            cnt[r] = len(lst)
+        ti, tc = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+        tv = torch.from_numpy(vals).cuda() if weighted else None
+        K.block_update(ti, tc, bs, step, meta, tv, decay)
+        for r in range(rows):
+            lst = idx[r, :cnt[r]]
+            sc_o[r], st_o[r] = O.block_update(sc_o[r], st_o[r], lst, vals[r, :cnt[r]] if weighted else None, bs,
+                                              step, decay)
+    torch.cuda.synchronize()
+    for r in range(rows):
+        assert stamp[r, :nb].cpu().numpy().tolist() == st_o[r].tolist()
+        assert max_rel(f64(score[r, :nb]), sc_o[r]) < 1e-5
+        assert score[r, nb:].abs().sum().item() == 0 and stamp[r, nb:].abs().sum().item() == 0

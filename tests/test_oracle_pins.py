@@ -514,6 +514,30 @@ def test_block_variants_limits_and_hand_values():
     assert O.select_threshold(sc, 5, 2.0).tolist() == []
 
 
+def test_block_update_hand_example_lazy_decay_and_counts():
+    # blocks of 4; positions 1, 2 | 5 | 12, 13 with weights; block 2 untouched
+    sc, st = O.block_update([1.0, 2.0, 3.0, 4.0], [0, 1, 0, 2], [1, 2, -1, 5, 12, 13],
+                            [0.1, 0.2, 9.0, 0.3, 0.4, 0.5], 4, 3, 0.5)
+    np.testing.assert_allclose(sc, [1.0 * 0.125 + 0.3, 2.0 * 0.25 + 0.3, 3.0, 4.0 * 0.5 + 0.9])
+    assert st.tolist() == [3, 3, 0, 3]
+    # lazy ageing = eager ageing of every block at every step, read out at the end
+    rng = np.random.default_rng(5)
+    nb, bs, d = 6, 8, 0.8
+    lazy_s, lazy_t = np.zeros(nb), np.zeros(nb, dtype=np.int64)
+    eager = np.zeros(nb)
+    for step in range(1, 12):
+        lst = np.sort(rng.choice(nb * bs, size=7, replace=False))
+        w = rng.random(7)
+        lazy_s, lazy_t = O.block_update(lazy_s, lazy_t, lst, w, bs, step, d)
+        eager *= d
+        np.add.at(eager, lst // bs, w)
+    np.testing.assert_allclose(lazy_s * d ** (11 - lazy_t), eager, rtol=1e-12)
+    # decay 1, unit weights: the hit count of every block
+    lst = np.sort(rng.choice(64, size=20, replace=False))
+    sc, _ = O.block_update(np.zeros(8), np.zeros(8, dtype=np.int64), lst, None, 8, 1)
+    assert sc.tolist() == np.bincount(lst // 8, minlength=8).astype(float).tolist()
+
+
 def test_union_keep_hand_example_and_library_union():
     assert O.union_keep([[3, 1, -1], [1, 7], []]).tolist() == [1, 3, 7]
     sets = [rng.integers(-3, 50, size=int(n)) for n in rng.integers(0, 30, size=5)]
