@@ -262,8 +262,10 @@ def long_context_workload(torch, K, synth, args) -> dict:
     step_rlens = [torch.full((Bq * HQq,), Lq + s + 1, dtype=torch.int32, device="cuda") for s in range(steps)]
     kv_i_s = [K.PagedKV(kit.k_pages, None, kit.block_table, ls, 16, cap) for ls in step_lens]
     kv_f_s = [K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, ls, 16, cap) for ls in step_lens]
-    scores = torch.empty((Bq, HQq, cap), device="cuda")
-    srows = scores.view(Bq * HQq, cap)
+    # score rows padded to a multiple of 64 positions: 16-byte aligned rows
+    # whatever the number of steps (the score stores are 16-byte vectors)
+    scores = torch.empty((Bq, HQq, -(-cap // 64) * 64), device="cuda")
+    srows = scores.view(Bq * HQq, scores.shape[-1])
     keep = torch.empty((Bq * HQq, 2048), dtype=torch.int32, device="cuda")
     kcnt = torch.empty((Bq * HQq,), dtype=torch.int32, device="cuda")
     out = torch.empty((Bq, HQq, 128), device="cuda")
@@ -305,6 +307,17 @@ def long_context_workload(torch, K, synth, args) -> dict:
     t_bup = timed(torch, g_bup.replay, 5) / 10
     t_bup_eager = timed(torch, lambda: K.block_update(keep, kcnt, 16, 1, bmeta, sp2, 0.9), 10)
     del sprobs, sp2, bmeta, g_bup
+    # the offloading layer's sizing: 256 requests x 2000 blocks of metadata,
+    # each step's top-512 blocks per request (block ids, block size 1)
+    gen = torch.Generator().manual_seed(77)
+    oi = torch.stack([torch.sort(torch.randperm(2000, generator=gen)[:512])[0] for _ in range(256)])
+    oi = oi.to(torch.int32).cuda()
+    oc = torch.full((256,), 512, dtype=torch.int32, device="cuda")
+    ov = torch.rand((256, 512), generator=gen).cuda()
+    ometa = K.block_meta(256, 2000)
+    g_o = capture(torch, lambda: [K.block_update(oi, oc, 1, 1, ometa, ov, 0.9) for _ in range(10)])
+    t_bup_o = timed(torch, g_o.replay, 5) / 10
+    del oi, oc, ov, ometa, g_o
 
     # the same indexer with its keys and queries stored as FP8 E4M3
     kv_i8 = K.PagedKV(kit.k_pages.to(torch.float8_e4m3fn), None, kit.block_table, kv_i_s[0].seq_lens, 16, cap)
@@ -371,7 +384,9 @@ def long_context_workload(torch, K, synth, args) -> dict:
                         "gb_per_s": round(sparse_bytes / (t_sparse * 1e-3) / 1e9, 1),
                         "bytes": sparse_bytes},
         "block_update": {"us_graph": round(t_bup * 1e3, 2), "us_eager_calls": round(t_bup_eager * 1e3, 1),
-                         "rows": Bq * HQq, "entries_per_row": 2048, "block_size": 16},
+                         "rows": Bq * HQq, "entries_per_row": 2048, "block_size": 16,
+                         "offload_sizing_us_graph": round(t_bup_o * 1e3, 2),
+                         "offload_sizing": "256 requests x 2000 blocks, top-512 blocks each"},
         "indexer": {"bf16_us": round(t_ix16 * 1e3, 1),
                     "bf16_gb_per_s": round((Bq * (Lq + 1) * 64 * 2 + ix_scores_bytes) / (t_ix16 * 1e-3) / 1e9, 1),
                     "fp8_us": round(t_ix8 * 1e3, 1),

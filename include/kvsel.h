@@ -104,6 +104,10 @@ typedef struct {
  *          j >= L_b are left untouched.  probs_stride >= max_seq_len.
  *   cum    [num_seqs][num_kv_heads][cum_stride] f32, read and written, or
  *          NULL.  Needs emit = PROBS.  cum_stride >= max_seq_len.
+ *          probs and cum rows that are 16-byte aligned (base aligned, stride
+ *          a multiple of 4) take 16-byte stores; other layouts are accepted
+ *          and take 4-byte stores, about twice as slow when the scores
+ *          dominate the traffic (the logits mode of an indexer).
  *   workspace: >= kvsel_decode_workspace_bytes(kv, num_q_heads,
  *          probs != NULL || cum == NULL) bytes of device memory, 256-byte
  *          aligned, contents ignored.
