@@ -39,7 +39,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kStage = 256;             // keys staged per chunk (16 tiles)
+#ifndef KVSEL_VOTE_STAGE
+#define KVSEL_VOTE_STAGE 256  // keys staged per chunk (16 tiles)
+#endif
+constexpr int kStage = KVSEL_VOTE_STAGE;
 constexpr int kTiles = kStage / 16;
 constexpr int kMaxHalo = 8;             // pass 2: extra keys on each side = the pool radius (<= 8)
 #ifndef KVSEL_VOTE_WGS
