@@ -243,8 +243,29 @@ __global__ __launch_bounds__(kThreads) void block_update_kernel(
     if (jk >= 0) break;
   }
   if (k >= 0 && block_of(jk) == blk) return;             // not the block's first entry
+  // The block's entries, summed in list order: eight LDS entries per round
+  // (independent reads, one latency per round), then one at a time past the
+  // staged range.
   float sum = 0.f;
-  for (int t = i; t < n; ++t) {
+  int t = i;
+  bool done = false;
+  for (; !done && t + 8 <= lim; t += 8) {
+    int jj[8];
+    float vv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      jj[u] = sidx[t + u - i0];
+      vv[u] = sval[t + u - i0];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (!done && jj[u] >= 0) {
+        if (block_of(jj[u]) != blk) done = true;
+        else sum += vv[u];
+      }
+    }
+  }
+  for (; !done && t < n; ++t) {
     const bool in_lds = t < lim;
     const int jt = in_lds ? sidx[t - i0] : li[t];
     if (jt < 0) continue;
