@@ -6,7 +6,8 @@ benchmark times, on outputs the float64 oracle can compute one by one:
   * 128K long-context case (B=4, L=131072, 32 / 8 heads): the SnapKV vote
     and its top-4096, the indexer scores and their top-2048, sparse attention
     over them, and dense decode; sampled rows in full, every keep set against
-    the oracle's selection on the GPU's own scores for sampled rows."""
+    the oracle's selection on the GPU's own scores for sampled rows, and the
+    per-block score / stamp records of the sparse step's selection."""
 import numpy as np
 import pytest
 import torch
@@ -100,7 +101,14 @@ def test_long_context_128k_full_size_sampled():
     K.select_keep(srows, lens.repeat_interleave(Hq).to(torch.int32), L + 1, 0, 0, None, 2048, sk, sc)
     kvf = K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, lens, 16, L + 1)
     sout = torch.empty((B, Hq, 128), device="cuda")
-    K.sparse_attn(kvf, cfg["q_dec"][0], Hq, sk.view(B, Hq, 2048), sc.view(B, Hq), 2048, cfg["scale"], sout)
+    sprobs = torch.empty((B, Hq, 2048), device="cuda")
+    K.sparse_attn(kvf, cfg["q_dec"][0], Hq, sk.view(B, Hq, 2048), sc.view(B, Hq), 2048, cfg["scale"], sout, sprobs)
+    # per-block records of the step's selection (blocks of 16), two steps
+    n_blk = -(-(L + 1) // 16)
+    meta = K.block_meta(B * Hq, n_blk)
+    K.block_update(sk, sc, 16, 1, meta, sprobs.view(B * Hq, 2048), 0.9)
+    K.block_update(sk, sc, 16, 3, meta, sprobs.view(B * Hq, 2048), 0.9)
+    m_score, m_stamp = K.block_meta_views(meta)
     # (iii) dense decode over the same cache
     kvd = K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, kvt.seq_lens, 16, L)
     dout = torch.empty((B, Hq, 128), device="cuda")
@@ -126,7 +134,13 @@ def test_long_context_128k_full_size_sampled():
         r = b * Hq + h
         assert sk[r, :int(sc[r])].cpu().numpy().tolist() == sel.tolist()
         Kl, Vl = logical_kv_rows(kvt.k_pages, kvt.v_pages, kvt.block_table, b, h // 4, L + 1)
-        so, _ = O.sparse_attention(f64(cfg["q_dec"][0, b, h])[None, :], Kl, Vl, [sel], cfg["scale"])
+        so, sp = O.sparse_attention(f64(cfg["q_dec"][0, b, h])[None, :], Kl, Vl, [sel], cfg["scale"])
         assert rel_l2(f64(sout[b, h]), so[0]) < OUT_TOL
+        pg = f64(sprobs[b, h])
+        assert max_rel(pg, sp[0]) < SCORE_TOL
+        bs_o, bt_o = O.block_update(np.zeros(n_blk), np.zeros(n_blk, dtype=np.int64), sel, pg, 16, 1, 0.9)
+        bs_o, bt_o = O.block_update(bs_o, bt_o, sel, pg, 16, 3, 0.9)
+        assert m_stamp[r].cpu().numpy().tolist() == bt_o.tolist()
+        assert max_rel(f64(m_score[r]), bs_o) < 1e-5
         dr = O.decode_attention(f64(cfg["q_dec"][0, b, h])[None, :], Kl[:, :L], Vl[:, :L], cfg["scale"])
         assert rel_l2(f64(dout[b, h]), dr["out"][0]) < OUT_TOL
