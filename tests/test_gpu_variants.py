@@ -104,18 +104,22 @@ def test_select_threshold_rows():
         assert (idx[r, n:] == -5).all()
 
 
-@pytest.mark.parametrize("bs,decay,weighted", [(16, 0.9, True), (64, 1.0, False), (1, 0.5, True)])
+@pytest.mark.parametrize("bs,decay,weighted", [(16, 0.9, True), (64, 1.0, False), (1, 0.5, True), (5, 0.7, True)])
 def test_block_update_over_steps(bs, decay, weighted):
     """kvsel_block_update over 6 steps of fresh ascending lists (ragged counts,
-    an empty row, a row of padding only, -1 entries inside lists): stamps
-    exact, scores within 1e-5 relative of the oracle, records past the last
-    block untouched."""
+    an empty row, a row of padding only, -1 entries inside lists, a block
+    whose entries straddle a padding run past the workgroup's staged range,
+    a block size that is not a power of two): stamps exact, scores within
+    1e-5 relative of the oracle, records past the last block untouched."""
     K = _K()
     note(f"block_update bs={bs} decay={decay} weighted={weighted}")
     rng = np.random.default_rng(300 + bs)
     L = 3000
     nb = -(-L // bs)
-    counts_base = [0, 1, 2048, 5, 777, 40]
+    counts_base = [0, 1, 2048, 5, 777, 40, 354]
+    # row 6: entry 250 opens a block, 100 padding entries, then two more
+    # entries of the same block (at 351, 352: past the 320 staged entries)
+    straddle = np.array([-1] * 250 + [320] + [-1] * 100 + [321, 322] + [2999], dtype=np.int32)
     rows, stride = len(counts_base), 2048 + 16
     sc_o = [np.zeros(nb) for _ in range(rows)]
     st_o = [np.zeros(nb, dtype=np.int64) for _ in range(rows)]
@@ -129,6 +133,8 @@ def test_block_update_over_steps(bs, decay, weighted):
             sel = np.sort(rng.choice(L, size=c, replace=False)).astype(np.int32)
             if r == 5:
                 lst = np.full(c, -1, dtype=np.int32)              # padding only
+            elif r == 6:
+                lst = straddle
             else:
                 lst = np.insert(sel, rng.integers(0, c + 1, size=min(c, 9)), -1) if c else sel
             idx[r, :len(lst)] = lst
