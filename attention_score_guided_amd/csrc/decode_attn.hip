@@ -925,6 +925,7 @@ __global__ __launch_bounds__(kThreads) void decode_logits_mfma(PartialParams p) 
   constexpr int QB = 4;                      // K tiles per load batch
   constexpr int GTL = 16 * NCT;
   __shared__ int page_lds[KVSEL_MAX_CHUNK / 16 + 2];
+  __shared__ float lg_stage[kWaves][16 * 16];   // per wave: one tile, [head slot][key]
   const int C = p.chunk;
   const int chunk_id = blockIdx.x;
   const int kvh = blockIdx.y / p.hgroups;
@@ -1002,16 +1003,35 @@ __global__ __launch_bounds__(kThreads) void decode_logits_mfma(PartialParams p) 
           for (int u = 0; u < NU; ++u)
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[t][u], qb[ct][u], acc, 0, 0, 0);
           const int hh = ct * 16 + col;
-          if (hh < n_heads) {
-            float* lg = p.logits + ((size_t)b * p.num_q_heads + h0 + hh) * p.logits_stride + start;
-            if (vec) {
+          if (vec) {
+            if (hh < n_heads) {
+              float* lg = p.logits + ((size_t)b * p.num_q_heads + h0 + hh) * p.logits_stride + start;
               *reinterpret_cast<float4*>(lg + k0) =
                   make_float4(acc[0] * p.scale, acc[1] * p.scale, acc[2] * p.scale, acc[3] * p.scale);
-            } else {
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (k0 + i < n_keys) lg[k0 + i] = acc[i] * p.scale;
             }
+          } else {
+            // Rows that are not 16-byte aligned, and the chunk's ragged end:
+            // the tile passes through this wave's LDS slice so that a store
+            // instruction writes runs of 16 consecutive keys (4 heads x 16
+            // keys) instead of 4-key pieces of 16 heads.  LDS operations of
+            // one wave complete in order; the barriers keep the compiler from
+            // moving the reads above the writes or the next writes above them.
+            float* sl = lg_stage[wave];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sl[col * 16 + grp * 4 + i] = acc[i] * p.scale;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int key = wbase + (t0 + t) * 16 + col;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int hl = r * 4 + grp;
+              if (ct * 16 + hl < n_heads && key < n_keys)
+                p.logits[((size_t)b * p.num_q_heads + h0 + ct * 16 + hl) * p.logits_stride + start + key] =
+                    sl[hl * 16 + col];
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
           }
         }
       }

@@ -106,8 +106,8 @@ typedef struct {
  *          NULL.  Needs emit = PROBS.  cum_stride >= max_seq_len.
  *          probs and cum rows that are 16-byte aligned (base aligned, stride
  *          a multiple of 4) take 16-byte stores; other layouts are accepted
- *          and take 4-byte stores, about twice as slow when the scores
- *          dominate the traffic (the logits mode of an indexer).
+ *          and take 4-byte stores (in the bf16 logits-only mode of an
+ *          indexer, runs of 16 keys staged through LDS: ~25% slower there).
  *   workspace: >= kvsel_decode_workspace_bytes(kv, num_q_heads,
  *          probs != NULL || cum == NULL) bytes of device memory, 256-byte
  *          aligned, contents ignored.
