@@ -47,6 +47,7 @@ __global__ __launch_bounds__(kIThreads) void indexer_fp8_kernel(IndexerParams p)
   constexpr int QB = 4;               // tiles whose loads are issued together
   constexpr int GTL = 16 * NCT;
   __shared__ int page_lds[kIMaxChunk / 16 + 2];
+  __shared__ float sc_stage[kIWaves][16 * 16];   // per wave: one tile, [head slot][key]
   const int C = p.chunk;
   const int kvh = blockIdx.y / p.hgroups, hg = blockIdx.y % p.hgroups, b = blockIdx.z;
   const int L = p.seq_lens[b];
@@ -109,16 +110,32 @@ __global__ __launch_bounds__(kIThreads) void indexer_fp8_kernel(IndexerParams p)
 #pragma unroll
         for (int u = 0; u < NU; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ka[u], qb[ct][u], acc, 0, 0, 0);
         const int hh = ct * 16 + col;
-        if (hh < n_heads) {
-          float* out = p.scores + ((size_t)b * p.num_q_heads + h0 + hh) * p.stride + start;
-          if (vec) {
+        if (vec) {
+          if (hh < n_heads) {
+            float* out = p.scores + ((size_t)b * p.num_q_heads + h0 + hh) * p.stride + start;
             *reinterpret_cast<float4*>(out + k0) =
                 make_float4(acc[0] * p.scale, acc[1] * p.scale, acc[2] * p.scale, acc[3] * p.scale);
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (k0 + i < n_keys) out[k0 + i] = acc[i] * p.scale;
           }
+        } else {
+          // Unaligned rows and the chunk's ragged end: through this wave's
+          // LDS slice, so a store instruction writes runs of 16 consecutive
+          // keys (4 heads x 16 keys).  One wave's LDS operations complete in
+          // order; the barriers pin the compiler's ordering.
+          float* sl = sc_stage[wave];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sl[col * 16 + grp * 4 + i] = acc[i] * p.scale;
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          const int key = wbase + (t0 + t) * 16 + col;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int hl = r * 4 + grp;
+            if (ct * 16 + hl < n_heads && key < n_keys)
+              p.scores[((size_t)b * p.num_q_heads + h0 + ct * 16 + hl) * p.stride + start + key] = sl[hl * 16 + col];
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
         }
       }
     }
