@@ -87,19 +87,24 @@ def test_decode_all_outputs(case):
         assert torch.equal(cum[b, :, L:], cum0[b, :, L:])
 
 
-def test_decode_logits_mode_without_values():
-    """Indexer-style call: one KV head, G=32, d=64, raw logits, no V."""
+@pytest.mark.parametrize("G,extra", [(32, 0), (32, 1), (24, 2), (32, 3)])
+def test_decode_logits_mode_without_values(G, extra):
+    """Indexer-style call: one KV head, G query heads (24: a partial second
+    column tile), d=64, raw logits, no V; row strides that are not 16-byte
+    aligned take the staged store path, whose writes stay inside [0, L_b)."""
     K = _K()
-    c = _random_case(21, torch.bfloat16, 64, 32, 1, 16, [3000, 17, 1024])
+    note(f"logits mode G={G} stride extra={extra}")
+    c = _random_case(21, torch.bfloat16, 64, G, 1, 16, [3000, 17, 1024], extra_stride=extra)
     kv = K.PagedKV(c["kp"], None, c["bt"], c["lens"], 16, c["max_len"])
-    logits = torch.zeros((3, 32, c["stride"]), device="cuda")
-    K.decode_attn_scores(kv, c["q"], 32, 1.0, None, None, logits, K.EMIT_LOGITS)
+    logits = torch.full((3, G, c["stride"]), -7.0, device="cuda")
+    K.decode_attn_scores(kv, c["q"], G, 1.0, None, None, logits, K.EMIT_LOGITS)
     torch.cuda.synchronize()
     for b, L in enumerate([3000, 17, 1024]):
         Kl, _ = logical_kv(c["kp"], None, c["bt"], b, L)
         want = O.indexer_scores(f64(c["q"][b]), Kl[0])
         err = np.abs(f64(logits[b, :, :L]) - want).max() / np.abs(want).max()
         assert err < 1e-5
+        assert (logits[b, :, L:] == -7.0).all()
 
 
 def test_decode_cum_without_probs_uses_scratch_and_lse_only():
