@@ -919,13 +919,17 @@ void decode_partial_mfma(PartialParams p) {
 // Emit raw scale * q.k for every key and up to 32 query heads of a KV head
 // per workgroup: NCT 16-column B tiles of Q^T share each K tile, so the K
 // stream is read once for the whole group.  No softmax, no V, no LDS tile.
-template <int D, int NCT>
+// ALIGNED: every logits row is 16-byte aligned (the host checks the base and
+// the stride), so whole chunks take 16-byte stores; otherwise every tile is
+// written through a per-wave LDS slice as runs of 16 consecutive keys.  The
+// two are separate instantiations so the aligned one keeps its own code.
+template <int D, int NCT, bool ALIGNED>
 __global__ __launch_bounds__(kThreads) void decode_logits_mfma(PartialParams p) {
   constexpr int NU = D / 32;
   constexpr int QB = 4;                      // K tiles per load batch
   constexpr int GTL = 16 * NCT;
   __shared__ int page_lds[KVSEL_MAX_CHUNK / 16 + 2];
-  __shared__ float lg_stage[kWaves][16 * 16];   // per wave: one tile, [head slot][key]
+  __shared__ float lg_stage[ALIGNED ? 1 : kWaves][16 * 16];   // per wave: one tile, [head slot][key]
   const int C = p.chunk;
   const int chunk_id = blockIdx.x;
   const int kvh = blockIdx.y / p.hgroups;
@@ -960,8 +964,7 @@ __global__ __launch_bounds__(kThreads) void decode_logits_mfma(PartialParams p) 
   const int per_wave = C / kWaves;
   const int nt = per_wave / 16;
   const int wbase = wave * per_wave;
-  const bool vec = (p.logits_stride & 3) == 0 && (reinterpret_cast<uintptr_t>(p.logits) & 15) == 0 &&
-                   n_keys == C;
+  const bool vec = ALIGNED && n_keys == C;
   for (int t0 = 0; t0 < nt; t0 += QB) {
     bf16x8 kb[QB][NU];
     auto krow = [&](int key) -> const uint8_t* {
@@ -1003,19 +1006,25 @@ __global__ __launch_bounds__(kThreads) void decode_logits_mfma(PartialParams p) 
           for (int u = 0; u < NU; ++u)
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[t][u], qb[ct][u], acc, 0, 0, 0);
           const int hh = ct * 16 + col;
-          if (vec) {
+          if constexpr (ALIGNED) {
             if (hh < n_heads) {
               float* lg = p.logits + ((size_t)b * p.num_q_heads + h0 + hh) * p.logits_stride + start;
-              *reinterpret_cast<float4*>(lg + k0) =
-                  make_float4(acc[0] * p.scale, acc[1] * p.scale, acc[2] * p.scale, acc[3] * p.scale);
+              if (vec) {
+                *reinterpret_cast<float4*>(lg + k0) =
+                    make_float4(acc[0] * p.scale, acc[1] * p.scale, acc[2] * p.scale, acc[3] * p.scale);
+              } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if (k0 + i < n_keys) lg[k0 + i] = acc[i] * p.scale;
+              }
             }
           } else {
-            // Rows that are not 16-byte aligned, and the chunk's ragged end:
-            // the tile passes through this wave's LDS slice so that a store
-            // instruction writes runs of 16 consecutive keys (4 heads x 16
-            // keys) instead of 4-key pieces of 16 heads.  LDS operations of
-            // one wave complete in order; the barriers keep the compiler from
-            // moving the reads above the writes or the next writes above them.
+            // Rows that are not 16-byte aligned: the tile passes through this
+            // wave's LDS slice so that a store instruction writes runs of 16
+            // consecutive keys (4 heads x 16 keys) instead of 4-key pieces of
+            // 16 heads.  LDS operations of one wave complete in order; the
+            // barriers keep the compiler from moving the reads above the
+            // writes or the next writes above them.
             float* sl = lg_stage[wave];
 #pragma unroll
             for (int i = 0; i < 4; ++i) sl[col * 16 + grp * 4 + i] = acc[i] * p.scale;
@@ -1037,6 +1046,12 @@ __global__ __launch_bounds__(kThreads) void decode_logits_mfma(PartialParams p) 
       }
     }
   }
+}
+
+template <int D, int NCT>
+void launch_logits(bool aligned, dim3 grid, hipStream_t stream, const PartialParams& pp) {
+  if (aligned) hipLaunchKernelGGL((decode_logits_mfma<D, NCT, true>), grid, dim3(kThreads), 0, stream, pp);
+  else hipLaunchKernelGGL((decode_logits_mfma<D, NCT, false>), grid, dim3(kThreads), 0, stream, pp);
 }
 
 // ---- combine ----------------------------------------------------------------
@@ -1488,12 +1503,13 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     pp.chunk = lchunk;
     pp.n_chunks = (a.max_seq_len + lchunk - 1) / lchunk;
     const dim3 lgrid(pp.n_chunks, a.num_kv_heads * pp.hgroups, a.num_seqs);
+    const bool al = (pp.logits_stride & 3) == 0 && (reinterpret_cast<uintptr_t>(pp.logits) & 15) == 0;
     if (a.head_dim == 128) {
-      if (nct == 2) hipLaunchKernelGGL((decode_logits_mfma<128, 2>), lgrid, dim3(kThreads), 0, stream, pp);
-      else hipLaunchKernelGGL((decode_logits_mfma<128, 1>), lgrid, dim3(kThreads), 0, stream, pp);
+      if (nct == 2) launch_logits<128, 2>(al, lgrid, stream, pp);
+      else launch_logits<128, 1>(al, lgrid, stream, pp);
     } else {
-      if (nct == 2) hipLaunchKernelGGL((decode_logits_mfma<64, 2>), lgrid, dim3(kThreads), 0, stream, pp);
-      else hipLaunchKernelGGL((decode_logits_mfma<64, 1>), lgrid, dim3(kThreads), 0, stream, pp);
+      if (nct == 2) launch_logits<64, 2>(al, lgrid, stream, pp);
+      else launch_logits<64, 1>(al, lgrid, stream, pp);
     }
     return hipGetLastError();
   }

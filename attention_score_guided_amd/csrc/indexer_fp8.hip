@@ -40,14 +40,17 @@ struct IndexerParams {
   float scale;
 };
 
-template <int D, int NCT>
+// ALIGNED: every score row is 16-byte aligned (checked on the host), so whole
+// chunks take 16-byte stores; otherwise every tile goes through a per-wave
+// LDS slice and is written as runs of 16 consecutive keys.
+template <int D, int NCT, bool ALIGNED>
 __global__ __launch_bounds__(kIThreads) void indexer_fp8_kernel(IndexerParams p) {
   constexpr int NU = D / 32;          // k-steps of 32 channels
   constexpr int BPL = D / 4;          // bytes of a key row per lane (16 or 32)
   constexpr int QB = 4;               // tiles whose loads are issued together
   constexpr int GTL = 16 * NCT;
   __shared__ int page_lds[kIMaxChunk / 16 + 2];
-  __shared__ float sc_stage[kIWaves][16 * 16];   // per wave: one tile, [head slot][key]
+  __shared__ float sc_stage[ALIGNED ? 1 : kIWaves][16 * 16];   // per wave: one tile, [head slot][key]
   const int C = p.chunk;
   const int kvh = blockIdx.y / p.hgroups, hg = blockIdx.y % p.hgroups, b = blockIdx.z;
   const int L = p.seq_lens[b];
@@ -85,7 +88,7 @@ __global__ __launch_bounds__(kIThreads) void indexer_fp8_kernel(IndexerParams p)
   const int per_wave = C / kIWaves;
   const int nt = per_wave / 16;
   const int wbase = wave * per_wave;
-  const bool vec = (p.stride & 3) == 0 && (reinterpret_cast<uintptr_t>(p.scores) & 15) == 0 && n_keys == C;
+  const bool vec = ALIGNED && n_keys == C;
   for (int t0 = 0; t0 < nt; t0 += QB) {
     uint4 kr[QB][BPL / 16];
 #pragma unroll
@@ -110,15 +113,20 @@ __global__ __launch_bounds__(kIThreads) void indexer_fp8_kernel(IndexerParams p)
 #pragma unroll
         for (int u = 0; u < NU; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ka[u], qb[ct][u], acc, 0, 0, 0);
         const int hh = ct * 16 + col;
-        if (vec) {
+        if constexpr (ALIGNED) {
           if (hh < n_heads) {
             float* out = p.scores + ((size_t)b * p.num_q_heads + h0 + hh) * p.stride + start;
-            *reinterpret_cast<float4*>(out + k0) =
-                make_float4(acc[0] * p.scale, acc[1] * p.scale, acc[2] * p.scale, acc[3] * p.scale);
+            if (vec) {
+              *reinterpret_cast<float4*>(out + k0) =
+                  make_float4(acc[0] * p.scale, acc[1] * p.scale, acc[2] * p.scale, acc[3] * p.scale);
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (k0 + i < n_keys) out[k0 + i] = acc[i] * p.scale;
+            }
           }
         } else {
-          // Unaligned rows and the chunk's ragged end: through this wave's
-          // LDS slice, so a store instruction writes runs of 16 consecutive
+          // Unaligned rows: through this wave's LDS slice, so a store instruction writes runs of 16 consecutive
           // keys (4 heads x 16 keys).  One wave's LDS operations complete in
           // order; the barriers pin the compiler's ordering.
           float* sl = sc_stage[wave];
@@ -140,6 +148,12 @@ __global__ __launch_bounds__(kIThreads) void indexer_fp8_kernel(IndexerParams p)
       }
     }
   }
+}
+
+template <int D, int NCT>
+void launch_fp8(bool aligned, dim3 grid, hipStream_t stream, const IndexerParams& ip) {
+  if (aligned) hipLaunchKernelGGL((indexer_fp8_kernel<D, NCT, true>), grid, dim3(kIThreads), 0, stream, ip);
+  else hipLaunchKernelGGL((indexer_fp8_kernel<D, NCT, false>), grid, dim3(kIThreads), 0, stream, ip);
 }
 
 }  // namespace
@@ -169,12 +183,13 @@ hipError_t launch_indexer_fp8(const void* k_pages, const int32_t* block_table, c
     chunk /= 2;
   ip.chunk = chunk;
   const dim3 grid((max_seq_len + chunk - 1) / chunk, num_kv_heads * ip.hgroups, num_seqs);
+  const bool al = (ip.stride & 3) == 0 && (reinterpret_cast<uintptr_t>(ip.scores) & 15) == 0;
   if (head_dim == 128) {
-    if (nct == 2) hipLaunchKernelGGL((indexer_fp8_kernel<128, 2>), grid, dim3(kIThreads), 0, stream, ip);
-    else hipLaunchKernelGGL((indexer_fp8_kernel<128, 1>), grid, dim3(kIThreads), 0, stream, ip);
+    if (nct == 2) launch_fp8<128, 2>(al, grid, stream, ip);
+    else launch_fp8<128, 1>(al, grid, stream, ip);
   } else {
-    if (nct == 2) hipLaunchKernelGGL((indexer_fp8_kernel<64, 2>), grid, dim3(kIThreads), 0, stream, ip);
-    else hipLaunchKernelGGL((indexer_fp8_kernel<64, 1>), grid, dim3(kIThreads), 0, stream, ip);
+    if (nct == 2) launch_fp8<64, 2>(al, grid, stream, ip);
+    else launch_fp8<64, 1>(al, grid, stream, ip);
   }
   return hipGetLastError();
 }
