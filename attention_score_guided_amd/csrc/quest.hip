@@ -161,14 +161,25 @@ __global__ __launch_bounds__(kQThreads) void quest_bounds_kernel(BoundParams p) 
   const size_t sum_stride = (size_t)p.num_kv_heads * 2 * D * EB;
   const uint8_t* sbase = p.summary + (size_t)kvh * 2 * D * EB + seg * 16;
   float* brow = p.bounds + ((size_t)b * p.num_q_heads + h0) * p.bounds_stride;
-  for (int lp0 = p_begin + wave * RPW * U + r0; lp0 < p_end; lp0 += kQWaves * RPW * U) {
+  // The physical page ids of the next step are loaded while this step's
+  // summaries are in flight, so the loop carries one memory latency per step.
+  constexpr int kStep = kQWaves * RPW * U;
+  const int lp_first = p_begin + wave * RPW * U + r0;
+  int pg_next[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) pg_next[u] = lp_first < p_end ? bt[min(lp_first + u * RPW, p_end - 1)] : 0;
+  for (int lp0 = lp_first; lp0 < p_end; lp0 += kStep) {
     uint4 mnw[U], mxw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int lp = min(lp0 + u * RPW, p_end - 1);   // clamped: loads stay unconditional
-      const uint8_t* s = sbase + (size_t)bt[lp] * sum_stride;
+      // clamped page ids: the loads stay unconditional
+      const uint8_t* s = sbase + (size_t)pg_next[u] * sum_stride;
       mnw[u] = ld16_stream(s);
       mxw[u] = ld16_stream(s + D * EB);
+    }
+    if (lp0 + kStep < p_end) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) pg_next[u] = bt[min(lp0 + kStep + u * RPW, p_end - 1)];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
