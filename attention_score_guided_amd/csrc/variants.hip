@@ -203,8 +203,8 @@ __global__ __launch_bounds__(kThreads) void select_threshold_kernel(
 // them (long blocks, padding runs) continues from global memory.
 constexpr int kBUTail = 64;
 
-// kPow2: block_of (position -> block index) is (a shift for power-of-two block sizes,
-// which the usual 16 / 32 / 64 are, else a division).
+// kPow2: block_of (position -> block index) is a shift, for power-of-two
+// block sizes (the usual 16, 32 and 64); otherwise it is a division.
 template <bool kPow2>
 __global__ __launch_bounds__(kThreads) void block_update_kernel(
     const int32_t* __restrict__ idx, int64_t idx_stride, const int32_t* __restrict__ counts, int max_count,
