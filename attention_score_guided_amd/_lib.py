@@ -34,7 +34,7 @@ EXPORTED = (
     "kvsel_block_aggregate", "kvsel_select_keep", "kvsel_select_workspace_bytes",
     "kvsel_snapkv_vote", "kvsel_snapkv_workspace_bytes", "kvsel_sparse_attn",
     "kvsel_sparse_workspace_bytes", "kvsel_quest_summarize", "kvsel_quest_select",
-    "kvsel_quest_workspace_bytes", "kvsel_accumulate_ex", "kvsel_block_aggregate_ex", "kvsel_select_threshold", "kvsel_block_update",
+    "kvsel_quest_workspace_bytes", "kvsel_accumulate_ex", "kvsel_block_aggregate_ex", "kvsel_select_threshold", "kvsel_block_update", "kvsel_read_probe",
     "kvsel_union_keep", "kvsel_indexer_scores_fp8", "kvsel_h2o_step", "kvsel_h2o_workspace_bytes", "kvsel_set_sync_spin_limit",
     "kvsel_status_string", "kvsel_last_error",
 )
@@ -88,6 +88,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvsel_union_keep": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, P, I64, P, P]),
         "kvsel_indexer_scores_fp8": (ctypes.c_int, [D, P, I32, F, P, I64, P]),
         "kvsel_block_update": (ctypes.c_int, [P, I64, P, I32, I32, P, I64, I32, I32, F, P, I64, P]),
+        "kvsel_read_probe": (ctypes.c_int, [P, SZ, P, P]),
         "kvsel_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "kvsel_set_sync_spin_limit": (I32, [I32]),
         "kvsel_last_error": (ctypes.c_char_p, []),
@@ -430,3 +431,10 @@ def block_update(idx: torch.Tensor, counts: torch.Tensor, block_size: int, step:
         _ptr(idx, torch.int32, "idx"), stride, _ptr(counts, torch.int32, "counts"), rows, stride,
         _ptr(values, torch.float32, "values"), 0 if values is None else values.shape[-1], int(block_size),
         int(step), float(decay), _ptr(meta, torch.int32, "meta"), meta.shape[1], _stream(stream)))
+
+
+def read_probe(buf: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """kvsel_read_probe: one streaming read of the contiguous device tensor ``buf``;
+    ``out`` is a one-element int32 device tensor (written only on a sentinel fold)."""
+    _check(_LIB.kvsel_read_probe(_ptr(buf, None, "buf"), buf.numel() * buf.element_size(),
+                                 _ptr(out, torch.int32, "out"), _stream(stream)))

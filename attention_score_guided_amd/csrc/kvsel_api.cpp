@@ -452,6 +452,16 @@ int kvsel_block_aggregate_ex(const float* scores, int64_t score_stride, const in
                     "block_aggregate_ex launch");
 }
 
+int kvsel_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream) {
+  if (!buf || !out) return fail(KVSEL_ERR_INVALID, "NULL pointer argument");
+  if ((reinterpret_cast<uintptr_t>(buf) & 15) != 0 || bytes % 16 != 0)
+    return fail(KVSEL_ERR_INVALID, "buf must be 16-byte aligned and bytes a multiple of 16");
+  int st = check_device();
+  if (st != KVSEL_OK) return st;
+  if (bytes == 0) return KVSEL_OK;
+  return hip_status(kvsel::launch_read_probe(buf, bytes, out, static_cast<hipStream_t>(stream)), "read_probe launch");
+}
+
 int kvsel_block_update(const int32_t* idx, int64_t idx_stride, const int32_t* counts, int32_t rows,
                        int32_t max_count, const float* values, int64_t values_stride, int32_t block_size,
                        int32_t step, float decay, kvsel_block_meta* meta, int64_t meta_stride, void* stream) {

@@ -86,6 +86,8 @@ hipError_t launch_block_update(const int32_t* idx, int64_t idx_stride, const int
                                int max_count, const float* values, int64_t values_stride, int block_size,
                                int step, float decay, kvsel_block_meta* meta, int64_t meta_stride, hipStream_t stream);
 
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* out, hipStream_t stream);
+
 size_t select_workspace_bytes(int rows, int max_len, int mode);
 
 hipError_t launch_select(const float* scores, int64_t stride, const int32_t* lengths, int rows,

@@ -207,6 +207,17 @@ def counters_mode(torch, K, synth) -> int:
     return 0
 
 
+def read_probe(torch, K) -> float:
+    """GB/s of the library's streaming read probe over 4 GiB on the current
+    GPU (non-temporal 16-byte loads, nothing written), best of three averages
+    of 5 runs."""
+    x = torch.zeros(1 << 30, dtype=torch.int32, device="cuda")
+    o = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ms = min(timed(torch, lambda: K.read_probe(x, o), 5) for _ in range(3))
+    del x, o
+    return (1 << 32) / (ms * 1e-3) / 1e9
+
+
 def timed(torch, fn, reps: int, warmup: int = 1) -> float:
     """Average milliseconds of ``fn`` over ``reps`` runs (HIP events on the
     current stream, after ``warmup`` untimed runs)."""
@@ -852,6 +863,7 @@ def main() -> int:
     mass = float(bufs["cum"][0].double().sum()) / B / (args.steps + args.warmup)
     kept = int(bufs["keep_cnt"].sum())
 
+    probe = read_probe(torch, K)
     kv_step = LAYERS * kv_bytes_per_layer()
     value = kv_step / (ms_step * 1e-3) / 1e9
     alg = decode_algorithmic_bytes()
@@ -886,7 +898,11 @@ def main() -> int:
         "extra": {"decode_share_of_step": round(dec_avg_ms * LAYERS / ms_step, 4),
                   "aggregate_select_us_per_step": round(sel_avg_ms * 1e3, 2),
                   "launch": "hip_graph" if args.graph else "eager",
-                  "prob_mass_per_seq_layer_step": round(mass, 4), "blocks_kept": kept},
+                  "prob_mass_per_seq_layer_step": round(mass, 4), "blocks_kept": kept,
+                  "hbm_read_probe_gb_per_s": round(probe, 1),
+                  "read_probe": "kvsel_read_probe over 4 GiB on the same GPU (16-byte streaming loads, "
+                                "nothing written), after the timed region; context for the 8 TB/s peak, "
+                                "not used in value or frac"},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the float64 oracle on a sample")

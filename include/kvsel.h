@@ -493,6 +493,18 @@ size_t kvsel_h2o_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads, 
 int32_t kvsel_set_sync_spin_limit(int32_t iterations);
 
 /* Name of a status code (static string). */
+/* kvsel_read_probe: one streaming read of `bytes` bytes of device memory
+ * with non-temporal 16-byte loads, sixteen workgroups per compute unit.  It gives the
+ * read bandwidth reachable on this GPU, the reference for the HBM-bound
+ * calls above (the vendor's peak is a pin rate).  Timing is the caller's.
+ * The loads are folded with XOR; `out` (one uint32 of device memory) is
+ * written only if the fold equals 0x9E3779B9, so with zeroed data nothing is
+ * written.  buf 16-byte aligned, bytes a multiple of 16.
+ * Errors: INVALID (NULL pointers, misaligned buf, bytes not a multiple of
+ * 16), HIP.
+ * ------------------------------------------------------------------------ */
+int kvsel_read_probe(const void* buf, size_t bytes, uint32_t* out, void* stream);
+
 const char* kvsel_status_string(int status);
 
 /* The message of the last failed call on this thread ("" if none). */

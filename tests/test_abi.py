@@ -267,6 +267,15 @@ def test_block_update_validation():
     assert f(FAKE, 8, FAKE, 65536, 8, None, 0, 16, 1, 1.0, FAKE, 4, None) == K.KVSEL_ERR_UNSUPPORTED
 
 
+def test_read_probe_validation():
+    lib = K.library()
+    f = lib.kvsel_read_probe
+    assert f(None, 1024, FAKE, None) == K.KVSEL_ERR_INVALID
+    assert f(FAKE, 1024, None, None) == K.KVSEL_ERR_INVALID
+    assert f(FAKE + 4, 1024, FAKE, None) == K.KVSEL_ERR_INVALID       # misaligned
+    assert f(FAKE, 1000, FAKE, None) == K.KVSEL_ERR_INVALID           # not a multiple of 16
+
+
 def test_union_validation():
     lib = K.library()
     u = lib.kvsel_union_keep
