@@ -76,15 +76,19 @@ struct SummaryParams {
   int num_kv_heads, page_log2, max_pages, first_page;
 };
 
-template <bool BF16, int D>
+// HEAD_MAJOR: blockIdx.x is the KV head, so consecutive workgroups read the
+// head slices of the same pages, one contiguous run of the page layout
+// (same-box A/B on the whole 128K cache: 231.7 -> 221.7 us); page-major
+// grids serve page counts beyond the grid's y limit.
+template <bool BF16, int D, bool HEAD_MAJOR>
 __global__ __launch_bounds__(kQThreads) void quest_summary_kernel(SummaryParams p) {
   constexpr int EB = BF16 ? 2 : 4;
   constexpr int EPL = 16 / EB;       // channels per lane segment
   constexpr int LPR = D / EPL;       // lanes per key row
   constexpr int RPW = kWave / LPR;   // key rows per wave load
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int lp = p.first_page + blockIdx.x * kQWaves + wave;   // the grid starts at first_page
-  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int lp = p.first_page + (HEAD_MAJOR ? blockIdx.y : blockIdx.x) * kQWaves + wave;  // from first_page
+  const int kvh = HEAD_MAJOR ? blockIdx.x : blockIdx.y, b = blockIdx.z;
   const int P = 1 << p.page_log2;
   if ((long long)(lp + 1) * P > p.seq_lens[b]) return;   // whole pages only
   const int pg = p.block_table[(size_t)b * p.max_pages + lp];
@@ -245,6 +249,21 @@ hipError_t launch_bounds_d(const BoundParams& bp, int gt, dim3 grid, hipStream_t
   return hipGetLastError();
 }
 
+template <bool HEAD_MAJOR>
+void launch_summary(const QuestArgs& a, dim3 grid, hipStream_t stream, const SummaryParams& sp) {
+  if (a.bf16) {
+    if (a.head_dim == 128)
+      hipLaunchKernelGGL((quest_summary_kernel<true, 128, HEAD_MAJOR>), grid, dim3(kQThreads), 0, stream, sp);
+    else
+      hipLaunchKernelGGL((quest_summary_kernel<true, 64, HEAD_MAJOR>), grid, dim3(kQThreads), 0, stream, sp);
+  } else {
+    if (a.head_dim == 128)
+      hipLaunchKernelGGL((quest_summary_kernel<false, 128, HEAD_MAJOR>), grid, dim3(kQThreads), 0, stream, sp);
+    else
+      hipLaunchKernelGGL((quest_summary_kernel<false, 64, HEAD_MAJOR>), grid, dim3(kQThreads), 0, stream, sp);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quest_summary(const QuestArgs& a, void* summary, int first_page, hipStream_t stream) {
@@ -259,13 +278,13 @@ hipError_t launch_quest_summary(const QuestArgs& a, void* summary, int first_pag
   sp.first_page = first_page;
   const int max_whole = a.max_seq_len / a.page_size;
   if (max_whole <= first_page) return hipSuccess;   // no whole page from first_page on
-  const dim3 grid((max_whole - first_page + kQWaves - 1) / kQWaves, a.num_kv_heads, a.num_seqs);
-  if (a.bf16) {
-    if (a.head_dim == 128) hipLaunchKernelGGL((quest_summary_kernel<true, 128>), grid, dim3(kQThreads), 0, stream, sp);
-    else hipLaunchKernelGGL((quest_summary_kernel<true, 64>), grid, dim3(kQThreads), 0, stream, sp);
+  const int n_grp = (max_whole - first_page + kQWaves - 1) / kQWaves;
+  if (n_grp <= 65535) {
+    const dim3 grid(a.num_kv_heads, n_grp, a.num_seqs);
+    launch_summary<true>(a, grid, stream, sp);
   } else {
-    if (a.head_dim == 128) hipLaunchKernelGGL((quest_summary_kernel<false, 128>), grid, dim3(kQThreads), 0, stream, sp);
-    else hipLaunchKernelGGL((quest_summary_kernel<false, 64>), grid, dim3(kQThreads), 0, stream, sp);
+    const dim3 grid(n_grp, a.num_kv_heads, a.num_seqs);
+    launch_summary<false>(a, grid, stream, sp);
   }
   return hipGetLastError();
 }
