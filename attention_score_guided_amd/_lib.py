@@ -35,7 +35,7 @@ EXPORTED = (
     "kvsel_snapkv_vote", "kvsel_snapkv_workspace_bytes", "kvsel_sparse_attn",
     "kvsel_sparse_workspace_bytes", "kvsel_quest_summarize", "kvsel_quest_select",
     "kvsel_quest_workspace_bytes", "kvsel_accumulate_ex", "kvsel_block_aggregate_ex", "kvsel_select_threshold", "kvsel_block_update", "kvsel_read_probe",
-    "kvsel_union_keep", "kvsel_indexer_scores_fp8", "kvsel_h2o_step", "kvsel_h2o_workspace_bytes", "kvsel_set_sync_spin_limit",
+    "kvsel_union_keep", "kvsel_indexer_scores_fp8", "kvsel_h2o_step", "kvsel_h2o_workspace_bytes", "kvsel_set_sync_wait_us",
     "kvsel_status_string", "kvsel_last_error",
 )
 
@@ -90,7 +90,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvsel_block_update": (ctypes.c_int, [P, I64, P, I32, I32, P, I64, I32, I32, F, P, I64, P]),
         "kvsel_read_probe": (ctypes.c_int, [P, SZ, P, P]),
         "kvsel_status_string": (ctypes.c_char_p, [ctypes.c_int]),
-        "kvsel_set_sync_spin_limit": (I32, [I32]),
+        "kvsel_set_sync_wait_us": (I32, [I32]),
         "kvsel_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -176,9 +176,9 @@ def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
 
 
 # --------------------------------------------------------------------------
-def set_sync_spin_limit(iterations: int) -> int:
-    """kvsel_set_sync_spin_limit: returns the previous limit."""
-    r = int(_LIB.kvsel_set_sync_spin_limit(int(iterations)))
+def set_sync_wait_us(microseconds: int) -> int:
+    """kvsel_set_sync_wait_us: returns the previous bound (microseconds)."""
+    r = int(_LIB.kvsel_set_sync_wait_us(int(microseconds)))
     if r < 0:
         _check(r)
     return r

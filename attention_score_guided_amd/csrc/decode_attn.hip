@@ -102,7 +102,7 @@ struct PartialParams {
   unsigned long long* lse_post;  // [B][Hq][n_chunks][2] chunk lse tagged with epoch / ~epoch
   uint32_t* chunk_flag;          // [B][H_kv][n_chunks] 1 when the chunk fell back, else 0
   uint32_t epoch;
-  int spin_limit;
+  unsigned long long wait_ticks; // bound of the wait for the row's posts, in wall-clock ticks
   float* probs;                  // final probabilities [B][Hq][probs_stride] or null
   int64_t probs_stride;
   float* raw;                    // fallback target for chunk-relative exp values
@@ -597,8 +597,10 @@ void decode_partial_mfma(PartialParams p) {
     // Post this chunk's log-sum-exp per head as two 64-bit words, the value
     // tagged once with the call's epoch and once with its complement.  Each
     // word validates itself, so neither side needs a fence (relaxed
-    // agent-scope stores, read back with relaxed loads), and whatever the
-    // workspace held before passes the check with probability 2^-64.
+    // agent-scope stores, read back with relaxed loads).  The combine zeroes
+    // the posts after the pass, so a workspace that served an earlier call
+    // holds none (a graph replays one epoch), and junk in a fresh workspace
+    // passes the check with probability 2^-64.
     if (tid < 2 * GT) {
       const int h = tid >> 1;
       const float2 ml = ml_lds[h];
@@ -769,15 +771,26 @@ void decode_partial_mfma(PartialParams p) {
       else lse_lds[i] = __uint_as_float((uint32_t)w);
     }
     bool ok = !__syncthreads_or(miss0);
-    for (int it = 0; !ok && it < p.spin_limit; ++it) {
-      __builtin_amdgcn_s_sleep(2);
-      int miss = 0;
-      for (int i = tid; i < nw; i += kThreads) {
-        const unsigned long long w = post_word(i);
-        if ((uint32_t)(w >> 32) != p.epoch) miss = 1;
-        else lse_lds[i] = __uint_as_float((uint32_t)w);
+    if (!ok && p.wait_ticks > 0) {
+      // Poll again until the row is complete or wait_ticks of the constant
+      // wall clock have passed.  Only thread 0's clock decides; it publishes
+      // the decision in LDS before the barrier that every thread then reads
+      // it after.  Two slots alternate, so the next write (after the next
+      // barrier) never races the reads.
+      __shared__ int expired[2];
+      const unsigned long long t0 = (unsigned long long)wall_clock64();
+      for (int it = 0; !ok; ++it) {
+        if (tid == 0) expired[it & 1] = ((unsigned long long)wall_clock64() - t0) >= p.wait_ticks;
+        __builtin_amdgcn_s_sleep(2);
+        int miss = 0;
+        for (int i = tid; i < nw; i += kThreads) {
+          const unsigned long long w = post_word(i);
+          if ((uint32_t)(w >> 32) != p.epoch) miss = 1;
+          else lse_lds[i] = __uint_as_float((uint32_t)w);
+        }
+        ok = !__syncthreads_or(miss);
+        if (!ok && expired[it & 1]) break;
       }
-      ok = !__syncthreads_or(miss);
     }
     if (ok) {
       for (int h = wave; h < GT; h += kWaves) {
@@ -1077,6 +1090,11 @@ struct CombineParams {
   float* cum;                  // [B][H_kv][cum_stride] or null
   int64_t cum_stride;
   float decay;
+  // The pass's posts of this (sequence, query head), [n_chunks][2] words,
+  // or null.  The combine zeroes those of the row's chunks: a zero pair never
+  // validates, so a later execution with the same tag (a replayed graph)
+  // cannot accept a post left by an earlier one.
+  unsigned long long* lse_post;
   int blk_bs;                  // > 0: block aggregates of the chunks finished here
   float* blk_max;
   float* blk_mean;
@@ -1128,6 +1146,12 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(CombineParams p) 
   for (int i = 0; i < kCombPre; ++i) {
     const int c = cg + i * ng;
     pre[i] = (do_out && c < nc) ? po[(size_t)c * D4 + d4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (p.lse_post) {
+    // The pass that wrote these posts has completed (stream order), so no
+    // reader is left; zero the pairs of every chunk the pass had.
+    unsigned long long* pw = p.lse_post + 2 * (size_t)bh * p.n_chunks;
+    for (int i = tid; i < 2 * nc; i += kCombThreads) pw[i] = 0ull;
   }
   const bool pres = HAS_V && p.prescaled != 0;
   const size_t row = (size_t)b * p.num_kv_heads + (bh % p.num_q_heads) / p.group;
@@ -1465,7 +1489,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   pp.lse_post = reinterpret_cast<unsigned long long*>(sync_base);
   pp.chunk_flag = reinterpret_cast<uint32_t*>(sync_base + post_bytes);
   pp.epoch = a.epoch;
-  pp.spin_limit = a.spin_limit;
+  pp.wait_ticks = a.wait_ticks;
   pp.probs = a.probs;
   pp.probs_stride = a.probs_stride;
   pp.raw = a.probs ? a.probs : scratch;
@@ -1554,6 +1578,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
         cp.blk_head_stride = pp.blk_head_stride;
         cp.blk_seq_stride = pp.blk_seq_stride;
         cp.chunk_flag = pp.chunk_flag;
+        cp.lse_post = pp.lse_post;
         cp.group = pp.group;
         cp.num_kv_heads = a.num_kv_heads;
         cp.probs = a.probs;

@@ -32,8 +32,10 @@ bool is_pow2(long long x) { return x > 0 && (x & (x - 1)) == 0; }
 
 // 0 = unknown, 1 = gfx950, -1 = other.  Indexed by device ordinal.
 std::atomic<int> g_arch_ok[64];
+// Rate of the device's constant wall clock (kHz), read with the arch check.
+std::atomic<int> g_clock_khz[64];
 
-int check_device() {
+int check_device(int* dev_out = nullptr) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(KVSEL_ERR_UNSUPPORTED, "no HIP device");
   if (dev < 0 || dev >= 64) return fail(KVSEL_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
@@ -42,10 +44,15 @@ int check_device() {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
       return fail(KVSEL_ERR_UNSUPPORTED, "cannot query device %d", dev);
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+      khz = 100000;   // the 100 MHz constant clock of CDNA parts
+    g_clock_khz[dev].store(khz, std::memory_order_relaxed);
     st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
     g_arch_ok[dev].store(st, std::memory_order_relaxed);
   }
   if (st != 1) return fail(KVSEL_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  if (dev_out) *dev_out = dev;
   return KVSEL_OK;
 }
 
@@ -91,7 +98,11 @@ uint32_t next_epoch() {
   }
 }
 
-std::atomic<int> g_spin_limit{1 << 14};
+// Bound of the decode pass's wait for the posts of a row, in microseconds of
+// the device's constant clock.  A workgroup of the 70B-shape layer runs for
+// ~65 us and normally finds its row complete after ~3 us of waiting.
+constexpr int kDefaultWaitUs = 40;
+std::atomic<int> g_wait_us{kDefaultWaitUs};
 
 }  // namespace
 
@@ -110,9 +121,10 @@ const char* kvsel_status_string(int status) {
 
 const char* kvsel_last_error(void) { return g_last_error; }
 
-int32_t kvsel_set_sync_spin_limit(int32_t iterations) {
-  if (iterations < 0) return fail(KVSEL_ERR_INVALID, "spin limit %d < 0", iterations);
-  return g_spin_limit.exchange(iterations, std::memory_order_relaxed);
+int32_t kvsel_set_sync_wait_us(int32_t microseconds) {
+  if (microseconds < 0) return fail(KVSEL_ERR_INVALID, "wait bound %d us < 0", microseconds);
+  if (microseconds > 1000000) return fail(KVSEL_ERR_INVALID, "wait bound %d us > 1 s", microseconds);
+  return g_wait_us.exchange(microseconds, std::memory_order_relaxed);
 }
 
 size_t kvsel_decode_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads,
@@ -153,7 +165,8 @@ int decode_impl(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads, fl
   if (!workspace || workspace_bytes < plan.total_bytes)
     return fail(KVSEL_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes,
                 plan.total_bytes);
-  st = check_device();
+  int dev = 0;
+  st = check_device(&dev);
   if (st != KVSEL_OK) return st;
   kvsel::DecodeArgs a{};
   a.k_pages = kv->k_pages;
@@ -180,7 +193,8 @@ int decode_impl(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads, fl
   a.decay = decay;
   a.workspace = workspace;
   a.epoch = next_epoch();
-  a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  a.wait_ticks = (unsigned long long)g_wait_us.load(std::memory_order_relaxed) *
+                 (unsigned long long)g_clock_khz[dev].load(std::memory_order_relaxed) / 1000ull;
   a.blk_bs = block_size;
   a.blk_max = blk_max;
   a.blk_mean = blk_mean;

@@ -42,7 +42,7 @@ struct DecodeArgs {
   float decay;
   void* workspace;
   uint32_t epoch;      // unique per call (never 0): tags the row arrival words
-  int spin_limit;      // bounded wait of the in-kernel normalisation
+  unsigned long long wait_ticks;  // bound of the in-kernel normalisation's wait (wall-clock ticks)
   // Optional block aggregates of the updated cum (blk_bs > 0, cum required).
   int blk_bs;
   float* blk_max;

@@ -38,8 +38,8 @@ struct SparseParams {
   const uint8_t* q;
   const int32_t* indices;   // [B][idx_heads][idx_stride]
   int64_t idx_stride;
-  const int32_t* counts;    // [B][idx_heads]
-  int num_kv_heads, num_q_heads, idx_heads, page_log2, max_pages, n_chunks;
+  const int32_t* counts;    // [B][idx_heads], read clamped to max_count
+  int num_kv_heads, num_q_heads, idx_heads, page_log2, max_pages, n_chunks, max_count;
   float scale;
   float* probs;             // [B][Hq][idx_stride] raw logits written here, or null
   float* part_o;            // [B][Hq][n_chunks][D]
@@ -67,7 +67,9 @@ __global__ __launch_bounds__(kThreads) void sparse_partial(SparseParams p) {
   const bool shared = p.idx_heads != p.num_q_heads;
   const int h0 = shared ? set * G : set;      // first query head served
   const int kvh = h0 / G;
-  const int count = p.counts[(size_t)b * p.idx_heads + set];
+  // A count above max_count is a caller error; clamping it keeps every
+  // access inside the index rows and the workspace the grid was sized for.
+  const int count = min(p.counts[(size_t)b * p.idx_heads + set], p.max_count);
   const int start = chunk * kSlice;
   if (start >= count) return;
   const int n = min(kSlice, count - start);
@@ -229,7 +231,7 @@ struct SparseCombineParams {
   const float2* part_ml;
   float* out;
   float* lse_ws;
-  int num_q_heads, num_kv_heads, idx_heads, n_chunks, D;
+  int num_q_heads, num_kv_heads, idx_heads, n_chunks, D, max_count;
 };
 
 __global__ __launch_bounds__(128) void sparse_combine(SparseCombineParams p) {
@@ -239,7 +241,9 @@ __global__ __launch_bounds__(128) void sparse_combine(SparseCombineParams p) {
   const int b = bh / p.num_q_heads, h = bh % p.num_q_heads;
   const int G = p.num_q_heads / p.num_kv_heads;
   const int set = p.idx_heads == p.num_q_heads ? h : h / G;
-  const int count = p.counts[(size_t)b * p.idx_heads + set];
+  // clamped as in the partial pass: nc <= n_chunks, the LDS and the
+  // workspace rows this row owns
+  const int count = min(p.counts[(size_t)b * p.idx_heads + set], p.max_count);
   const int nc = (count + kSlice - 1) / kSlice;
   const float2* ml = p.part_ml + (size_t)bh * p.n_chunks;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -283,13 +287,13 @@ __global__ __launch_bounds__(128) void sparse_combine(SparseCombineParams p) {
 // Listed probabilities: raw logit -> exp(s - lse); ignored entries -> 0.
 __global__ __launch_bounds__(256) void sparse_normalize(const int32_t* counts, const int32_t* indices,
                                                         int64_t idx_stride, int num_q_heads,
-                                                        int num_kv_heads, int idx_heads,
+                                                        int num_kv_heads, int idx_heads, int max_count,
                                                         const float* lse_ws, float* probs) {
   const int bh = blockIdx.y;
   const int b = bh / num_q_heads, h = bh % num_q_heads;
   const int G = num_q_heads / num_kv_heads;
   const int set = idx_heads == num_q_heads ? h : h / G;
-  const int count = counts[(size_t)b * idx_heads + set];
+  const int count = min(counts[(size_t)b * idx_heads + set], max_count);
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= count) return;
   const int j = indices[((size_t)b * idx_heads + set) * idx_stride + i];
@@ -348,6 +352,7 @@ hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream) {
   sp.page_log2 = __builtin_ctz((unsigned)a.page_size);
   sp.max_pages = a.max_pages;
   sp.n_chunks = n_chunks;
+  sp.max_count = a.max_count;
   sp.scale = a.scale;
   sp.probs = a.probs;
   sp.part_o = part_o;
@@ -362,13 +367,13 @@ hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream) {
                           : launch_sparse_d<false, 64>(sp, gt, grid, stream);
   if (e != hipSuccess) return e;
   SparseCombineParams cp{a.counts, part_o, part_ml, a.out, a.lse_out ? a.lse_out : lse_ws, a.num_q_heads,
-                         a.num_kv_heads, a.idx_heads, n_chunks, a.head_dim};
+                         a.num_kv_heads, a.idx_heads, n_chunks, a.head_dim, a.max_count};
   hipLaunchKernelGGL(sparse_combine, dim3((unsigned)bh), dim3(128), n_chunks * sizeof(float), stream, cp);
   e = hipGetLastError();
   if (e != hipSuccess || !a.probs || a.raw_logits) return e;
   hipLaunchKernelGGL(sparse_normalize, dim3((a.max_count + 255) / 256, (unsigned)bh), dim3(256), 0,
                      stream, a.counts, a.indices, a.idx_stride, a.num_q_heads, a.num_kv_heads,
-                     a.idx_heads, cp.lse_ws, a.probs);
+                     a.idx_heads, a.max_count, cp.lse_ws, a.probs);
   return hipGetLastError();
 }
 

@@ -20,7 +20,7 @@
  *   - Tensor pointers are DEVICE pointers, allocated and owned by the caller.
  *     The library allocates nothing and frees nothing.  Its only state is a
  *     per-device architecture check, a per-call counter that tags the decode
- *     pass's synchronisation words, and the spin limit below.  Scratch space
+ *     pass's synchronisation words, and the wait bound below.  Scratch space
  *     is passed in as `workspace` (device memory, size from the matching
  *     *_workspace_bytes); two calls must not share a workspace concurrently.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
@@ -264,7 +264,9 @@ size_t kvsel_snapkv_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_head
  *   indices [num_seqs][idx_heads][idx_stride] i32 logical positions < L_b,
  *           distinct; entries < 0 are ignored; only the first counts[b][g]
  *           entries of a row are read.
- *   counts  [num_seqs][idx_heads] i32, 0 <= counts <= max_count <= idx_stride.
+ *   counts  [num_seqs][idx_heads] i32, 0 <= counts <= max_count <= idx_stride
+ *           (a precondition; a larger count is read as max_count, so no
+ *           access leaves the index rows or the workspace).
  *   out     [num_seqs][num_q_heads][head_dim] f32 (all zero for an empty set).
  *   probs   [num_seqs][num_q_heads][idx_stride] f32 or NULL: entry i < count
  *           receives the probability of the listed position (0 for an ignored
@@ -484,13 +486,16 @@ size_t kvsel_h2o_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads, 
 
 /* The bf16 decode pass normalises probabilities in-kernel: each workgroup
  * posts its chunk's log-sum-exp per head, then reads the posts of the other
- * chunks of its (sequence, KV head) row, polling again up to `iterations`
- * times while some are missing.  A workgroup that stops waiting leaves its
- * chunk to a fix-up pass, so results are exact either way.  With 0 only
- * the chunks that find their whole row posted at the first look finish
- * in-kernel (tests use this to exercise the fix-up).  Returns the previous
- * limit, or KVSEL_ERR_INVALID for a negative value.  Process-wide. */
-int32_t kvsel_set_sync_spin_limit(int32_t iterations);
+ * chunks of its (sequence, KV head) row, polling again while some are
+ * missing, for at most `microseconds` of the device's constant wall clock
+ * (default 40).  A workgroup that stops waiting leaves its chunk to a fix-up
+ * pass, so results are exact either way; the bound only caps the time a
+ * workgroup can spend waiting when the chunks of its row are not resident
+ * together (other work holding compute units).  With 0 only the chunks that
+ * find their whole row posted at the first look finish in-kernel (tests use
+ * this to exercise the fix-up).  Returns the previous bound, or
+ * KVSEL_ERR_INVALID for a value outside [0, 1000000].  Process-wide. */
+int32_t kvsel_set_sync_wait_us(int32_t microseconds);
 
 /* Name of a status code (static string). */
 /* kvsel_read_probe: one streaming read of `bytes` bytes of device memory

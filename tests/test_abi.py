@@ -157,16 +157,18 @@ def test_snapkv_validation():
     assert lib.kvsel_snapkv_workspace_bytes(ctypes.byref(_kv()), 32, 32) >= 2 * 32 * 32 * 4 * 8
 
 
-def test_sync_spin_limit_setter():
-    prev = K.set_sync_spin_limit(7)
+def test_sync_wait_bound_setter():
+    prev = K.set_sync_wait_us(7)
     try:
         assert prev >= 0
-        assert K.set_sync_spin_limit(0) == 7
+        assert K.set_sync_wait_us(0) == 7
         with pytest.raises(K.KvselError):
-            K.set_sync_spin_limit(-1)
-        assert K.set_sync_spin_limit(0) == 0
+            K.set_sync_wait_us(-1)
+        with pytest.raises(K.KvselError):
+            K.set_sync_wait_us(1000001)
+        assert K.set_sync_wait_us(0) == 0
     finally:
-        K.set_sync_spin_limit(prev)
+        K.set_sync_wait_us(prev)
 
 
 @pytest.mark.parametrize("kw,status", [

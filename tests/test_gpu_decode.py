@@ -231,11 +231,11 @@ def test_llama70b_layer_full_size_sampled():
         assert max_rel(f64(cum[b, c]), r["probs"].sum(axis=0)) < SCORE_TOL
 
 
-@pytest.mark.parametrize("spin", [0, 1 << 14], ids=["fallback", "in-kernel"])
-def test_decode_normalisation_paths_and_workspace_reuse(spin):
+@pytest.mark.parametrize("wait_us", [0, 40], ids=["fallback", "in-kernel"])
+def test_decode_normalisation_paths_and_workspace_reuse(wait_us):
     """The bf16 pass normalises in-kernel once all chunks of a (sequence, KV
     head) row have posted their (max, sum); a workgroup that stops waiting
-    hands its chunk to the fix-up pass.  Spin limit 0 forces a mix of both
+    hands its chunk to the fix-up pass.  A wait bound of 0 forces a mix of both
     (only the last chunk of a row to arrive sees the row complete).  One
     workspace, first filled with junk, serves three calls in a row so stale
     arrival words of earlier calls are exercised."""
@@ -245,7 +245,7 @@ def test_decode_normalisation_paths_and_workspace_reuse(spin):
     kv = K.PagedKV(c["kp"], c["vp"], c["bt"], c["lens"], 16, c["max_len"])
     nbytes = K.decode_workspace_bytes(kv, Hq, True)
     ws = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda")
-    prev = K.set_sync_spin_limit(spin)
+    prev = K.set_sync_wait_us(wait_us)
     try:
         cum = torch.zeros((B, Hkv, c["stride"]), device="cuda")
         for it in range(3):
@@ -262,7 +262,7 @@ def test_decode_normalisation_paths_and_workspace_reuse(spin):
                 want = (it + 1) * r["probs"].reshape(Hkv, Hq // Hkv, L).sum(axis=1)
                 assert max_rel(f64(cum[b, :, :L]), want) < SCORE_TOL
     finally:
-        K.set_sync_spin_limit(prev)
+        K.set_sync_wait_us(prev)
 
 
 def test_decode_cum_only_fallback_uses_scratch():
@@ -271,13 +271,13 @@ def test_decode_cum_only_fallback_uses_scratch():
     K = _K()
     c = _random_case(32, torch.bfloat16, 64, 4, 3, 32, [3100, 700])
     kv = K.PagedKV(c["kp"], None, c["bt"], c["lens"], 32, c["max_len"])
-    prev = K.set_sync_spin_limit(0)
+    prev = K.set_sync_wait_us(0)
     try:
         cum = torch.zeros((2, 3, c["stride"]), device="cuda")
         K.decode_attn_scores(kv, c["q"], 12, c["scale"], None, None, None, K.EMIT_PROBS, cum, 1.0)
         torch.cuda.synchronize()
     finally:
-        K.set_sync_spin_limit(prev)
+        K.set_sync_wait_us(prev)
     for b, L in enumerate([3100, 700]):
         r = _oracle(c, b, with_v=False)
         want = r["probs"].reshape(3, 4, L).sum(axis=1)
@@ -285,7 +285,7 @@ def test_decode_cum_only_fallback_uses_scratch():
 
 
 AGG_CASES = [
-    # seed, dtype, d, G, Hkv, P, lengths, block, spin (None: default)
+    # seed, dtype, d, G, Hkv, P, lengths, block, wait bound in us (None: default)
     (41, torch.bfloat16, 128, 8, 2, 64, [4096, 1500, 64], 64, None),    # fused in the pass
     (42, torch.bfloat16, 128, 4, 3, 16, [2049, 777], 16, None),
     (43, torch.bfloat16, 64, 2, 2, 32, [3000, 100], 256, None),
@@ -295,12 +295,12 @@ AGG_CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", AGG_CASES, ids=lambda c: f"s{c[0]}-{str(c[1])[6:]}-G{c[3]}-bs{c[7]}-spin{c[8]}")
+@pytest.mark.parametrize("case", AGG_CASES, ids=lambda c: f"s{c[0]}-{str(c[1])[6:]}-G{c[3]}-bs{c[7]}-wait{c[8]}")
 def test_decode_with_block_aggregates(case):
     """kvsel_decode_attn_scores_agg: probabilities and cum as the plain call,
     plus the block max / mean of the updated cum per (sequence, KV head),
     written into a strided array (two 'layers' stacked as extra heads)."""
-    seed, dtype, d, G, Hkv, P, lengths, bs, spin = case
+    seed, dtype, d, G, Hkv, P, lengths, bs, wait_us = case
     note(f"decode+agg case {case}")
     K = _K()
     c = _random_case(seed, dtype, d, G, Hkv, P, lengths, extra_stride=3)
@@ -316,7 +316,7 @@ def test_decode_with_block_aggregates(case):
     probs = torch.full((B, Hq, c["stride"]), -7.0, device="cuda")
     cum0 = torch.rand((B, Hkv, c["stride"]), device="cuda")
     cum = cum0.clone()
-    prev = K.set_sync_spin_limit(spin) if spin is not None else None
+    prev = K.set_sync_wait_us(wait_us) if wait_us is not None else None
     try:
         layer = 1                                                # write the second stacked layer
         off = layer * Hkv * head_stride
@@ -325,7 +325,7 @@ def test_decode_with_block_aggregates(case):
         torch.cuda.synchronize()
     finally:
         if prev is not None:
-            K.set_sync_spin_limit(prev)
+            K.set_sync_wait_us(prev)
     bm = blk_max.view(-1)
     bn = blk_mean.view(-1)
     for b in range(B):

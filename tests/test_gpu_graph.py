@@ -1,9 +1,11 @@
 """The hot-path calls captured in a HIP graph (as bench.py replays them)
-give, on every replay, bit-identical results to the same calls run eagerly.
-Between replays the test does eager work of its own (resetting the scores)
-and synchronises."""
+give, on every replay, bit-identical results to the same calls run eagerly,
+and a single decode call replayed with new inputs matches the oracle on every
+replay.  Between replays the tests do eager work of their own and
+synchronise."""
 import math
 
+import numpy as np
 import pytest
 import torch
 
@@ -70,3 +72,111 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         for a, b in zip(snapshot(), eager):
             assert torch.equal(a, b), f"replay {rep} differs from the eager run"
+
+
+def _valid_post_pairs(ws: torch.Tensor) -> int:
+    """Number of 16-byte-aligned word pairs in a workspace that would pass the
+    decode pass's post check under SOME tag: (tag << 32 | v, ~tag << 32 | v)
+    with tag != 0.  Layout-free: it scans the whole buffer."""
+    w = ws.cpu().numpy().view(np.uint64).reshape(-1, 2)
+    hi0, hi1 = w[:, 0] >> np.uint64(32), w[:, 1] >> np.uint64(32)
+    lo0, lo1 = w[:, 0] & np.uint64(0xFFFFFFFF), w[:, 1] & np.uint64(0xFFFFFFFF)
+    ok = (hi0 != 0) & (hi1 == (hi0 ^ np.uint64(0xFFFFFFFF))) & (lo0 == lo1)
+    return int(ok.sum())
+
+
+def _probs_case(seed, B, Hkv, G, d, P, cap):
+    g = synth.generator(seed)
+    bt, n_pages = synth.shuffled_block_table(B, cap, P, g)
+    kp = synth.normal((n_pages, Hkv, P, d), g, torch.bfloat16).cuda()
+    vp = synth.normal((n_pages, Hkv, P, d), g, torch.bfloat16).cuda()
+    return g, bt.cuda(), kp, vp
+
+
+def test_no_post_survives_a_call():
+    """After a decode call that normalises in-kernel, no word pair anywhere in
+    its workspace validates as a post for any tag (the combine zeroes the
+    pass's posts), so a later execution replaying the same tag cannot take a
+    stale one.  The workspace starts as junk, as a fresh allocation might."""
+    import attention_score_guided_amd as K
+    B, Hkv, G, d, P, cap = 4, 4, 8, 128, 64, 8192
+    Hq = Hkv * G
+    g, bt, kp, vp = _probs_case(5, B, Hkv, G, d, P, cap)
+    lens = torch.tensor([8192, 5000, 1, 7777], dtype=torch.int32).cuda()
+    kv = K.PagedKV(kp, vp, bt, lens, P, cap)
+    q = synth.normal((B, Hq, d), g, torch.bfloat16).cuda()
+    nbytes = K.decode_workspace_bytes(kv, Hq, True)
+    ws = torch.randint(0, 256, (nbytes // 16 * 16,), dtype=torch.uint8, device="cuda",
+                       generator=torch.Generator(device="cuda").manual_seed(3))
+    assert _valid_post_pairs(ws) == 0     # random junk: a chance pair is 2^-64 per pair
+    out = torch.empty((B, Hq, d), device="cuda")
+    probs = torch.empty((B, Hq, cap), device="cuda")
+    cum = torch.zeros((B, Hkv, cap), device="cuda")
+    for _ in range(2):
+        K.decode_attn_scores(kv, q, Hq, 1 / math.sqrt(d), out, None, probs, K.EMIT_PROBS, cum, 1.0,
+                             workspace=ws)
+        torch.cuda.synchronize()
+        n = _valid_post_pairs(ws)
+        print(f"valid post pairs left in the workspace: {n}", flush=True)
+        assert n == 0
+
+
+def test_single_call_graph_replays_with_new_inputs():
+    """One decode call (probabilities, cum, out) captured alone in a graph on
+    its own workspace, replayed three times with a new query and longer
+    device-side lengths written between replays.  Every replay is compared
+    with the float64 oracle: probabilities and cum within 1e-4 relative, out
+    within 2e-3 relative L2.  The grid (8 sequences x 8 KV heads x 16 chunks)
+    exceeds the chip's resident workgroups, so rows meet at different times."""
+    import attention_score_guided_amd as K
+    import oracle as O
+    from tests.parity_util import f64, logical_kv_rows, max_rel, rel_l2
+    B, Hkv, G, d, P, cap = 8, 8, 8, 128, 64, 16384
+    Hq = Hkv * G
+    scale = 1 / math.sqrt(d)
+    g, bt, kp, vp = _probs_case(6, B, Hkv, G, d, P, cap)
+    lens0 = torch.randint(8192, 12000, (B,), generator=g, dtype=torch.int32)
+    lens = lens0.cuda()
+    kv = K.PagedKV(kp, vp, bt, lens, P, cap)
+    q = torch.empty((B, Hq, d), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((B, Hq, d), device="cuda")
+    probs = torch.empty((B, Hq, cap), device="cuda")
+    cum = torch.zeros((B, Hkv, cap), device="cuda")
+    ws = torch.empty(K.decode_workspace_bytes(kv, Hq, True), dtype=torch.uint8, device="cuda")
+    q.copy_(synth.normal((B, Hq, d), g, torch.bfloat16).cuda())
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            K.decode_attn_scores(kv, q, Hq, scale, out, None, probs, K.EMIT_PROBS, cum, 1.0, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    cum.zero_()
+    cum_ref = np.zeros((B, Hkv, cap))
+    cur = lens0.clone()
+    for rep in range(3):
+        if rep > 0:
+            cur = torch.minimum(cur + torch.randint(1, 1500, (B,), generator=g, dtype=torch.int32),
+                                torch.tensor(cap, dtype=torch.int32))
+            q.copy_(synth.normal((B, Hq, d), g, torch.bfloat16).cuda())
+            lens.copy_(cur.cuda())
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        worst = [0.0, 0.0, 0.0]
+        for b in range(B):
+            L = int(cur[b])
+            for c in range(Hkv):
+                Kl, Vl = logical_kv_rows(kp, vp, bt, b, c, L)
+                hs = slice(c * G, (c + 1) * G)
+                r = O.decode_attention(f64(q[b, hs]), Kl, Vl, scale)
+                cum_ref[b, c, :L] = O.accumulate(cum_ref[b, c:c + 1, :L], r["probs"])[0]
+                e = (rel_l2(f64(out[b, hs]), r["out"]), max_rel(f64(probs[b, hs, :L]), r["probs"]),
+                     max_rel(f64(cum[b, c, :L]), cum_ref[b, c, :L]))
+                worst = [max(x, y) for x, y in zip(worst, e)]
+                assert e[0] < 2e-3 and e[1] < 1e-4 and e[2] < 1e-4, (rep, b, c, e)
+        print(f"replay {rep}: lengths {cur.tolist()} worst out {worst[0]:.2e} probs {worst[1]:.2e} "
+              f"cum {worst[2]:.2e}", flush=True)

@@ -153,3 +153,32 @@ def test_indexer_topk_sparse_flow_long_context():
             hot |= set(range(c - 255, c + 256))
         frac = np.mean([np.isin(kp[b, h], list(hot | set(range(4)))).mean() for h in range(Hq)])
         assert frac > 0.5
+
+
+def test_sparse_counts_above_max_count_are_clamped():
+    """A count above max_count (a caller error) reads as max_count: only the
+    first max_count listed entries take part, every access stays inside the
+    index rows, the probability rows and the workspace sized for max_count.
+    Compared with the oracle on the clamped sets; probability entries past
+    max_count stay untouched."""
+    K = _K()
+    d, G, Hkv, P, L = 128, 4, 2, 16, 3000
+    kp, vp, bt, lens, q = _case(48, torch.bfloat16, d, G, Hkv, P, [L])
+    Hq, max_count, stride = Hkv * G, 300, 700
+    rng = np.random.default_rng(48)
+    idx = np.stack([rng.choice(L, size=stride, replace=False) for _ in range(Hq)]).astype(np.int32)[None]
+    cnt = np.array([[stride, max_count + 1, max_count, 17, 513, 299, 300, 301]], dtype=np.int32)
+    kv = K.PagedKV(kp, vp, bt, lens, P, L)
+    out = torch.full((1, Hq, d), float("nan"), device="cuda")
+    probs = torch.full((1, Hq, stride), -3.0, device="cuda")
+    K.sparse_attn(kv, q, Hq, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), max_count,
+                  1 / math.sqrt(d), out, probs)
+    torch.cuda.synchronize()
+    Kl, Vl = logical_kv(kp, vp, bt, 0, L)
+    used = np.minimum(cnt[0], max_count)
+    sets = [idx[0, h, :used[h]] for h in range(Hq)]
+    want_out, want_p = O.sparse_attention(f64(q[0]), Kl, Vl, sets, 1 / math.sqrt(d))
+    for h in range(Hq):
+        assert rel_l2(f64(out[0, h]), want_out[h]) < OUT_TOL
+        assert max_rel(f64(probs[0, h, :used[h]]), want_p[h]) < SCORE_TOL
+        assert (probs[0, h, used[h]:] == -3.0).all()
