@@ -370,7 +370,7 @@ void decode_partial_mfma(PartialParams p) {
   constexpr int VU = KVSEL_PV_VU > 0 ? KVSEL_PV_VU : GT >= 8 ? 4 : !COOP ? 8 : GT == 4 ? 6 : GT == 2 ? 7 : 8;
   constexpr int QB = kQkBatch;
 
-  extern __shared__ float smem[];
+  extern __shared__ __align__(16) float smem[];
   const int C = p.chunk;
   float* p_lds = smem;                               // [C][GT] logits, then exp(s - m)
   float* red = smem + C * GT;                        // [kWaves][GT][D]
@@ -776,8 +776,10 @@ void decode_partial_mfma(PartialParams p) {
       // wall clock have passed.  Only thread 0's clock decides; it publishes
       // the decision in LDS before the barrier that every thread then reads
       // it after.  Two slots alternate, so the next write (after the next
-      // barrier) never races the reads.
-      __shared__ int expired[2];
+      // barrier) never races the reads.  The slots sit in the dynamic area
+      // (wstat past fac[GT]): a static LDS variable would shift the dynamic
+      // area off its 16-byte alignment and split every float4 LDS access.
+      int* expired = reinterpret_cast<int*>(wstat + 64);
       const unsigned long long t0 = (unsigned long long)wall_clock64();
       for (int it = 0; !ok; ++it) {
         if (tid == 0) expired[it & 1] = ((unsigned long long)wall_clock64() - t0) >= p.wait_ticks;
