@@ -47,3 +47,30 @@ def max_rel(a: np.ndarray, b: np.ndarray, floor: float = 1e-30) -> float:
 def note(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()
+
+
+def keep_swap_gap(got, want, scores, n: int, sinks: int = 0, window: int = 0, tol: float = 1e-6) -> float:
+    """End-to-end keep-set check: the GPU's set ``got`` (chosen from the GPU's
+    own scores) against the oracle's set ``want`` (chosen from the oracle's
+    float64 scores ``scores``).  They must have the same size and keep the same
+    forced positions; every position in which they differ must be a middle
+    position whose oracle score lies within tol * max(1, |tau|) of the cut tau
+    (the lowest oracle score the oracle kept in the middle): a swap between
+    near-equal scores, which fp32 rounding may decide either way.  Returns the
+    worst |score - tau| / max(1, |tau|) over the differences (0 when equal)."""
+    got = set(int(x) for x in np.asarray(got).ravel())
+    want = set(int(x) for x in np.asarray(want).ravel())
+    assert len(got) == len(want), f"keep sets differ in size: {len(got)} vs {len(want)}"
+    diff = sorted(got ^ want)
+    if not diff:
+        return 0.0
+    lo, hi = min(sinks, n), max(n - window, 0)
+    assert all(lo <= j < hi for j in diff), f"a forced position differs: {[j for j in diff if not lo <= j < hi]}"
+    kept_mid = [j for j in want if lo <= j < hi]
+    tau = min(scores[j] for j in kept_mid)
+    scale = max(1.0, abs(tau))
+    gaps = [abs(scores[j] - tau) / scale for j in diff]
+    worst = max(gaps)
+    assert worst <= tol, (f"{len(diff)} differing positions, worst gap {worst:.3e} > {tol:g} "
+                          f"(tau {tau:.9g}; positions {diff[:8]})")
+    return worst

@@ -7,14 +7,18 @@ benchmark times, on outputs the float64 oracle can compute one by one:
     and its top-4096, the indexer scores and their top-2048, sparse attention
     over them, and dense decode; sampled rows in full, every keep set against
     the oracle's selection on the GPU's own scores for sampled rows, and the
-    per-block score / stamp records of the sparse step's selection."""
+    per-block score / stamp records of the sparse step's selection.
+Keep sets are checked twice: bit-exact against the oracle's selection on the
+GPU's own scores, and end to end against the oracle's selection on the
+oracle's scores (any difference must be a swap between scores within 1e-6 of
+the cut; the worst gap is printed)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
 import synth
-from tests.parity_util import f64, logical_kv_rows, max_rel, note, rel_l2
+from tests.parity_util import f64, keep_swap_gap, logical_kv_rows, max_rel, note, rel_l2
 
 pytestmark = pytest.mark.gpu
 OUT_TOL, SCORE_TOL = 2e-3, 1e-4
@@ -71,8 +75,12 @@ def test_llama3_8b_layer_full_size_sampled():
         mx, mean = O.block_aggregate(got[None, :], L, 16)
         nb = mx.shape[1]
         assert max_rel(f64(bmax[b, c, :nb]), mx[0]) < 1e-6 and max_rel(f64(bmean[b, c, :nb]), mean[0]) < 1e-5
+        gk = keep[b * Hkv + c, :int(kc[b * Hkv + c])].cpu().numpy()
         want = O.select_keep(got, L, 4, 512, int(budgets[b * Hkv + c]))
-        assert keep[b * Hkv + c, :int(kc[b * Hkv + c])].cpu().numpy().tolist() == want.tolist()
+        assert gk.tolist() == want.tolist()                       # the selection on the GPU's scores
+        e2e = O.select_keep(cum_ref[0], L, 4, 512, int(budgets[b * Hkv + c]))   # the oracle's own set
+        gap = keep_swap_gap(gk, e2e, cum_ref[0], L, 4, 512)
+        note(f"  20% keep set vs the oracle's: {len(set(gk) ^ set(e2e.tolist()))} differing, worst gap {gap:.2e}")
 
 
 def test_long_context_128k_full_size_sampled():
@@ -115,11 +123,16 @@ def test_long_context_128k_full_size_sampled():
     K.decode_attn_scores(kvd, cfg["q_dec"][0], Hq, cfg["scale"], dout, None, None, K.EMIT_PROBS)
     torch.cuda.synchronize()
 
-    for b, c in [(1, 5)]:
+    for b, c in [(1, 5), (3, 0)]:
         note(f"128K vote row b={b} kvh={c}")
         Kl, _ = logical_kv_rows(kvt.k_pages, None, kvt.block_table, b, c, L)
         want = O.snapkv_vote(f64(cfg["q_win"][b, c * 4:c * 4 + 4]), Kl, cfg["scale"], 7, group_sum=True)
         assert max_rel(f64(votes[b, c, :L - W]), want[0]) < SCORE_TOL
+        r = b * Hkv + c
+        gk = vk[r, :int(vc[r])].cpu().numpy()
+        e2e = O.select_keep(want[0], L - W, 0, 0, 4096)          # the oracle's set from its own votes
+        gap = keep_swap_gap(gk, e2e, want[0], L - W)
+        note(f"  vote top-4096 vs the oracle's: {len(set(gk) ^ set(e2e.tolist()))} differing, worst gap {gap:.2e}")
     vg = f64(votes)
     for r in [0, 13, 31]:
         want = O.select_keep(vg[r // Hkv, r % Hkv], L - W, 0, 0, 4096)
@@ -133,6 +146,10 @@ def test_long_context_128k_full_size_sampled():
         sel = O.select_keep(sg[b, h], L + 1, 0, 0, 2048)
         r = b * Hq + h
         assert sk[r, :int(sc[r])].cpu().numpy().tolist() == sel.tolist()
+        e2e = O.select_keep(want_s, L + 1, 0, 0, 2048)            # the oracle's set from its own scores
+        gap = keep_swap_gap(sel, e2e, want_s, L + 1)
+        note(f"  indexer top-2048 vs the oracle's: {len(set(sel.tolist()) ^ set(e2e.tolist()))} differing, "
+             f"worst gap {gap:.2e}")
         Kl, Vl = logical_kv_rows(kvt.k_pages, kvt.v_pages, kvt.block_table, b, h // 4, L + 1)
         so, sp = O.sparse_attention(f64(cfg["q_dec"][0, b, h])[None, :], Kl, Vl, [sel], cfg["scale"])
         assert rel_l2(f64(sout[b, h]), so[0]) < OUT_TOL
