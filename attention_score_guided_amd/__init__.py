@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     KVSEL_ERR_UNSUPPORTED, KVSEL_ERR_WORKSPACE, KVSEL_F32, KVSEL_OK, REDUCE_NONE, REDUCE_SUM,
     SELECT_GLOBAL_PERCENTILE, SELECT_ROWS, KvselError, PagedKV, PagedKVDesc, accumulate,
     block_aggregate, decode_attn_scores, decode_attn_scores_agg, decode_workspace_bytes, library,
+    decode_attn_scores_noalloc, NOALLOC_SCRATCH_BYTES,
     select_keep, select_workspace_bytes, set_sync_wait_us, snapkv_vote, snapkv_workspace_bytes,
     sparse_attn, sparse_workspace_bytes, quest_summarize, quest_select, quest_workspace_bytes,
     h2o_step, h2o_workspace_bytes, accumulate_ex, block_aggregate_ex, select_threshold,

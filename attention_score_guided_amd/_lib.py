@@ -30,6 +30,7 @@ BLOCK_TOP_P_MEAN, BLOCK_FRAC_ABOVE, BLOCK_ALL_COLD = 0, 1, 2
 # Every symbol include/kvsel.h declares.
 EXPORTED = (
     "kvsel_decode_attn_scores", "kvsel_decode_attn_scores_agg", "kvsel_decode_workspace_bytes",
+    "kvsel_decode_attn_scores_noalloc",
     "kvsel_accumulate",
     "kvsel_block_aggregate", "kvsel_select_keep", "kvsel_select_workspace_bytes",
     "kvsel_snapkv_vote", "kvsel_snapkv_workspace_bytes", "kvsel_sparse_attn",
@@ -69,6 +70,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvsel_decode_attn_scores_agg": (ctypes.c_int, [D, P, I32, F, P, P, P, I64, P, I64, F, I32, P, P, I64, I64,
                                                          P, SZ, P]),
         "kvsel_decode_workspace_bytes": (SZ, [D, I32, I32]),
+        "kvsel_decode_attn_scores_noalloc": (ctypes.c_int, [D, P, I32, F, P, P, P, I64, I32, P, I64, F, P]),
         "kvsel_accumulate": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, F, P, I64, P]),
         "kvsel_block_aggregate": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, I32, I32, P, P, I64, P]),
         "kvsel_select_keep": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, P, I32, I32, I32, P, I64, P, P, SZ, P]),
@@ -186,6 +188,25 @@ def set_sync_wait_us(microseconds: int) -> int:
 
 def decode_workspace_bytes(kv: PagedKV, num_q_heads: int, probs_given: bool) -> int:
     return int(_LIB.kvsel_decode_workspace_bytes(kv.ref(), num_q_heads, int(bool(probs_given))))
+
+
+NOALLOC_SCRATCH_BYTES = 96 << 20
+
+
+def decode_attn_scores_noalloc(kv: PagedKV, q: torch.Tensor, num_q_heads: int, scale: float,
+                               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                               probs: Optional[torch.Tensor] = None, emit: int = EMIT_PROBS,
+                               cum: Optional[torch.Tensor] = None, decay: float = 1.0, stream=None) -> None:
+    """kvsel_decode_attn_scores_noalloc: as decode_attn_scores, with the
+    library's static device scratch in place of a workspace (allocates
+    nothing, here or in the library)."""
+    if q.dtype != kv.dtype:
+        raise TypeError("q must have the cache dtype")
+    _check(_LIB.kvsel_decode_attn_scores_noalloc(
+        kv.ref(), _ptr(q, None, "q"), num_q_heads, float(scale), _ptr(out, torch.float32, "out"),
+        _ptr(lse, torch.float32, "lse"), _ptr(probs, torch.float32, "probs"),
+        probs.shape[-1] if probs is not None else 0, emit, _ptr(cum, torch.float32, "cum"),
+        cum.shape[-1] if cum is not None else 0, float(decay), _stream(stream)))
 
 
 def decode_attn_scores(kv: PagedKV, q: torch.Tensor, num_q_heads: int, scale: float,

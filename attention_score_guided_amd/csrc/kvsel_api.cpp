@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/kvsel.h"
 #include "kvsel_internal.hpp"
@@ -104,6 +105,29 @@ uint32_t next_epoch() {
 constexpr int kDefaultWaitUs = 40;
 std::atomic<int> g_wait_us{kDefaultWaitUs};
 
+// ---- allocation-free decode: the workspace lives in a static device array ----
+// Each device that loads the library holds its own copy of `scratch` for the
+// life of the process.  In host code the array's name is only a stand-in for
+// the symbol: its device address comes from hipGetSymbolAddress, taken once
+// per device with that device current and kept here.
+static __device__ __align__(256) unsigned char scratch[KVSEL_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];   // per device ordinal, under g_scratch_mu
+
+int scratch_address(int dev, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail(KVSEL_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    if (!ptr) return fail(KVSEL_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVSEL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -140,7 +164,8 @@ namespace {
 int decode_impl(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads, float scale, float* out,
                 float* lse, float* probs, int64_t probs_stride, int32_t emit, float* cum, int64_t cum_stride,
                 float decay, int32_t block_size, float* blk_max, float* blk_mean, int64_t blk_head_stride,
-                int64_t blk_seq_stride, void* workspace, size_t workspace_bytes, void* stream) {
+                int64_t blk_seq_stride, void* workspace, size_t workspace_bytes, void* stream,
+                bool static_scratch = false) {
   int st = check_kv(kv, num_q_heads, out != nullptr);
   if (st != KVSEL_OK) return st;
   if (!q) return fail(KVSEL_ERR_INVALID, "q is NULL");
@@ -162,12 +187,26 @@ int decode_impl(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads, fl
   const bool need_scratch = probs == nullptr && cum != nullptr;
   const kvsel::DecodePlan plan = kvsel::plan_decode(kv->num_seqs, kv->num_kv_heads, num_q_heads,
                                                     kv->head_dim, kv->max_seq_len, need_scratch);
-  if (!workspace || workspace_bytes < plan.total_bytes)
+  if (static_scratch) {
+    if (plan.total_bytes > (size_t)KVSEL_NOALLOC_SCRATCH_BYTES)
+      return fail(KVSEL_ERR_WORKSPACE,
+                  "this call needs %zu bytes of scratch; the static scratch holds %zu (use "
+                  "kvsel_decode_attn_scores with a workspace)",
+                  plan.total_bytes, (size_t)KVSEL_NOALLOC_SCRATCH_BYTES);
+  } else if (!workspace || workspace_bytes < plan.total_bytes) {
     return fail(KVSEL_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes,
                 plan.total_bytes);
+  }
   int dev = 0;
   st = check_device(&dev);
   if (st != KVSEL_OK) return st;
+  if (static_scratch) {
+    // Nothing in the scratch has to start at zero: the normalisation's posts
+    // validate themselves and the combine zeroes them after every pass (the
+    // array is zero when the library loads).
+    st = scratch_address(dev, &workspace);
+    if (st != KVSEL_OK) return st;
+  }
   kvsel::DecodeArgs a{};
   a.k_pages = kv->k_pages;
   a.v_pages = kv->v_pages;
@@ -205,6 +244,16 @@ int decode_impl(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads, fl
 }
 
 }  // namespace
+
+int kvsel_decode_attn_scores_noalloc(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads,
+                                     float scale, float* out, float* lse, float* probs,
+                                     int64_t probs_stride, int32_t emit, float* cum, int64_t cum_stride,
+                                     float decay, void* stream) {
+  // The workspace variant's checks, then the scratch size, all before any
+  // HIP call; the static array takes the caller workspace's place.
+  return decode_impl(kv, q, num_q_heads, scale, out, lse, probs, probs_stride, emit, cum, cum_stride, decay,
+                     0, nullptr, nullptr, 0, 0, nullptr, 0, stream, /*static_scratch=*/true);
+}
 
 int kvsel_decode_attn_scores(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads,
                              float scale, float* out, float* lse, float* probs,

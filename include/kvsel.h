@@ -123,6 +123,33 @@ int kvsel_decode_attn_scores(const kvsel_paged_kv* kv, const void* q, int32_t nu
                              int64_t probs_stride, int32_t emit, float* cum, int64_t cum_stride,
                              float decay, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * kvsel_decode_attn_scores without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP-graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The call computes exactly what
+ * kvsel_decode_attn_scores computes (same kernels) and allocates nothing
+ * (no hipMalloc / hipFree, no allocating library routine).  Its scratch is a
+ * static device array of KVSEL_NOALLOC_SCRATCH_BYTES that every device the
+ * library runs on holds until the process ends; its device address is looked
+ * up once per device, on that device's first call.
+ *   Size limit: calls whose workspace (kvsel_decode_workspace_bytes with
+ *   probs_given = (probs != NULL || cum == NULL)) exceeds the array return
+ *   KVSEL_ERR_WORKSPACE before any HIP call.  The 70B-shape layer (8 x 32K,
+ *   64/8 heads, probs given) needs ~9 MB; cum without probs adds
+ *   num_seqs * num_q_heads * max_seq_len * 4 bytes.
+ *   Sharing: all calls on one device share its array, which keeps the last
+ *   call's contents; calls that overlap in time on one device (different
+ *   streams or threads) race and give undefined results.  Stream-ordered
+ *   calls are safe.
+ * Arguments, results and other errors as kvsel_decode_attn_scores.
+ * ------------------------------------------------------------------------ */
+#define KVSEL_NOALLOC_SCRATCH_BYTES (96u << 20)
+
+int kvsel_decode_attn_scores_noalloc(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads,
+                                     float scale, float* out, float* lse, float* probs,
+                                     int64_t probs_stride, int32_t emit, float* cum, int64_t cum_stride,
+                                     float decay, void* stream);
+
 /* Workspace bytes for kvsel_decode_attn_scores (0 if the arguments are
  * invalid).  probs_given = 0 adds the logits scratch needed when cum is
  * fused without a caller probs buffer (an upper bound for every call). */

@@ -299,3 +299,28 @@ def test_indexer_fp8_validation():
              None) == K.KVSEL_ERR_UNSUPPORTED
     # the other calls refuse FP8 pages
     assert _decode(_kv(dtype=K.KVSEL_FP8_E4M3)) == K.KVSEL_ERR_UNSUPPORTED
+
+
+def test_noalloc_decode_rejects_before_hip():
+    """The allocation-free decode validates like the workspace variant and
+    rejects a call whose workspace would exceed the static scratch, all
+    before any HIP call.  The limit the binding states is the header's."""
+    import os
+    lib = K.library()
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", HEADER)).read()
+    m = re.search(r"#define KVSEL_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == K.NOALLOC_SCRATCH_BYTES
+
+    def call(kv, hq=32, probs=FAKE, cum=None, q=FAKE, out=FAKE):
+        return lib.kvsel_decode_attn_scores_noalloc(ctypes.byref(kv), q, hq, 0.1, out, None, probs,
+                                                    kv.max_seq_len, 0, cum, kv.max_seq_len, 1.0, None)
+    assert call(_kv(), q=None) == K.KVSEL_ERR_INVALID
+    assert call(_kv(v_pages=None)) == K.KVSEL_ERR_INVALID
+    assert call(_kv(), hq=30) == K.KVSEL_ERR_INVALID
+    assert call(_kv(head_dim=96)) == K.KVSEL_ERR_UNSUPPORTED
+    # 8 x 64 heads x 1M keys with cum and no probs: a 2 GiB logits scratch
+    big = _kv(num_seqs=8, max_seq_len=1 << 20, max_pages_per_seq=1 << 16)
+    assert call(big, hq=64, probs=None, cum=FAKE) == K.KVSEL_ERR_WORKSPACE
+    assert b"static scratch" in lib.kvsel_last_error()
+    # the workspace the same call would need, for comparison
+    assert lib.kvsel_decode_workspace_bytes(ctypes.byref(big), 64, 0) > K.NOALLOC_SCRATCH_BYTES
