@@ -17,7 +17,9 @@ from typing import Optional
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkvsel.so")
+# KVSEL_LIBRARY names another build of the same library (the tests load the
+# host-AddressSanitizer build this way); there is no fallback either way.
+LIB_PATH = os.environ.get("KVSEL_LIBRARY") or os.path.join(HERE, "libkvsel.so")
 
 KVSEL_OK, KVSEL_ERR_INVALID, KVSEL_ERR_UNSUPPORTED, KVSEL_ERR_WORKSPACE, KVSEL_ERR_HIP = 0, -1, -2, -3, -4
 KVSEL_F32, KVSEL_BF16, KVSEL_FP8_E4M3 = 0, 1, 2
@@ -34,7 +36,7 @@ EXPORTED = (
     "kvsel_accumulate",
     "kvsel_block_aggregate", "kvsel_select_keep", "kvsel_select_workspace_bytes",
     "kvsel_snapkv_vote", "kvsel_snapkv_workspace_bytes", "kvsel_sparse_attn",
-    "kvsel_sparse_workspace_bytes", "kvsel_quest_summarize", "kvsel_quest_select",
+    "kvsel_sparse_workspace_bytes", "kvsel_quest_summarize", "kvsel_quest_select", "kvsel_quest_select_causal",
     "kvsel_quest_workspace_bytes", "kvsel_accumulate_ex", "kvsel_block_aggregate_ex", "kvsel_select_threshold", "kvsel_block_update", "kvsel_read_probe",
     "kvsel_union_keep", "kvsel_indexer_scores_fp8", "kvsel_h2o_step", "kvsel_h2o_workspace_bytes", "kvsel_set_sync_wait_us",
     "kvsel_status_string", "kvsel_last_error",
@@ -81,6 +83,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvsel_sparse_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "kvsel_quest_summarize": (ctypes.c_int, [D, I32, P, P]),
         "kvsel_quest_select": (ctypes.c_int, [D, P, P, I32, I32, P, I64, P, I64, P, P, SZ, P]),
+        "kvsel_quest_select_causal": (ctypes.c_int, [D, P, P, I32, I32, P, P, I64, P, I64, P, P, SZ, P]),
         "kvsel_quest_workspace_bytes": (SZ, [D, I32, I32]),
         "kvsel_h2o_step": (ctypes.c_int, [D, P, I32, F, P, P, P, I64, I32, I32, I32, P, F, P, P, P, SZ, P]),
         "kvsel_h2o_workspace_bytes": (SZ, [D, I32, I64, I32, I32, I32]),
@@ -347,6 +350,23 @@ def quest_select(kv: PagedKV, summary: torch.Tensor, q: torch.Tensor, num_q_head
     ws, wsb = _workspace(quest_workspace_bytes(kv, num_q_heads, budget_pages), q.device, workspace)
     _check(_LIB.kvsel_quest_select(
         kv.ref(), _ptr(summary, None, "summary"), _ptr(q, None, "q"), num_q_heads, int(budget_pages),
+        _ptr(bounds, torch.float32, "bounds"), 0 if bounds is None else bounds.shape[-1],
+        _ptr(out_idx, torch.int32, "out_idx"), out_idx.shape[-1], _ptr(out_count, torch.int32, "out_count"),
+        _ptr(ws, None, "workspace"), wsb, _stream(stream)))
+
+
+def quest_select_causal(kv: PagedKV, summary: torch.Tensor, q: torch.Tensor, num_q_heads: int, budget_pages: int,
+                        query_pos: torch.Tensor, out_idx: torch.Tensor, out_count: torch.Tensor,
+                        bounds: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                        stream=None) -> None:
+    """kvsel_quest_select_causal: as quest_select over all cached positions,
+    then only positions <= query_pos[b] (``[B]`` int32) are kept."""
+    if q.dtype != kv.dtype or summary.dtype != kv.dtype:
+        raise TypeError("q and summary must have the cache dtype")
+    ws, wsb = _workspace(quest_workspace_bytes(kv, num_q_heads, budget_pages), q.device, workspace)
+    _check(_LIB.kvsel_quest_select_causal(
+        kv.ref(), _ptr(summary, None, "summary"), _ptr(q, None, "q"), num_q_heads, int(budget_pages),
+        _ptr(query_pos, torch.int32, "query_pos"),
         _ptr(bounds, torch.float32, "bounds"), 0 if bounds is None else bounds.shape[-1],
         _ptr(out_idx, torch.int32, "out_idx"), out_idx.shape[-1], _ptr(out_count, torch.int32, "out_count"),
         _ptr(ws, None, "workspace"), wsb, _stream(stream)))

@@ -36,25 +36,35 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str, build_dir: str = BUILD_DIR, defines=()) -> str:
+# Host-side AddressSanitizer for the CPU tests of the C ABI: only the host
+# pass is instrumented (the device code is built as usual).
+HOST_ASAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+ASAN_OUT = os.path.join(HERE, "_build_asan", "libkvsel_asan.so")
+
+
+def _compile(src: str, build_dir: str = BUILD_DIR, defines=(), extra=()) -> str:
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, *[f"-D{d}" for d in defines], "-x", "hip", "-c", src, "-o", obj]
+    cmd = [_hipcc(), *COMMON, *extra, *[f"-D{d}" for d in defines], "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False, out: str = OUT, build_dir: str = BUILD_DIR, defines=()) -> str:
+def build(verbose: bool = False, out: str = OUT, build_dir: str = BUILD_DIR, defines=(),
+          host_asan: bool = False) -> str:
     """Compile every source and link ``out``.  ``defines`` are extra -D
-    tuning macros (the defaults in the sources are the shipped values)."""
+    tuning macros (the defaults in the sources are the shipped values).
+    ``host_asan`` instruments the host code with AddressSanitizer (a test
+    build: load it with the sanitizer runtime preloaded)."""
     os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
+    extra = HOST_ASAN if host_asan else []
     jobs = min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, build_dir, defines), srcs))
+        objs = list(ex.map(lambda s: _compile(s, build_dir, defines, extra), srcs))
     tmp = out + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

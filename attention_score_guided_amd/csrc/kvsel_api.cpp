@@ -612,10 +612,12 @@ size_t kvsel_quest_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads
   return kvsel::quest_workspace_bytes(kv->num_seqs, num_q_heads, kv->page_size, kv->max_seq_len, budget_pages);
 }
 
-int kvsel_quest_select(const kvsel_paged_kv* kv, const void* summary, const void* q, int32_t num_q_heads,
-                       int32_t budget_pages, float* bounds, int64_t bounds_stride, int32_t* out_idx,
-                       int64_t out_stride, int32_t* out_count, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+namespace {
+
+int quest_select_impl(const kvsel_paged_kv* kv, const void* summary, const void* q, int32_t num_q_heads,
+                      int32_t budget_pages, const int32_t* query_pos, float* bounds, int64_t bounds_stride,
+                      int32_t* out_idx, int64_t out_stride, int32_t* out_count, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   int st = check_kv(kv, num_q_heads, false);
   if (st != KVSEL_OK) return st;
   if (!summary || !q || !out_idx || !out_count) return fail(KVSEL_ERR_INVALID, "NULL pointer argument");
@@ -639,10 +641,29 @@ int kvsel_quest_select(const kvsel_paged_kv* kv, const void* summary, const void
   kvsel::QuestArgs a{kv->k_pages, kv->block_table, kv->seq_lens, kv->num_seqs, kv->num_kv_heads,
                      num_q_heads, kv->head_dim, kv->page_size, kv->max_pages_per_seq,
                      kv->max_seq_len, kv->dtype == KVSEL_BF16};
-  return hip_status(kvsel::launch_quest_select(a, summary, q, budget_pages, bounds, bounds_stride, out_idx,
-                                               out_stride, out_count, workspace,
+  return hip_status(kvsel::launch_quest_select(a, summary, q, budget_pages, query_pos, bounds, bounds_stride,
+                                               out_idx, out_stride, out_count, workspace,
                                                static_cast<hipStream_t>(stream)),
                     "quest_select launch");
+}
+
+}  // namespace
+
+int kvsel_quest_select(const kvsel_paged_kv* kv, const void* summary, const void* q, int32_t num_q_heads,
+                       int32_t budget_pages, float* bounds, int64_t bounds_stride, int32_t* out_idx,
+                       int64_t out_stride, int32_t* out_count, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return quest_select_impl(kv, summary, q, num_q_heads, budget_pages, nullptr, bounds, bounds_stride, out_idx,
+                           out_stride, out_count, workspace, workspace_bytes, stream);
+}
+
+int kvsel_quest_select_causal(const kvsel_paged_kv* kv, const void* summary, const void* q, int32_t num_q_heads,
+                              int32_t budget_pages, const int32_t* query_pos, float* bounds,
+                              int64_t bounds_stride, int32_t* out_idx, int64_t out_stride, int32_t* out_count,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!query_pos) return fail(KVSEL_ERR_INVALID, "query_pos is NULL");
+  return quest_select_impl(kv, summary, q, num_q_heads, budget_pages, query_pos, bounds, bounds_stride, out_idx,
+                           out_stride, out_count, workspace, workspace_bytes, stream);
 }
 
 size_t kvsel_h2o_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads, int64_t slot_stride,

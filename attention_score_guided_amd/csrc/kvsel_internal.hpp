@@ -149,8 +149,8 @@ struct QuestArgs {
 hipError_t launch_quest_summary(const QuestArgs& a, void* summary, int first_page, hipStream_t stream);
 size_t quest_workspace_bytes(int num_seqs, int num_q_heads, int page_size, int max_seq_len, int budget_pages);
 hipError_t launch_quest_select(const QuestArgs& a, const void* summary, const void* q, int budget_pages,
-                               float* bounds, int64_t bounds_stride, int32_t* out_idx, int64_t out_stride,
-                               int32_t* out_count, void* workspace, hipStream_t stream);
+                               const int32_t* query_pos, float* bounds, int64_t bounds_stride, int32_t* out_idx,
+                               int64_t out_stride, int32_t* out_count, void* workspace, hipStream_t stream);
 
 // H2O decode step with per-step eviction over per-KV-head slot lists.
 struct H2oArgs {

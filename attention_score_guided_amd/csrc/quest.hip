@@ -210,6 +210,7 @@ __global__ __launch_bounds__(kQThreads) void quest_bounds_kernel(BoundParams p) 
 
 struct ExpandParams {
   const int32_t* seq_lens;
+  const int32_t* query_pos;  // [B] or null: keep only positions <= query_pos[b]
   const int32_t* page_idx;   // [rows][page_stride] ascending chosen pages
   const int32_t* page_cnt;   // [rows] or null (no whole page anywhere)
   int page_stride;
@@ -230,9 +231,26 @@ __global__ __launch_bounds__(kQThreads) void quest_expand_kernel(ExpandParams p)
   const int total = chosen + (L - n_full * P);
   const int32_t* pi = p.page_idx + (size_t)r * p.page_stride;
   int32_t* out = p.out_idx + (size_t)r * p.out_stride;
-  for (int i = threadIdx.x; i < total; i += kQThreads)
-    out[i] = i < chosen ? (pi[i >> p.page_log2] << p.page_log2) + (i & (P - 1)) : n_full * P + (i - chosen);
-  if (threadIdx.x == 0) p.out_count[r] = total;
+  if (!p.query_pos) {
+    for (int i = threadIdx.x; i < total; i += kQThreads)
+      out[i] = i < chosen ? (pi[i >> p.page_log2] << p.page_log2) + (i & (P - 1)) : n_full * P + (i - chosen);
+    if (threadIdx.x == 0) p.out_count[r] = total;
+    return;
+  }
+  // The causal cut after the choice: the list is ascending, so the positions
+  // <= query_pos form a prefix; every thread runs the same number of rounds
+  // so that the block-wide count sees each of them.
+  const int limit = p.query_pos[b];
+  int kept = 0;
+  for (int base = 0; base < total; base += kQThreads) {
+    const int i = base + threadIdx.x;
+    int v = 0;
+    if (i < total) v = i < chosen ? (pi[i >> p.page_log2] << p.page_log2) + (i & (P - 1)) : n_full * P + (i - chosen);
+    const bool in = i < total && v <= limit;
+    if (in) out[i] = v;
+    kept += __syncthreads_count(in);
+  }
+  if (threadIdx.x == 0) p.out_count[r] = kept;
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -302,8 +320,8 @@ size_t quest_workspace_bytes(int num_seqs, int num_q_heads, int page_size, int m
 }
 
 hipError_t launch_quest_select(const QuestArgs& a, const void* summary, const void* q, int budget_pages,
-                               float* bounds, int64_t bounds_stride, int32_t* out_idx, int64_t out_stride,
-                               int32_t* out_count, void* workspace, hipStream_t stream) {
+                               const int32_t* query_pos, float* bounds, int64_t bounds_stride, int32_t* out_idx,
+                               int64_t out_stride, int32_t* out_count, void* workspace, hipStream_t stream) {
   const size_t rows = (size_t)a.num_seqs * a.num_q_heads;
   const int max_whole = a.max_seq_len / a.page_size;
   const int kp = std::max(1, budget_pages);
@@ -356,6 +374,7 @@ hipError_t launch_quest_select(const QuestArgs& a, const void* summary, const vo
   }
   ExpandParams ep{};
   ep.seq_lens = a.seq_lens;
+  ep.query_pos = query_pos;
   ep.page_idx = page_idx;
   ep.page_cnt = max_whole > 0 ? page_cnt : nullptr;
   ep.page_stride = kp;

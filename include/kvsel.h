@@ -29,9 +29,15 @@
  *     call returns KVSEL_ERR_INVALID / _UNSUPPORTED / _WORKSPACE, launches
  *     nothing, and kvsel_last_error() (thread-local) says why.
  *   - Device-resident values (seq_lens, block tables, indices, budgets) are
- *     preconditions and are not read by the host: lengths must lie in
- *     [1, max_seq_len], block-table entries must name pages of the pool,
- *     indices must be < the row length.  Violating them is undefined.
+ *     preconditions and are not read by the host; each call lists its own
+ *     under "Preconditions".  In general: lengths lie in [1, max_seq_len],
+ *     block-table entries name pages of the pool, index lists hold distinct
+ *     positions < the row length, counts and budgets stay within the
+ *     host-known bounds passed beside them, scores are finite or -inf (no
+ *     NaN).  A violation gives undefined results and may make a kernel read
+ *     or write outside the caller's buffers (a page id outside the pool is
+ *     dereferenced as given); only the counts of kvsel_sparse_attn are
+ *     clamped, because that costs nothing.
  *   - Results are bitwise reproducible for identical inputs (no float
  *     atomics; every output element has exactly one writer).
  *   - Strides are in elements.  Row-major layouts are spelled out per call.
@@ -111,6 +117,9 @@ typedef struct {
  *   workspace: >= kvsel_decode_workspace_bytes(kv, num_q_heads,
  *          probs != NULL || cum == NULL) bytes of device memory, 256-byte
  *          aligned, contents ignored.
+ * Preconditions: 1 <= seq_lens[b] <= max_seq_len; block_table[b][p] names a
+ * page of k_pages (and v_pages) for every p < ceil(L_b / page_size); probs,
+ * cum and workspace do not overlap each other or the inputs.
  * Supported: head_dim 64/128; dtype F32/BF16; G a power of two <= 8 or a
  * multiple of 8.  Errors: INVALID (NULL kv/q/k_pages/block_table/seq_lens,
  * dims <= 0, num_q_heads % num_kv_heads != 0, stride < max_seq_len,
@@ -161,7 +170,8 @@ size_t kvsel_decode_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_head
  * decay aggregation of [OFFLOAD] §2.1):
  *   cum[b][c][j] = decay * cum[b][c][j] + sum_{h: h / G == c} probs[b][h][j],
  * for j < seq_lens[b].  probs [num_seqs][num_q_heads][probs_stride] f32,
- * cum [num_seqs][num_kv_heads][cum_stride] f32 (in place).  Errors: INVALID.
+ * cum [num_seqs][num_kv_heads][cum_stride] f32 (in place).
+ * Preconditions: 1 <= seq_lens[b] <= max_seq_len.  Errors: INVALID.
  * ------------------------------------------------------------------------ */
 int kvsel_accumulate(const float* probs, int64_t probs_stride, const int32_t* seq_lens,
                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -207,6 +217,7 @@ int kvsel_decode_attn_scores_agg(const kvsel_paged_kv* kv, const void* q, int32_
  *   accumulate = 1 adds into out_* (e.g. a sum over layers); 0 overwrites.
  * Blocks n >= ceil(L_b / block_size) are left untouched.  Either output may
  * be NULL (not both).  out_stride >= ceil(max_seq_len / block_size).
+ * Preconditions: 1 <= seq_lens[b] <= max_seq_len.
  * Errors: INVALID.
  * ------------------------------------------------------------------------ */
 int kvsel_block_aggregate(const float* scores, int64_t score_stride, const int32_t* seq_lens,
@@ -239,6 +250,9 @@ int kvsel_block_aggregate(const float* scores, int64_t score_stride, const int32
  *   out_stride >= min(max_len, max(max_budget, sinks + window)) in ROWS mode
  *   (budgets[r] <= max_budget is a precondition) and >= max_len in
  *   GLOBAL_PERCENTILE mode.
+ *   Preconditions: 1 <= lengths[r] <= max_len; 0 <= budgets[r] <= max_budget;
+ *   scores[r][j] for j < lengths[r] finite or -inf (NaN has no place in the
+ *   order).
  *   workspace: >= kvsel_select_workspace_bytes(rows, max_len, mode) bytes
  *   (device memory, any contents; may be 0 bytes).  ROWS mode needs one only
  *   for shapes whose long rows it may split over several workgroups (at most
@@ -268,7 +282,8 @@ size_t kvsel_select_workspace_bytes(int32_t rows, int32_t max_len, int32_t mode)
  *   q_win [num_seqs][num_q_heads][window][head_dim] (dtype kv->dtype),
  *   votes [num_seqs][H_kv or H_q][votes_stride] f32; positions
  *   j >= L_b - window are left untouched.  votes_stride >= max_seq_len.
- * Precondition: window < L_b for every sequence.
+ * Preconditions: window < L_b <= max_seq_len for every sequence; block-table
+ * entries as for kvsel_decode_attn_scores.
  *   workspace: >= kvsel_snapkv_workspace_bytes(kv, num_q_heads, window).
  * Errors: INVALID (NULL pointers, window <= 0, window >= max_seq_len, even or
  * non-positive pool_kernel, votes_stride < max_seq_len), UNSUPPORTED (dtype
@@ -300,6 +315,9 @@ size_t kvsel_snapkv_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_head
  *           entry); entries past the count are left untouched.
  *   workspace: >= kvsel_sparse_workspace_bytes(num_seqs, num_q_heads,
  *           head_dim, max_count) bytes of device memory.
+ * Preconditions: the non-negative entries of a row are distinct positions
+ * < L_b (a repeat would count its key twice in the softmax); L_b and the
+ * block table as for kvsel_decode_attn_scores; counts as above.
  * Errors: INVALID, UNSUPPORTED (also max_count > 2^24), WORKSPACE, HIP.
  * ------------------------------------------------------------------------ */
 int kvsel_sparse_attn(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads,
@@ -467,6 +485,26 @@ int kvsel_quest_select(const kvsel_paged_kv* kv, const void* summary, const void
                        int32_t num_q_heads, int32_t budget_pages, float* bounds,
                        int64_t bounds_stride, int32_t* out_idx, int64_t out_stride,
                        int32_t* out_count, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Quest selection with the causal cut applied after the choice ([LONGCTX]
+ * sparse-attention experiment, the Quest strategy as its code states it: the
+ * pages are ranked among ALL whole pages of the prompt, the trailing partial
+ * page is always taken, and only then are positions after the query
+ * dropped).  Identical to kvsel_quest_select over the L_b cached positions,
+ * followed by keeping only the listed positions <= query_pos[b]; out_count
+ * counts what is kept (the list stays ascending).  This is how a prefill
+ * chunk's queries use summaries of the whole prompt; kvsel_quest_select is
+ * the decode reading (the query is the last position, nothing to cut).
+ *   query_pos [num_seqs] i32 device, 0 <= query_pos[b] < L_b (a
+ *             precondition; a value >= L_b - 1 cuts nothing).
+ * Other arguments, workspace and errors as kvsel_quest_select, plus INVALID
+ * for query_pos == NULL.
+ * ------------------------------------------------------------------------ */
+int kvsel_quest_select_causal(const kvsel_paged_kv* kv, const void* summary, const void* q,
+                              int32_t num_q_heads, int32_t budget_pages, const int32_t* query_pos,
+                              float* bounds, int64_t bounds_stride, int32_t* out_idx, int64_t out_stride,
+                              int32_t* out_count, void* workspace, size_t workspace_bytes, void* stream);
 
 size_t kvsel_quest_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads, int32_t budget_pages);
 

@@ -214,6 +214,14 @@ def test_quest_validation():
     assert need >= 2 * 32 * 64 * 4              # the bounds rows of every (sequence, head)
     assert call(wsb=need - 1) == K.KVSEL_ERR_WORKSPACE
 
+    def causal(qpos=FAKE, summary=FAKE, ws=FAKE, wsb=1 << 30, ostride=8 * 16 + 15):
+        return lib.kvsel_quest_select_causal(ctypes.byref(kv), summary, FAKE, 32, 8, qpos, None, 0, FAKE,
+                                             ostride, FAKE, ws, wsb, None)
+    assert causal(qpos=None) == K.KVSEL_ERR_INVALID
+    assert causal(summary=None) == K.KVSEL_ERR_INVALID
+    assert causal(ostride=8 * 16 + 14) == K.KVSEL_ERR_INVALID
+    assert causal(ws=None) == K.KVSEL_ERR_WORKSPACE
+
 
 def test_h2o_validation():
     lib = K.library()

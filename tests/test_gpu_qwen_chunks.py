@@ -165,3 +165,59 @@ def test_qwen_like_quest_on_last_queries():
             sets.append(got)
         o_out, _ = O.sparse_attention(Qd[:, p], Kd, Vd, sets, scale)
         assert rel_l2(f64(out[i]), o_out) < OUT_TOL
+
+
+def test_qwen_like_quest_literal_reading_on_last_queries():
+    """The Quest cell of the experiment as its code states it: the 16 pages
+    are ranked among ALL whole pages of the 1600-token prompt (summaries of
+    the whole prompt), and only then are positions after the query dropped
+    (kvsel_quest_select_causal).  Sets against oracle.quest_page_selection on
+    the full keys: any difference must be a page whose bound lies within
+    rounding of the 16th bound.  Outputs against the oracle's sparse
+    attention on the GPU's sets."""
+    K = _K()
+    cfg = synth.qwen_like_layer()
+    Kd, Vd, Qd = f64(cfg["K"]), f64(cfg["V"]), f64(cfg["Q"])
+    Hkv, N, d = Kd.shape
+    Hq, C, scale, P, budget = cfg["num_q_heads"], 64, cfg["scale"], 16, 16
+    G = Hq // Hkv
+    kp, vp, bt = _paged(cfg)
+    full = K.PagedKV(kp, vp, bt.cuda(), torch.tensor([N], dtype=torch.int32, device="cuda"), P, N)
+    summary = torch.empty((kp.shape[0], Hkv, 2, d), dtype=torch.bfloat16, device="cuda")
+    K.quest_summarize(full, summary)
+    pos = np.arange(N - C, N)
+    kv = K.PagedKV(kp, vp, bt.repeat(C, 1).cuda(), torch.full((C,), N, dtype=torch.int32, device="cuda"), P, N)
+    qpos = torch.tensor(pos, dtype=torch.int32, device="cuda")
+    q = cfg["Q"][:, N - C:].permute(1, 0, 2).contiguous().cuda()
+    idx = torch.full((C, Hq, budget * P + P - 1), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.empty((C, Hq), dtype=torch.int32, device="cuda")
+    bounds = torch.empty((C, Hq, N // P), device="cuda")
+    K.quest_select_causal(kv, summary, q, Hq, budget, qpos, idx, cnt, bounds=bounds)
+    out = torch.empty((C, Hq, d), device="cuda")
+    K.sparse_attn(kv, q, Hq, idx, cnt, idx.shape[-1], scale, out)
+    torch.cuda.synchronize()
+    from tests.test_gpu_quest import BOUND_TOL
+    worst = 0.0
+    for i in range(0, C, 3):
+        p = int(pos[i])
+        sets = []
+        for h in range(Hq):
+            Kh = Kd[h // G]
+            got = idx[i, h, :int(cnt[i, h])].cpu().numpy()
+            assert (idx[i, h, int(cnt[i, h]):] == -7).all()
+            assert np.all(np.diff(got) > 0) and got.max() <= p
+            kmin, kmax = O.quest_page_summary(Kh, P)
+            want_b = O.quest_page_bounds(Qd[h, p], kmin, kmax)
+            tol = BOUND_TOL * (np.abs(Qd[h, p]) * np.maximum(np.abs(kmin), np.abs(kmax))).sum(axis=1).max()
+            assert np.max(np.abs(f64(bounds[i, h]) - want_b)) <= tol
+            want = O.quest_page_selection(Qd[h, p], Kh, p, budget * P, P)
+            if got.tolist() != want.tolist():
+                kth = np.sort(want_b)[::-1][budget - 1]
+                gs, ws_ = set(got.tolist()), set(want.tolist())
+                for pg in sorted({j // P for j in gs ^ ws_}):
+                    assert abs(want_b[pg] - kth) <= 2 * tol, (i, h, pg, want_b[pg], kth)
+                    worst = max(worst, abs(want_b[pg] - kth) / tol)
+            sets.append(got)
+        o_out, _ = O.sparse_attention(Qd[:, p], Kd, Vd, sets, scale)
+        assert rel_l2(f64(out[i]), o_out) < OUT_TOL
+    note(f"literal Quest: page swaps at most {worst:.2f} of the bound tolerance from the cut")
