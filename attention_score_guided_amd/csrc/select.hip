@@ -116,21 +116,20 @@ struct RowsParams {
 
 // LDS of the one-workgroup row selection.
 struct RowLds {
-  int hist[kSubHist][2048];
+  __attribute__((aligned(16))) int hist[kSubHist][2048];
   int ws[kRowThreads / kWave];
   int res[2];
 };
 
-// Selection of row r by one workgroup of kRowThreads threads (every thread
-// calls it).
-__device__ void select_row(const RowsParams& p, int r, RowLds& sh) {
+// Selection of row r with budget B by one workgroup of kRowThreads threads
+// (every thread calls it).
+__device__ void select_row(const RowsParams& p, int r, RowLds& sh, int B) {
   constexpr int NT = kRowThreads;
   auto& hist = sh.hist;
   int* ws = sh.ws;
   int* res = sh.res;
   const int tid = threadIdx.x;
   const int n = p.lengths[r];
-  const int B = p.budgets ? p.budgets[r] : p.max_budget;
   const float* row = p.scores + (size_t)r * p.stride;
   int32_t* out = p.out_idx + (size_t)r * p.out_stride;
   const int lo = min(p.sinks, n);
@@ -264,9 +263,71 @@ __device__ void select_row(const RowsParams& p, int r, RowLds& sh) {
   if (tid == 0) p.out_count[r] = out_base;
 }
 
+// Rows of at most kRowThreads positions: one position per thread, its key
+// held in a register through the three radix passes (LDS histograms only,
+// no re-reads of the row), then the ordered output by block scans.  Same
+// result as the radix selection over global memory.
+constexpr int kSmallRow = kRowThreads;
+
+__device__ void select_row_small(const RowsParams& p, int r, RowLds& sh, int B) {
+  int* hist = sh.hist[0];
+  int* ws = sh.ws;
+  int* res = sh.res;
+  const int tid = threadIdx.x;
+  const int n = p.lengths[r];
+  const float* row = p.scores + (size_t)r * p.stride;
+  int32_t* out = p.out_idx + (size_t)r * p.out_stride;
+  const int lo = min(p.sinks, n);
+  const int hi = max(n - p.window, 0);
+  const bool keep_all = B >= n || hi <= lo;
+  const int fsize = keep_all ? n : lo + (n - hi);
+  const int k = keep_all ? 0 : max(0, B - fsize);
+  const bool mid = tid >= lo && tid < hi;
+  int keep;
+  if (keep_all || k == 0) {
+    keep = tid < n && (keep_all || !mid) ? 1 : 0;
+  } else {
+    const uint32_t key = mid ? order_key(row[tid]) : 0u;
+    uint32_t prefix = 0, pmask = 0;
+    int rank = k;
+    const int shifts[3] = {21, 10, 0};
+    const int widths[3] = {11, 11, 10};
+#pragma unroll
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shf = shifts[pass];
+      const uint32_t dmask = (1u << widths[pass]) - 1u;
+      const int nb = 1 << widths[pass];
+      for (int i = tid; i < nb; i += kRowThreads) hist[i] = 0;
+      __syncthreads();
+      if (mid && (key & pmask) == prefix) atomicAdd(&hist[(key >> shf) & dmask], 1);
+      __syncthreads();
+      int above;
+      const int d = find_digit<kRowThreads>(hist, nb, rank, ws, res, above);
+      rank -= above;
+      prefix |= (uint32_t)d << shf;
+      pmask |= dmask << shf;
+    }
+    // keys above tau are kept; of the keys equal to tau, the `rank` lowest
+    // positions
+    const bool eq = mid && key == prefix;
+    int eq_total;
+    const int eq_before = block_exclusive_scan<kRowThreads>(eq ? 1 : 0, ws, eq_total);
+    keep = tid < n && (!mid || key > prefix || (eq && eq_before < rank)) ? 1 : 0;
+  }
+  int total;
+  const int pos = block_exclusive_scan<kRowThreads>(keep, ws, total);
+  if (keep) out[pos] = tid;
+  if (tid == 0) p.out_count[r] = total;
+}
+
+__device__ __forceinline__ int row_budget(const RowsParams& p, int r) {
+  return p.budgets ? p.budgets[r] : p.max_budget;
+}
+
 __global__ __launch_bounds__(kRowThreads) void select_rows_kernel(RowsParams p) {
   __shared__ RowLds sh;
-  select_row(p, blockIdx.x, sh);
+  if (p.lengths[blockIdx.x] <= kSmallRow) select_row_small(p, blockIdx.x, sh, row_budget(p, blockIdx.x));
+  else select_row(p, blockIdx.x, sh, row_budget(p, blockIdx.x));
 }
 
 // ---- ROWS mode, split over workgroups (long rows, small budgets) ---------
@@ -276,12 +337,12 @@ __global__ __launch_bounds__(kRowThreads) void select_rows_kernel(RowsParams p) 
 //   1. histogram kernel: the first digit (top 11 bits of the key) of every
 //      middle position, one workgroup per (segment, row), LDS histograms
 //      folded into the row's global histogram with integer atomics;
-//   2. digit kernel (one workgroup per row): the boundary digit d0 and the
-//      rank still needed among the keys whose first digit is d0;
-//   3. compaction kernel: per 4096-position segment, the middle positions
-//      whose first digit is above d0 (kept) or equal to it (candidates) are
-//      stored in position order with their keys, in bounded slots;
-//   4. final kernel (one workgroup per row): the last two digits among the
+//   2. compaction kernel: every workgroup finds the boundary digit d0 and
+//      the rank still needed among the keys whose first digit is d0 from the
+//      row's histogram, then, per 4096-position segment, stores the middle
+//      positions whose first digit is above d0 (kept) or equal to it
+//      (candidates) in position order with their keys, in bounded slots;
+//   3. final kernel (one workgroup per row): the last two digits among the
 //      candidates in LDS give tau and the ties still needed; the stored
 //      positions are written out in order between the forced ranges.
 // With budgets of at most 1/8 of a row the stored positions are a small
@@ -349,12 +410,12 @@ __device__ __forceinline__ float4 load4(const float* row, bool vec, int j0, int 
   return make_float4(v[0], v[1], v[2], v[3]);
 }
 
-template <int PASS>
+// The first digit (top 11 bits of the order key) of every middle position of
+// one segment, counted in two LDS histograms (even and odd waves) and added
+// to the row's global histogram.
 __global__ __launch_bounds__(kSegThreads) void select_split_hist(SplitParams sp) {
-  constexpr int kShift[3] = {21, 10, 0};
-  constexpr int kWidth[3] = {11, 11, 10};
-  constexpr int sh = kShift[PASS];
-  constexpr uint32_t dmask = (1u << kWidth[PASS]) - 1u;
+  constexpr int sh = 21;
+  constexpr uint32_t dmask = 0x7FFu;
   __shared__ int hist[2][2048];
   const RowsParams& p = sp.rp;
   const int r = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
@@ -362,12 +423,6 @@ __global__ __launch_bounds__(kSegThreads) void select_split_hist(SplitParams sp)
   if (q.k == 0) return;
   const int j_lo = q.lo + s * sp.seg_len, j_hi = min(j_lo + sp.seg_len, q.hi);
   if (j_lo >= j_hi) return;
-  uint32_t prefix = 0, pmask = 0;
-  if (PASS > 0) {
-    const int4 st = sp.state[r];
-    prefix = (uint32_t)st.x;
-    pmask = (uint32_t)st.y;
-  }
   for (int i = tid; i < 2 * 2048; i += kSegThreads) (&hist[0][0])[i] = 0;
   __syncthreads();
   int* my = hist[(tid / kWave) & 1];
@@ -389,8 +444,7 @@ __global__ __launch_bounds__(kSegThreads) void select_split_hist(SplitParams sp)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const uint32_t kk = order_key(e[c]);
-        if (q0 + u * kSegThreads < q_hi && j + c >= j_lo && j + c < j_hi && (kk & pmask) == prefix)
-          atomicAdd(&my[(kk >> sh) & dmask], 1);
+        if (q0 + u * kSegThreads < q_hi && j + c >= j_lo && j + c < j_hi) atomicAdd(&my[(kk >> sh) & dmask], 1);
       }
     }
   }
@@ -400,39 +454,6 @@ __global__ __launch_bounds__(kSegThreads) void select_split_hist(SplitParams sp)
     const int c = hist[0][i] + hist[1][i];
     if (c) atomicAdd(&gh[i], (uint32_t)c);
   }
-}
-
-template <int PASS>
-__global__ __launch_bounds__(kSegThreads) void select_split_digit(SplitParams sp) {
-  constexpr int kShift[3] = {21, 10, 0};
-  constexpr int kWidth[3] = {11, 11, 10};
-  constexpr int sh = kShift[PASS];
-  constexpr int nb = 1 << kWidth[PASS];
-  __shared__ int hist[2048];
-  __shared__ int ws[kSegThreads / kWave];
-  __shared__ int res[2];
-  const int r = blockIdx.x, tid = threadIdx.x;
-  const RowPlan q = row_plan(sp.rp, r);
-  if (q.k == 0) return;
-  uint32_t* gh = sp.ghist + (size_t)r * 2048;
-  for (int i = tid; i < nb; i += kSegThreads) {
-    hist[i] = (int)gh[i];
-    gh[i] = 0u;                       // ready for the next pass (or the next call)
-  }
-  __syncthreads();
-  uint32_t prefix = 0, pmask = 0;
-  int rank = q.k;
-  if (PASS > 0) {
-    const int4 st = sp.state[r];
-    prefix = (uint32_t)st.x;
-    pmask = (uint32_t)st.y;
-    rank = st.z;
-  }
-  int above;
-  const int d = find_digit<kSegThreads>(hist, nb, rank, ws, res, above);
-  if (tid == 0)
-    sp.state[r] = make_int4((int)(prefix | ((uint32_t)d << sh)), (int)(pmask | ((uint32_t)(nb - 1) << sh)),
-                            rank - above, 0);
 }
 
 // The kOutSeg positions of segment s of row r, one float4 per thread and
@@ -455,20 +476,36 @@ __device__ __forceinline__ void load_out_seg(const SplitParams& sp, const RowPla
 __global__ __launch_bounds__(kSegThreads) void select_split_compact(SplitParams sp) {
   constexpr int IT = kOutSeg / (4 * kSegThreads);
   __shared__ int ws[kSegThreads / kWave];
+  __shared__ int hist[2048];
+  __shared__ int res[2];
   const RowsParams& p = sp.rp;
   const int r = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
   const RowPlan q = row_plan(p, r);
   if (q.k == 0) return;
   const int sb = s * kOutSeg, sb_hi = min(sb + kOutSeg, q.n);
   int2* cnt = sp.counts + (size_t)r * sp.n_oseg + s;
-  if (max(sb, q.lo) >= min(sb_hi, q.hi)) {
+  const bool empty = max(sb, q.lo) >= min(sb_hi, q.hi);
+  if (empty && s != 0) {
     if (tid == 0) *cnt = make_int2(0, 0);
     return;
   }
-  const uint32_t d0 = (uint32_t)sp.state[r].x >> 21;
+  // The segment's scores are requested first; meanwhile every workgroup of
+  // the row finds the boundary digit d0 (the first digit of the k-th largest
+  // middle key) from the row's complete first-digit histogram, and the
+  // row's first segment records it for the final kernel.
   const float* row = p.scores + (size_t)r * p.stride;
   float4 v[IT];
   load_out_seg(sp, q, row, sb, sb_hi, v);
+  const uint32_t* gh = sp.ghist + (size_t)r * 2048;
+  for (int i = tid; i < 2048; i += kSegThreads) hist[i] = (int)gh[i];
+  __syncthreads();
+  int above;
+  const uint32_t d0 = (uint32_t)find_digit<kSegThreads>(hist, 2048, q.k, ws, res, above);
+  if (s == 0 && tid == 0) sp.state[r] = make_int4((int)(d0 << 21), (int)(0x7FFu << 21), q.k - above, 0);
+  if (empty) {
+    if (tid == 0) *cnt = make_int2(0, 0);
+    return;
+  }
   uint2* slot = sp.slots + ((size_t)r * sp.n_oseg + s) * kCapSeg;
   int base = 0, n_cand = 0;
 #pragma unroll
@@ -529,7 +566,7 @@ __global__ __launch_bounds__(kRowThreads) void select_split_final(SplitParams sp
   const RowPlan q = row_plan(p, r);
   const int n_seg = (q.n + kOutSeg - 1) / kOutSeg;
   if (q.k == 0 || n_seg > kFinSegs) {
-    select_row(p, r, sh);
+    select_row(p, r, sh, row_budget(p, r));
     return;
   }
   int* ws = sh.ws;
@@ -539,7 +576,7 @@ __global__ __launch_bounds__(kRowThreads) void select_split_final(SplitParams sp
   if (tid < n_seg) seg_pre[tid] = pre;
   if (tid == 0) seg_pre[n_seg] = tot;
   if (__syncthreads_or(c.x > kCapSeg) || tot > kFinEnt) {
-    select_row(p, r, sh);
+    select_row(p, r, sh, row_budget(p, r));
     return;
   }
   // every entry's load is issued before any is stored
@@ -650,7 +687,7 @@ inline size_t split_layout(int rows, int max_len, size_t* o_state, size_t* o_cou
 }
 
 // The global histograms must start at zero: they are cleared here once per
-// call (the digit kernel leaves its row's histogram cleared again).
+// call.
 __global__ void select_split_zero(uint32_t* gh, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
     gh[i] = 0u;
@@ -668,8 +705,7 @@ hipError_t launch_split(const RowsParams& rp, int rows, int max_len, void* works
   const size_t nh = (size_t)rows * 2048;
   hipLaunchKernelGGL(select_split_zero, dim3((unsigned)std::min<size_t>((nh + 255) / 256, 1024)), dim3(256), 0,
                      stream, sp.ghist, nh);
-  hipLaunchKernelGGL(select_split_hist<0>, dim3(sp.n_seg, rows), dim3(kSegThreads), 0, stream, sp);
-  hipLaunchKernelGGL(select_split_digit<0>, dim3(rows), dim3(kSegThreads), 0, stream, sp);
+  hipLaunchKernelGGL(select_split_hist, dim3(sp.n_seg, rows), dim3(kSegThreads), 0, stream, sp);
   hipLaunchKernelGGL(select_split_compact, dim3(sp.n_oseg, rows), dim3(kSegThreads), 0, stream, sp);
   hipLaunchKernelGGL(select_split_final, dim3(rows), dim3(kRowThreads), 0, stream, sp);
   return hipGetLastError();
@@ -800,6 +836,144 @@ __global__ __launch_bounds__(kSelThreads) void global_output_kernel(const uint64
   if (threadIdx.x == 0) out_count[r] = base;
 }
 
+// ---- GLOBAL_PERCENTILE in one launch ----------------------------------------
+// The percentile keys of a row of n items are exactly 1/n, 2/n, ..., n/n,
+// whatever its scores: the scores only decide which item takes which key.
+// The global top K by (key desc, row asc) therefore fixes, from the lengths
+// alone, how many items m_r each row keeps, and the row keeps its m_r best
+// items by (score desc, position asc): those hold its m_r largest keys.
+// Every workgroup (one per row) finds the K-th largest key T from the lengths
+// by a 64-way search over the integer keys Q(k, n) = floor(k 2^43 / n) (exact
+// and order-preserving for n <= 2^20), derives its m_r, and runs the row
+// selection with budget m_r.  No workspace, no second launch.
+constexpr int kPctFastRows = 4096;   // rows whose lengths the search holds in LDS
+
+// Items of a row of n whose key Q(k, n) is >= T (T >= 1):
+// Q(k, n) >= T  <=>  k >= T n / 2^43  (T n < 2^64 for T <= 2^43 + 1, n <= 2^20).
+__device__ __forceinline__ long long pct_count_ge(uint64_t T, int n) {
+  const uint64_t kmin = (T * (uint64_t)n + ((1ull << 43) - 1)) >> 43;
+  const long long lo = kmin < 1 ? 1 : (long long)kmin;
+  return lo > n ? 0 : (long long)n - lo + 1;
+}
+
+__global__ __launch_bounds__(kRowThreads) void global_percentile_rows_kernel(RowsParams p, int rows, int K) {
+  __shared__ RowLds sh;
+  __shared__ int len_s[kPctFastRows];
+  __shared__ unsigned long long cnt_s[64];
+  __shared__ unsigned long long lohi_s[2];
+  const int tid = threadIdx.x, r = blockIdx.x;
+  if (rows <= kWave) {
+    // Up to 64 rows: one wave finds every row's share, lane i holding row
+    // i's length, without a barrier; the others wait at the one below.
+    __shared__ int m_s;
+    if (tid < kWave) {
+      const int ni = tid < rows ? p.lengths[tid] : 0;
+      int total = ni;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) total += __shfl_xor(total, off, kWave);
+      int mi;
+      if (K <= 0) {
+        mi = 0;
+      } else if (K >= total) {
+        mi = ni;
+      } else {
+        uint64_t lo = 1, hi = (1ull << 43) + 1;     // count_ge(lo) >= K > count_ge(hi)
+        while (hi - lo > 1) {
+          const uint64_t step = (hi - lo + 63) / 64;
+          const uint64_t t = lo + (uint64_t)tid * step;
+          long long cnt = 0;
+          for (int i = 0; i < rows; ++i) cnt += pct_count_ge(t, __shfl(ni, i, kWave));
+          const unsigned long long mask = __ballot(t < hi && cnt >= K);
+          const uint64_t nlo = lo + (uint64_t)(63 - __builtin_clzll(mask)) * step;
+          hi = nlo + step < hi ? nlo + step : hi;
+          lo = nlo;
+        }
+        const int g = tid < rows ? (int)pct_count_ge(lo + 1, ni) : 0;
+        const bool tie = tid < rows && pct_count_ge(lo, ni) > g;
+        int gt = g;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) gt += __shfl_xor(gt, off, kWave);
+        const unsigned long long tmask = __ballot(tie);
+        const int before = __popcll(tmask & ((1ull << tid) - 1ull));
+        mi = g + ((tie && before < K - gt) ? 1 : 0);
+      }
+      if (tid == r) m_s = mi;
+    }
+    __syncthreads();
+    const int m = m_s;
+    if (p.lengths[r] <= kSmallRow) select_row_small(p, r, sh, m);
+    else select_row(p, r, sh, m);
+    return;
+  }
+  for (int i = tid; i < rows; i += kRowThreads) len_s[i] = p.lengths[i];
+  if (tid < 64) cnt_s[tid] = 0;
+  __syncthreads();
+  long long part = 0;
+  for (int i = tid; i < rows; i += kRowThreads) part += len_s[i];
+  if (part) atomicAdd(&cnt_s[0], (unsigned long long)part);
+  __syncthreads();
+  const long long total = (long long)cnt_s[0];
+  __syncthreads();
+  const int n = len_s[r];
+  int m;
+  if (K <= 0) {
+    m = 0;
+  } else if (K >= total) {
+    m = n;
+  } else {
+    // count_ge(lo) >= K > count_ge(hi); each round tests 64 keys and keeps
+    // the sub-range where the count crosses K
+    uint64_t lo = 1, hi = (1ull << 43) + 1;
+    const int c = tid & 63;
+    while (hi - lo > 1) {
+      const uint64_t step = (hi - lo + 63) / 64;
+      if (tid < 64) cnt_s[tid] = 0;
+      __syncthreads();
+      const uint64_t t = lo + (uint64_t)c * step;
+      long long q = 0;
+      if (t < hi)
+        for (int i = tid >> 6; i < rows; i += kRowThreads / 64) q += pct_count_ge(t, len_s[i]);
+      if (q) atomicAdd(&cnt_s[c], (unsigned long long)q);
+      __syncthreads();
+      if (tid < kWave) {
+        // the counts fall with the key: the candidates still holding K form
+        // a prefix, and the highest lane of it gives the new range
+        const bool ok = lo + (uint64_t)tid * step < hi && (long long)cnt_s[tid] >= K;
+        const unsigned long long mask = __ballot(ok);
+        const int best = 63 - __builtin_clzll(mask);     // lane 0 always qualifies
+        if (tid == 0) {
+          const uint64_t nlo = lo + (uint64_t)best * step;
+          lohi_s[0] = nlo;
+          lohi_s[1] = nlo + step < hi ? nlo + step : hi;
+        }
+      }
+      __syncthreads();
+      lo = lohi_s[0];
+      hi = lohi_s[1];
+    }
+    // T = lo: every row keeps its keys > T, and the key equal to T (at most
+    // one per row) goes to the lowest rows until K is reached
+    if (tid < 2) cnt_s[tid] = 0;
+    __syncthreads();
+    long long gt = 0, ties_before = 0;
+    for (int i = tid; i < rows; i += kRowThreads) {
+      const long long g = pct_count_ge(lo + 1, len_s[i]);
+      gt += g;
+      if (i < r && pct_count_ge(lo, len_s[i]) > g) ++ties_before;
+    }
+    if (gt) atomicAdd(&cnt_s[0], (unsigned long long)gt);
+    if (ties_before) atomicAdd(&cnt_s[1], (unsigned long long)ties_before);
+    __syncthreads();
+    const long long ties_needed = K - (long long)cnt_s[0];
+    const long long g_r = pct_count_ge(lo + 1, n);
+    const bool tie_r = pct_count_ge(lo, n) > g_r;
+    m = (int)g_r + ((tie_r && (long long)cnt_s[1] < ties_needed) ? 1 : 0);
+    __syncthreads();
+  }
+  if (n <= kSmallRow) select_row_small(p, r, sh, m);
+  else select_row(p, r, sh, m);
+}
+
 }  // namespace
 
 size_t select_workspace_bytes(int rows, int max_len, int mode) {
@@ -817,6 +991,12 @@ hipError_t launch_select(const float* scores, int64_t stride, const int32_t* len
                   out_count};
     if (use_split(rows, max_len, max_budget)) return launch_split(rp, rows, max_len, workspace, stream);
     hipLaunchKernelGGL(select_rows_kernel, dim3(rows), dim3(kRowThreads), 0, stream, rp);
+    return hipGetLastError();
+  }
+  if (rows <= kPctFastRows) {
+    RowsParams rp{scores, stride, lengths, nullptr, 0, 0, 0, out_idx, out_stride, out_count};
+    hipLaunchKernelGGL(global_percentile_rows_kernel, dim3(rows), dim3(kRowThreads), 0, stream, rp, rows,
+                       global_budget);
     return hipGetLastError();
   }
   uint8_t* ws = static_cast<uint8_t*>(workspace);

@@ -29,7 +29,9 @@ def test_graph_replays_match_eager():
     scale = 1 / math.sqrt(d)
     n_blk = L // BS
     out = torch.empty((B, Hq, d), device="cuda")
-    probs = torch.empty((B, Hq, L), device="cuda")
+    # zero-filled: positions past a sequence's length are left untouched, and
+    # uninitialised memory there may hold NaNs, which never compare equal
+    probs = torch.zeros((B, Hq, L), device="cuda")
     cum = torch.zeros((layers_n, B, Hkv, L), device="cuda")
     agg = torch.zeros((B, n_blk), device="cuda")
     blk_lens = ((lens + BS - 1) // BS).to(torch.int32)

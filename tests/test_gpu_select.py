@@ -94,12 +94,28 @@ def test_rows_llama3_8b_keep_shape():
     _check_rows(scores, lengths, 4, 512, budgets, idx, cnt)
 
 
-@pytest.mark.parametrize("seed", range(4))
-def test_global_percentile(seed):
+GLOBAL_SHAPES = {
+    # id: (lengths, global budget); None = drawn from the seed
+    "70b_blocks": ([512] * 8, 1024),                               # the 70B block-selection shape
+    "shared_rationals": ([4, 8, 16, 12, 6, 24, 3, 48], 31),         # equal keys across rows: row order decides
+    "shared_rationals_k0": ([4, 8, 16, 12], 0),
+    "all_items": ([7, 1, 300, 64], 372),
+    "all_but_one": ([7, 1, 300, 64], 371),
+    "single_items": ([1] * 40, 17),
+    "many_rows": ([int(x) for x in np.random.default_rng(5).integers(1, 65, size=300)], 4000),
+    "past_lds_rows": ([2] * 5000, 3333),                            # more rows than the one-launch search holds
+    "random_1": None, "random_2": None, "random_3": None, "random_4": None, "random_5": None,
+}
+
+
+@pytest.mark.parametrize("shape", list(GLOBAL_SHAPES))
+def test_global_percentile(shape):
     K = _K()
+    seed = list(GLOBAL_SHAPES).index(shape)
     rng = np.random.default_rng(200 + seed)
-    if seed == 0:
-        rows, lengths, gb = 8, [512] * 8, 1024          # the 70B block-selection shape
+    if GLOBAL_SHAPES[shape] is not None:
+        lengths, gb = GLOBAL_SHAPES[shape]
+        rows = len(lengths)
     else:
         rows = int(rng.integers(1, 12))
         lengths = [int(x) for x in rng.integers(1, 700, size=rows)]
