@@ -273,6 +273,13 @@ def long_context_workload(torch, K, synth, args) -> dict:
         vote()
         K.select_keep(vrows, vlens, Lq - W, 0, 0, None, 4096, vkeep, vcnt, workspace=ws_vs)
 
+    if args.counters:
+        # counter-collection mode: three votes and nothing else
+        for _ in range(3):
+            vote()
+        torch.cuda.synchronize()
+        log("counters mode done: snapkv vote x3 (128K case)")
+        return None
     t_vote = timed(torch, vote, 10, warmup=3)
     t_vote_sel = timed(torch, vote_select, 10, warmup=1)
     k_bytes = Bq * HKVq * Lq * 128 * 2
@@ -811,7 +818,8 @@ def main() -> int:
                     help="the default is the 70B decode step; the others report their own line")
     ap.add_argument("--counters", action="store_true",
                     help="counter-collection mode: one layer, 3 decode calls, then a plain 1 GiB "
-                         "device copy used to calibrate FETCH_SIZE / WRITE_SIZE; prints no JSON")
+                         "device copy used to calibrate FETCH_SIZE / WRITE_SIZE (with --workload "
+                         "long_context_128k: three SnapKV votes); prints no JSON")
     args = ap.parse_args()
     if args.steps is None:
         args.steps = 256 if args.workload == "llama3_8b_steps" else 20
@@ -827,6 +835,9 @@ def main() -> int:
         print("bench.py needs an MI355X GPU", file=sys.stderr)
         return 2
 
+    if args.counters and args.workload == "long_context_128k":
+        long_context_workload(torch, K, synth, args)
+        return 0
     if args.counters:
         return counters_mode(torch, K, synth)
     if args.workload == "long_context_128k":
