@@ -121,10 +121,10 @@ struct RowLds {
   int res[2];
 };
 
-// Selection of row r with budget B by one workgroup of kRowThreads threads
-// (every thread calls it).
+// Selection of row r with budget B by one workgroup of NT threads (every
+// thread calls it; NT a multiple of 256 up to kRowThreads).
+template <int NT = kRowThreads>
 __device__ void select_row(const RowsParams& p, int r, RowLds& sh, int B) {
-  constexpr int NT = kRowThreads;
   auto& hist = sh.hist;
   int* ws = sh.ws;
   int* res = sh.res;
@@ -332,35 +332,43 @@ __global__ __launch_bounds__(kRowThreads) void select_rows_kernel(RowsParams p) 
 
 // ---- ROWS mode, split over workgroups (long rows, small budgets) ---------
 // One workgroup per row leaves most of the chip idle when a few hundred rows
-// are each tens of thousands of positions long.  Rows are then cut into
-// segments:
-//   1. histogram kernel: the first digit (top 11 bits of the key) of every
-//      middle position, one workgroup per (segment, row), LDS histograms
-//      folded into the row's global histogram with integer atomics;
-//   2. compaction kernel: every workgroup finds the boundary digit d0 and
-//      the rank still needed among the keys whose first digit is d0 from the
-//      row's histogram, then, per 4096-position segment, stores the middle
-//      positions whose first digit is above d0 (kept) or equal to it
-//      (candidates) in position order with their keys, in bounded slots;
-//   3. final kernel (one workgroup per row): the last two digits among the
-//      candidates in LDS give tau and the ties still needed; the stored
-//      positions are written out in order between the forced ranges.
-// With budgets of at most 1/8 of a row the stored positions are a small
-// fraction of it; a row with more stored positions than the final kernel
-// holds in LDS (a boundary digit shared by many positions) is selected by
-// the one-workgroup algorithm inside the final kernel.  Results are
-// identical either way.
-constexpr int kSegQuantum = 4096;      // segment lengths are multiples of this
-#ifndef KVSEL_SEG_TARGET
-#define KVSEL_SEG_TARGET 1024
-#endif
-constexpr int kSegTarget = KVSEL_SEG_TARGET;  // aim for about this many workgroups per kernel
-constexpr int kSegThreads = 256;
-constexpr int kOutSeg = 4096;          // compaction segment: 4 float4 per thread
-constexpr int kCapSeg = kOutSeg;       // entries stored per compaction segment: all of it, so
-                                       // keeps clustered in a few segments never overflow
-constexpr int kFinEnt = 12288;         // stored entries the final kernel holds in LDS
-constexpr int kFinSegs = kRowThreads;  // compaction segments per row the final kernel handles
+// are each tens of thousands of positions long, and reading every row twice
+// (a histogram pass, then a compaction pass) doubles the traffic.  Such rows
+// are selected in three launches that read the scores once:
+//   1. sample kernel (one workgroup per row): the middle keys of one 16-
+//      position line in every 16 give an estimate of the row's distribution;
+//      a lower bound tau_lo is put a few standard deviations below the
+//      sample's estimate of the cut (the k-th largest middle key);
+//   2. compaction kernel (one wave per 4096-position segment): the middle
+//      positions whose key is at least tau_lo are stored with their keys, in
+//      position order, per segment (ballots give each lane its slots);
+//   3. final kernel (one workgroup per row): if at least k positions were
+//      stored, the cut is among them: each thread loads a run of consecutive
+//      stored entries into registers, a radix select over them finds tau and
+//      the ties still needed, and one scan places the kept positions in order
+//      between the forced ranges.
+// The bound only decides how much is stored, never the result: a row whose
+// stored positions are fewer than k (the sample over-estimated the cut) or
+// more than the final kernel holds (many ties, or a sample that
+// under-estimated it) is selected from its scores by the one-workgroup
+// algorithm inside the final kernel.  Results are identical either way.
+// Digits here are 8 bits, counted in 16 copies of a 256-bin histogram (lane
+// mod 16 picks the copy): the keys near a cut crowd into few bins, and the
+// copies bound the lanes of one instruction that hit the same LDS word.
+constexpr int kLine = 16;              // positions per sampled line (64 bytes)
+constexpr int kSampleEvery = 16;       // one line in this many is sampled
+constexpr int kUnit = 8;               // sampled positions per thread and load (half a line)
+constexpr int kSampleThreads = kRowThreads;
+constexpr int kSampleRegUnits = 2;     // sample units per thread kept in registers
+constexpr int kOutSeg = 4096;          // compaction segment: one wave, 16 float4 per lane
+constexpr int kCapSeg = kOutSeg;       // entries stored per segment: all of it, so no overflow
+constexpr int kCompactWaves = 4;       // segments per compaction workgroup
+constexpr int kFinThreads = 512;
+constexpr int kFinPer = 32;            // stored entries per thread in the final kernel
+constexpr int kFinEnt = kFinPer * kFinThreads;  // stored entries the final kernel holds
+constexpr int kFinSegs = 1024;         // compaction segments per row the split path handles
+constexpr int kHCopies = 16;           // histogram copies
+constexpr int kHStride = 257;          // words per copy: equal bins of copies in distinct banks
 #ifndef KVSEL_SPLIT_MIN_LEN
 #define KVSEL_SPLIT_MIN_LEN 16384
 #endif
@@ -369,8 +377,9 @@ constexpr int kFinSegs = kRowThreads;  // compaction segments per row the final 
 #endif
 constexpr int kSplitMinLen = KVSEL_SPLIT_MIN_LEN;    // split rows at least this long ...
 constexpr int kSplitMaxRows = KVSEL_SPLIT_MAX_ROWS;  // ... when there are at most this many rows ...
-constexpr int kSplitMaxFrac = 8;                     // ... and budgets keep at most 1/8 of a row
-                                                     // (more would overflow the final kernel's LDS)
+constexpr int kSplitMaxFrac = 8;                     // ... budgets keep at most 1/8 of a row ...
+constexpr int kSplitMaxK = 6144;                     // ... and at most this many positions (the
+                                                     // stored ones must fit the final kernel)
 
 struct RowPlan {
   int n, lo, hi, k, fsize;
@@ -391,151 +400,261 @@ __device__ __forceinline__ RowPlan row_plan(const RowsParams& p, int r) {
 
 struct SplitParams {
   RowsParams rp;
-  uint32_t* ghist;   // [rows][2048], zero between calls
-  int4* state;       // [rows]: prefix, pmask, rank after the first digit, -
-  int2* counts;      // [rows][n_oseg]: stored entries, candidates
-  uint2* slots;      // [rows][n_oseg][kCapSeg]: (position | candidate << 31, key) past the first digit
-  int n_seg, seg_len;  // histogram passes: segments of the middle
-  int n_oseg;          // count / output: segments of kOutSeg positions of the row
-  bool vec;          // rows 16-byte aligned: float4 loads
+  uint32_t* tau;     // [rows]: lower bound of the stored keys (top 16 bits; the rest 0)
+  int* counts;       // [rows][n_oseg]: stored entries per segment
+  uint2* slots;      // [rows][n_oseg][kCapSeg]: (position, key) of middle positions with key >= tau
+  int n_oseg;        // segments of kOutSeg positions per row
 };
 
-// Loads positions j0 .. j0+3 of a row (entries outside [j_lo, j_hi) are
-// returned but must be ignored by the caller).
-__device__ __forceinline__ float4 load4(const float* row, bool vec, int j0, int j_lo, int j_hi) {
-  if (vec) return *reinterpret_cast<const float4*>(row + j0);
+// Buffer resource over positions [0, n_valid) of a row: loads past it
+// return 0 instead of reading memory, so a thread's loads need no branch and
+// can all be in flight at once, from one offset register each.  Rows 16-byte
+// aligned: the range is rounded up to a whole quad, which stays inside the
+// row (aligned rows are at least round_up(length, 4) floats apart).  Word 3
+// selects 32-bit data, which untyped loads need to be valid.
+template <bool kVec>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float* row, int n_valid) {
+  const int words = kVec ? ((n_valid + 3) & ~3) : n_valid;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(row), (short)0, words * 4, 0x00020000);
+}
+
+// Positions j0 .. j0+3 of a row through its buffer resource (j0 >= 0, a
+// multiple of 4 when kVec; positions past the resource read as 0).
+template <bool kVec>
+__device__ __forceinline__ float4 load4(__amdgpu_buffer_rsrc_t rs, int j0) {
+  if (kVec) return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, j0 * 4, 0, 0));
   float v[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = (j0 + i >= j_lo && j0 + i < j_hi) ? row[j0 + i] : 0.f;
+  for (int i = 0; i < 4; ++i) v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (j0 + i) * 4, 0, 0));
   return make_float4(v[0], v[1], v[2], v[3]);
 }
 
-// The first digit (top 11 bits of the order key) of every middle position of
-// one segment, counted in two LDS histograms (even and odd waves) and added
-// to the row's global histogram.
-__global__ __launch_bounds__(kSegThreads) void select_split_hist(SplitParams sp) {
-  constexpr int sh = 21;
-  constexpr uint32_t dmask = 0x7FFu;
-  __shared__ int hist[2][2048];
+// Sample unit u of a row: half u % 2 of sampled line u / 2, i.e. positions
+// (u/2)*256 + (u%2)*8 .. +7 (the last unit when u >= n_units, whose keys
+// unit_keys then drops).
+template <bool kVec>
+__device__ __forceinline__ void unit_load(__amdgpu_buffer_rsrc_t rs, int u, int n_units, float4 (&v)[kUnit / 4]) {
+  const int uc = min(u, n_units - 1);
+  const int j0 = (uc >> 1) * kLine * kSampleEvery + (uc & 1) * kUnit;
+#pragma unroll
+  for (int c4 = 0; c4 < kUnit / 4; ++c4) v[c4] = load4<kVec>(rs, j0 + c4 * 4);
+}
+
+// Top 16 bits of the keys of a sample unit; 0 marks a position outside the
+// middle or a unit past the row (a key whose top 16 bits are 0, a NaN with
+// those bits set, is left out of the sample, which only changes the
+// estimate).
+__device__ __forceinline__ void unit_keys(const float4 (&v)[kUnit / 4], int u, int n_units, int lo, int hi,
+                                          uint32_t (&kk)[kUnit]) {
+  const int j0 = (u >> 1) * kLine * kSampleEvery + (u & 1) * kUnit;
+#pragma unroll
+  for (int c4 = 0; c4 < kUnit / 4; ++c4) {
+    const float e[4] = {v[c4].x, v[c4].y, v[c4].z, v[c4].w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = j0 + c4 * 4 + c;
+      kk[c4 * 4 + c] = (u < n_units && j >= lo && j < hi) ? order_key(e[c]) >> 16 : 0u;
+    }
+  }
+}
+
+// LDS of the 8-bit radix steps: two sets of 16-copy histograms (pass p adds
+// into set p & 1 while the other is cleared for pass p + 1), per-wave sums
+// of the 256 bins and the step's result, each doubled the same way, so one
+// step needs three barriers.
+struct DigitLds {
+  int h[2][kHCopies * kHStride];
+  int wsum[2][256 / kWave];
+  int res[2][2];
+  int total;
+};
+
+__device__ __forceinline__ void hist_add(int* h, uint32_t bin) {
+  atomicAdd(&h[(threadIdx.x & (kHCopies - 1)) * kHStride + bin], 1);
+}
+
+// Clears set 0 and the total before the first pass (a barrier must follow).
+template <int NT>
+__device__ __forceinline__ void digit_init(DigitLds& L) {
+  for (int i = threadIdx.x; i < kHCopies * kHStride; i += NT) L.h[0][i] = 0;
+  if (threadIdx.x == 0) L.total = 0;
+}
+
+// One digit step, called by every thread (NT >= 256) after the barrier that
+// follows pass p's hist_add calls into set p & 1: threads t < 256 sum bin
+// 255 - t over the copies (so that scanning threads in order walks the bins
+// from the top) while set (p + 1) & 1 is cleared; the digit d with
+// count(digits > d) < rank <= count(digits >= d) is then found with one
+// wave scan and one exchange of wave sums.  rank >= 1 and at most the
+// pass's total.  Returns d and sets above = count(digits > d).
+template <int NT>
+__device__ int digit_step(DigitLds& L, int p, int rank, int& above) {
+  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave, cur = p & 1;
+  const int* h = L.h[cur];
+  int c = 0;
+  if (tid < 256) {
+#pragma unroll
+    for (int k = 0; k < kHCopies; ++k) c += h[k * kHStride + (255 - tid)];
+  }
+  for (int i = tid; i < kHCopies * kHStride; i += NT) L.h[cur ^ 1][i] = 0;
+  int x = c;
+  if (tid < 256) {
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int y = __shfl_up(x, off, kWave);
+      if (lane >= off) x += y;
+    }
+    if (lane == kWave - 1) L.wsum[cur][w] = x;
+  }
+  __syncthreads();
+  if (tid < 256) {
+    int before = x - c;
+#pragma unroll
+    for (int i = 0; i < 256 / kWave; ++i) before += i < w ? L.wsum[cur][i] : 0;
+    if (before < rank && rank <= before + c) {
+      L.res[cur][0] = 255 - tid;
+      L.res[cur][1] = before;
+    }
+  }
+  __syncthreads();
+  above = L.res[cur][1];
+  return L.res[cur][0];
+}
+
+// tau_lo of row r: with m sampled middle keys out of n_mid, the cut's
+// expected rank in the sample is k_s = k m / n_mid.  The count of the row's
+// k largest keys that fall in the sample has variance at most kLine * k_s
+// (binomial over lines, each line holding up to kLine of them when they come
+// in runs, as max-pooled scores do; runs longer than the sampling period are
+// sampled systematically), so the sample's k_lo-th largest key,
+// k_lo = k_s + 4 sqrt(kLine k_s) + 4, is below the cut unless that count is
+// 4 standard deviations above its mean.  tau_lo is that key truncated to its
+// top 16 bits (two 8-bit digits; the sample keeps only those bits); 0 (store
+// every middle position) when the sample holds fewer than k_lo keys.
+template <bool kVec>
+__global__ __launch_bounds__(kSampleThreads) void select_split_sample(SplitParams sp) {
+  constexpr int NT = kSampleThreads;
+  __shared__ DigitLds L;
   const RowsParams& p = sp.rp;
-  const int r = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
+  const int r = blockIdx.x, tid = threadIdx.x;
   const RowPlan q = row_plan(p, r);
   if (q.k == 0) return;
-  const int j_lo = q.lo + s * sp.seg_len, j_hi = min(j_lo + sp.seg_len, q.hi);
-  if (j_lo >= j_hi) return;
-  for (int i = tid; i < 2 * 2048; i += kSegThreads) (&hist[0][0])[i] = 0;
+  const auto rs = row_rsrc<kVec>(p.scores + (size_t)r * p.stride, q.hi);
+  const int n_units = 2 * ((q.hi + kLine * kSampleEvery - 1) / (kLine * kSampleEvery));  // below hi
+  // every load is issued before any key is formed
+  float4 raw[kSampleRegUnits][kUnit / 4];
+#pragma unroll
+  for (int it = 0; it < kSampleRegUnits; ++it) unit_load<kVec>(rs, tid + it * NT, n_units, raw[it]);
+  __builtin_amdgcn_sched_barrier(0);
+  digit_init<NT>(L);
   __syncthreads();
-  int* my = hist[(tid / kWave) & 1];
-  const float* row = p.scores + (size_t)r * p.stride;
-  // aligned quads covering [j_lo, j_hi), four per thread in flight
-  const int q_lo = j_lo >> 2, q_hi = (j_hi + 3) >> 2;
-  constexpr int QU = 8;
-  for (int q0 = q_lo + tid; q0 < q_hi; q0 += kSegThreads * QU) {
-    float4 v[QU];
+  uint32_t kr[kSampleRegUnits][kUnit];
+  int m = 0;
 #pragma unroll
-    for (int u = 0; u < QU; ++u) {
-      const int qq = min(q0 + u * kSegThreads, q_hi - 1);
-      v[u] = load4(row, sp.vec, qq * 4, j_lo, j_hi);
-    }
+  for (int it = 0; it < kSampleRegUnits; ++it) {
+    unit_keys(raw[it], tid + it * NT, n_units, q.lo, q.hi, kr[it]);
 #pragma unroll
-    for (int u = 0; u < QU; ++u) {
-      const int j = (q0 + u * kSegThreads) * 4;
-      const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t kk = order_key(e[c]);
-        if (q0 + u * kSegThreads < q_hi && j + c >= j_lo && j + c < j_hi) atomicAdd(&my[(kk >> sh) & dmask], 1);
+    for (int c = 0; c < kUnit; ++c)
+      if (kr[it][c]) {
+        hist_add(L.h[0], kr[it][c] >> 8);
+        ++m;
       }
-    }
+  }
+  for (int u = tid + kSampleRegUnits * NT; u < n_units; u += NT) {   // units past the register ones
+    float4 v[kUnit / 4];
+    uint32_t kk[kUnit];
+    unit_load<kVec>(rs, u, n_units, v);
+    unit_keys(v, u, n_units, q.lo, q.hi, kk);
+#pragma unroll
+    for (int c = 0; c < kUnit; ++c)
+      if (kk[c]) {
+        hist_add(L.h[0], kk[c] >> 8);
+        ++m;
+      }
+  }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) m += __shfl_xor(m, off, kWave);
+  if (tid % kWave == 0 && m) atomicAdd(&L.total, m);
+  __syncthreads();
+  const int m_all = L.total;
+  const double k_s = (double)q.k * m_all / (double)(q.hi - q.lo);
+  const int k_lo = (int)ceil(k_s + 4.0 * sqrt((double)kLine * k_s) + 4.0);
+  if (k_lo > m_all) {
+    if (tid == 0) sp.tau[r] = 0u;
+    return;
+  }
+  int above;
+  const int d1 = digit_step<NT>(L, 0, k_lo, above);
+#pragma unroll
+  for (int it = 0; it < kSampleRegUnits; ++it)
+#pragma unroll
+    for (int c = 0; c < kUnit; ++c)
+      if (kr[it][c] && (int)(kr[it][c] >> 8) == d1) hist_add(L.h[1], kr[it][c] & 0xFFu);
+  for (int u = tid + kSampleRegUnits * NT; u < n_units; u += NT) {
+    float4 v[kUnit / 4];
+    uint32_t kk[kUnit];
+    unit_load<kVec>(rs, u, n_units, v);
+    unit_keys(v, u, n_units, q.lo, q.hi, kk);
+#pragma unroll
+    for (int c = 0; c < kUnit; ++c)
+      if (kk[c] && (int)(kk[c] >> 8) == d1) hist_add(L.h[1], kk[c] & 0xFFu);
   }
   __syncthreads();
-  uint32_t* gh = sp.ghist + (size_t)r * 2048;
-  for (int i = tid; i <= (int)dmask; i += kSegThreads) {
-    const int c = hist[0][i] + hist[1][i];
-    if (c) atomicAdd(&gh[i], (uint32_t)c);
-  }
+  const int d2 = digit_step<NT>(L, 1, k_lo - above, above);
+  if (tid == 0) sp.tau[r] = ((uint32_t)d1 << 24) | ((uint32_t)d2 << 16);
 }
 
-// The kOutSeg positions of segment s of row r, one float4 per thread and
-// iteration (4 iterations), all loaded up front.
-__device__ __forceinline__ void load_out_seg(const SplitParams& sp, const RowPlan& q, const float* row,
-                                             int j_lo, int j_hi, float4 (&v)[kOutSeg / (4 * kSegThreads)]) {
-#pragma unroll
-  for (int it = 0; it < kOutSeg / (4 * kSegThreads); ++it) {
-    const int j0 = j_lo + (it * kSegThreads + threadIdx.x) * 4;
-    v[it] = (q.k && j0 < j_hi) ? load4(row, sp.vec, j0, j_lo, j_hi) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-}
-
-// Middle positions of output segment s (kOutSeg positions) that pass the
-// first digit: above the row's boundary digit (kept whatever the rest of
-// the selection decides) or equal to it (candidates).  They are stored in
-// position order, at most kCapSeg per segment, bit 31 marking a candidate;
-// the segment's (stored-or-not count, candidate count) goes to `counts`.
-// Each entry carries its order key.
-__global__ __launch_bounds__(kSegThreads) void select_split_compact(SplitParams sp) {
-  constexpr int IT = kOutSeg / (4 * kSegThreads);
-  __shared__ int ws[kSegThreads / kWave];
-  __shared__ int hist[2048];
-  __shared__ int res[2];
+// Segments of row r (kOutSeg positions each, one wave per segment): the
+// middle positions whose key is at least the row's tau_lo are stored in
+// position order with their keys; the segment's count goes to `counts`.  A
+// lane holds positions j0 .. j0+3 of each 256-position step, so in position
+// order an entry follows every entry of the lanes below it in the same step:
+// one ballot per position within the quad gives each lane its slot.
+template <bool kVec>
+__global__ __launch_bounds__(kWave * kCompactWaves) void select_split_compact(SplitParams sp) {
+  constexpr int IT = kOutSeg / (4 * kWave);
   const RowsParams& p = sp.rp;
-  const int r = blockIdx.y, s = blockIdx.x, tid = threadIdx.x;
+  const int r = blockIdx.y, s = blockIdx.x * kCompactWaves + threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  if (s >= sp.n_oseg) return;
   const RowPlan q = row_plan(p, r);
   if (q.k == 0) return;
-  const int sb = s * kOutSeg, sb_hi = min(sb + kOutSeg, q.n);
-  int2* cnt = sp.counts + (size_t)r * sp.n_oseg + s;
-  const bool empty = max(sb, q.lo) >= min(sb_hi, q.hi);
-  if (empty && s != 0) {
-    if (tid == 0) *cnt = make_int2(0, 0);
+  const int sb = s * kOutSeg;
+  const int j_lo = max(sb, q.lo), j_hi = min(sb + kOutSeg, q.hi);
+  int* cnt = sp.counts + (size_t)r * sp.n_oseg + s;
+  if (j_lo >= j_hi) {
+    if (lane == 0) *cnt = 0;
     return;
   }
-  // The segment's scores are requested first; meanwhile every workgroup of
-  // the row finds the boundary digit d0 (the first digit of the k-th largest
-  // middle key) from the row's complete first-digit histogram, and the
-  // row's first segment records it for the final kernel.
-  const float* row = p.scores + (size_t)r * p.stride;
+  const auto rs = row_rsrc<kVec>(p.scores + (size_t)r * p.stride, j_hi);
   float4 v[IT];
-  load_out_seg(sp, q, row, sb, sb_hi, v);
-  const uint32_t* gh = sp.ghist + (size_t)r * 2048;
-  for (int i = tid; i < 2048; i += kSegThreads) hist[i] = (int)gh[i];
-  __syncthreads();
-  int above;
-  const uint32_t d0 = (uint32_t)find_digit<kSegThreads>(hist, 2048, q.k, ws, res, above);
-  if (s == 0 && tid == 0) sp.state[r] = make_int4((int)(d0 << 21), (int)(0x7FFu << 21), q.k - above, 0);
-  if (empty) {
-    if (tid == 0) *cnt = make_int2(0, 0);
-    return;
-  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) v[it] = load4<kVec>(rs, sb + it * 4 * kWave + lane * 4);
+  __builtin_amdgcn_sched_barrier(0);   // every load is issued before the first is used
+  const uint32_t tau = sp.tau[r];
   uint2* slot = sp.slots + ((size_t)r * sp.n_oseg + s) * kCapSeg;
-  int base = 0, n_cand = 0;
+  int base = 0;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const int j0 = sb + (it * kSegThreads + tid) * 4;
-    const float e4[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
-    int f[4], packed = 0;
+    const int j0 = sb + it * 4 * kWave + lane * 4;
+    const float e[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
     uint32_t kk[4];
+    bool f[4];
+    int below = 0, step = 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int j = j0 + c;
-      const bool mid = j >= q.lo && j < q.hi && j < sb_hi;
-      kk[c] = order_key(e4[c]);
-      const uint32_t dig = kk[c] >> 21;
-      f[c] = !mid ? 0 : dig > d0 ? 1 : dig == d0 ? 2 : 0;
-      packed += (f[c] != 0) + ((f[c] == 2) << 16);   // stored | candidates << 16 (both <= 4096)
+      kk[c] = order_key(e[c]);
+      f[c] = j0 + c >= j_lo && j0 + c < j_hi && kk[c] >= tau;
+      const uint64_t b = __ballot(f[c]);
+      below += __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+      step += __popcll(b);
     }
-    int tot;
-    int pos = base + (block_exclusive_scan<kSegThreads>(packed, ws, tot) & 0xFFFF);
+    int pos = base + below;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (f[c]) {
-        if (pos < kCapSeg) slot[pos] = make_uint2((uint32_t)(j0 + c) | (f[c] == 2 ? 0x80000000u : 0u), kk[c]);
-        ++pos;
-      }
-    }
-    base += tot & 0xFFFF;
-    n_cand += tot >> 16;
+    for (int c = 0; c < 4; ++c)
+      if (f[c]) slot[pos++] = make_uint2((uint32_t)(j0 + c), kk[c]);
+    base += step;
   }
-  if (tid == 0) *cnt = make_int2(base, n_cand);
+  if (lane == 0) *cnt = base;
 }
 
 // Segment of flat entry f: the s with pre[s] <= f < pre[s + 1].
@@ -549,165 +668,170 @@ __device__ __forceinline__ int seg_of(const int* pre, int n_seg, int f) {
   return lo;
 }
 
-// One workgroup per row: the row's stored entries are loaded into LDS in one
-// batch; the remaining two digits are resolved among the candidates there,
-// then the entries are written out in position order between the forced
-// ranges.  A row whose segments overflowed their slots, or with more
-// entries than LDS holds, is selected from its scores by the one-workgroup
-// algorithm instead; the result is the same.
-__global__ __launch_bounds__(kRowThreads) void select_split_final(SplitParams sp) {
-  constexpr int NT = kRowThreads;
-  constexpr int EPT = 4;                  // entries per thread and output step
+// One workgroup per row.  The stored entries, in position order, are split
+// into runs of consecutive entries, one per thread, held in registers.  If
+// there are at least k of them, the k-th largest middle key is among them.
+// Every stored key is at least tau_lo, so the first digit is the key's top
+// 16 bits above tau_lo's, capped at 255: when the cut lies below the cap,
+// that one step fixes 16 bits and two 8-bit steps finish tau; otherwise four
+// 8-bit steps over the whole keys follow.  One scan of (kept above tau, equal
+// to tau) per thread then places every kept position between the forced
+// ranges.  A row with fewer than k stored entries, or more than kFinEnt, is
+// selected from its scores by the one-workgroup algorithm; the result is the
+// same.
+__global__ __launch_bounds__(kFinThreads) void select_split_final(SplitParams sp) {
+  constexpr int NT = kFinThreads;
   __shared__ RowLds sh;
-  __shared__ uint2 ent[kFinEnt];
+  __shared__ DigitLds L;
   __shared__ int seg_pre[kFinSegs + 1];
   const RowsParams& p = sp.rp;
   const int r = blockIdx.x, tid = threadIdx.x;
   const RowPlan q = row_plan(p, r);
   const int n_seg = (q.n + kOutSeg - 1) / kOutSeg;
-  if (q.k == 0 || n_seg > kFinSegs) {
-    select_row(p, r, sh, row_budget(p, r));
+  if (q.k == 0) {
+    select_row<NT>(p, r, sh, row_budget(p, r));
     return;
   }
   int* ws = sh.ws;
-  const int2 c = tid < n_seg ? sp.counts[(size_t)r * sp.n_oseg + tid] : make_int2(0, 0);
+  // segment prefixes: thread t holds segments 2t and 2t + 1
+  static_assert(kFinSegs == 2 * NT, "two segments per thread");
+  const int* cnt = sp.counts + (size_t)r * sp.n_oseg;
+  const int c0 = 2 * tid < n_seg ? cnt[2 * tid] : 0, c1 = 2 * tid + 1 < n_seg ? cnt[2 * tid + 1] : 0;
   int tot;
-  const int pre = block_exclusive_scan<NT>(c.x, ws, tot);
-  if (tid < n_seg) seg_pre[tid] = pre;
+  const int pre = block_exclusive_scan<NT>(c0 + c1, ws, tot);
+  if (2 * tid < n_seg) seg_pre[2 * tid] = pre;
+  if (2 * tid + 1 < n_seg) seg_pre[2 * tid + 1] = pre + c0;
   if (tid == 0) seg_pre[n_seg] = tot;
-  if (__syncthreads_or(c.x > kCapSeg) || tot > kFinEnt) {
-    select_row(p, r, sh, row_budget(p, r));
+  if (tot < q.k || tot > kFinEnt) {
+    select_row<NT>(p, r, sh, row_budget(p, r));
     return;
   }
-  // every entry's load is issued before any is stored
+  __syncthreads();
+  // this thread's run: entries [f_beg, f_end), one search for the first
+  // segment, then a walk across the (rare) segment boundaries; every load is
+  // issued before any is used
   const uint2* slots = sp.slots + (size_t)r * sp.n_oseg * kCapSeg;
-  constexpr int kLoads = (kFinEnt + NT - 1) / NT;
-  uint2 e[kLoads];
+  const int per = (tot + NT - 1) / NT;
+  const int f_beg = min(tid * per, tot), f_end = min(f_beg + per, tot);
+  uint2 e[kFinPer];
 #pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    const int f = tid + i * NT;
-    if (f < tot) {
-      const int sg = seg_of(seg_pre, n_seg, f);
-      e[i] = slots[(size_t)sg * kCapSeg + (f - seg_pre[sg])];
+  for (int i = 0; i < kFinPer; ++i) e[i] = make_uint2(0u, 0u);
+  if (f_beg < f_end) {
+    int sg = seg_of(seg_pre, n_seg, f_beg);
+    int cur = seg_pre[sg], nxt = seg_pre[sg + 1];
+#pragma unroll
+    for (int i = 0; i < kFinPer; ++i) {
+      const int f = f_beg + i;
+      if (f < f_end) {
+        while (f >= nxt) {
+          ++sg;
+          cur = nxt;
+          nxt = seg_pre[sg + 1];
+        }
+        e[i] = slots[(size_t)sg * kCapSeg + (f - cur)];
+      }
     }
   }
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i)
-    if (tid + i * NT < tot) ent[tid + i * NT] = e[i];
+  const int mine = f_end - f_beg;
+  const uint32_t base16 = sp.tau[r] >> 16;
+  digit_init<NT>(L);
   __syncthreads();
-  const int4 st = sp.state[r];
-  uint32_t prefix = (uint32_t)st.x, pmask = (uint32_t)st.y;
-  int rank = st.z;
-  int* hist = sh.hist[0];
-  constexpr int kShift[2] = {10, 0};
-  constexpr int kWidth[2] = {11, 10};
+  // first step: top 16 bits relative to tau_lo's, capped at 255
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int shf = kShift[pass];
-    const uint32_t dmask = (1u << kWidth[pass]) - 1u;
-    for (int i = tid; i < 2048; i += NT) hist[i] = 0;
+  for (int i = 0; i < kFinPer; ++i)
+    if (i < mine) hist_add(L.h[0], min((e[i].y >> 16) - base16, 255u));
+  __syncthreads();
+  int above;
+  const int d0 = digit_step<NT>(L, 0, q.k, above);
+  int rank = q.k - above;
+  uint32_t prefix, pmask;
+  int pass;
+  if (d0 < 255) {
+    prefix = (base16 + (uint32_t)d0) << 16;
+    pmask = 0xFFFF0000u;
+    pass = 2;            // bits 15..8, then 7..0
+  } else {
+    prefix = 0u;
+    pmask = 0u;
+    rank = q.k;
+    pass = 0;            // bits 31..24 .. 7..0 over every key
+  }
+  for (int step = 1; pass < 4; ++pass, ++step) {
+    const int shf = 24 - 8 * pass;
+    int* h = L.h[step & 1];
+#pragma unroll
+    for (int i = 0; i < kFinPer; ++i)
+      if (i < mine && (e[i].y & pmask) == prefix) hist_add(h, (e[i].y >> shf) & 0xFFu);
     __syncthreads();
-    for (int i = tid; i < tot; i += NT) {
-      const uint2 v = ent[i];
-      if ((v.x >> 31) && (v.y & pmask) == prefix) atomicAdd(&hist[(v.y >> shf) & dmask], 1);
-    }
-    __syncthreads();
-    int above;
-    const int d = find_digit<NT>(hist, 1 << kWidth[pass], rank, ws, sh.res, above);
+    const int d = digit_step<NT>(L, step, rank, above);
     rank -= above;
     prefix |= (uint32_t)d << shf;
-    pmask |= dmask << shf;
+    pmask |= 0xFFu << shf;
   }
   const uint32_t tau = prefix;
-  const int ties_needed = rank;
+  const int ties_needed = rank;        // keys equal to tau to keep, lowest positions first
+  // one scan of (above tau, equal to tau) counts, 16 bits each
+  int n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int i = 0; i < kFinPer; ++i)
+    if (i < mine) {
+      n_gt += e[i].y > tau;
+      n_eq += e[i].y == tau;
+    }
+  int both;
+  const int before = block_exclusive_scan<NT>(n_gt | (n_eq << 16), ws, both);
   int32_t* out = p.out_idx + (size_t)r * p.out_stride;
   for (int j = tid; j < q.lo; j += NT) out[j] = j;
-  int out_base = q.lo, tie_base = 0;
-  for (int f0 = 0; f0 < tot; f0 += NT * EPT) {
-    int keep[EPT], eq[EPT], jv[EPT], n_eq = 0;
+  int eq_run = before >> 16;
+  int pos = q.lo + (before & 0xFFFF) + min(eq_run, ties_needed);
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-      const int f = f0 + tid * EPT + i;
-      keep[i] = eq[i] = jv[i] = 0;
-      if (f < tot) {
-        const uint2 v = ent[f];
-        jv[i] = (int)(v.x & 0x7FFFFFFFu);
-        if (v.x >> 31) {
-          keep[i] = v.y > tau ? 1 : 0;
-          eq[i] = v.y == tau ? 1 : 0;
-        } else {
-          keep[i] = 1;
-        }
-      }
-      n_eq += eq[i];
+  for (int i = 0; i < kFinPer; ++i)
+    if (i < mine) {
+      const uint32_t key = e[i].y;
+      bool keep = key > tau;
+      if (key == tau) keep = eq_run++ < ties_needed;
+      if (keep) out[pos++] = (int)e[i].x;
     }
-    int eq_total, keep_total;
-    int run = tie_base + block_exclusive_scan<NT>(n_eq, ws, eq_total);
-    int n_keep = 0;
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-      if (eq[i]) keep[i] = run++ < ties_needed ? 1 : 0;
-      n_keep += keep[i];
-    }
-    int pos = out_base + block_exclusive_scan<NT>(n_keep, ws, keep_total);
-#pragma unroll
-    for (int i = 0; i < EPT; ++i)
-      if (keep[i]) out[pos++] = jv[i];
-    tie_base += eq_total;
-    out_base += keep_total;
-  }
-  for (int j = q.hi + tid; j < q.n; j += NT) out[out_base + (j - q.hi)] = j;
-  if (tid == 0) p.out_count[r] = out_base + (q.n - q.hi);
+  const int kept = (both & 0xFFFF) + min(both >> 16, ties_needed);
+  for (int j = q.hi + tid; j < q.n; j += NT) out[q.lo + kept + (j - q.hi)] = j;
+  if (tid == 0) p.out_count[r] = q.lo + kept + (q.n - q.hi);
 }
 
 // Shapes that may split (the workspace is sized for them) and those that do.
-inline bool may_split(int rows, int max_len) { return rows <= kSplitMaxRows && max_len >= kSplitMinLen; }
+inline bool may_split(int rows, int max_len) {
+  return rows <= kSplitMaxRows && max_len >= kSplitMinLen && max_len <= kFinSegs * kOutSeg;
+}
 inline bool use_split(int rows, int max_len, int max_budget) {
-  return may_split(rows, max_len) && (long long)max_budget * kSplitMaxFrac <= max_len;
+  return may_split(rows, max_len) && (long long)max_budget * kSplitMaxFrac <= max_len &&
+         max_budget <= kSplitMaxK;
 }
 
-// Segment length: a multiple of kSegQuantum giving about kSegTarget
-// workgroups over all rows.
-inline int split_seg_len(int rows, int max_len) {
-  const int per_row = std::max(1, (kSegTarget + rows - 1) / rows);
-  const int len = (max_len + per_row - 1) / per_row;
-  return std::max(kSegQuantum, (len + kSegQuantum - 1) / kSegQuantum * kSegQuantum);
-}
-
-inline size_t split_layout(int rows, int max_len, size_t* o_state, size_t* o_counts, size_t* o_slots) {
+inline size_t split_layout(int rows, int max_len, size_t* o_counts, size_t* o_slots) {
   const int n_seg = (max_len + kOutSeg - 1) / kOutSeg;
-  const size_t a = ((size_t)rows * 2048 * sizeof(uint32_t) + 255) & ~size_t(255);
-  const size_t b = ((size_t)rows * sizeof(int4) + 255) & ~size_t(255);
-  const size_t c = ((size_t)rows * n_seg * sizeof(int2) + 255) & ~size_t(255);
-  const size_t d = ((size_t)rows * n_seg * kCapSeg * sizeof(uint2) + 255) & ~size_t(255);
-  if (o_state) *o_state = a;
-  if (o_counts) *o_counts = a + b;
-  if (o_slots) *o_slots = a + b + c;
-  return a + b + c + d;
-}
-
-// The global histograms must start at zero: they are cleared here once per
-// call.
-__global__ void select_split_zero(uint32_t* gh, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    gh[i] = 0u;
+  const size_t a = ((size_t)rows * sizeof(uint32_t) + 255) & ~size_t(255);
+  const size_t b = ((size_t)rows * n_seg * sizeof(int) + 255) & ~size_t(255);
+  const size_t c = ((size_t)rows * n_seg * kCapSeg * sizeof(uint2) + 255) & ~size_t(255);
+  if (o_counts) *o_counts = a;
+  if (o_slots) *o_slots = a + b;
+  return a + b + c;
 }
 
 hipError_t launch_split(const RowsParams& rp, int rows, int max_len, void* workspace, hipStream_t stream) {
-  size_t o_state, o_counts, o_slots;
-  split_layout(rows, max_len, &o_state, &o_counts, &o_slots);
+  size_t o_counts, o_slots;
+  split_layout(rows, max_len, &o_counts, &o_slots);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const int seg_len = split_seg_len(rows, max_len);
-  SplitParams sp{rp, reinterpret_cast<uint32_t*>(ws), reinterpret_cast<int4*>(ws + o_state),
-                 reinterpret_cast<int2*>(ws + o_counts), reinterpret_cast<uint2*>(ws + o_slots),
-                 (max_len + seg_len - 1) / seg_len, seg_len, (max_len + kOutSeg - 1) / kOutSeg,
-                 (rp.stride & 3) == 0 && (reinterpret_cast<uintptr_t>(rp.scores) & 15) == 0};
-  const size_t nh = (size_t)rows * 2048;
-  hipLaunchKernelGGL(select_split_zero, dim3((unsigned)std::min<size_t>((nh + 255) / 256, 1024)), dim3(256), 0,
-                     stream, sp.ghist, nh);
-  hipLaunchKernelGGL(select_split_hist, dim3(sp.n_seg, rows), dim3(kSegThreads), 0, stream, sp);
-  hipLaunchKernelGGL(select_split_compact, dim3(sp.n_oseg, rows), dim3(kSegThreads), 0, stream, sp);
-  hipLaunchKernelGGL(select_split_final, dim3(rows), dim3(kRowThreads), 0, stream, sp);
+  SplitParams sp{rp, reinterpret_cast<uint32_t*>(ws), reinterpret_cast<int*>(ws + o_counts),
+                 reinterpret_cast<uint2*>(ws + o_slots), (max_len + kOutSeg - 1) / kOutSeg};
+  const dim3 cgrid((unsigned)((sp.n_oseg + kCompactWaves - 1) / kCompactWaves), (unsigned)rows);
+  // rows 16-byte aligned: float4 loads
+  if ((rp.stride & 3) == 0 && (reinterpret_cast<uintptr_t>(rp.scores) & 15) == 0) {
+    hipLaunchKernelGGL(select_split_sample<true>, dim3(rows), dim3(kSampleThreads), 0, stream, sp);
+    hipLaunchKernelGGL(select_split_compact<true>, cgrid, dim3(kWave * kCompactWaves), 0, stream, sp);
+  } else {
+    hipLaunchKernelGGL(select_split_sample<false>, dim3(rows), dim3(kSampleThreads), 0, stream, sp);
+    hipLaunchKernelGGL(select_split_compact<false>, cgrid, dim3(kWave * kCompactWaves), 0, stream, sp);
+  }
+  hipLaunchKernelGGL(select_split_final, dim3(rows), dim3(kFinThreads), 0, stream, sp);
   return hipGetLastError();
 }
 
@@ -977,7 +1101,7 @@ __global__ __launch_bounds__(kRowThreads) void global_percentile_rows_kernel(Row
 }  // namespace
 
 size_t select_workspace_bytes(int rows, int max_len, int mode) {
-  if (mode != 1) return may_split(rows, max_len) ? split_layout(rows, max_len, nullptr, nullptr, nullptr) : 0;
+  if (mode != 1) return may_split(rows, max_len) ? split_layout(rows, max_len, nullptr, nullptr) : 0;
   return ((size_t)rows * max_len * sizeof(uint64_t) + 255 & ~size_t(255)) + 256;
 }
 

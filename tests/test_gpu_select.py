@@ -180,18 +180,27 @@ def test_rows_long_rows_split_over_workgroups(seed):
         _check_rows(scores, lengths, sinks, window, budgets, idx.cpu().numpy(), cnt.cpu().numpy())
 
 
-@pytest.mark.parametrize("case", ["gaussian", "quantised", "clustered", "many_candidates", "dense_segment"])
+@pytest.mark.parametrize("case", ["gaussian", "quantised", "clustered", "many_candidates", "dense_segment",
+                                  "sampled_lines_hot", "sampled_lines_cold", "cut_far_above_bound"])
 def test_rows_long_rows_compaction(case):
-    """Long rows with a small keep fraction (the indexer and vote shape):
-    after the first digit, the positions that pass it are compacted per
-    segment and the selection finishes on them.  Cases cover ties at the
-    threshold (quantised scores), kept positions clustered in a few
-    segments, a segment whose every position passes the first digit, and
-    more boundary-digit candidates than the final stage holds (the per-row
-    selection takes over); every result must equal the oracle's."""
+    """Long rows with a small keep fraction (the indexer and vote shape): a
+    sample of the row bounds the cut from below, the positions at or above
+    the bound are compacted per segment and the selection finishes on them.
+    Cases cover ties at the threshold (quantised scores), kept positions
+    clustered in a few segments, a segment whose every position passes,
+    more positions at the threshold than the final stage holds, and samples
+    that misjudge the row (the sample reads one 16-position line in every
+    16): the largest scores only on the sampled lines, so fewer than k
+    positions pass the bound, or only off them, so far too many pass (the
+    per-row selection takes over in both), or a few thousand scores far
+    above the rest only off them, so that the stored positions fit but the
+    cut lies far above the bound (the final stage's digits restart from the
+    whole key); every result must equal the oracle's."""
     K = _K()
     rng = np.random.default_rng({"gaussian": 11, "quantised": 12, "clustered": 13,
-                                 "many_candidates": 14, "dense_segment": 15}[case])
+                                 "many_candidates": 14, "dense_segment": 15,
+                                 "sampled_lines_hot": 16, "sampled_lines_cold": 17,
+                                 "cut_far_above_bound": 18}[case])
     rows, n = 6, 131072
     lengths = [n, n - 1, 65536, 100003, 70001, n]
     scores = rng.standard_normal((rows, n)).astype(np.float32)
@@ -211,6 +220,18 @@ def test_rows_long_rows_compaction(case):
         scores[~sel] = np.minimum(scores[~sel], 0.9)
     if case == "dense_segment":
         scores[:, 8192:8192 + 4096] = 3.0 + rng.random((rows, 4096)).astype(np.float32)  # one full segment passes
+    on_sampled = (np.arange(n) % 256) < 16
+    if case == "sampled_lines_hot":
+        scores[:, on_sampled] += 5.0
+    if case == "sampled_lines_cold":
+        hot = np.zeros(n, dtype=bool)
+        for c in rng.integers(0, n // 4096 - 1, size=10):
+            hot[c * 4096:(c + 1) * 4096] = True
+        scores[:, hot & ~on_sampled] += 5.0
+    if case == "cut_far_above_bound":
+        off = np.flatnonzero(~on_sampled)
+        for r in range(rows):
+            scores[r, rng.choice(off[off < lengths[r]], size=3000, replace=False)] += 50.0
     note(f"select compaction case={case}")
     max_budget = max(budgets)
     out_stride = max(max_budget, sinks + window)
