@@ -8,12 +8,15 @@
 // The window logits are a real dense contraction: for one query head, the
 // W x d window queries against every key, 16 keys x 16 window rows per
 // v_mfma_f32_16x16x32_bf16 chain.  A workgroup serves all G query heads of
-// a KV head for a run of chunks of one sequence: each chunk's keys are
-// staged in LDS once and read by every wave as MFMA fragments, and the next
-// chunk's keys are loaded into registers while the current one is computed.
-// The cost that bounds the vote is the vector ALU (one exp per window logit,
-// quarter rate), so the per-logit work is kept to one FMA, one exp2 and one
-// add on tiles that need no causal mask.  Two passes over K:
+// a KV head for a run of chunks of one sequence: each 128-key chunk is
+// staged in LDS once and read by every wave as MFMA fragments.  The pass is
+// bound by latency (dependent MFMA -> FMA -> exp -> add chains), so the
+// design favours occupancy: 128-key chunks (~37 KB of LDS), two tiles in
+// flight and no register prefetch of the next chunk keep a workgroup within
+// 128 VGPRs, and four workgroups per CU (four waves per SIMD) overlap one
+// workgroup's chunk loads with the others' compute.  The per-logit vector
+// work is one FMA, one exp2 (quarter rate) and one add on tiles that need no
+// causal mask.  Two passes over K:
 //   pass 1  per window row, (max, sum of exp) over the workgroup's keys, in
 //           base-2 units with a lazily moved reference (the running sum is
 //           rescaled only when a logit exceeds the reference by 2^64);
@@ -40,22 +43,25 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 #ifndef KVSEL_VOTE_STAGE
-#define KVSEL_VOTE_STAGE 256  // keys staged per chunk (16 tiles)
+#define KVSEL_VOTE_STAGE 128  // keys staged per chunk (8 tiles)
 #endif
 constexpr int kStage = KVSEL_VOTE_STAGE;
 constexpr int kTiles = kStage / 16;
 constexpr int kMaxHalo = 8;             // pass 2: extra keys on each side = the pool radius (<= 8)
 #ifndef KVSEL_VOTE_WGS
-#define KVSEL_VOTE_WGS 1024   // grid target (128K case: 992 workgroups, ~2 rounds of 2 per CU)
+#define KVSEL_VOTE_WGS 1024   // grid target (128K case: ~1000 workgroups, one round of 4 per CU)
 #endif
 #ifndef KVSEL_VOTE_TN1
-#define KVSEL_VOTE_TN1 4     // pass 1: fully visible tiles computed together
+#define KVSEL_VOTE_TN1 2     // pass 1: fully visible tiles computed together
+#endif
+#ifndef KVSEL_VOTE_TN2
+#define KVSEL_VOTE_TN2 2     // pass 2: fully visible tiles computed together (2 or 4)
 #endif
 #ifndef KVSEL_VOTE_WPE1
-#define KVSEL_VOTE_WPE1 2    // >0: occupancy hint (waves per SIMD) for pass 1
+#define KVSEL_VOTE_WPE1 4    // >0: occupancy hint (waves per SIMD) for pass 1
 #endif
 #ifndef KVSEL_VOTE_WPE2
-#define KVSEL_VOTE_WPE2 2    // >0: occupancy hint (waves per SIMD) for pass 2
+#define KVSEL_VOTE_WPE2 4    // >0: occupancy hint (waves per SIMD) for pass 2
 #endif
 constexpr int kMaxWgs = KVSEL_VOTE_WGS;  // grid target: chunks are grouped into runs beyond it
 constexpr float kRescale = 64.f;        // pass 1: move the reference past this (base-2 units)
@@ -178,9 +184,8 @@ __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2)
 //
 // NHW > 0: the window rows of the wave's (at most NHW) heads are loaded once,
 // before the chunk loop, and held in registers, so the only global loads in
-// the loop are the next chunk's keys, and no wait in the compute covers
-// them (vector loads retire in order).  NHW == 0: the rows are reloaded per
-// chunk and head (wide groups).
+// the loop are the chunk's keys.  NHW == 0: the rows are reloaded per chunk
+// and head (wide groups).
 template <int D, int RT, int NHW>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(KVSEL_VOTE_WPE1 > 0 ? KVSEL_VOTE_WPE1 : 1)))
@@ -327,13 +332,14 @@ void snapkv_pass1(VoteParams p) {
 
   const int pg0 = load_pages(p, b, L, c_first * kStage, c_end * kStage - 1, page_lds);
   __syncthreads();
-  uint4 buf[Stage<D>::kPer];
-  stage_load<D>(p, page_lds, pg0, kvh, L, c_first * kStage, buf);
   for (int c = c_first; c < c_end; ++c) {
-    __syncthreads();                       // previous chunk's readers are done
-    stage_store<D>(buf, kst);
+    {
+      uint4 buf[Stage<D>::kPer];
+      stage_load<D>(p, page_lds, pg0, kvh, L, c * kStage, buf);
+      __syncthreads();                       // previous chunk's readers are done
+      stage_store<D>(buf, kst);
+    }
     __syncthreads();
-    if (c + 1 < c_end) stage_load<D>(p, page_lds, pg0, kvh, L, (c + 1) * kStage, buf);
     const int start = c * kStage;
     if constexpr (PRE) {
 #pragma unroll
@@ -509,12 +515,12 @@ void snapkv_pass2(VoteParams p) {
       for (int k = 0; k < TN; ++k) hv[g * kStage + (t + k) * 16 + col] = cs[k];
     }
   };
-  // Fully visible tiles per step: four when the window rows of one head are
-  // held (measured ~1.5% faster at W = 32 with the same two waves per SIMD
-  // the staged keys allow, bitwise the same), else two.
+  // Fully visible tiles per step: two, or four (KVSEL_VOTE_TN2) when the
+  // window rows of one head are held; four measured ~1.5% faster at two
+  // waves per SIMD, but need more registers than four waves per SIMD allow.
   auto tiles = [&](int kbase, int g, int t_lo, int t_hi, const bf16x8 (&q)[RT][NU], const float (&lr)[RT][4]) {
     int t = t_lo;
-    if constexpr (NS == 1 && RT <= 2) {
+    if constexpr (NS == 1 && RT <= 2 && KVSEL_VOTE_TN2 == 4) {
       for (; t + 3 < t_hi; t += 4) {
         const int key0 = kbase + t * 16;
         if (key0 >= 0 && key0 + 63 < prefix) {
@@ -542,13 +548,14 @@ void snapkv_pass2(VoteParams p) {
 
   const int pg0 = load_pages(p, b, L, c_first * kOut - kHalo, (c_end - 1) * kOut - kHalo + kStage - 1, page_lds);
   __syncthreads();
-  uint4 buf[Stage<D>::kPer];
-  stage_load<D>(p, page_lds, pg0, kvh, L, c_first * kOut - kHalo, buf);
   for (int c = c_first; c < c_end; ++c) {
-    __syncthreads();                       // previous chunk's readers are done
-    stage_store<D>(buf, kst);
+    {
+      uint4 buf[Stage<D>::kPer];
+      stage_load<D>(p, page_lds, pg0, kvh, L, c * kOut - kHalo, buf);
+      __syncthreads();                       // previous chunk's readers are done
+      stage_store<D>(buf, kst);
+    }
     __syncthreads();
-    if (c + 1 < c_end) stage_load<D>(p, page_lds, pg0, kvh, L, (c + 1) * kOut - kHalo, buf);
     const int kbase = c * kOut - kHalo;    // key of staged row 0
     if constexpr (PRE) {
 #pragma unroll

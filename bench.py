@@ -280,8 +280,8 @@ def long_context_workload(torch, K, synth, args) -> dict:
         torch.cuda.synchronize()
         log("counters mode done: snapkv vote x3 (128K case)")
         return None
-    t_vote = timed(torch, vote, 10, warmup=3)
-    t_vote_sel = timed(torch, vote_select, 10, warmup=1)
+    t_vote = timed(torch, vote, 30, warmup=30)
+    t_vote_sel = timed(torch, vote_select, 30, warmup=5)
     k_bytes = Bq * HKVq * Lq * 128 * 2
     vote_flops = 2 * (2.0 * Bq * HQq * W * Lq * 128)       # two passes of Q_win K^T
 
