@@ -21,8 +21,8 @@
 //           base-2 units with a lazily moved reference (the running sum is
 //           rescaled only when a logit exceeds the reference by 2^64);
 //   combine per window row: lse over the workgroups' partials;
-//   pass 2  recompute the logits of each chunk plus an 8-key halo on each
-//           side with the window rows as the MFMA A operand, so a lane holds
+//   pass 2  recompute the logits of each chunk plus a halo of the pool
+//           radius on each side with the window rows as the MFMA A operand, so a lane holds
 //           four rows of one key: p = exp2(s - lse2), column sums by local
 //           adds and two cross-lane steps, the group sum in head order, the
 //           max-pool, and the final votes of the chunk's prefix keys.
