@@ -182,3 +182,67 @@ def test_single_call_graph_replays_with_new_inputs():
                 assert e[0] < 2e-3 and e[1] < 1e-4 and e[2] < 1e-4, (rep, b, c, e)
         print(f"replay {rep}: lengths {cur.tolist()} worst out {worst[0]:.2e} probs {worst[1]:.2e} "
               f"cum {worst[2]:.2e}", flush=True)
+
+
+def test_sparse_step_graph_replays_with_new_queries():
+    """One sparse decode step (indexer logits, the split top-2048 selection,
+    sparse attention over the kept keys) captured in one graph, as bench.py
+    replays it, and replayed with new queries copied into the captured inputs
+    between replays: every replay equals the same step run eagerly on those
+    queries, bit for bit (the path keeps no state between calls and clears
+    nothing with memsets)."""
+    import attention_score_guided_amd as K
+    B, Hq, Hkv, d, dI, P, L, k = 2, 8, 2, 128, 64, 16, 40000, 2048
+    g = synth.generator(91)
+    bt, n_pages = synth.shuffled_block_table(B, L, P, g)
+    bt = bt.cuda()
+    kp = synth.normal((n_pages, Hkv, P, d), g, torch.bfloat16).cuda()
+    vp = synth.normal((n_pages, Hkv, P, d), g, torch.bfloat16).cuda()
+    kip = synth.normal((n_pages, 1, P, dI), g, torch.bfloat16).cuda()
+    lens = torch.tensor([L, L - 777], dtype=torch.int32).cuda()
+    kvi = K.PagedKV(kip, None, bt, lens, P, L)
+    kvf = K.PagedKV(kp, vp, bt, lens, P, L)
+    qi = torch.empty((B, Hq, dI), dtype=torch.bfloat16, device="cuda")
+    q = torch.empty((B, Hq, d), dtype=torch.bfloat16, device="cuda")
+    scores = torch.zeros((B, Hq, L), device="cuda")
+    rl = lens.repeat_interleave(Hq).to(torch.int32)
+    keep = torch.zeros((B * Hq, k), dtype=torch.int32, device="cuda")
+    kc = torch.zeros((B * Hq,), dtype=torch.int32, device="cuda")
+    out = torch.zeros((B, Hq, d), device="cuda")
+    ws_d = torch.empty(K.decode_workspace_bytes(kvi, Hq, True), dtype=torch.uint8, device="cuda")
+    ws_k = torch.empty(K.select_workspace_bytes(B * Hq, L, K.SELECT_ROWS), dtype=torch.uint8, device="cuda")
+    ws_s = torch.empty(K.sparse_workspace_bytes(B, Hq, d, k), dtype=torch.uint8, device="cuda")
+
+    def step():
+        K.decode_attn_scores(kvi, qi, Hq, 1.0, None, None, scores, K.EMIT_LOGITS, workspace=ws_d)
+        K.select_keep(scores.view(B * Hq, L), rl, L, 0, 0, None, k, keep, kc, workspace=ws_k)
+        K.sparse_attn(kvf, q, Hq, keep.view(B, Hq, k), kc.view(B, Hq), k, 1 / math.sqrt(d), out, workspace=ws_s)
+
+    def new_queries(seed):
+        gg = synth.generator(seed)
+        qi.copy_(synth.normal((B, Hq, dI), gg, torch.bfloat16).cuda())
+        q.copy_(synth.normal((B, Hq, d), gg, torch.bfloat16).cuda())
+        torch.cuda.synchronize()
+
+    new_queries(1)
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        new_queries(100 + rep)
+        step()                      # eager on the same queries
+        torch.cuda.synchronize()
+        want = [t.clone() for t in (scores, keep, kc, out)]
+        out.fill_(float("nan"))
+        keep.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((scores, keep, kc, out), want):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager step"
+        assert int(kc.min()) == k
