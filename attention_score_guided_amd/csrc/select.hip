@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kRowThreads) void select_rows_kernel(RowsParams p) 
 //      position line in every 16 give an estimate of the row's distribution;
 //      a lower bound tau_lo is put a few standard deviations below the
 //      sample's estimate of the cut (the k-th largest middle key);
-//   2. compaction kernel (one wave per 4096-position segment): the middle
+//   2. compaction kernel (one wave per 1024-position segment): the middle
 //      positions whose key is at least tau_lo are stored with their keys, in
 //      position order, per segment (ballots give each lane its slots);
 //   3. final kernel (one workgroup per row): if at least k positions were
@@ -360,9 +360,15 @@ constexpr int kSampleEvery = 16;       // one line in this many is sampled
 constexpr int kUnit = 8;               // sampled positions per thread and load (half a line)
 constexpr int kSampleThreads = kRowThreads;
 constexpr int kSampleRegUnits = 2;     // sample units per thread kept in registers
-constexpr int kOutSeg = 4096;          // compaction segment: one wave, 16 float4 per lane
+#ifndef KVSEL_OUT_SEG
+#define KVSEL_OUT_SEG 1024
+#endif
+#ifndef KVSEL_COMPACT_WAVES
+#define KVSEL_COMPACT_WAVES 4
+#endif
+constexpr int kOutSeg = KVSEL_OUT_SEG;  // compaction segment: one wave, kOutSeg / 256 float4 per lane
 constexpr int kCapSeg = kOutSeg;       // entries stored per segment: all of it, so no overflow
-constexpr int kCompactWaves = 4;       // segments per compaction workgroup
+constexpr int kCompactWaves = KVSEL_COMPACT_WAVES;  // segments per compaction workgroup
 constexpr int kFinThreads = 512;
 constexpr int kFinPer = 32;            // stored entries per thread in the final kernel
 constexpr int kFinEnt = kFinPer * kFinThreads;  // stored entries the final kernel holds

@@ -320,13 +320,16 @@ def long_context_workload(torch, K, synth, args) -> dict:
     b.record()
     torch.cuda.synchronize()
     t_sparse = a.elapsed_time(b) / steps
-    # each step alone after a 512 MB write that evicts the Infinity Cache
-    # (256 MB), so that no step reads what an earlier one left there; the
-    # median of the per-step event intervals
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    # each step alone after a 512 MB read that evicts the Infinity Cache
+    # (256 MB) with clean lines, so that no step reads what an earlier one
+    # left there (a write would instead leave 256 MB of dirty lines whose
+    # write-back then competes with the step); the median of the per-step
+    # event intervals
+    flush = torch.ones(128 << 20, device="cuda")
+    torch.cuda.synchronize()
     per_step = []
     for s in range(steps):
-        flush.zero_()
+        flush.sum()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         sparse_step(s)
