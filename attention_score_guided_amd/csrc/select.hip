@@ -410,6 +410,7 @@ struct SplitParams {
   int* counts;       // [rows][n_oseg]: stored entries per segment
   uint2* slots;      // [rows][n_oseg][kCapSeg]: (position, key) of middle positions with key >= tau
   int n_oseg;        // segments of kOutSeg positions per row
+  int max_len;       // positions below it lie inside every row (stride >= max_len)
 };
 
 // Buffer resource over positions [0, n_valid) of a row: loads past it
@@ -543,15 +544,17 @@ __global__ __launch_bounds__(kSampleThreads) void select_split_sample(SplitParam
   __shared__ DigitLds L;
   const RowsParams& p = sp.rp;
   const int r = blockIdx.x, tid = threadIdx.x;
-  const RowPlan q = row_plan(p, r);
-  if (q.k == 0) return;
-  const auto rs = row_rsrc<kVec>(p.scores + (size_t)r * p.stride, q.hi);
-  const int n_units = 2 * ((q.hi + kLine * kSampleEvery - 1) / (kLine * kSampleEvery));  // below hi
-  // every load is issued before any key is formed
+  // The register units' loads go out before the row's plan is read (their
+  // range is every row's [0, max_len); keys outside the middle are dropped)
+  const auto rs = row_rsrc<kVec>(p.scores + (size_t)r * p.stride, sp.max_len);
+  const int n_units_max = 2 * ((sp.max_len + kLine * kSampleEvery - 1) / (kLine * kSampleEvery));
   float4 raw[kSampleRegUnits][kUnit / 4];
 #pragma unroll
-  for (int it = 0; it < kSampleRegUnits; ++it) unit_load<kVec>(rs, tid + it * NT, n_units, raw[it]);
+  for (int it = 0; it < kSampleRegUnits; ++it) unit_load<kVec>(rs, tid + it * NT, n_units_max, raw[it]);
   __builtin_amdgcn_sched_barrier(0);
+  const RowPlan q = row_plan(p, r);
+  if (q.k == 0) return;
+  const int n_units = 2 * ((q.hi + kLine * kSampleEvery - 1) / (kLine * kSampleEvery));  // below hi
   digit_init<NT>(L);
   __syncthreads();
   uint32_t kr[kSampleRegUnits][kUnit];
@@ -622,20 +625,22 @@ __global__ __launch_bounds__(kWave * kCompactWaves) void select_split_compact(Sp
   const RowsParams& p = sp.rp;
   const int r = blockIdx.y, s = blockIdx.x * kCompactWaves + threadIdx.x / kWave, lane = threadIdx.x % kWave;
   if (s >= sp.n_oseg) return;
+  const int sb = s * kOutSeg;
+  // The segment's loads go out before the row's plan is read (their range
+  // is every row's [0, max_len); positions outside the middle are masked).
+  const auto rs = row_rsrc<kVec>(p.scores + (size_t)r * p.stride, min(sb + kOutSeg, sp.max_len));
+  float4 v[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) v[it] = load4<kVec>(rs, sb + it * 4 * kWave + lane * 4);
+  __builtin_amdgcn_sched_barrier(0);   // every load is issued before the first is used
   const RowPlan q = row_plan(p, r);
   if (q.k == 0) return;
-  const int sb = s * kOutSeg;
   const int j_lo = max(sb, q.lo), j_hi = min(sb + kOutSeg, q.hi);
   int* cnt = sp.counts + (size_t)r * sp.n_oseg + s;
   if (j_lo >= j_hi) {
     if (lane == 0) *cnt = 0;
     return;
   }
-  const auto rs = row_rsrc<kVec>(p.scores + (size_t)r * p.stride, j_hi);
-  float4 v[IT];
-#pragma unroll
-  for (int it = 0; it < IT; ++it) v[it] = load4<kVec>(rs, sb + it * 4 * kWave + lane * 4);
-  __builtin_amdgcn_sched_barrier(0);   // every load is issued before the first is used
   const uint32_t tau = sp.tau[r];
   uint2* slot = sp.slots + ((size_t)r * sp.n_oseg + s) * kCapSeg;
   int base = 0;
@@ -692,6 +697,12 @@ __global__ __launch_bounds__(kFinThreads) void select_split_final(SplitParams sp
   __shared__ int seg_pre[kFinSegs + 1];
   const RowsParams& p = sp.rp;
   const int r = blockIdx.x, tid = threadIdx.x;
+  // segment counts: thread t holds segments 2t and 2t + 1, loaded before the
+  // row's plan is read (unused when the row needs no selection)
+  static_assert(kFinSegs == 2 * NT, "two segments per thread");
+  const int* cnt = sp.counts + (size_t)r * sp.n_oseg;
+  const int c0_all = 2 * tid < sp.n_oseg ? cnt[2 * tid] : 0;
+  const int c1_all = 2 * tid + 1 < sp.n_oseg ? cnt[2 * tid + 1] : 0;
   const RowPlan q = row_plan(p, r);
   const int n_seg = (q.n + kOutSeg - 1) / kOutSeg;
   if (q.k == 0) {
@@ -699,10 +710,7 @@ __global__ __launch_bounds__(kFinThreads) void select_split_final(SplitParams sp
     return;
   }
   int* ws = sh.ws;
-  // segment prefixes: thread t holds segments 2t and 2t + 1
-  static_assert(kFinSegs == 2 * NT, "two segments per thread");
-  const int* cnt = sp.counts + (size_t)r * sp.n_oseg;
-  const int c0 = 2 * tid < n_seg ? cnt[2 * tid] : 0, c1 = 2 * tid + 1 < n_seg ? cnt[2 * tid + 1] : 0;
+  const int c0 = 2 * tid < n_seg ? c0_all : 0, c1 = 2 * tid + 1 < n_seg ? c1_all : 0;
   int tot;
   const int pre = block_exclusive_scan<NT>(c0 + c1, ws, tot);
   if (2 * tid < n_seg) seg_pre[2 * tid] = pre;
@@ -827,7 +835,7 @@ hipError_t launch_split(const RowsParams& rp, int rows, int max_len, void* works
   split_layout(rows, max_len, &o_counts, &o_slots);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   SplitParams sp{rp, reinterpret_cast<uint32_t*>(ws), reinterpret_cast<int*>(ws + o_counts),
-                 reinterpret_cast<uint2*>(ws + o_slots), (max_len + kOutSeg - 1) / kOutSeg};
+                 reinterpret_cast<uint2*>(ws + o_slots), (max_len + kOutSeg - 1) / kOutSeg, max_len};
   const dim3 cgrid((unsigned)((sp.n_oseg + kCompactWaves - 1) / kCompactWaves), (unsigned)rows);
   // rows 16-byte aligned: float4 loads
   if ((rp.stride & 3) == 0 && (reinterpret_cast<uintptr_t>(rp.scores) & 15) == 0) {
