@@ -59,10 +59,10 @@ constexpr int kUnroll = 4;
 #define KVSEL_QK_DB 0        // 1: double-buffer the K batches of the QK phase
 #endif
 #ifndef KVSEL_QK_BATCH
-#define KVSEL_QK_BATCH 4     // >0: issue the K loads of this many tiles before their MFMAs
+#define KVSEL_QK_BATCH 0     // >0: issue the K loads of this many tiles before their MFMAs (0: per kernel)
 #endif
 #ifndef KVSEL_WAVES_PER_EU
-#define KVSEL_WAVES_PER_EU 0 // >0: occupancy hint for the G=8 kernel
+#define KVSEL_WAVES_PER_EU 0 // >0: occupancy hint for the kernels with P.V (0: per kernel)
 #endif
 #ifndef KVSEL_COOP_NORM
 #define KVSEL_COOP_NORM 1  // normalise probabilities inside the split-K pass (bf16, G <= 8)
@@ -354,11 +354,20 @@ __device__ __forceinline__ void k_line_exchange(bf16x8& s0, bf16x8& s1, bool lo)
   s1 = __builtin_bit_cast(bf16x8, c);
 }
 
-constexpr int kQkBatch = KVSEL_QK_BATCH > 0 ? KVSEL_QK_BATCH : 1;  // K tiles per load batch
+// Occupancy of the kernels with P.V: four workgroups (16 waves) per CU.
+// LDS allows it at 1024-key chunks (the [C][GT] probability tile, 32 KB at
+// G = 8, plus one [GT][D] reduction tile); registers (<= 128) need one K tile
+// per load batch and two value loads per lane at G = 8 with the normalisation,
+// two K tiles and four value loads below G = 8.  D = 64 at G = 8 does not fit
+// 128 registers without spills and keeps three waves per SIMD.
+template <int D, int GT, bool HAS_V>
+constexpr bool kDecodeWide64 = HAS_V && D == 64 && GT >= 8;
+template <int D, int GT, bool HAS_V>
+constexpr int kDecodeWaves = KVSEL_WAVES_PER_EU > 0 && HAS_V ? KVSEL_WAVES_PER_EU : kDecodeWide64<D, GT, HAS_V> ? 3 : 4;
 
 template <int D, int GT, bool HAS_V, bool WRITE_LOGITS, bool COOP>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(HAS_V ? (KVSEL_WAVES_PER_EU > 0 ? KVSEL_WAVES_PER_EU : 3) : 4)))
+__attribute__((amdgpu_waves_per_eu(kDecodeWaves<D, GT, HAS_V>)))
 void decode_partial_mfma(PartialParams p) {
   constexpr int NU = D / 32;                 // MFMA k-steps (32 dims each)
   constexpr int EPL = 8;                     // P.V: dims per lane
@@ -367,14 +376,17 @@ void decode_partial_mfma(PartialParams p) {
   constexpr int KPI = kWaves * KPW;          // P.V: keys per workgroup per load
   // P.V: value loads per lane per batch, as many as the register budget of
   // the group width allows without spilling.
-  constexpr int VU = KVSEL_PV_VU > 0 ? KVSEL_PV_VU : GT >= 8 ? 4 : !COOP ? 8 : GT == 4 ? 6 : GT == 2 ? 7 : 8;
-  constexpr int QB = kQkBatch;
+  constexpr bool W64 = kDecodeWide64<D, GT, HAS_V>;
+  constexpr int VU = KVSEL_PV_VU > 0 ? KVSEL_PV_VU : GT >= 8 && COOP && !W64 ? 2 : 4;
+  // K tiles per load batch
+  constexpr int QB = KVSEL_QK_BATCH > 0 ? KVSEL_QK_BATCH : !HAS_V || W64 ? 4 : GT >= 8 ? 1 : 2;
 
   extern __shared__ __align__(16) float smem[];
   const int C = p.chunk;
   float* p_lds = smem;                               // [C][GT] logits, then exp(s - m)
-  float* red = smem + C * GT;                        // [kWaves][GT][D]
-  float* wstat = red + kWaves * GT * D;              // [2][kWaves][16]
+  // [GT][D] reduction tile of P.V; then [GT][n_chunks] posts of the row
+  float* red = smem + C * GT;
+  float* wstat = red + GT * (COOP ? max(D, p.n_chunks) : D);           // [2][kWaves][16]
   float2* ml_lds = reinterpret_cast<float2*>(wstat + 2 * kWaves * 16);  // [GT]
   int* page_lds = reinterpret_cast<int*>(ml_lds + GT);                  // [C/16 + 2]
 
@@ -731,17 +743,32 @@ void decode_partial_mfma(PartialParams p) {
         for (int off = LPK; off < kWave; off *= 2) a += __shfl_xor(a, off, kWave);
         acc[h][e] = a;
       }
-    if (slot == 0) {
+    // The waves' sums meet in one [GT][D] tile: the last wave stores its
+    // own, each earlier wave in turn adds its own (one tile rather than one
+    // per wave is what keeps four workgroups per CU within the LDS).
 #pragma unroll
-      for (int h = 0; h < GT; ++h)
+    for (int w = kWaves - 1; w >= 0; --w) {
+      if (wave == w && slot == 0) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) red[(wave * GT + h) * D + seg * EPL + e] = acc[h][e];
+        for (int h = 0; h < GT; ++h) {
+          float4* r = reinterpret_cast<float4*>(red + h * D + seg * EPL);
+          float4 x0 = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+          float4 x1 = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+          if (w != kWaves - 1) {
+            const float4 y0 = r[0], y1 = r[1];
+            x0 = make_float4(y0.x + x0.x, y0.y + x0.y, y0.z + x0.z, y0.w + x0.w);
+            x1 = make_float4(y1.x + x1.x, y1.y + x1.y, y1.z + x1.z, y1.w + x1.w);
+          }
+          r[0] = x0;
+          r[1] = x1;
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
 #pragma unroll
     for (int i = 0; i < kNO; ++i) {
       const int idx = tid + i * kThreads;
-      ov[i] = idx < GT * D ? (red[idx] + red[GT * D + idx]) + (red[2 * GT * D + idx] + red[3 * GT * D + idx]) : 0.f;
+      ov[i] = idx < GT * D ? red[idx] : 0.f;
       // Without in-kernel normalisation the partial output goes out as is;
       // with it, once the row's lse is known (phase 4).
       if (!COOP && idx < GT * D) p.part_o[((ml_base + (size_t)(idx / D) * p.n_chunks)) * D + idx % D] = ov[i];
@@ -1451,8 +1478,9 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   const bool use_v = a.v_pages != nullptr && a.out != nullptr;
   const bool need_norm = !a.emit_logits && (a.probs != nullptr || a.cum != nullptr);
   // In-kernel normalisation: bf16, one workgroup serves a whole group.
-  // The lse of a row's chunks are gathered in the kWaves x GT x D staging
-  // area of the P.V reduction, hence the bound on the chunk count.
+  // The lse of a row's chunks are gathered in LDS ([GT][n_chunks] floats in
+  // the area of the P.V reduction tile), hence a bound on the chunk count
+  // (kWaves * d: 16 KB at G = 8 and d = 128).
   const bool coop = KVSEL_COOP_NORM && a.bf16 && need_norm && pl.hgroups == 1 &&
                     pl.n_chunks <= kWaves * a.head_dim && (a.probs != nullptr || pl.scratch_bytes > 0);
   float* logits = nullptr;
@@ -1540,8 +1568,11 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     return hipGetLastError();
   }
   const dim3 grid(pl.n_chunks, a.num_kv_heads * pl.hgroups, a.num_seqs);
-  const size_t lds = (size_t)pl.gt * pl.chunk * sizeof(float) +
-                     (size_t)kWaves * pl.gt * a.head_dim * sizeof(float) +
+  // the bf16 pass sums its waves through one [GT][D] tile, which the
+  // in-kernel normalisation then reuses for the row's [GT][n_chunks] posts
+  const size_t red_floats = !a.bf16 ? (size_t)kWaves * pl.gt * a.head_dim
+                                    : (size_t)pl.gt * (coop ? std::max(a.head_dim, pl.n_chunks) : a.head_dim);
+  const size_t lds = (size_t)pl.gt * pl.chunk * sizeof(float) + red_floats * sizeof(float) +
                      (a.bf16 ? 2 * kWaves * 16 * sizeof(float) : 0) + pl.gt * sizeof(float2) +
                      ((size_t)pl.chunk / 16 + 2) * sizeof(int);
   const bool wl = logits != nullptr;
