@@ -1158,37 +1158,45 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(CombineParams p) 
   const int bh = blockIdx.x;
   const int b = bh / p.num_q_heads;
   const int L = p.seq_lens[b];
-  const int nc = (L + p.chunk - 1) / p.chunk;
   const float2* ml = p.part_ml + (size_t)bh * p.n_chunks;
   const int tid = threadIdx.x;
   // Every global load of the common case is issued before the first
-  // reduction: the chunk (max, sum) pairs, the first kCombPre partial
-  // outputs of this thread's chunk group, and the fix-up flags.
+  // reduction, and before the row's chunk count (from seq_lens) is known:
+  // the chunk (max, sum) pairs, the first kCombPre partial outputs of this
+  // thread's chunk group and the fix-up flags are read for every workspace
+  // slot, and the slots past the row's chunks are masked afterwards.
   const bool do_out = HAS_V && p.out != nullptr;
   const int D4 = p.D / 4;
   const int d4 = tid % D4, cg = tid / D4, ng = kCombThreads / D4;
   const float4* po = reinterpret_cast<const float4*>(p.part_o + (size_t)bh * p.n_chunks * p.D);
   float2 mv = make_float2(kNegInf, 0.f);
-  if (tid < nc) mv = ml[tid];
+  if (tid < p.n_chunks) mv = ml[tid];
   float4 pre[kCombPre];
 #pragma unroll
   for (int i = 0; i < kCombPre; ++i) {
     const int c = cg + i * ng;
-    pre[i] = (do_out && c < nc) ? po[(size_t)c * D4 + d4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    pre[i] = (do_out && c < p.n_chunks) ? po[(size_t)c * D4 + d4] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  const bool pres = HAS_V && p.prescaled != 0;
+  const size_t row = (size_t)b * p.num_kv_heads + (bh % p.num_q_heads) / p.group;
+  const uint32_t* flags = p.chunk_flag != nullptr ? p.chunk_flag + row * p.n_chunks : nullptr;
+  const bool fix_head = flags != nullptr && (bh % p.num_q_heads) % p.group == 0;
+  const bool read_flags = fix_head || (pres && flags);
+  const uint32_t f0 = read_flags && tid < p.n_chunks ? flags[tid] : 0u;
+  const int nc = (L + p.chunk - 1) / p.chunk;
+  if (tid >= nc) mv = make_float2(kNegInf, 0.f);
+#pragma unroll
+  for (int i = 0; i < kCombPre; ++i)
+    if (cg + i * ng >= nc) pre[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   if (p.lse_post) {
     // The pass that wrote these posts has completed (stream order), so no
     // reader is left; zero the pairs of every chunk the pass had.
     unsigned long long* pw = p.lse_post + 2 * (size_t)bh * p.n_chunks;
     for (int i = tid; i < 2 * nc; i += kCombThreads) pw[i] = 0ull;
   }
-  const bool pres = HAS_V && p.prescaled != 0;
-  const size_t row = (size_t)b * p.num_kv_heads + (bh % p.num_q_heads) / p.group;
-  const uint32_t* flags = p.chunk_flag != nullptr ? p.chunk_flag + row * p.n_chunks : nullptr;
-  const bool fix_head = flags != nullptr && (bh % p.num_q_heads) % p.group == 0;
-  int any = 0;
-  if (fix_head || (pres && flags))
-    for (int c = tid; c < nc; c += kCombThreads) any |= (int)flags[c];
+  int any = tid < nc ? (int)f0 : 0;
+  if (read_flags)
+    for (int c = tid + kCombThreads; c < nc; c += kCombThreads) any |= (int)flags[c];
 
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   auto add = [&](float w, const float4& v) {
@@ -1604,6 +1612,8 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
       cp.chunk = pl.chunk;
       cp.n_chunks = pl.n_chunks;
       cp.D = a.head_dim;
+      cp.group = pp.group;
+      cp.num_kv_heads = a.num_kv_heads;
       if (coop) {
         cp.blk_bs = pp.blk_bs;
         cp.blk_max = pp.blk_max;
@@ -1612,8 +1622,6 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
         cp.blk_seq_stride = pp.blk_seq_stride;
         cp.chunk_flag = pp.chunk_flag;
         cp.lse_post = pp.lse_post;
-        cp.group = pp.group;
-        cp.num_kv_heads = a.num_kv_heads;
         cp.probs = a.probs;
         cp.probs_stride = a.probs_stride;
         cp.raw = pp.raw;
