@@ -13,7 +13,7 @@ from ._lib import (  # noqa: F401
     select_keep, select_workspace_bytes, set_sync_wait_us, snapkv_vote, snapkv_workspace_bytes,
     sparse_attn, sparse_workspace_bytes, quest_summarize, quest_select, quest_select_causal, quest_workspace_bytes,
     h2o_step, h2o_workspace_bytes, accumulate_ex, block_aggregate_ex, select_threshold,
-    union_keep, indexer_scores_fp8, KVSEL_FP8_E4M3, block_update,
+    union_keep, indexer_scores_fp8, indexer_topk, indexer_topk_workspace_bytes, KVSEL_FP8_E4M3, block_update,
     block_meta, block_meta_views, read_probe,
     ACC_SUM, ACC_MAX, ACC_WINDOW_MEAN, BLOCK_TOP_P_MEAN, BLOCK_FRAC_ABOVE, BLOCK_ALL_COLD,
 )

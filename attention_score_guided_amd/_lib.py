@@ -38,7 +38,8 @@ EXPORTED = (
     "kvsel_snapkv_vote", "kvsel_snapkv_workspace_bytes", "kvsel_sparse_attn",
     "kvsel_sparse_workspace_bytes", "kvsel_quest_summarize", "kvsel_quest_select", "kvsel_quest_select_causal",
     "kvsel_quest_workspace_bytes", "kvsel_accumulate_ex", "kvsel_block_aggregate_ex", "kvsel_select_threshold", "kvsel_block_update", "kvsel_read_probe",
-    "kvsel_union_keep", "kvsel_indexer_scores_fp8", "kvsel_h2o_step", "kvsel_h2o_workspace_bytes", "kvsel_set_sync_wait_us",
+    "kvsel_union_keep", "kvsel_indexer_scores_fp8", "kvsel_indexer_topk", "kvsel_indexer_topk_workspace_bytes",
+    "kvsel_h2o_step", "kvsel_h2o_workspace_bytes", "kvsel_set_sync_wait_us",
     "kvsel_status_string", "kvsel_last_error",
 )
 
@@ -92,6 +93,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvsel_select_threshold": (ctypes.c_int, [P, I64, P, I32, I32, F, P, I64, P, P]),
         "kvsel_union_keep": (ctypes.c_int, [P, I64, P, I32, I32, I32, I32, P, I64, P, P]),
         "kvsel_indexer_scores_fp8": (ctypes.c_int, [D, P, I32, F, P, I64, P]),
+        "kvsel_indexer_topk": (ctypes.c_int, [D, P, I32, F, I32, P, I64, P, P, SZ, P]),
+        "kvsel_indexer_topk_workspace_bytes": (SZ, [D, I32, I32]),
         "kvsel_block_update": (ctypes.c_int, [P, I64, P, I32, I32, P, I64, I32, I32, F, P, I64, P]),
         "kvsel_read_probe": (ctypes.c_int, [P, SZ, P, P]),
         "kvsel_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -448,6 +451,23 @@ def indexer_scores_fp8(kv: PagedKV, q: torch.Tensor, num_q_heads: int, scale: fl
         raise TypeError("the FP8 indexer takes float8_e4m3fn pages and queries")
     _check(_LIB.kvsel_indexer_scores_fp8(kv.ref(), _ptr(q, None, "q"), num_q_heads, float(scale),
                                          _ptr(scores, torch.float32, "scores"), scores.shape[-1], _stream(stream)))
+
+
+def indexer_topk_workspace_bytes(kv: PagedKV, num_q_heads: int, topk: int) -> int:
+    return int(_LIB.kvsel_indexer_topk_workspace_bytes(kv.ref(), num_q_heads, topk))
+
+
+def indexer_topk(kv: PagedKV, q: torch.Tensor, num_q_heads: int, scale: float, topk: int, keep: torch.Tensor,
+                 counts: torch.Tensor, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """kvsel_indexer_topk: bf16 indexer pages and q ``[B][H_q][d]`` -> keep ``[B*H_q][keep_stride]`` int32
+    (ascending positions) and counts ``[B*H_q]``."""
+    if q.dtype != torch.bfloat16:
+        raise TypeError("the indexer top-k takes bfloat16 queries")
+    ws, wsb = _workspace(indexer_topk_workspace_bytes(kv, num_q_heads, topk), q.device, workspace)
+    _check(_LIB.kvsel_indexer_topk(kv.ref(), _ptr(q, None, "q"), num_q_heads, float(scale), int(topk),
+                                   _ptr(keep, torch.int32, "keep"), keep.shape[-1],
+                                   _ptr(counts, torch.int32, "counts"), _ptr(ws, None, "workspace"), wsb,
+                                   _stream(stream)))
 
 
 def block_meta(rows: int, num_blocks: int, device="cuda") -> torch.Tensor:

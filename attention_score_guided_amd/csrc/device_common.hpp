@@ -83,4 +83,34 @@ __device__ __forceinline__ void st16_stream(void* p, float4 v) {
   __builtin_nontemporal_store(f32x4v{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4v*>(p));
 }
 
+// ---- MFMA operands (v_mfma_f32_16x16x32_bf16) ------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Whole-line K fragment loads for v_mfma_f32_16x16x32_bf16.  Its A operand
+// gives lane (r = lane & 15, g = lane >> 4) 8 dims of key row r, so the
+// fragment of one 32-dim k-step holds 64 bytes of each of 16 rows: every
+// load instruction touches 16 half lines.  Two consecutive k-steps 2v and
+// 2v + 1 together span bytes [128 v, 128 v + 128) of each row, one line.
+// They are loaded as two instructions that each read 8 whole lines: lane
+// (r, g) takes 16 bytes at line segment g + 4 (r >> 3) of key r & 7 (first
+// load) and of key 8 + (r & 7) (second).  Lane r < 8 then holds its own
+// step-2v fragment and lane r + 8's step-2v + 1 fragment; lane r >= 8 the
+// reverse.  One DPP row rotation by 8 per dword swaps the misplaced halves.
+__device__ __forceinline__ void k_line_exchange(bf16x8& s0, bf16x8& s1, bool lo) {
+  uint4 a = __builtin_bit_cast(uint4, s0), c = __builtin_bit_cast(uint4, s1);
+  auto ex = [lo](uint32_t& u0, uint32_t& u1) {
+    const uint32_t give = lo ? u1 : u0;
+    const uint32_t take = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)give, 0x128 /* row_ror:8 */, 0xF, 0xF, false);
+    u0 = lo ? u0 : take;
+    u1 = lo ? take : u1;
+  };
+  ex(a.x, c.x);
+  ex(a.y, c.y);
+  ex(a.z, c.z);
+  ex(a.w, c.w);
+  s0 = __builtin_bit_cast(bf16x8, a);
+  s1 = __builtin_bit_cast(bf16x8, c);
+}
+
 }  // namespace kvsel

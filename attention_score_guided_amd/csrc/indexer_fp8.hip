@@ -27,7 +27,6 @@ namespace {
 constexpr int kIThreads = 256;
 constexpr int kIWaves = kIThreads / kWave;
 constexpr int kIMaxChunk = 1024;
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct IndexerParams {
   const uint8_t* k_pages;     // [num_pages][H_kv][P][D] E4M3

@@ -90,6 +90,24 @@ hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* out, hipSt
 
 size_t select_workspace_bytes(int rows, int max_len, int mode);
 
+// Indexer top-k: the keep sets select_keep (sinks 0, window 0, budget topk)
+// would pick from the bf16 indexer's logits, without storing the logits.
+struct IndexerTopkArgs {
+  const void* k_pages;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  const void* q;
+  int num_seqs, num_kv_heads, num_q_heads, head_dim, page_size, max_pages, max_seq_len;
+  float scale;
+  int topk;
+  int32_t* keep;
+  int64_t keep_stride;
+  int32_t* counts;
+  void* workspace;
+};
+size_t indexer_topk_workspace_bytes(int num_seqs, int num_q_heads, int max_seq_len, int topk);
+hipError_t launch_indexer_topk(const IndexerTopkArgs& a, hipStream_t stream);
+
 hipError_t launch_select(const float* scores, int64_t stride, const int32_t* lengths, int rows,
                          int max_len, int sinks, int window, const int32_t* budgets,
                          int max_budget, int mode, int global_budget, int32_t* out_idx,

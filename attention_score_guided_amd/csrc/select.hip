@@ -411,6 +411,10 @@ struct SplitParams {
   uint2* slots;      // [rows][n_oseg][kCapSeg]: (position, key) of middle positions with key >= tau
   int n_oseg;        // segments of kOutSeg positions per row
   int max_len;       // positions below it lie inside every row (stride >= max_len)
+  // Compact samples (or null): samp[r][16 m + t] is the key at position
+  // 256 m + t of row r, t < 16, the positions the sample kernel reads.
+  const float* samp;
+  int samp_stride;
 };
 
 // Buffer resource over positions [0, n_valid) of a row: loads past it
@@ -447,10 +451,21 @@ __device__ __forceinline__ void unit_load(__amdgpu_buffer_rsrc_t rs, int u, int 
   for (int c4 = 0; c4 < kUnit / 4; ++c4) v[c4] = load4<kVec>(rs, j0 + c4 * 4);
 }
 
+// Sample unit u of a compact sample row (entry i is the key at position
+// 16 i): entries u*8 .. u*8+7.
+__device__ __forceinline__ void unit_load_compact(__amdgpu_buffer_rsrc_t rs, int u, int n_units,
+                                                  float4 (&v)[kUnit / 4]) {
+  const int uc = min(u, n_units - 1);
+#pragma unroll
+  for (int c4 = 0; c4 < kUnit / 4; ++c4) v[c4] = load4<true>(rs, uc * kUnit + c4 * 4);
+}
+
 // Top 16 bits of the keys of a sample unit; 0 marks a position outside the
 // middle or a unit past the row (a key whose top 16 bits are 0, a NaN with
 // those bits set, is left out of the sample, which only changes the
 // estimate).
+// STRIDED: a compact unit, whose entry i is position 16 i.
+template <bool STRIDED = false>
 __device__ __forceinline__ void unit_keys(const float4 (&v)[kUnit / 4], int u, int n_units, int lo, int hi,
                                           uint32_t (&kk)[kUnit]) {
   const int j0 = (u >> 1) * kLine * kSampleEvery + (u & 1) * kUnit;
@@ -459,7 +474,7 @@ __device__ __forceinline__ void unit_keys(const float4 (&v)[kUnit / 4], int u, i
     const float e[4] = {v[c4].x, v[c4].y, v[c4].z, v[c4].w};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int j = j0 + c4 * 4 + c;
+      const int j = STRIDED ? kSampleEvery * (u * kUnit + c4 * 4 + c) : j0 + c4 * 4 + c;
       kk[c4 * 4 + c] = (u < n_units && j >= lo && j < hi) ? order_key(e[c]) >> 16 : 0u;
     }
   }
@@ -538,7 +553,11 @@ __device__ int digit_step(DigitLds& L, int p, int rank, int& above) {
 // 4 standard deviations above its mean.  tau_lo is that key truncated to its
 // top 16 bits (two 8-bit digits; the sample keeps only those bits); 0 (store
 // every middle position) when the sample holds fewer than k_lo keys.
-template <bool kVec>
+// COMPACT: the sample is every 16th position, read from sp.samp (entry i =
+// position 16 i) instead of the score rows; positions sampled one by one
+// (no lines), the count has variance at most k_s, so the margin is
+// 4 sqrt(k_s) + 4.
+template <bool kVec, bool COMPACT = false>
 __global__ __launch_bounds__(kSampleThreads) void select_split_sample(SplitParams sp) {
   constexpr int NT = kSampleThreads;
   __shared__ DigitLds L;
@@ -546,22 +565,29 @@ __global__ __launch_bounds__(kSampleThreads) void select_split_sample(SplitParam
   const int r = blockIdx.x, tid = threadIdx.x;
   // The register units' loads go out before the row's plan is read (their
   // range is every row's [0, max_len); keys outside the middle are dropped)
-  const auto rs = row_rsrc<kVec>(p.scores + (size_t)r * p.stride, sp.max_len);
-  const int n_units_max = 2 * ((sp.max_len + kLine * kSampleEvery - 1) / (kLine * kSampleEvery));
+  const auto rs = COMPACT ? row_rsrc<true>(sp.samp + (size_t)r * sp.samp_stride, sp.samp_stride)
+                          : row_rsrc<kVec>(p.scores + (size_t)r * p.stride, sp.max_len);
+  const int n_units_max = COMPACT ? sp.samp_stride / kUnit
+                                  : 2 * ((sp.max_len + kLine * kSampleEvery - 1) / (kLine * kSampleEvery));
+  auto load_unit = [&](int u, int nu, float4 (&v)[kUnit / 4]) {
+    if constexpr (COMPACT) unit_load_compact(rs, u, nu, v);
+    else unit_load<kVec>(rs, u, nu, v);
+  };
   float4 raw[kSampleRegUnits][kUnit / 4];
 #pragma unroll
-  for (int it = 0; it < kSampleRegUnits; ++it) unit_load<kVec>(rs, tid + it * NT, n_units_max, raw[it]);
+  for (int it = 0; it < kSampleRegUnits; ++it) load_unit(tid + it * NT, n_units_max, raw[it]);
   __builtin_amdgcn_sched_barrier(0);
   const RowPlan q = row_plan(p, r);
   if (q.k == 0) return;
-  const int n_units = 2 * ((q.hi + kLine * kSampleEvery - 1) / (kLine * kSampleEvery));  // below hi
+  const int n_units = COMPACT ? ((q.hi + kSampleEvery - 1) / kSampleEvery + kUnit - 1) / kUnit   // below hi
+                              : 2 * ((q.hi + kLine * kSampleEvery - 1) / (kLine * kSampleEvery));
   digit_init<NT>(L);
   __syncthreads();
   uint32_t kr[kSampleRegUnits][kUnit];
   int m = 0;
 #pragma unroll
   for (int it = 0; it < kSampleRegUnits; ++it) {
-    unit_keys(raw[it], tid + it * NT, n_units, q.lo, q.hi, kr[it]);
+    unit_keys<COMPACT>(raw[it], tid + it * NT, n_units, q.lo, q.hi, kr[it]);
 #pragma unroll
     for (int c = 0; c < kUnit; ++c)
       if (kr[it][c]) {
@@ -572,8 +598,8 @@ __global__ __launch_bounds__(kSampleThreads) void select_split_sample(SplitParam
   for (int u = tid + kSampleRegUnits * NT; u < n_units; u += NT) {   // units past the register ones
     float4 v[kUnit / 4];
     uint32_t kk[kUnit];
-    unit_load<kVec>(rs, u, n_units, v);
-    unit_keys(v, u, n_units, q.lo, q.hi, kk);
+    load_unit(u, n_units, v);
+    unit_keys<COMPACT>(v, u, n_units, q.lo, q.hi, kk);
 #pragma unroll
     for (int c = 0; c < kUnit; ++c)
       if (kk[c]) {
@@ -587,7 +613,7 @@ __global__ __launch_bounds__(kSampleThreads) void select_split_sample(SplitParam
   __syncthreads();
   const int m_all = L.total;
   const double k_s = (double)q.k * m_all / (double)(q.hi - q.lo);
-  const int k_lo = (int)ceil(k_s + 4.0 * sqrt((double)kLine * k_s) + 4.0);
+  const int k_lo = (int)ceil(k_s + 4.0 * sqrt((COMPACT ? 1.0 : (double)kLine) * k_s) + 4.0);
   if (k_lo > m_all) {
     if (tid == 0) sp.tau[r] = 0u;
     return;
@@ -602,8 +628,8 @@ __global__ __launch_bounds__(kSampleThreads) void select_split_sample(SplitParam
   for (int u = tid + kSampleRegUnits * NT; u < n_units; u += NT) {
     float4 v[kUnit / 4];
     uint32_t kk[kUnit];
-    unit_load<kVec>(rs, u, n_units, v);
-    unit_keys(v, u, n_units, q.lo, q.hi, kk);
+    load_unit(u, n_units, v);
+    unit_keys<COMPACT>(v, u, n_units, q.lo, q.hi, kk);
 #pragma unroll
     for (int c = 0; c < kUnit; ++c)
       if (kk[c] && (int)(kk[c] >> 8) == d1) hist_add(L.h[1], kk[c] & 0xFFu);
@@ -690,33 +716,46 @@ __device__ __forceinline__ int seg_of(const int* pre, int n_seg, int f) {
 // ranges.  A row with fewer than k stored entries, or more than kFinEnt, is
 // selected from its scores by the one-workgroup algorithm; the result is the
 // same.
-__global__ __launch_bounds__(kFinThreads) void select_split_final(SplitParams sp) {
+//
+// SEG is the segment size of the stored entries (kOutSeg for the
+// compaction kernel).  prep(r) runs before the one-workgroup fallback of a
+// row that needs its scores (every thread calls it; it may fill the row in
+// sp.rp.scores).
+// SPT segments per thread: rows of at most SPT * kFinThreads segments
+// (seg_pre holds that many + 1).
+template <int SEG, int SPT, class Prep>
+__device__ void split_final_row(const SplitParams& sp, RowLds& sh, DigitLds& L, int* seg_pre, Prep&& prep) {
   constexpr int NT = kFinThreads;
-  __shared__ RowLds sh;
-  __shared__ DigitLds L;
-  __shared__ int seg_pre[kFinSegs + 1];
   const RowsParams& p = sp.rp;
   const int r = blockIdx.x, tid = threadIdx.x;
-  // segment counts: thread t holds segments 2t and 2t + 1, loaded before the
-  // row's plan is read (unused when the row needs no selection)
-  static_assert(kFinSegs == 2 * NT, "two segments per thread");
+  // segment counts: thread t holds segments SPT t .. SPT t + SPT - 1,
+  // loaded before the row's plan is read (unused when the row needs no
+  // selection)
   const int* cnt = sp.counts + (size_t)r * sp.n_oseg;
-  const int c0_all = 2 * tid < sp.n_oseg ? cnt[2 * tid] : 0;
-  const int c1_all = 2 * tid + 1 < sp.n_oseg ? cnt[2 * tid + 1] : 0;
+  int c_all[SPT];
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) c_all[i] = SPT * tid + i < sp.n_oseg ? cnt[SPT * tid + i] : 0;
   const RowPlan q = row_plan(p, r);
-  const int n_seg = (q.n + kOutSeg - 1) / kOutSeg;
+  const int n_seg = (q.n + SEG - 1) / SEG;
   if (q.k == 0) {
     select_row<NT>(p, r, sh, row_budget(p, r));
     return;
   }
   int* ws = sh.ws;
-  const int c0 = 2 * tid < n_seg ? c0_all : 0, c1 = 2 * tid + 1 < n_seg ? c1_all : 0;
+  int c_sum = 0;
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) c_sum += SPT * tid + i < n_seg ? c_all[i] : 0;
   int tot;
-  const int pre = block_exclusive_scan<NT>(c0 + c1, ws, tot);
-  if (2 * tid < n_seg) seg_pre[2 * tid] = pre;
-  if (2 * tid + 1 < n_seg) seg_pre[2 * tid + 1] = pre + c0;
+  int pre = block_exclusive_scan<NT>(c_sum, ws, tot);
+#pragma unroll
+  for (int i = 0; i < SPT; ++i)
+    if (SPT * tid + i < n_seg) {
+      seg_pre[SPT * tid + i] = pre;
+      pre += c_all[i];
+    }
   if (tid == 0) seg_pre[n_seg] = tot;
   if (tot < q.k || tot > kFinEnt) {
+    prep(r);
     select_row<NT>(p, r, sh, row_budget(p, r));
     return;
   }
@@ -724,7 +763,7 @@ __global__ __launch_bounds__(kFinThreads) void select_split_final(SplitParams sp
   // this thread's run: entries [f_beg, f_end), one search for the first
   // segment, then a walk across the (rare) segment boundaries; every load is
   // issued before any is used
-  const uint2* slots = sp.slots + (size_t)r * sp.n_oseg * kCapSeg;
+  const uint2* slots = sp.slots + (size_t)r * sp.n_oseg * SEG;
   const int per = (tot + NT - 1) / NT;
   const int f_beg = min(tid * per, tot), f_end = min(f_beg + per, tot);
   uint2 e[kFinPer];
@@ -742,7 +781,7 @@ __global__ __launch_bounds__(kFinThreads) void select_split_final(SplitParams sp
           cur = nxt;
           nxt = seg_pre[sg + 1];
         }
-        e[i] = slots[(size_t)sg * kCapSeg + (f - cur)];
+        e[i] = slots[(size_t)sg * SEG + (f - cur)];
       }
     }
   }
@@ -811,6 +850,338 @@ __global__ __launch_bounds__(kFinThreads) void select_split_final(SplitParams sp
   if (tid == 0) p.out_count[r] = q.lo + kept + (q.n - q.hi);
 }
 
+__global__ __launch_bounds__(kFinThreads) void select_split_final(SplitParams sp) {
+  __shared__ RowLds sh;
+  __shared__ DigitLds L;
+  __shared__ int seg_pre[kFinSegs + 1];
+  static_assert(kFinSegs == 2 * kFinThreads, "two segments per thread");
+  split_final_row<kOutSeg, 2>(sp, sh, L, seg_pre, [](int) {});
+}
+
+// ---- indexer top-k: the indexer's scores selected without being stored ----
+// [LONGCTX] "sparse attention" experiment: a small indexer scores every
+// cached key, s_j = scale * q . k_j, and each query keeps its k best keys.
+// The split selection above needs the scores only three times: at the
+// sampled positions (the lower bound tau_lo), once to store the keys at or
+// above tau_lo, and in a row's rare fallback.  Each of these computes the
+// scores it needs from K with the same MFMA chain as the indexer pass
+// (K_tile (16 keys x d) . Q^T (d x the heads of a KV head), fp32
+// accumulation over the k-steps in order, then * scale), so every score is
+// bit-identical to what that pass would write, and the selection equals
+// select_keep on those scores.  The 67 MB of scores of the 128K case are
+// neither written nor read back.
+struct IxkParams {
+  const uint8_t* k_pages;      // [pages][H_kv][P][D] bf16
+  const int32_t* block_table;  // [B][max_pages]
+  const int32_t* seq_lens;     // [B]
+  const uint8_t* q;            // [B][H_q][D] bf16
+  int num_kv_heads, num_q_heads, group, page_log2, max_pages, topk;
+  float scale;
+  float* samp;                 // [rows][samp_stride] scores at the sampled positions
+  int samp_stride;             // 16 per sampled line
+  int32_t* row_len;            // [rows] L_b of row r = b * H_q + h
+  const uint32_t* tau;         // [rows] tau_lo
+  int* counts;                 // [rows][n_oseg]
+  uint2* slots;                // [rows][n_oseg][kIxkSeg]
+  int n_oseg;
+};
+
+#ifndef KVSEL_IXK_QB
+#define KVSEL_IXK_QB 0   // K tiles per load batch of the fused compaction (0: 8 at d = 64, 4 at d = 128)
+#endif
+constexpr int kIxkSeg = 128;             // positions per stored segment: one wave's run of a chunk
+constexpr int kIxkChunk = kIxkSeg * 4;   // keys per compaction workgroup (4 waves)
+constexpr int kIxkSegs = 2048;           // segments per row the final pass takes (4 per thread)
+constexpr int kIxkSampTiles = 4;         // sampled lines (16-key tiles) per wave
+constexpr int kIxkStage = 16;            // stored entries per (wave, head) staged in LDS
+
+// Q^T fragments of the NCT 16-column tiles of KV head kvh's query heads
+// (column = head slot; heads past the group read as zero).  The loads are
+// unconditional (from a clamped head) so they go out together with the
+// caller's other loads; the zeroing waits for them.
+template <int D, int NCT>
+__device__ __forceinline__ void ixk_q(const IxkParams& p, int b, int kvh, int col, int grp,
+                                      bf16x8 (&qb)[NCT][D / 32]) {
+  uint4 w[NCT][D / 32];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u) {
+      const int hh = min(ct * 16 + col, p.group - 1);
+      w[ct][u] = ld16(p.q + (((size_t)b * p.num_q_heads + kvh * p.group + hh) * D + u * 32 + grp * 8) * 2);
+    }
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u)
+      qb[ct][u] = __builtin_bit_cast(bf16x8, ct * 16 + col < p.group ? w[ct][u] : make_uint4(0, 0, 0, 0));
+}
+
+// Byte address of key j of (sequence b, KV head kvh), its page read from the
+// block table.
+__device__ __forceinline__ const uint8_t* ixk_key(const IxkParams& p, int b, int kvh, int j, int D) {
+  const int P = 1 << p.page_log2;
+  const int pg = p.block_table[(size_t)b * p.max_pages + (j >> p.page_log2)];
+  return p.k_pages + (((size_t)pg * p.num_kv_heads + kvh) * P + (j & (P - 1))) * (size_t)D * 2;
+}
+
+// K fragments of the 16-key tile at keys key0 .. key0 + 15 (each clamped to
+// L - 1): lane (col, grp) holds dims u * 32 + grp * 8 .. + 8 of key
+// key0 + col.
+template <int D>
+__device__ __forceinline__ void ixk_tile(const IxkParams& p, int b, int kvh, int key0, int L, int col, int grp,
+                                         bf16x8 (&kf)[D / 32]) {
+  const uint8_t* rp = ixk_key(p, b, kvh, min(key0 + col, L - 1), D) + grp * 16;
+#pragma unroll
+  for (int u = 0; u < D / 32; ++u) kf[u] = __builtin_bit_cast(bf16x8, ld16(rp + u * 64));
+}
+
+// Scores of the sampled positions (every 16th) for every head of a KV head,
+// into the compact rows samp[b * H_q + h][i] = s_{16 i}; also each row's
+// length.  Grid (ceil(max_len / (256 * 4 kIxkSampTiles)), H_kv, B), 256
+// threads; a wave scores kIxkSampTiles tiles of 16 sampled positions.
+template <int D, int NCT>
+__global__ __launch_bounds__(256) void ixk_samples(IxkParams p) {
+  constexpr int NU = D / 32;
+  const int b = blockIdx.z, kvh = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int col = lane & 15, grp = lane >> 4;
+  const int L = p.seq_lens[b];
+  if (blockIdx.x == 0)
+    for (int i = tid; i < p.group; i += 256) p.row_len[(size_t)b * p.num_q_heads + kvh * p.group + i] = L;
+  const int tile0 = (blockIdx.x * 4 + wave) * kIxkSampTiles;
+  if (tile0 * 256 >= L) return;
+  bf16x8 qb[NCT][NU];
+  ixk_q<D, NCT>(p, b, kvh, col, grp, qb);
+  bf16x8 kf[kIxkSampTiles][NU];
+#pragma unroll
+  for (int t = 0; t < kIxkSampTiles; ++t) {
+    // lane col loads sampled position 16 (16 tile + col)
+    const uint8_t* rp = ixk_key(p, b, kvh, min((tile0 + t) * 256 + 16 * col, L - 1), D) + grp * 16;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) kf[t][u] = __builtin_bit_cast(bf16x8, ld16(rp + u * 64));
+  }
+#pragma unroll
+  for (int t = 0; t < kIxkSampTiles; ++t) {
+    const int line = tile0 + t;   // entries 16 line .. + 15
+    if (line * 256 >= L) break;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < NU; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][u], qb[ct][u], acc, 0, 0, 0);
+      const int hh = ct * 16 + col;
+      if (hh < p.group) {
+        float* dst = p.samp + ((size_t)b * p.num_q_heads + kvh * p.group + hh) * p.samp_stride + line * 16 + grp * 4;
+        *reinterpret_cast<float4*>(dst) =
+            make_float4(acc[0] * p.scale, acc[1] * p.scale, acc[2] * p.scale, acc[3] * p.scale);
+      }
+    }
+  }
+}
+
+// The indexer pass fused with the compaction: grid (ceil(max_len /
+// kIxkChunk), H_kv, B), 256 threads.  Wave w scores positions
+// start + kIxkSeg w .. + kIxkSeg - 1 (segment 4 * chunk + w of every row of
+// the KV head) tile by tile and appends, for each head, the positions whose key is
+// at least the row's tau_lo, with their keys, in position order: the four
+// lanes holding a head's 16 keys of a tile take their slots from ballots
+// of the tile's four key columns (no cross-lane exchange).  A head's first
+// kIxkStage entries of the segment are staged in LDS and written out at the
+// end as whole 16-byte pairs, so the few, scattered entries of a tile do not
+// each become a store of their own; entries past them go out directly.  Rows that keep everything
+// (k >= L_b) store nothing.
+template <int D, int NCT>
+__global__ __launch_bounds__(256) void ixk_compact(IxkParams p) {
+  constexpr int NU = D / 32;
+  constexpr int QB = KVSEL_IXK_QB > 0 ? KVSEL_IXK_QB : D == 128 ? 4 : 8;   // K tiles per load batch
+  __shared__ int page_lds[kIxkChunk / 16 + 2];
+  __shared__ uint4 stage[4][16 * NCT][kIxkStage / 2];    // per wave and head slot: entry pairs
+  __shared__ int stage_n[4][16 * NCT];
+  const int b = blockIdx.z, kvh = blockIdx.y, chunk = blockIdx.x;
+  const int L = p.seq_lens[b];
+  const int start = chunk * kIxkChunk;
+  if (start >= L) return;
+  const int n_keys = min(kIxkChunk, L - start);
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int col = lane & 15, grp = lane >> 4;
+  const int P = 1 << p.page_log2;
+  const int first_page = start >> p.page_log2;
+  const int n_pages = ((start + n_keys - 1) >> p.page_log2) - first_page + 1;
+  // the page ids, the queries and the rows' bounds are loaded together
+  // (one round trip) before the page ids go to LDS
+  static_assert(kIxkChunk / 16 + 2 <= 256, "one page id per thread");
+  const int pg_id = tid < n_pages ? p.block_table[(size_t)b * p.max_pages + first_page + tid] : 0;
+  bf16x8 qb[NCT][NU];
+  const bool keep_all = p.topk >= L;
+  uint32_t tau[NCT];
+  size_t rowi[NCT];
+  bool on[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    rowi[ct] = (size_t)b * p.num_q_heads + kvh * p.group + min(ct * 16 + col, p.group - 1);
+    tau[ct] = p.tau[rowi[ct]];   // read for every lane; used only where `on`
+  }
+  ixk_q<D, NCT>(p, b, kvh, col, grp, qb);
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    on[ct] = ct * 16 + col < p.group && !keep_all;
+    if (!on[ct]) tau[ct] = 0xFFFFFFFFu;
+  }
+  if (tid < n_pages) page_lds[tid] = pg_id;
+  __syncthreads();
+  const int wbase = wave * kIxkSeg;
+  if (wbase >= n_keys) return;
+  const int seg = chunk * 4 + wave;
+  const size_t head_stride = (size_t)P * D * 2;
+  const size_t page_stride = head_stride * p.num_kv_heads;
+  auto krow = [&](int key) -> const uint8_t* {
+    const int j = start + key;
+    const int pg = page_lds[(j >> p.page_log2) - first_page];
+    return p.k_pages + (size_t)pg * page_stride + kvh * head_stride + (size_t)(j & (P - 1)) * D * 2;
+  };
+  constexpr int nt = kIxkSeg / 16;
+  static_assert(nt % QB == 0, "whole load batches per segment");
+  const uint64_t mine = 0x0001000100010001ull << col;          // lanes col + 16 g
+  const uint64_t below = mine & ((1ull << (16 * grp)) - 1ull);  // those with g < grp
+  int base[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) base[ct] = 0;
+  for (int t0 = 0; t0 < nt; t0 += QB) {
+    bf16x8 kb[QB][NU];
+#pragma unroll
+    for (int t = 0; t < QB; ++t) {
+      // whole-line loads, then one DPP exchange (k_line_exchange)
+      const int key = wbase + (t0 + t) * 16 + (col & 7);
+      const int sg = (grp + 4 * (col >> 3)) * 16;
+      const uint8_t* ra = krow(min(key, n_keys - 1)) + sg;
+      const uint8_t* rb = krow(min(key + 8, n_keys - 1)) + sg;
+#pragma unroll
+      for (int v = 0; v < NU / 2; ++v) {
+        kb[t][2 * v] = __builtin_bit_cast(bf16x8, ld16(ra + v * 128));
+        kb[t][2 * v + 1] = __builtin_bit_cast(bf16x8, ld16(rb + v * 128));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < QB; ++t) {
+#pragma unroll
+      for (int v = 0; v < NU / 2; ++v) k_line_exchange(kb[t][2 * v], kb[t][2 * v + 1], col < 8);
+      const int k0 = wbase + (t0 + t) * 16 + grp * 4;   // chunk-relative key of acc[0]
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < NU; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[t][u], qb[ct][u], acc, 0, 0, 0);
+        uint32_t kk[4];
+        bool f[4];
+        int before = 0, tot = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          kk[i] = order_key(acc[i] * p.scale);
+          f[i] = on[ct] && k0 + i < n_keys && kk[i] >= tau[ct];
+          // the head's four lanes are col, col + 16, col + 32, col + 48: its
+          // entries of this tile in lanes below this one, and in all four
+          const uint64_t m = __ballot(f[i]);
+          before += __popcll(m & below);
+          tot += __popcll(m & mine);
+        }
+        if (f[0] | f[1] | f[2] | f[3]) {
+          uint2* slot = p.slots + (rowi[ct] * p.n_oseg + seg) * kIxkSeg;
+          uint2* st = reinterpret_cast<uint2*>(stage[wave][ct * 16 + col]);
+          int pos = base[ct] + before;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (f[i]) {
+              const uint2 e = make_uint2((uint32_t)(start + k0 + i), kk[i]);
+              if (pos < kIxkStage) st[pos] = e;
+              else slot[pos] = e;
+              ++pos;
+            }
+        }
+        base[ct] += tot;
+      }
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+    if (grp == 0) {
+      const int n = on[ct] ? base[ct] : 0;
+      stage_n[wave][ct * 16 + col] = n;
+      if (ct * 16 + col < p.group) p.counts[rowi[ct] * p.n_oseg + seg] = n;
+    }
+  // This wave's staged pairs out: head slot hs, pair i; LDS operations of a
+  // wave complete in order, and the fences keep the compiler from moving the
+  // reads above the writes.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  constexpr int kPairs = kIxkStage / 2;
+  for (int x = lane; x < 16 * NCT * kPairs; x += kWave) {
+    const int hs = x / kPairs, i = x % kPairs;
+    if (hs < p.group && 2 * i < min(stage_n[wave][hs], kIxkStage)) {
+      const size_t row = (size_t)b * p.num_q_heads + kvh * p.group + hs;
+      reinterpret_cast<uint4*>(p.slots + (row * p.n_oseg + seg) * kIxkSeg)[i] = stage[wave][hs][i];
+    }
+  }
+}
+
+// Scores of row r (positions 0 .. L - 1) into dst, by the whole workgroup
+// (kFinThreads threads): the fallback of a row whose stored entries do not
+// decide its selection.  Head h sits in its column slot of the indexer's
+// tile (the same MFMA element), so the values are those of the other passes.
+template <int D>
+__device__ void ixk_row_scores(const IxkParams& p, int r, float* dst) {
+  constexpr int NU = D / 32;
+  const int b = r / p.num_q_heads, h = r % p.num_q_heads;
+  const int kvh = h / p.group, hs = (h - kvh * p.group) % 16;
+  const int L = p.seq_lens[b];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int col = lane & 15, grp = lane >> 4;
+  bf16x8 qb[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (col == hs) w = ld16(p.q + (((size_t)b * p.num_q_heads + h) * D + u * 32 + grp * 8) * 2);
+    qb[u] = __builtin_bit_cast(bf16x8, w);
+  }
+  const int n_tiles = (L + 15) / 16;
+  for (int t = wave; t < n_tiles; t += kFinThreads / kWave) {
+    bf16x8 kf[NU];
+    ixk_tile<D>(p, b, kvh, t * 16, L, col, grp, kf);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < NU; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], qb[u], acc, 0, 0, 0);
+    if (col == hs) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = t * 16 + grp * 4 + i;
+        if (j < L) dst[j] = acc[i] * p.scale;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// The final selection of the fused path: segments of kIxkSeg positions; a
+// row that falls back first has its scores computed into its own slot area
+// (sp.rp.scores and sp.rp.stride point there), which it no longer needs.
+template <int D>
+__global__ __launch_bounds__(kFinThreads) void ixk_final(SplitParams sp, IxkParams ip) {
+  __shared__ RowLds sh;
+  __shared__ DigitLds L;
+  __shared__ int seg_pre[kIxkSegs + 1];
+  split_final_row<kIxkSeg, kIxkSegs / kFinThreads>(sp, sh, L, seg_pre, [&](int r) {
+    ixk_row_scores<D>(ip, r, const_cast<float*>(sp.rp.scores) + (size_t)r * sp.rp.stride);
+  });
+}
+
+// Row lengths of the unfused path (row r = b * H_q + h has L_b positions).
+__global__ void ixk_row_len(const int32_t* seq_lens, int num_q_heads, int rows, int32_t* row_len) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < rows) row_len[r] = seq_lens[r / num_q_heads];
+}
+
 // Shapes that may split (the workspace is sized for them) and those that do.
 inline bool may_split(int rows, int max_len) {
   return rows <= kSplitMaxRows && max_len >= kSplitMinLen && max_len <= kFinSegs * kOutSeg;
@@ -835,7 +1206,7 @@ hipError_t launch_split(const RowsParams& rp, int rows, int max_len, void* works
   split_layout(rows, max_len, &o_counts, &o_slots);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   SplitParams sp{rp, reinterpret_cast<uint32_t*>(ws), reinterpret_cast<int*>(ws + o_counts),
-                 reinterpret_cast<uint2*>(ws + o_slots), (max_len + kOutSeg - 1) / kOutSeg, max_len};
+                 reinterpret_cast<uint2*>(ws + o_slots), (max_len + kOutSeg - 1) / kOutSeg, max_len, nullptr, 0};
   const dim3 cgrid((unsigned)((sp.n_oseg + kCompactWaves - 1) / kCompactWaves), (unsigned)rows);
   // rows 16-byte aligned: float4 loads
   if ((rp.stride & 3) == 0 && (reinterpret_cast<uintptr_t>(rp.scores) & 15) == 0) {
@@ -1113,6 +1484,135 @@ __global__ __launch_bounds__(kRowThreads) void global_percentile_rows_kernel(Row
 }
 
 }  // namespace
+
+namespace {
+
+inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// The fused path takes the shapes the split selection takes, with rows of at
+// most kIxkSegs segments of kIxkSeg positions.
+inline bool ixk_fused(int rows, int max_len, int topk) {
+  return use_split(rows, max_len, topk) && max_len <= kIxkSegs * kIxkSeg;
+}
+
+// Workspace of the fused path: compact samples, row lengths, tau_lo, the
+// segment counts and the stored entries (a fallback row's scores reuse its
+// own entry area); of the other path: the logits, row lengths and the
+// selection's own workspace.
+struct IxkLayout {
+  size_t o_row_len, o_tau, o_counts, o_slots, total;
+  int samp_stride, n_oseg;
+  int64_t stride;   // the other path: floats per logits row
+};
+
+inline IxkLayout ixk_layout(int num_seqs, int num_q_heads, int max_len, int topk) {
+  IxkLayout l{};
+  const size_t rows = (size_t)num_seqs * num_q_heads;
+  if (ixk_fused((int)rows, max_len, topk)) {
+    l.samp_stride = 16 * ((max_len + 255) / 256);
+    l.n_oseg = (max_len + kIxkSeg - 1) / kIxkSeg;
+    l.o_row_len = al256(rows * l.samp_stride * sizeof(float));
+    l.o_tau = l.o_row_len + al256(rows * sizeof(int32_t));
+    l.o_counts = l.o_tau + al256(rows * sizeof(uint32_t));
+    l.o_slots = l.o_counts + al256(rows * l.n_oseg * sizeof(int));
+    l.total = l.o_slots + al256(rows * l.n_oseg * kIxkSeg * sizeof(uint2));
+  } else {
+    l.stride = ((int64_t)max_len + 3) & ~int64_t(3);
+    l.o_row_len = al256(rows * (size_t)l.stride * sizeof(float));
+    l.o_slots = l.o_row_len + al256(rows * sizeof(int32_t));   // the selection's workspace
+    l.total = l.o_slots + al256(select_workspace_bytes((int)rows, max_len, 0));
+  }
+  return l;
+}
+
+template <int D, int NCT>
+hipError_t launch_ixk(const IxkParams& ip, const SplitParams& sp, int num_seqs, int max_len, hipStream_t stream) {
+  const int rows = num_seqs * ip.num_q_heads;
+  const int lines = (max_len + 255) / 256;
+  hipLaunchKernelGGL((ixk_samples<D, NCT>), dim3((lines + 4 * kIxkSampTiles - 1) / (4 * kIxkSampTiles),
+                     ip.num_kv_heads, num_seqs), dim3(256), 0, stream, ip);
+  hipLaunchKernelGGL((select_split_sample<true, true>), dim3(rows), dim3(kSampleThreads), 0, stream, sp);
+  hipLaunchKernelGGL((ixk_compact<D, NCT>), dim3((max_len + kIxkChunk - 1) / kIxkChunk, ip.num_kv_heads, num_seqs),
+                     dim3(256), 0, stream, ip);
+  hipLaunchKernelGGL((ixk_final<D>), dim3(rows), dim3(kFinThreads), 0, stream, sp, ip);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t indexer_topk_workspace_bytes(int num_seqs, int num_q_heads, int max_seq_len, int topk) {
+  return ixk_layout(num_seqs, num_q_heads, max_seq_len, topk).total;
+}
+
+hipError_t launch_indexer_topk(const IndexerTopkArgs& a, hipStream_t stream) {
+  const IxkLayout l = ixk_layout(a.num_seqs, a.num_q_heads, a.max_seq_len, a.topk);
+  uint8_t* ws = static_cast<uint8_t*>(a.workspace);
+  const int rows = a.num_seqs * a.num_q_heads;
+  int32_t* row_len = reinterpret_cast<int32_t*>(ws + l.o_row_len);
+  if (!ixk_fused(rows, a.max_seq_len, a.topk)) {
+    // the logits in the workspace, then the row selection on them
+    float* logits = reinterpret_cast<float*>(ws);
+    hipLaunchKernelGGL(ixk_row_len, dim3((rows + 255) / 256), dim3(256), 0, stream, a.seq_lens, a.num_q_heads,
+                       rows, row_len);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const DecodePlan pl = plan_decode(a.num_seqs, a.num_kv_heads, a.num_q_heads, a.head_dim, a.max_seq_len, false);
+    DecodeArgs d{};
+    d.k_pages = a.k_pages;
+    d.block_table = a.block_table;
+    d.seq_lens = a.seq_lens;
+    d.q = a.q;
+    d.num_seqs = a.num_seqs;
+    d.num_kv_heads = a.num_kv_heads;
+    d.num_q_heads = a.num_q_heads;
+    d.head_dim = a.head_dim;
+    d.page_size = a.page_size;
+    d.max_pages = a.max_pages;
+    d.max_seq_len = a.max_seq_len;
+    d.bf16 = true;
+    d.scale = a.scale;
+    d.probs = logits;
+    d.probs_stride = l.stride;
+    d.emit_logits = true;
+    d.decay = 1.f;
+    d.workspace = ws;   // the logits-only pass uses no workspace
+    e = launch_decode(d, pl, stream);
+    if (e != hipSuccess) return e;
+    return launch_select(logits, l.stride, row_len, rows, a.max_seq_len, 0, 0, nullptr, a.topk, 0, 0, a.keep,
+                         a.keep_stride, a.counts, ws + l.o_slots, stream);
+  }
+  IxkParams ip{};
+  ip.k_pages = static_cast<const uint8_t*>(a.k_pages);
+  ip.block_table = a.block_table;
+  ip.seq_lens = a.seq_lens;
+  ip.q = static_cast<const uint8_t*>(a.q);
+  ip.num_kv_heads = a.num_kv_heads;
+  ip.num_q_heads = a.num_q_heads;
+  ip.group = a.num_q_heads / a.num_kv_heads;
+  ip.page_log2 = __builtin_ctz((unsigned)a.page_size);
+  ip.max_pages = a.max_pages;
+  ip.topk = a.topk;
+  ip.scale = a.scale;
+  ip.samp = reinterpret_cast<float*>(ws);
+  ip.samp_stride = l.samp_stride;
+  ip.row_len = row_len;
+  ip.tau = reinterpret_cast<uint32_t*>(ws + l.o_tau);
+  ip.counts = reinterpret_cast<int*>(ws + l.o_counts);
+  ip.slots = reinterpret_cast<uint2*>(ws + l.o_slots);
+  ip.n_oseg = l.n_oseg;
+  // The selection reads the row lengths the sample pass writes; a fallback
+  // row's scores go to its own entry area (n_oseg * kIxkSeg * 2 floats).
+  RowsParams rp{reinterpret_cast<const float*>(ws + l.o_slots), (int64_t)l.n_oseg * kIxkSeg * 2, row_len, nullptr,
+                a.topk, 0, 0, a.keep, a.keep_stride, a.counts};
+  SplitParams sp{rp, reinterpret_cast<uint32_t*>(ws + l.o_tau), reinterpret_cast<int*>(ws + l.o_counts),
+                 reinterpret_cast<uint2*>(ws + l.o_slots), l.n_oseg, a.max_seq_len, ip.samp, l.samp_stride};
+  const bool two = ip.group > 16;
+  if (a.head_dim == 128)
+    return two ? launch_ixk<128, 2>(ip, sp, a.num_seqs, a.max_seq_len, stream)
+               : launch_ixk<128, 1>(ip, sp, a.num_seqs, a.max_seq_len, stream);
+  return two ? launch_ixk<64, 2>(ip, sp, a.num_seqs, a.max_seq_len, stream)
+             : launch_ixk<64, 1>(ip, sp, a.num_seqs, a.max_seq_len, stream);
+}
 
 size_t select_workspace_bytes(int rows, int max_len, int mode) {
   if (mode != 1) return may_split(rows, max_len) ? split_layout(rows, max_len, nullptr, nullptr) : 0;

@@ -303,8 +303,18 @@ def long_context_workload(torch, K, synth, args) -> dict:
     ws_s = torch.empty(K.sparse_workspace_bytes(Bq, HQq, 128, 2048), dtype=torch.uint8, device="cuda")
     ws_k = torch.empty(max(256, K.select_workspace_bytes(Bq * HQq, cap, K.SELECT_ROWS)), dtype=torch.uint8,
                        device="cuda")
+    ws_x = torch.empty(K.indexer_topk_workspace_bytes(kv_i_s[0], HQq, 2048), dtype=torch.uint8, device="cuda")
 
+    # a step: the indexer's top-2048 per query head (scores computed where the
+    # selection needs them, never stored), then sparse attention over them
     def sparse_step(s):
+        K.indexer_topk(kv_i_s[s], cfg["qi_dec"][s], HQq, 1.0, 2048, keep, kcnt, workspace=ws_x)
+        K.sparse_attn(kv_f_s[s], cfg["q_dec"][s], HQq, keep.view(Bq, HQq, 2048), kcnt.view(Bq, HQq), 2048,
+                      cfg["scale"], out, workspace=ws_s)
+
+    # the same step with the scores written out by the indexer pass and then
+    # selected by select_keep (the same keep sets)
+    def sparse_step_stored(s):
         K.decode_attn_scores(kv_i_s[s], cfg["qi_dec"][s], HQq, 1.0, None, None, scores, K.EMIT_LOGITS,
                              workspace=ws_d)
         K.select_keep(srows, step_rlens[s], cap, 0, 0, None, 2048, keep, kcnt, workspace=ws_k)
@@ -320,6 +330,14 @@ def long_context_workload(torch, K, synth, args) -> dict:
     b.record()
     torch.cuda.synchronize()
     t_sparse = a.elapsed_time(b) / steps
+    sparse_step_stored(0)
+    torch.cuda.synchronize()
+    a.record()
+    for s in range(steps):
+        sparse_step_stored(s)
+    b.record()
+    torch.cuda.synchronize()
+    t_sparse_stored = a.elapsed_time(b) / steps
     # each step alone after a 512 MB read that evicts the Infinity Cache
     # (256 MB) with clean lines, so that no step reads what an earlier one
     # left there (a write would instead leave 256 MB of dirty lines whose
@@ -344,7 +362,10 @@ def long_context_workload(torch, K, synth, args) -> dict:
     g_sp = capture(torch, lambda: [sparse_step(s) for s in range(steps)])
     t_sparse_graph = timed(torch, g_sp.replay, 3) / steps
     del g_sp
-    sparse_bytes = (Bq * Lq * 64 * 2) + 2 * Bq * HQq * Lq * 4 + Bq * HQq * 2048 * 128 * 2 * 2
+    # algorithmic bytes of a step: the indexer keys once and the gathered K/V
+    # rows; the stored-scores step also writes and reads back the scores
+    sparse_bytes = (Bq * Lq * 64 * 2) + Bq * HQq * 2048 * 128 * 2 * 2
+    sparse_bytes_stored = sparse_bytes + 2 * Bq * HQq * Lq * 4
 
     # per-block metadata of the offloading layer: the step's probabilities
     # (emitted by the sparse pass) walked into a float score and an int32
@@ -438,7 +459,9 @@ def long_context_workload(torch, K, synth, args) -> dict:
                         "gb_per_s": round(sparse_bytes / (t_sparse * 1e-3) / 1e9, 1),
                         "us_graph": round(t_sparse_graph * 1e3, 1),
                         "us_cache_flushed_median": round(t_sparse_flushed * 1e3, 1),
-                        "bytes": sparse_bytes},
+                        "bytes": sparse_bytes,
+                        "us_scores_stored": round(t_sparse_stored * 1e3, 1),
+                        "bytes_scores_stored": sparse_bytes_stored},
         "block_update": {"us_graph": round(t_bup * 1e3, 2), "us_eager_calls": round(t_bup_eager * 1e3, 1),
                          "rows": Bq * HQq, "entries_per_row": 2048, "block_size": 16,
                          "offload_sizing_us_graph": round(t_bup_o * 1e3, 2),

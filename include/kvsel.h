@@ -441,6 +441,40 @@ int kvsel_indexer_scores_fp8(const kvsel_paged_kv* kv, const void* q, int32_t nu
                              float* scores, int64_t stride, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Indexer top-k ([LONGCTX] "sparse attention" experiment: the indexer scores
+ * every cached key of a query and the query attends to its top 2048 keys).
+ * For sequence b and query head h (indexer KV head c = h / G), with
+ * s_j = scale * q[b][h] . k[c][j] for the L_b cached keys j < L_b:
+ *   keep[b * num_q_heads + h][0 .. n)  the positions of the min(topk, L_b)
+ *        largest s_j, equal scores resolved toward the lower position,
+ *        ascending;  counts[b * num_q_heads + h] = n.
+ * The sets are exactly those of kvsel_decode_attn_scores (EMIT_LOGITS, same
+ * scale) followed by kvsel_select_keep (ROWS mode, sinks 0, window 0,
+ * budgets NULL, max_budget topk) on the logits, without the logits being
+ * written: long rows compute the scores where the selection needs them
+ * (sampled positions, the pass that stores the keys at or above a sampled
+ * lower bound of the cut, and a row's fallback) with the same products.
+ *   kv      bf16 pages, head_dim 64 or 128; v_pages is not read.
+ *   q       [num_seqs][num_q_heads][head_dim] bf16.
+ *   keep    [num_seqs * num_q_heads][keep_stride] i32, keep_stride >=
+ *           min(topk, max_seq_len); entries past counts are left untouched.
+ *   workspace: >= kvsel_indexer_topk_workspace_bytes(kv, num_q_heads, topk)
+ *           bytes of device memory, 256-byte aligned, contents ignored.
+ * Preconditions as kvsel_decode_attn_scores (1 <= seq_lens[b] <=
+ * max_seq_len, block table entries name pages); keep, counts and workspace
+ * do not overlap each other or the inputs.
+ * Supported: G = num_q_heads / num_kv_heads a power of two <= 8 or 16, 24,
+ * 32.  Errors: INVALID (NULL pointers, dims, topk < 1, keep_stride),
+ * UNSUPPORTED (dtype other than BF16, head_dim, page_size, G, no gfx950
+ * device), WORKSPACE, HIP.
+ * ------------------------------------------------------------------------ */
+int kvsel_indexer_topk(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads, float scale, int32_t topk,
+                       int32_t* keep, int64_t keep_stride, int32_t* counts, void* workspace,
+                       size_t workspace_bytes, void* stream);
+/* 0 for an invalid descriptor or topk < 1. */
+size_t kvsel_indexer_topk_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads, int32_t topk);
+
+/* ------------------------------------------------------------------------
  * Quest page summaries ([LONGCTX] sparse-attention experiment, the Quest
  * strategy: the per-channel minimum and maximum of a page's keys).
  * For every whole page p of every sequence with p >= first_page (pages with

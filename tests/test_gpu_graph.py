@@ -246,3 +246,69 @@ def test_sparse_step_graph_replays_with_new_queries():
         for a, b in zip((scores, keep, kc, out), want):
             assert torch.equal(a, b), f"replay {rep} differs from the eager step"
         assert int(kc.min()) == k
+
+
+def test_fused_sparse_step_graph_replays_with_new_queries():
+    """The sparse decode step as bench.py times it (kvsel_indexer_topk, whose
+    scores are never stored, then sparse attention) captured in one graph and
+    replayed with new queries copied in between: every replay equals the
+    eager step on those queries bit for bit, and the keep sets equal those of
+    the stored-scores path."""
+    import attention_score_guided_amd as K
+    B, Hq, Hkv, d, dI, P, L, k = 2, 8, 2, 128, 64, 16, 40000, 2048
+    g = synth.generator(92)
+    bt, n_pages = synth.shuffled_block_table(B, L, P, g)
+    bt = bt.cuda()
+    kp = synth.normal((n_pages, Hkv, P, d), g, torch.bfloat16).cuda()
+    vp = synth.normal((n_pages, Hkv, P, d), g, torch.bfloat16).cuda()
+    kip = synth.normal((n_pages, 1, P, dI), g, torch.bfloat16).cuda()
+    lens = torch.tensor([L, L - 777], dtype=torch.int32).cuda()
+    kvi = K.PagedKV(kip, None, bt, lens, P, L)
+    kvf = K.PagedKV(kp, vp, bt, lens, P, L)
+    qi = torch.empty((B, Hq, dI), dtype=torch.bfloat16, device="cuda")
+    q = torch.empty((B, Hq, d), dtype=torch.bfloat16, device="cuda")
+    keep = torch.zeros((B * Hq, k), dtype=torch.int32, device="cuda")
+    kc = torch.zeros((B * Hq,), dtype=torch.int32, device="cuda")
+    out = torch.zeros((B, Hq, d), device="cuda")
+    ws_x = torch.empty(K.indexer_topk_workspace_bytes(kvi, Hq, k), dtype=torch.uint8, device="cuda")
+    ws_s = torch.empty(K.sparse_workspace_bytes(B, Hq, d, k), dtype=torch.uint8, device="cuda")
+    scores = torch.zeros((B, Hq, L), device="cuda")
+    rl = lens.repeat_interleave(Hq).to(torch.int32)
+    keep_s = torch.zeros_like(keep)
+    kc_s = torch.zeros_like(kc)
+
+    def step():
+        K.indexer_topk(kvi, qi, Hq, 1.0, k, keep, kc, workspace=ws_x)
+        K.sparse_attn(kvf, q, Hq, keep.view(B, Hq, k), kc.view(B, Hq), k, 1 / math.sqrt(d), out, workspace=ws_s)
+
+    def new_queries(seed):
+        gg = synth.generator(seed)
+        qi.copy_(synth.normal((B, Hq, dI), gg, torch.bfloat16).cuda())
+        q.copy_(synth.normal((B, Hq, d), gg, torch.bfloat16).cuda())
+        torch.cuda.synchronize()
+
+    new_queries(1)
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        new_queries(200 + rep)
+        step()                      # eager on the same queries
+        K.decode_attn_scores(kvi, qi, Hq, 1.0, None, None, scores, K.EMIT_LOGITS)
+        K.select_keep(scores.view(B * Hq, L), rl, L, 0, 0, None, k, keep_s, kc_s)
+        torch.cuda.synchronize()
+        assert torch.equal(keep, keep_s) and torch.equal(kc, kc_s), "fused keep sets differ from the stored-scores path"
+        want = [t.clone() for t in (keep, kc, out)]
+        out.fill_(float("nan"))
+        keep.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((keep, kc, out), want):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager step"
+        assert int(kc.min()) == k
