@@ -1043,7 +1043,18 @@ __global__ __launch_bounds__(256) void ixk_compact(IxkParams p) {
   constexpr int nt = kIxkSeg / 16;
   static_assert(nt % QB == 0, "whole load batches per segment");
   const uint64_t mine = 0x0001000100010001ull << col;          // lanes col + 16 g
-  const uint64_t below = mine & ((1ull << (16 * grp)) - 1ull);  // those with g < grp
+  // The bound as a float: for a score s (never NaN), key(s) >= tau exactly
+  // when s >= the float whose key is tau (-0 and +0 share one key and
+  // compare equal).  Bounds at or below key(-inf) (tau = 0: store every
+  // position) become -inf; bounds above key(+inf), and heads that store
+  // nothing, a NaN that no score reaches.
+  float tau_f[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const uint32_t t = tau[ct];
+    const float x = __uint_as_float((t & 0x80000000u) ? (t & 0x7FFFFFFFu) : ~t);
+    tau_f[ct] = !on[ct] ? __builtin_nanf("") : t < 0x00800000u ? -__builtin_inff() : x;
+  }
   int base[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) base[ct] = 0;
@@ -1073,18 +1084,18 @@ __global__ __launch_bounds__(256) void ixk_compact(IxkParams p) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < NU; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[t][u], qb[ct][u], acc, 0, 0, 0);
-        uint32_t kk[4];
+        float sc[4];
         bool f[4];
         int before = 0, tot = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          kk[i] = order_key(acc[i] * p.scale);
-          f[i] = on[ct] && k0 + i < n_keys && kk[i] >= tau[ct];
+          sc[i] = acc[i] * p.scale;
+          f[i] = k0 + i < n_keys && sc[i] >= tau_f[ct];
           // the head's four lanes are col, col + 16, col + 32, col + 48: its
           // entries of this tile in lanes below this one, and in all four
-          const uint64_t m = __ballot(f[i]);
-          before += __popcll(m & below);
-          tot += __popcll(m & mine);
+          const uint64_t m = __ballot(f[i]) & mine;
+          before = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, before));
+          tot += __popcll(m);
         }
         if (f[0] | f[1] | f[2] | f[3]) {
           uint2* slot = p.slots + (rowi[ct] * p.n_oseg + seg) * kIxkSeg;
@@ -1093,7 +1104,7 @@ __global__ __launch_bounds__(256) void ixk_compact(IxkParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (f[i]) {
-              const uint2 e = make_uint2((uint32_t)(start + k0 + i), kk[i]);
+              const uint2 e = make_uint2((uint32_t)(start + k0 + i), order_key(sc[i]));
               if (pos < kIxkStage) st[pos] = e;
               else slot[pos] = e;
               ++pos;

@@ -10,7 +10,8 @@ The fused call never writes the scores, so it is checked two ways:
     of the cut (the worst gap is printed).
 Cases: the 128K sparse-step configuration the benchmark times (B=4, 32 query
 heads on one d=64 indexer head, L=131073, k=2048), ragged rows, d=128 with
-G=4, G=32, rows that keep everything (k >= L_b), the shapes that take the
+G=4, G=32, rows that keep everything (k >= L_b), a row too short for its
+sample to bound the cut (every position stored), the shapes that take the
 materialised path (short rows, k > L/8), and both fallbacks of the fused
 path: massive ties (every score equal, so more than 16384 keys reach the
 sampled bound) and a bound set too high by keys that score high only at the
@@ -126,6 +127,7 @@ def test_indexer_topk_128k_sparse_step():
     (2, 2, 8, 128, [20000, 16391], 1024, 32, 0.125),     # fused, d=128, G=4
     (1, 1, 32, 64, [70001], 2048, 64, 1.0),              # fused, G=32 (two column tiles)
     (3, 1, 16, 64, [17000, 1500, 2048], 2048, 16, 1.0),  # fused; two rows keep everything
+    (2, 1, 8, 64, [20000, 2100], 2048, 16, 1.0),         # fused; a short row's sample is below k_lo (bound 0)
     (2, 1, 4, 64, [4000, 3001], 512, 16, 1.0),           # short rows: materialised logits
     (1, 1, 8, 64, [20000], 6144, 16, 1.0),               # k > L / 8: materialised logits
 ])
