@@ -889,9 +889,12 @@ struct IxkParams {
 #ifndef KVSEL_IXK_QB
 #define KVSEL_IXK_QB 0   // K tiles per load batch of the fused compaction (0: 8 at d = 64, 4 at d = 128)
 #endif
-constexpr int kIxkSeg = 128;             // positions per stored segment: one wave's run of a chunk
+#ifndef KVSEL_IXK_SEG
+#define KVSEL_IXK_SEG 64   // 128K top-2048: 48.7 us at 64, 49.9 at 128, 51.9 at 256 (same box)
+#endif
+constexpr int kIxkSeg = KVSEL_IXK_SEG;   // positions per stored segment: one wave's run of a chunk
 constexpr int kIxkChunk = kIxkSeg * 4;   // keys per compaction workgroup (4 waves)
-constexpr int kIxkSegs = 2048;           // segments per row the final pass takes (4 per thread)
+constexpr int kIxkSegs = kIxkSeg >= 128 ? 2048 : 4096;   // segments per row the final pass takes (4 or 8 per thread)
 constexpr int kIxkSampTiles = 4;         // sampled lines (16-key tiles) per wave
 constexpr int kIxkStage = 16;            // stored entries per (wave, head) staged in LDS
 
@@ -994,7 +997,7 @@ __global__ __launch_bounds__(256) void ixk_samples(IxkParams p) {
 template <int D, int NCT>
 __global__ __launch_bounds__(256) void ixk_compact(IxkParams p) {
   constexpr int NU = D / 32;
-  constexpr int QB = KVSEL_IXK_QB > 0 ? KVSEL_IXK_QB : D == 128 ? 4 : 8;   // K tiles per load batch
+  constexpr int QB = KVSEL_IXK_QB > 0 ? KVSEL_IXK_QB : (D == 128 ? 4 : 8) < kIxkSeg / 16 ? (D == 128 ? 4 : 8) : kIxkSeg / 16;
   __shared__ int page_lds[kIxkChunk / 16 + 2];
   __shared__ uint4 stage[4][16 * NCT][kIxkStage / 2];    // per wave and head slot: entry pairs
   __shared__ int stage_n[4][16 * NCT];
@@ -1056,8 +1059,16 @@ __global__ __launch_bounds__(256) void ixk_compact(IxkParams p) {
     tau_f[ct] = !on[ct] ? __builtin_nanf("") : t < 0x00800000u ? -__builtin_inff() : x;
   }
   int base[NCT];
+  uint2* slot[NCT];     // this head's entries of the segment
+  uint2* st[NCT];       // and their LDS stage
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) base[ct] = 0;
+  for (int ct = 0; ct < NCT; ++ct) {
+    base[ct] = 0;
+    slot[ct] = p.slots + (rowi[ct] * p.n_oseg + seg) * kIxkSeg;
+    st[ct] = reinterpret_cast<uint2*>(stage[wave][ct * 16 + col]);
+  }
+  // whole segments test no key against the row's end
+  const bool whole = wbase + kIxkSeg <= n_keys;
   for (int t0 = 0; t0 < nt; t0 += QB) {
     bf16x8 kb[QB][NU];
 #pragma unroll
@@ -1090,7 +1101,7 @@ __global__ __launch_bounds__(256) void ixk_compact(IxkParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           sc[i] = acc[i] * p.scale;
-          f[i] = k0 + i < n_keys && sc[i] >= tau_f[ct];
+          f[i] = (whole || k0 + i < n_keys) && sc[i] >= tau_f[ct];
           // the head's four lanes are col, col + 16, col + 32, col + 48: its
           // entries of this tile in lanes below this one, and in all four
           const uint64_t m = __ballot(f[i]) & mine;
@@ -1098,15 +1109,13 @@ __global__ __launch_bounds__(256) void ixk_compact(IxkParams p) {
           tot += __popcll(m);
         }
         if (f[0] | f[1] | f[2] | f[3]) {
-          uint2* slot = p.slots + (rowi[ct] * p.n_oseg + seg) * kIxkSeg;
-          uint2* st = reinterpret_cast<uint2*>(stage[wave][ct * 16 + col]);
           int pos = base[ct] + before;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (f[i]) {
               const uint2 e = make_uint2((uint32_t)(start + k0 + i), order_key(sc[i]));
-              if (pos < kIxkStage) st[pos] = e;
-              else slot[pos] = e;
+              if (pos < kIxkStage) st[ct][pos] = e;
+              else slot[ct][pos] = e;
               ++pos;
             }
         }
