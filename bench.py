@@ -854,7 +854,8 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default 20; the Llama-3-8B workload runs its stated 256 decode steps)")
+                    help="timed steps (default 20; the Llama-3-8B workload runs its stated 256 decode steps, "
+                         "the 128K workload its 64 sparse decode steps)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
@@ -871,7 +872,7 @@ def main() -> int:
                          "long_context_128k: three SnapKV votes); prints no JSON")
     args = ap.parse_args()
     if args.steps is None:
-        args.steps = 256 if args.workload == "llama3_8b_steps" else 20
+        args.steps = {"llama3_8b_steps": 256, "long_context_128k": 64}.get(args.workload, 20)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path has no "
               "multi-GPU component to run", file=sys.stderr)

@@ -10,7 +10,12 @@ benchmark uses, end to end against the float64 oracle:
     page 64): the fused decode + block-64 aggregation per layer, the head and
     layer sum at block size 1, and the global percentile top 25%; block
     scores of EVERY (layer, sequence, KV head) row and the kept blocks of
-    every sequence.
+    every sequence;
+  * 128K long-context case: all 64 sparse decode steps at full size (B=4,
+    32 query heads, L = 131072 + s + 1), each step's indexer top-2048 by
+    kvsel_indexer_topk (equal to the stored-scores path on every row of every
+    step) and sparse attention; sampled rows of the first and last steps
+    against the oracle (keep sets and attention outputs).
 Keep sets are checked twice: bit-exact against the oracle's selection on the
 GPU's own scores, and end to end against the oracle's selection on the
 oracle's scores, where a difference must be a swap between scores within
@@ -208,3 +213,47 @@ def test_llama70b_step_two_stacked_layers_full_size():
         worst = max(worst, keep_swap_gap(gsel[b], np.asarray(e2e[b]), want_agg_max[b], n_blk))
     assert sum(len(x) for x in gsel) == budget
     note(f"70B step kept blocks vs the oracle's: worst gap {worst:.2e}")
+
+
+def test_long_context_128k_64_sparse_steps_full_size():
+    K = _K()
+    L, B, Hq, steps, k = 131072, 4, 32, 64, 2048
+    cfg = synth.long_context_128k(seq_len=L, sparse_steps=steps, device="cuda")
+    kvt, kit = cfg["kv"], cfg["kv_index"]
+    cap = L + steps
+    keep = torch.empty((B * Hq, k), dtype=torch.int32, device="cuda")
+    kc = torch.empty((B * Hq,), dtype=torch.int32, device="cuda")
+    keep_s = torch.empty_like(keep)
+    kc_s = torch.empty_like(kc)
+    scores = torch.empty((B, Hq, -(-cap // 64) * 64), device="cuda")
+    out = torch.empty((B, Hq, 128), device="cuda")
+    ws_x = torch.empty(K.indexer_topk_workspace_bytes(
+        K.PagedKV(kit.k_pages, None, kit.block_table, kit.seq_lens, 16, cap), Hq, k), dtype=torch.uint8, device="cuda")
+    checked = {}
+    for s_ in range(steps):
+        lens = torch.full((B,), L + s_ + 1, dtype=torch.int32, device="cuda")
+        kvi = K.PagedKV(kit.k_pages, None, kit.block_table, lens, 16, cap)
+        kvf = K.PagedKV(kvt.k_pages, kvt.v_pages, kvt.block_table, lens, 16, cap)
+        K.indexer_topk(kvi, cfg["qi_dec"][s_], Hq, 1.0, k, keep, kc, workspace=ws_x)
+        K.sparse_attn(kvf, cfg["q_dec"][s_], Hq, keep.view(B, Hq, k), kc.view(B, Hq), k, cfg["scale"], out)
+        K.decode_attn_scores(kvi, cfg["qi_dec"][s_], Hq, 1.0, None, None, scores, K.EMIT_LOGITS)
+        K.select_keep(scores.view(B * Hq, scores.shape[-1]), lens.repeat_interleave(Hq).to(torch.int32), cap, 0, 0,
+                      None, k, keep_s, kc_s)
+        torch.cuda.synchronize()
+        assert torch.equal(kc, kc_s) and torch.equal(keep, keep_s), f"step {s_}: fused keep sets differ"
+        assert int(kc.min()) == k
+        if s_ in (0, steps - 1):
+            checked[s_] = (keep.clone(), out.clone())
+    for s_, (kk, oo) in checked.items():
+        n = L + s_ + 1
+        for b, h in [(0, 3), (3, 30)]:
+            note(f"128K sparse step {s_ + 1}/{steps}, row b={b} h={h}")
+            KI, _ = logical_kv_rows(kit.k_pages, None, kit.block_table, b, 0, n)
+            want_s = O.indexer_scores(f64(cfg["qi_dec"][s_, b, h])[None, :], KI[0])[0]
+            e2e = O.select_keep(want_s, n, 0, 0, k)
+            got = kk[b * Hq + h].cpu().numpy()
+            gap = keep_swap_gap(got, e2e, want_s, n)
+            note(f"  top-2048 vs the oracle's: {len(set(got.tolist()) ^ set(e2e.tolist()))} differing, worst gap {gap:.2e}")
+            Kl, Vl = logical_kv_rows(kvt.k_pages, kvt.v_pages, kvt.block_table, b, h // 4, n)
+            so, _ = O.sparse_attention(f64(cfg["q_dec"][s_, b, h])[None, :], Kl, Vl, [np.sort(got)], cfg["scale"])
+            assert rel_l2(f64(oo[b, h]), so[0]) < OUT_TOL
