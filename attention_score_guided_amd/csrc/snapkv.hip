@@ -168,6 +168,19 @@ __device__ __forceinline__ void wave_items(int G, int wave, int& i0, int& i1) {
   i1 = min(items, i0 + per);
 }
 
+// Sum of a lane's value over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four
+// row-quads of one MFMA output column), with the cross-row swaps of gfx950
+// (v_permlane16_swap / v_permlane32_swap: two VALU operations, no LDS
+// round trip).  With the same register as both operands, the swap's two
+// results hold the values of the two rows (halves) paired by it, so their sum
+// is the pairwise sum in every lane.
+__device__ __forceinline__ float quad_rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ void merge_ml(float& m, float& l, float m2, float l2) {
   const float mn = fmaxf(m, m2);
   if (mn == kNegInf) return;  // both empty
@@ -476,8 +489,7 @@ void snapkv_pass2(VoteParams p) {
         }
       }
     }
-    cs += __shfl_xor(cs, 16, kWave);
-    cs += __shfl_xor(cs, 32, kWave);
+    cs = quad_rows_sum(cs);
     if (grp == 0) hv[g * kStage + t * 16 + col] = cs;
   };
 
@@ -505,9 +517,7 @@ void snapkv_pass2(VoteParams p) {
         for (int k = 0; k < TN; ++k) cs[k] += exp2_hw(fmaf(a[k][i], p.c2, -lr[rt][i]));
     }
 #pragma unroll
-    for (int k = 0; k < TN; ++k) cs[k] += __shfl_xor(cs[k], 16, kWave);
-#pragma unroll
-    for (int k = 0; k < TN; ++k) cs[k] += __shfl_xor(cs[k], 32, kWave);
+    for (int k = 0; k < TN; ++k) cs[k] = quad_rows_sum(cs[k]);
     if (grp == 0) {
 #pragma unroll
       for (int k = 0; k < TN; ++k) hv[g * kStage + (t + k) * 16 + col] = cs[k];
