@@ -180,13 +180,17 @@ def test_rows_long_rows_split_over_workgroups(seed):
         _check_rows(scores, lengths, sinks, window, budgets, idx.cpu().numpy(), cnt.cpu().numpy())
 
 
-@pytest.mark.parametrize("case", ["gaussian", "quantised", "clustered", "many_candidates", "dense_segment",
-                                  "sampled_lines_hot", "sampled_lines_cold", "cut_far_above_bound"])
+@pytest.mark.parametrize("case", ["gaussian", "quantised", "fine_ties", "plateau_at_cut", "clustered",
+                                  "many_candidates", "dense_segment", "sampled_lines_hot", "sampled_lines_cold",
+                                  "cut_far_above_bound"])
 def test_rows_long_rows_compaction(case):
     """Long rows with a small keep fraction (the indexer and vote shape): a
     sample of the row bounds the cut from below, the positions at or above
     the bound are compacted per segment and the selection finishes on them.
-    Cases cover ties at the threshold (quantised scores), kept positions
+    Cases cover ties at the threshold (quantised scores: coarsely, so the
+    cut's 16-bit bin holds more keys than are ranked directly, or finely, so
+    a few dozen keys with repeated values are; or 700 keys equal to the
+    cut, more than are ranked directly, with few others stored), kept positions
     clustered in a few segments, a segment whose every position passes,
     more positions at the threshold than the final stage holds, and samples
     that misjudge the row (the sample reads one 16-position line in every
@@ -197,7 +201,7 @@ def test_rows_long_rows_compaction(case):
     cut lies far above the bound (the final stage's digits restart from the
     whole key); every result must equal the oracle's."""
     K = _K()
-    rng = np.random.default_rng({"gaussian": 11, "quantised": 12, "clustered": 13,
+    rng = np.random.default_rng({"gaussian": 11, "quantised": 12, "fine_ties": 19, "plateau_at_cut": 20, "clustered": 13,
                                  "many_candidates": 14, "dense_segment": 15,
                                  "sampled_lines_hot": 16, "sampled_lines_cold": 17,
                                  "cut_far_above_bound": 18}[case])
@@ -208,6 +212,12 @@ def test_rows_long_rows_compaction(case):
     sinks, window = (4, 512) if case in ("gaussian", "clustered") else (0, 0)
     if case == "quantised":
         scores = np.round(scores * 64.0).astype(np.float32) / 64.0        # heavy ties at tau
+    if case == "fine_ties":
+        scores = np.round(scores * 2048.0).astype(np.float32) / 2048.0    # ~40 keys per bin at the cut, repeated values
+    if case == "plateau_at_cut":
+        for r in range(rows):                     # 700 keys equal to the (k - 200)-th largest
+            v = np.sort(scores[r, :lengths[r]])[::-1][budgets[r] - 200]
+            scores[r, rng.choice(lengths[r], size=700, replace=False)] = v
     if case == "clustered":
         for r in range(rows):                                            # top keys in a few segments
             for c in rng.integers(2000, lengths[r] - 2000, size=3):
