@@ -133,10 +133,29 @@ struct SparseArgs {
   // (sequence, query head)'s log-sum-exp also written to lse_out (or null).
   bool raw_logits;
   float* lse_out;
+  // Only the split-K partial pass runs: the caller combines the partials
+  // (sparse_partials) itself; out, lse_out and probs normalisation are its own.
+  bool partials_only;
+  // Each set also holds the current token, position seq_lens[b] - 1, as an
+  // entry after its `count` listed ones (when count < max_count), not yet
+  // written to `indices`.
+  bool append_current;
 };
 
 size_t sparse_workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int max_count);
 hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream);
+
+// Where launch_sparse leaves its split-K partials in a.workspace: for
+// (sequence, query head) bh and chunk c < ceil(count / slice), the chunk's
+// (max logit, sum of exp(logit - max)) at part_ml[bh * n_chunks + c] and its
+// unnormalised output sum_j exp(s_j - max) v_j at part_o[(bh * n_chunks + c) * D];
+// chunk c covers listed entries [c * slice, (c + 1) * slice).
+struct SparsePartials {
+  float* part_o;
+  float2* part_ml;
+  int n_chunks, slice;
+};
+SparsePartials sparse_partials(const SparseArgs& a);
 
 struct SnapkvArgs {
   const void* k_pages;

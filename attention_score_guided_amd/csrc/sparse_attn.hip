@@ -40,6 +40,7 @@ struct SparseParams {
   int64_t idx_stride;
   const int32_t* counts;    // [B][idx_heads], read clamped to max_count
   int num_kv_heads, num_q_heads, idx_heads, page_log2, max_pages, n_chunks, max_count;
+  bool append_current;      // entry `count` (< max_count) is position seq_lens[b] - 1
   float scale;
   float* probs;             // [B][Hq][idx_stride] raw logits written here, or null
   float* part_o;            // [B][Hq][n_chunks][D]
@@ -69,7 +70,9 @@ __global__ __launch_bounds__(kThreads) void sparse_partial(SparseParams p) {
   const int kvh = h0 / G;
   // A count above max_count is a caller error; clamping it keeps every
   // access inside the index rows and the workspace the grid was sized for.
-  const int count = min(p.counts[(size_t)b * p.idx_heads + set], p.max_count);
+  const int listed = min(p.counts[(size_t)b * p.idx_heads + set], p.max_count);
+  const bool app = p.append_current && listed < p.max_count;
+  const int count = listed + (app ? 1 : 0);
   const int start = chunk * kSlice;
   if (start >= count) return;
   const int n = min(kSlice, count - start);
@@ -83,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void sparse_partial(SparseParams p) {
   // Row offsets of the listed positions, resolved through the block table
   // once, so the gathers below need no dependent load.
   for (int i = tid; i < kSlice; i += kThreads) {
-    const int j = i < n ? list[i] : -1;
+    const int j = i >= n ? -1 : start + i == listed ? L - 1 : list[i];
     long long off = -1;
     if (j >= 0 && j < L) {
       const int pg = p.block_table[(size_t)b * p.max_pages + (j >> p.page_log2)];
@@ -325,12 +328,24 @@ size_t sparse_workspace_bytes(int num_seqs, int num_q_heads, int head_dim, int m
          align256(bh * sizeof(float));
 }
 
-hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream) {
+SparsePartials sparse_partials(const SparseArgs& a) {
   const int n_chunks = max(1, (a.max_count + kSlice - 1) / kSlice);
   const size_t bh = (size_t)a.num_seqs * a.num_q_heads;
   uint8_t* ws = static_cast<uint8_t*>(a.workspace);
-  float* part_o = reinterpret_cast<float*>(ws);
-  float2* part_ml = reinterpret_cast<float2*>(ws + align256(bh * n_chunks * a.head_dim * sizeof(float)));
+  SparsePartials r;
+  r.part_o = reinterpret_cast<float*>(ws);
+  r.part_ml = reinterpret_cast<float2*>(ws + align256(bh * n_chunks * a.head_dim * sizeof(float)));
+  r.n_chunks = n_chunks;
+  r.slice = kSlice;
+  return r;
+}
+
+hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream) {
+  const SparsePartials pt = sparse_partials(a);
+  const int n_chunks = pt.n_chunks;
+  const size_t bh = (size_t)a.num_seqs * a.num_q_heads;
+  float* part_o = pt.part_o;
+  float2* part_ml = pt.part_ml;
   float* lse_ws = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(part_ml) +
                                            align256(bh * n_chunks * sizeof(float2)));
   const int G = a.num_q_heads / a.num_kv_heads;
@@ -353,6 +368,7 @@ hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream) {
   sp.max_pages = a.max_pages;
   sp.n_chunks = n_chunks;
   sp.max_count = a.max_count;
+  sp.append_current = a.append_current;
   sp.scale = a.scale;
   sp.probs = a.probs;
   sp.part_o = part_o;
@@ -365,7 +381,7 @@ hipError_t launch_sparse(const SparseArgs& a, hipStream_t stream) {
   else
     e = a.head_dim == 128 ? launch_sparse_d<false, 128>(sp, gt, grid, stream)
                           : launch_sparse_d<false, 64>(sp, gt, grid, stream);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.partials_only) return e;
   SparseCombineParams cp{a.counts, part_o, part_ml, a.out, a.lse_out ? a.lse_out : lse_ws, a.num_q_heads,
                          a.num_kv_heads, a.idx_heads, n_chunks, a.head_dim, a.max_count};
   hipLaunchKernelGGL(sparse_combine, dim3((unsigned)bh), dim3(128), n_chunks * sizeof(float), stream, cp);

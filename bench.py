@@ -846,7 +846,7 @@ def llama3_h2o_workload(torch, K, synth, args) -> dict:
         "step_us": round(t * 1e3, 1),
         "kept_keys_per_step": round(keys),
         "kept_fraction": round(keys / full_keys, 4),
-        "launches_per_step": 6,
+        "launches_per_step": 2,
     }
 
 
