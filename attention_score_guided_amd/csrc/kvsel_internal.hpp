@@ -113,6 +113,10 @@ hipError_t launch_select(const float* scores, int64_t stride, const int32_t* len
                          int max_budget, int mode, int global_budget, int32_t* out_idx,
                          int64_t out_stride, int32_t* out_count, void* workspace,
                          hipStream_t stream);
+// Whether launch_select (ROWS mode) splits these rows over workgroups; when it
+// does not, every row is selected by the one-workgroup algorithm of
+// row_select.hpp, which a caller may then run inside its own kernel.
+bool select_rows_split(int rows, int max_len, int max_budget);
 
 struct SparseArgs {
   const void* k_pages;

@@ -22,12 +22,15 @@
 //                         segments, the bound is summed across the page's
 //                         lanes with DPP.  HBM-bound: 2*d*E bytes per
 //                         (page, KV head) in, 4*G bytes out.
-//   (row selection)       the radix top-k of the row selection kernels over
-//                         each (sequence, query head) row of page bounds.
-//   quest_expand_kernel   one workgroup per row: chosen pages (ascending) to
-//                         token positions, then the partial tail page.
+//   quest_pick_kernel     one workgroup per (sequence, query head) row of
+//                         page bounds: the radix top-k of the row selection
+//                         (row_select.hpp), then the chosen pages (ascending)
+//                         expanded to token positions, followed by the
+//                         partial tail page.  Rows long enough for the split
+//                         selection take it, then quest_expand_kernel.
 #include "device_common.hpp"
 #include "kvsel_internal.hpp"
+#include "row_select.hpp"
 
 #include <algorithm>
 
@@ -220,8 +223,11 @@ struct ExpandParams {
   int num_q_heads, page_log2;
 };
 
-__global__ __launch_bounds__(kQThreads) void quest_expand_kernel(ExpandParams p) {
-  const int r = blockIdx.x;
+// Row r's chosen pages (ascending) expanded to token positions, then the
+// partial tail page; with query_pos, only positions <= query_pos[b] (every
+// thread of the NT-thread workgroup calls it).
+template <int NT>
+__device__ void expand_row(const ExpandParams& p, int r) {
   const int b = r / p.num_q_heads;
   const int L = p.seq_lens[b];
   const int P = 1 << p.page_log2;
@@ -232,7 +238,7 @@ __global__ __launch_bounds__(kQThreads) void quest_expand_kernel(ExpandParams p)
   const int32_t* pi = p.page_idx + (size_t)r * p.page_stride;
   int32_t* out = p.out_idx + (size_t)r * p.out_stride;
   if (!p.query_pos) {
-    for (int i = threadIdx.x; i < total; i += kQThreads)
+    for (int i = threadIdx.x; i < total; i += NT)
       out[i] = i < chosen ? (pi[i >> p.page_log2] << p.page_log2) + (i & (P - 1)) : n_full * P + (i - chosen);
     if (threadIdx.x == 0) p.out_count[r] = total;
     return;
@@ -242,7 +248,7 @@ __global__ __launch_bounds__(kQThreads) void quest_expand_kernel(ExpandParams p)
   // so that the block-wide count sees each of them.
   const int limit = p.query_pos[b];
   int kept = 0;
-  for (int base = 0; base < total; base += kQThreads) {
+  for (int base = 0; base < total; base += NT) {
     const int i = base + threadIdx.x;
     int v = 0;
     if (i < total) v = i < chosen ? (pi[i >> p.page_log2] << p.page_log2) + (i & (P - 1)) : n_full * P + (i - chosen);
@@ -251,6 +257,24 @@ __global__ __launch_bounds__(kQThreads) void quest_expand_kernel(ExpandParams p)
     kept += __syncthreads_count(in);
   }
   if (threadIdx.x == 0) p.out_count[r] = kept;
+}
+
+__global__ __launch_bounds__(kQThreads) void quest_expand_kernel(ExpandParams p) {
+  expand_row<kQThreads>(p, blockIdx.x);
+}
+
+// The row's top pages by bound (when some sequence has a whole page), then
+// their expansion, in one workgroup: the chosen page ids written by the
+// selection are read back after a barrier.
+__global__ __launch_bounds__(kRowThreads) void quest_pick_kernel(RowsParams rp, ExpandParams ep) {
+  __shared__ RowLds sh;
+  const int r = blockIdx.x;
+  if (ep.page_cnt) {
+    if (rp.lengths[r] <= kSmallRow) select_row_small(rp, r, sh, rp.max_budget);
+    else select_row<kRowThreads>(rp, r, sh, rp.max_budget);
+    __syncthreads();
+  }
+  expand_row<kRowThreads>(ep, r);
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -367,10 +391,6 @@ hipError_t launch_quest_select(const QuestArgs& a, const void* summary, const vo
     else e = a.head_dim == 128 ? launch_bounds_d<false, 128>(bp, gt, grid, stream)
                                : launch_bounds_d<false, 64>(bp, gt, grid, stream);
     if (e != hipSuccess) return e;
-    // top budget_pages pages of each (sequence, query head) row, ascending
-    e = launch_select(bounds, bounds_stride, row_pages, (int)rows, max_whole, 0, 0, nullptr, budget_pages, 0, 0,
-                      page_idx, kp, page_cnt, ws, stream);
-    if (e != hipSuccess) return e;
   }
   ExpandParams ep{};
   ep.seq_lens = a.seq_lens;
@@ -383,7 +403,17 @@ hipError_t launch_quest_select(const QuestArgs& a, const void* summary, const vo
   ep.out_count = out_count;
   ep.num_q_heads = a.num_q_heads;
   ep.page_log2 = log2p;
-  hipLaunchKernelGGL(quest_expand_kernel, dim3((unsigned)rows), dim3(kQThreads), 0, stream, ep);
+  // top budget_pages pages of each (sequence, query head) row, ascending,
+  // then their positions
+  const RowsParams rp{bounds, bounds_stride, row_pages, nullptr, budget_pages, 0, 0, page_idx, kp, page_cnt};
+  if (max_whole > 0 && select_rows_split((int)rows, max_whole, budget_pages)) {
+    hipError_t e = launch_select(bounds, bounds_stride, row_pages, (int)rows, max_whole, 0, 0, nullptr,
+                                 budget_pages, 0, 0, page_idx, kp, page_cnt, ws, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(quest_expand_kernel, dim3((unsigned)rows), dim3(kQThreads), 0, stream, ep);
+  } else {
+    hipLaunchKernelGGL(quest_pick_kernel, dim3((unsigned)rows), dim3(kRowThreads), 0, stream, rp, ep);
+  }
   return hipGetLastError();
 }
 

@@ -1341,6 +1341,8 @@ hipError_t launch_indexer_topk(const IndexerTopkArgs& a, hipStream_t stream) {
              : launch_ixk<64, 1>(ip, sp, a.num_seqs, a.max_seq_len, stream);
 }
 
+bool select_rows_split(int rows, int max_len, int max_budget) { return use_split(rows, max_len, max_budget); }
+
 size_t select_workspace_bytes(int rows, int max_len, int mode) {
   if (mode != 1) return may_split(rows, max_len) ? split_layout(rows, max_len, nullptr, nullptr) : 0;
   return ((size_t)rows * max_len * sizeof(uint64_t) + 255 & ~size_t(255)) + 256;
