@@ -459,10 +459,10 @@ def indexer_topk_workspace_bytes(kv: PagedKV, num_q_heads: int, topk: int) -> in
 
 def indexer_topk(kv: PagedKV, q: torch.Tensor, num_q_heads: int, scale: float, topk: int, keep: torch.Tensor,
                  counts: torch.Tensor, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    """kvsel_indexer_topk: bf16 indexer pages and q ``[B][H_q][d]`` -> keep ``[B*H_q][keep_stride]`` int32
-    (ascending positions) and counts ``[B*H_q]``."""
-    if q.dtype != torch.bfloat16:
-        raise TypeError("the indexer top-k takes bfloat16 queries")
+    """kvsel_indexer_topk: indexer pages and q ``[B][H_q][d]``, both bfloat16 or both float8_e4m3fn ->
+    keep ``[B*H_q][keep_stride]`` int32 (ascending positions) and counts ``[B*H_q]``."""
+    if q.dtype not in (torch.bfloat16, torch.float8_e4m3fn) or q.dtype != kv.dtype:
+        raise TypeError("the indexer top-k takes bfloat16 or float8_e4m3fn pages and queries of one dtype")
     ws, wsb = _workspace(indexer_topk_workspace_bytes(kv, num_q_heads, topk), q.device, workspace)
     _check(_LIB.kvsel_indexer_topk(kv.ref(), _ptr(q, None, "q"), num_q_heads, float(scale), int(topk),
                                    _ptr(keep, torch.int32, "keep"), keep.shape[-1],

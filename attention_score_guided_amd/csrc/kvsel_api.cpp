@@ -593,21 +593,33 @@ int kvsel_indexer_scores_fp8(const kvsel_paged_kv* kv, const void* q, int32_t nu
                     "indexer_scores_fp8 launch");
 }
 
+// The indexer top-k's keys are bf16 or FP8 E4M3; the descriptor's other
+// fields take the checks of the other calls.
+static int check_indexer_kv(const kvsel_paged_kv* kv, int32_t num_q_heads) {
+  if (!kv) return fail(KVSEL_ERR_INVALID, "kv descriptor is NULL");
+  if (kv->dtype != KVSEL_BF16 && kv->dtype != KVSEL_FP8_E4M3)
+    return fail(KVSEL_ERR_UNSUPPORTED, "dtype %d (the indexer top-k takes BF16 or FP8_E4M3)", kv->dtype);
+  kvsel_paged_kv shape = *kv;
+  shape.dtype = KVSEL_BF16;
+  return check_kv(&shape, num_q_heads, false);
+}
+
 size_t kvsel_indexer_topk_workspace_bytes(const kvsel_paged_kv* kv, int32_t num_q_heads, int32_t topk) {
-  if (check_kv(kv, num_q_heads, false) != KVSEL_OK || topk < 1) return 0;
+  if (check_indexer_kv(kv, num_q_heads) != KVSEL_OK || topk < 1) return 0;
   return kvsel::indexer_topk_workspace_bytes(kv->num_seqs, num_q_heads, kv->max_seq_len, topk);
 }
 
 int kvsel_indexer_topk(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads, float scale, int32_t topk,
                        int32_t* keep, int64_t keep_stride, int32_t* counts, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  int st = check_kv(kv, num_q_heads, false);
+  int st = check_indexer_kv(kv, num_q_heads);
   if (st != KVSEL_OK) return st;
   if (!q || !keep || !counts) return fail(KVSEL_ERR_INVALID, "NULL pointer argument");
   if (topk < 1) return fail(KVSEL_ERR_INVALID, "topk %d < 1", topk);
   if (keep_stride < std::min<int64_t>(topk, kv->max_seq_len))
     return fail(KVSEL_ERR_INVALID, "keep_stride %lld < min(topk, max_seq_len)", (long long)keep_stride);
-  if (kv->dtype != KVSEL_BF16) return fail(KVSEL_ERR_UNSUPPORTED, "dtype %d (the indexer top-k takes BF16)", kv->dtype);
+  if (kv->dtype == KVSEL_FP8_E4M3 && ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv->k_pages)) & 15))
+    return fail(KVSEL_ERR_INVALID, "q and k_pages must be 16-byte aligned");
   const int g = num_q_heads / kv->num_kv_heads;
   if (!group_supported(g) || g > 32) return fail(KVSEL_ERR_UNSUPPORTED, "group size %d (power of two <= 8, 16, 24 or 32)", g);
   if ((long long)kv->num_seqs * num_q_heads > (1 << 24))
@@ -620,6 +632,7 @@ int kvsel_indexer_topk(const kvsel_paged_kv* kv, const void* q, int32_t num_q_he
   kvsel::IndexerTopkArgs a{kv->k_pages, kv->block_table, kv->seq_lens, q, kv->num_seqs, kv->num_kv_heads,
                            num_q_heads, kv->head_dim, kv->page_size, kv->max_pages_per_seq, kv->max_seq_len,
                            scale, topk, keep, keep_stride, counts, workspace};
+  a.fp8 = kv->dtype == KVSEL_FP8_E4M3;
   return hip_status(kvsel::launch_indexer_topk(a, static_cast<hipStream_t>(stream)), "indexer_topk launch");
 }
 

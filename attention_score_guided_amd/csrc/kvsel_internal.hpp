@@ -104,6 +104,7 @@ struct IndexerTopkArgs {
   int64_t keep_stride;
   int32_t* counts;
   void* workspace;
+  bool fp8;   // keys and queries in FP8 E4M3 (else bf16)
 };
 size_t indexer_topk_workspace_bytes(int num_seqs, int num_q_heads, int max_seq_len, int topk);
 hipError_t launch_indexer_topk(const IndexerTopkArgs& a, hipStream_t stream);

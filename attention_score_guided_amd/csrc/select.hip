@@ -20,6 +20,7 @@
 // distinct 64-bit composites whose top-K (radix select in one workgroup)
 // equals the top-K by (percentile desc, row asc, position asc).
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "kvsel_internal.hpp"
@@ -578,10 +579,10 @@ __global__ __launch_bounds__(kFinThreads) void select_split_final(SplitParams sp
 // select_keep on those scores.  The 67 MB of scores of the 128K case are
 // neither written nor read back.
 struct IxkParams {
-  const uint8_t* k_pages;      // [pages][H_kv][P][D] bf16
+  const uint8_t* k_pages;      // [pages][H_kv][P][D] bf16 or FP8 E4M3
   const int32_t* block_table;  // [B][max_pages]
   const int32_t* seq_lens;     // [B]
-  const uint8_t* q;            // [B][H_q][D] bf16
+  const uint8_t* q;            // [B][H_q][D] in the keys' format
   int num_kv_heads, num_q_heads, group, page_log2, max_pages, topk;
   float scale;
   float* samp;                 // [rows][samp_stride] scores at the sampled positions
@@ -605,52 +606,87 @@ constexpr int kIxkSegs = kIxkSeg >= 128 ? 2048 : 4096;   // segments per row the
 constexpr int kIxkSampTiles = 4;         // sampled lines (16-key tiles) per wave
 constexpr int kIxkStage = 16;            // stored entries per (wave, head) staged in LDS
 
+// The two key formats: bf16 (one 32-channel k-step per 16-byte fragment,
+// v_mfma_f32_16x16x32_bf16) and FP8 E4M3 (8-byte fragments,
+// v_mfma_f32_16x16x32_fp8_fp8).  Both take D / 32 k-steps per 16 x 16 tile.
+// The channels a lane feeds are those of the matching indexer pass, so
+// every score is bit-identical to the one it would have written: bf16, lane
+// group g gives channels u * 32 + 8 g .. + 8 to step u; FP8, lane group g
+// gives channels g D / 4 + 8 u .. + 8 to step u.
+template <bool F8>
+using IxkFrag = std::conditional_t<F8, long, bf16x8>;
+
+template <bool F8>
+__device__ __forceinline__ f32x4 ixk_mfma(IxkFrag<F8> a, IxkFrag<F8> b, f32x4 c) {
+  if constexpr (F8) return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// One key or query row's fragments for lane group grp, from its first byte.
+template <int D, bool F8>
+__device__ __forceinline__ void ixk_row_frags(const uint8_t* row, int grp, IxkFrag<F8> (&f)[D / 32]) {
+  if constexpr (F8) {
+    const uint8_t* rp = row + grp * (D / 4);
+#pragma unroll
+    for (int v = 0; v < D / 64; ++v) {
+      const uint4 w = ld16(rp + v * 16);
+      f[2 * v] = (long)w.x | ((long)w.y << 32);
+      f[2 * v + 1] = (long)w.z | ((long)w.w << 32);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u) f[u] = __builtin_bit_cast(bf16x8, ld16(row + grp * 16 + u * 64));
+  }
+}
+
+template <bool F8>
+__device__ __forceinline__ IxkFrag<F8> ixk_zero() {
+  if constexpr (F8) return 0l;
+  else return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+}
+
 // Q^T fragments of the NCT 16-column tiles of KV head kvh's query heads
 // (column = head slot; heads past the group read as zero).  The loads are
 // unconditional (from a clamped head) so they go out together with the
 // caller's other loads; the zeroing waits for them.
-template <int D, int NCT>
+template <int D, int NCT, bool F8>
 __device__ __forceinline__ void ixk_q(const IxkParams& p, int b, int kvh, int col, int grp,
-                                      bf16x8 (&qb)[NCT][D / 32]) {
-  uint4 w[NCT][D / 32];
+                                      IxkFrag<F8> (&qb)[NCT][D / 32]) {
+  constexpr int EB = F8 ? 1 : 2;
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-    for (int u = 0; u < D / 32; ++u) {
-      const int hh = min(ct * 16 + col, p.group - 1);
-      w[ct][u] = ld16(p.q + (((size_t)b * p.num_q_heads + kvh * p.group + hh) * D + u * 32 + grp * 8) * 2);
-    }
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int hh = min(ct * 16 + col, p.group - 1);
+    ixk_row_frags<D, F8>(p.q + ((size_t)b * p.num_q_heads + kvh * p.group + hh) * D * EB, grp, qb[ct]);
+  }
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
     for (int u = 0; u < D / 32; ++u)
-      qb[ct][u] = __builtin_bit_cast(bf16x8, ct * 16 + col < p.group ? w[ct][u] : make_uint4(0, 0, 0, 0));
+      if (ct * 16 + col >= p.group) qb[ct][u] = ixk_zero<F8>();
 }
 
 // Byte address of key j of (sequence b, KV head kvh), its page read from the
 // block table.
+template <bool F8>
 __device__ __forceinline__ const uint8_t* ixk_key(const IxkParams& p, int b, int kvh, int j, int D) {
   const int P = 1 << p.page_log2;
   const int pg = p.block_table[(size_t)b * p.max_pages + (j >> p.page_log2)];
-  return p.k_pages + (((size_t)pg * p.num_kv_heads + kvh) * P + (j & (P - 1))) * (size_t)D * 2;
+  return p.k_pages + (((size_t)pg * p.num_kv_heads + kvh) * P + (j & (P - 1))) * (size_t)D * (F8 ? 1 : 2);
 }
 
 // K fragments of the 16-key tile at keys key0 .. key0 + 15 (each clamped to
-// L - 1): lane (col, grp) holds dims u * 32 + grp * 8 .. + 8 of key
-// key0 + col.
-template <int D>
+// L - 1): lane (col, grp) holds its channels of key key0 + col.
+template <int D, bool F8>
 __device__ __forceinline__ void ixk_tile(const IxkParams& p, int b, int kvh, int key0, int L, int col, int grp,
-                                         bf16x8 (&kf)[D / 32]) {
-  const uint8_t* rp = ixk_key(p, b, kvh, min(key0 + col, L - 1), D) + grp * 16;
-#pragma unroll
-  for (int u = 0; u < D / 32; ++u) kf[u] = __builtin_bit_cast(bf16x8, ld16(rp + u * 64));
+                                         IxkFrag<F8> (&kf)[D / 32]) {
+  ixk_row_frags<D, F8>(ixk_key<F8>(p, b, kvh, min(key0 + col, L - 1), D), grp, kf);
 }
 
 // Scores of the sampled positions (every 16th) for every head of a KV head,
 // into the compact rows samp[b * H_q + h][i] = s_{16 i}; also each row's
 // length.  Grid (ceil(max_len / (256 * 4 kIxkSampTiles)), H_kv, B), 256
 // threads; a wave scores kIxkSampTiles tiles of 16 sampled positions.
-template <int D, int NCT>
+template <int D, int NCT, bool F8>
 __global__ __launch_bounds__(256) void ixk_samples(IxkParams p) {
   constexpr int NU = D / 32;
   const int b = blockIdx.z, kvh = blockIdx.y;
@@ -661,16 +697,12 @@ __global__ __launch_bounds__(256) void ixk_samples(IxkParams p) {
     for (int i = tid; i < p.group; i += 256) p.row_len[(size_t)b * p.num_q_heads + kvh * p.group + i] = L;
   const int tile0 = (blockIdx.x * 4 + wave) * kIxkSampTiles;
   if (tile0 * 256 >= L) return;
-  bf16x8 qb[NCT][NU];
-  ixk_q<D, NCT>(p, b, kvh, col, grp, qb);
-  bf16x8 kf[kIxkSampTiles][NU];
+  IxkFrag<F8> qb[NCT][NU];
+  ixk_q<D, NCT, F8>(p, b, kvh, col, grp, qb);
+  IxkFrag<F8> kf[kIxkSampTiles][NU];
 #pragma unroll
-  for (int t = 0; t < kIxkSampTiles; ++t) {
-    // lane col loads sampled position 16 (16 tile + col)
-    const uint8_t* rp = ixk_key(p, b, kvh, min((tile0 + t) * 256 + 16 * col, L - 1), D) + grp * 16;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) kf[t][u] = __builtin_bit_cast(bf16x8, ld16(rp + u * 64));
-  }
+  for (int t = 0; t < kIxkSampTiles; ++t)   // lane col loads sampled position 16 (16 tile + col)
+    ixk_row_frags<D, F8>(ixk_key<F8>(p, b, kvh, min((tile0 + t) * 256 + 16 * col, L - 1), D), grp, kf[t]);
 #pragma unroll
   for (int t = 0; t < kIxkSampTiles; ++t) {
     const int line = tile0 + t;   // entries 16 line .. + 15
@@ -679,7 +711,7 @@ __global__ __launch_bounds__(256) void ixk_samples(IxkParams p) {
     for (int ct = 0; ct < NCT; ++ct) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < NU; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][u], qb[ct][u], acc, 0, 0, 0);
+      for (int u = 0; u < NU; ++u) acc = ixk_mfma<F8>(kf[t][u], qb[ct][u], acc);
       const int hh = ct * 16 + col;
       if (hh < p.group) {
         float* dst = p.samp + ((size_t)b * p.num_q_heads + kvh * p.group + hh) * p.samp_stride + line * 16 + grp * 4;
@@ -701,7 +733,7 @@ __global__ __launch_bounds__(256) void ixk_samples(IxkParams p) {
 // end as whole 16-byte pairs, so the few, scattered entries of a tile do not
 // each become a store of their own; entries past them go out directly.  Rows that keep everything
 // (k >= L_b) store nothing.
-template <int D, int NCT>
+template <int D, int NCT, bool F8>
 __global__ __launch_bounds__(256) void ixk_compact(IxkParams p) {
   constexpr int NU = D / 32;
   constexpr int QB = KVSEL_IXK_QB > 0 ? KVSEL_IXK_QB : (D == 128 ? 4 : 8) < kIxkSeg / 16 ? (D == 128 ? 4 : 8) : kIxkSeg / 16;
@@ -722,7 +754,7 @@ __global__ __launch_bounds__(256) void ixk_compact(IxkParams p) {
   // (one round trip) before the page ids go to LDS
   static_assert(kIxkChunk / 16 + 2 <= 256, "one page id per thread");
   const int pg_id = tid < n_pages ? p.block_table[(size_t)b * p.max_pages + first_page + tid] : 0;
-  bf16x8 qb[NCT][NU];
+  IxkFrag<F8> qb[NCT][NU];
   const bool keep_all = p.topk >= L;
   uint32_t tau[NCT];
   size_t rowi[NCT];
@@ -732,7 +764,7 @@ __global__ __launch_bounds__(256) void ixk_compact(IxkParams p) {
     rowi[ct] = (size_t)b * p.num_q_heads + kvh * p.group + min(ct * 16 + col, p.group - 1);
     tau[ct] = p.tau[rowi[ct]];   // read for every lane; used only where `on`
   }
-  ixk_q<D, NCT>(p, b, kvh, col, grp, qb);
+  ixk_q<D, NCT, F8>(p, b, kvh, col, grp, qb);
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
     on[ct] = ct * 16 + col < p.group && !keep_all;
@@ -743,12 +775,12 @@ __global__ __launch_bounds__(256) void ixk_compact(IxkParams p) {
   const int wbase = wave * kIxkSeg;
   if (wbase >= n_keys) return;
   const int seg = chunk * 4 + wave;
-  const size_t head_stride = (size_t)P * D * 2;
+  const size_t head_stride = (size_t)P * D * (F8 ? 1 : 2);
   const size_t page_stride = head_stride * p.num_kv_heads;
   auto krow = [&](int key) -> const uint8_t* {
     const int j = start + key;
     const int pg = page_lds[(j >> p.page_log2) - first_page];
-    return p.k_pages + (size_t)pg * page_stride + kvh * head_stride + (size_t)(j & (P - 1)) * D * 2;
+    return p.k_pages + (size_t)pg * page_stride + kvh * head_stride + (size_t)(j & (P - 1)) * D * (F8 ? 1 : 2);
   };
   constexpr int nt = kIxkSeg / 16;
   static_assert(nt % QB == 0, "whole load batches per segment");
@@ -777,31 +809,38 @@ __global__ __launch_bounds__(256) void ixk_compact(IxkParams p) {
   // whole segments test no key against the row's end
   const bool whole = wbase + kIxkSeg <= n_keys;
   for (int t0 = 0; t0 < nt; t0 += QB) {
-    bf16x8 kb[QB][NU];
+    IxkFrag<F8> kb[QB][NU];
 #pragma unroll
     for (int t = 0; t < QB; ++t) {
-      // whole-line loads, then one DPP exchange (k_line_exchange)
-      const int key = wbase + (t0 + t) * 16 + (col & 7);
-      const int sg = (grp + 4 * (col >> 3)) * 16;
-      const uint8_t* ra = krow(min(key, n_keys - 1)) + sg;
-      const uint8_t* rb = krow(min(key + 8, n_keys - 1)) + sg;
+      if constexpr (F8) {
+        // a lane reads its D / 4 channels of key col: a tile's rows whole
+        ixk_row_frags<D, true>(krow(min(wbase + (t0 + t) * 16 + col, n_keys - 1)), grp, kb[t]);
+      } else {
+        // whole-line loads, then one DPP exchange (k_line_exchange)
+        const int key = wbase + (t0 + t) * 16 + (col & 7);
+        const int sg = (grp + 4 * (col >> 3)) * 16;
+        const uint8_t* ra = krow(min(key, n_keys - 1)) + sg;
+        const uint8_t* rb = krow(min(key + 8, n_keys - 1)) + sg;
 #pragma unroll
-      for (int v = 0; v < NU / 2; ++v) {
-        kb[t][2 * v] = __builtin_bit_cast(bf16x8, ld16(ra + v * 128));
-        kb[t][2 * v + 1] = __builtin_bit_cast(bf16x8, ld16(rb + v * 128));
+        for (int v = 0; v < NU / 2; ++v) {
+          kb[t][2 * v] = __builtin_bit_cast(bf16x8, ld16(ra + v * 128));
+          kb[t][2 * v + 1] = __builtin_bit_cast(bf16x8, ld16(rb + v * 128));
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < QB; ++t) {
+      if constexpr (!F8) {
 #pragma unroll
-      for (int v = 0; v < NU / 2; ++v) k_line_exchange(kb[t][2 * v], kb[t][2 * v + 1], col < 8);
+        for (int v = 0; v < NU / 2; ++v) k_line_exchange(kb[t][2 * v], kb[t][2 * v + 1], col < 8);
+      }
       const int k0 = wbase + (t0 + t) * 16 + grp * 4;   // chunk-relative key of acc[0]
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < NU; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[t][u], qb[ct][u], acc, 0, 0, 0);
+        for (int u = 0; u < NU; ++u) acc = ixk_mfma<F8>(kb[t][u], qb[ct][u], acc);
         float sc[4];
         bool f[4];
         int before = 0, tot = 0;
@@ -857,7 +896,7 @@ __global__ __launch_bounds__(256) void ixk_compact(IxkParams p) {
 // (kFinThreads threads): the fallback of a row whose stored entries do not
 // decide its selection.  Head h sits in its column slot of the indexer's
 // tile (the same MFMA element), so the values are those of the other passes.
-template <int D>
+template <int D, bool F8>
 __device__ void ixk_row_scores(const IxkParams& p, int r, float* dst) {
   constexpr int NU = D / 32;
   const int b = r / p.num_q_heads, h = r % p.num_q_heads;
@@ -865,20 +904,18 @@ __device__ void ixk_row_scores(const IxkParams& p, int r, float* dst) {
   const int L = p.seq_lens[b];
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int col = lane & 15, grp = lane >> 4;
-  bf16x8 qb[NU];
+  IxkFrag<F8> qb[NU];
+  ixk_row_frags<D, F8>(p.q + ((size_t)b * p.num_q_heads + h) * D * (F8 ? 1 : 2), grp, qb);
 #pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (col == hs) w = ld16(p.q + (((size_t)b * p.num_q_heads + h) * D + u * 32 + grp * 8) * 2);
-    qb[u] = __builtin_bit_cast(bf16x8, w);
-  }
+  for (int u = 0; u < NU; ++u)
+    if (col != hs) qb[u] = ixk_zero<F8>();
   const int n_tiles = (L + 15) / 16;
   for (int t = wave; t < n_tiles; t += kFinThreads / kWave) {
-    bf16x8 kf[NU];
-    ixk_tile<D>(p, b, kvh, t * 16, L, col, grp, kf);
+    IxkFrag<F8> kf[NU];
+    ixk_tile<D, F8>(p, b, kvh, t * 16, L, col, grp, kf);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < NU; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], qb[u], acc, 0, 0, 0);
+    for (int u = 0; u < NU; ++u) acc = ixk_mfma<F8>(kf[u], qb[u], acc);
     if (col == hs) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -893,13 +930,13 @@ __device__ void ixk_row_scores(const IxkParams& p, int r, float* dst) {
 // The final selection of the fused path: segments of kIxkSeg positions; a
 // row that falls back first has its scores computed into its own slot area
 // (sp.rp.scores and sp.rp.stride point there), which it no longer needs.
-template <int D>
+template <int D, bool F8>
 __global__ __launch_bounds__(kFinThreads) void ixk_final(SplitParams sp, IxkParams ip) {
   __shared__ RowLds sh;
   __shared__ DigitLds L;
   __shared__ int seg_pre[kIxkSegs + 1];
   split_final_row<kIxkSeg, kIxkSegs / kFinThreads>(sp, sh, L, seg_pre, [&](int r) {
-    ixk_row_scores<D>(ip, r, const_cast<float*>(sp.rp.scores) + (size_t)r * sp.rp.stride);
+    ixk_row_scores<D, F8>(ip, r, const_cast<float*>(sp.rp.scores) + (size_t)r * sp.rp.stride);
   });
 }
 
@@ -1252,16 +1289,16 @@ inline IxkLayout ixk_layout(int num_seqs, int num_q_heads, int max_len, int topk
   return l;
 }
 
-template <int D, int NCT>
+template <int D, int NCT, bool F8>
 hipError_t launch_ixk(const IxkParams& ip, const SplitParams& sp, int num_seqs, int max_len, hipStream_t stream) {
   const int rows = num_seqs * ip.num_q_heads;
   const int lines = (max_len + 255) / 256;
-  hipLaunchKernelGGL((ixk_samples<D, NCT>), dim3((lines + 4 * kIxkSampTiles - 1) / (4 * kIxkSampTiles),
+  hipLaunchKernelGGL((ixk_samples<D, NCT, F8>), dim3((lines + 4 * kIxkSampTiles - 1) / (4 * kIxkSampTiles),
                      ip.num_kv_heads, num_seqs), dim3(256), 0, stream, ip);
   hipLaunchKernelGGL((select_split_sample<true, true>), dim3(rows), dim3(kSampleThreads), 0, stream, sp);
-  hipLaunchKernelGGL((ixk_compact<D, NCT>), dim3((max_len + kIxkChunk - 1) / kIxkChunk, ip.num_kv_heads, num_seqs),
+  hipLaunchKernelGGL((ixk_compact<D, NCT, F8>), dim3((max_len + kIxkChunk - 1) / kIxkChunk, ip.num_kv_heads, num_seqs),
                      dim3(256), 0, stream, ip);
-  hipLaunchKernelGGL((ixk_final<D>), dim3(rows), dim3(kFinThreads), 0, stream, sp, ip);
+  hipLaunchKernelGGL((ixk_final<D, F8>), dim3(rows), dim3(kFinThreads), 0, stream, sp, ip);
   return hipGetLastError();
 }
 
@@ -1283,6 +1320,13 @@ hipError_t launch_indexer_topk(const IndexerTopkArgs& a, hipStream_t stream) {
                        rows, row_len);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.fp8) {
+      e = launch_indexer_fp8(a.k_pages, a.block_table, a.seq_lens, a.q, a.num_seqs, a.num_kv_heads, a.num_q_heads,
+                             a.head_dim, a.page_size, a.max_pages, a.max_seq_len, a.scale, logits, l.stride, stream);
+      if (e != hipSuccess) return e;
+      return launch_select(logits, l.stride, row_len, rows, a.max_seq_len, 0, 0, nullptr, a.topk, 0, 0, a.keep,
+                           a.keep_stride, a.counts, ws + l.o_slots, stream);
+    }
     const DecodePlan pl = plan_decode(a.num_seqs, a.num_kv_heads, a.num_q_heads, a.head_dim, a.max_seq_len, false);
     DecodeArgs d{};
     d.k_pages = a.k_pages;
@@ -1334,11 +1378,15 @@ hipError_t launch_indexer_topk(const IndexerTopkArgs& a, hipStream_t stream) {
   SplitParams sp{rp, reinterpret_cast<uint32_t*>(ws + l.o_tau), reinterpret_cast<int*>(ws + l.o_counts),
                  reinterpret_cast<uint2*>(ws + l.o_slots), l.n_oseg, a.max_seq_len, ip.samp, l.samp_stride};
   const bool two = ip.group > 16;
-  if (a.head_dim == 128)
-    return two ? launch_ixk<128, 2>(ip, sp, a.num_seqs, a.max_seq_len, stream)
-               : launch_ixk<128, 1>(ip, sp, a.num_seqs, a.max_seq_len, stream);
-  return two ? launch_ixk<64, 2>(ip, sp, a.num_seqs, a.max_seq_len, stream)
-             : launch_ixk<64, 1>(ip, sp, a.num_seqs, a.max_seq_len, stream);
+  auto go = [&](auto f8) {
+    constexpr bool F8 = decltype(f8)::value;
+    if (a.head_dim == 128)
+      return two ? launch_ixk<128, 2, F8>(ip, sp, a.num_seqs, a.max_seq_len, stream)
+                 : launch_ixk<128, 1, F8>(ip, sp, a.num_seqs, a.max_seq_len, stream);
+    return two ? launch_ixk<64, 2, F8>(ip, sp, a.num_seqs, a.max_seq_len, stream)
+               : launch_ixk<64, 1, F8>(ip, sp, a.num_seqs, a.max_seq_len, stream);
+  };
+  return a.fp8 ? go(std::true_type{}) : go(std::false_type{});
 }
 
 bool select_rows_split(int rows, int max_len, int max_budget) { return use_split(rows, max_len, max_budget); }

@@ -449,13 +449,16 @@ int kvsel_indexer_scores_fp8(const kvsel_paged_kv* kv, const void* q, int32_t nu
  *        largest s_j, equal scores resolved toward the lower position,
  *        ascending;  counts[b * num_q_heads + h] = n.
  * The sets are exactly those of kvsel_decode_attn_scores (EMIT_LOGITS, same
- * scale) followed by kvsel_select_keep (ROWS mode, sinks 0, window 0,
- * budgets NULL, max_budget topk) on the logits, without the logits being
- * written: long rows compute the scores where the selection needs them
- * (sampled positions, the pass that stores the keys at or above a sampled
- * lower bound of the cut, and a row's fallback) with the same products.
- *   kv      bf16 pages, head_dim 64 or 128; v_pages is not read.
- *   q       [num_seqs][num_q_heads][head_dim] bf16.
+ * scale) -- or, for FP8 E4M3 pages, kvsel_indexer_scores_fp8 -- followed by
+ * kvsel_select_keep (ROWS mode, sinks 0, window 0, budgets NULL, max_budget
+ * topk) on the scores, without the scores being written: long rows compute
+ * them where the selection needs them (sampled positions, the pass that
+ * stores the keys at or above a sampled lower bound of the cut, and a row's
+ * fallback) with the same products in the same order.
+ *   kv      bf16 or FP8 E4M3 pages (kv->dtype KVSEL_BF16 or KVSEL_FP8_E4M3),
+ *           head_dim 64 or 128; v_pages is not read.
+ *   q       [num_seqs][num_q_heads][head_dim] in the pages' format; FP8 q
+ *           and pages 16-byte aligned.
  *   keep    [num_seqs * num_q_heads][keep_stride] i32, keep_stride >=
  *           min(topk, max_seq_len); entries past counts are left untouched.
  *   workspace: >= kvsel_indexer_topk_workspace_bytes(kv, num_q_heads, topk)
@@ -464,9 +467,9 @@ int kvsel_indexer_scores_fp8(const kvsel_paged_kv* kv, const void* q, int32_t nu
  * max_seq_len, block table entries name pages); keep, counts and workspace
  * do not overlap each other or the inputs.
  * Supported: G = num_q_heads / num_kv_heads a power of two <= 8 or 16, 24,
- * 32.  Errors: INVALID (NULL pointers, dims, topk < 1, keep_stride),
- * UNSUPPORTED (dtype other than BF16, head_dim, page_size, G, no gfx950
- * device), WORKSPACE, HIP.
+ * 32.  Errors: INVALID (NULL pointers, dims, topk < 1, keep_stride, unaligned
+ * FP8 q or pages), UNSUPPORTED (dtype other than BF16 or FP8_E4M3, head_dim,
+ * page_size, G, no gfx950 device), WORKSPACE, HIP.
  * ------------------------------------------------------------------------ */
 int kvsel_indexer_topk(const kvsel_paged_kv* kv, const void* q, int32_t num_q_heads, float scale, int32_t topk,
                        int32_t* keep, int64_t keep_stride, int32_t* counts, void* workspace,

@@ -309,6 +309,31 @@ def test_indexer_fp8_validation():
     assert _decode(_kv(dtype=K.KVSEL_FP8_E4M3)) == K.KVSEL_ERR_UNSUPPORTED
 
 
+def test_indexer_topk_validation():
+    """bf16 and FP8 E4M3 pages are taken (the FP8 q and pages 16-byte
+    aligned), f32 pages are not; everything else fails before any HIP call."""
+    lib = K.library()
+    f, wsq = lib.kvsel_indexer_topk, lib.kvsel_indexer_topk_workspace_bytes
+    kv16 = _kv(num_kv_heads=1, head_dim=64, v_pages=None)
+    kv8 = _kv(num_kv_heads=1, head_dim=64, v_pages=None, dtype=K.KVSEL_FP8_E4M3)
+
+    def call(kvd, q=FAKE, topk=256, keep=FAKE, kstride=256, ws=FAKE, wsb=1 << 30):
+        return f(ctypes.byref(kvd), q, 32, 1.0, topk, keep, kstride, FAKE, ws, wsb, None)
+
+    assert wsq(ctypes.byref(kv16), 32, 256) > 0 and wsq(ctypes.byref(kv8), 32, 256) > 0
+    assert wsq(ctypes.byref(_kv(num_kv_heads=1, head_dim=64, dtype=K.KVSEL_F32)), 32, 256) == 0
+    for kvd in (kv16, kv8):
+        assert call(kvd, q=None) == K.KVSEL_ERR_INVALID
+        assert call(kvd, topk=0) == K.KVSEL_ERR_INVALID
+        assert call(kvd, kstride=100) == K.KVSEL_ERR_INVALID
+        assert call(kvd, wsb=16) == K.KVSEL_ERR_WORKSPACE
+    assert call(kv8, q=FAKE + 8) == K.KVSEL_ERR_INVALID                                    # unaligned FP8 q
+    assert call(_kv(num_kv_heads=1, head_dim=64, v_pages=None, dtype=K.KVSEL_FP8_E4M3, k_pages=FAKE + 4)) == \
+        K.KVSEL_ERR_INVALID                                                                  # unaligned FP8 pages
+    assert call(_kv(num_kv_heads=1, head_dim=64, v_pages=None, dtype=K.KVSEL_F32)) == K.KVSEL_ERR_UNSUPPORTED
+    assert call(_kv(num_kv_heads=1, head_dim=96, v_pages=None, dtype=K.KVSEL_FP8_E4M3)) == K.KVSEL_ERR_UNSUPPORTED
+
+
 def test_noalloc_decode_rejects_before_hip():
     """The allocation-free decode validates like the workspace variant and
     rejects a call whose workspace would exceed the static scratch, all

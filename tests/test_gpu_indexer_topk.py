@@ -1,4 +1,4 @@
-"""GPU parity of kvsel_indexer_topk ([LONGCTX] "sparse attention" experiment:
+"""GPU parity of kvsel_indexer_topk, bf16 and FP8 E4M3 ([LONGCTX] "sparse attention" experiment:
 the indexer scores every cached key and each query keeps its top 2048).
 
 The fused call never writes the scores, so it is checked two ways:
@@ -196,3 +196,126 @@ def test_indexer_topk_fallback_bound_too_high():
     assert hot == int(((torch.arange(L, device="cuda") % 256) < 16).sum()) and hot < k
     rows = [(r, kf[r, :int(cf[r])].cpu().numpy()) for r in (0, Hq - 1)]
     _oracle_rows(kp, bt, q, 1.0, [L], Hq, Hq, k, rows)
+
+
+# ---- FP8 E4M3 indexer (keys and queries stored as E4M3) ---------------------
+# The fused call scores with the FP8 matrix-core chain of
+# kvsel_indexer_scores_fp8 (same channels per k-step, same order), so its sets
+# equal kvsel_indexer_scores_fp8 + kvsel_select_keep bit for bit; sampled rows
+# are checked against the oracle's selection on float64 scores of the decoded
+# E4M3 values.  The FP8 matrix cores do not sum their products like a chain of
+# fp32 adds (errors up to ~3e-5 of sum_d |q_d k_d| were measured for the FP8
+# indexer), so a swap with the oracle's set is allowed where both keys' oracle
+# scores lie within the FP8 score tolerance, 1e-4 of that sum, of the cut.
+FP8_SCORE_TOL = 1e-4
+
+
+def _fp8_swaps_ok(got, want, scores, err_scale):
+    """Equal sets, or every differing key's oracle score within FP8_SCORE_TOL
+    of its error scale from the oracle's cut; returns the worst such ratio."""
+    got, want = set(int(x) for x in got), set(int(x) for x in want)
+    assert len(got) == len(want), f"keep sets differ in size: {len(got)} vs {len(want)}"
+    diff = sorted(got ^ want)
+    if not diff:
+        return 0.0
+    tau = min(scores[j] for j in want)
+    worst = max(abs(scores[j] - tau) / err_scale[j] for j in diff)
+    assert worst <= FP8_SCORE_TOL, (f"{len(diff)} differing positions, worst |s - tau| / sum|q k| {worst:.3e} "
+                                    f"> {FP8_SCORE_TOL:g} (tau {tau:.9g}; positions {diff[:8]})")
+    return worst
+
+def _fp8_from(t):
+    return t.to(torch.float8_e4m3fn)
+
+
+def _unfused_fp8(kv, q, Hq, scale, k):
+    K = _K()
+    B, cap = q.shape[0], kv.desc.max_seq_len
+    stride = -(-cap // 4) * 4
+    scores = torch.empty((B, Hq, stride), device="cuda")
+    K.indexer_scores_fp8(kv, q, Hq, scale, scores)
+    rows = scores.view(B * Hq, stride)
+    lens = kv.seq_lens.repeat_interleave(Hq).to(torch.int32)
+    kk = min(k, cap)
+    keep = torch.full((B * Hq, kk), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B * Hq,), -7, dtype=torch.int32, device="cuda")
+    K.select_keep(rows, lens, cap, 0, 0, None, k, keep, cnt)
+    return keep, cnt
+
+
+def _oracle_rows_fp8(kp, bt, q, scale, lens, Hq, G, k, rows):
+    P = kp.shape[2]
+    for r, got in rows:
+        b, h = r // Hq, r % Hq
+        L = lens[b]
+        n_pg = -(-L // P)
+        pages = bt[b, :n_pg].long()
+        kbits = kp[pages, h // G].contiguous().view(torch.uint8).cpu().numpy()     # [n_pg][P][d]
+        KI = O.fp8_e4m3_bits_to_f64(kbits).reshape(n_pg * P, -1)[:L]
+        qv = O.fp8_e4m3_bits_to_f64(q[b, h].contiguous().view(torch.uint8).cpu().numpy())
+        want_s = O.indexer_scores(qv[None, :], KI)[0] * scale
+        err_scale = np.maximum(scale * (np.abs(KI) @ np.abs(qv)), 1e-30)
+        e2e = O.select_keep(want_s, L, 0, 0, k)
+        gap = _fp8_swaps_ok(got, e2e, want_s, err_scale)
+        note(f"  fp8 row b={b} h={h}: {len(set(got.tolist()) ^ set(e2e.tolist()))} differing from the oracle's "
+             f"set, worst |s - tau| / sum|q k| {gap:.2e}")
+
+
+def test_indexer_topk_fp8_128k_sparse_step():
+    """The 128K sparse step's indexer in FP8 at full size (B=4, 32 heads on
+    one d=64 indexer head, L=131073, top-2048)."""
+    K = _K()
+    L, B, Hq = 131072, 4, 32
+    cfg = synth.long_context_128k(seq_len=L, sparse_steps=1, device="cuda")
+    kit = cfg["kv_index"]
+    lens = kit.seq_lens.clone() + 1
+    kp8 = _fp8_from(kit.k_pages)
+    kvi = K.PagedKV(kp8, None, kit.block_table, lens, 16, L + 1)
+    q = _fp8_from(cfg["qi_dec"][0])
+    kf, cf = _fused(kvi, q, Hq, 1.0, 2048)
+    ku, cu = _unfused_fp8(kvi, q, Hq, 1.0, 2048)
+    torch.cuda.synchronize()
+    _same_sets(kf, cf, ku, cu)
+    assert int(cf.min()) == 2048
+    rows = [(r, kf[r, :int(cf[r])].cpu().numpy()) for r in (0, Hq + 5, 3 * Hq + 31)]
+    _oracle_rows_fp8(kp8, kit.block_table, q, 1.0, [L + 1] * B, Hq, Hq, 2048, rows)
+
+
+@pytest.mark.parametrize("B,Hkv,Hq,d,lens,k,P,scale", [
+    (2, 1, 8, 64, [40000, 23457], 2048, 16, 1.0),        # fused, ragged rows
+    (2, 2, 8, 128, [20000, 16391], 1024, 32, 0.125),     # fused, d=128, G=4
+    (1, 1, 32, 64, [70001], 2048, 64, 1.0),              # fused, G=32 (two column tiles)
+    (2, 1, 4, 64, [4000, 3001], 512, 16, 1.0),           # short rows: materialised FP8 scores
+    (1, 1, 8, 64, [20000], 6144, 16, 1.0),               # k > L / 8: materialised FP8 scores
+])
+def test_indexer_topk_fp8_shapes(B, Hkv, Hq, d, lens, k, P, scale):
+    note(f"fp8 indexer top-{k}: B={B} H_kv={Hkv} H_q={Hq} d={d} lens={lens} page={P}")
+    K = _K()
+    g = synth.generator(31 + B + d, "cuda")
+    cap = max(lens)
+    bt, n_pages = synth.shuffled_block_table(B, cap, P, g, "cuda")
+    kp = _fp8_from(2.0 * synth.normal((n_pages, Hkv, P, d), g, torch.float32, "cuda"))
+    kv = K.PagedKV(kp, None, bt, torch.tensor(lens, dtype=torch.int32, device="cuda"), P, cap)
+    q = _fp8_from(2.0 * synth.normal((B, Hq, d), g, torch.float32, "cuda"))
+    kf, cf = _fused(kv, q, Hq, scale, k)
+    ku, cu = _unfused_fp8(kv, q, Hq, scale, k)
+    torch.cuda.synchronize()
+    _same_sets(kf, cf, ku, cu)
+    assert cf.cpu().tolist() == [min(k, lens[r // Hq]) for r in range(B * Hq)]
+    picks = sorted({0, B * Hq - 1, (B // 2) * Hq + Hq // 2})
+    rows = [(r, kf[r, :int(cf[r])].cpu().numpy()) for r in picks]
+    _oracle_rows_fp8(kp, bt, q, scale, lens, Hq, Hq // Hkv, k, rows)
+
+
+def test_indexer_topk_mixed_dtypes_rejected():
+    """bf16 queries on FP8 pages are refused before any launch."""
+    K = _K()
+    g = synth.generator(5, "cuda")
+    bt, n_pages = synth.shuffled_block_table(1, 4096, 16, g, "cuda")
+    kp = _fp8_from(synth.normal((n_pages, 1, 16, 64), g, torch.float32, "cuda"))
+    kv = K.PagedKV(kp, None, bt, torch.tensor([4096], dtype=torch.int32, device="cuda"), 16, 4096)
+    q = synth.normal((1, 8, 64), g, torch.bfloat16, "cuda")
+    keep = torch.empty((8, 256), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((8,), dtype=torch.int32, device="cuda")
+    with pytest.raises(TypeError):
+        K.indexer_topk(kv, q, 8, 1.0, 256, keep, cnt)
