@@ -319,3 +319,60 @@ def test_indexer_topk_mixed_dtypes_rejected():
     cnt = torch.empty((8,), dtype=torch.int32, device="cuda")
     with pytest.raises(TypeError):
         K.indexer_topk(kv, q, 8, 1.0, 256, keep, cnt)
+
+
+def test_indexer_topk_fp8_fallback_ties():
+    """FP8 keys all zero: every score is 0, more keys reach the sampled bound
+    than the final pass holds, and each row is selected from its scores
+    recomputed with the FP8 chain; ties resolve to the lowest positions."""
+    K = _K()
+    B, Hq, L, k = 2, 8, 20000, 2048
+    g = synth.generator(3, "cuda")
+    bt, n_pages = synth.shuffled_block_table(B, L, 16, g, "cuda")
+    kp = torch.zeros((n_pages, 1, 16, 64), device="cuda").to(torch.float8_e4m3fn)
+    kv = K.PagedKV(kp, None, bt, torch.tensor([L, L - 3], dtype=torch.int32, device="cuda"), 16, L)
+    q = _fp8_from(synth.normal((B, Hq, 64), g, torch.float32, "cuda"))
+    kf, cf = _fused(kv, q, Hq, 1.0, k)
+    ku, cu = _unfused_fp8(kv, q, Hq, 1.0, k)
+    torch.cuda.synchronize()
+    _same_sets(kf, cf, ku, cu)
+    expect = torch.arange(k, dtype=torch.int32, device="cuda")
+    for r in range(B * Hq):
+        assert torch.equal(kf[r, :k], expect)
+
+
+def test_indexer_topk_fp8_fallback_bound_too_high():
+    """FP8 keys that score high only at the sampled positions (the first 16
+    of every 256): fewer than k keys reach the sampled bound, so each row
+    falls back to its FP8 scores recomputed in the final pass."""
+    K = _K()
+    B, Hq, L, k, d = 1, 2, 30000, 2048, 64
+    g = synth.generator(21, "cuda")
+    q32 = synth.normal((B, Hq, d), g, torch.float32, "cuda")
+    q = _fp8_from(q32)
+    qdir = q.float()[0, 0]
+    qdir = qdir / qdir.norm()
+    bt, n_pages = synth.shuffled_block_table(B, L, 16, g, "cuda")
+    kl = 0.05 * synth.normal((L, d), g, torch.float32, "cuda")
+    pos = torch.arange(L, device="cuda")
+    hot = (pos % 256) < 16
+    amp = 2.0 + torch.rand(L, generator=g, device="cuda")
+    kl[hot] += amp[hot, None] * qdir[None, :]
+    kl[~hot] += 0.5 * amp[~hot, None] * qdir[None, :]
+    kp = torch.zeros((n_pages, 1, 16, d), device="cuda")
+    synth.write_positions(kp, bt[0], 0, kl[None, :, :])
+    kp = kp.to(torch.float8_e4m3fn)
+    kv = K.PagedKV(kp, None, bt, torch.tensor([L], dtype=torch.int32, device="cuda"), 16, L)
+    kf, cf = _fused(kv, q, Hq, 1.0, k)
+    ku, cu = _unfused_fp8(kv, q, Hq, 1.0, k)
+    torch.cuda.synchronize()
+    _same_sets(kf, cf, ku, cu)
+    # the premise on the FP8 scores of head 0: the k largest reach past the sampled positions
+    stride = -(-L // 4) * 4
+    sc = torch.empty((B, Hq, stride), device="cuda")
+    K.indexer_scores_fp8(kv, q, Hq, 1.0, sc)
+    top = torch.topk(sc[0, 0, :L], k).indices
+    n_hot = int(hot.sum())
+    assert int(((top % 256) < 16).sum()) == n_hot and n_hot < k
+    rows = [(r, kf[r, :int(cf[r])].cpu().numpy()) for r in (0, Hq - 1)]
+    _oracle_rows_fp8(kp, bt, q, 1.0, [L], Hq, Hq, k, rows)
