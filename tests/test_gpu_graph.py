@@ -312,3 +312,74 @@ def test_fused_sparse_step_graph_replays_with_new_queries():
         for a, b in zip((keep, kc, out), want):
             assert torch.equal(a, b), f"replay {rep} differs from the eager step"
         assert int(kc.min()) == k
+
+
+def test_h2o_step_graph_replays_with_new_tokens():
+    """The H2O step with per-step eviction (two launches: the sparse pass
+    that reads the current token as each list's next entry, and the tail
+    kernel) captured once and replayed for successive tokens, with the
+    sequence lengths and queries copied in between: after every replay the
+    lists, their scores, their counts and the outputs equal those of eager
+    steps run on a copy of the lists, bit for bit."""
+    import attention_score_guided_amd as K
+    B, Hq, Hkv, d, P, L0, T = 2, 8, 2, 128, 16, 3000, 4
+    sinks, window, budget = 4, 64, 400
+    g = synth.generator(93)
+    cap = L0 + T + 1
+    bt, n_pages = synth.shuffled_block_table(B, cap, P, g)
+    bt = bt.cuda()
+    kp = synth.normal((n_pages, Hkv, P, d), g, torch.bfloat16).cuda()
+    vp = synth.normal((n_pages, Hkv, P, d), g, torch.bfloat16).cuda()
+    qs = synth.normal((T, B, Hq, d), g, torch.bfloat16).cuda()
+    stride = budget + 16
+    # lists seeded with the last `budget` positions and random scores
+    rng = torch.Generator().manual_seed(93)
+    slots0 = torch.zeros((B, Hkv, stride), dtype=torch.int32)
+    slots0[:, :, :budget] = torch.arange(L0 - budget, L0, dtype=torch.int32)
+    cum0 = torch.zeros((B, Hkv, stride))
+    cum0[:, :, :budget] = torch.rand((B, Hkv, budget), generator=rng)
+    cnt0 = torch.full((B, Hkv), budget, dtype=torch.int32)
+    slots0, cum0, cnt0 = slots0.cuda(), cum0.cuda(), cnt0.cuda()
+    lens = torch.full((B,), L0 + 1, dtype=torch.int32, device="cuda")
+    q = torch.empty((B, Hq, d), dtype=torch.bfloat16, device="cuda")
+    kv = K.PagedKV(kp, vp, bt, lens, P, cap)
+    scale = 1 / math.sqrt(d)
+
+    def run(sl, cm, cn, out, ws):
+        K.h2o_step(kv, q, Hq, scale, sl, cm, cn, sinks, window, budget, out, workspace=ws)
+
+    ws_bytes = K.h2o_workspace_bytes(kv, Hq, stride, sinks, window, budget)
+    g_state = [slots0.clone(), cum0.clone(), cnt0.clone(), torch.zeros((B, Hq, d), device="cuda"),
+               torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")]
+    e_state = [slots0.clone(), cum0.clone(), cnt0.clone(), torch.zeros((B, Hq, d), device="cuda"),
+               torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")]
+    q.copy_(qs[0])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    cap_state = [t.clone() for t in g_state[:3]]   # capture does not run the kernels
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            run(*g_state)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for t_, c_ in zip(g_state[:3], cap_state):
+        t_.copy_(c_)
+    for t in range(T):
+        lens.fill_(L0 + 1 + t)
+        q.copy_(qs[t])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        run(*e_state)
+        torch.cuda.synchronize()
+        n = e_state[2]
+        assert torch.equal(g_state[2], n), f"replay {t}: counts differ"
+        for b in range(B):
+            for c in range(Hkv):
+                m = int(n[b, c])
+                assert torch.equal(g_state[0][b, c, :m], e_state[0][b, c, :m]), f"replay {t}: list ({b}, {c})"
+                assert torch.equal(g_state[1][b, c, :m], e_state[1][b, c, :m]), f"replay {t}: scores ({b}, {c})"
+        assert torch.equal(g_state[3], e_state[3]), f"replay {t}: outputs differ"
+    assert int(g_state[2].min()) == budget   # one token in, one out per step
