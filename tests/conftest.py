@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # A GPU test must never silently pass on a host without a GPU: skip it
-    # explicitly there (the driver runs `-m gpu` only on GPU hosts).
+    # explicitly there (`-m gpu` is meant for hosts with an MI355X).
     try:
         import torch
         has_gpu = torch.cuda.is_available()
