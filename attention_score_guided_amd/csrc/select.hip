@@ -811,30 +811,11 @@ __global__ __launch_bounds__(256) void ixk_compact(IxkParams p) {
   for (int t0 = 0; t0 < nt; t0 += QB) {
     IxkFrag<F8> kb[QB][NU];
 #pragma unroll
-    for (int t = 0; t < QB; ++t) {
-      if constexpr (F8) {
-        // a lane reads its D / 4 channels of key col: a tile's rows whole
-        ixk_row_frags<D, true>(krow(min(wbase + (t0 + t) * 16 + col, n_keys - 1)), grp, kb[t]);
-      } else {
-        // whole-line loads, then one DPP exchange (k_line_exchange)
-        const int key = wbase + (t0 + t) * 16 + (col & 7);
-        const int sg = (grp + 4 * (col >> 3)) * 16;
-        const uint8_t* ra = krow(min(key, n_keys - 1)) + sg;
-        const uint8_t* rb = krow(min(key + 8, n_keys - 1)) + sg;
-#pragma unroll
-        for (int v = 0; v < NU / 2; ++v) {
-          kb[t][2 * v] = __builtin_bit_cast(bf16x8, ld16(ra + v * 128));
-          kb[t][2 * v + 1] = __builtin_bit_cast(bf16x8, ld16(rb + v * 128));
-        }
-      }
-    }
+    for (int t = 0; t < QB; ++t)   // a lane reads its channels of key col (a tile's rows whole)
+      ixk_row_frags<D, F8>(krow(min(wbase + (t0 + t) * 16 + col, n_keys - 1)), grp, kb[t]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < QB; ++t) {
-      if constexpr (!F8) {
-#pragma unroll
-        for (int v = 0; v < NU / 2; ++v) k_line_exchange(kb[t][2 * v], kb[t][2 * v + 1], col < 8);
-      }
       const int k0 = wbase + (t0 + t) * 16 + grp * 4;   // chunk-relative key of acc[0]
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
