@@ -285,6 +285,8 @@ def test_indexer_topk_fp8_128k_sparse_step():
     (2, 1, 8, 64, [40000, 23457], 2048, 16, 1.0),        # fused, ragged rows
     (2, 2, 8, 128, [20000, 16391], 1024, 32, 0.125),     # fused, d=128, G=4
     (1, 1, 32, 64, [70001], 2048, 64, 1.0),              # fused, G=32 (two column tiles)
+    (3, 1, 16, 64, [17000, 1500, 2048], 2048, 16, 1.0),  # fused; two rows keep everything
+    (2, 1, 8, 64, [20000, 2100], 2048, 16, 1.0),         # fused; a short row's sample is below k_lo (bound 0)
     (2, 1, 4, 64, [4000, 3001], 512, 16, 1.0),           # short rows: materialised FP8 scores
     (1, 1, 8, 64, [20000], 6144, 16, 1.0),               # k > L / 8: materialised FP8 scores
 ])
